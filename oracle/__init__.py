@@ -1,0 +1,335 @@
+"""CPU oracle of the 3D Gaussian Splatting training step (numpy front end).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
+the CPU-baseline leg of ``bench.py``; never by the product path.  The
+arithmetic lives in ``gs_oracle.cpp`` (plain C++17, built with g++ by
+``build()``); this module only marshals numpy arrays.
+
+Every function returns fresh numpy arrays.  Per-Gaussian outputs are
+indexed by Gaussian; images are ``[3][H][W]``; parameter planes are
+``[59][n]``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gs_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+TILE = 16
+
+# The oracle's arithmetic contract: no FMA contraction, no fast-math, IEEE
+# division/sqrt, no flush-to-zero (x86-64 SSE keeps subnormals by default).
+CXXFLAGS = ["-O2", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-fPIC", "-shared", "-Wall"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with g++ (a few seconds)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["g++", *CXXFLAGS, "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Cam(C.Structure):
+    _fields_ = [("width", C.c_int32), ("height", C.c_int32),
+                ("fx", C.c_float), ("fy", C.c_float), ("cx", C.c_float), ("cy", C.c_float),
+                ("R", C.c_float * 9), ("t", C.c_float * 3), ("campos", C.c_float * 3),
+                ("near_z", C.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        i64, i32, f64 = C.c_int64, C.c_int, C.c_double
+        L.or_pexp.restype = C.c_float
+        L.or_pexp.argtypes = [C.c_float]
+        L.or_num_threads.restype = C.c_int
+        L.or_set_threads.argtypes = [C.c_int]
+        L.or_sh_basis_f64.argtypes = [P, i64, P]
+        L.or_sh_basis_f32.argtypes = [P, i64, P]
+        L.or_preprocess.argtypes = [P, i64, i64, P] + [P] * 11
+        L.or_preprocess_f64.argtypes = [P, i64, i64, P] + [P] * 6
+        L.or_bin.restype = i64
+        L.or_bin.argtypes = [P, i64, i64, P, P, P, i64, P]
+        L.or_render.argtypes = [P, i64, i64, P, P, P, P, P]
+        L.or_render_brute.argtypes = [P, i64, i64, P, P, P, P]
+        L.or_loss.restype = f64
+        L.or_loss.argtypes = [P, P, i32, i32, f64, f64, P, P, P]
+        L.or_render_frozen_f64.argtypes = [P, P, i64, i64, P, P]
+        L.or_loss_frozen_f64.restype = f64
+        L.or_loss_frozen_f64.argtypes = [P, P, P, i32, i32, f64, f64]
+        L.or_backward.argtypes = [P, i64, i64, P, P, P, P, P, P]
+        L.or_project_backward.argtypes = [P, i64, i64, P, P, P]
+        L.or_project_outputs_f64.argtypes = [P, P, i64, i64, P, P]
+        L.or_adam.argtypes = [P, P, P, P, i64, P, i64, f64, f64, f64, f64, f64, f64]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def cam_struct(cam) -> _Cam:
+    """ctypes camera from a ``synth.Camera`` (or anything with its fields)."""
+    c = _Cam()
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    R = np.asarray(cam.R, np.float32).reshape(9)
+    for k in range(9):
+        c.R[k] = float(R[k])
+    for k in range(3):
+        c.t[k] = float(np.float32(cam.t[k]))
+        c.campos[k] = float(np.float32(cam.campos[k]))
+    c.near_z = float(cam.near)
+    return c
+
+
+def tiles_of(cam):
+    return (cam.width + TILE - 1) // TILE, (cam.height + TILE - 1) // TILE
+
+
+def _params(params):
+    p = np.ascontiguousarray(params, np.float32)
+    assert p.ndim == 2 and p.shape[0] == 59
+    return p
+
+
+def set_threads(n: int):
+    lib().or_set_threads(int(n))
+
+
+def num_threads() -> int:
+    return lib().or_num_threads()
+
+
+def pexp(x):
+    f = lib().or_pexp
+    return np.array([f(float(v)) for v in np.asarray(x, np.float32).ravel()], np.float32)
+
+
+def sh_basis(dirs, dtype=np.float64):
+    d = np.ascontiguousarray(dirs, dtype).reshape(-1, 3)
+    Y = np.empty((d.shape[0], 16), dtype)
+    fn = lib().or_sh_basis_f64 if dtype == np.float64 else lib().or_sh_basis_f32
+    fn(_p(d), d.shape[0], _p(Y))
+    return Y
+
+
+def preprocess(params, cam):
+    """fp32 canonical projection: dict of per-Gaussian arrays."""
+    p = _params(params)
+    n = p.shape[1]
+    out = dict(mean2d=np.empty((n, 2), np.float32), depth=np.empty(n, np.float32),
+               cov2d=np.empty((n, 3), np.float32), conic=np.empty((n, 3), np.float32),
+               opacity=np.empty(n, np.float32), rgb=np.empty((n, 3), np.float32),
+               rgb_pos=np.empty((n, 3), np.uint8), radius=np.empty(n, np.int32),
+               rect=np.empty((n, 4), np.int32), tiles=np.empty(n, np.uint32),
+               visible=np.empty(n, np.uint8))
+    c = cam_struct(cam)
+    lib().or_preprocess(_p(p), n, n, C.byref(c), *[_p(out[k]) for k in (
+        "mean2d", "depth", "cov2d", "conic", "opacity", "rgb", "rgb_pos", "radius", "rect",
+        "tiles", "visible")])
+    out["visible"] = out["visible"].astype(bool)
+    out["rgb_pos"] = out["rgb_pos"].astype(bool)
+    return out
+
+
+def preprocess_f64(params64, cam):
+    p = np.ascontiguousarray(params64, np.float64)
+    n = p.shape[1]
+    out = dict(mean2d=np.empty((n, 2)), depth=np.empty(n), cov2d=np.empty((n, 3)),
+               conic=np.empty((n, 3)), opacity=np.empty(n), rgb=np.empty((n, 3)))
+    c = cam_struct(cam)
+    lib().or_preprocess_f64(_p(p), n, n, C.byref(c), *[_p(out[k]) for k in (
+        "mean2d", "depth", "cov2d", "conic", "opacity", "rgb")])
+    return out
+
+
+def visible_list(params, cam):
+    """Ascending int32 indices of the Gaussians visible in the view."""
+    return np.flatnonzero(preprocess(params, cam)["visible"]).astype(np.int32)
+
+
+def bin_sort(params, cam):
+    """Sorted (key, value) pairs and tile ranges: keys (tile << 32 | depth
+    bits) uint64 [M], values int32 [M], ranges uint32 [T][2]."""
+    p = _params(params)
+    n = p.shape[1]
+    c = cam_struct(cam)
+    M = lib().or_bin(_p(p), n, n, C.byref(c), None, None, 0, None)
+    TX, TY = tiles_of(cam)
+    keys = np.empty(max(M, 1), np.uint64)
+    vals = np.empty(max(M, 1), np.int32)
+    ranges = np.empty((TX * TY, 2), np.uint32)
+    lib().or_bin(_p(p), n, n, C.byref(c), _p(keys), _p(vals), max(M, 1), _p(ranges))
+    return keys[:M], vals[:M], ranges
+
+
+def render(params, cam):
+    """fp32 canonical tiled render: image [3][H][W], T_final [H][W],
+    last [H][W] uint32, tile_processed [T] uint32."""
+    p = _params(params)
+    n = p.shape[1]
+    W, H = cam.width, cam.height
+    TX, TY = tiles_of(cam)
+    img = np.empty((3, H, W), np.float32)
+    Tf = np.empty((H, W), np.float32)
+    last = np.empty((H, W), np.uint32)
+    proc = np.empty(TX * TY, np.uint32)
+    c = cam_struct(cam)
+    lib().or_render(_p(p), n, n, C.byref(c), _p(img), _p(Tf), _p(last), _p(proc))
+    return img, Tf, last, proc
+
+
+def render_brute(params, cam):
+    p = _params(params)
+    n = p.shape[1]
+    W, H = cam.width, cam.height
+    img = np.empty((3, H, W), np.float32)
+    Tf = np.empty((H, W), np.float32)
+    last = np.empty((H, W), np.uint32)
+    c = cam_struct(cam)
+    lib().or_render_brute(_p(p), n, n, C.byref(c), _p(img), _p(Tf), _p(last))
+    return img, Tf, last
+
+
+def loss(image, target, w_l1, w_ssim):
+    """fp64 loss of an fp32 image: (L, dL/dI [3][H][W] f64, mean L1, mean SSIM)."""
+    img = np.ascontiguousarray(image, np.float32)
+    tgt = np.ascontiguousarray(target, np.float32)
+    _, H, W = img.shape
+    dL = np.empty((3, H, W), np.float64)
+    l1 = C.c_double()
+    ss = C.c_double()
+    L = lib().or_loss(_p(img), _p(tgt), W, H, float(w_l1), float(w_ssim), _p(dL),
+                      C.byref(l1), C.byref(ss))
+    return L, dL, l1.value, ss.value
+
+
+def render_frozen_f64(base_params, params64, cam):
+    b = _params(base_params)
+    p = np.ascontiguousarray(params64, np.float64)
+    n = b.shape[1]
+    img = np.empty((3, cam.height, cam.width), np.float64)
+    c = cam_struct(cam)
+    lib().or_render_frozen_f64(_p(b), _p(p), n, n, C.byref(c), _p(img))
+    return img
+
+
+def loss_frozen_f64(image64, image32, target, w_l1, w_ssim):
+    i64 = np.ascontiguousarray(image64, np.float64)
+    i32 = np.ascontiguousarray(image32, np.float32)
+    t = np.ascontiguousarray(target, np.float32)
+    _, H, W = t.shape
+    return lib().or_loss_frozen_f64(_p(i64), _p(i32), _p(t), W, H, float(w_l1), float(w_ssim))
+
+
+def backward(params, cam, dL_dimage, grads=None, mags=None):
+    """fp64 backward of one view.  Returns (g2d [n][9], m2d [n][9],
+    grads [59][n], mags [59][n]); grads/mags accumulate into the given
+    arrays when passed (batch accumulation)."""
+    p = _params(params)
+    n = p.shape[1]
+    dL = np.ascontiguousarray(dL_dimage, np.float64)
+    g2d = np.empty((n, 9))
+    m2d = np.empty((n, 9))
+    if grads is None:
+        grads = np.zeros((59, n))
+    if mags is None:
+        mags = np.zeros((59, n))
+    assert grads.dtype == np.float64 and grads.flags.c_contiguous and grads.shape == (59, n)
+    assert mags.dtype == np.float64 and mags.flags.c_contiguous and mags.shape == (59, n)
+    c = cam_struct(cam)
+    lib().or_backward(_p(p), n, n, C.byref(c), _p(dL), _p(g2d), _p(m2d), _p(grads), _p(mags))
+    return g2d, m2d, grads, mags
+
+
+def project_backward(params, cam, g2d):
+    p = _params(params)
+    n = p.shape[1]
+    g = np.ascontiguousarray(g2d, np.float64)
+    out = np.zeros((59, n))
+    c = cam_struct(cam)
+    lib().or_project_backward(_p(p), n, n, C.byref(c), _p(g), _p(out))
+    return out
+
+
+def project_outputs_f64(base_params, params64, cam):
+    b = _params(base_params)
+    p = np.ascontiguousarray(params64, np.float64)
+    n = b.shape[1]
+    out = np.empty((n, 9))
+    c = cam_struct(cam)
+    lib().or_project_outputs_f64(_p(b), _p(p), n, n, C.byref(c), _p(out))
+    return out
+
+
+def adam(params, grads, m, v, rows, lr, b1, b2, eps, step=1):
+    """fp64 Adam over the listed rows; returns new (params, m, v).  The
+    bias corrections 1 - beta^step are formed here in fp64."""
+    p = np.array(params, np.float64, order="C")
+    g = np.ascontiguousarray(grads, np.float64)
+    mm = np.array(m, np.float64, order="C")
+    vv = np.array(v, np.float64, order="C")
+    r = np.ascontiguousarray(rows, np.int32)
+    ld = p.shape[1]
+    bc1 = 1.0 - b1 ** step
+    bc2 = 1.0 - b2 ** step
+    lib().or_adam(_p(p), _p(g), _p(mm), _p(vv), ld, _p(r), r.shape[0], lr, b1, b2, eps, bc1, bc2)
+    return p, mm, vv
+
+
+def union_list(visible_lists):
+    """Ascending union of per-view visible index lists."""
+    out = np.zeros(0, np.int32)
+    for v in visible_lists:
+        out = np.union1d(out, v)
+    return out.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# one whole training step, stage by stage
+# ---------------------------------------------------------------------------
+
+def step(work, params=None, m=None, v=None, t=1, with_mags=True):
+    """One oracle training step over all views of ``work`` (a
+    ``synth.Workload``).  Returns a dict with per-view forward results,
+    the accumulated fp64 gradients (+ magnitudes), the union list, and the
+    Adam-updated fp64 params / m / v."""
+    p32 = _params(work.params if params is None else params)
+    n = p32.shape[1]
+    grads = np.zeros((59, n))
+    mags = np.zeros((59, n))
+    views = []
+    total_loss = 0.0
+    for cam, tgt in zip(work.cameras, work.targets):
+        img, Tf, last, proc = render(p32, cam)
+        L, dL, l1, ss = loss(img, tgt, work.w_l1, work.w_ssim)
+        g2d, m2d, _, _ = backward(p32, cam, dL, grads, mags)
+        vis = visible_list(p32, cam)
+        views.append(dict(image=img, T_final=Tf, last=last, tile_processed=proc, loss=L,
+                          dL_dimage=dL, g2d=g2d, m2d=m2d, visible=vis))
+        total_loss += L
+    rows = union_list([vw["visible"] for vw in views])
+    m0 = np.zeros((59, n)) if m is None else m
+    v0 = np.zeros((59, n)) if v is None else v
+    p_new, m_new, v_new = adam(p32, grads, m0, v0, rows, work.lr, work.beta1, work.beta2,
+                               work.eps, step=t)
+    return dict(views=views, loss=total_loss, grads=grads, mags=mags, union=rows,
+                params=p_new, m=m_new, v=v_new)
