@@ -1,0 +1,187 @@
+"""Benchmark: train steps/s of one 3D Gaussian Splatting training step on one
+MI355X (forward + backward + sparse Adam), on the mid workload: 1,000,000
+seeded synthetic Gaussians, four 1920x1080 ring views per step.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+Prints ONE JSON line.  `value` = steps/s with every input resident in HBM
+when the timed region starts.  Per-stage times come from HIP events on the
+stream the library launches on; the dominant raster kernel's roofline uses
+them (each raster entry point is a single kernel launch).  `cpu_baseline` is
+the oracle timed on the host's cores on one view of the same workload,
+scaled to a step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train steps/sec (fwd+bwd+Adam), 1M Gaussians @1080p; % of HBM peak"
+HBM_PEAK = 8.0e12              # bytes/s, MI355X HBM3E
+FP32_VECTOR_PEAK = 157.3e12    # flop/s, MI355X fp32 vector (packed)
+TILE = 16
+
+# Algorithmic flops of one pixel examining one list entry, counted from the
+# canonical rule (mul/add/sub/div = 1, fma = 2; rint, ldexp, compares free):
+#   forward : dx, dy 2 + power 7 + exp 19 + alpha 1 + 1 - alpha, T(1 - alpha) 2
+#             + weight 1 + 3 colour fma 6                                  = 38
+#   backward: the forward's alpha 29 + T_i 2 + weight 1 + dL/dc 3
+#             + dL/dalpha 9 + suffix colour 10 + opacity/power 2
+#             + conic 9 + mean 8 + conic recovery 3                        = 76
+FLOPS_PER_EVAL = {"render_fwd": 38, "render_bwd": 76}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(N, views, U):
+    """Compulsory HBM bytes of one step: each stage's inputs read once and
+    outputs written once; sort at its floor of one read + one write of each
+    pair; rasterisers count only the processed prefix M_proc.  Per view with
+    V visible, M pairs, P pixels, T tiles."""
+    total = 0
+    for v in views:
+        V, M, Mp, P, T = v["V"], v["M"], v["M_proc"], v["P"], v["T"]
+        total += (288 * N                 # preprocess: 236 B params in, 52 B projected out
+                  + 16 * N                # visibility scan + visible list
+                  + 16 * V + 12 * M       # key duplication
+                  + 24 * M                # sort floor
+                  + 4 * M + 8 * T         # tile ranges
+                  + 40 * Mp + 20 * P      # raster forward
+                  + 36 * P                # loss
+                  + 40 * Mp + 20 * P + 72 * V   # raster backward
+                  + 744 * V)              # projection backward
+    return total + 1892 * U               # sparse Adam
+
+
+def cpu_baseline(work):
+    """The oracle as it stands, on view 0 of the workload (preprocess, bin,
+    render, loss, backward) plus Adam over the union of view 0, scaled to a
+    step of len(work.cameras) views."""
+    import numpy as np
+
+    import oracle
+    cam, tgt = work.cameras[0], work.targets[0]
+    t0 = time.perf_counter()
+    pre = oracle.preprocess(work.params, cam)
+    oracle.bin_sort(work.params, cam)
+    img, _, _, _ = oracle.render(work.params, cam)
+    _, dL, _, _ = oracle.loss(img, tgt, work.w_l1, work.w_ssim)
+    _, _, grads, _ = oracle.backward(work.params, cam, dL)
+    t_view = time.perf_counter() - t0
+    rows = np.flatnonzero(pre["visible"]).astype(np.int32)
+    t1 = time.perf_counter()
+    oracle.adam(work.params, grads, np.zeros_like(grads), np.zeros_like(grads), rows, work.lr, work.beta1,
+                work.beta2, work.eps)
+    t_adam = time.perf_counter() - t1
+    t_step = len(work.cameras) * t_view + t_adam
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"view 0 of {len(work.cameras)} (full size) + Adam over its visible rows; "
+                      f"step = {len(work.cameras)} x {t_view:.2f} s + {t_adam:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the multi-GPU sharding is a design in DESIGN.md, not code)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"[bench] generating workload {args.config}")
+    work = synth.workload(args.config)
+    N = work.n
+    step = gs.from_workload(work, device="cuda:0", record_tiles=True)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step.step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    step.timer = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer, step.timer = step.timer, None
+    stages = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in timer.items()}
+    launches = {k: len(v) for k, v in timer.items()}
+    ms_per_step = 1e3 * wall / args.steps
+    steps_per_s = args.steps / wall
+
+    # sizes of the last step (scene drifts slowly under Adam; sizes are re-read)
+    views = []
+    for vw, k in zip(step.views, range(len(step.views))):
+        views.append(dict(V=int(step.vis_count[k].item()), M=vw.num_pairs,
+                          M_proc=int(vw.tile_processed.to(torch.int64).sum().item()),
+                          P=vw.W * vw.H, T=vw.T))
+    U = int(step.union_count.item())
+    B = algorithmic_bytes(N, views, U)
+
+    # roofline of the dominant raster kernel (one launch per view)
+    dom = max(("render_fwd", "render_bwd"), key=lambda k: stages.get(k, 0.0))
+    evals = float(np.mean([TILE * TILE * v["M_proc"] for v in views]))
+    flops = evals * FLOPS_PER_EVAL[dom]
+    achieved = flops / (stages[dom] * 1e-3)
+    roofline = {"kernel": "k_render_bwd" if dom == "render_bwd" else "k_render_fwd", "bound": "alu",
+                "achieved": achieved / 1e12, "peak": FP32_VECTOR_PEAK / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / FP32_VECTOR_PEAK, "traffic": None,
+                "avg_launch_ms": stages[dom], "flops_per_launch": flops,
+                "evals_per_launch": evals, "flops_per_eval": FLOPS_PER_EVAL[dom]}
+
+    out = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{work.name}: {N:,} Gaussians, {len(work.cameras)} views of "
+                               f"{work.cameras[0].width}x{work.cameras[0].height}, sparse Adam",
+                   "n": N, "views": len(work.cameras), "width": work.cameras[0].width,
+                   "height": work.cameras[0].height},
+        "images_per_s": steps_per_s * len(work.cameras),
+        "hbm": {"alg_bytes_per_step": B, "alg_GBps": B / (ms_per_step * 1e-3) / 1e9,
+                "frac_of_peak": B / (ms_per_step * 1e-3) / HBM_PEAK},
+        "stages_ms_per_launch": stages,
+        "launches": launches,
+        "sizes": {"V": [v["V"] for v in views], "M": [v["M"] for v in views],
+                  "M_proc": [v["M_proc"] for v in views], "U": U},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] oracle cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(work)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

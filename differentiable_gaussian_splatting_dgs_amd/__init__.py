@@ -1,0 +1,343 @@
+"""Python binding of libgs, the HIP (gfx950) library for one 3D Gaussian
+Splatting training step.
+
+The functions below carry the names of the C entry points declared in
+``include/gs.h`` and only marshal arguments (torch tensors -> device
+pointers, the current HIP stream); every step of the computation runs in the
+library's kernels.  Importing this module fails loudly if ``libgs.so`` has
+not been built: there is no fallback.
+
+``TrainStep`` strings the entry points together for a batch of views and
+owns the device buffers (allocated once with torch, reused across steps).
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgs.so")
+
+GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
+GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM = 0, 1, 2, 3
+GS_PROJ_WORDS = 16
+GS_GRAD2D_WORDS = 12
+TILE = 16
+
+EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
+           "gs_bin_sort", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd", "gs_sparse_adam"]
+
+
+class gs_camera(C.Structure):
+    _fields_ = [("width", C.c_int32), ("height", C.c_int32),
+                ("fx", C.c_float), ("fy", C.c_float), ("cx", C.c_float), ("cy", C.c_float),
+                ("R", C.c_float * 9), ("t", C.c_float * 3), ("campos", C.c_float * 3),
+                ("near_z", C.c_float)]
+
+
+_P, _i64, _i32, _f32, _sz = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_size_t
+_handle = None
+
+
+def lib():
+    """The loaded libgs.so with argument types set (loaded on first use;
+    raises if it has not been built -- there is no fallback)."""
+    global _handle
+    if _handle is not None:
+        return _handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python differentiable_gaussian_splatting_dgs_amd/build.py` "
+                           "(or __graft_entry__.build()); there is no CPU fallback")
+    L = C.CDLL(LIB_PATH)
+    L.gs_status_string.restype = C.c_char_p
+    L.gs_status_string.argtypes = [C.c_int]
+    L.gs_last_error.restype = C.c_char_p
+    L.gs_last_error.argtypes = []
+    L.gs_version.restype = C.c_int
+    L.gs_workspace_size.argtypes = [C.c_int, _i64, _i32, _i32, _i64, C.POINTER(_sz)]
+    L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _sz, _P]
+    L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _sz, _P]
+    L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
+    L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
+    L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
+    L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
+    L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
+                                 _P, _sz, _P]
+    for name in EXPORTS[3:]:
+        getattr(L, name).restype = C.c_int
+    _handle = L
+    return L
+
+
+class GSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().gs_last_error().decode() or lib().gs_status_string(status).decode()
+        super().__init__(f"{where}: {lib().gs_status_string(status).decode()} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != GS_OK:
+        raise GSError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def make_camera(cam) -> gs_camera:
+    """ctypes camera from anything with the fields of ``gs_camera``
+    (width, height, fx, fy, cx, cy, R (3x3), t, campos, near)."""
+    c = gs_camera()
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    R = [float(x) for row in cam.R for x in row]
+    for k in range(9):
+        c.R[k] = R[k]
+    for k in range(3):
+        c.t[k] = float(cam.t[k])
+        c.campos[k] = float(cam.campos[k])
+    c.near_z = float(getattr(cam, "near", getattr(cam, "near_z", 0.2)))
+    return c
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, one wrapper each
+# ---------------------------------------------------------------------------
+
+def gs_version() -> int:
+    return lib().gs_version()
+
+
+def gs_status_string(status: int) -> str:
+    return lib().gs_status_string(status).decode()
+
+
+def gs_last_error() -> str:
+    return lib().gs_last_error().decode()
+
+
+def gs_workspace_size(op: int, n: int = 0, width: int = 0, height: int = 0, pair_capacity: int = 0) -> int:
+    b = _sz(0)
+    _check(lib().gs_workspace_size(op, n, width, height, pair_capacity, C.byref(b)), "gs_workspace_size")
+    return b.value
+
+
+def gs_preprocess(params, n, ld, cam, proj, vis_idx, vis_count, union_flags, workspace, stream=None):
+    c = cam if isinstance(cam, gs_camera) else make_camera(cam)
+    _check(lib().gs_preprocess(_ptr(params), n, ld, C.byref(c), _ptr(proj), _ptr(vis_idx), _ptr(vis_count),
+                              _ptr(union_flags), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)), "gs_preprocess")
+
+
+def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_capacity, tile_ranges, workspace,
+                stream=None) -> int:
+    """Returns M (the pair count); raises GSError(GS_ERR_CAPACITY) with
+    ``.num_pairs`` set when M > pair_capacity."""
+    m = _i64(0)
+    st = lib().gs_bin_sort(_ptr(proj), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys), _ptr(vals),
+                          pair_capacity, C.byref(m), _ptr(tile_ranges), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != GS_OK:
+        err = GSError(st, "gs_bin_sort")
+        err.num_pairs = m.value
+        raise err
+    return m.value
+
+
+def gs_render_fwd(proj, n, vals, tile_ranges, num_pairs, width, height, image, T_final, last,
+                  tile_processed=None, stream=None):
+    _check(lib().gs_render_fwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), num_pairs, width, height,
+                              _ptr(image), _ptr(T_final), _ptr(last), _ptr(tile_processed), _stream(stream)),
+           "gs_render_fwd")
+
+
+def gs_loss(image, target, width, height, w_l1, w_ssim, loss, dL_dimage, workspace, stream=None):
+    _check(lib().gs_loss(_ptr(image), _ptr(target), width, height, float(w_l1), float(w_ssim), _ptr(loss),
+                        _ptr(dL_dimage), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream(stream)), "gs_loss")
+
+
+def gs_render_bwd(proj, n, vals, tile_ranges, num_pairs, width, height, T_final, last, dL_dimage, grad2d,
+                  stream=None):
+    _check(lib().gs_render_bwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), num_pairs, width, height,
+                              _ptr(T_final), _ptr(last), _ptr(dL_dimage), _ptr(grad2d), _stream(stream)),
+           "gs_render_bwd")
+
+
+def gs_project_bwd(params, n, ld, cam, vis_idx, vis_count, grad2d, grads, stream=None):
+    c = cam if isinstance(cam, gs_camera) else make_camera(cam)
+    _check(lib().gs_project_bwd(_ptr(params), n, ld, C.byref(c), _ptr(vis_idx), _ptr(vis_count), _ptr(grad2d),
+                               _ptr(grads), _stream(stream)), "gs_project_bwd")
+
+
+def gs_sparse_adam(params, grads, m, v, n, ld, union_flags, union_idx, union_count, lr, beta1, beta2, eps,
+                   bias_c1, bias_c2, workspace, stream=None):
+    _check(lib().gs_sparse_adam(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, _ptr(union_flags),
+                               _ptr(union_idx), _ptr(union_count), float(lr), float(beta1), float(beta2),
+                               float(eps), float(bias_c1), float(bias_c2), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)), "gs_sparse_adam")
+
+
+# ---------------------------------------------------------------------------
+# a training step over a batch of views
+# ---------------------------------------------------------------------------
+
+def _bytes(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class View:
+    """Per-view device buffers (image-sized ones and the pair arrays)."""
+
+    def __init__(self, cam, target, n, pair_capacity, device):
+        self.cam = make_camera(cam)
+        W, H = self.cam.width, self.cam.height
+        self.W, self.H = W, H
+        self.T = ((W + TILE - 1) // TILE) * ((H + TILE - 1) // TILE)
+        self.target = torch.as_tensor(target, dtype=torch.float32).to(device).contiguous()
+        self.image = torch.empty((3, H, W), dtype=torch.float32, device=device)
+        self.T_final = torch.empty((H, W), dtype=torch.float32, device=device)
+        self.last = torch.empty((H, W), dtype=torch.int32, device=device)
+        self.dL = torch.empty((3, H, W), dtype=torch.float32, device=device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self.ranges = torch.empty((self.T, 2), dtype=torch.int32, device=device)
+        self.tile_processed = torch.empty(self.T, dtype=torch.int32, device=device)
+        self.num_pairs = 0
+
+
+class TrainStep:
+    """Owns parameters, Adam state and scratch; ``step()`` runs one training
+    step (all views of the batch, then sparse Adam)."""
+
+    def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
+                 pair_capacity=None, record_tiles=False):
+        p = torch.as_tensor(params, dtype=torch.float32)
+        assert p.ndim == 2 and p.shape[0] == 59
+        self.device = torch.device(device)
+        self.n = n = int(p.shape[1])
+        self.ld = n
+        self.params = p.to(self.device).contiguous()
+        self.grads = torch.zeros_like(self.params)
+        self.m = torch.zeros_like(self.params)
+        self.v = torch.zeros_like(self.params)
+        self.w_l1, self.w_ssim = float(w_l1), float(w_ssim)
+        self.lr, self.beta1, self.beta2, self.eps = float(lr), float(beta1), float(beta2), float(eps)
+        self.t = 0
+        self.record_tiles = record_tiles
+        self.timer = None        # optional: name -> list of (start, end) torch.cuda.Event pairs
+        rows = max(n, 1)
+        self.proj = torch.empty((rows, GS_PROJ_WORDS), dtype=torch.float32, device=self.device)
+        self.grad2d = torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
+        self.vis_idx = [torch.empty(rows, dtype=torch.int32, device=self.device) for _ in cameras]
+        self.vis_count = torch.zeros(len(cameras), dtype=torch.int64, device=self.device)
+        self.union_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
+        self.union_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
+        self.union_count = torch.zeros(1, dtype=torch.int64, device=self.device)
+        if pair_capacity is None:
+            pair_capacity = max(1 << 20, 48 * n)
+        self.pair_capacity = int(min(pair_capacity, (1 << 31) - 1))
+        self.views = [View(c, tg, n, self.pair_capacity, self.device) for c, tg in zip(cameras, targets)]
+        self._alloc_pairs(self.pair_capacity)
+        self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
+        self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
+        self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
+
+    def _alloc_pairs(self, cap):
+        self.pair_capacity = cap
+        self.keys = torch.empty(max(cap, 1), dtype=torch.int64, device=self.device)
+        self.vals = torch.empty(max(cap, 1), dtype=torch.int32, device=self.device)
+        self.ws_sort = _bytes(gs_workspace_size(GS_OP_BIN_SORT, self.n, 0, 0, cap), self.device)
+
+    @contextlib.contextmanager
+    def _stage(self, name):
+        """Bracket the enclosed launches with events on the current stream
+        (the stream the library launches on) when timing is enabled."""
+        if self.timer is None:
+            yield
+            return
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        yield
+        b.record()
+        self.timer.setdefault(name, []).append((a, b))
+
+    # -- one view ---------------------------------------------------------
+    def forward_view(self, k):
+        vw = self.views[k]
+        n = self.n
+        with self._stage("preprocess"):
+            gs_preprocess(self.params, n, self.ld, vw.cam, self.proj, self.vis_idx[k], self.vis_count[k:k + 1],
+                          self.union_flags, self.ws_pre)
+        with self._stage("bin_sort"):
+            self._bin_sort(k)
+        with self._stage("render_fwd"):
+            gs_render_fwd(self.proj, n, self.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.image, vw.T_final,
+                          vw.last, vw.tile_processed if self.record_tiles else None)
+        with self._stage("loss"):
+            gs_loss(vw.image, vw.target, vw.W, vw.H, self.w_l1, self.w_ssim, vw.loss, vw.dL, self.ws_loss)
+
+    def _bin_sort(self, k):
+        vw = self.views[k]
+        n = self.n
+        try:
+            M = gs_bin_sort(self.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, self.keys,
+                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort)
+        except GSError as e:
+            if e.status != GS_ERR_CAPACITY:
+                raise
+            # grow (once per new high-water mark) and redo the sort
+            self._alloc_pairs(int(min(e.num_pairs * 5 // 4 + 1024, (1 << 31) - 1)))
+            M = gs_bin_sort(self.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, self.keys,
+                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort)
+        vw.num_pairs = M
+
+    def backward_view(self, k, keep_grad2d=False):
+        """Raster backward, then (unless keep_grad2d) projection backward."""
+        vw = self.views[k]
+        with self._stage("render_bwd"):
+            gs_render_bwd(self.proj, self.n, self.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.T_final, vw.last,
+                          vw.dL, self.grad2d)
+        if not keep_grad2d:
+            self.project_view(k)
+
+    def project_view(self, k):
+        vw = self.views[k]
+        with self._stage("project_bwd"):
+            gs_project_bwd(self.params, self.n, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1],
+                           self.grad2d, self.grads)
+
+    def adam(self):
+        self.t += 1
+        bc1 = 1.0 - self.beta1 ** self.t
+        bc2 = 1.0 - self.beta2 ** self.t
+        with self._stage("sparse_adam"):
+            gs_sparse_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.union_flags,
+                           self.union_idx, self.union_count, self.lr, self.beta1, self.beta2, self.eps, bc1,
+                           bc2, self.ws_adam)
+
+    def step(self):
+        """One training step: for each view preprocess, bin/sort, render,
+        loss, backward (gradients accumulate); then sparse Adam."""
+        for k in range(len(self.views)):
+            self.forward_view(k)
+            self.backward_view(k)
+        self.adam()
+
+
+def from_workload(work, device="cuda", **kw) -> TrainStep:
+    """TrainStep for a ``synth.Workload``."""
+    return TrainStep(work.params, work.cameras, work.targets, work.w_l1, work.w_ssim, work.lr, work.beta1,
+                     work.beta2, work.eps, device=device, **kw)

@@ -1,0 +1,267 @@
+// C-ABI layer of libgs: argument checks, workspace carving, stream plumbing
+// and the status/error strings.  Every check runs on the host before any
+// work is enqueued, so a GS_ERR_INVALID_ARG call has launched nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gs.h"
+#include "gs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gs_status fail(gs_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gs_status ok() {
+  g_err[0] = '\0';
+  return GS_OK;
+}
+
+gs_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(GS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int32_t kMaxDim = 65535 * 16;   // tile coordinates are stored in 16 bits
+
+gs_status check_camera(const gs_camera* cam, gs::CamArgs& out) {
+  if (cam == nullptr) return fail(GS_ERR_INVALID_ARG, "camera is NULL");
+  if (cam->width <= 0 || cam->height <= 0 || cam->width > kMaxDim || cam->height > kMaxDim)
+    return fail(GS_ERR_INVALID_ARG, "camera size %dx%d out of range", cam->width, cam->height);
+  const float fs[] = {cam->fx, cam->fy, cam->cx, cam->cy, cam->near_z};
+  for (float f : fs)
+    if (!std::isfinite(f)) return fail(GS_ERR_INVALID_ARG, "camera intrinsics not finite");
+  for (int k = 0; k < 9; ++k) out.R[k] = cam->R[k];
+  for (int k = 0; k < 3; ++k) {
+    out.t[k] = cam->t[k];
+    out.campos[k] = cam->campos[k];
+  }
+  out.fx = cam->fx;
+  out.fy = cam->fy;
+  out.cx = cam->cx;
+  out.cy = cam->cy;
+  out.near_z = cam->near_z;
+  out.width = cam->width;
+  out.height = cam->height;
+  out.tiles_x = (cam->width + 15) / 16;
+  out.tiles_y = (cam->height + 15) / 16;
+  return GS_OK;
+}
+
+gs_status check_size(int32_t width, int32_t height) {
+  if (width <= 0 || height <= 0 || width > kMaxDim || height > kMaxDim)
+    return fail(GS_ERR_INVALID_ARG, "image size %dx%d out of range", width, height);
+  return GS_OK;
+}
+
+#define REQUIRE(cond, ...)                                   \
+  do {                                                       \
+    if (!(cond)) return fail(GS_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+#define CHECK(expr)                          \
+  do {                                       \
+    const gs_status s_ = (expr);             \
+    if (s_ != GS_OK) return s_;              \
+  } while (0)
+
+gs::SsimWindow make_window() {
+  gs::SsimWindow w;
+  double g[11], s = 0.0;
+  for (int k = 0; k < 11; ++k) {
+    g[k] = std::exp(-double((k - 5) * (k - 5)) / (2.0 * 1.5 * 1.5));
+    s += g[k];
+  }
+  for (int k = 0; k < 11; ++k) w.g[k] = float(g[k] / s);
+  return w;
+}
+
+size_t adam_ws_bytes(int64_t n) { return gs::compact_ws_bytes(n); }
+
+}  // namespace
+
+extern "C" {
+
+const char* gs_status_string(int status) {
+  switch (status) {
+    case GS_OK: return "GS_OK";
+    case GS_ERR_INVALID_ARG: return "GS_ERR_INVALID_ARG: invalid argument";
+    case GS_ERR_CAPACITY: return "GS_ERR_CAPACITY: pair capacity exceeded";
+    case GS_ERR_HIP: return "GS_ERR_HIP: HIP runtime error";
+    default: return "unknown gs_status";
+  }
+}
+
+const char* gs_last_error(void) { return g_err; }
+
+int gs_version(void) { return 1; }
+
+gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, int64_t pair_capacity,
+                            size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  switch (op) {
+    case GS_OP_PREPROCESS:
+      REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+      *bytes = gs::preprocess_ws_bytes(n);
+      return ok();
+    case GS_OP_BIN_SORT:
+      REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+      REQUIRE(pair_capacity >= 0 && pair_capacity < (int64_t(1) << 31), "pair_capacity out of range");
+      *bytes = gs::binsort_ws_bytes(n, pair_capacity);
+      return ok();
+    case GS_OP_LOSS:
+      CHECK(check_size(width, height));
+      *bytes = gs::loss_ws_bytes(width, height);
+      return ok();
+    case GS_OP_SPARSE_ADAM:
+      REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+      *bytes = adam_ws_bytes(n);
+      return ok();
+  }
+  return fail(GS_ERR_INVALID_ARG, "unknown op %d", int(op));
+}
+
+gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_camera* cam, float* proj,
+                        int32_t* vis_idx, int64_t* vis_count, uint8_t* union_flags, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  gs::CamArgs c;
+  CHECK(check_camera(cam, c));
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(ld >= n, "ld < n");
+  REQUIRE(vis_count != nullptr, "vis_count is NULL");
+  if (n > 0) {
+    REQUIRE(params && proj && vis_idx, "NULL array");
+    REQUIRE(aligned(proj, 16) && aligned(params, 4) && aligned(vis_idx, 4), "misaligned array");
+  }
+  REQUIRE(union_flags == nullptr || aligned(union_flags, 16), "union_flags not 16-byte aligned");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::preprocess_ws_bytes(n), "workspace too small");
+  return hip_status(gs::launch_preprocess(params, n, ld, c, proj, vis_idx, vis_count, union_flags, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                    "gs_preprocess");
+}
+
+gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                      int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
+                      int64_t* num_pairs, uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  CHECK(check_size(width, height));
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(pair_capacity >= 0 && pair_capacity < (int64_t(1) << 31), "pair_capacity out of range");
+  REQUIRE(vis_count != nullptr && num_pairs != nullptr && tile_ranges != nullptr, "NULL argument");
+  if (n > 0) REQUIRE(proj && vis_idx && aligned(proj, 16), "NULL or misaligned proj / vis_idx");
+  if (pair_capacity > 0) REQUIRE(keys && vals && aligned(keys, 8), "NULL or misaligned keys / vals");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::binsort_ws_bytes(n, pair_capacity), "workspace too small");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, workspace, pair_capacity, st);
+  if (e != hipSuccess) return hip_status(e, "gs_bin_sort (depth sort)");
+  int64_t M = 0;
+  e = hipMemcpyAsync(&M, gs::binsort_count_ptr(workspace, n, pair_capacity), sizeof(int64_t), hipMemcpyDeviceToHost,
+                     st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e, "gs_bin_sort (pair count)");
+  *num_pairs = M;
+  if (M > pair_capacity)
+    return fail(GS_ERR_CAPACITY, "%lld pairs > capacity %lld", (long long)M, (long long)pair_capacity);
+  const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
+  e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, M, TX, TY, keys, vals, tile_ranges, workspace,
+                                pair_capacity, st);
+  return hip_status(e, "gs_bin_sort");
+}
+
+gs_status gs_render_fwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
+                        int64_t num_pairs, int32_t width, int32_t height, float* image, float* T_final,
+                        uint32_t* last, uint32_t* tile_processed, void* stream) {
+  CHECK(check_size(width, height));
+  REQUIRE(n >= 0 && num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "n / num_pairs out of range");
+  REQUIRE(tile_ranges && image && T_final && last, "NULL output or tile_ranges");
+  if (num_pairs > 0) REQUIRE(proj && vals && aligned(proj, 16), "NULL or misaligned proj / vals");
+  return hip_status(gs::launch_render_fwd(proj, vals, tile_ranges, num_pairs, width, height, image, T_final, last,
+                                          tile_processed, static_cast<hipStream_t>(stream)),
+                    "gs_render_fwd");
+}
+
+gs_status gs_loss(const float* image, const float* target, int32_t width, int32_t height, float w_l1,
+                  float w_ssim, float* loss, float* dL_dimage, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  CHECK(check_size(width, height));
+  REQUIRE(image && target && loss && dL_dimage, "NULL argument");
+  REQUIRE(std::isfinite(w_l1) && std::isfinite(w_ssim), "loss weights not finite");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::loss_ws_bytes(width, height), "workspace too small");
+  static const gs::SsimWindow win = make_window();
+  return hip_status(gs::launch_loss(image, target, width, height, w_l1, w_ssim, win, loss, dL_dimage, workspace,
+                                    static_cast<hipStream_t>(stream)),
+                    "gs_loss");
+}
+
+gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
+                        int64_t num_pairs, int32_t width, int32_t height, const float* T_final,
+                        const uint32_t* last, const float* dL_dimage, float* grad2d, void* stream) {
+  CHECK(check_size(width, height));
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "num_pairs out of range");
+  REQUIRE(tile_ranges && T_final && last && dL_dimage, "NULL argument");
+  if (num_pairs > 0) {
+    REQUIRE(proj && vals && grad2d, "NULL array");
+    REQUIRE(aligned(proj, 16) && aligned(grad2d, 16), "proj / grad2d not 16-byte aligned");
+  }
+  return hip_status(gs::launch_render_bwd(proj, vals, tile_ranges, num_pairs, width, height, T_final, last,
+                                          dL_dimage, grad2d, static_cast<hipStream_t>(stream)),
+                    "gs_render_bwd");
+}
+
+gs_status gs_project_bwd(const float* params, int64_t n, int64_t ld, const gs_camera* cam, const int32_t* vis_idx,
+                         const int64_t* vis_count, float* grad2d, float* grads, void* stream) {
+  gs::CamArgs c;
+  CHECK(check_camera(cam, c));
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(ld >= n, "ld < n");
+  REQUIRE(vis_count != nullptr, "vis_count is NULL");
+  if (n > 0) {
+    REQUIRE(params && vis_idx && grad2d && grads, "NULL array");
+    REQUIRE(aligned(grad2d, 16), "grad2d not 16-byte aligned");
+  }
+  return hip_status(gs::launch_project_bwd(params, n, ld, c, vis_idx, vis_count, grad2d, grads,
+                                           static_cast<hipStream_t>(stream)),
+                    "gs_project_bwd");
+}
+
+gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
+                         uint8_t* union_flags, int32_t* union_idx, int64_t* union_count, float lr, float beta1,
+                         float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(ld >= n, "ld < n");
+  REQUIRE(union_count != nullptr, "union_count is NULL");
+  if (n > 0) {
+    REQUIRE(params && grads && m && v && union_flags && union_idx, "NULL array");
+    REQUIRE(aligned(union_flags, 16), "union_flags not 16-byte aligned");
+  }
+  REQUIRE(std::isfinite(lr) && std::isfinite(beta1) && std::isfinite(beta2) && std::isfinite(eps), "non-finite scalar");
+  REQUIRE(bias_c1 > 0.0f && bias_c2 > 0.0f, "bias corrections must be > 0");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= adam_ws_bytes(n), "workspace too small");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = gs::launch_compact(union_flags, n, union_idx, union_count, true, workspace, st);
+  if (e == hipSuccess)
+    e = gs::launch_sparse_adam(params, grads, m, v, n, ld, union_idx, union_count, lr, beta1, beta2, eps, bias_c1,
+                               bias_c2, st);
+  return hip_status(e, "gs_sparse_adam");
+}
+
+}  // extern "C"

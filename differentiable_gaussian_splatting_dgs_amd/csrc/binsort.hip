@@ -1,0 +1,374 @@
+// Binning of Gaussian-tile pairs and their depth order (the Grendel-GS
+// notes' training pipeline: for each pixel find the covering Gaussians and
+// sort them by depth), then the range-extraction stage the Odin summary page
+// lists first in its stage task graph.
+//
+// The sort order is the one of the keys (tile_id << 32 | bits(depth)) with
+// ties in ascending Gaussian index.  It is produced in two steps that give
+// exactly that order with less traffic than a 45-bit radix sort of all
+// pairs:
+//   1. the visible list (ascending indices) is radix-sorted stably by the
+//      32 depth bits -- V elements, not M;
+//   2. pairs are written in that depth order, and a stable LSD radix sort
+//      on the tile bits alone (8-bit digits; 1-2 passes) groups them by
+//      tile while keeping the depth order (and the index order of equal
+//      depths) inside each tile.
+// Radix passes are reduce-then-scan: per-block digit histograms, a scan of
+// each digit row, then a scatter whose in-block rank comes from wave64
+// ballot matching (8 ballots per digit) and per-wave running counts in LDS.
+// No workgroup ever waits on another.
+#include <algorithm>
+
+#include "gs_scan.hpp"
+
+namespace gs {
+namespace {
+
+constexpr int kRT = 256;                 // radix threads per block
+constexpr int kRI = 16;                  // items per thread
+constexpr int kRB = kRT * kRI;           // items per block
+constexpr int kWaves = kRT / 64;
+constexpr int kWaveItems = kRI * 64;
+
+__device__ __forceinline__ uint32_t digit_of(uint32_t k, int shift) { return (k >> shift) & 0xFFu; }
+__device__ __forceinline__ uint32_t digit_of(uint64_t k, int shift) { return uint32_t(k >> shift) & 0xFFu; }
+
+__device__ __forceinline__ int64_t count_of(const int64_t* dev, int64_t host) {
+  return dev != nullptr ? *dev : host;
+}
+
+// ---------------------------------------------------------------------------
+// radix pass pieces
+// ---------------------------------------------------------------------------
+template <class K>
+__global__ __launch_bounds__(kRT) void k_upsweep(const K* __restrict__ keys, const int64_t* count_dev,
+                                                 int64_t count_host, int shift, uint32_t* __restrict__ H,
+                                                 int nb) {
+  __shared__ uint32_t hist[256];
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  hist[t] = 0;
+  __syncthreads();
+  const int64_t count = count_of(count_dev, count_host);
+  const int64_t base = int64_t(blockIdx.x) * kRB + int64_t(w) * kWaveItems;
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    const bool valid = idx < count;
+    const uint64_t act = ballot(valid);
+    if (act == 0) break;
+    const uint32_t d = valid ? digit_of(keys[idx], shift) : 0u;
+    const uint64_t peers = match_bits<8>(d, act);
+    if (valid && count_below(peers) == 0) atomicAdd(&hist[d], uint32_t(__popcll(peers)));
+  }
+  __syncthreads();
+  H[size_t(t) * nb + blockIdx.x] = hist[t];
+}
+
+// grid = 256 blocks, one per digit: exclusive scan of H[d][0..nb) in place,
+// row total to rowtot[d].
+__global__ __launch_bounds__(kRT) void k_rowscan(uint32_t* __restrict__ H, int nb, uint32_t* __restrict__ rowtot) {
+  __shared__ uint32_t sh[kRT / 64];
+  uint32_t* row = H + size_t(blockIdx.x) * nb;
+  uint32_t carry = 0;
+  for (int base = 0; base < nb; base += kRT) {
+    const int i = base + int(threadIdx.x);
+    const uint32_t v = i < nb ? row[i] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<kRT, uint32_t>(v, sh, tot);
+    if (i < nb) row[i] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) rowtot[blockIdx.x] = carry;
+}
+
+template <class K>
+__global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, const uint32_t* __restrict__ vin,
+                                                 K* __restrict__ kout, uint32_t* __restrict__ vout,
+                                                 const int64_t* count_dev, int64_t count_host, int shift,
+                                                 const uint32_t* __restrict__ H,
+                                                 const uint32_t* __restrict__ rowtot, int nb) {
+  __shared__ uint32_t s_w[kWaves][256];     // per-wave running counts, then per-wave offsets
+  __shared__ uint32_t s_dstart[256];
+  __shared__ uint32_t s_gbase[256];
+  __shared__ uint32_t s_sc[kRT / 64];
+  __shared__ K s_key[kRB];
+  __shared__ uint32_t s_val[kRB];
+  const int64_t count = count_of(count_dev, count_host);
+  const int64_t bbase = int64_t(blockIdx.x) * kRB;
+  if (bbase >= count) return;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) s_w[k][t] = 0;
+  __syncthreads();
+  K key[kRI];
+  uint32_t val[kRI], rk[kRI];
+  const int64_t base = bbase + int64_t(w) * kWaveItems;
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    const bool valid = idx < count;
+    key[it] = valid ? kin[idx] : K(0);
+    val[it] = valid ? vin[idx] : 0u;
+    const uint64_t act = ballot(valid);
+    const uint32_t d = digit_of(key[it], shift);
+    const uint64_t peers = match_bits<8>(d, act);
+    const uint32_t below = uint32_t(count_below(peers));
+    const uint32_t prior = s_w[w][d];
+    rk[it] = prior + below;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && below == 0) s_w[w][d] = prior + uint32_t(__popcll(peers));
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // digit t: per-wave counts -> block-local offsets
+  uint32_t c[kWaves], tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    c[k] = s_w[k][t];
+    tot += c[k];
+  }
+  uint32_t btot;
+  const uint32_t ex = block_exclusive_scan<kRT, uint32_t>(tot, s_sc, btot);
+  s_dstart[t] = ex;
+  uint32_t run = ex;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    s_w[k][t] = run;
+    run += c[k];
+  }
+  uint32_t rtot;
+  const uint32_t rex = block_exclusive_scan<kRT, uint32_t>(rowtot[t], s_sc, rtot);
+  s_gbase[t] = rex + H[size_t(t) * nb + blockIdx.x];
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    if (idx < count) {
+      const uint32_t pos = s_w[w][digit_of(key[it], shift)] + rk[it];
+      s_key[pos] = key[it];
+      s_val[pos] = val[it];
+    }
+  }
+  __syncthreads();
+  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
+  for (int j = t; j < nvalid; j += kRT) {
+    const K k = s_key[j];
+    const uint32_t d = digit_of(k, shift);
+    const uint32_t g = s_gbase[d] + (uint32_t(j) - s_dstart[d]);
+    kout[g] = k;
+    vout[g] = s_val[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pipeline kernels
+// ---------------------------------------------------------------------------
+
+// depth keys of the visible list (in ascending index order)
+__global__ __launch_bounds__(256) void k_depth_gather(const float4* __restrict__ proj,
+                                                      const int32_t* __restrict__ vis,
+                                                      const int64_t* __restrict__ vis_count,
+                                                      uint32_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= *vis_count) return;
+  const int32_t g = vis[r];
+  keys[r] = __builtin_bit_cast(uint32_t, proj[4 * int64_t(g) + 3].x);
+  vals[r] = uint32_t(g);
+}
+
+// per-block sums of tiles_touched in depth order
+__global__ __launch_bounds__(kRT) void k_tilesum(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+                                                 const int64_t* __restrict__ vis_count,
+                                                 int64_t* __restrict__ block_sums) {
+  __shared__ int64_t sh[kRT / 64];
+  const int64_t V = *vis_count;
+  const int64_t start = int64_t(blockIdx.x) * kRB + int64_t(threadIdx.x) * kRI;
+  int64_t s = 0;
+  for (int k = 0; k < kRI; ++k) {
+    const int64_t r = start + k;
+    if (r < V) s += __builtin_bit_cast(uint32_t, proj[4 * int64_t(order[r]) + 3].w);
+  }
+  int64_t tot;
+  block_exclusive_scan<kRT, int64_t>(s, sh, tot);
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_sums(int64_t* __restrict__ sums, int nb, int64_t* __restrict__ total) {
+  __shared__ int64_t sh[16];
+  __shared__ int64_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < nb; base += 1024) {
+    const int i = base + int(threadIdx.x);
+    const int64_t v = i < nb ? sums[i] : 0;
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan<1024, int64_t>(v, sh, tot);
+    if (i < nb) sums[i] = carry + ex;
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *total = carry;
+}
+
+// pairs in depth order: for each visible Gaussian (depth rank r), one pair
+// per tile of its rectangle, row-major
+__global__ __launch_bounds__(kRT) void k_duplicate(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+                                                   const int64_t* __restrict__ vis_count,
+                                                   const int64_t* __restrict__ block_offsets, int32_t tiles_x,
+                                                   uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+  __shared__ int64_t sh[kRT / 64];
+  const int64_t V = *vis_count;
+  const int64_t start = int64_t(blockIdx.x) * kRB + int64_t(threadIdx.x) * kRI;
+  int64_t s = 0;
+  for (int k = 0; k < kRI; ++k) {
+    const int64_t r = start + k;
+    if (r < V) s += __builtin_bit_cast(uint32_t, proj[4 * int64_t(order[r]) + 3].w);
+  }
+  int64_t tot;
+  int64_t off = block_exclusive_scan<kRT, int64_t>(s, sh, tot) + block_offsets[blockIdx.x];
+  for (int k = 0; k < kRI; ++k) {
+    const int64_t r = start + k;
+    if (r >= V) break;
+    const uint32_t g = order[r];
+    const float4 q3 = proj[4 * int64_t(g) + 3];
+    const uint64_t dbits = __builtin_bit_cast(uint32_t, q3.x);
+    const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
+    const int x0 = rx & 0xFFFF, x1 = rx >> 16, y0 = ry & 0xFFFF, y1 = ry >> 16;
+    for (int ty = y0; ty < y1; ++ty)
+      for (int tx = x0; tx < x1; ++tx) {
+        keys[off] = (uint64_t(uint32_t(ty * tiles_x + tx)) << 32) | dbits;
+        vals[off] = g;
+        ++off;
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_ranges(const uint64_t* __restrict__ keys, int64_t M,
+                                                uint32_t* __restrict__ ranges) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= M) return;
+  const uint32_t t = uint32_t(keys[i] >> 32);
+  if (i == 0 || uint32_t(keys[i - 1] >> 32) != t) ranges[2 * size_t(t)] = uint32_t(i);
+  if (i == M - 1 || uint32_t(keys[i + 1] >> 32) != t) ranges[2 * size_t(t) + 1] = uint32_t(i + 1);
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+struct Ws {
+  uint32_t *dkA, *dvA, *dkB, *dvB;   // depth sort ping-pong [n]
+  uint32_t* H;                       // radix histograms [256][nb]
+  uint32_t* rowtot;                  // [256]
+  int64_t* bsums;                    // per-block tile sums [nbv + 1]
+  int64_t* m_dev;                    // pair count
+  uint64_t* pk;                      // pair keys scratch [cap]
+  uint32_t* pv;                      // pair values scratch [cap]
+  int nb_hist;
+};
+
+inline int64_t nblocks(int64_t count) { return (count + kRB - 1) / kRB; }
+
+Ws carve(void* ws, int64_t n, int64_t cap) {
+  Ws w;
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) { char* q = p; p += align_up(bytes, 256); return q; };
+  const int64_t nbh = std::max<int64_t>(1, std::max(nblocks(n), nblocks(cap)));
+  w.dkA = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
+  w.dvA = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
+  w.dkB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
+  w.dvB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
+  w.H = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(nbh)));
+  w.rowtot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
+  w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t(nblocks(n) + 1)));
+  w.m_dev = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
+  w.pk = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * size_t(cap)));
+  w.pv = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(cap)));
+  w.nb_hist = int(nbh);
+  return w;
+}
+
+size_t carve_bytes(int64_t n, int64_t cap) {
+  const int64_t nbh = std::max<int64_t>(1, std::max(nblocks(n), nblocks(cap)));
+  size_t b = 0;
+  b += 4 * align_up(sizeof(uint32_t) * size_t(n), 256);
+  b += align_up(sizeof(uint32_t) * 256 * size_t(nbh), 256);
+  b += align_up(sizeof(uint32_t) * 256, 256);
+  b += align_up(sizeof(int64_t) * size_t(nblocks(n) + 1), 256);
+  b += align_up(sizeof(int64_t), 256);
+  b += align_up(sizeof(uint64_t) * size_t(cap), 256);
+  b += align_up(sizeof(uint32_t) * size_t(cap), 256);
+  return b;
+}
+
+template <class K>
+void radix_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, const int64_t* count_dev,
+                int64_t count_host, int64_t count_bound, int shift, const Ws& w, hipStream_t st) {
+  const int nb = int(std::max<int64_t>(1, nblocks(count_bound)));
+  k_upsweep<K><<<nb, kRT, 0, st>>>(kin, count_dev, count_host, shift, w.H, nb);
+  k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
+  k_scatter<K><<<nb, kRT, 0, st>>>(kin, vin, kout, vout, count_dev, count_host, shift, w.H, w.rowtot, nb);
+}
+
+}  // namespace
+
+size_t binsort_ws_bytes(int64_t n, int64_t pair_capacity) { return carve_bytes(n, pair_capacity); }
+
+int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity) {
+  return carve(ws, n, pair_capacity).m_dev;
+}
+
+hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx,
+                                 const int64_t* vis_count, void* ws, int64_t pair_capacity, hipStream_t st) {
+  Ws w = carve(ws, n, pair_capacity);
+  int64_t* m_dev = w.m_dev;
+  const float4* P = reinterpret_cast<const float4*>(proj);
+  if (n > 0) {
+    k_depth_gather<<<unsigned((n + 255) / 256), 256, 0, st>>>(P, vis_idx, vis_count, w.dkA, w.dvA);
+    // stable LSD radix on the 32 depth bits: A -> B -> A -> B -> A
+    for (int pass = 0; pass < 4; ++pass) {
+      const bool even = (pass & 1) == 0;
+      radix_pass<uint32_t>(even ? w.dkA : w.dkB, even ? w.dvA : w.dvB, even ? w.dkB : w.dkA,
+                           even ? w.dvB : w.dvA, vis_count, 0, n, 8 * pass, w, st);
+    }
+  }
+  const int nbv = int(nblocks(n));
+  if (nbv > 0) k_tilesum<<<nbv, kRT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
+  k_scan_sums<<<1, 1024, 0, st>>>(w.bsums, nbv, m_dev);
+  return hipGetLastError();
+}
+
+hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx,
+                                 const int64_t* vis_count, int64_t M, int32_t tiles_x, int32_t tiles_y,
+                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, void* ws,
+                                 int64_t pair_capacity, hipStream_t st) {
+  (void)vis_idx;
+  Ws w = carve(ws, n, pair_capacity);
+  const float4* P = reinterpret_cast<const float4*>(proj);
+  const int64_t T = int64_t(tiles_x) * tiles_y;
+  k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
+  if (M == 0) return hipGetLastError();
+  // number of 8-bit passes over the tile bits
+  int tbits = 0;
+  while ((int64_t(1) << tbits) < T) ++tbits;
+  const int passes = std::max(1, (tbits + 7) / 8);
+  uint32_t* uvals = reinterpret_cast<uint32_t*>(vals);
+  // duplicate into the buffer that makes the last pass land in (keys, vals)
+  uint64_t* bufk[2] = {keys, w.pk};
+  uint32_t* bufv[2] = {uvals, w.pv};
+  int cur = (passes & 1) ? 1 : 0;
+  const int nbv = int(nblocks(n));
+  k_duplicate<<<nbv, kRT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, bufk[cur], bufv[cur]);
+  for (int pass = 0; pass < passes; ++pass) {
+    radix_pass<uint64_t>(bufk[cur], bufv[cur], bufk[cur ^ 1], bufv[cur ^ 1], nullptr, M, M, 32 + 8 * pass, w, st);
+    cur ^= 1;
+  }
+  k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
+  return hipGetLastError();
+}
+
+}  // namespace gs

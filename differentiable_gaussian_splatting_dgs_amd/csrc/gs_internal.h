@@ -1,0 +1,76 @@
+// Internal declarations shared by the translation units of libgs: the
+// camera as passed to kernels and the host-side launchers each kernel file
+// provides to the C-ABI layer.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gs {
+
+// Camera as a kernel argument (by value).
+struct CamArgs {
+  float R[9];
+  float t[3];
+  float campos[3];
+  float fx, fy, cx, cy, near_z;
+  int32_t width, height, tiles_x, tiles_y;
+};
+
+// Gaussian-window weights of the SSIM loss (11 taps, sigma 1.5).
+struct SsimWindow {
+  float g[11];
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// --- preprocess (preprocess.hip) -----------------------------------------
+size_t preprocess_ws_bytes(int64_t n);
+hipError_t launch_preprocess(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
+                             float* proj, int32_t* vis_idx, int64_t* vis_count,
+                             uint8_t* union_flags, void* ws, hipStream_t st);
+
+// --- compaction of a flag array into ascending indices (compact.hip) -----
+size_t compact_ws_bytes(int64_t n);
+// flags[i] != 0 -> idx listed; if clear_flags, flags are zeroed afterwards.
+hipError_t launch_compact(uint8_t* flags, int64_t n, int32_t* idx, int64_t* count, bool clear_flags,
+                          void* ws, hipStream_t st);
+
+// --- bin sort (binsort.hip) ------------------------------------------------
+size_t binsort_ws_bytes(int64_t n, int64_t pair_capacity);
+// Stage 1 (asynchronous): depth sort of the visible list and the pair
+// count M, left in device memory at binsort_count_ptr(ws, ...).
+hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx,
+                                 const int64_t* vis_count, void* ws, int64_t pair_capacity, hipStream_t st);
+int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity);
+// Stage 2 (after M is known on the host): duplication, tile radix sort,
+// tile ranges.
+hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx,
+                                 const int64_t* vis_count, int64_t M, int32_t tiles_x, int32_t tiles_y,
+                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, void* ws,
+                                 int64_t pair_capacity, hipStream_t st);
+
+// --- rasteriser (raster_fwd.hip / raster_bwd.hip) ---------------------------
+hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
+                             int64_t num_pairs, int32_t width, int32_t height, float* image,
+                             float* T_final, uint32_t* last, uint32_t* tile_processed, hipStream_t st);
+hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges, int64_t num_pairs,
+                             int32_t width, int32_t height, const float* T_final, const uint32_t* last,
+                             const float* dL_dimage, float* grad2d, hipStream_t st);
+hipError_t launch_project_bwd(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
+                              const int32_t* vis_idx, const int64_t* vis_count, float* grad2d, float* grads,
+                              hipStream_t st);
+
+// --- loss (loss.hip) --------------------------------------------------------
+size_t loss_ws_bytes(int32_t width, int32_t height);
+hipError_t launch_loss(const float* image, const float* target, int32_t width, int32_t height,
+                       float w_l1, float w_ssim, const SsimWindow& win, float* loss, float* dL_dimage,
+                       void* ws, hipStream_t st);
+
+// --- sparse Adam (adam.hip) ---------------------------------------------------
+hipError_t launch_sparse_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
+                              const int32_t* rows, const int64_t* row_count, float lr, float beta1,
+                              float beta2, float eps, float bc1, float bc2, hipStream_t st);
+
+}  // namespace gs

@@ -1,0 +1,239 @@
+/*
+ * libgs -- one training step of 3D Gaussian Splatting on an AMD MI355X
+ * (gfx950), as a C ABI over hand-written HIP kernels.
+ *
+ * The step (Grendel-GS notes, "Grendel-GS: On Scaling Up 3D Gaussian
+ * Splatting Training", section "Background -- training pipeline"):
+ * project each Gaussian to screen space (2D mean, depth, cover radius,
+ * colour); for each pixel find the covering Gaussians, sort them by depth
+ * and alpha-composite them; L1 + SSIM loss; back-propagate into the
+ * Gaussian parameters.  The Odin summary page ("Odin: Primitive-Level
+ * Synchronization for Distributed Point-Based Neural Rendering", section
+ * "Background and motivation") adds that each view reads and writes only a
+ * sparse, view-dependent set of primitive indices: gs_preprocess emits that
+ * set as a sorted list, gs_render_bwd writes gradients only for it, and
+ * gs_sparse_adam updates only the union of the sets of a batch.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are caller-owned device memory (e.g. PyTorch
+ *    tensors' data_ptr()); the library never allocates, frees or keeps
+ *    them.  "host" pointers are read or written during the call only.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and is asynchronous unless stated otherwise.  Only gs_bin_sort blocks
+ *    (one device-to-host read of the pair count).
+ *  - Errors are returned as gs_status; gs_last_error() gives a
+ *    thread-local message.  Argument checks happen on the host before any
+ *    work is enqueued: on GS_ERR_INVALID_ARG nothing was launched.
+ *  - Concurrent calls on distinct streams with distinct buffers are safe.
+ *
+ * Parameter layout: 59 fp32 planes, plane-major params[k * ld + i] for
+ * Gaussian i (Grendel-GS notes, parameter table): planes 0-2 position,
+ * 3-5 log-scale, 6-9 quaternion (w, x, y, z; normalised by the library),
+ * 10 opacity logit, 11 + 3k + c spherical-harmonic coefficient of basis
+ * k = 0..15 (degree <= 3) and colour channel c.
+ *
+ * Images are planar [3][H][W] fp32; per-pixel planes are [H][W].  Tiles are
+ * 16x16 pixels (Grendel-GS notes, "pixel-wise distribution"), numbered
+ * tile = ty * TX + tx with TX = ceil(W / 16), TY = ceil(H / 16).
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gs_status {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or workspace */
+  GS_ERR_CAPACITY = 2,    /* more Gaussian-tile pairs than pair_capacity */
+  GS_ERR_HIP = 3          /* a HIP runtime call failed */
+} gs_status;
+
+/* Pinhole camera, world -> camera x_c = R x_w + t (R row-major); camera axes
+ * x right, y down, z forward; pixel (i, j) is sampled at (i + 1/2, j + 1/2).
+ * Gaussians with camera-space z <= near_z are not visible. */
+typedef struct gs_camera {
+  int32_t width, height;
+  float fx, fy, cx, cy;
+  float R[9];
+  float t[3];
+  float campos[3]; /* camera centre in world coordinates (view direction of the SH colour) */
+  float near_z;
+} gs_camera;
+
+/* Projected record of a Gaussian: 16 32-bit words, 64-byte aligned rows.
+ *   0 u, 1 v            screen mean (pixels)
+ *   2 A, 3 B, 4 C       conic = inverse screen covariance, power =
+ *                       -(A dx^2 + C dy^2)/2 - B dx dy
+ *   5 opacity           sigmoid(logit)
+ *   6 r, 7 g, 8 b       colour max(0, SH(view dir) + 1/2)
+ *   9, 10               culling half-extents (library-internal)
+ *  11 radius (int32)    ceil(3 sqrt(largest eigenvalue of the covariance))
+ *  12 depth (float)     camera-space z
+ *  13 x0 | x1 << 16, 14 y0 | y1 << 16   half-open tile rectangle
+ *  15 tiles (uint32)    (x1 - x0) (y1 - y0); 0 when not visible
+ * Words 0-11 and 13-15 are zero (9, 10: -inf) for Gaussians that are not
+ * visible. */
+#define GS_PROJ_WORDS 16
+/* floats per Gaussian in the screen-space gradient buffer of gs_render_bwd:
+ * dL/d(u, v, A, B, C, opacity, r, g, b) then 3 unused */
+#define GS_GRAD2D_WORDS 12
+
+typedef enum gs_op {
+  GS_OP_PREPROCESS = 0,
+  GS_OP_BIN_SORT = 1,
+  GS_OP_LOSS = 2,
+  GS_OP_SPARSE_ADAM = 3
+} gs_op;
+
+/* Static description of a status code (never NULL). */
+const char* gs_status_string(int status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* gs_last_error(void);
+/* Library interface version (1). */
+int gs_version(void);
+
+/* Workspace bytes an entry point needs (host, no device work):
+ *   GS_OP_PREPROCESS  n
+ *   GS_OP_BIN_SORT    n, pair_capacity
+ *   GS_OP_LOSS        width, height
+ *   GS_OP_SPARSE_ADAM n
+ * Unused arguments are ignored.  The workspace is caller-owned device
+ * memory, 256-byte aligned; its contents need no initialisation and are
+ * scratch between calls. */
+gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, int64_t pair_capacity,
+                            size_t* bytes);
+
+/* Projection of n Gaussians for one view and the view's visible set
+ * (Grendel-GS notes, training pipeline: "Gaussian transform"; Odin summary
+ * page: the sparse, view-dependent primitive set).
+ *   params       device, [59][ld] fp32, ld >= n
+ *   cam          host
+ *   proj         device out, [n][GS_PROJ_WORDS], 16-byte aligned
+ *   vis_idx      device out, [n] int32: the visible indices in ascending
+ *                order in the first *vis_count entries
+ *   vis_count    device out, int64 scalar
+ *   union_flags  device in/out, [n] uint8, 16-byte aligned, or NULL: set to
+ *                1 for every visible Gaussian, never cleared here (the batch
+ *                union consumed by gs_sparse_adam)
+ *   workspace    device, >= gs_workspace_size(GS_OP_PREPROCESS) bytes
+ * Visible = all 59 parameters finite, z > near_z, non-degenerate
+ * quaternion and screen covariance, finite projection, and a non-empty
+ * tile rectangle. */
+gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_camera* cam, float* proj,
+                        int32_t* vis_idx, int64_t* vis_count, uint8_t* union_flags, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Gaussian-tile pairs sorted by depth within each tile, and the tile ranges
+ * (Grendel-GS notes, training pipeline: "find the covering Gaussians, sort
+ * by depth"; Odin summary page, stage task graph: range extraction).
+ *   proj, vis_idx, vis_count   device, from gs_preprocess (same n, view)
+ *   keys         device out, [pair_capacity] uint64: (tile << 32) | bit
+ *                pattern of the fp32 depth, ascending; equal keys in
+ *                ascending Gaussian index
+ *   vals         device out, [pair_capacity] int32 Gaussian index per pair
+ *   num_pairs    host out: M, the number of pairs
+ *   tile_ranges  device out, [TX*TY][2] uint32: [start, end) of each tile's
+ *                pairs, [0, 0) for empty tiles
+ *   workspace    device, >= gs_workspace_size(GS_OP_BIN_SORT, n, .., pair_capacity)
+ * Blocks the calling thread once, to read M.  If M > pair_capacity the call
+ * writes *num_pairs = M, returns GS_ERR_CAPACITY and writes neither pairs
+ * nor ranges.  pair_capacity must be < 2^31. */
+gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                      int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
+                      int64_t* num_pairs, uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Front-to-back alpha compositing per 16x16 tile (Grendel-GS notes,
+ * training pipeline: "alpha compositing").  Per pixel, over its tile's
+ * pairs in order: power as in GS_PROJ_WORDS; skip if power > 0;
+ * alpha = min(0.99, opacity e^power), skip if alpha < 1/255; stop before the
+ * Gaussian that would bring the transmittance T (1 - alpha) below 1e-4;
+ * C += colour alpha T; T *= 1 - alpha.  Black background.
+ *   proj, vals, tile_ranges, num_pairs   device/host, from gs_preprocess and gs_bin_sort
+ *   image        device out, [3][H][W]
+ *   T_final      device out, [H][W] final transmittance
+ *   last         device out, [H][W] uint32: 1 + list position (within the
+ *                tile's range) of the last composited Gaussian, 0 if none
+ *   tile_processed  device out or NULL, [TX*TY] uint32: per tile, the
+ *                largest number of list entries any of its pixels read
+ *                (up to and including the stopping one) */
+gs_status gs_render_fwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
+                        int64_t num_pairs, int32_t width, int32_t height, float* image, float* T_final,
+                        uint32_t* last, uint32_t* tile_processed, void* stream);
+
+/* Loss of a rendered image against a target (Grendel-GS notes, training
+ * pipeline: "L1 + SSIM loss"):
+ *   L = w_l1 mean|I - I_t| + w_ssim (1 - mean SSIM), means over 3 H W;
+ * SSIM per channel with the 11x11 Gaussian window of sigma 1.5, zero
+ * padding, C1 = 0.01^2, C2 = 0.03^2.  w_ssim = 0 skips the SSIM work.
+ *   image, target   device, [3][H][W]
+ *   loss            device out, fp32 scalar
+ *   dL_dimage       device out, [3][H][W]
+ *   workspace       device, >= gs_workspace_size(GS_OP_LOSS, .., W, H) */
+gs_status gs_loss(const float* image, const float* target, int32_t width, int32_t height, float w_l1,
+                  float w_ssim, float* loss, float* dL_dimage, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Raster backward of one view (Grendel-GS notes, training pipeline:
+ * "back-propagation"): per pixel, the composited Gaussians in reverse order
+ * with the transmittance rebuilt by division and the colour of what lies
+ * behind carried along; the partials of every (pixel, Gaussian) are summed
+ * per Gaussian into its screen-space gradient.
+ *   proj, vals, tile_ranges, num_pairs, T_final, last   from the forward
+ *   dL_dimage    device, [3][H][W]
+ *   grad2d       device in/out, [n][GS_GRAD2D_WORDS] fp32, 16-byte aligned:
+ *                dL/d(u, v, A, B, C, opacity, r, g, b) of the view are ADDED
+ *                to the rows of the Gaussians in the pairs.  Those rows must
+ *                be zero on entry (allocate zeroed; gs_project_bwd re-zeroes
+ *                the rows it consumes, so the buffer stays zero between
+ *                views).
+ * The discrete decisions (skip, stop, 0.99 clamp) are held at the
+ * forward's; the 2D mean gradient is in pixels; depth gets none. */
+gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
+                        int64_t num_pairs, int32_t width, int32_t height, const float* T_final,
+                        const uint32_t* last, const float* dL_dimage, float* grad2d, void* stream);
+
+/* Projection backward of one view: the chain rule from the screen-space
+ * gradients to all 59 parameters (SH coefficients and view direction, EWA
+ * covariance, scale through exp, rotation through the normalised
+ * quaternion, mean through the pinhole map, opacity through the sigmoid),
+ * for the view's visible Gaussians only (Odin summary page: a view writes
+ * only its primitive set).
+ *   params, cam          as for gs_preprocess
+ *   vis_idx, vis_count   device, from gs_preprocess
+ *   grad2d       device in/out, from gs_render_bwd; the visible rows are
+ *                read, then set to zero
+ *   grads        device in/out, [59][ld]: dL/dparams ADDED (+=) for the
+ *                visible rows (accumulates the views of a batch)
+ * The colour clamp decision is recomputed with the forward's arithmetic. */
+gs_status gs_project_bwd(const float* params, int64_t n, int64_t ld, const gs_camera* cam, const int32_t* vis_idx,
+                         const int64_t* vis_count, float* grad2d, float* grads, void* stream);
+
+/* Adam on the union of the batch's visible sets (Odin summary page: updates
+ * touch only the primitives a view used; Grendel-GS notes, "Hyper-parameter
+ * scaling rule": pass lr * sqrt(b) and beta^b for a batch of b views).
+ *   params, grads, m, v   device, [59][ld] fp32
+ *   union_flags  device in/out, [n] uint8, 16-byte aligned: rows to update
+ *                (from gs_preprocess); cleared to 0 on return
+ *   union_idx    device out, [n] int32: the updated rows, ascending
+ *   union_count  device out, int64 scalar
+ *   bias_c1, bias_c2   1 - beta1^t and 1 - beta2^t for step t (t >= 1)
+ * For each listed row i and plane k:
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;
+ *   p -= lr (m / bias_c1) / (sqrt(v / bias_c2) + eps);  g = 0.
+ * Unlisted rows keep p, m, v and g. */
+gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
+                         uint8_t* union_flags, int32_t* union_idx, int64_t* union_count, float lr, float beta1,
+                         float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H */
