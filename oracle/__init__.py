@@ -73,7 +73,7 @@ def lib():
         L.or_render_frozen_f64.argtypes = [P, P, i64, i64, P, P]
         L.or_loss_frozen_f64.restype = f64
         L.or_loss_frozen_f64.argtypes = [P, P, P, i32, i32, f64, f64]
-        L.or_backward.argtypes = [P, i64, i64, P, P, P, P, P, P]
+        L.or_backward.argtypes = [P, i64, i64, P, P, P, P, P, P, P, i32]
         L.or_project_backward.argtypes = [P, i64, i64, P, P, P]
         L.or_project_outputs_f64.argtypes = [P, P, i64, i64, P, P]
         L.or_adam.argtypes = [P, P, P, P, i64, P, i64, f64, f64, f64, f64, f64, f64]
@@ -240,13 +240,18 @@ def loss_frozen_f64(image64, image32, target, w_l1, w_ssim):
     return lib().or_loss_frozen_f64(_p(i64), _p(i32), _p(t), W, H, float(w_l1), float(w_ssim))
 
 
-def backward(params, cam, dL_dimage, grads=None, mags=None):
+def backward(params, cam, dL_dimage, grads=None, mags=None, at_fp32=False, gmag=None):
     """fp64 backward of one view.  Returns (g2d [n][9], m2d [n][9],
     grads [59][n], mags [59][n]); grads/mags accumulate into the given
-    arrays when passed (batch accumulation)."""
+    arrays when passed (batch accumulation).  With ``at_fp32`` the chain
+    rule is evaluated at the fp32 forward's values (screen-space mean,
+    conic, opacity, colour, and the projection's intermediates) instead of
+    their fp64 recomputation.
+    ``gmag`` ([3][H][W], optional) replaces |dL/dI| in the magnitudes."""
     p = _params(params)
     n = p.shape[1]
     dL = np.ascontiguousarray(dL_dimage, np.float64)
+    gm = None if gmag is None else np.ascontiguousarray(gmag, np.float64)
     g2d = np.empty((n, 9))
     m2d = np.empty((n, 9))
     if grads is None:
@@ -256,7 +261,8 @@ def backward(params, cam, dL_dimage, grads=None, mags=None):
     assert grads.dtype == np.float64 and grads.flags.c_contiguous and grads.shape == (59, n)
     assert mags.dtype == np.float64 and mags.flags.c_contiguous and mags.shape == (59, n)
     c = cam_struct(cam)
-    lib().or_backward(_p(p), n, n, C.byref(c), _p(dL), _p(g2d), _p(m2d), _p(grads), _p(mags))
+    lib().or_backward(_p(p), n, n, C.byref(c), _p(dL), None if gm is None else _p(gm), _p(g2d), _p(m2d),
+                      _p(grads), _p(mags), int(at_fp32))
     return g2d, m2d, grads, mags
 
 
@@ -307,29 +313,40 @@ def union_list(visible_lists):
 # one whole training step, stage by stage
 # ---------------------------------------------------------------------------
 
-def step(work, params=None, m=None, v=None, t=1, with_mags=True):
+def step(work, params=None, m=None, v=None, t=1, at_fp32=True, dl_tol=None):
     """One oracle training step over all views of ``work`` (a
     ``synth.Workload``).  Returns a dict with per-view forward results,
     the accumulated fp64 gradients (+ magnitudes), the union list, and the
-    Adam-updated fp64 params / m / v."""
+    Adam-updated fp64 params / m / v.
+
+    The chain rule is evaluated at the fp32 forward's values by default (the
+    gradient of the image that was rendered).  With
+    ``dl_tol = (a, r)`` the image-gradient tolerance a * max|dL/dI| +
+    r * |dL/dI| is also propagated through the backward's magnitudes
+    (``mags_dl``, per view ``m2d_dl``)."""
     p32 = _params(work.params if params is None else params)
     n = p32.shape[1]
     grads = np.zeros((59, n))
     mags = np.zeros((59, n))
+    mags_dl = np.zeros((59, n))
     views = []
     total_loss = 0.0
     for cam, tgt in zip(work.cameras, work.targets):
         img, Tf, last, proc = render(p32, cam)
         L, dL, l1, ss = loss(img, tgt, work.w_l1, work.w_ssim)
-        g2d, m2d, _, _ = backward(p32, cam, dL, grads, mags)
-        vis = visible_list(p32, cam)
-        views.append(dict(image=img, T_final=Tf, last=last, tile_processed=proc, loss=L,
-                          dL_dimage=dL, g2d=g2d, m2d=m2d, visible=vis))
+        g2d, m2d, _, _ = backward(p32, cam, dL, grads, mags, at_fp32=at_fp32)
+        vw = dict(image=img, T_final=Tf, last=last, tile_processed=proc, loss=L, dL_dimage=dL, g2d=g2d, m2d=m2d)
+        if dl_tol is not None:
+            gm = dl_tol[0] * np.max(np.abs(dL)) + dl_tol[1] * np.abs(dL)
+            _, m2d_dl, _, _ = backward(p32, cam, dL, None, mags_dl, at_fp32=at_fp32, gmag=gm)
+            vw["m2d_dl"] = m2d_dl
+        vw["visible"] = visible_list(p32, cam)
+        views.append(vw)
         total_loss += L
     rows = union_list([vw["visible"] for vw in views])
     m0 = np.zeros((59, n)) if m is None else m
     v0 = np.zeros((59, n)) if v is None else v
     p_new, m_new, v_new = adam(p32, grads, m0, v0, rows, work.lr, work.beta1, work.beta2,
                                work.eps, step=t)
-    return dict(views=views, loss=total_loss, grads=grads, mags=mags, union=rows,
+    return dict(views=views, loss=total_loss, grads=grads, mags=mags, mags_dl=mags_dl, union=rows,
                 params=p_new, m=m_new, v=v_new)

@@ -39,6 +39,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #ifdef _OPENMP
@@ -151,6 +152,33 @@ void sh_basis_grad(double x, double y, double z, double dY[16][3]) {
   dY[15][0] = C::c3a * (3.0 * x * x - 3.0 * y * y); dY[15][1] = -6.0 * C::c3a * x * y;
 }
 
+// Magnitudes of the same polynomials: every monomial taken absolutely, so
+// the result bounds what an fp32 evaluation rounds against (used by the
+// error bounds of the backward).
+void sh_basis_mag(double x, double y, double z, double Y[16], double dY[16][3]) {
+  using C = SHC<double>;
+  x = std::fabs(x); y = std::fabs(y); z = std::fabs(z);
+  Y[0] = C::c0; Y[1] = C::c1 * y; Y[2] = C::c1 * z; Y[3] = C::c1 * x;
+  Y[4] = C::c2a * x * y; Y[5] = C::c2a * y * z; Y[6] = C::c2b * (3 * z * z + 1); Y[7] = C::c2a * x * z;
+  Y[8] = C::c2c * (x * x + y * y); Y[9] = C::c3a * y * (3 * x * x + y * y); Y[10] = C::c3b * x * y * z;
+  Y[11] = C::c3c * y * (5 * z * z + 1); Y[12] = C::c3d * z * (5 * z * z + 3); Y[13] = C::c3c * x * (5 * z * z + 1);
+  Y[14] = C::c3e * z * (x * x + y * y); Y[15] = C::c3a * x * (x * x + 3 * y * y);
+  std::memset(dY, 0, sizeof(double) * 48);
+  dY[1][1] = C::c1; dY[2][2] = C::c1; dY[3][0] = C::c1;
+  dY[4][0] = C::c2a * y; dY[4][1] = C::c2a * x;
+  dY[5][1] = C::c2a * z; dY[5][2] = C::c2a * y;
+  dY[6][2] = 6.0 * C::c2b * z;
+  dY[7][0] = C::c2a * z; dY[7][2] = C::c2a * x;
+  dY[8][0] = 2.0 * C::c2c * x; dY[8][1] = 2.0 * C::c2c * y;
+  dY[9][0] = 6.0 * C::c3a * x * y; dY[9][1] = C::c3a * (3.0 * x * x + 3.0 * y * y);
+  dY[10][0] = C::c3b * y * z; dY[10][1] = C::c3b * x * z; dY[10][2] = C::c3b * x * y;
+  dY[11][1] = C::c3c * (5.0 * z * z + 1.0); dY[11][2] = 10.0 * C::c3c * y * z;
+  dY[12][2] = C::c3d * (15.0 * z * z + 3.0);
+  dY[13][0] = C::c3c * (5.0 * z * z + 1.0); dY[13][2] = 10.0 * C::c3c * x * z;
+  dY[14][0] = 2.0 * C::c3e * x * z; dY[14][1] = 2.0 * C::c3e * y * z; dY[14][2] = C::c3e * (x * x + y * y);
+  dY[15][0] = C::c3a * (3.0 * x * x + 3.0 * y * y); dY[15][1] = 6.0 * C::c3a * x * y;
+}
+
 // ---------------------------------------------------------------------------
 // Projection of one Gaussian ("Gaussian transform" of the Grendel-GS
 // training pipeline: 3D Gaussian -> screen-space 2D mean, depth, cover
@@ -174,7 +202,37 @@ template <class F> struct Proj {
   int32_t radius;
   int32_t rect[4];    // x0, y0, x1, y1 (half-open, tiles)
   uint32_t tiles;
+  // intermediates of the forward, consumed by the backward
+  F iz, ux, uy;       // 1/t_z, t_x/t_z, t_y/t_z
+  F s[3];             // exp(log-scale)
+  F qn, q[4];         // |q|^2 and the unit quaternion (w, x, y, z)
+  F R[9];             // rotation of the unit quaternion, row-major
+  F S[6];             // Sigma: 00 01 02 11 12 22
+  F T[6];             // T = J R: rows (T00 T01 T02), (T10 T11 T12)
+  F det;              // det of the dilated screen covariance
+  F dir[3], dn;       // unit view direction and |x - campos|
 };
+
+// fp32 intermediates widened to fp64 (exact)
+Proj<double> widen(const Proj<float>& f) {
+  Proj<double> d;
+  d.visible = f.visible;
+  d.u = f.u; d.v = f.v; d.depth = f.depth;
+  d.a = f.a; d.b = f.b; d.c = f.c;
+  d.A = f.A; d.B = f.B; d.C = f.C;
+  d.opacity = f.opacity;
+  for (int k = 0; k < 3; ++k) {
+    d.rgb[k] = f.rgb[k]; d.rgb_raw[k] = f.rgb_raw[k]; d.rgb_pos[k] = f.rgb_pos[k];
+    d.s[k] = f.s[k]; d.dir[k] = f.dir[k];
+  }
+  d.radius = f.radius;
+  for (int k = 0; k < 4; ++k) { d.rect[k] = f.rect[k]; d.q[k] = f.q[k]; }
+  d.tiles = f.tiles;
+  d.iz = f.iz; d.ux = f.ux; d.uy = f.uy; d.qn = f.qn; d.det = f.det; d.dn = f.dn;
+  for (int k = 0; k < 9; ++k) d.R[k] = f.R[k];
+  for (int k = 0; k < 6; ++k) { d.S[k] = f.S[k]; d.T[k] = f.T[k]; }
+  return d;
+}
 
 template <class F> inline F clampf_tiles(F v, int hi) {
   return v < F(0) ? F(0) : (v > F(hi) ? F(hi) : v);
@@ -201,12 +259,16 @@ void project_one(const F p[59], const or_camera& cam, Proj<F>& o) {
   vis = vis && qn > F(0) && finite(qn);
   const F qi = F(1) / std::sqrt(qn);
   const F w = qw * qi, x = qx * qi, y = qy * qi, z = qz * qi;
+  o.qn = qn; o.q[0] = w; o.q[1] = x; o.q[2] = y; o.q[3] = z;
+  o.s[0] = s0; o.s[1] = s1; o.s[2] = s2;
   const F xx = x * x, yy = y * y, zz = z * z;
   const F xy = x * y, xz = x * z, yz = y * z;
   const F wx = w * x, wy = w * y, wz = w * z;
   const F r00 = F(1) - F(2) * (yy + zz), r01 = F(2) * (xy - wz), r02 = F(2) * (xz + wy);
   const F r10 = F(2) * (xy + wz), r11 = F(1) - F(2) * (xx + zz), r12 = F(2) * (yz - wx);
   const F r20 = F(2) * (xz - wy), r21 = F(2) * (yz + wx), r22 = F(1) - F(2) * (xx + yy);
+  o.R[0] = r00; o.R[1] = r01; o.R[2] = r02; o.R[3] = r10; o.R[4] = r11; o.R[5] = r12;
+  o.R[6] = r20; o.R[7] = r21; o.R[8] = r22;
   // M = Rq diag(s)
   const F m00 = r00 * s0, m01 = r01 * s1, m02 = r02 * s2;
   const F m10 = r10 * s0, m11 = r11 * s1, m12 = r12 * s2;
@@ -218,12 +280,15 @@ void project_one(const F p[59], const or_camera& cam, Proj<F>& o) {
   const F S11 = std::fma(m12, m12, std::fma(m11, m11, m10 * m10));
   const F S12 = std::fma(m12, m22, std::fma(m11, m21, m10 * m20));
   const F S22 = std::fma(m22, m22, std::fma(m21, m21, m20 * m20));
+  o.S[0] = S00; o.S[1] = S01; o.S[2] = S02; o.S[3] = S11; o.S[4] = S12; o.S[5] = S22;
   // T = J R : rows jx (R_0k - ux R_2k), jy (R_1k - uy R_2k)
   const F iz = F(1) / tz;
   const F ux = tx * iz, uy = ty * iz;
   const F jx = F(cam.fx) * iz, jy = F(cam.fy) * iz;
   const F T00 = jx * std::fma(-ux, R6, R0), T01 = jx * std::fma(-ux, R7, R1), T02 = jx * std::fma(-ux, R8, R2);
   const F T10 = jy * std::fma(-uy, R6, R3), T11 = jy * std::fma(-uy, R7, R4), T12 = jy * std::fma(-uy, R8, R5);
+  o.iz = iz; o.ux = ux; o.uy = uy;
+  o.T[0] = T00; o.T[1] = T01; o.T[2] = T02; o.T[3] = T10; o.T[4] = T11; o.T[5] = T12;
   // rows of T Sigma
   const F a00 = std::fma(T02, S02, std::fma(T01, S01, T00 * S00));
   const F a01 = std::fma(T02, S12, std::fma(T01, S11, T00 * S01));
@@ -237,6 +302,7 @@ void project_one(const F p[59], const or_camera& cam, Proj<F>& o) {
   const F ca = c00 + F(0.3), cb = c01, cc = c11 + F(0.3);
   o.a = ca; o.b = cb; o.c = cc;
   const F det = std::fma(ca, cc, -(cb * cb));
+  o.det = det;
   vis = vis && det > F(0) && finite(det);
   const F idet = F(1) / det;
   o.A = cc * idet;
@@ -259,8 +325,10 @@ void project_one(const F p[59], const or_camera& cam, Proj<F>& o) {
   const F dx = X - F(cam.campos[0]), dy = Y - F(cam.campos[1]), dz = Z - F(cam.campos[2]);
   const F dn = std::sqrt(std::fma(dz, dz, std::fma(dy, dy, dx * dx)));
   const F idn = F(1) / dn;
+  o.dn = dn;
+  o.dir[0] = dx * idn; o.dir[1] = dy * idn; o.dir[2] = dz * idn;
   F Yb[16];
-  sh_basis<F>(dx * idn, dy * idn, dz * idn, Yb);
+  sh_basis<F>(o.dir[0], o.dir[1], o.dir[2], Yb);
   for (int ch = 0; ch < 3; ++ch) {
     F acc = Yb[0] * p[11 + ch];
     for (int k = 1; k < 16; ++k) acc = std::fma(Yb[k], p[11 + 3 * k + ch], acc);
@@ -463,57 +531,56 @@ template <> inline double mk<double>(double x) { return x; }
 template <> inline Mag mk<Mag>(double x) { return Mag(x); }
 
 // ---------------------------------------------------------------------------
-// Backward of the projection for one Gaussian (fp64 forward recomputed;
-// colour clamp frozen at the fp32 decision).  g2d = dL/d(u, v, A, B, C,
-// opacity, r, g, b); adds dL/dparam into g[59].  Exact chain rule of
-// project_one.
+// Backward of the projection for one Gaussian: the exact chain rule of
+// project_one, evaluated at the forward intermediates `f` (fp64 ones, or the
+// fp32 forward's widened), with the colour clamp held at rgb_pos.
+// g2d = dL/d(u, v, A, B, C, opacity, r, g, b); writes dL/dparam into g[59].
 // ---------------------------------------------------------------------------
 template <class V>
-void project_backward_one(const double p[59], const or_camera& cam, const bool rgb_pos[3],
+void project_backward_one(const Proj<double>& f, const double p[59], const or_camera& cam, const bool rgb_pos[3],
                           const V g2d[9], V g[59]) {
   const double R[9] = {cam.R[0], cam.R[1], cam.R[2], cam.R[3], cam.R[4], cam.R[5], cam.R[6], cam.R[7], cam.R[8]};
-  const double X = p[0], Y = p[1], Z = p[2];
-  const double tx = R[0] * X + R[1] * Y + R[2] * Z + cam.t[0];
-  const double ty = R[3] * X + R[4] * Y + R[5] * Z + cam.t[1];
-  const double tz = R[6] * X + R[7] * Y + R[8] * Z + cam.t[2];
-  const double s[3] = {std::exp(p[3]), std::exp(p[4]), std::exp(p[5])};
-  const double qn2 = p[6] * p[6] + p[7] * p[7] + p[8] * p[8] + p[9] * p[9];
-  const double qn = std::sqrt(qn2);
-  const double w = p[6] / qn, x = p[7] / qn, y = p[8] / qn, z = p[9] / qn;
-  const double Rq[3][3] = {
-      {1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y)},
-      {2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x)},
-      {2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)}};
-  double M[3][3], S[3][3];
+  const double* s = f.s;
+  const double w = f.q[0], x = f.q[1], y = f.q[2], z = f.q[3];
+  const double qn = std::sqrt(f.qn);
+  double Rq[3][3], M[3][3], S[3][3], T[2][3];
   for (int i = 0; i < 3; ++i)
-    for (int j = 0; j < 3; ++j) M[i][j] = Rq[i][j] * s[j];
+    for (int j = 0; j < 3; ++j) {
+      Rq[i][j] = f.R[3 * i + j];
+      M[i][j] = Rq[i][j] * s[j];
+    }
+  const int sidx[3][3] = {{0, 1, 2}, {1, 3, 4}, {2, 4, 5}};
   for (int i = 0; i < 3; ++i)
-    for (int j = 0; j < 3; ++j) S[i][j] = M[i][0] * M[j][0] + M[i][1] * M[j][1] + M[i][2] * M[j][2];
-  const double fx = cam.fx, fy = cam.fy;
-  const double J[2][3] = {{fx / tz, 0.0, -fx * tx / (tz * tz)}, {0.0, fy / tz, -fy * ty / (tz * tz)}};
-  double T[2][3];
+    for (int j = 0; j < 3; ++j) S[i][j] = f.S[sidx[i][j]];
   for (int i = 0; i < 2; ++i)
-    for (int k = 0; k < 3; ++k) T[i][k] = J[i][0] * R[k] + J[i][1] * R[3 + k] + J[i][2] * R[6 + k];
+    for (int k = 0; k < 3; ++k) T[i][k] = f.T[3 * i + k];
+  // For the error-bound instantiation (V = Mag) every product sum the
+  // backward forms from forward values enters with its terms' magnitudes.
+  constexpr bool kMag = std::is_same<V, Mag>::value;
   double TS[2][3];
   for (int i = 0; i < 2; ++i)
-    for (int k = 0; k < 3; ++k) TS[i][k] = T[i][0] * S[0][k] + T[i][1] * S[1][k] + T[i][2] * S[2][k];
-  const double a = TS[0][0] * T[0][0] + TS[0][1] * T[0][1] + TS[0][2] * T[0][2] + 0.3;
-  const double b = TS[0][0] * T[1][0] + TS[0][1] * T[1][1] + TS[0][2] * T[1][2];
-  const double c = TS[1][0] * T[1][0] + TS[1][1] * T[1][1] + TS[1][2] * T[1][2] + 0.3;
-  const double det = a * c - b * b, det2 = det * det;
-  const double o = 1.0 / (1.0 + std::exp(-p[10]));
+    for (int k = 0; k < 3; ++k)
+      TS[i][k] = kMag ? std::fabs(T[i][0] * S[0][k]) + std::fabs(T[i][1] * S[1][k]) + std::fabs(T[i][2] * S[2][k])
+                      : T[i][0] * S[0][k] + T[i][1] * S[1][k] + T[i][2] * S[2][k];
+  const double a = f.a, b = f.b, c = f.c;
+  const double det2 = f.det * f.det;
+  const double o = f.opacity;
+  const double iz = f.iz, ux = f.ux, uy = f.uy;
+  const double jx = double(cam.fx) * iz, jy = double(cam.fy) * iz;
 
   const V gu = g2d[0], gv = g2d[1], gA = g2d[2], gB = g2d[3], gC = g2d[4], go = g2d[5];
   for (int k = 0; k < 59; ++k) g[k] = mk<V>(0.0);
   // opacity logit
   g[10] = go * (o * (1.0 - o));
   // colour -> SH coefficients and view direction
-  const double dx = X - cam.campos[0], dy = Y - cam.campos[1], dz = Z - cam.campos[2];
-  const double dn = std::sqrt(dx * dx + dy * dy + dz * dz);
-  const double d[3] = {dx / dn, dy / dn, dz / dn};
+  const double* d = f.dir;
   double Yb[16], dY[16][3];
-  sh_basis<double>(d[0], d[1], d[2], Yb);
-  sh_basis_grad(d[0], d[1], d[2], dY);
+  if (kMag) {
+    sh_basis_mag(d[0], d[1], d[2], Yb, dY);
+  } else {
+    sh_basis<double>(d[0], d[1], d[2], Yb);
+    sh_basis_grad(d[0], d[1], d[2], dY);
+  }
   V graw[3];
   for (int ch = 0; ch < 3; ++ch) graw[ch] = rgb_pos[ch] ? g2d[6 + ch] : mk<V>(0.0);
   V gd[3] = {mk<V>(0.0), mk<V>(0.0), mk<V>(0.0)};
@@ -528,7 +595,7 @@ void project_backward_one(const double p[59], const or_camera& cam, const bool r
   // through d = (x - campos) / |x - campos|
   V gdd = gd[0] * d[0] + gd[1] * d[1] + gd[2] * d[2];
   V gpos[3];
-  for (int e = 0; e < 3; ++e) gpos[e] = (gd[e] - gdd * d[e]) / dn;
+  for (int e = 0; e < 3; ++e) gpos[e] = (gd[e] - gdd * d[e]) / f.dn;
   // conic (A, B, C) = (c, -b, a) / det
   const V ga = gA * (-c * c / det2) + gB * (b * c / det2) + gC * (-b * b / det2);
   const V gb = gA * (2.0 * b * c / det2) + gB * (-(a * c + b * b) / det2) + gC * (2.0 * a * b / det2);
@@ -560,11 +627,11 @@ void project_backward_one(const double p[59], const or_camera& cam, const bool r
       for (int k = 0; k < 3; ++k) acc += GT[r][k] * R[3 * m + k];
       GJ[r][m] = acc;
     }
-  V gtx = GJ[0][2] * (-fx / (tz * tz)) + gu * (fx / tz);
-  V gty = GJ[1][2] * (-fy / (tz * tz)) + gv * (fy / tz);
-  V gtz = GJ[0][0] * (-fx / (tz * tz)) + GJ[0][2] * (2.0 * fx * tx / (tz * tz * tz)) +
-          GJ[1][1] * (-fy / (tz * tz)) + GJ[1][2] * (2.0 * fy * ty / (tz * tz * tz)) +
-          gu * (-fx * tx / (tz * tz)) + gv * (-fy * ty / (tz * tz));
+  // J = [[fx/tz, 0, -fx tx/tz^2], [0, fy/tz, -fy ty/tz^2]]; u = fx tx/tz + cx
+  V gtx = GJ[0][2] * (-jx * iz) + gu * jx;
+  V gty = GJ[1][2] * (-jy * iz) + gv * jy;
+  V gtz = GJ[0][0] * (-jx * iz) + GJ[0][2] * (2.0 * jx * ux * iz) + GJ[1][1] * (-jy * iz) +
+          GJ[1][2] * (2.0 * jy * uy * iz) + gu * (-jx * ux) + gv * (-jy * uy);
   // t = R x + t_c
   for (int e = 0; e < 3; ++e) g[e] = gpos[e] + gtx * R[e] + gty * R[3 + e] + gtz * R[6 + e];
   // Sigma = M M^T : G_M = 2 G_Sigma M
@@ -943,21 +1010,28 @@ double or_loss_frozen_f64(const double* image, const float* image32, const float
 
 // ---------------------------------------------------------------------------
 // Backward of one view (fp64), "back-propagation" of the Grendel-GS
-// training pipeline.  Decisions from the fp32 run, values in fp64.
+// training pipeline.  Decisions from the fp32 run, values in fp64; with
+// `at_fp32` the chain rule is evaluated at the fp32 forward's values (the
+// screen-space values the image was rendered from, and the projection's
+// intermediates), i.e. the gradient of the rendered image; without it at
+// the fp64 recomputation of the forward.
 // Per pixel, reverse over its composited Gaussians with
 //   dL/dc_i = alpha_i T_i G,  dL/dalpha_i = T_i (c_i - S_i) . G,
 //   S_{i-1} = alpha_i c_i + (1 - alpha_i) S_i,  S_K = 0 (black background),
 // then alpha = o e^power (unless clamped), power of (u, v, A, B, C).
 // Outputs (all fp64):
 //   g2d  [n][9]  dL/d(u, v, A, B, C, opacity, r, g, b)
-//   m2d  [n][9]  sum over pixels of |partial| (magnitudes)
+//   m2d  [n][9]  sum over pixels of |partial| (magnitudes); with `gmag`
+//                given, |G| is replaced by gmag in them, so passing a bound
+//                on an error of G gives the bound on its effect
 //   grads[59][ld] += dL/dparam  (ld = n here: dense planes)
 //   mags [59][ld] += magnitudes propagated through the projection
 // Per-tile partial sums are merged in tile order, so the result does not
 // depend on the thread count.
 // ---------------------------------------------------------------------------
 void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* cam,
-                 const double* dL_dimage, double* g2d, double* m2d, double* grads, double* mags) {
+                 const double* dL_dimage, const double* gmag, double* g2d, double* m2d, double* grads,
+                 double* mags, int at_fp32) {
   std::vector<Proj<float>> g;
   project_all(params, n, ld, *cam, g);
   std::vector<Proj<double>> h(n);
@@ -968,6 +1042,14 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
     project_one<double>(p, *cam, h[i]);
     // frozen colour clamp: the raw value passes where the fp32 run said > 0
     for (int c = 0; c < 3; ++c) h[i].rgb[c] = g[i].rgb_pos[c] ? h[i].rgb_raw[c] : 0.0;
+    if (at_fp32) {
+      // evaluate the raster backward at the fp32 forward's screen-space
+      // values (what the rendered image was computed from)
+      h[i].u = g[i].u; h[i].v = g[i].v;
+      h[i].A = g[i].A; h[i].B = g[i].B; h[i].C = g[i].C;
+      h[i].opacity = g[i].opacity;
+      for (int c = 0; c < 3; ++c) h[i].rgb[c] = g[i].rgb[c];
+    }
   }
   const int W = cam->width, H = cam->height;
   const int TX = (W + kTile - 1) / kTile, TY = (H + kTile - 1) / kTile;
@@ -990,6 +1072,10 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
         trace_pixel(g, L.data(), int64_t(L.size()), px, py, tr);
         const size_t pix = size_t(py) * W + px;
         const double G[3] = {dL_dimage[pix], dL_dimage[P + pix], dL_dimage[2 * P + pix]};
+        // magnitude of the image gradient used by the bound: |G|, or the
+        // caller's map (e.g. a tolerance on G, to propagate it)
+        const double Gm[3] = {gmag ? gmag[pix] : std::fabs(G[0]), gmag ? gmag[P + pix] : std::fabs(G[1]),
+                              gmag ? gmag[2 * P + pix] : std::fabs(G[2])};
         const double pxc = px + 0.5, pyc = py + 0.5;
         const size_t K = tr.pos.size();
         al.assign(K, 0.0);
@@ -1012,9 +1098,9 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
           double dalpha = 0.0, malpha = 0.0;
           for (int c = 0; c < 3; ++c) {
             o[6 + c] += a * Tk * G[c];
-            o[9 + 6 + c] += std::fabs(a * Tk * G[c]);
+            o[9 + 6 + c] += a * Tk * Gm[c];
             dalpha += Tk * (q.rgb[c] - S[c]) * G[c];
-            malpha += Tk * (std::fabs(q.rgb[c]) + std::fabs(S[c])) * std::fabs(G[c]);
+            malpha += Tk * (std::fabs(q.rgb[c]) + std::fabs(S[c])) * Gm[c];
           }
           for (int c = 0; c < 3; ++c) S[c] = a * q.rgb[c] + (1.0 - a) * S[c];
           if (tr.clamped[kk]) continue;
@@ -1054,10 +1140,11 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
     double p[59];
     load_params<double>(params, ld, i, p);
     double gp[59];
-    project_backward_one<double>(p, *cam, g[i].rgb_pos, &g2d[size_t(i) * 9], gp);
+    const Proj<double> f = at_fp32 ? widen(g[i]) : h[i];
+    project_backward_one<double>(f, p, *cam, g[i].rgb_pos, &g2d[size_t(i) * 9], gp);
     Mag mp[59], m9[9];
     for (int c = 0; c < 9; ++c) m9[c].v = m2d[size_t(i) * 9 + c];
-    project_backward_one<Mag>(p, *cam, g[i].rgb_pos, m9, mp);
+    project_backward_one<Mag>(f, p, *cam, g[i].rgb_pos, m9, mp);
     for (int k = 0; k < 59; ++k) {
       grads[k * ld + i] += gp[k];
       mags[k * ld + i] += mp[k].v;
@@ -1077,7 +1164,9 @@ void or_project_backward(const float* params, int64_t n, int64_t ld, const or_ca
     double p[59];
     load_params<double>(params, ld, i, p);
     double gp[59];
-    project_backward_one<double>(p, *cam, g[i].rgb_pos, &g2d[size_t(i) * 9], gp);
+    Proj<double> f;
+    project_one<double>(p, *cam, f);
+    project_backward_one<double>(f, p, *cam, g[i].rgb_pos, &g2d[size_t(i) * 9], gp);
     for (int k = 0; k < 59; ++k) grads[k * ld + i] += gp[k];
   }
 }

@@ -13,8 +13,11 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:0"):
-    """One training step of the HIP path; per-view snapshots."""
+def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:0", dL_override=None):
+    """One training step of the HIP path; per-view snapshots.  With
+    ``dL_override`` (one [3][H][W] array per view) the backward is fed that
+    image gradient instead of the library's loss output (to test the
+    backward stages in isolation)."""
     import torch
 
     import differentiable_gaussian_splatting_dgs_amd as gs
@@ -40,6 +43,8 @@ def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:
             loss=float(vw.loss.item()),
             dL=vw.dL.cpu().numpy().copy(),
         )
+        if dL_override is not None:
+            vw.dL.copy_(torch.as_tensor(np.asarray(dL_override[k], np.float32)))
         step.backward_view(k, keep_grad2d=True)
         torch.cuda.synchronize()
         out["grad2d"] = step.grad2d[: step.n, :9].cpu().numpy().copy()
@@ -71,17 +76,23 @@ def proj_fields(proj):
     )
 
 
-def check_grad(name, gpu, ref, mag, rel=1e-3, mtol=1e-4):
-    """|gpu - ref| <= rel |ref| + mtol * mag, elementwise, where mag bounds
-    the sum of |terms| behind ref (so fp32 summation order can move the
-    result by a few ulps of mag).  Returns the worst ratio."""
+def check_grad(name, gpu, ref, mag, extra=0.0, rel=1e-3, mtol=1e-4):
+    """|gpu - ref| <= rel |ref| + mtol * mag + extra, elementwise, where mag
+    bounds the sum of |terms| behind ref (so fp32 summation order can move
+    the result by a few ulps of mag) and extra is an input tolerance
+    propagated through the same terms.  Returns the worst ratio."""
     gpu = np.asarray(gpu, np.float64)
     err = np.abs(gpu - ref)
-    tol = rel * np.abs(ref) + mtol * mag + 1e-30
+    tol = rel * np.abs(ref) + mtol * mag + extra + 1e-30
     ratio = err / tol
     worst = float(ratio.max()) if ratio.size else 0.0
     nbad = int((ratio > 1).sum())
     say(f"  {name}: max|err|={err.max() if err.size else 0:.3g} worst err/tol={worst:.3g} bad={nbad}/{err.size}")
+    if nbad:
+        for idx in np.argsort(ratio, axis=None)[::-1][:8]:
+            at = np.unravel_index(idx, ratio.shape)
+            say(f"    at {tuple(int(x) for x in at)}: gpu={gpu[at]:.6e} ref={ref[at]:.6e} "
+                f"mag={np.broadcast_to(mag, ratio.shape)[at]:.3e} ratio={ratio[at]:.3g}")
     assert nbad == 0, f"{name}: {nbad} entries outside tolerance (worst ratio {worst:.3g})"
     return worst
 
