@@ -60,10 +60,10 @@ def lib():
     L.gs_version.restype = C.c_int
     L.gs_workspace_size.argtypes = [C.c_int, _i64, _i32, _i32, _i64, C.POINTER(_sz)]
     L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _sz, _P]
-    L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _sz, _P]
-    L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
+    L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
+    L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
     L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
-    L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
+    L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
     L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
@@ -142,12 +142,12 @@ def gs_preprocess(params, n, ld, cam, proj, vis_idx, vis_count, union_flags, wor
 
 
 def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_capacity, tile_ranges, workspace,
-                stream=None) -> int:
+                tile_order=None, stream=None) -> int:
     """Returns M (the pair count); raises GSError(GS_ERR_CAPACITY) with
     ``.num_pairs`` set when M > pair_capacity."""
     m = _i64(0)
     st = lib().gs_bin_sort(_ptr(proj), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys), _ptr(vals),
-                          pair_capacity, C.byref(m), _ptr(tile_ranges), _ptr(workspace),
+                          pair_capacity, C.byref(m), _ptr(tile_ranges), _ptr(tile_order), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(stream))
     if st != GS_OK:
         err = GSError(st, "gs_bin_sort")
@@ -157,8 +157,9 @@ def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_cap
 
 
 def gs_render_fwd(proj, n, vals, tile_ranges, num_pairs, width, height, image, T_final, last,
-                  tile_processed=None, stream=None):
-    _check(lib().gs_render_fwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), num_pairs, width, height,
+                  tile_processed=None, tile_order=None, stream=None):
+    _check(lib().gs_render_fwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), _ptr(tile_order), num_pairs, width,
+                               height,
                               _ptr(image), _ptr(T_final), _ptr(last), _ptr(tile_processed), _stream(stream)),
            "gs_render_fwd")
 
@@ -170,8 +171,9 @@ def gs_loss(image, target, width, height, w_l1, w_ssim, loss, dL_dimage, workspa
 
 
 def gs_render_bwd(proj, n, vals, tile_ranges, num_pairs, width, height, T_final, last, dL_dimage, grad2d,
-                  stream=None):
-    _check(lib().gs_render_bwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), num_pairs, width, height,
+                  tile_order=None, stream=None):
+    _check(lib().gs_render_bwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), _ptr(tile_order), num_pairs, width,
+                               height,
                               _ptr(T_final), _ptr(last), _ptr(dL_dimage), _ptr(grad2d), _stream(stream)),
            "gs_render_bwd")
 
@@ -213,6 +215,7 @@ class View:
         self.dL = torch.empty((3, H, W), dtype=torch.float32, device=device)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self.ranges = torch.empty((self.T, 2), dtype=torch.int32, device=device)
+        self.order = torch.empty(self.T, dtype=torch.int32, device=device)
         self.tile_processed = torch.empty(self.T, dtype=torch.int32, device=device)
         self.num_pairs = 0
 
@@ -285,7 +288,7 @@ class TrainStep:
             self._bin_sort(k)
         with self._stage("render_fwd"):
             gs_render_fwd(self.proj, n, self.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.image, vw.T_final,
-                          vw.last, vw.tile_processed if self.record_tiles else None)
+                          vw.last, vw.tile_processed if self.record_tiles else None, vw.order)
         with self._stage("loss"):
             gs_loss(vw.image, vw.target, vw.W, vw.H, self.w_l1, self.w_ssim, vw.loss, vw.dL, self.ws_loss)
 
@@ -294,14 +297,14 @@ class TrainStep:
         n = self.n
         try:
             M = gs_bin_sort(self.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, self.keys,
-                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort)
+                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort, vw.order)
         except GSError as e:
             if e.status != GS_ERR_CAPACITY:
                 raise
             # grow (once per new high-water mark) and redo the sort
             self._alloc_pairs(int(min(e.num_pairs * 5 // 4 + 1024, (1 << 31) - 1)))
             M = gs_bin_sort(self.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, self.keys,
-                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort)
+                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort, vw.order)
         vw.num_pairs = M
 
     def backward_view(self, k, keep_grad2d=False):
@@ -309,7 +312,7 @@ class TrainStep:
         vw = self.views[k]
         with self._stage("render_bwd"):
             gs_render_bwd(self.proj, self.n, self.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.T_final, vw.last,
-                          vw.dL, self.grad2d)
+                          vw.dL, self.grad2d, vw.order)
         if not keep_grad2d:
             self.project_view(k)
 

@@ -34,28 +34,29 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, csrc: str = CSRC, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, f"-I{csrc}", *extra, "-c", os.path.join(csrc, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile every kernel source and link libgs.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, csrc: str = CSRC, out: str = OUT, build_dir: str = BUILD, extra=()) -> str:
+    """Compile every kernel source of `csrc` and link `out` (libgs.so by
+    default); returns its path."""
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(8, len(SOURCES))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, csrc, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -156,8 +156,8 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
 
 gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
                       int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
-                      int64_t* num_pairs, uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      int64_t* num_pairs, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   CHECK(check_size(width, height));
   REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
   REQUIRE(pair_capacity >= 0 && pair_capacity < (int64_t(1) << 31), "pair_capacity out of range");
@@ -178,20 +178,20 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   if (M > pair_capacity)
     return fail(GS_ERR_CAPACITY, "%lld pairs > capacity %lld", (long long)M, (long long)pair_capacity);
   const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
-  e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, M, TX, TY, keys, vals, tile_ranges, workspace,
-                                pair_capacity, st);
+  e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, M, TX, TY, keys, vals, tile_ranges, tile_order,
+                                workspace, pair_capacity, st);
   return hip_status(e, "gs_bin_sort");
 }
 
 gs_status gs_render_fwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
-                        int64_t num_pairs, int32_t width, int32_t height, float* image, float* T_final,
-                        uint32_t* last, uint32_t* tile_processed, void* stream) {
+                        const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height, float* image,
+                        float* T_final, uint32_t* last, uint32_t* tile_processed, void* stream) {
   CHECK(check_size(width, height));
   REQUIRE(n >= 0 && num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "n / num_pairs out of range");
   REQUIRE(tile_ranges && image && T_final && last, "NULL output or tile_ranges");
   if (num_pairs > 0) REQUIRE(proj && vals && aligned(proj, 16), "NULL or misaligned proj / vals");
-  return hip_status(gs::launch_render_fwd(proj, vals, tile_ranges, num_pairs, width, height, image, T_final, last,
-                                          tile_processed, static_cast<hipStream_t>(stream)),
+  return hip_status(gs::launch_render_fwd(proj, vals, tile_ranges, tile_order, num_pairs, width, height, image,
+                                          T_final, last, tile_processed, static_cast<hipStream_t>(stream)),
                     "gs_render_fwd");
 }
 
@@ -210,8 +210,9 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
 }
 
 gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
-                        int64_t num_pairs, int32_t width, int32_t height, const float* T_final,
-                        const uint32_t* last, const float* dL_dimage, float* grad2d, void* stream) {
+                        const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
+                        const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
+                        void* stream) {
   CHECK(check_size(width, height));
   REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
   REQUIRE(num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "num_pairs out of range");
@@ -220,8 +221,8 @@ gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const
     REQUIRE(proj && vals && grad2d, "NULL array");
     REQUIRE(aligned(proj, 16) && aligned(grad2d, 16), "proj / grad2d not 16-byte aligned");
   }
-  return hip_status(gs::launch_render_bwd(proj, vals, tile_ranges, num_pairs, width, height, T_final, last,
-                                          dL_dimage, grad2d, static_cast<hipStream_t>(stream)),
+  return hip_status(gs::launch_render_bwd(proj, vals, tile_ranges, tile_order, num_pairs, width, height, T_final,
+                                          last, dL_dimage, grad2d, static_cast<hipStream_t>(stream)),
                     "gs_render_bwd");
 }
 

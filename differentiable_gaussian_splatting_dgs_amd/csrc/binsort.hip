@@ -257,6 +257,64 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t* __restrict__ key
   if (i == M - 1 || uint32_t(keys[i + 1] >> 32) != t) ranges[2 * size_t(t) + 1] = uint32_t(i + 1);
 }
 
+// Launch order of the tiles for the rasterisers: stable counting sort of
+// the tiles by descending bucket of their pair count (bucket = bit length
+// of the count), so the longest lists start first and short ones fill the
+// gaps.  One workgroup; deterministic (wave ballot ranking, no atomics
+// whose order matters).
+__global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ ranges, int nT,
+                                                     uint32_t* __restrict__ order) {
+  constexpr int kB = 33;                     // buckets: bit length 0..32
+  __shared__ uint32_t s_cnt[kB];
+  __shared__ uint32_t s_base[kB];
+  __shared__ uint32_t s_w[16][kB];           // per-wave counts of the current round
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  if (t < kB) s_cnt[t] = 0;
+  __syncthreads();
+  auto bucket_of = [&](int tile) -> uint32_t {       // 0 = longest lists
+    const uint32_t len = ranges[2 * tile + 1] - ranges[2 * tile];
+    const uint32_t bits = len != 0 ? 32u - uint32_t(__builtin_clz(len)) : 0u;
+    return 32u - bits;
+  };
+  for (int base = 0; base < nT; base += 1024) {
+    const int tile = base + t;
+    if (tile < nT) atomicAdd(&s_cnt[bucket_of(tile)], 1u);
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint32_t run = 0;
+    for (int b = 0; b < kB; ++b) {
+      s_base[b] = run;
+      run += s_cnt[b];
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < nT; base += 1024) {
+    const int tile = base + t;
+    const bool valid = tile < nT;
+    const uint32_t b = valid ? bucket_of(tile) : 0u;
+    const uint64_t act = ballot(valid);
+    const uint64_t peers = match_bits<6>(b, act);
+    const uint32_t below = uint32_t(count_below(peers));
+    if (t < 16 * kB) (&s_w[0][0])[t] = 0;
+    __syncthreads();
+    if (valid && below == 0) s_w[w][b] = uint32_t(__popcll(peers));
+    __syncthreads();
+    if (valid) {
+      uint32_t off = s_base[b] + below;
+      for (int k = 0; k < w; ++k) off += s_w[k][b];
+      order[off] = uint32_t(tile);
+    }
+    __syncthreads();
+    if (t < kB) {
+      uint32_t add = 0;
+      for (int k = 0; k < 16; ++k) add += s_w[k][t];
+      s_base[t] += add;
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // workspace layout
 // ---------------------------------------------------------------------------
@@ -344,14 +402,17 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
 
 hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx,
                                  const int64_t* vis_count, int64_t M, int32_t tiles_x, int32_t tiles_y,
-                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, void* ws,
-                                 int64_t pair_capacity, hipStream_t st) {
+                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, uint32_t* tile_order,
+                                 void* ws, int64_t pair_capacity, hipStream_t st) {
   (void)vis_idx;
   Ws w = carve(ws, n, pair_capacity);
   const float4* P = reinterpret_cast<const float4*>(proj);
   const int64_t T = int64_t(tiles_x) * tiles_y;
   k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
-  if (M == 0) return hipGetLastError();
+  if (M == 0) {
+    if (tile_order != nullptr) k_tile_order<<<1, 1024, 0, st>>>(ranges, int(T), tile_order);
+    return hipGetLastError();
+  }
   // number of 8-bit passes over the tile bits
   int tbits = 0;
   while ((int64_t(1) << tbits) < T) ++tbits;
@@ -368,6 +429,7 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     cur ^= 1;
   }
   k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
+  if (tile_order != nullptr) k_tile_order<<<1, 1024, 0, st>>>(ranges, int(T), tile_order);
   return hipGetLastError();
 }
 

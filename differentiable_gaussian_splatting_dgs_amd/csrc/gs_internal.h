@@ -48,16 +48,17 @@ int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity);
 // tile ranges.
 hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx,
                                  const int64_t* vis_count, int64_t M, int32_t tiles_x, int32_t tiles_y,
-                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, void* ws,
-                                 int64_t pair_capacity, hipStream_t st);
+                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, uint32_t* tile_order,
+                                 void* ws, int64_t pair_capacity, hipStream_t st);
 
 // --- rasteriser (raster_fwd.hip / raster_bwd.hip) ---------------------------
 hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
-                             int64_t num_pairs, int32_t width, int32_t height, float* image,
-                             float* T_final, uint32_t* last, uint32_t* tile_processed, hipStream_t st);
-hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges, int64_t num_pairs,
-                             int32_t width, int32_t height, const float* T_final, const uint32_t* last,
-                             const float* dL_dimage, float* grad2d, hipStream_t st);
+                             const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
+                             float* image, float* T_final, uint32_t* last, uint32_t* tile_processed, hipStream_t st);
+hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
+                             const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
+                             const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
+                             hipStream_t st);
 hipError_t launch_project_bwd(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
                               const int32_t* vis_idx, const int64_t* vis_count, float* grad2d, float* grads,
                               hipStream_t st);

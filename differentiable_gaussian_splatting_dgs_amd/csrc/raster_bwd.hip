@@ -1,8 +1,9 @@
 // Backward pass of one view (the "back-propagation" step of the Grendel-GS
 // notes' training pipeline), in two kernels, one per entry point:
 //
-//  k_render_bwd  -- per 16x16 tile, reverse traversal of the tile's list from
-//    the last Gaussian any pixel composited.  Each pixel rebuilds its
+//  k_render_bwd  -- the forward's layout (waves owning 8x8 quarters of a
+//    tile), reverse traversal of the tile's list from the last Gaussian
+//    any pixel composited.  Each pixel rebuilds its
 //    transmittance by division, T_i = T_{i+1} / (1 - alpha_i), carries the
 //    suffix colour S (S_{i-1} = alpha_i c_i + (1 - alpha_i) S_i, S = 0 behind
 //    the last one: black background), and forms
@@ -10,10 +11,9 @@
 //    then chains alpha = o e^power (unless clamped at 0.99) into the opacity,
 //    the conic and the 2D mean.  Skip decisions are recomputed with the same
 //    fp32 arithmetic as the forward, so exactly the composited set is
-//    visited.  The nine per-pixel partials of a Gaussian are summed over the
-//    wave with DPP row operations, over the four waves with LDS float
-//    atomics, and leave the workgroup as nine global float atomics per
-//    (Gaussian, tile).
+//    visited.  The nine partials of a Gaussian are summed over a lane's
+//    pixels in registers, then over the wave with DPP row operations, and
+//    leave as nine global float atomics per (Gaussian, wave).
 //
 //  k_project_bwd -- one thread per visible Gaussian: the chain rule of the
 //    projection from the screen-space gradients to all 59 parameters
@@ -21,145 +21,142 @@
 //    rotation via the normalised quaternion, mean via the pinhole map),
 //    accumulated (+=) into the [59][ld] gradient planes; the consumed
 //    screen-space rows are zeroed so the buffer is clean for the next view.
-#include "gs_device.hpp"
+#include "raster_common.hpp"
 
 namespace gs {
 namespace {
 
 constexpr int kG2 = 12;   // floats per Gaussian in the screen-gradient buffer
 
-__global__ __launch_bounds__(kBlock) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
-                                                       const uint32_t* __restrict__ ranges, int64_t num_pairs,
-                                                       int W, int H, int TX, const float* __restrict__ T_final,
-                                                       const uint32_t* __restrict__ last,
-                                                       const float* __restrict__ dL_dimage, float* __restrict__ grad2d) {
-  __shared__ float4 s_q0[kBlock];   // u, v, -A/2, -B
-  __shared__ float4 s_q1[kBlock];   // -C/2, opacity, r, g
-  __shared__ float4 s_box[kBlock];
-  __shared__ float s_b[kBlock];
-  __shared__ int32_t s_gid[kBlock];
-  __shared__ float s_acc[kBlock][9];
-  __shared__ uint32_t s_max;
-  const int tile = blockIdx.x;
+__global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
+                                                   const uint32_t* __restrict__ ranges,
+                                                   const uint32_t* __restrict__ order, int64_t num_pairs, int W,
+                                                   int H, int TX, int nT, const float* __restrict__ T_final,
+                                                   const uint32_t* __restrict__ last,
+                                                   const float* __restrict__ dL_dimage, float* __restrict__ grad2d) {
+  __shared__ float4 s_a[kChunk];
+  __shared__ float4 s_c[kChunk];
+  __shared__ float s_b[kChunk];
+  __shared__ int32_t s_g[kChunk];
+  int q0;
+  const int tile = order_tile(order, nT, q0);
+  if (tile < 0) return;
+  const int lane = threadIdx.x;
   const int tx = tile % TX, ty = tile / TX;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  const int bx = tx * kTile + (w & 1) * 8, by = ty * kTile + (w >> 1) * 8;
-  const int px = bx + (lane & 7), py = by + (lane >> 3);
-  const bool inside = px < W && py < H;
-  const float bx0 = float(bx) + 0.5f, bx1 = bx0 + 7.0f;
-  const float by0 = float(by) + 0.5f, by1 = by0 + 7.0f;
+  const int x0 = tx * kTile, y0 = ty * kTile;
+  const float bx0 = float(x0) + 0.5f, by0 = float(y0) + 0.5f;
   uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
   if (end > uint64_t(num_pairs)) end = uint32_t(num_pairs);
   if (start > end) start = end;
-  const float pxc = float(px) + 0.5f, pyc = float(py) + 0.5f;
-  float T = 1.0f, G0 = 0.0f, G1 = 0.0f, G2 = 0.0f;
-  uint32_t lastp = 0;
-  if (inside) {
+
+  const size_t P = size_t(W) * H;
+  float pxc[kQPW], pyc[kQPW], T[kQPW], G0[kQPW], G1[kQPW], G2[kQPW], S0[kQPW], S1[kQPW], S2[kQPW];
+  uint32_t lastp[kQPW], qmax[kQPW];
+  int qi[kQPW];
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int i = 0; i < kQPW; ++i) {
+    qi[i] = q0 + i;
+    const int px = x0 + (qi[i] & 1) * 8 + (lane & 7), py = y0 + (qi[i] >> 1) * 8 + (lane >> 3);
+    pxc[i] = float(px) + 0.5f;
+    pyc[i] = float(py) + 0.5f;
+    const bool inside = px < W && py < H;
     const size_t pix = size_t(py) * W + px;
-    const size_t P = size_t(W) * H;
-    T = T_final[pix];
-    lastp = last[pix];
-    G0 = dL_dimage[pix];
-    G1 = dL_dimage[P + pix];
-    G2 = dL_dimage[2 * P + pix];
+    T[i] = inside ? T_final[pix] : 1.0f;
+    lastp[i] = inside ? last[pix] : 0u;
+    G0[i] = inside ? dL_dimage[pix] : 0.0f;
+    G1[i] = inside ? dL_dimage[P + pix] : 0.0f;
+    G2[i] = inside ? dL_dimage[2 * P + pix] : 0.0f;
+    S0[i] = S1[i] = S2[i] = 0.0f;
+    qmax[i] = wave_max_u32(lastp[i]);     // entries a pixel of the quarter composited
+    lmax = qmax[i] > lmax ? qmax[i] : lmax;
   }
-  if (t == 0) s_max = 0;
-  __syncthreads();
-  if (lastp > 0) atomicMax(&s_max, lastp);
-  __syncthreads();
-  const uint32_t stop = start + min(s_max, end - start);
-  float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
-  for (uint32_t bend = stop; bend > start;) {
-    const uint32_t bbeg = (bend - start > uint32_t(kBlock)) ? bend - kBlock : start;
-    const int cnt = int(bend - bbeg);
-    __syncthreads();
-    if (t < cnt) {
-      const int64_t g = vals[bbeg + t];
-      const float4 q0 = proj[4 * g], q1 = proj[4 * g + 1], q2 = proj[4 * g + 2];
-      s_q0[t] = make_float4(q0.x, q0.y, -0.5f * q0.z, -q0.w);
-      s_q1[t] = make_float4(-0.5f * q1.x, q1.y, q1.z, q1.w);
-      s_b[t] = q2.x;
-      s_box[t] = make_float4(q0.x - q2.y, q0.x + q2.y, q0.y - q2.z, q0.y + q2.z);
-      s_gid[t] = int32_t(g);
-    }
+  if (lmax > end - start) lmax = end - start;
+  if (lmax == 0) return;
+
+  // chunks from the last composited entry down to the first
+  for (int64_t cs = int64_t(start) + int64_t((lmax - 1) / kChunk) * kChunk; cs >= int64_t(start); cs -= kChunk) {
+    const uint32_t j = uint32_t(cs) + uint32_t(lane);
+    const uint32_t pos = j - start;
+    const uint32_t mq = stage_entry(proj, vals, j, pos < lmax, bx0, by0, s_a, s_c, s_b, s_g, lane);
+    uint64_t m[kQPW];
+    uint64_t active = 0;
 #pragma unroll
-    for (int c = 0; c < 9; ++c) s_acc[t][c] = 0.0f;
-    __syncthreads();
-    for (int k = cnt - 1; k >= 0; --k) {
-      const uint32_t pos = bbeg + uint32_t(k) - start;    // list position
-      const bool mine = pos < lastp;
-      if (!__any(mine)) continue;
-      const float4 box = s_box[k];
-      if (box.y < bx0 || box.x > bx1 || box.w < by0 || box.z > by1) continue;
-      const float4 a = s_q0[k];
-      const float4 c = s_q1[k];
-      const float dx = pxc - a.x, dy = pyc - a.y;
-      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
-      float e = 0.0f, araw = 0.0f, alpha = 0.0f;
-      bool contrib = mine && !(power > 0.0f || power < -5.6f);
-      if (contrib) {
-        e = pexp(power);
-        araw = c.y * e;
-        alpha = fminf(0.99f, araw);
-        contrib = !(alpha < 1.0f / 255.0f);
-      }
-      float gu = 0.f, gv = 0.f, gA = 0.f, gB = 0.f, gC = 0.f, go = 0.f, gr = 0.f, gg = 0.f, gb = 0.f;
-      if (contrib) {
-        const float cb = s_b[k];
-        const float Ti = T / (1.0f - alpha);
+    for (int i = 0; i < kQPW; ++i) {
+      m[i] = uint64_t(__ballot(((mq >> qi[i]) & 1u) && pos < qmax[i]));
+      active |= m[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    while (active != 0) {
+      const int k = 63 - __builtin_clzll(active);      // back to front
+      active &= ~(1ull << k);
+      const float4 a = s_a[k];
+      const float4 c = s_c[k];
+      const float cb = s_b[k];
+      const uint32_t kpos = uint32_t(cs) + uint32_t(k) - start;
+      float au = 0.f, av = 0.f, aA = 0.f, aB = 0.f, aC = 0.f, ao = 0.f, ar = 0.f, ag = 0.f, abl = 0.f;
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < kQPW; ++i) {
+        if (!((m[i] >> k) & 1ull)) continue;
+        const float dx = pxc[i] - a.x, dy = pyc[i] - a.y;
+        const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
+        bool ok = kpos < lastp[i] && !(power > 0.0f) && !(power < -5.6f);
+        if (!__any(ok)) continue;
+        const float e = pexp_core(power);
+        const float araw = c.y * e;
+        const float alpha = fminf(0.99f, araw);
+        ok = ok && !(alpha < 1.0f / 255.0f);
+        // same decisions as the forward: `ok` = this pixel composited it
+        const float om = 1.0f - alpha;
+        const float Ti = T[i] * __builtin_amdgcn_rcpf(om);
         const float wgt = alpha * Ti;
-        gr = wgt * G0;
-        gg = wgt * G1;
-        gb = wgt * G2;
-        const float dal = Ti * fmaf(cb - S2, G2, fmaf(c.w - S1, G1, (c.z - S0) * G0));
-        S0 = fmaf(alpha, c.z, (1.0f - alpha) * S0);
-        S1 = fmaf(alpha, c.w, (1.0f - alpha) * S1);
-        S2 = fmaf(alpha, cb, (1.0f - alpha) * S2);
-        T = Ti;
-        if (!(araw > 0.99f)) {
-          go = dal * e;
-          const float dp = dal * alpha;
-          const float A = -2.0f * a.z, B = -a.w, C = -2.0f * c.x;
-          gA = dp * (-0.5f * dx * dx);
-          gB = dp * (-dx * dy);
-          gC = dp * (-0.5f * dy * dy);
-          gu = dp * fmaf(A, dx, B * dy);
-          gv = dp * fmaf(B, dx, C * dy);
-        }
+        const float gG0 = ok ? G0[i] : 0.0f, gG1 = ok ? G1[i] : 0.0f, gG2 = ok ? G2[i] : 0.0f;
+        ar = fmaf(wgt, gG0, ar);
+        ag = fmaf(wgt, gG1, ag);
+        abl = fmaf(wgt, gG2, abl);
+        const float dal = Ti * fmaf(cb - S2[i], gG2, fmaf(c.w - S1[i], gG1, (c.z - S0[i]) * gG0));
+        S0[i] = ok ? fmaf(alpha, c.z, om * S0[i]) : S0[i];
+        S1[i] = ok ? fmaf(alpha, c.w, om * S1[i]) : S1[i];
+        S2[i] = ok ? fmaf(alpha, cb, om * S2[i]) : S2[i];
+        T[i] = ok ? Ti : T[i];
+        const float dl = (araw > 0.99f) ? 0.0f : dal;     // the 0.99 clamp passes no gradient
+        ao = fmaf(dl, e, ao);
+        const float dp = dl * alpha;
+        const float A = -2.0f * a.z, B = -a.w, C = -2.0f * c.x;
+        aA = fmaf(dp, -0.5f * dx * dx, aA);
+        aB = fmaf(dp, -dx * dy, aB);
+        aC = fmaf(dp, -0.5f * dy * dy, aC);
+        au = fmaf(dp, fmaf(A, dx, B * dy), au);
+        av = fmaf(dp, fmaf(B, dx, C * dy), av);
+        any = true;
       }
-      if (__any(contrib)) {
-        gu = wave_sum_to_lane63(gu);
-        gv = wave_sum_to_lane63(gv);
-        gA = wave_sum_to_lane63(gA);
-        gB = wave_sum_to_lane63(gB);
-        gC = wave_sum_to_lane63(gC);
-        go = wave_sum_to_lane63(go);
-        gr = wave_sum_to_lane63(gr);
-        gg = wave_sum_to_lane63(gg);
-        gb = wave_sum_to_lane63(gb);
-        if (lane == 63) {
-          atomicAdd(&s_acc[k][0], gu);
-          atomicAdd(&s_acc[k][1], gv);
-          atomicAdd(&s_acc[k][2], gA);
-          atomicAdd(&s_acc[k][3], gB);
-          atomicAdd(&s_acc[k][4], gC);
-          atomicAdd(&s_acc[k][5], go);
-          atomicAdd(&s_acc[k][6], gr);
-          atomicAdd(&s_acc[k][7], gg);
-          atomicAdd(&s_acc[k][8], gb);
-        }
-      }
-    }
-    __syncthreads();
-    if (t < cnt) {
-      float* dst = grad2d + size_t(s_gid[t]) * kG2;
-#pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        const float v = s_acc[t][c];
-        if (v != 0.0f) unsafeAtomicAdd(dst + c, v);
+      if (!any) continue;
+      au = wave_sum_to_lane63(au);
+      av = wave_sum_to_lane63(av);
+      aA = wave_sum_to_lane63(aA);
+      aB = wave_sum_to_lane63(aB);
+      aC = wave_sum_to_lane63(aC);
+      ao = wave_sum_to_lane63(ao);
+      ar = wave_sum_to_lane63(ar);
+      ag = wave_sum_to_lane63(ag);
+      abl = wave_sum_to_lane63(abl);
+      if (lane == 63) {
+        float* dst = grad2d + size_t(s_g[k]) * kG2;
+        if (au != 0.0f) unsafeAtomicAdd(dst + 0, au);
+        if (av != 0.0f) unsafeAtomicAdd(dst + 1, av);
+        if (aA != 0.0f) unsafeAtomicAdd(dst + 2, aA);
+        if (aB != 0.0f) unsafeAtomicAdd(dst + 3, aB);
+        if (aC != 0.0f) unsafeAtomicAdd(dst + 4, aC);
+        if (ao != 0.0f) unsafeAtomicAdd(dst + 5, ao);
+        if (ar != 0.0f) unsafeAtomicAdd(dst + 6, ar);
+        if (ag != 0.0f) unsafeAtomicAdd(dst + 7, ag);
+        if (abl != 0.0f) unsafeAtomicAdd(dst + 8, abl);
       }
     }
-    bend = bbeg;
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -309,12 +306,14 @@ __global__ __launch_bounds__(256) void k_project_bwd(const float* __restrict__ p
 
 }  // namespace
 
-hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges, int64_t num_pairs,
-                             int32_t width, int32_t height, const float* T_final, const uint32_t* last,
-                             const float* dL_dimage, float* grad2d, hipStream_t st) {
+hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
+                             const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
+                             const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
+                             hipStream_t st) {
   const int TX = (width + kTile - 1) / kTile, TY = (height + kTile - 1) / kTile;
-  k_render_bwd<<<unsigned(TX * TY), kBlock, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, num_pairs,
-                                                     width, height, TX, T_final, last, dL_dimage, grad2d);
+  const int nT = TX * TY;
+  k_render_bwd<<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
+                                              num_pairs, width, height, TX, nT, T_final, last, dL_dimage, grad2d);
   return hipGetLastError();
 }
 

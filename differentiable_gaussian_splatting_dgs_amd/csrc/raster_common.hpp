@@ -1,0 +1,100 @@
+// Pieces shared by the forward and backward rasterisers.
+//
+// Work layout: kWPT waves (64 lanes each) per 16x16 tile, each owning kQPW
+// of the tile's four 8x8 quarters (quarter q covers x + 8 (q & 1),
+// y + 8 (q >> 1)); lane l owns the pixel at offset (l & 7, l >> 3) of each
+// of its wave's quarters.  The tile's
+// depth-sorted list is consumed in chunks of 64 entries: lane l stages entry
+// l's record in LDS and tests the Gaussian's alpha >= 1/255 footprint box
+// against the quarters; one ballot per quarter gives the 64-bit set of chunk
+// entries that can reach it.  The loop then visits only set bits
+// (scalar bit scans), and evaluates only the quarters whose bit is set
+// (wave-uniform branches), so Gaussians that cannot reach a quarter cost no
+// vector work there.
+#pragma once
+
+#include "gs_device.hpp"
+
+namespace gs {
+
+constexpr int kChunk = 64;
+
+// Waves per tile and quarters per wave: each wave owns QPW of the tile's
+// four 8x8 quarters (one pixel of each per lane).  More waves per tile
+// shorten the sequential chain the heaviest tiles put on one wave.
+constexpr int kQPW = 1;
+constexpr int kWPT = 4 / kQPW;
+
+// Workgroup -> (tile, first quarter).  Tiles are taken in `order` (longest
+// lists first) when given, so the heavy ones start early and light ones
+// fill the gaps.  Returns -1 for workgroups past the end.
+__device__ __forceinline__ int order_tile(const uint32_t* __restrict__ order, int nT, int& q0) {
+  const int rank = int(blockIdx.x) / kWPT;
+  q0 = (int(blockIdx.x) % kWPT) * kQPW;
+  if (rank >= nT) return -1;
+  return order != nullptr ? int(order[rank]) : rank;
+}
+
+inline unsigned raster_grid(int nT) { return unsigned(nT * kWPT); }
+
+// e^x for x in [-5.6, 0]: the written exponential without its range
+// checks (which never trigger there), so the same bits as pexp.
+__device__ __forceinline__ float pexp_core(float x) {
+  const float kf = rintf(x * 1.44269504088896341f);
+  float r = fmaf(-kf, 0.693145751953125f, x);
+  r = fmaf(-kf, 1.428606820309417232e-6f, r);
+  float p = 1.0f / 5040.0f;
+  p = fmaf(p, r, 1.0f / 720.0f);
+  p = fmaf(p, r, 1.0f / 120.0f);
+  p = fmaf(p, r, 1.0f / 24.0f);
+  p = fmaf(p, r, 1.0f / 6.0f);
+  p = fmaf(p, r, 0.5f);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, static_cast<int>(kf));
+}
+
+// A Gaussian as the rasterisers read it from LDS: (u, v, -A/2, -B),
+// (-C/2, opacity, r, g), b.
+struct RasterRec {
+  float4 a;
+  float4 c;
+  float b;
+};
+
+// Stage entry `j` (if valid) of the list into LDS slot `lane` and return its
+// 4-bit quarter-overlap mask.  bx0/by0: pixel-centre coordinate of the
+// tile's first pixel.
+__device__ __forceinline__ uint32_t stage_entry(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
+                                                uint32_t j, bool valid, float bx0, float by0, float4* s_a,
+                                                float4* s_c, float* s_b, int32_t* s_g, int lane) {
+  uint32_t m = 0;
+  if (valid) {
+    const int64_t g = vals[j];
+    const float4 q0 = proj[4 * g], q1 = proj[4 * g + 1], q2 = proj[4 * g + 2];
+    s_a[lane] = make_float4(q0.x, q0.y, -0.5f * q0.z, -q0.w);
+    s_c[lane] = make_float4(-0.5f * q1.x, q1.y, q1.z, q1.w);
+    s_b[lane] = q2.x;
+    if (s_g != nullptr) s_g[lane] = int32_t(g);
+    // footprint box [u - ex, u + ex] x [v - ey, v + ey] against the quarters'
+    // pixel-centre ranges [b0 + 8k, b0 + 8k + 7]
+    const float lx = q0.x - q2.y, hx = q0.x + q2.y, ly = q0.y - q2.z, hy = q0.y + q2.z;
+    const bool x0 = hx >= bx0 && lx <= bx0 + 7.0f;
+    const bool x1 = hx >= bx0 + 8.0f && lx <= bx0 + 15.0f;
+    const bool y0 = hy >= by0 && ly <= by0 + 7.0f;
+    const bool y1 = hy >= by0 + 8.0f && ly <= by0 + 15.0f;
+    m = uint32_t(x0 && y0) | (uint32_t(x1 && y0) << 1) | (uint32_t(x0 && y1) << 2) | (uint32_t(x1 && y1) << 3);
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    const uint32_t o = uint32_t(__shfl_xor(int(v), d, 64));
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace gs

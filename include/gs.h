@@ -139,14 +139,18 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
  *   num_pairs    host out: M, the number of pairs
  *   tile_ranges  device out, [TX*TY][2] uint32: [start, end) of each tile's
  *                pairs, [0, 0) for empty tiles
+ *   tile_order   device out or NULL, [TX*TY] uint32: a launch order of the
+ *                tiles for the rasterisers -- tiles by descending bit length
+ *                of their pair count, ties in tile order (a schedule only:
+ *                results do not depend on it)
  *   workspace    device, >= gs_workspace_size(GS_OP_BIN_SORT, n, .., pair_capacity)
  * Blocks the calling thread once, to read M.  If M > pair_capacity the call
  * writes *num_pairs = M, returns GS_ERR_CAPACITY and writes neither pairs
  * nor ranges.  pair_capacity must be < 2^31. */
 gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
                       int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
-                      int64_t* num_pairs, uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      int64_t* num_pairs, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Front-to-back alpha compositing per 16x16 tile (Grendel-GS notes,
  * training pipeline: "alpha compositing").  Per pixel, over its tile's
@@ -155,6 +159,7 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
  * Gaussian that would bring the transmittance T (1 - alpha) below 1e-4;
  * C += colour alpha T; T *= 1 - alpha.  Black background.
  *   proj, vals, tile_ranges, num_pairs   device/host, from gs_preprocess and gs_bin_sort
+ *   tile_order   device or NULL: gs_bin_sort's launch order (NULL = tile order)
  *   image        device out, [3][H][W]
  *   T_final      device out, [H][W] final transmittance
  *   last         device out, [H][W] uint32: 1 + list position (within the
@@ -163,8 +168,8 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
  *                largest number of list entries any of its pixels read
  *                (up to and including the stopping one) */
 gs_status gs_render_fwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
-                        int64_t num_pairs, int32_t width, int32_t height, float* image, float* T_final,
-                        uint32_t* last, uint32_t* tile_processed, void* stream);
+                        const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height, float* image,
+                        float* T_final, uint32_t* last, uint32_t* tile_processed, void* stream);
 
 /* Loss of a rendered image against a target (Grendel-GS notes, training
  * pipeline: "L1 + SSIM loss"):
@@ -185,6 +190,7 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
  * behind carried along; the partials of every (pixel, Gaussian) are summed
  * per Gaussian into its screen-space gradient.
  *   proj, vals, tile_ranges, num_pairs, T_final, last   from the forward
+ *   tile_order   device or NULL: gs_bin_sort's launch order (NULL = tile order)
  *   dL_dimage    device, [3][H][W]
  *   grad2d       device in/out, [n][GS_GRAD2D_WORDS] fp32, 16-byte aligned:
  *                dL/d(u, v, A, B, C, opacity, r, g, b) of the view are ADDED
@@ -195,8 +201,9 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
  * The discrete decisions (skip, stop, 0.99 clamp) are held at the
  * forward's; the 2D mean gradient is in pixels; depth gets none. */
 gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
-                        int64_t num_pairs, int32_t width, int32_t height, const float* T_final,
-                        const uint32_t* last, const float* dL_dimage, float* grad2d, void* stream);
+                        const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
+                        const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
+                        void* stream);
 
 /* Projection backward of one view: the chain rule from the screen-space
  * gradients to all 59 parameters (SH coefficients and view direction, EWA

@@ -36,6 +36,7 @@ def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:
             keys=step.keys[:M].cpu().numpy().view(np.uint64).copy(),
             vals=step.vals[:M].cpu().numpy().copy(),
             ranges=vw.ranges.cpu().numpy().view(np.uint32).copy(),
+            order=vw.order.cpu().numpy().view(np.uint32).copy(),
             image=vw.image.cpu().numpy().copy(),
             T_final=vw.T_final.cpu().numpy().copy(),
             last=vw.last.cpu().numpy().view(np.uint32).copy(),
@@ -118,6 +119,12 @@ def check_forward(gv, ov_pre, okeys, ovals, oranges, oimg, oT, olast, oproc, tag
     assert np.array_equal(gv["keys"], okeys), f"{tag} keys"
     assert np.array_equal(gv["vals"], ovals), f"{tag} values"
     assert np.array_equal(gv["ranges"], oranges), f"{tag} tile ranges"
+    if "order" in gv:
+        # launch order: tiles stably sorted by descending bit length of the pair count
+        n_pairs = (oranges[:, 1] - oranges[:, 0]).astype(np.int64)
+        bits = np.where(n_pairs > 0, np.floor(np.log2(np.maximum(n_pairs, 1))).astype(np.int64) + 1, 0)
+        expect = np.argsort(-bits, kind="stable").astype(np.uint32)
+        assert np.array_equal(gv["order"], expect), f"{tag} tile order"
     d_img = float(np.max(np.abs(gv["image"] - oimg))) if oimg.size else 0.0
     n_img = int((gv["image"].view(np.uint32) != oimg.view(np.uint32)).sum())
     say(f"  {tag} image max|diff|={d_img:.3g} not bit-identical {n_img}/{oimg.size}")

@@ -78,9 +78,9 @@ def test_invalid_arguments_rejected_on_host():
     # bin sort: capacity beyond int32 range, negative n
     m = C.c_int64(0)
     assert lib.gs_bin_sort(P(16), 1, P(16), P(16), 8, 8, P(16), P(16), C.c_int64(1 << 31), C.byref(m), P(16),
-                           P(256), 1 << 30, None) == 1
-    assert lib.gs_bin_sort(P(16), -1, P(16), P(16), 8, 8, P(16), P(16), 10, C.byref(m), P(16), P(256), 1 << 30,
-                           None) == 1
+                           None, P(256), 1 << 30, None) == 1
+    assert lib.gs_bin_sort(P(16), -1, P(16), P(16), 8, 8, P(16), P(16), 10, C.byref(m), P(16), None, P(256),
+                           1 << 30, None) == 1
     # adam: zero bias correction
     assert lib.gs_sparse_adam(P(16), P(16), P(16), P(16), 4, 4, P(16), P(16), P(16), C.c_float(1e-3),
                               C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.0), C.c_float(0.1),
