@@ -12,8 +12,10 @@
 //    the conic and the 2D mean.  Skip decisions are recomputed with the same
 //    fp32 arithmetic as the forward, so exactly the composited set is
 //    visited.  The nine partials of a Gaussian are summed over a lane's
-//    pixels in registers, then over the wave with DPP row operations, and
-//    leave as nine global float atomics per (Gaussian, wave).
+//    pixels in registers, then over the wave by two lane-half swaps that fold
+//    several values at once (permlane32/16 swap) and four DPP row steps, and
+//    leave as nine global float atomics per (Gaussian, wave), issued from
+//    four lanes.
 //
 //  k_project_bwd -- one thread per visible Gaussian: the chain rule of the
 //    projection from the screen-space gradients to all 59 parameters
@@ -27,6 +29,42 @@ namespace gs {
 namespace {
 
 constexpr int kG2 = 12;   // floats per Gaussian in the screen-gradient buffer
+
+__device__ __forceinline__ float f_of(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t u_of(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Lanes l and l ^ 32 summed: lanes 0-31 carry x's sums, lanes 32-63 y's.
+__device__ __forceinline__ float fold32(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane32_swap(u_of(x), u_of(y), false, false);
+  return f_of(s[0]) + f_of(s[1]);
+}
+
+// Within each half, rows (16 lanes) 0 and 1 summed: of x = [a | b] and
+// y = [c | d] (halves), rows 0..3 of the result carry a, c, b, d.
+__device__ __forceinline__ float fold16(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(u_of(x), u_of(y), false, false);
+  return f_of(s[0]) + f_of(s[1]);
+}
+
+// Sum over the 16 lanes of each row; every lane ends with its row's total.
+__device__ __forceinline__ float row_sum(float v) {
+  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
+// Sums of nine per-lane values over the wave, folded so each fold serves
+// several values: q0 rows 0..3 end with the totals of v0, v2, v1, v3; q1
+// rows with v4, v6, v5, v7; q2 row 0 with v8.
+__device__ __forceinline__ void wave_sum9(const float v[9], float& q0, float& q1, float& q2) {
+  const float r0 = fold32(v[0], v[1]), r1 = fold32(v[2], v[3]), r2 = fold32(v[4], v[5]);
+  const float r3 = fold32(v[6], v[7]), r4 = fold32(v[8], 0.0f);
+  q0 = row_sum(fold16(r0, r1));
+  q1 = row_sum(fold16(r2, r3));
+  q2 = row_sum(fold16(r4, 0.0f));
+}
 
 __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                                    const uint32_t* __restrict__ ranges,
@@ -134,26 +172,17 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
         any = true;
       }
       if (!any) continue;
-      au = wave_sum_to_lane63(au);
-      av = wave_sum_to_lane63(av);
-      aA = wave_sum_to_lane63(aA);
-      aB = wave_sum_to_lane63(aB);
-      aC = wave_sum_to_lane63(aC);
-      ao = wave_sum_to_lane63(ao);
-      ar = wave_sum_to_lane63(ar);
-      ag = wave_sum_to_lane63(ag);
-      abl = wave_sum_to_lane63(abl);
-      if (lane == 63) {
+      const float v9[9] = {au, av, aA, aB, aC, ao, ar, ag, abl};
+      float q0s, q1s, q2s;
+      wave_sum9(v9, q0s, q1s, q2s);
+      if ((lane & 15) == 0) {
+        // row r of q0 / q1 holds component (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
+        const int row = lane >> 4;
+        const int c0 = ((row & 1) << 1) | (row >> 1);
         float* dst = grad2d + size_t(s_g[k]) * kG2;
-        if (au != 0.0f) unsafeAtomicAdd(dst + 0, au);
-        if (av != 0.0f) unsafeAtomicAdd(dst + 1, av);
-        if (aA != 0.0f) unsafeAtomicAdd(dst + 2, aA);
-        if (aB != 0.0f) unsafeAtomicAdd(dst + 3, aB);
-        if (aC != 0.0f) unsafeAtomicAdd(dst + 4, aC);
-        if (ao != 0.0f) unsafeAtomicAdd(dst + 5, ao);
-        if (ar != 0.0f) unsafeAtomicAdd(dst + 6, ar);
-        if (ag != 0.0f) unsafeAtomicAdd(dst + 7, ag);
-        if (abl != 0.0f) unsafeAtomicAdd(dst + 8, abl);
+        if (q0s != 0.0f) unsafeAtomicAdd(dst + c0, q0s);
+        if (q1s != 0.0f) unsafeAtomicAdd(dst + 4 + c0, q1s);
+        if (lane == 0 && q2s != 0.0f) unsafeAtomicAdd(dst + 8, q2s);
       }
     }
     __builtin_amdgcn_wave_barrier();
