@@ -50,14 +50,21 @@ __global__ __launch_bounds__(kRT) void k_upsweep(const K* __restrict__ keys, con
   __syncthreads();
   const int64_t count = count_of(count_dev, count_host);
   const int64_t base = int64_t(blockIdx.x) * kRB + int64_t(w) * kWaveItems;
+  // all loads first, so they are in flight together
+  uint32_t dg[kRI];
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    dg[it] = idx < count ? digit_of(keys[idx], shift) : 0u;
+  }
+#pragma unroll
   for (int it = 0; it < kRI; ++it) {
     const int64_t idx = base + it * 64 + lane;
     const bool valid = idx < count;
     const uint64_t act = ballot(valid);
     if (act == 0) break;
-    const uint32_t d = valid ? digit_of(keys[idx], shift) : 0u;
-    const uint64_t peers = match_bits<8>(d, act);
-    if (valid && count_below(peers) == 0) atomicAdd(&hist[d], uint32_t(__popcll(peers)));
+    const uint64_t peers = match_bits<8>(dg[it], act);
+    if (valid && count_below(peers) == 0) atomicAdd(&hist[dg[it]], uint32_t(__popcll(peers)));
   }
   __syncthreads();
   H[size_t(t) * nb + blockIdx.x] = hist[t];
@@ -102,12 +109,18 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
   K key[kRI];
   uint32_t val[kRI], rk[kRI];
   const int64_t base = bbase + int64_t(w) * kWaveItems;
+  // all loads first, so they are in flight together
 #pragma unroll
   for (int it = 0; it < kRI; ++it) {
     const int64_t idx = base + it * 64 + lane;
     const bool valid = idx < count;
     key[it] = valid ? kin[idx] : K(0);
     val[it] = valid ? vin[idx] : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    const bool valid = idx < count;
     const uint64_t act = ballot(valid);
     const uint32_t d = digit_of(key[it], shift);
     const uint64_t peers = match_bits<8>(d, act);
@@ -175,20 +188,26 @@ __global__ __launch_bounds__(256) void k_depth_gather(const float4* __restrict__
   vals[r] = uint32_t(g);
 }
 
+// Duplication works on blocks of kDB consecutive depth ranks.
+constexpr int kDT = 256;                 // threads
+constexpr int kDI = 4;                   // Gaussians per thread
+constexpr int kDB = kDT * kDI;           // Gaussians per block
+
 // per-block sums of tiles_touched in depth order
-__global__ __launch_bounds__(kRT) void k_tilesum(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+__global__ __launch_bounds__(kDT) void k_tilesum(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
                                                  const int64_t* __restrict__ vis_count,
                                                  int64_t* __restrict__ block_sums) {
-  __shared__ int64_t sh[kRT / 64];
+  __shared__ int64_t sh[kDT / 64];
   const int64_t V = *vis_count;
-  const int64_t start = int64_t(blockIdx.x) * kRB + int64_t(threadIdx.x) * kRI;
+  const int64_t start = int64_t(blockIdx.x) * kDB + int64_t(threadIdx.x) * kDI;
   int64_t s = 0;
-  for (int k = 0; k < kRI; ++k) {
+#pragma unroll
+  for (int k = 0; k < kDI; ++k) {
     const int64_t r = start + k;
     if (r < V) s += __builtin_bit_cast(uint32_t, proj[4 * int64_t(order[r]) + 3].w);
   }
   int64_t tot;
-  block_exclusive_scan<kRT, int64_t>(s, sh, tot);
+  block_exclusive_scan<kDT, int64_t>(s, sh, tot);
   if (threadIdx.x == 0) block_sums[blockIdx.x] = tot;
 }
 
@@ -210,36 +229,68 @@ __global__ __launch_bounds__(1024) void k_scan_sums(int64_t* __restrict__ sums, 
   if (threadIdx.x == 0) *total = carry;
 }
 
-// pairs in depth order: for each visible Gaussian (depth rank r), one pair
-// per tile of its rectangle, row-major
-__global__ __launch_bounds__(kRT) void k_duplicate(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+// Pairs in depth order: for each visible Gaussian (depth rank r), one pair
+// per tile of its rectangle, row-major.  Load-balanced: the block's
+// Gaussians and their exclusive pair offsets go to LDS, then the block's
+// threads write its output range round-robin (coalesced), each locating
+// its Gaussian by binary search over the offsets.
+__global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
                                                    const int64_t* __restrict__ vis_count,
                                                    const int64_t* __restrict__ block_offsets, int32_t tiles_x,
                                                    uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
-  __shared__ int64_t sh[kRT / 64];
+  __shared__ int64_t sh[kDT / 64];
+  __shared__ uint32_t s_off[kDB];        // exclusive pair offset within the block
+  __shared__ uint32_t s_rx[kDB];         // x0 | width << 16
+  __shared__ uint32_t s_y0[kDB];
+  __shared__ uint32_t s_dep[kDB];
+  __shared__ uint32_t s_g[kDB];
   const int64_t V = *vis_count;
-  const int64_t start = int64_t(blockIdx.x) * kRB + int64_t(threadIdx.x) * kRI;
-  int64_t s = 0;
-  for (int k = 0; k < kRI; ++k) {
-    const int64_t r = start + k;
-    if (r < V) s += __builtin_bit_cast(uint32_t, proj[4 * int64_t(order[r]) + 3].w);
+  const int64_t r0 = int64_t(blockIdx.x) * kDB;
+  const int t = threadIdx.x;
+  uint32_t cnt[kDI];
+  uint32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kDI; ++k) {
+    const int64_t r = r0 + t * kDI + k;
+    cnt[k] = 0;
+    if (r < V) {
+      const uint32_t g = order[r];
+      const float4 q3 = proj[4 * int64_t(g) + 3];
+      const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
+      const uint32_t x0 = rx & 0xFFFFu, x1 = rx >> 16;
+      cnt[k] = __builtin_bit_cast(uint32_t, q3.w);
+      s_rx[t * kDI + k] = x0 | ((x1 - x0) << 16);
+      s_y0[t * kDI + k] = ry & 0xFFFFu;
+      s_dep[t * kDI + k] = __builtin_bit_cast(uint32_t, q3.x);
+      s_g[t * kDI + k] = g;
+    }
+    s += cnt[k];
   }
   int64_t tot;
-  int64_t off = block_exclusive_scan<kRT, int64_t>(s, sh, tot) + block_offsets[blockIdx.x];
-  for (int k = 0; k < kRI; ++k) {
-    const int64_t r = start + k;
-    if (r >= V) break;
-    const uint32_t g = order[r];
-    const float4 q3 = proj[4 * int64_t(g) + 3];
-    const uint64_t dbits = __builtin_bit_cast(uint32_t, q3.x);
-    const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
-    const int x0 = rx & 0xFFFF, x1 = rx >> 16, y0 = ry & 0xFFFF, y1 = ry >> 16;
-    for (int ty = y0; ty < y1; ++ty)
-      for (int tx = x0; tx < x1; ++tx) {
-        keys[off] = (uint64_t(uint32_t(ty * tiles_x + tx)) << 32) | dbits;
-        vals[off] = g;
-        ++off;
-      }
+  uint32_t off = uint32_t(block_exclusive_scan<kDT, int64_t>(int64_t(s), sh, tot));
+#pragma unroll
+  for (int k = 0; k < kDI; ++k) {
+    s_off[t * kDI + k] = off;
+    off += cnt[k];
+  }
+  __syncthreads();
+  const int64_t base = block_offsets[blockIdx.x];
+  const int nvalid = int(V - r0 < kDB ? V - r0 : kDB);
+  const uint32_t total = uint32_t(tot);
+  for (uint32_t o = uint32_t(t); o < total; o += kDT) {
+    // last i in [0, nvalid) with s_off[i] <= o (entries with no pairs have
+    // equal offsets; visible Gaussians always have at least one)
+    int lo = 0, hi = nvalid - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= o) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t local = o - s_off[lo];
+    const uint32_t rx = s_rx[lo];
+    const uint32_t w = rx >> 16;
+    const uint32_t ty = s_y0[lo] + local / w, tx = (rx & 0xFFFFu) + local % w;
+    keys[base + o] = (uint64_t(ty * uint32_t(tiles_x) + tx) << 32) | s_dep[lo];
+    vals[base + o] = s_g[lo];
   }
 }
 
@@ -342,7 +393,7 @@ Ws carve(void* ws, int64_t n, int64_t cap) {
   w.dvB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.H = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(nbh)));
   w.rowtot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
-  w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t(nblocks(n) + 1)));
+  w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t((n + kDB - 1) / kDB + 1)));
   w.m_dev = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.pk = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * size_t(cap)));
   w.pv = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(cap)));
@@ -356,7 +407,7 @@ size_t carve_bytes(int64_t n, int64_t cap) {
   b += 4 * align_up(sizeof(uint32_t) * size_t(n), 256);
   b += align_up(sizeof(uint32_t) * 256 * size_t(nbh), 256);
   b += align_up(sizeof(uint32_t) * 256, 256);
-  b += align_up(sizeof(int64_t) * size_t(nblocks(n) + 1), 256);
+  b += align_up(sizeof(int64_t) * size_t((n + kDB - 1) / kDB + 1), 256);
   b += align_up(sizeof(int64_t), 256);
   b += align_up(sizeof(uint64_t) * size_t(cap), 256);
   b += align_up(sizeof(uint32_t) * size_t(cap), 256);
@@ -394,8 +445,8 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
                            even ? w.dvB : w.dvA, vis_count, 0, n, 8 * pass, w, st);
     }
   }
-  const int nbv = int(nblocks(n));
-  if (nbv > 0) k_tilesum<<<nbv, kRT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
+  const int nbv = int((n + kDB - 1) / kDB);
+  if (nbv > 0) k_tilesum<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
   k_scan_sums<<<1, 1024, 0, st>>>(w.bsums, nbv, m_dev);
   return hipGetLastError();
 }
@@ -422,8 +473,8 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
   uint64_t* bufk[2] = {keys, w.pk};
   uint32_t* bufv[2] = {uvals, w.pv};
   int cur = (passes & 1) ? 1 : 0;
-  const int nbv = int(nblocks(n));
-  k_duplicate<<<nbv, kRT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, bufk[cur], bufv[cur]);
+  const int nbv = int((n + kDB - 1) / kDB);
+  k_duplicate<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, bufk[cur], bufv[cur]);
   for (int pass = 0; pass < passes; ++pass) {
     radix_pass<uint64_t>(bufk[cur], bufv[cur], bufk[cur ^ 1], bufv[cur ^ 1], nullptr, M, M, 32 + 8 * pass, w, st);
     cur ^= 1;
