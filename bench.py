@@ -8,8 +8,8 @@ Prints ONE JSON line.  `value` = steps/s with every input resident in HBM
 when the timed region starts.  Per-stage times come from HIP events on the
 stream the library launches on; the dominant raster kernel's roofline uses
 them (each raster entry point is a single kernel launch).  `cpu_baseline` is
-the oracle timed on the host's cores on one view of the same workload,
-scaled to a step.
+the oracle timed on the host's cores over one step of the same workload
+(bounded: see cpu_baseline).
 """
 from __future__ import annotations
 
@@ -61,30 +61,63 @@ def algorithmic_bytes(N, views, U):
     return total + 1892 * U               # sparse Adam
 
 
-def cpu_baseline(work):
-    """The oracle as it stands, on view 0 of the workload (preprocess, bin,
-    render, loss, backward) plus Adam over the union of view 0, scaled to a
-    step of len(work.cameras) views."""
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's reading), or
+    None when the summary is for another workload or the kernel's sources
+    have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][kernel]
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return float(rec["bytes_per_launch"]) if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def cpu_baseline(work, budget_s=30.0):
+    """The oracle as it stands, timed on the host's cores over one training
+    step of the same workload at its initial parameters: per view
+    preprocess, binning, render, loss and backward (gradients summed over
+    views), then Adam over the union of the visible sets.  Views are taken
+    in order until the step is complete or `budget_s` has passed; the view
+    part is then scaled by (views in the step) / (views run)."""
     import numpy as np
 
     import oracle
-    cam, tgt = work.cameras[0], work.targets[0]
-    t0 = time.perf_counter()
-    pre = oracle.preprocess(work.params, cam)
-    oracle.bin_sort(work.params, cam)
-    img, _, _, _ = oracle.render(work.params, cam)
-    _, dL, _, _ = oracle.loss(img, tgt, work.w_l1, work.w_ssim)
-    _, _, grads, _ = oracle.backward(work.params, cam, dL)
-    t_view = time.perf_counter() - t0
-    rows = np.flatnonzero(pre["visible"]).astype(np.int32)
-    t1 = time.perf_counter()
-    oracle.adam(work.params, grads, np.zeros_like(grads), np.zeros_like(grads), rows, work.lr, work.beta1,
-                work.beta2, work.eps)
-    t_adam = time.perf_counter() - t1
-    t_step = len(work.cameras) * t_view + t_adam
+    t = time.perf_counter
+    nv = len(work.cameras)
+    grads = None
+    seen = np.zeros(work.n, bool)
+    t0 = t()
+    done = 0
+    for cam, tgt in zip(work.cameras, work.targets):
+        pre = oracle.preprocess(work.params, cam)
+        oracle.bin_sort(work.params, cam)
+        img, _, _, _ = oracle.render(work.params, cam)
+        _, dL, _, _ = oracle.loss(img, tgt, work.w_l1, work.w_ssim)
+        _, _, g, _ = oracle.backward(work.params, cam, dL)
+        grads = g if grads is None else grads + g
+        seen |= pre["visible"]
+        done += 1
+        if t() - t0 > budget_s:
+            break
+    t_views = (t() - t0) * nv / done
+    rows = np.flatnonzero(seen).astype(np.int32)
+    zeros = np.zeros_like(grads)
+    t1 = t()
+    oracle.adam(work.params, grads, zeros, zeros, rows, work.lr, work.beta1, work.beta2, work.eps)
+    t_adam = t() - t1
+    t_step = t_views + t_adam
     return {"value": 1.0 / t_step, "unit": "steps/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"view 0 of {len(work.cameras)} (full size) + Adam over its visible rows; "
-                      f"step = {len(work.cameras)} x {t_view:.2f} s + {t_adam:.2f} s"}
+            "sample": f"one step at the initial parameters: {done} of {nv} views (full size) in "
+                      f"{t_views * done / nv:.1f} s" + (f", scaled x{nv / done:.2f}" if done < nv else "") +
+                      f", Adam over {rows.shape[0]:,} rows in {t_adam:.1f} s"}
 
 
 def main():
@@ -145,9 +178,12 @@ def main():
     evals = float(np.mean([TILE * TILE * v["M_proc"] for v in views]))
     flops = evals * FLOPS_PER_EVAL[dom]
     achieved = flops / (stages[dom] * 1e-3)
-    roofline = {"kernel": "k_render_bwd" if dom == "render_bwd" else "k_render_fwd", "bound": "alu",
+    kname = "k_render_bwd" if dom == "render_bwd" else "k_render_fwd"
+    wl = {2: "mid_1080p"}.get(args.config)
+    roofline = {"kernel": kname, "bound": "alu",
                 "achieved": achieved / 1e12, "peak": FP32_VECTOR_PEAK / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / FP32_VECTOR_PEAK, "traffic": None,
+                "frac": achieved / FP32_VECTOR_PEAK,
+                "traffic": recorded_traffic(kname, wl) if wl else None,
                 "avg_launch_ms": stages[dom], "flops_per_launch": flops,
                 "evals_per_launch": evals, "flops_per_eval": FLOPS_PER_EVAL[dom]}
 
