@@ -113,10 +113,19 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   if (lmax == 0) return;
 
   // chunks from the last composited entry down to the first
-  for (int64_t cs = int64_t(start) + int64_t((lmax - 1) / kChunk) * kChunk; cs >= int64_t(start); cs -= kChunk) {
-    const uint32_t j = uint32_t(cs) + uint32_t(lane);
+  // (every chunk below the first one processed lies wholly inside the
+  // composited prefix; entries are loaded one chunk ahead, indices two)
+  const uint32_t ul = uint32_t(lane);
+  const int64_t top = int64_t(start) + int64_t((lmax - 1) / kChunk) * kChunk;
+  EntryRec cur = load_entry(proj, load_index(vals, uint32_t(top) + ul, uint32_t(top) + ul - start < lmax));
+  int32_t gnext = load_index(vals, uint32_t(top - kChunk) + ul, top - kChunk >= int64_t(start));
+  for (int64_t cs = top; cs >= int64_t(start); cs -= kChunk) {
+    const EntryRec nxt = load_entry(proj, gnext);
+    gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= int64_t(start));
+    const uint32_t j = uint32_t(cs) + ul;
     const uint32_t pos = j - start;
-    const uint32_t mq = stage_entry(proj, vals, j, pos < lmax, bx0, by0, s_a, s_c, s_b, s_g, lane);
+    const uint32_t mq = stage_entry(cur, bx0, by0, s_a, s_c, s_b, s_g, lane);
+    cur = nxt;
     uint64_t m[kQPW];
     uint64_t active = 0;
 #pragma unroll

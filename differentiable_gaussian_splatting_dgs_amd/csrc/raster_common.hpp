@@ -62,23 +62,56 @@ struct RasterRec {
   float b;
 };
 
-// Stage entry `j` (if valid) of the list into LDS slot `lane` and return its
-// 4-bit quarter-overlap mask.  bx0/by0: pixel-centre coordinate of the
+// One list entry's record as loaded from HBM: the first 11 words of the
+// projected record (u, v, A, B | C, opacity, r, g | b, cull extent x, y)
+// and the Gaussian's index (-1: no entry).
+struct EntryRec {
+  float4 q0, q1;
+  float b, ex, ey;
+  int32_t g;
+};
+
+__device__ __forceinline__ int32_t load_index(const int32_t* __restrict__ vals, uint32_t j, bool valid) {
+  return valid ? vals[j] : -1;
+}
+
+__device__ __forceinline__ EntryRec load_entry(const float4* __restrict__ proj, int32_t g) {
+  EntryRec r;
+  r.g = g;
+  if (g >= 0) {
+    const float4* q = proj + 4 * int64_t(g);
+    r.q0 = q[0];
+    r.q1 = q[1];
+    const float4 q2 = q[2];
+    r.b = q2.x;
+    r.ex = q2.y;
+    r.ey = q2.z;
+  } else {
+    r.q0 = r.q1 = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.b = r.ex = r.ey = 0.f;
+  }
+  return r;
+}
+
+// The chunk is consumed while the next one is in flight: the records of
+// chunk c + 1 and the list indices of chunk c + 2 are loaded before chunk c
+// is staged, so the two dependent HBM round trips (index, then record) of
+// a chunk overlap the compositing of the one before it.
+//
+// Stage a loaded entry (if any) into LDS slot `lane` and return its 4-bit
+// quarter-overlap mask: the Gaussian's alpha >= 1/255 box
+// [u - ex, u + ex] x [v - ey, v + ey] against the quarters' pixel-centre
+// ranges [b0 + 8k, b0 + 8k + 7].  bx0/by0: pixel-centre coordinate of the
 // tile's first pixel.
-__device__ __forceinline__ uint32_t stage_entry(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
-                                                uint32_t j, bool valid, float bx0, float by0, float4* s_a,
-                                                float4* s_c, float* s_b, int32_t* s_g, int lane) {
+__device__ __forceinline__ uint32_t stage_entry(const EntryRec& r, float bx0, float by0, float4* s_a, float4* s_c,
+                                                float* s_b, int32_t* s_g, int lane) {
   uint32_t m = 0;
-  if (valid) {
-    const int64_t g = vals[j];
-    const float4 q0 = proj[4 * g], q1 = proj[4 * g + 1], q2 = proj[4 * g + 2];
-    s_a[lane] = make_float4(q0.x, q0.y, -0.5f * q0.z, -q0.w);
-    s_c[lane] = make_float4(-0.5f * q1.x, q1.y, q1.z, q1.w);
-    s_b[lane] = q2.x;
-    if (s_g != nullptr) s_g[lane] = int32_t(g);
-    // footprint box [u - ex, u + ex] x [v - ey, v + ey] against the quarters'
-    // pixel-centre ranges [b0 + 8k, b0 + 8k + 7]
-    const float lx = q0.x - q2.y, hx = q0.x + q2.y, ly = q0.y - q2.z, hy = q0.y + q2.z;
+  if (r.g >= 0) {
+    s_a[lane] = make_float4(r.q0.x, r.q0.y, -0.5f * r.q0.z, -r.q0.w);
+    s_c[lane] = make_float4(-0.5f * r.q1.x, r.q1.y, r.q1.z, r.q1.w);
+    s_b[lane] = r.b;
+    if (s_g != nullptr) s_g[lane] = r.g;
+    const float lx = r.q0.x - r.ex, hx = r.q0.x + r.ex, ly = r.q0.y - r.ey, hy = r.q0.y + r.ey;
     const bool x0 = hx >= bx0 && lx <= bx0 + 7.0f;
     const bool x1 = hx >= bx0 + 8.0f && lx <= bx0 + 15.0f;
     const bool y0 = hy >= by0 && ly <= by0 + 7.0f;

@@ -59,9 +59,15 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     qlive |= (__ballot(!done[i]) != 0 ? 1u : 0u) << i;
   }
 
+  const uint32_t ul = uint32_t(lane);
+  EntryRec cur = load_entry(proj, load_index(vals, start + ul, start + ul < end));
+  int32_t gnext = load_index(vals, start + kChunk + ul, start + kChunk + ul < end);
   for (uint32_t cs = start; cs < end && qlive != 0; cs += kChunk) {
-    const uint32_t j = cs + uint32_t(lane);
-    const uint32_t mq = stage_entry(proj, vals, j, j < end, bx0, by0, s_a, s_c, s_b, nullptr, lane);
+    const EntryRec nxt = load_entry(proj, gnext);
+    const uint32_t j2 = cs + 2 * kChunk + ul;
+    gnext = load_index(vals, j2, j2 < end);
+    const uint32_t mq = stage_entry(cur, bx0, by0, s_a, s_c, s_b, nullptr, lane);
+    cur = nxt;
     uint64_t m[kQPW];
     uint64_t active = 0;
 #pragma unroll
