@@ -4,15 +4,22 @@
 // lists first in its stage task graph.
 //
 // The sort order is the one of the keys (tile_id << 32 | bits(depth)) with
-// ties in ascending Gaussian index.  It is produced in two steps that give
-// exactly that order with less traffic than a 45-bit radix sort of all
-// pairs:
+// ties in ascending Gaussian index.  It is produced in steps that give
+// exactly that order with far less traffic than a 45-bit radix sort of
+// all pairs:
 //   1. the visible list (ascending indices) is radix-sorted stably by the
 //      32 depth bits -- V elements, not M;
-//   2. pairs are written in that depth order, and a stable LSD radix sort
-//      on the tile bits alone (8-bit digits; 1-2 passes) groups them by
-//      tile while keeping the depth order (and the index order of equal
-//      depths) inside each tile.
+//   2. pairs are written in that depth order as (tile column | tile row
+//      << 8, depth rank): 6 bytes;
+//   3. a stable pass on the tile column packs each pair into one word
+//      (row << 24 | depth rank);
+//   4. a stable pass on the row writes the final (key, value): the column
+//      comes from the pair's position (the column groups of pass 3), the
+//      depth bits and Gaussian index from the depth-sorted list by rank.
+//   Column then row (LSD) is tile-id order, and the stable passes keep the
+//   depth order (and the index order of equal depths) inside each tile.
+//   Images wider or taller than 256 tiles, or 2^24 or more Gaussians, use
+//   plain stable passes on 8-bit digits of the 64-bit keys instead.
 // Radix passes are reduce-then-scan: per-block digit histograms, a scan of
 // each digit row, then a scatter whose in-block rank comes from wave64
 // ballot matching (8 ballots per digit) and per-wave running counts in LDS.
@@ -30,6 +37,7 @@ constexpr int kRB = kRT * kRI;           // items per block
 constexpr int kWaves = kRT / 64;
 constexpr int kWaveItems = kRI * 64;
 
+__device__ __forceinline__ uint32_t digit_of(uint16_t k, int shift) { return (uint32_t(k) >> shift) & 0xFFu; }
 __device__ __forceinline__ uint32_t digit_of(uint32_t k, int shift) { return (k >> shift) & 0xFFu; }
 __device__ __forceinline__ uint32_t digit_of(uint64_t k, int shift) { return uint32_t(k >> shift) & 0xFFu; }
 
@@ -87,27 +95,81 @@ __global__ __launch_bounds__(kRT) void k_rowscan(uint32_t* __restrict__ H, int n
   if (threadIdx.x == 0) rowtot[blockIdx.x] = carry;
 }
 
+struct RankSmem {
+  uint32_t w[kWaves][256];     // per-wave running counts, then per-wave offsets
+  uint32_t dstart[256];        // block-local start of each digit
+  uint32_t gbase[256];         // global destination of each digit's first item
+  uint32_t sc[kRT / 64];
+};
+
+// Stable ranking of one block's items by their 8-bit digit.  Item `it` of
+// this thread sits at input index base + it * 64 + lane; items at index >=
+// count are absent.  On return pos[it] is the item's place in the block's
+// digit-sorted order, and sm.dstart / sm.gbase hold each digit's local
+// start and global destination (from the scanned histograms H / rowtot).
+__device__ __forceinline__ void rank_block(const uint32_t (&d)[kRI], int64_t base, int64_t count,
+                                           const uint32_t* __restrict__ H, const uint32_t* __restrict__ rowtot,
+                                           int nb, RankSmem& sm, uint32_t (&pos)[kRI]) {
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) sm.w[k][t] = 0;
+  __syncthreads();
+  uint32_t rk[kRI];
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    const bool valid = idx < count;
+    const uint64_t act = ballot(valid);
+    const uint64_t peers = match_bits<8>(d[it], act);
+    const uint32_t below = uint32_t(count_below(peers));
+    const uint32_t prior = sm.w[w][d[it]];
+    rk[it] = prior + below;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && below == 0) sm.w[w][d[it]] = prior + uint32_t(__popcll(peers));
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // digit t: per-wave counts -> block-local offsets
+  uint32_t c[kWaves], tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    c[k] = sm.w[k][t];
+    tot += c[k];
+  }
+  uint32_t btot;
+  const uint32_t ex = block_exclusive_scan<kRT, uint32_t>(tot, sm.sc, btot);
+  sm.dstart[t] = ex;
+  uint32_t run = ex;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    sm.w[k][t] = run;
+    run += c[k];
+  }
+  uint32_t rtot;
+  const uint32_t rex = block_exclusive_scan<kRT, uint32_t>(rowtot[t], sm.sc, rtot);
+  sm.gbase[t] = rex + H[size_t(t) * nb + blockIdx.x];
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) pos[it] = sm.w[w][d[it]] + rk[it];
+}
+
+// Plain stable pass: (key, value) -> (key, value) ordered by the digit at
+// `shift`.
 template <class K>
 __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, const uint32_t* __restrict__ vin,
                                                  K* __restrict__ kout, uint32_t* __restrict__ vout,
                                                  const int64_t* count_dev, int64_t count_host, int shift,
                                                  const uint32_t* __restrict__ H,
                                                  const uint32_t* __restrict__ rowtot, int nb) {
-  __shared__ uint32_t s_w[kWaves][256];     // per-wave running counts, then per-wave offsets
-  __shared__ uint32_t s_dstart[256];
-  __shared__ uint32_t s_gbase[256];
-  __shared__ uint32_t s_sc[kRT / 64];
+  __shared__ RankSmem sm;
   __shared__ K s_key[kRB];
   __shared__ uint32_t s_val[kRB];
   const int64_t count = count_of(count_dev, count_host);
   const int64_t bbase = int64_t(blockIdx.x) * kRB;
   if (bbase >= count) return;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) s_w[k][t] = 0;
-  __syncthreads();
   K key[kRI];
-  uint32_t val[kRI], rk[kRI];
+  uint32_t val[kRI], d[kRI], pos[kRI];
   const int64_t base = bbase + int64_t(w) * kWaveItems;
   // all loads first, so they are in flight together
 #pragma unroll
@@ -118,57 +180,119 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
     val[it] = valid ? vin[idx] : 0u;
   }
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
-    const int64_t idx = base + it * 64 + lane;
-    const bool valid = idx < count;
-    const uint64_t act = ballot(valid);
-    const uint32_t d = digit_of(key[it], shift);
-    const uint64_t peers = match_bits<8>(d, act);
-    const uint32_t below = uint32_t(count_below(peers));
-    const uint32_t prior = s_w[w][d];
-    rk[it] = prior + below;
-    __builtin_amdgcn_wave_barrier();
-    if (valid && below == 0) s_w[w][d] = prior + uint32_t(__popcll(peers));
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
-  // digit t: per-wave counts -> block-local offsets
-  uint32_t c[kWaves], tot = 0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) {
-    c[k] = s_w[k][t];
-    tot += c[k];
-  }
-  uint32_t btot;
-  const uint32_t ex = block_exclusive_scan<kRT, uint32_t>(tot, s_sc, btot);
-  s_dstart[t] = ex;
-  uint32_t run = ex;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) {
-    s_w[k][t] = run;
-    run += c[k];
-  }
-  uint32_t rtot;
-  const uint32_t rex = block_exclusive_scan<kRT, uint32_t>(rowtot[t], s_sc, rtot);
-  s_gbase[t] = rex + H[size_t(t) * nb + blockIdx.x];
-  __syncthreads();
+  for (int it = 0; it < kRI; ++it) d[it] = digit_of(key[it], shift);
+  rank_block(d, base, count, H, rowtot, nb, sm, pos);
 #pragma unroll
   for (int it = 0; it < kRI; ++it) {
-    const int64_t idx = base + it * 64 + lane;
-    if (idx < count) {
-      const uint32_t pos = s_w[w][digit_of(key[it], shift)] + rk[it];
-      s_key[pos] = key[it];
-      s_val[pos] = val[it];
+    if (base + it * 64 + lane < count) {
+      s_key[pos[it]] = key[it];
+      s_val[pos[it]] = val[it];
     }
   }
   __syncthreads();
   const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
   for (int j = t; j < nvalid; j += kRT) {
     const K k = s_key[j];
-    const uint32_t d = digit_of(k, shift);
-    const uint32_t g = s_gbase[d] + (uint32_t(j) - s_dstart[d]);
+    const uint32_t dg = digit_of(k, shift);
+    const uint32_t g = sm.gbase[dg] + (uint32_t(j) - sm.dstart[dg]);
     kout[g] = k;
     vout[g] = s_val[j];
+  }
+}
+
+// Column pass: (column | row << 8, depth rank) -> row << 24 | depth rank,
+// ordered by column.
+__global__ __launch_bounds__(kRT) void k_scatter_col(const uint16_t* __restrict__ kin,
+                                                     const uint32_t* __restrict__ vin, uint32_t* __restrict__ out,
+                                                     int64_t count, const uint32_t* __restrict__ H,
+                                                     const uint32_t* __restrict__ rowtot, int nb) {
+  __shared__ RankSmem sm;
+  __shared__ uint32_t s_p[kRB];
+  __shared__ uint8_t s_d[kRB];
+  const int64_t bbase = int64_t(blockIdx.x) * kRB;
+  if (bbase >= count) return;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  uint32_t p[kRI], d[kRI], pos[kRI];
+  const int64_t base = bbase + int64_t(w) * kWaveItems;
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    const bool valid = idx < count;
+    const uint32_t k = valid ? uint32_t(kin[idx]) : 0u;
+    const uint32_t v = valid ? vin[idx] : 0u;
+    d[it] = k & 0xFFu;
+    p[it] = ((k >> 8) << 24) | v;
+  }
+  rank_block(d, base, count, H, rowtot, nb, sm, pos);
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    if (base + it * 64 + lane < count) {
+      s_p[pos[it]] = p[it];
+      s_d[pos[it]] = uint8_t(d[it]);
+    }
+  }
+  __syncthreads();
+  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
+  for (int j = t; j < nvalid; j += kRT) {
+    const uint32_t dg = s_d[j];
+    out[sm.gbase[dg] + (uint32_t(j) - sm.dstart[dg])] = s_p[j];
+  }
+}
+
+// Row pass: row << 24 | depth rank, grouped by column (group c starts at the
+// exclusive scan of the column pass's digit totals col_tot), -> final
+// (tile << 32 | depth bits, Gaussian index) ordered by row.
+__global__ __launch_bounds__(kRT) void k_scatter_row(const uint32_t* __restrict__ pin, int64_t count,
+                                                     const uint32_t* __restrict__ H,
+                                                     const uint32_t* __restrict__ rowtot, int nb,
+                                                     const uint32_t* __restrict__ col_tot,
+                                                     const uint32_t* __restrict__ dkey,
+                                                     const uint32_t* __restrict__ dval, int32_t tiles_x,
+                                                     uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+  __shared__ RankSmem sm;
+  __shared__ uint32_t s_col[256];
+  __shared__ uint32_t s_p[kRB];
+  __shared__ uint8_t s_c[kRB];
+  const int64_t bbase = int64_t(blockIdx.x) * kRB;
+  if (bbase >= count) return;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  {
+    uint32_t tot;
+    s_col[t] = block_exclusive_scan<kRT, uint32_t>(col_tot[t], sm.sc, tot);
+  }
+  __syncthreads();
+  uint32_t p[kRI], d[kRI], pos[kRI], cc[kRI];
+  const int64_t base = bbase + int64_t(w) * kWaveItems;
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    p[it] = idx < count ? pin[idx] : 0u;
+    d[it] = p[it] >> 24;
+    // column group: the last c with s_col[c] <= idx (empty groups share
+    // their start with the next one, so the last such c is non-empty)
+    int lo = 0, hi = 255;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (int64_t(s_col[mid]) <= idx) lo = mid; else hi = mid - 1;
+    }
+    cc[it] = uint32_t(lo);
+  }
+  rank_block(d, base, count, H, rowtot, nb, sm, pos);
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    if (base + it * 64 + lane < count) {
+      s_p[pos[it]] = p[it];
+      s_c[pos[it]] = uint8_t(cc[it]);
+    }
+  }
+  __syncthreads();
+  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
+  for (int j = t; j < nvalid; j += kRT) {
+    const uint32_t pj = s_p[j];
+    const uint32_t row = pj >> 24, rank = pj & 0xFFFFFFu;
+    const uint32_t g = sm.gbase[row] + (uint32_t(j) - sm.dstart[row]);
+    keys[g] = (uint64_t(row * uint32_t(tiles_x) + s_c[j]) << 32) | dkey[rank];
+    vals[g] = dval[rank];
   }
 }
 
@@ -294,6 +418,62 @@ __global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ pr
   }
 }
 
+// As k_duplicate, for the column/row passes: (column | row << 8, depth
+// rank) per pair.
+__global__ __launch_bounds__(kDT) void k_duplicate_cr(const float4* __restrict__ proj,
+                                                      const uint32_t* __restrict__ order,
+                                                      const int64_t* __restrict__ vis_count,
+                                                      const int64_t* __restrict__ block_offsets,
+                                                      uint16_t* __restrict__ kout, uint32_t* __restrict__ vout) {
+  __shared__ int64_t sh[kDT / 64];
+  __shared__ uint32_t s_off[kDB];        // exclusive pair offset within the block
+  __shared__ uint32_t s_rx[kDB];         // x0 | width << 16
+  __shared__ uint32_t s_y0[kDB];
+  const int64_t V = *vis_count;
+  const int64_t r0 = int64_t(blockIdx.x) * kDB;
+  const int t = threadIdx.x;
+  uint32_t cnt[kDI];
+  uint32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kDI; ++k) {
+    const int64_t r = r0 + t * kDI + k;
+    cnt[k] = 0;
+    if (r < V) {
+      const float4 q3 = proj[4 * int64_t(order[r]) + 3];
+      const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
+      const uint32_t x0 = rx & 0xFFFFu, x1 = rx >> 16;
+      cnt[k] = __builtin_bit_cast(uint32_t, q3.w);
+      s_rx[t * kDI + k] = x0 | ((x1 - x0) << 16);
+      s_y0[t * kDI + k] = ry & 0xFFFFu;
+    }
+    s += cnt[k];
+  }
+  int64_t tot;
+  uint32_t off = uint32_t(block_exclusive_scan<kDT, int64_t>(int64_t(s), sh, tot));
+#pragma unroll
+  for (int k = 0; k < kDI; ++k) {
+    s_off[t * kDI + k] = off;
+    off += cnt[k];
+  }
+  __syncthreads();
+  const int64_t base = block_offsets[blockIdx.x];
+  const int nvalid = int(V - r0 < kDB ? V - r0 : kDB);
+  const uint32_t total = uint32_t(tot);
+  for (uint32_t o = uint32_t(t); o < total; o += kDT) {
+    int lo = 0, hi = nvalid - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= o) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t local = o - s_off[lo];
+    const uint32_t rx = s_rx[lo];
+    const uint32_t w = rx >> 16;
+    const uint32_t ty = s_y0[lo] + local / w, tx = (rx & 0xFFFFu) + local % w;
+    kout[base + o] = uint16_t(tx | (ty << 8));
+    vout[base + o] = uint32_t(r0) + uint32_t(lo);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) p[i] = v;
@@ -373,6 +553,7 @@ struct Ws {
   uint32_t *dkA, *dvA, *dkB, *dvB;   // depth sort ping-pong [n]
   uint32_t* H;                       // radix histograms [256][nb]
   uint32_t* rowtot;                  // [256]
+  uint32_t* rowtot2;                 // [256], the column pass's totals
   int64_t* bsums;                    // per-block tile sums [nbv + 1]
   int64_t* m_dev;                    // pair count
   uint64_t* pk;                      // pair keys scratch [cap]
@@ -393,6 +574,7 @@ Ws carve(void* ws, int64_t n, int64_t cap) {
   w.dvB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.H = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(nbh)));
   w.rowtot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
+  w.rowtot2 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
   w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t((n + kDB - 1) / kDB + 1)));
   w.m_dev = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.pk = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * size_t(cap)));
@@ -406,7 +588,7 @@ size_t carve_bytes(int64_t n, int64_t cap) {
   size_t b = 0;
   b += 4 * align_up(sizeof(uint32_t) * size_t(n), 256);
   b += align_up(sizeof(uint32_t) * 256 * size_t(nbh), 256);
-  b += align_up(sizeof(uint32_t) * 256, 256);
+  b += 2 * align_up(sizeof(uint32_t) * 256, 256);
   b += align_up(sizeof(int64_t) * size_t((n + kDB - 1) / kDB + 1), 256);
   b += align_up(sizeof(int64_t), 256);
   b += align_up(sizeof(uint64_t) * size_t(cap), 256);
@@ -464,20 +646,36 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     if (tile_order != nullptr) k_tile_order<<<1, 1024, 0, st>>>(ranges, int(T), tile_order);
     return hipGetLastError();
   }
-  // number of 8-bit passes over the tile bits
-  int tbits = 0;
-  while ((int64_t(1) << tbits) < T) ++tbits;
-  const int passes = std::max(1, (tbits + 7) / 8);
   uint32_t* uvals = reinterpret_cast<uint32_t*>(vals);
-  // duplicate into the buffer that makes the last pass land in (keys, vals)
-  uint64_t* bufk[2] = {keys, w.pk};
-  uint32_t* bufv[2] = {uvals, w.pv};
-  int cur = (passes & 1) ? 1 : 0;
   const int nbv = int((n + kDB - 1) / kDB);
-  k_duplicate<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, bufk[cur], bufv[cur]);
-  for (int pass = 0; pass < passes; ++pass) {
-    radix_pass<uint64_t>(bufk[cur], bufv[cur], bufk[cur ^ 1], bufv[cur ^ 1], nullptr, M, M, 32 + 8 * pass, w, st);
-    cur ^= 1;
+  if (tiles_x <= 256 && tiles_y <= 256 && n < (int64_t(1) << 24)) {
+    // column / row passes; the pair scratch holds the 6-byte pairs, then
+    // (in pv) the packed words
+    uint16_t* k16 = reinterpret_cast<uint16_t*>(w.pk);
+    uint32_t* r32 = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(w.pk) + ((2 * size_t(M) + 3) & ~size_t(3)));
+    const int nb = int(std::max<int64_t>(1, nblocks(M)));
+    k_duplicate_cr<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, k16, r32);
+    k_upsweep<uint16_t><<<nb, kRT, 0, st>>>(k16, nullptr, M, 0, w.H, nb);
+    k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot2);
+    k_scatter_col<<<nb, kRT, 0, st>>>(k16, r32, w.pv, M, w.H, w.rowtot2, nb);
+    k_upsweep<uint32_t><<<nb, kRT, 0, st>>>(w.pv, nullptr, M, 24, w.H, nb);
+    k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
+    k_scatter_row<<<nb, kRT, 0, st>>>(w.pv, M, w.H, w.rowtot, nb, w.rowtot2, w.dkA, w.dvA, tiles_x, keys, uvals);
+  } else {
+    // number of 8-bit passes over the tile bits
+    int tbits = 0;
+    while ((int64_t(1) << tbits) < T) ++tbits;
+    const int passes = std::max(1, (tbits + 7) / 8);
+    // duplicate into the buffer that makes the last pass land in (keys, vals)
+    uint64_t* bufk[2] = {keys, w.pk};
+    uint32_t* bufv[2] = {uvals, w.pv};
+    int cur = (passes & 1) ? 1 : 0;
+    k_duplicate<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, bufk[cur], bufv[cur]);
+    for (int pass = 0; pass < passes; ++pass) {
+      radix_pass<uint64_t>(bufk[cur], bufv[cur], bufk[cur ^ 1], bufv[cur ^ 1], nullptr, M, M, 32 + 8 * pass, w,
+                           st);
+      cur ^= 1;
+    }
   }
   k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
   if (tile_order != nullptr) k_tile_order<<<1, 1024, 0, st>>>(ranges, int(T), tile_order);

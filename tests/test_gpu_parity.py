@@ -142,12 +142,10 @@ def test_determinism_of_integer_outputs():
             assert np.array_equal(x[key], y[key]), key
 
 
-def test_mid_full_view_forward():
-    """The 1M-Gaussian 1080p workload at full size, first view: projection,
-    visible list, every sort key and value, tile ranges and the image."""
-    work = synth.workload(2)
-    one = synth.Workload(2, "mid_v0", work.params, work.cameras[:1], work.targets[:1], work.w_l1, work.w_ssim,
-                         work.lr, work.beta1, work.beta2, work.eps)
+def forward_only_parity(one, tag):
+    """First view of `one` through preprocess, binning and the forward:
+    projection, visible list, every sort key and value, tile ranges, the
+    image, and the loss."""
     import differentiable_gaussian_splatting_dgs_amd as gs
     step = gs.from_workload(one, record_tiles=True)
     step.forward_view(0)
@@ -159,14 +157,33 @@ def test_mid_full_view_forward():
               ranges=vw.ranges.cpu().numpy().view(np.uint32), image=vw.image.cpu().numpy(),
               T_final=vw.T_final.cpu().numpy(), last=vw.last.cpu().numpy().view(np.uint32),
               tile_processed=vw.tile_processed.cpu().numpy().view(np.uint32))
-    say(f"[mid full] M={M}")
+    say(f"[{tag}] M={M}")
     cam = one.cameras[0]
     pre = oracle.preprocess(one.params, cam)
     okeys, ovals, oranges = oracle.bin_sort(one.params, cam)
     img, Tf, last, proc = oracle.render(one.params, cam)
-    check_forward(gv, pre, okeys, ovals, oranges, img, Tf, last, proc, tag="mid_full/v0")
+    check_forward(gv, pre, okeys, ovals, oranges, img, Tf, last, proc, tag=tag)
     L, dL, _, _ = oracle.loss(img, one.targets[0], one.w_l1, one.w_ssim)
     assert abs(float(vw.loss.item()) - L) <= 1e-5 * L
+
+
+def first_view(work, name):
+    return synth.Workload(work.config, name, work.params, work.cameras[:1], work.targets[:1], work.w_l1,
+                          work.w_ssim, work.lr, work.beta1, work.beta2, work.eps)
+
+
+def test_mid_full_view_forward():
+    """The 1M-Gaussian 1080p workload at full size, first view."""
+    forward_only_parity(first_view(synth.workload(2), "mid_v0"), "mid_full/v0")
+
+
+@pytest.mark.parametrize("shape", [(4128, 96), (96, 4128)])
+def test_more_than_256_tile_columns_or_rows(shape):
+    """Images over 256 tiles wide or tall take the plain 64-bit key passes
+    of the binning instead of the column/row passes; same outputs."""
+    w, h = shape
+    work = synth.cut_down(synth.workload(1), w, h, n=20000, views=1)
+    forward_only_parity(work, f"wide_{w}x{h}")
 
 
 # ---------------------------------------------------------------------------
