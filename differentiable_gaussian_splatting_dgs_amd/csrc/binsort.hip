@@ -11,11 +11,12 @@
 //      32 depth bits -- V elements, not M;
 //   2. pairs are written in that depth order as (tile column | tile row
 //      << 8, depth rank): 6 bytes;
-//   3. a stable pass on the tile column packs each pair into one word
-//      (row << 24 | depth rank);
-//   4. a stable pass on the row writes the final (key, value): the column
-//      comes from the pair's position (the column groups of pass 3), the
-//      depth bits and Gaussian index from the depth-sorted list by rank.
+//   3. a stable pass on the tile column packs each pair into one 64-bit
+//      word (row << 56 | Gaussian index << 32 | depth bits), reading the
+//      index and depth bits from the depth-sorted list by rank (in rank
+//      order, so the reads stream);
+//   4. a stable pass on the row writes the final (key, value), the column
+//      coming from the pair's position (the column groups of pass 3).
 //   Column then row (LSD) is tile-id order, and the stable passes keep the
 //   depth order (and the index order of equal depths) inside each tile.
 //   Images wider or taller than 256 tiles, or 2^24 or more Gaussians, use
@@ -67,12 +68,7 @@ __global__ __launch_bounds__(kRT) void k_upsweep(const K* __restrict__ keys, con
   }
 #pragma unroll
   for (int it = 0; it < kRI; ++it) {
-    const int64_t idx = base + it * 64 + lane;
-    const bool valid = idx < count;
-    const uint64_t act = ballot(valid);
-    if (act == 0) break;
-    const uint64_t peers = match_bits<8>(dg[it], act);
-    if (valid && count_below(peers) == 0) atomicAdd(&hist[dg[it]], uint32_t(__popcll(peers)));
+    if (base + it * 64 + lane < count) atomicAdd(&hist[dg[it]], 1u);
   }
   __syncthreads();
   H[size_t(t) * nb + blockIdx.x] = hist[t];
@@ -200,28 +196,34 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
   }
 }
 
-// Column pass: (column | row << 8, depth rank) -> row << 24 | depth rank,
-// ordered by column.
+// Column pass: (column | row << 8, depth rank) -> row << 56 | Gaussian
+// index << 32 | depth bits, ordered by column.
 __global__ __launch_bounds__(kRT) void k_scatter_col(const uint16_t* __restrict__ kin,
-                                                     const uint32_t* __restrict__ vin, uint32_t* __restrict__ out,
+                                                     const uint32_t* __restrict__ vin,
+                                                     const uint32_t* __restrict__ dkey,
+                                                     const uint32_t* __restrict__ dval, uint64_t* __restrict__ out,
                                                      int64_t count, const uint32_t* __restrict__ H,
                                                      const uint32_t* __restrict__ rowtot, int nb) {
   __shared__ RankSmem sm;
-  __shared__ uint32_t s_p[kRB];
+  __shared__ uint64_t s_p[kRB];
   __shared__ uint8_t s_d[kRB];
   const int64_t bbase = int64_t(blockIdx.x) * kRB;
   if (bbase >= count) return;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  uint32_t p[kRI], d[kRI], pos[kRI];
+  uint32_t k[kRI], r[kRI], d[kRI], pos[kRI];
+  uint64_t p[kRI];
   const int64_t base = bbase + int64_t(w) * kWaveItems;
 #pragma unroll
   for (int it = 0; it < kRI; ++it) {
     const int64_t idx = base + it * 64 + lane;
     const bool valid = idx < count;
-    const uint32_t k = valid ? uint32_t(kin[idx]) : 0u;
-    const uint32_t v = valid ? vin[idx] : 0u;
-    d[it] = k & 0xFFu;
-    p[it] = ((k >> 8) << 24) | v;
+    k[it] = valid ? uint32_t(kin[idx]) : 0u;
+    r[it] = valid ? vin[idx] : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    d[it] = k[it] & 0xFFu;
+    p[it] = (uint64_t(k[it] >> 8) << 56) | (uint64_t(dval[r[it]]) << 32) | dkey[r[it]];
   }
   rank_block(d, base, count, H, rowtot, nb, sm, pos);
 #pragma unroll
@@ -239,19 +241,18 @@ __global__ __launch_bounds__(kRT) void k_scatter_col(const uint16_t* __restrict_
   }
 }
 
-// Row pass: row << 24 | depth rank, grouped by column (group c starts at the
-// exclusive scan of the column pass's digit totals col_tot), -> final
-// (tile << 32 | depth bits, Gaussian index) ordered by row.
-__global__ __launch_bounds__(kRT) void k_scatter_row(const uint32_t* __restrict__ pin, int64_t count,
+// Row pass: row << 56 | index << 32 | depth bits, grouped by column (group
+// c starts at the exclusive scan of the column pass's digit totals
+// col_tot), -> final (tile << 32 | depth bits, Gaussian index) ordered by
+// row.
+__global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict__ pin, int64_t count,
                                                      const uint32_t* __restrict__ H,
                                                      const uint32_t* __restrict__ rowtot, int nb,
-                                                     const uint32_t* __restrict__ col_tot,
-                                                     const uint32_t* __restrict__ dkey,
-                                                     const uint32_t* __restrict__ dval, int32_t tiles_x,
+                                                     const uint32_t* __restrict__ col_tot, int32_t tiles_x,
                                                      uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
   __shared__ RankSmem sm;
   __shared__ uint32_t s_col[256];
-  __shared__ uint32_t s_p[kRB];
+  __shared__ uint64_t s_p[kRB];
   __shared__ uint8_t s_c[kRB];
   const int64_t bbase = int64_t(blockIdx.x) * kRB;
   if (bbase >= count) return;
@@ -261,21 +262,29 @@ __global__ __launch_bounds__(kRT) void k_scatter_row(const uint32_t* __restrict_
     s_col[t] = block_exclusive_scan<kRT, uint32_t>(col_tot[t], sm.sc, tot);
   }
   __syncthreads();
-  uint32_t p[kRI], d[kRI], pos[kRI], cc[kRI];
+  uint64_t p[kRI];
+  uint32_t d[kRI], pos[kRI], cc[kRI];
   const int64_t base = bbase + int64_t(w) * kWaveItems;
 #pragma unroll
   for (int it = 0; it < kRI; ++it) {
     const int64_t idx = base + it * 64 + lane;
-    p[it] = idx < count ? pin[idx] : 0u;
-    d[it] = p[it] >> 24;
-    // column group: the last c with s_col[c] <= idx (empty groups share
-    // their start with the next one, so the last such c is non-empty)
-    int lo = 0, hi = 255;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (int64_t(s_col[mid]) <= idx) lo = mid; else hi = mid - 1;
+    p[it] = idx < count ? pin[idx] : 0ull;
+    d[it] = uint32_t(p[it] >> 56);
+  }
+  // column group of each item: the last c with s_col[c] <= idx (empty
+  // groups share their start with the next one, so the last such c is
+  // non-empty).  A thread's indices increase with `it`: one search for the
+  // first, a forward walk for the rest.
+  {
+    int c = 0;
+#pragma unroll
+    for (int step = 128; step >= 1; step >>= 1) c = int64_t(s_col[c + step]) <= base + lane ? c + step : c;
+#pragma unroll
+    for (int it = 0; it < kRI; ++it) {
+      const int64_t idx = base + it * 64 + lane;
+      while (c < 255 && int64_t(s_col[c + 1]) <= idx) ++c;
+      cc[it] = uint32_t(c);
     }
-    cc[it] = uint32_t(lo);
   }
   rank_block(d, base, count, H, rowtot, nb, sm, pos);
 #pragma unroll
@@ -288,11 +297,11 @@ __global__ __launch_bounds__(kRT) void k_scatter_row(const uint32_t* __restrict_
   __syncthreads();
   const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
   for (int j = t; j < nvalid; j += kRT) {
-    const uint32_t pj = s_p[j];
-    const uint32_t row = pj >> 24, rank = pj & 0xFFFFFFu;
+    const uint64_t pj = s_p[j];
+    const uint32_t row = uint32_t(pj >> 56);
     const uint32_t g = sm.gbase[row] + (uint32_t(j) - sm.dstart[row]);
-    keys[g] = (uint64_t(row * uint32_t(tiles_x) + s_c[j]) << 32) | dkey[rank];
-    vals[g] = dval[rank];
+    keys[g] = (uint64_t(row * uint32_t(tiles_x) + s_c[j]) << 32) | (pj & 0xFFFFFFFFull);
+    vals[g] = uint32_t(pj >> 32) & 0xFFFFFFu;
   }
 }
 
@@ -316,6 +325,16 @@ __global__ __launch_bounds__(256) void k_depth_gather(const float4* __restrict__
 constexpr int kDT = 256;                 // threads
 constexpr int kDI = 4;                   // Gaussians per thread
 constexpr int kDB = kDT * kDI;           // Gaussians per block
+
+// Last i in [0, kDB) with off[i] <= o, for non-decreasing off with off[0] = 0
+// (Gaussians without pairs share the next one's offset, so the last such i
+// has pairs); fixed depth and branch-free, so several searches overlap.
+__device__ __forceinline__ int last_at_or_below(const uint32_t* off, uint32_t o) {
+  int lo = 0;
+#pragma unroll
+  for (int step = kDB / 2; step >= 1; step >>= 1) lo = off[lo + step] <= o ? lo + step : lo;
+  return lo;
+}
 
 // per-block sums of tiles_touched in depth order
 __global__ __launch_bounds__(kDT) void k_tilesum(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
@@ -394,27 +413,27 @@ __global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ pr
   uint32_t off = uint32_t(block_exclusive_scan<kDT, int64_t>(int64_t(s), sh, tot));
 #pragma unroll
   for (int k = 0; k < kDI; ++k) {
-    s_off[t * kDI + k] = off;
+    // absent entries (past the visible count) get an offset no pair reaches
+    s_off[t * kDI + k] = r0 + t * kDI + k < V ? off : 0xFFFFFFFFu;
     off += cnt[k];
   }
   __syncthreads();
   const int64_t base = block_offsets[blockIdx.x];
   const int nvalid = int(V - r0 < kDB ? V - r0 : kDB);
   const uint32_t total = uint32_t(tot);
-  for (uint32_t o = uint32_t(t); o < total; o += kDT) {
-    // last i in [0, nvalid) with s_off[i] <= o (entries with no pairs have
-    // equal offsets; visible Gaussians always have at least one)
-    int lo = 0, hi = nvalid - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= o) lo = mid; else hi = mid - 1;
-    }
+  for (uint32_t o0 = uint32_t(t); o0 < total; o0 += 4 * kDT) {
+#pragma unroll
+   for (int u = 0; u < 4; ++u) {
+    const uint32_t o = o0 + uint32_t(u * kDT);
+    if (o >= total) break;
+    const int lo = last_at_or_below(s_off, o);
     const uint32_t local = o - s_off[lo];
     const uint32_t rx = s_rx[lo];
     const uint32_t w = rx >> 16;
     const uint32_t ty = s_y0[lo] + local / w, tx = (rx & 0xFFFFu) + local % w;
     keys[base + o] = (uint64_t(ty * uint32_t(tiles_x) + tx) << 32) | s_dep[lo];
     vals[base + o] = s_g[lo];
+   }
   }
 }
 
@@ -452,25 +471,27 @@ __global__ __launch_bounds__(kDT) void k_duplicate_cr(const float4* __restrict__
   uint32_t off = uint32_t(block_exclusive_scan<kDT, int64_t>(int64_t(s), sh, tot));
 #pragma unroll
   for (int k = 0; k < kDI; ++k) {
-    s_off[t * kDI + k] = off;
+    // absent entries (past the visible count) get an offset no pair reaches
+    s_off[t * kDI + k] = r0 + t * kDI + k < V ? off : 0xFFFFFFFFu;
     off += cnt[k];
   }
   __syncthreads();
   const int64_t base = block_offsets[blockIdx.x];
   const int nvalid = int(V - r0 < kDB ? V - r0 : kDB);
   const uint32_t total = uint32_t(tot);
-  for (uint32_t o = uint32_t(t); o < total; o += kDT) {
-    int lo = 0, hi = nvalid - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= o) lo = mid; else hi = mid - 1;
-    }
+  for (uint32_t o0 = uint32_t(t); o0 < total; o0 += 4 * kDT) {
+#pragma unroll
+   for (int u = 0; u < 4; ++u) {
+    const uint32_t o = o0 + uint32_t(u * kDT);
+    if (o >= total) break;
+    const int lo = last_at_or_below(s_off, o);
     const uint32_t local = o - s_off[lo];
     const uint32_t rx = s_rx[lo];
     const uint32_t w = rx >> 16;
     const uint32_t ty = s_y0[lo] + local / w, tx = (rx & 0xFFFFu) + local % w;
     kout[base + o] = uint16_t(tx | (ty << 8));
     vout[base + o] = uint32_t(r0) + uint32_t(lo);
+   }
   }
 }
 
@@ -649,18 +670,19 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
   uint32_t* uvals = reinterpret_cast<uint32_t*>(vals);
   const int nbv = int((n + kDB - 1) / kDB);
   if (tiles_x <= 256 && tiles_y <= 256 && n < (int64_t(1) << 24)) {
-    // column / row passes; the pair scratch holds the 6-byte pairs, then
-    // (in pv) the packed words
-    uint16_t* k16 = reinterpret_cast<uint16_t*>(w.pk);
-    uint32_t* r32 = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(w.pk) + ((2 * size_t(M) + 3) & ~size_t(3)));
+    // column / row passes: the 6-byte pairs live in the output key buffer
+    // (free until the row pass writes it), the packed words in the pair
+    // scratch
+    uint16_t* k16 = reinterpret_cast<uint16_t*>(keys);
+    uint32_t* r32 = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(keys) + ((2 * size_t(M) + 3) & ~size_t(3)));
     const int nb = int(std::max<int64_t>(1, nblocks(M)));
     k_duplicate_cr<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, k16, r32);
     k_upsweep<uint16_t><<<nb, kRT, 0, st>>>(k16, nullptr, M, 0, w.H, nb);
     k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot2);
-    k_scatter_col<<<nb, kRT, 0, st>>>(k16, r32, w.pv, M, w.H, w.rowtot2, nb);
-    k_upsweep<uint32_t><<<nb, kRT, 0, st>>>(w.pv, nullptr, M, 24, w.H, nb);
+    k_scatter_col<<<nb, kRT, 0, st>>>(k16, r32, w.dkA, w.dvA, w.pk, M, w.H, w.rowtot2, nb);
+    k_upsweep<uint64_t><<<nb, kRT, 0, st>>>(w.pk, nullptr, M, 56, w.H, nb);
     k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
-    k_scatter_row<<<nb, kRT, 0, st>>>(w.pv, M, w.H, w.rowtot, nb, w.rowtot2, w.dkA, w.dvA, tiles_x, keys, uvals);
+    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, M, w.H, w.rowtot, nb, w.rowtot2, tiles_x, keys, uvals);
   } else {
     // number of 8-bit passes over the tile bits
     int tbits = 0;
