@@ -4,7 +4,9 @@
 
 Arithmetic flags: no FMA contraction (the canonical fp32 order writes every
 fma explicitly), IEEE-correct fp32 division and square root, fp32
-subnormals kept, and the packed-fp32 instructions disabled.
+subnormals kept, and the packed-fp32 instructions disabled.  The atomic
+optimizer is off: every atomic here is issued by one lane or has lane-
+varying addresses, so its wave-reduction rewrite only adds work.
 """
 from __future__ import annotations
 
@@ -29,6 +31,8 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # single-lane atomics stay single instructions (no wave-reduction loop)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]

@@ -143,7 +143,10 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       const float4 c = s_c[k];
       const float cb = s_b[k];
       const uint32_t kpos = uint32_t(cs) + uint32_t(k) - start;
-      float au = 0.f, av = 0.f, aA = 0.f, aB = 0.f, aC = 0.f, ao = 0.f, ar = 0.f, ag = 0.f, abl = 0.f;
+      // per-lane terms of the nine sums: the 2D mean and conic gradients
+      // are carried as sums of dp (dx, dy) and dp (dx^2, dx dy, dy^2),
+      // dp = dL/dalpha * alpha, and turned into gradients once per entry
+      float sx = 0.f, sy = 0.f, sxx = 0.f, sxy = 0.f, syy = 0.f, ao = 0.f, ar = 0.f, ag = 0.f, abl = 0.f;
       bool any = false;
 #pragma unroll
       for (int i = 0; i < kQPW; ++i) {
@@ -159,38 +162,47 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
         // same decisions as the forward: `ok` = this pixel composited it
         const float om = 1.0f - alpha;
         const float Ti = T[i] * __builtin_amdgcn_rcpf(om);
-        const float wgt = alpha * Ti;
-        const float gG0 = ok ? G0[i] : 0.0f, gG1 = ok ? G1[i] : 0.0f, gG2 = ok ? G2[i] : 0.0f;
-        ar = fmaf(wgt, gG0, ar);
-        ag = fmaf(wgt, gG1, ag);
-        abl = fmaf(wgt, gG2, abl);
-        const float dal = Ti * fmaf(cb - S2[i], gG2, fmaf(c.w - S1[i], gG1, (c.z - S0[i]) * gG0));
+        const float wgt = ok ? alpha * Ti : 0.0f;
+        const float dal = Ti * fmaf(cb - S2[i], G2[i], fmaf(c.w - S1[i], G1[i], (c.z - S0[i]) * G0[i]));
         S0[i] = ok ? fmaf(alpha, c.z, om * S0[i]) : S0[i];
         S1[i] = ok ? fmaf(alpha, c.w, om * S1[i]) : S1[i];
         S2[i] = ok ? fmaf(alpha, cb, om * S2[i]) : S2[i];
         T[i] = ok ? Ti : T[i];
-        const float dl = (araw > 0.99f) ? 0.0f : dal;     // the 0.99 clamp passes no gradient
-        ao = fmaf(dl, e, ao);
+        // the 0.99 clamp passes no gradient
+        const float dl = (ok && !(araw > 0.99f)) ? dal : 0.0f;
         const float dp = dl * alpha;
-        const float A = -2.0f * a.z, B = -a.w, C = -2.0f * c.x;
-        aA = fmaf(dp, -0.5f * dx * dx, aA);
-        aB = fmaf(dp, -dx * dy, aB);
-        aC = fmaf(dp, -0.5f * dy * dy, aC);
-        au = fmaf(dp, fmaf(A, dx, B * dy), au);
-        av = fmaf(dp, fmaf(B, dx, C * dy), av);
+        const float px = dp * dx, py = dp * dy;
+        const float t_ar = wgt * G0[i], t_ag = wgt * G1[i], t_ab = wgt * G2[i], t_ao = dl * e;
+        const float t_xx = px * dx, t_xy = px * dy, t_yy = py * dy;
+        if (i == 0) {
+          sx = px; sy = py; sxx = t_xx; sxy = t_xy; syy = t_yy; ao = t_ao; ar = t_ar; ag = t_ag; abl = t_ab;
+        } else {
+          sx += px; sy += py; sxx += t_xx; sxy += t_xy; syy += t_yy; ao += t_ao; ar += t_ar; ag += t_ag;
+          abl += t_ab;
+        }
         any = true;
       }
       if (!any) continue;
-      const float v9[9] = {au, av, aA, aB, aC, ao, ar, ag, abl};
+      const float v9[9] = {sx, sy, sxx, sxy, syy, ao, ar, ag, abl};
       float q0s, q1s, q2s;
       wave_sum9(v9, q0s, q1s, q2s);
+      // q0 rows hold (sx, sxx, sy, sxy): lanes 0 and 32 need each other's
+      // row for the mean gradient (A sx + B sy, B sx + C sy)
+      const auto sw = __builtin_amdgcn_permlane32_swap(u_of(q0s), u_of(q0s), false, false);
+      const float q0o = f_of(lane < 32 ? sw[1] : sw[0]);
       if ((lane & 15) == 0) {
-        // row r of q0 / q1 holds component (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
+        // row r of q0 / q1 carries component (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
         const int row = lane >> 4;
         const int c0 = ((row & 1) << 1) | (row >> 1);
+        const float A = -2.0f * a.z, B = -a.w, C = -2.0f * c.x;
+        const float g0 = row == 0   ? fmaf(A, q0s, B * q0o)
+                         : row == 2 ? fmaf(B, q0o, C * q0s)
+                         : row == 1 ? -0.5f * q0s
+                                    : -q0s;
+        const float g1 = row == 0 ? -0.5f * q1s : q1s;
         float* dst = grad2d + size_t(s_g[k]) * kG2;
-        if (q0s != 0.0f) unsafeAtomicAdd(dst + c0, q0s);
-        if (q1s != 0.0f) unsafeAtomicAdd(dst + 4 + c0, q1s);
+        if (g0 != 0.0f) unsafeAtomicAdd(dst + c0, g0);
+        if (g1 != 0.0f) unsafeAtomicAdd(dst + 4 + c0, g1);
         if (lane == 0 && q2s != 0.0f) unsafeAtomicAdd(dst + 8, q2s);
       }
     }
