@@ -220,9 +220,35 @@ class View:
         self.num_pairs = 0
 
 
+class _PairSet:
+    """Buffers one view's binning and rasterisation read: projected records,
+    sorted pairs and the binning workspace.  A step alternates between two
+    sets so that the next view's preprocess and binning can run while the
+    current view renders and back-propagates."""
+
+    def __init__(self, n, cap, device):
+        rows = max(n, 1)
+        self.n, self.device = n, device
+        self.proj = torch.empty((rows, GS_PROJ_WORDS), dtype=torch.float32, device=device)
+        self.alloc(cap)
+
+    def alloc(self, cap):
+        self.capacity = cap
+        self.keys = torch.empty(max(cap, 1), dtype=torch.int64, device=self.device)
+        self.vals = torch.empty(max(cap, 1), dtype=torch.int32, device=self.device)
+        self.ws_sort = _bytes(gs_workspace_size(GS_OP_BIN_SORT, self.n, 0, 0, cap), self.device)
+
+
 class TrainStep:
     """Owns parameters, Adam state and scratch; ``step()`` runs one training
-    step (all views of the batch, then sparse Adam)."""
+    step (all views of the batch, then sparse Adam).
+
+    Views alternate between two buffer sets.  In ``step()`` view k + 1's
+    preprocess and binning are issued on a second stream while view k
+    renders, takes its loss and back-propagates on the caller's stream;
+    events order every reuse of a set and the hand-over of each binned view.
+    ``forward_view`` / ``backward_view`` run one view's stages in order on
+    the current stream."""
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
                  pair_capacity=None, record_tiles=False):
@@ -241,7 +267,6 @@ class TrainStep:
         self.record_tiles = record_tiles
         self.timer = None        # optional: name -> list of (start, end) torch.cuda.Event pairs
         rows = max(n, 1)
-        self.proj = torch.empty((rows, GS_PROJ_WORDS), dtype=torch.float32, device=self.device)
         self.grad2d = torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
         self.vis_idx = [torch.empty(rows, dtype=torch.int32, device=self.device) for _ in cameras]
         self.vis_count = torch.zeros(len(cameras), dtype=torch.int64, device=self.device)
@@ -252,16 +277,26 @@ class TrainStep:
             pair_capacity = max(1 << 20, 48 * n)
         self.pair_capacity = int(min(pair_capacity, (1 << 31) - 1))
         self.views = [View(c, tg, n, self.pair_capacity, self.device) for c, tg in zip(cameras, targets)]
-        self._alloc_pairs(self.pair_capacity)
+        self.sets = [_PairSet(n, self.pair_capacity, self.device) for _ in range(2)]
+        self._cur = 0                       # set of the view last prepared
+        self._free = [None, None]           # per set: event after its last reader
+        self.side = torch.cuda.Stream(device=self.device) if len(self.views) > 1 else None
         self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
         self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
         self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
 
-    def _alloc_pairs(self, cap):
-        self.pair_capacity = cap
-        self.keys = torch.empty(max(cap, 1), dtype=torch.int64, device=self.device)
-        self.vals = torch.empty(max(cap, 1), dtype=torch.int32, device=self.device)
-        self.ws_sort = _bytes(gs_workspace_size(GS_OP_BIN_SORT, self.n, 0, 0, cap), self.device)
+    # the buffer set of the view last prepared (what tests read back)
+    @property
+    def proj(self):
+        return self.sets[self._cur].proj
+
+    @property
+    def keys(self):
+        return self.sets[self._cur].keys
+
+    @property
+    def vals(self):
+        return self.sets[self._cur].vals
 
     @contextlib.contextmanager
     def _stage(self, name):
@@ -278,40 +313,54 @@ class TrainStep:
         self.timer.setdefault(name, []).append((a, b))
 
     # -- one view ---------------------------------------------------------
-    def forward_view(self, k):
+    def prepare_view(self, k):
+        """Preprocess and bin/sort view k into buffer set k % 2 (blocks the
+        host once, for the pair count)."""
         vw = self.views[k]
-        n = self.n
+        ps = self.sets[k % 2]
+        self._cur = k % 2
         with self._stage("preprocess"):
-            gs_preprocess(self.params, n, self.ld, vw.cam, self.proj, self.vis_idx[k], self.vis_count[k:k + 1],
+            gs_preprocess(self.params, self.n, self.ld, vw.cam, ps.proj, self.vis_idx[k], self.vis_count[k:k + 1],
                           self.union_flags, self.ws_pre)
         with self._stage("bin_sort"):
-            self._bin_sort(k)
+            self._bin_sort(k, ps)
+
+    def render_view(self, k):
+        """Forward raster and loss of a prepared view."""
+        vw = self.views[k]
+        ps = self.sets[k % 2]
         with self._stage("render_fwd"):
-            gs_render_fwd(self.proj, n, self.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.image, vw.T_final,
+            gs_render_fwd(ps.proj, self.n, ps.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.image, vw.T_final,
                           vw.last, vw.tile_processed if self.record_tiles else None, vw.order)
         with self._stage("loss"):
             gs_loss(vw.image, vw.target, vw.W, vw.H, self.w_l1, self.w_ssim, vw.loss, vw.dL, self.ws_loss)
 
-    def _bin_sort(self, k):
+    def forward_view(self, k):
+        self.prepare_view(k)
+        self.render_view(k)
+
+    def _bin_sort(self, k, ps):
         vw = self.views[k]
         n = self.n
         try:
-            M = gs_bin_sort(self.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, self.keys,
-                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort, vw.order)
+            M = gs_bin_sort(ps.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
+                            ps.capacity, vw.ranges, ps.ws_sort, vw.order)
         except GSError as e:
             if e.status != GS_ERR_CAPACITY:
                 raise
             # grow (once per new high-water mark) and redo the sort
-            self._alloc_pairs(int(min(e.num_pairs * 5 // 4 + 1024, (1 << 31) - 1)))
-            M = gs_bin_sort(self.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, self.keys,
-                            self.vals, self.pair_capacity, vw.ranges, self.ws_sort, vw.order)
+            ps.alloc(int(min(e.num_pairs * 5 // 4 + 1024, (1 << 31) - 1)))
+            self.pair_capacity = max(self.pair_capacity, ps.capacity)
+            M = gs_bin_sort(ps.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
+                            ps.capacity, vw.ranges, ps.ws_sort, vw.order)
         vw.num_pairs = M
 
     def backward_view(self, k, keep_grad2d=False):
         """Raster backward, then (unless keep_grad2d) projection backward."""
         vw = self.views[k]
+        ps = self.sets[k % 2]
         with self._stage("render_bwd"):
-            gs_render_bwd(self.proj, self.n, self.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.T_final, vw.last,
+            gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.T_final, vw.last,
                           vw.dL, self.grad2d, vw.order)
         if not keep_grad2d:
             self.project_view(k)
@@ -321,6 +370,29 @@ class TrainStep:
         with self._stage("project_bwd"):
             gs_project_bwd(self.params, self.n, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1],
                            self.grad2d, self.grads)
+
+    def run_views(self):
+        """Every view of the batch, gradients accumulated; view k + 1 is
+        prepared on the side stream while view k renders and
+        back-propagates on the current one."""
+        main = torch.cuda.current_stream(self.device)
+        nv = len(self.views)
+        self.prepare_view(0)
+        for k in range(nv):
+            self.render_view(k)
+            self.backward_view(k)
+            done = torch.cuda.Event()
+            done.record(main)
+            self._free[k % 2] = done           # set k % 2: last reader enqueued
+            if k + 1 < nv:
+                with torch.cuda.stream(self.side):
+                    prev = self._free[(k + 1) % 2]     # (from an earlier step when k = 0)
+                    if prev is not None:
+                        self.side.wait_event(prev)
+                    self.prepare_view(k + 1)
+                    ready = torch.cuda.Event()
+                    ready.record(self.side)
+                main.wait_event(ready)
 
     def adam(self):
         self.t += 1
@@ -334,9 +406,7 @@ class TrainStep:
     def step(self):
         """One training step: for each view preprocess, bin/sort, render,
         loss, backward (gradients accumulate); then sparse Adam."""
-        for k in range(len(self.views)):
-            self.forward_view(k)
-            self.backward_view(k)
+        self.run_views()
         self.adam()
 
 

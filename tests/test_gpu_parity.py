@@ -120,6 +120,48 @@ def test_training_step_parity(case):
     check_adam(res, ref, work, p0, tol_g)
 
 
+@pytest.mark.parametrize("case", ["mid_cut", "small_cut"])
+def test_pipelined_step_matches_oracle(case):
+    """The step as bench.py runs it: view k + 1 prepared on a second stream
+    while view k renders and back-propagates.  Images, losses, accumulated
+    gradients and the Adam update against the oracle; then a second step
+    (buffer sets reused across steps) against the first one's images."""
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    work = workload_case(case)
+    p0 = work.params.copy()
+    ref = oracle.step(work, dl_tol=DL_TOL)
+    step = gs.from_workload(work, record_tiles=True)
+    step.run_views()
+    torch.cuda.synchronize()
+    for k, (vw, ov) in enumerate(zip(step.views, ref["views"])):
+        img = vw.image.cpu().numpy()
+        assert float(np.max(np.abs(img - ov["image"]))) <= 1e-4, f"{case}/v{k} image"
+        assert np.array_equal(vw.last.cpu().numpy().view(np.uint32), ov["last"]), f"{case}/v{k} last"
+        assert abs(float(vw.loss.item()) - ov["loss"]) <= 1e-5 * abs(ov["loss"]) + 1e-7, f"{case}/v{k} loss"
+    grads = step.grads.cpu().numpy().copy()
+    check_grad(f"{case} grads (pipelined)", grads, ref["grads"], ref["mags"], ref["mags_dl"])
+    step.adam()
+    torch.cuda.synchronize()
+    U = int(step.union_count.item())
+    res = dict(grads=grads, params=step.params.cpu().numpy(), m=step.m.cpu().numpy(), v=step.v.cpu().numpy(),
+               union=step.union_idx[:U].cpu().numpy().copy(), grads_after=step.grads.cpu().numpy(),
+               union_flags=step.union_flags[: step.n].cpu().numpy().copy())
+    tol_g = 1e-3 * np.abs(ref["grads"]) + 1e-4 * ref["mags"] + ref["mags_dl"]
+    check_adam(res, ref, work, p0, tol_g)
+    # second step on the updated parameters, sequential vs pipelined
+    seq = gs.from_workload(work, record_tiles=True)
+    seq.params.copy_(step.params)
+    for k in range(len(seq.views)):
+        seq.forward_view(k)
+        seq.backward_view(k)
+    step.run_views()
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(zip(step.views, seq.views)):
+        assert torch.equal(a.image, b.image), f"{case}/v{k} second-step image"
+        assert torch.equal(a.last, b.last), f"{case}/v{k} second-step last"
+        assert torch.equal(a.ranges, b.ranges), f"{case}/v{k} second-step ranges"
+
+
 @pytest.mark.parametrize("case", ["small_cut", "mid_cut"])
 def test_backward_stages_in_isolation(case):
     """Raster and projection backward fed the oracle's image gradient: only
