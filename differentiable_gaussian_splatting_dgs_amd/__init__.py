@@ -243,10 +243,11 @@ class TrainStep:
     """Owns parameters, Adam state and scratch; ``step()`` runs one training
     step (all views of the batch, then sparse Adam).
 
-    Views alternate between two buffer sets.  In ``step()`` view k + 1's
-    preprocess and binning are issued on a second stream while view k
-    renders, takes its loss and back-propagates on the caller's stream;
-    events order every reuse of a set and the hand-over of each binned view.
+    Views alternate between two buffer sets and two screen-gradient buffers.
+    In ``step()`` view k + 1's preprocess and binning are issued on a second
+    stream while view k renders, takes its loss and runs the raster backward
+    on the caller's stream, and view k's projection backward runs on a third
+    stream; events order every reuse of a set or buffer and every hand-over.
     ``forward_view`` / ``backward_view`` run one view's stages in order on
     the current stream."""
 
@@ -267,7 +268,9 @@ class TrainStep:
         self.record_tiles = record_tiles
         self.timer = None        # optional: name -> list of (start, end) torch.cuda.Event pairs
         rows = max(n, 1)
-        self.grad2d = torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
+        self.g2d = [torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
+                    for _ in range(2)]
+        self._gcur = 0
         self.vis_idx = [torch.empty(rows, dtype=torch.int32, device=self.device) for _ in cameras]
         self.vis_count = torch.zeros(len(cameras), dtype=torch.int64, device=self.device)
         self.union_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
@@ -280,7 +283,8 @@ class TrainStep:
         self.sets = [_PairSet(n, self.pair_capacity, self.device) for _ in range(2)]
         self._cur = 0                       # set of the view last prepared
         self._free = [None, None]           # per set: event after its last reader
-        self.side = torch.cuda.Stream(device=self.device) if len(self.views) > 1 else None
+        self.side = torch.cuda.Stream(device=self.device)      # preprocess + binning of the next view
+        self.gstream = torch.cuda.Stream(device=self.device)   # projection backward
         self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
         self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
         self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
@@ -297,6 +301,11 @@ class TrainStep:
     @property
     def vals(self):
         return self.sets[self._cur].vals
+
+    # the screen-gradient buffer of the view last back-propagated
+    @property
+    def grad2d(self):
+        return self.g2d[self._gcur]
 
     @contextlib.contextmanager
     def _stage(self, name):
@@ -359,9 +368,10 @@ class TrainStep:
         """Raster backward, then (unless keep_grad2d) projection backward."""
         vw = self.views[k]
         ps = self.sets[k % 2]
+        self._gcur = k % 2
         with self._stage("render_bwd"):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.T_final, vw.last,
-                          vw.dL, self.grad2d, vw.order)
+                          vw.dL, self.g2d[k % 2], vw.order)
         if not keep_grad2d:
             self.project_view(k)
 
@@ -369,30 +379,41 @@ class TrainStep:
         vw = self.views[k]
         with self._stage("project_bwd"):
             gs_project_bwd(self.params, self.n, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1],
-                           self.grad2d, self.grads)
+                           self.g2d[k % 2], self.grads)
 
     def run_views(self):
-        """Every view of the batch, gradients accumulated; view k + 1 is
-        prepared on the side stream while view k renders and
-        back-propagates on the current one."""
+        """Every view of the batch, gradients accumulated: view k + 1 is
+        prepared on the side stream and view k's projection backward runs on
+        the gradient stream while the current stream renders and
+        back-propagates through the rasteriser."""
         main = torch.cuda.current_stream(self.device)
         nv = len(self.views)
+        proj_done = [None, None]
         self.prepare_view(0)
         for k in range(nv):
             self.render_view(k)
-            self.backward_view(k)
-            done = torch.cuda.Event()
-            done.record(main)
-            self._free[k % 2] = done           # set k % 2: last reader enqueued
+            if proj_done[k % 2] is not None:
+                main.wait_event(proj_done[k % 2])          # buffer k % 2 re-zeroed by view k - 2
+            self.backward_view(k, keep_grad2d=True)
+            raster_done = torch.cuda.Event()
+            raster_done.record(main)
+            with torch.cuda.stream(self.gstream):
+                self.gstream.wait_event(raster_done)
+                self.project_view(k)
+                done = torch.cuda.Event()
+                done.record(self.gstream)
+            proj_done[k % 2] = done
+            self._free[k % 2] = done                       # set k % 2: last reader enqueued
             if k + 1 < nv:
                 with torch.cuda.stream(self.side):
-                    prev = self._free[(k + 1) % 2]     # (from an earlier step when k = 0)
+                    prev = self._free[(k + 1) % 2]         # (from an earlier step when k = 0)
                     if prev is not None:
                         self.side.wait_event(prev)
                     self.prepare_view(k + 1)
                     ready = torch.cuda.Event()
                     ready.record(self.side)
                 main.wait_event(ready)
+        main.wait_event(proj_done[(nv - 1) % 2])
 
     def adam(self):
         self.t += 1
