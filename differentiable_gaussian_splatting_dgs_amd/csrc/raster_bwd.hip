@@ -88,27 +88,17 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   if (start > end) start = end;
 
   const size_t P = size_t(W) * H;
-  float pxc[kQPW], pyc[kQPW], T[kQPW], G0[kQPW], G1[kQPW], G2[kQPW], S0[kQPW], S1[kQPW], S2[kQPW];
-  uint32_t lastp[kQPW], qmax[kQPW];
-  int qi[kQPW];
-  uint32_t lmax = 0;
-#pragma unroll
-  for (int i = 0; i < kQPW; ++i) {
-    qi[i] = q0 + i;
-    const int px = x0 + (qi[i] & 1) * 8 + (lane & 7), py = y0 + (qi[i] >> 1) * 8 + (lane >> 3);
-    pxc[i] = float(px) + 0.5f;
-    pyc[i] = float(py) + 0.5f;
-    const bool inside = px < W && py < H;
-    const size_t pix = size_t(py) * W + px;
-    T[i] = inside ? T_final[pix] : 1.0f;
-    lastp[i] = inside ? last[pix] : 0u;
-    G0[i] = inside ? dL_dimage[pix] : 0.0f;
-    G1[i] = inside ? dL_dimage[P + pix] : 0.0f;
-    G2[i] = inside ? dL_dimage[2 * P + pix] : 0.0f;
-    S0[i] = S1[i] = S2[i] = 0.0f;
-    qmax[i] = wave_max_u32(lastp[i]);     // entries a pixel of the quarter composited
-    lmax = qmax[i] > lmax ? qmax[i] : lmax;
-  }
+  const int px = x0 + (q0 & 1) * 8 + (lane & 7), py = y0 + (q0 >> 1) * 8 + (lane >> 3);
+  const float pxc = float(px) + 0.5f, pyc = float(py) + 0.5f;
+  const bool inside = px < W && py < H;
+  const size_t pix = size_t(py) * W + px;
+  float T = inside ? T_final[pix] : 1.0f;
+  const uint32_t lastp = inside ? last[pix] : 0u;
+  const float G0 = inside ? dL_dimage[pix] : 0.0f;
+  const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
+  const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
+  float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
+  uint32_t lmax = wave_max_u32(lastp);     // entries a pixel of the quarter composited
   if (lmax > end - start) lmax = end - start;
   if (lmax == 0) return;
 
@@ -122,68 +112,46 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   for (int64_t cs = top; cs >= int64_t(start); cs -= kChunk) {
     const EntryRec nxt = load_entry(proj, gnext);
     gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= int64_t(start));
-    const uint32_t j = uint32_t(cs) + ul;
-    const uint32_t pos = j - start;
+    const uint32_t pos = uint32_t(cs) + ul - start;
     const uint32_t mq = stage_entry(cur, bx0, by0, s_a, s_c, s_b, s_g, lane);
     cur = nxt;
-    uint64_t m[kQPW];
-    uint64_t active = 0;
-#pragma unroll
-    for (int i = 0; i < kQPW; ++i) {
-      m[i] = uint64_t(__ballot(((mq >> qi[i]) & 1u) && pos < qmax[i]));
-      active |= m[i];
-    }
+    uint64_t active = uint64_t(__ballot(((mq >> q0) & 1u) && pos < lmax));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t pos0 = uint32_t(cs) - start;
     while (active != 0) {
       const int k = 63 - __builtin_clzll(active);      // back to front
       active &= ~(1ull << k);
       const float4 a = s_a[k];
       const float4 c = s_c[k];
+      const uint32_t kpos = pos0 + uint32_t(k);
+      const float dx = pxc - a.x, dy = pyc - a.y;
+      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
+      bool ok = kpos < lastp && !(power > 0.0f) && !(power < -5.6f);
+      if (!__any(ok)) continue;
       const float cb = s_b[k];
-      const uint32_t kpos = uint32_t(cs) + uint32_t(k) - start;
+      const float e = pexp_core(power);
+      const float araw = c.y * e;
+      const float alpha = fminf(0.99f, araw);
+      ok = ok && !(alpha < 1.0f / 255.0f);
+      // same decisions as the forward: `ok` = this pixel composited it
+      const float om = 1.0f - alpha;
+      const float Ti = T * __builtin_amdgcn_rcpf(om);
+      const float wgt = ok ? alpha * Ti : 0.0f;
+      const float dal = Ti * fmaf(cb - S2, G2, fmaf(c.w - S1, G1, (c.z - S0) * G0));
+      S0 = ok ? fmaf(alpha, c.z, om * S0) : S0;
+      S1 = ok ? fmaf(alpha, c.w, om * S1) : S1;
+      S2 = ok ? fmaf(alpha, cb, om * S2) : S2;
+      T = ok ? Ti : T;
+      // the 0.99 clamp passes no gradient
+      const float dl = (ok && !(araw > 0.99f)) ? dal : 0.0f;
+      const float dp = dl * alpha;
       // per-lane terms of the nine sums: the 2D mean and conic gradients
-      // are carried as sums of dp (dx, dy) and dp (dx^2, dx dy, dy^2),
-      // dp = dL/dalpha * alpha, and turned into gradients once per entry
-      float sx = 0.f, sy = 0.f, sxx = 0.f, sxy = 0.f, syy = 0.f, ao = 0.f, ar = 0.f, ag = 0.f, abl = 0.f;
-      bool any = false;
-#pragma unroll
-      for (int i = 0; i < kQPW; ++i) {
-        if (!((m[i] >> k) & 1ull)) continue;
-        const float dx = pxc[i] - a.x, dy = pyc[i] - a.y;
-        const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
-        bool ok = kpos < lastp[i] && !(power > 0.0f) && !(power < -5.6f);
-        if (!__any(ok)) continue;
-        const float e = pexp_core(power);
-        const float araw = c.y * e;
-        const float alpha = fminf(0.99f, araw);
-        ok = ok && !(alpha < 1.0f / 255.0f);
-        // same decisions as the forward: `ok` = this pixel composited it
-        const float om = 1.0f - alpha;
-        const float Ti = T[i] * __builtin_amdgcn_rcpf(om);
-        const float wgt = ok ? alpha * Ti : 0.0f;
-        const float dal = Ti * fmaf(cb - S2[i], G2[i], fmaf(c.w - S1[i], G1[i], (c.z - S0[i]) * G0[i]));
-        S0[i] = ok ? fmaf(alpha, c.z, om * S0[i]) : S0[i];
-        S1[i] = ok ? fmaf(alpha, c.w, om * S1[i]) : S1[i];
-        S2[i] = ok ? fmaf(alpha, cb, om * S2[i]) : S2[i];
-        T[i] = ok ? Ti : T[i];
-        // the 0.99 clamp passes no gradient
-        const float dl = (ok && !(araw > 0.99f)) ? dal : 0.0f;
-        const float dp = dl * alpha;
-        const float px = dp * dx, py = dp * dy;
-        const float t_ar = wgt * G0[i], t_ag = wgt * G1[i], t_ab = wgt * G2[i], t_ao = dl * e;
-        const float t_xx = px * dx, t_xy = px * dy, t_yy = py * dy;
-        if (i == 0) {
-          sx = px; sy = py; sxx = t_xx; sxy = t_xy; syy = t_yy; ao = t_ao; ar = t_ar; ag = t_ag; abl = t_ab;
-        } else {
-          sx += px; sy += py; sxx += t_xx; sxy += t_xy; syy += t_yy; ao += t_ao; ar += t_ar; ag += t_ag;
-          abl += t_ab;
-        }
-        any = true;
-      }
-      if (!any) continue;
-      const float v9[9] = {sx, sy, sxx, sxy, syy, ao, ar, ag, abl};
+      // are carried as sums of dp (dx, dy) and dp (dx^2, dx dy, dy^2) and
+      // turned into gradients once per entry
+      const float sx = dp * dx, sy = dp * dy;
+      const float v9[9] = {sx, sy, sx * dx, sx * dy, sy * dy, dl * e, wgt * G0, wgt * G1, wgt * G2};
       float q0s, q1s, q2s;
       wave_sum9(v9, q0s, q1s, q2s);
       // q0 rows hold (sx, sxx, sy, sxy): lanes 0 and 32 need each other's

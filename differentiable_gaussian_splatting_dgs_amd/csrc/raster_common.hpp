@@ -1,16 +1,14 @@
 // Pieces shared by the forward and backward rasterisers.
 //
-// Work layout: kWPT waves (64 lanes each) per 16x16 tile, each owning kQPW
-// of the tile's four 8x8 quarters (quarter q covers x + 8 (q & 1),
-// y + 8 (q >> 1)); lane l owns the pixel at offset (l & 7, l >> 3) of each
-// of its wave's quarters.  The tile's
-// depth-sorted list is consumed in chunks of 64 entries: lane l stages entry
-// l's record in LDS and tests the Gaussian's alpha >= 1/255 footprint box
-// against the quarters; one ballot per quarter gives the 64-bit set of chunk
-// entries that can reach it.  The loop then visits only set bits
-// (scalar bit scans), and evaluates only the quarters whose bit is set
-// (wave-uniform branches), so Gaussians that cannot reach a quarter cost no
-// vector work there.
+// Work layout: four waves (64 lanes each) per 16x16 tile, wave q owning the
+// tile's 8x8 quarter q (x + 8 (q & 1), y + 8 (q >> 1)); lane l owns the
+// pixel at offset (l & 7, l >> 3) of it.  The tile's depth-sorted list is
+// consumed in chunks of 64 entries: lane l stages entry l's record in LDS
+// and tests the Gaussian's alpha >= 1/255 footprint box against the
+// quarters; one ballot gives the 64-bit set of chunk entries that can
+// reach the wave's quarter.  The loop then visits only set bits (scalar
+// bit scans), so Gaussians that cannot reach a quarter cost it no vector
+// work.
 #pragma once
 
 #include "gs_device.hpp"
@@ -19,18 +17,15 @@ namespace gs {
 
 constexpr int kChunk = 64;
 
-// Waves per tile and quarters per wave: each wave owns QPW of the tile's
-// four 8x8 quarters (one pixel of each per lane).  More waves per tile
-// shorten the sequential chain the heaviest tiles put on one wave.
-constexpr int kQPW = 1;
-constexpr int kWPT = 4 / kQPW;
+// Waves (one per quarter) per tile.
+constexpr int kWPT = 4;
 
-// Workgroup -> (tile, first quarter).  Tiles are taken in `order` (longest
+// Workgroup -> (tile, quarter).  Tiles are taken in `order` (longest
 // lists first) when given, so the heavy ones start early and light ones
 // fill the gaps.  Returns -1 for workgroups past the end.
 __device__ __forceinline__ int order_tile(const uint32_t* __restrict__ order, int nT, int& q0) {
   const int rank = int(blockIdx.x) / kWPT;
-  q0 = (int(blockIdx.x) % kWPT) * kQPW;
+  q0 = int(blockIdx.x) % kWPT;
   if (rank >= nT) return -1;
   return order != nullptr ? int(order[rank]) : rank;
 }

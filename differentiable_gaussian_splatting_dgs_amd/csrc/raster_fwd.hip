@@ -6,8 +6,8 @@
 // Waves own 8x8 quarters of a tile (see raster_common.hpp).  Per pixel the
 // canonical fp32 rule decides skip / composite / stop, evaluated without
 // branches (selects), so the image and every decision are bit-identical to
-// the checker's.  A quarter whose 64 pixels have all stopped drops out of
-// the masks; the wave ends when all of its quarters have.
+// the checker's.  A wave ends at the first chunk boundary after all 64 of
+// its pixels have stopped.
 #include "raster_common.hpp"
 
 namespace gs {
@@ -38,111 +38,69 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   if (end > uint64_t(num_pairs)) end = uint32_t(num_pairs);
   if (start > end) start = end;
 
-  float pxc[kQPW], pyc[kQPW], T[kQPW], C0[kQPW], C1[kQPW], C2[kQPW];
-  uint32_t lastp[kQPW], read[kQPW];
-  bool done[kQPW], inside[kQPW];
-  int qi[kQPW], pxi[kQPW], pyi[kQPW];
-  uint32_t qlive = 0;       // wave-uniform: quarters with a pixel still compositing
-#pragma unroll
-  for (int i = 0; i < kQPW; ++i) {
-    qi[i] = q0 + i;
-    pxi[i] = x0 + (qi[i] & 1) * 8 + (lane & 7);
-    pyi[i] = y0 + (qi[i] >> 1) * 8 + (lane >> 3);
-    pxc[i] = float(pxi[i]) + 0.5f;
-    pyc[i] = float(pyi[i]) + 0.5f;
-    inside[i] = pxi[i] < W && pyi[i] < H;
-    done[i] = !inside[i];
-    T[i] = 1.0f;
-    C0[i] = C1[i] = C2[i] = 0.0f;
-    lastp[i] = 0;
-    read[i] = end - start;
-    qlive |= (__ballot(!done[i]) != 0 ? 1u : 0u) << i;
-  }
+  const int px = x0 + (q0 & 1) * 8 + (lane & 7), py = y0 + (q0 >> 1) * 8 + (lane >> 3);
+  const float pxc = float(px) + 0.5f, pyc = float(py) + 0.5f;
+  const bool inside = px < W && py < H;
+  float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
+  uint32_t lastp = 0, read = end - start;
+  bool live = inside;       // still compositing
 
   const uint32_t ul = uint32_t(lane);
   EntryRec cur = load_entry(proj, load_index(vals, start + ul, start + ul < end));
   int32_t gnext = load_index(vals, start + kChunk + ul, start + kChunk + ul < end);
-  for (uint32_t cs = start; cs < end && qlive != 0; cs += kChunk) {
+  for (uint32_t cs = start; cs < end && __any(live); cs += kChunk) {
     const EntryRec nxt = load_entry(proj, gnext);
     const uint32_t j2 = cs + 2 * kChunk + ul;
     gnext = load_index(vals, j2, j2 < end);
     const uint32_t mq = stage_entry(cur, bx0, by0, s_a, s_c, s_b, nullptr, lane);
     cur = nxt;
-    uint64_t m[kQPW];
-    uint64_t active = 0;
-#pragma unroll
-    for (int i = 0; i < kQPW; ++i) {
-      m[i] = ((qlive >> i) & 1u) ? uint64_t(__ballot((mq >> qi[i]) & 1u)) : 0ull;
-      active |= m[i];
-    }
+    uint64_t active = __ballot((mq >> q0) & 1u);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t pos0 = cs - start + 1;   // list position + 1 of the chunk's entry 0
     while (active != 0) {
       const int k = __builtin_ctzll(active);
       active &= active - 1;
       const float4 a = s_a[k];
       const float4 c = s_c[k];
+      const float dx = pxc - a.x, dy = pyc - a.y;
+      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
+      // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1
+      bool ok = live && !(power > 0.0f) && !(power < -5.6f);
+      if (!__any(ok)) continue;
       const float cb = s_b[k];
-      const uint32_t pos1 = cs + uint32_t(k) - start + 1;   // list position + 1
-      bool stopped = false;
-#pragma unroll
-      for (int i = 0; i < kQPW; ++i) {
-        if (!((m[i] >> k) & 1ull)) continue;
-        const float dx = pxc[i] - a.x, dy = pyc[i] - a.y;
-        const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
-        // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1
-        bool ok = !done[i] && !(power > 0.0f) && !(power < -5.6f);
-        if (!__any(ok)) continue;
-        const float alpha = fminf(0.99f, c.y * pexp_core(power));
-        ok = ok && !(alpha < 1.0f / 255.0f);
-        const float nt = T[i] * (1.0f - alpha);
-        const bool stop = ok && nt < 0.0001f;
-        const bool comp = ok && !stop;
-        const float wgt = alpha * T[i];
-        C0[i] = comp ? fmaf(c.z, wgt, C0[i]) : C0[i];
-        C1[i] = comp ? fmaf(c.w, wgt, C1[i]) : C1[i];
-        C2[i] = comp ? fmaf(cb, wgt, C2[i]) : C2[i];
-        T[i] = comp ? nt : T[i];
-        lastp[i] = comp ? pos1 : lastp[i];
-        read[i] = stop ? pos1 : read[i];
-        done[i] = done[i] || stop;
-        stopped = stopped || stop;
-      }
-      if (__any(stopped)) {
-        uint32_t ql = 0;
-#pragma unroll
-        for (int i = 0; i < kQPW; ++i) ql |= (__ballot(!done[i]) != 0 ? 1u : 0u) << i;
-        if (ql != qlive) {
-          qlive = ql;
-          uint64_t keep = 0;
-#pragma unroll
-          for (int i = 0; i < kQPW; ++i) {
-            if (!((qlive >> i) & 1u)) m[i] = 0;
-            keep |= m[i];
-          }
-          active &= keep;
-        }
-      }
+      const float alpha = fminf(0.99f, c.y * pexp_core(power));
+      ok = ok && !(alpha < 1.0f / 255.0f);
+      const float nt = T * (1.0f - alpha);
+      const bool stop = ok && nt < 0.0001f;
+      const bool comp = ok && !stop;
+      const uint32_t pos1 = pos0 + uint32_t(k);
+      // a zero weight leaves the colour sums exactly as they are
+      // (non-negative colours, sums from +0)
+      const float wgt = comp ? alpha * T : 0.0f;
+      C0 = fmaf(c.z, wgt, C0);
+      C1 = fmaf(c.w, wgt, C1);
+      C2 = fmaf(cb, wgt, C2);
+      T = comp ? nt : T;
+      lastp = comp ? pos1 : lastp;
+      read = stop ? pos1 : read;
+      live = live && !stop;
     }
     __builtin_amdgcn_wave_barrier();
   }
 
-  const size_t P = size_t(W) * H;
-  uint32_t rmax = 0;
-#pragma unroll
-  for (int i = 0; i < kQPW; ++i) {
-    if (!inside[i]) continue;
-    const size_t pix = size_t(pyi[i]) * W + pxi[i];
-    image[pix] = C0[i];
-    image[P + pix] = C1[i];
-    image[2 * P + pix] = C2[i];
-    T_final[pix] = T[i];
-    last[pix] = lastp[i];
-    rmax = read[i] > rmax ? read[i] : rmax;
+  if (inside) {
+    const size_t P = size_t(W) * H;
+    const size_t pix = size_t(py) * W + px;
+    image[pix] = C0;
+    image[P + pix] = C1;
+    image[2 * P + pix] = C2;
+    T_final[pix] = T;
+    last[pix] = lastp;
   }
   if (tile_processed != nullptr) {
-    rmax = wave_max_u32(rmax);
+    const uint32_t rmax = wave_max_u32(inside ? read : 0u);
     if (lane == 0 && rmax != 0) atomicMax(tile_processed + tile, rmax);
   }
 }
