@@ -9,18 +9,17 @@
 // all pairs:
 //   1. the visible list (ascending indices) is radix-sorted stably by the
 //      32 depth bits -- V elements, not M;
-//   2. pairs are written in that depth order as (tile column | tile row
-//      << 8, depth rank): 6 bytes;
-//   3. a stable pass on the tile column packs each pair into one 64-bit
-//      word (row << 56 | Gaussian index << 32 | depth bits), reading the
-//      index and depth bits from the depth-sorted list by rank (in rank
-//      order, so the reads stream);
+//   2. per block of depth ranks, its pairs in each tile column come from
+//      the Gaussians' tile rectangles (a difference array over columns);
+//   3. pairs are generated in depth order and written straight to their
+//      place in tile-column order (column start + earlier blocks + stable
+//      rank in the block), packed as row << 56 | index << 32 | depth bits;
 //   4. a stable pass on the row writes the final (key, value), the column
-//      coming from the pair's position (the column groups of pass 3).
-//   Column then row (LSD) is tile-id order, and the stable passes keep the
-//   depth order (and the index order of equal depths) inside each tile.
-//   Images wider or taller than 256 tiles, or 2^24 or more Gaussians, use
-//   plain stable passes on 8-bit digits of the 64-bit keys instead.
+//      coming from the pair's position (the column groups of step 3).
+//   Column then row is tile-id order, and every placement keeps the depth
+//   order (and the index order of equal depths) inside each tile.  Images
+//   over 256 tiles wide or tall, or 2^24 or more Gaussians, use plain
+//   stable LSD passes on 8-bit digits of the 64-bit keys instead.
 // Radix passes are reduce-then-scan: per-block digit histograms, a scan of
 // each digit row, then a scatter whose in-block rank comes from wave64
 // ballot matching (8 ballots per digit) and per-wave running counts in LDS.
@@ -94,34 +93,34 @@ __global__ __launch_bounds__(kRT) void k_rowscan(uint32_t* __restrict__ H, int n
 struct RankSmem {
   uint32_t w[kWaves][256];     // per-wave running counts, then per-wave offsets
   uint32_t dstart[256];        // block-local start of each digit
+  uint32_t dcnt[256];          // items of each digit in the chunk
   uint32_t gbase[256];         // global destination of each digit's first item
   uint32_t sc[kRT / 64];
 };
 
-// Stable ranking of one block's items by their 8-bit digit.  Item `it` of
-// this thread sits at input index base + it * 64 + lane; items at index >=
-// count are absent.  On return pos[it] is the item's place in the block's
-// digit-sorted order, and sm.dstart / sm.gbase hold each digit's local
-// start and global destination (from the scanned histograms H / rowtot).
-__device__ __forceinline__ void rank_block(const uint32_t (&d)[kRI], int64_t base, int64_t count,
-                                           const uint32_t* __restrict__ H, const uint32_t* __restrict__ rowtot,
-                                           int nb, RankSmem& sm, uint32_t (&pos)[kRI]) {
+// Stable ranking of one chunk of NI * 256 items by their 8-bit digit (256
+// threads).  Item `it` of thread (wave w, lane l) is the chunk's item
+// w * NI * 64 + it * 64 + l; absent items have valid[it] = false and sort
+// after all present ones.  On return pos[it] is the item's place in the
+// chunk's digit-sorted order, sm.dstart[d] / sm.dcnt[d] each digit's local
+// start and count.  Ends with a barrier.
+template <int NI>
+__device__ __forceinline__ void rank_chunk(const uint32_t (&d)[NI], const bool (&valid)[NI], RankSmem& sm,
+                                           uint32_t (&pos)[NI]) {
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) sm.w[k][t] = 0;
   __syncthreads();
-  uint32_t rk[kRI];
+  uint32_t rk[NI];
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
-    const int64_t idx = base + it * 64 + lane;
-    const bool valid = idx < count;
-    const uint64_t act = ballot(valid);
+  for (int it = 0; it < NI; ++it) {
+    const uint64_t act = ballot(valid[it]);
     const uint64_t peers = match_bits<8>(d[it], act);
     const uint32_t below = uint32_t(count_below(peers));
     const uint32_t prior = sm.w[w][d[it]];
     rk[it] = prior + below;
     __builtin_amdgcn_wave_barrier();
-    if (valid && below == 0) sm.w[w][d[it]] = prior + uint32_t(__popcll(peers));
+    if (valid[it] && below == 0) sm.w[w][d[it]] = prior + uint32_t(__popcll(peers));
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
@@ -135,18 +134,34 @@ __device__ __forceinline__ void rank_block(const uint32_t (&d)[kRI], int64_t bas
   uint32_t btot;
   const uint32_t ex = block_exclusive_scan<kRT, uint32_t>(tot, sm.sc, btot);
   sm.dstart[t] = ex;
+  sm.dcnt[t] = tot;
   uint32_t run = ex;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) {
     sm.w[k][t] = run;
     run += c[k];
   }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < NI; ++it) pos[it] = sm.w[w][d[it]] + rk[it];
+  __syncthreads();
+}
+
+// One radix block (kRI items per thread, input index base + it * 64 + lane
+// for this thread, absent past `count`): rank_chunk plus each digit's
+// global destination from the scanned histograms H / rowtot.
+__device__ __forceinline__ void rank_block(const uint32_t (&d)[kRI], int64_t base, int64_t count,
+                                           const uint32_t* __restrict__ H, const uint32_t* __restrict__ rowtot,
+                                           int nb, RankSmem& sm, uint32_t (&pos)[kRI]) {
+  const int t = threadIdx.x, lane = t & 63;
+  bool valid[kRI];
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) valid[it] = base + it * 64 + lane < count;
+  rank_chunk<kRI>(d, valid, sm, pos);
   uint32_t rtot;
   const uint32_t rex = block_exclusive_scan<kRT, uint32_t>(rowtot[t], sm.sc, rtot);
   sm.gbase[t] = rex + H[size_t(t) * nb + blockIdx.x];
   __syncthreads();
-#pragma unroll
-  for (int it = 0; it < kRI; ++it) pos[it] = sm.w[w][d[it]] + rk[it];
 }
 
 // Plain stable pass: (key, value) -> (key, value) ordered by the digit at
@@ -196,51 +211,6 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
   }
 }
 
-// Column pass: (column | row << 8, depth rank) -> row << 56 | Gaussian
-// index << 32 | depth bits, ordered by column.
-__global__ __launch_bounds__(kRT) void k_scatter_col(const uint16_t* __restrict__ kin,
-                                                     const uint32_t* __restrict__ vin,
-                                                     const uint32_t* __restrict__ dkey,
-                                                     const uint32_t* __restrict__ dval, uint64_t* __restrict__ out,
-                                                     int64_t count, const uint32_t* __restrict__ H,
-                                                     const uint32_t* __restrict__ rowtot, int nb) {
-  __shared__ RankSmem sm;
-  __shared__ uint64_t s_p[kRB];
-  __shared__ uint8_t s_d[kRB];
-  const int64_t bbase = int64_t(blockIdx.x) * kRB;
-  if (bbase >= count) return;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  uint32_t k[kRI], r[kRI], d[kRI], pos[kRI];
-  uint64_t p[kRI];
-  const int64_t base = bbase + int64_t(w) * kWaveItems;
-#pragma unroll
-  for (int it = 0; it < kRI; ++it) {
-    const int64_t idx = base + it * 64 + lane;
-    const bool valid = idx < count;
-    k[it] = valid ? uint32_t(kin[idx]) : 0u;
-    r[it] = valid ? vin[idx] : 0u;
-  }
-#pragma unroll
-  for (int it = 0; it < kRI; ++it) {
-    d[it] = k[it] & 0xFFu;
-    p[it] = (uint64_t(k[it] >> 8) << 56) | (uint64_t(dval[r[it]]) << 32) | dkey[r[it]];
-  }
-  rank_block(d, base, count, H, rowtot, nb, sm, pos);
-#pragma unroll
-  for (int it = 0; it < kRI; ++it) {
-    if (base + it * 64 + lane < count) {
-      s_p[pos[it]] = p[it];
-      s_d[pos[it]] = uint8_t(d[it]);
-    }
-  }
-  __syncthreads();
-  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
-  for (int j = t; j < nvalid; j += kRT) {
-    const uint32_t dg = s_d[j];
-    out[sm.gbase[dg] + (uint32_t(j) - sm.dstart[dg])] = s_p[j];
-  }
-}
-
 // Row pass: row << 56 | index << 32 | depth bits, grouped by column (group
 // c starts at the exclusive scan of the column pass's digit totals
 // col_tot), -> final (tile << 32 | depth bits, Gaussian index) ordered by
@@ -259,7 +229,7 @@ __global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict_
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   {
     uint32_t tot;
-    s_col[t] = block_exclusive_scan<kRT, uint32_t>(col_tot[t], sm.sc, tot);
+    s_col[t] = block_exclusive_scan<kRT, uint32_t>(t < tiles_x ? col_tot[t] : 0u, sm.sc, tot);
   }
   __syncthreads();
   uint64_t p[kRI];
@@ -437,20 +407,79 @@ __global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ pr
   }
 }
 
-// As k_duplicate, for the column/row passes: (column | row << 8, depth
-// rank) per pair.
-__global__ __launch_bounds__(kDT) void k_duplicate_cr(const float4* __restrict__ proj,
-                                                      const uint32_t* __restrict__ order,
-                                                      const int64_t* __restrict__ vis_count,
-                                                      const int64_t* __restrict__ block_offsets,
-                                                      uint16_t* __restrict__ kout, uint32_t* __restrict__ vout) {
+// ---------------------------------------------------------------------------
+// exact placement of the pairs (images up to 256 x 256 tiles, < 2^24
+// Gaussians): tile-column then tile-row order without histogram passes
+// ---------------------------------------------------------------------------
+constexpr int kMaxT = 256;               // tile columns / rows this path handles
+constexpr int kPI = 4;                   // pairs per thread per chunk of the column placement
+
+// Per block of kDB Gaussians in depth order: its pair total (block_sums)
+// and its pairs in each tile column (colcnt[c][b], from a difference array
+// over columns: a rectangle adds its row count on [x0, x1)); block 0 also
+// clears the total slot colcnt[c][nbv].
+__global__ __launch_bounds__(kDT) void k_count_pairs(const float4* __restrict__ proj,
+                                                     const uint32_t* __restrict__ order,
+                                                     const int64_t* __restrict__ vis_count, int nbv, int tiles_x,
+                                                     int64_t* __restrict__ block_sums, uint32_t* __restrict__ colcnt) {
+  __shared__ int64_t sh[kDT / 64];
+  __shared__ uint32_t s_sc[kDT / 64];
+  __shared__ int32_t s_cd[kMaxT + 1];
+  const int t = threadIdx.x;
+  for (int i = t; i <= kMaxT; i += kDT) s_cd[i] = 0;
+  __syncthreads();
+  const int64_t V = *vis_count;
+  const int64_t r0 = int64_t(blockIdx.x) * kDB;
+  int64_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kDI; ++k) {
+    const int64_t r = r0 + t * kDI + k;
+    if (r < V) {
+      const float4 q3 = proj[4 * int64_t(order[r]) + 3];
+      const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
+      const int x0 = int(rx & 0xFFFFu), x1 = int(rx >> 16), y0 = int(ry & 0xFFFFu), y1 = int(ry >> 16);
+      s += __builtin_bit_cast(uint32_t, q3.w);
+      const int h = y1 - y0;
+      atomicAdd(&s_cd[x0], h);
+      atomicAdd(&s_cd[x1], -h);
+    }
+  }
+  int64_t tot;
+  block_exclusive_scan<kDT, int64_t>(s, sh, tot);
+  if (t == 0) block_sums[blockIdx.x] = tot;
+  // column counts: inclusive prefix of the column differences (mod 2^32)
+  const uint32_t v = uint32_t(s_cd[t]);
+  uint32_t vt;
+  const uint32_t incl = block_exclusive_scan<kDT, uint32_t>(v, s_sc, vt) + v;
+  if (t < tiles_x) {
+    colcnt[size_t(t) * (nbv + 1) + blockIdx.x] = incl;
+    if (blockIdx.x == 0) colcnt[size_t(t) * (nbv + 1) + nbv] = 0u;
+  }
+}
+
+// Pairs of a block of kDB Gaussians (depth order) straight into tile-column
+// order: generated in order (depth rank, rectangle row-major) in chunks of
+// kDT * kPI, ranked stably by column, and written at col_start[c] +
+// colcnt[c][b] (pairs of c in earlier blocks) + pairs of c in earlier
+// chunks + rank, each as row << 56 | Gaussian index << 32 | depth bits.
+__global__ __launch_bounds__(kDT) void k_dup_col(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+                                                 const int64_t* __restrict__ vis_count,
+                                                 const uint32_t* __restrict__ colcnt,
+                                                 const uint32_t* __restrict__ coltot, int nbv, int tiles_x,
+                                                 uint64_t* __restrict__ out) {
   __shared__ int64_t sh[kDT / 64];
   __shared__ uint32_t s_off[kDB];        // exclusive pair offset within the block
   __shared__ uint32_t s_rx[kDB];         // x0 | width << 16
   __shared__ uint32_t s_y0[kDB];
+  __shared__ uint32_t s_g[kDB];
+  __shared__ uint32_t s_dep[kDB];
+  __shared__ uint32_t s_cb[kMaxT];       // running destination of each column
+  __shared__ RankSmem sm;
+  __shared__ uint64_t s_p[kDT * kPI];
+  __shared__ uint8_t s_d[kDT * kPI];
   const int64_t V = *vis_count;
   const int64_t r0 = int64_t(blockIdx.x) * kDB;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   uint32_t cnt[kDI];
   uint32_t s = 0;
 #pragma unroll
@@ -458,12 +487,15 @@ __global__ __launch_bounds__(kDT) void k_duplicate_cr(const float4* __restrict__
     const int64_t r = r0 + t * kDI + k;
     cnt[k] = 0;
     if (r < V) {
-      const float4 q3 = proj[4 * int64_t(order[r]) + 3];
+      const uint32_t g = order[r];
+      const float4 q3 = proj[4 * int64_t(g) + 3];
       const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
       const uint32_t x0 = rx & 0xFFFFu, x1 = rx >> 16;
       cnt[k] = __builtin_bit_cast(uint32_t, q3.w);
       s_rx[t * kDI + k] = x0 | ((x1 - x0) << 16);
       s_y0[t * kDI + k] = ry & 0xFFFFu;
+      s_dep[t * kDI + k] = __builtin_bit_cast(uint32_t, q3.x);
+      s_g[t * kDI + k] = g;
     }
     s += cnt[k];
   }
@@ -475,23 +507,50 @@ __global__ __launch_bounds__(kDT) void k_duplicate_cr(const float4* __restrict__
     s_off[t * kDI + k] = r0 + t * kDI + k < V ? off : 0xFFFFFFFFu;
     off += cnt[k];
   }
+  {
+    uint32_t ct;
+    const uint32_t cstart = block_exclusive_scan<kDT, uint32_t>(t < tiles_x ? coltot[t] : 0u, sm.sc, ct);
+    s_cb[t] = t < tiles_x ? cstart + colcnt[size_t(t) * (nbv + 1) + blockIdx.x] : 0u;
+  }
   __syncthreads();
-  const int64_t base = block_offsets[blockIdx.x];
-  const int nvalid = int(V - r0 < kDB ? V - r0 : kDB);
   const uint32_t total = uint32_t(tot);
-  for (uint32_t o0 = uint32_t(t); o0 < total; o0 += 4 * kDT) {
+  for (uint32_t c0 = 0; c0 < total; c0 += kDT * kPI) {
+    uint32_t d[kPI], pos[kPI];
+    bool valid[kPI];
+    uint64_t pk[kPI];
 #pragma unroll
-   for (int u = 0; u < 4; ++u) {
-    const uint32_t o = o0 + uint32_t(u * kDT);
-    if (o >= total) break;
-    const int lo = last_at_or_below(s_off, o);
-    const uint32_t local = o - s_off[lo];
-    const uint32_t rx = s_rx[lo];
-    const uint32_t w = rx >> 16;
-    const uint32_t ty = s_y0[lo] + local / w, tx = (rx & 0xFFFFu) + local % w;
-    kout[base + o] = uint16_t(tx | (ty << 8));
-    vout[base + o] = uint32_t(r0) + uint32_t(lo);
-   }
+    for (int it = 0; it < kPI; ++it) {
+      const uint32_t o = c0 + uint32_t(w * kPI * 64 + it * 64 + lane);
+      valid[it] = o < total;
+      d[it] = 0;
+      pk[it] = 0;
+      if (valid[it]) {
+        const int lo = last_at_or_below(s_off, o);
+        const uint32_t local = o - s_off[lo];
+        const uint32_t rx = s_rx[lo];
+        const uint32_t wd = rx >> 16;
+        const uint32_t ty = s_y0[lo] + local / wd, tx = (rx & 0xFFFFu) + local % wd;
+        d[it] = tx;
+        pk[it] = (uint64_t(ty) << 56) | (uint64_t(s_g[lo]) << 32) | s_dep[lo];
+      }
+    }
+    rank_chunk<kPI>(d, valid, sm, pos);
+#pragma unroll
+    for (int it = 0; it < kPI; ++it) {
+      if (valid[it]) {
+        s_p[pos[it]] = pk[it];
+        s_d[pos[it]] = uint8_t(d[it]);
+      }
+    }
+    __syncthreads();
+    const int nvalid = int(total - c0 < uint32_t(kDT * kPI) ? total - c0 : uint32_t(kDT * kPI));
+    for (int j = t; j < nvalid; j += kDT) {
+      const uint32_t dd = s_d[j];
+      out[s_cb[dd] + (uint32_t(j) - sm.dstart[dd])] = s_p[j];
+    }
+    __syncthreads();
+    s_cb[t] += sm.dcnt[t];
+    __syncthreads();
   }
 }
 
@@ -574,47 +633,50 @@ struct Ws {
   uint32_t *dkA, *dvA, *dkB, *dvB;   // depth sort ping-pong [n]
   uint32_t* H;                       // radix histograms [256][nb]
   uint32_t* rowtot;                  // [256]
-  uint32_t* rowtot2;                 // [256], the column pass's totals
+  uint32_t* coltot;                  // [256], pairs per tile column
   int64_t* bsums;                    // per-block tile sums [nbv + 1]
   int64_t* m_dev;                    // pair count
+  uint32_t* colcnt;                  // [kMaxT][nbv + 1], pairs per (column, block), then scanned
   uint64_t* pk;                      // pair keys scratch [cap]
   uint32_t* pv;                      // pair values scratch [cap]
-  int nb_hist;
 };
 
 inline int64_t nblocks(int64_t count) { return (count + kRB - 1) / kRB; }
+inline int64_t dup_blocks(int64_t n) { return (n + kDB - 1) / kDB; }
 
-Ws carve(void* ws, int64_t n, int64_t cap) {
+// Workspace layout; with ws == nullptr only the size is computed.
+Ws carve(void* ws, int64_t n, int64_t cap, size_t* bytes = nullptr) {
   Ws w;
-  char* p = static_cast<char*>(ws);
-  auto take = [&](size_t bytes) { char* q = p; p += align_up(bytes, 256); return q; };
+  char* base = static_cast<char*>(ws);
+  size_t at = 0;
+  auto take = [&](size_t b) { char* q = base != nullptr ? base + at : nullptr; at += align_up(b, 256); return q; };
   const int64_t nbh = std::max<int64_t>(1, std::max(nblocks(n), nblocks(cap)));
+  const int64_t nbv = dup_blocks(n);
   w.dkA = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.dvA = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.dkB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.dvB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.H = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(nbh)));
   w.rowtot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
-  w.rowtot2 = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
-  w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t((n + kDB - 1) / kDB + 1)));
+  w.coltot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
+  w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t(nbv + 1)));
   w.m_dev = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
+  w.colcnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kMaxT * size_t(nbv + 1)));
   w.pk = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * size_t(cap)));
   w.pv = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(cap)));
-  w.nb_hist = int(nbh);
+  if (bytes != nullptr) *bytes = at;
   return w;
 }
 
 size_t carve_bytes(int64_t n, int64_t cap) {
-  const int64_t nbh = std::max<int64_t>(1, std::max(nblocks(n), nblocks(cap)));
   size_t b = 0;
-  b += 4 * align_up(sizeof(uint32_t) * size_t(n), 256);
-  b += align_up(sizeof(uint32_t) * 256 * size_t(nbh), 256);
-  b += 2 * align_up(sizeof(uint32_t) * 256, 256);
-  b += align_up(sizeof(int64_t) * size_t((n + kDB - 1) / kDB + 1), 256);
-  b += align_up(sizeof(int64_t), 256);
-  b += align_up(sizeof(uint64_t) * size_t(cap), 256);
-  b += align_up(sizeof(uint32_t) * size_t(cap), 256);
+  carve(nullptr, n, cap, &b);
   return b;
+}
+
+// The exact-placement path: column and row fit a byte, Gaussian indices 24 bits.
+inline bool exact_path(int64_t n, int32_t tiles_x, int32_t tiles_y) {
+  return tiles_x <= kMaxT && tiles_y <= kMaxT && n < (int64_t(1) << 24);
 }
 
 template <class K>
@@ -635,7 +697,8 @@ int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity) {
 }
 
 hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx,
-                                 const int64_t* vis_count, void* ws, int64_t pair_capacity, hipStream_t st) {
+                                 const int64_t* vis_count, int32_t tiles_x, int32_t tiles_y, void* ws,
+                                 int64_t pair_capacity, hipStream_t st) {
   Ws w = carve(ws, n, pair_capacity);
   int64_t* m_dev = w.m_dev;
   const float4* P = reinterpret_cast<const float4*>(proj);
@@ -648,8 +711,14 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
                            even ? w.dvB : w.dvA, vis_count, 0, n, 8 * pass, w, st);
     }
   }
-  const int nbv = int((n + kDB - 1) / kDB);
-  if (nbv > 0) k_tilesum<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
+  const int nbv = int(dup_blocks(n));
+  if (nbv > 0 && exact_path(n, tiles_x, tiles_y)) {
+    // pair totals and per-(column, block) counts
+    k_count_pairs<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, nbv, tiles_x, w.bsums, w.colcnt);
+    k_rowscan<<<unsigned(tiles_x), kRT, 0, st>>>(w.colcnt, nbv + 1, w.coltot);
+  } else if (nbv > 0) {
+    k_tilesum<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
+  }
   k_scan_sums<<<1, 1024, 0, st>>>(w.bsums, nbv, m_dev);
   return hipGetLastError();
 }
@@ -662,27 +731,19 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
   Ws w = carve(ws, n, pair_capacity);
   const float4* P = reinterpret_cast<const float4*>(proj);
   const int64_t T = int64_t(tiles_x) * tiles_y;
-  k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
-  if (M == 0) {
-    if (tile_order != nullptr) k_tile_order<<<1, 1024, 0, st>>>(ranges, int(T), tile_order);
-    return hipGetLastError();
-  }
   uint32_t* uvals = reinterpret_cast<uint32_t*>(vals);
-  const int nbv = int((n + kDB - 1) / kDB);
-  if (tiles_x <= 256 && tiles_y <= 256 && n < (int64_t(1) << 24)) {
-    // column / row passes: the 6-byte pairs live in the output key buffer
-    // (free until the row pass writes it), the packed words in the pair
-    // scratch
-    uint16_t* k16 = reinterpret_cast<uint16_t*>(keys);
-    uint32_t* r32 = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(keys) + ((2 * size_t(M) + 3) & ~size_t(3)));
+  const int nbv = int(dup_blocks(n));
+  if (M == 0) {
+    k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
+  } else if (exact_path(n, tiles_x, tiles_y)) {
+    // pairs straight into tile-column order, then a stable pass on the row
     const int nb = int(std::max<int64_t>(1, nblocks(M)));
-    k_duplicate_cr<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, k16, r32);
-    k_upsweep<uint16_t><<<nb, kRT, 0, st>>>(k16, nullptr, M, 0, w.H, nb);
-    k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot2);
-    k_scatter_col<<<nb, kRT, 0, st>>>(k16, r32, w.dkA, w.dvA, w.pk, M, w.H, w.rowtot2, nb);
+    k_dup_col<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.colcnt, w.coltot, nbv, tiles_x, w.pk);
     k_upsweep<uint64_t><<<nb, kRT, 0, st>>>(w.pk, nullptr, M, 56, w.H, nb);
     k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
-    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, M, w.H, w.rowtot, nb, w.rowtot2, tiles_x, keys, uvals);
+    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, M, w.H, w.rowtot, nb, w.coltot, tiles_x, keys, uvals);
+    k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
+    k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
   } else {
     // number of 8-bit passes over the tile bits
     int tbits = 0;
@@ -698,8 +759,9 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
                            st);
       cur ^= 1;
     }
+    k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
+    k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
   }
-  k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
   if (tile_order != nullptr) k_tile_order<<<1, 1024, 0, st>>>(ranges, int(T), tile_order);
   return hipGetLastError();
 }

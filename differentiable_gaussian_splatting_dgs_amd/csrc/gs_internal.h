@@ -41,8 +41,8 @@ hipError_t launch_compact(uint8_t* flags, int64_t n, int32_t* idx, int64_t* coun
 size_t binsort_ws_bytes(int64_t n, int64_t pair_capacity);
 // Stage 1 (asynchronous): depth sort of the visible list and the pair
 // count M, left in device memory at binsort_count_ptr(ws, ...).
-hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx,
-                                 const int64_t* vis_count, void* ws, int64_t pair_capacity, hipStream_t st);
+hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                                 int32_t tiles_x, int32_t tiles_y, void* ws, int64_t pair_capacity, hipStream_t st);
 int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity);
 // Stage 2 (after M is known on the host): duplication, tile radix sort,
 // tile ranges.
