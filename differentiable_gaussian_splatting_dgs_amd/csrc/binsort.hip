@@ -214,12 +214,15 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
 // Row pass: row << 56 | index << 32 | depth bits, grouped by column (group
 // c starts at the exclusive scan of the column pass's digit totals
 // col_tot), -> final (tile << 32 | depth bits, Gaussian index) ordered by
-// row.
+// row.  Each run of one tile in the block's sorted items also extends the
+// tile's range ([min start, max end) by atomics on a range array holding
+// (UINT_MAX, 0) beforehand).
 __global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict__ pin, int64_t count,
                                                      const uint32_t* __restrict__ H,
                                                      const uint32_t* __restrict__ rowtot, int nb,
                                                      const uint32_t* __restrict__ col_tot, int32_t tiles_x,
-                                                     uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+                                                     uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
+                                                     uint32_t* __restrict__ ranges) {
   __shared__ RankSmem sm;
   __shared__ uint32_t s_col[256];
   __shared__ uint64_t s_p[kRB];
@@ -266,13 +269,32 @@ __global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict_
   }
   __syncthreads();
   const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
+  auto tile_at = [&](int j) { return uint32_t(s_p[j] >> 56) * uint32_t(tiles_x) + s_c[j]; };
   for (int j = t; j < nvalid; j += kRT) {
     const uint64_t pj = s_p[j];
     const uint32_t row = uint32_t(pj >> 56);
     const uint32_t g = sm.gbase[row] + (uint32_t(j) - sm.dstart[row]);
-    keys[g] = (uint64_t(row * uint32_t(tiles_x) + s_c[j]) << 32) | (pj & 0xFFFFFFFFull);
+    const uint32_t tile = row * uint32_t(tiles_x) + s_c[j];
+    keys[g] = (uint64_t(tile) << 32) | (pj & 0xFFFFFFFFull);
     vals[g] = uint32_t(pj >> 32) & 0xFFFFFFu;
+    if (j == 0 || tile_at(j - 1) != tile) atomicMin(ranges + 2 * size_t(tile), g);
+    if (j == nvalid - 1 || tile_at(j + 1) != tile) atomicMax(ranges + 2 * size_t(tile) + 1, g + 1);
   }
+}
+
+// Range array before the row pass: (UINT_MAX, 0) per tile.
+__global__ __launch_bounds__(256) void k_init_ranges(uint32_t* __restrict__ ranges, int T) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i < T) {
+    ranges[2 * i] = 0xFFFFFFFFu;
+    ranges[2 * i + 1] = 0u;
+  }
+}
+
+// After it: tiles no pair reached get [0, 0).
+__global__ __launch_bounds__(256) void k_fix_ranges(uint32_t* __restrict__ ranges, int T) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i < T && ranges[2 * i] == 0xFFFFFFFFu) ranges[2 * i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -741,9 +763,9 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     k_dup_col<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.colcnt, w.coltot, nbv, tiles_x, w.pk);
     k_upsweep<uint64_t><<<nb, kRT, 0, st>>>(w.pk, nullptr, M, 56, w.H, nb);
     k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
-    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, M, w.H, w.rowtot, nb, w.coltot, tiles_x, keys, uvals);
-    k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
-    k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
+    k_init_ranges<<<unsigned((T + 255) / 256), 256, 0, st>>>(ranges, int(T));
+    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, M, w.H, w.rowtot, nb, w.coltot, tiles_x, keys, uvals, ranges);
+    k_fix_ranges<<<unsigned((T + 255) / 256), 256, 0, st>>>(ranges, int(T));
   } else {
     // number of 8-bit passes over the tile bits
     int tbits = 0;
