@@ -68,6 +68,7 @@ def lib():
         L.or_bin.argtypes = [P, i64, i64, P, P, P, i64, P]
         L.or_render.argtypes = [P, i64, i64, P, P, P, P, P]
         L.or_render_brute.argtypes = [P, i64, i64, P, P, P, P]
+        L.or_composite_pixels.argtypes = [P, i64, i64, P, P, P, P, P, i64, P, P, P]
         L.or_loss.restype = f64
         L.or_loss.argtypes = [P, P, i32, i32, f64, f64, P, P, P]
         L.or_render_frozen_f64.argtypes = [P, P, i64, i64, P, P]
@@ -207,6 +208,25 @@ def render_brute(params, cam):
     c = cam_struct(cam)
     lib().or_render_brute(_p(p), n, n, C.byref(c), _p(img), _p(Tf), _p(last))
     return img, Tf, last
+
+
+def composite_pixels(params, cam, vals, ranges, px, py):
+    """Pixels (px[k], py[k]) composited with the fp32 rule of ``render``
+    against the per-tile lists given by (vals, ranges [T][2]): rgb [k][3],
+    T_final [k], last [k]."""
+    p = _params(params)
+    n = p.shape[1]
+    v = np.ascontiguousarray(vals, np.int32)
+    r = np.ascontiguousarray(ranges, np.uint32).reshape(-1)
+    x = np.ascontiguousarray(px, np.int32)
+    y = np.ascontiguousarray(py, np.int32)
+    k = x.shape[0]
+    rgb = np.empty((k, 3), np.float32)
+    Tf = np.empty(k, np.float32)
+    last = np.empty(k, np.uint32)
+    c = cam_struct(cam)
+    lib().or_composite_pixels(_p(p), n, n, C.byref(c), _p(v), _p(r), _p(x), _p(y), k, _p(rgb), _p(Tf), _p(last))
+    return rgb, Tf, last
 
 
 def loss(image, target, w_l1, w_ssim):

@@ -841,6 +841,29 @@ void or_render_brute(const float* params, int64_t n, int64_t ld, const or_camera
   }
 }
 
+// Sampled pixels composited against given per-tile lists (values and
+// [start, end) ranges of a sorted pair array, e.g. one produced elsewhere
+// and checked against the definition separately): for pixel k at (px[k],
+// py[k]) its tile's list is composited with the same per-pixel rule as
+// or_render.  rgb [k][3], T_final [k], last [k].
+void or_composite_pixels(const float* params, int64_t n, int64_t ld, const or_camera* cam, const int32_t* vals,
+                         const uint32_t* ranges, const int32_t* px, const int32_t* py, int64_t count, float* rgb,
+                         float* T_final, uint32_t* last) {
+  std::vector<Proj<float>> g;
+  project_all(params, n, ld, *cam, g);
+  const int TX = (cam->width + kTile - 1) / kTile;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t k = 0; k < count; ++k) {
+    const int64_t t = int64_t(py[k] / kTile) * TX + px[k] / kTile;
+    const uint32_t a = ranges[2 * t], b = ranges[2 * t + 1];
+    PixelTrace tr;
+    trace_pixel(g, vals + a, int64_t(b) - int64_t(a), px[k], py[k], tr);
+    for (int c = 0; c < 3; ++c) rgb[3 * k + c] = tr.rgb[c];
+    T_final[k] = tr.T_final;
+    last[k] = tr.last;
+  }
+}
+
 // Loss (fp64) of a rendered image against a target, both [3][H][W] fp32:
 // L = w_l1 * mean|I - I_t| + w_ssim * (1 - mean SSIM), means over 3 H W.
 // dL/dI [3][H][W].  The L1 subgradient at 0 is 0.  Returns L; also writes

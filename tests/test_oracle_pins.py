@@ -254,6 +254,21 @@ def test_brute_force_equals_tiled_bitwise(case):
         assert np.array_equal(x, y)
 
 
+def test_sampled_pixel_compositing_equals_tiled_render():
+    """Compositing single pixels against given tile lists reproduces the
+    tiled render bit for bit (the lists here are the oracle's own sort)."""
+    w = synth.cut_down(synth.workload(1), 160, 96, n=3000)
+    cam = w.cameras[0]
+    img, Tf, last, _ = oracle.render(w.params, cam)
+    _, vals, ranges = oracle.bin_sort(w.params, cam)
+    py, px = np.mgrid[0:cam.height, 0:cam.width]
+    rgb, T1, l1 = oracle.composite_pixels(w.params, cam, vals, ranges, px.ravel(), py.ravel())
+    assert np.array_equal(rgb.T.reshape(3, cam.height, cam.width), img)
+    assert np.array_equal(T1.reshape(cam.height, cam.width), Tf)
+    assert np.array_equal(l1.reshape(cam.height, cam.width), last)
+    assert (last > 0).mean() > 0.1
+
+
 def test_binning_matches_numpy_stable_sort():
     w = synth.cut_down(synth.workload(1), 200, 136, n=6000)
     cam = w.cameras[0]
