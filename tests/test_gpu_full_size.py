@@ -1,0 +1,159 @@
+"""Parity of the HIP path at the full sizes of the two largest workloads.
+
+* aerial (3,000,000 Gaussians, one 3840x2160 view with empty sky rows):
+  the whole training step against the oracle, exactly as the cut-down
+  cases in test_gpu_parity (every key, value, range, pixel and gradient).
+* capacity (12,000,000 Gaussians, 16 views of 1920x1080 per step), run as
+  bench.py runs a step (views overlapped on three streams): for the last two
+  views, which the step leaves in its two buffer sets, the projection and
+  visible list against the oracle's preprocess, the sorted pair array
+  checked against its definition from those projections (every visible
+  Gaussian's rectangle tiles exactly once, ordered by tile, depth bits,
+  index; ranges delimit the tiles), and sampled pixels (random ones plus
+  every pixel of the longest tile) composited by the oracle against that
+  pair array, bit for bit; then Adam on sampled rows against its closed
+  form at t = 1 from the step's own gradients.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import check_grad, proj_fields, run_gpu_step, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_aerial_full_size_training_step():
+    from test_gpu_parity import DL_TOL, check_adam, check_loss_grad
+    from gpu_helpers import check_forward
+    work = synth.workload(3)
+    say(f"[aerial full] n={work.n} {work.cameras[0].width}x{work.cameras[0].height}")
+    p0 = work.params.copy()
+    res, _ = run_gpu_step(work, record_tiles=True)
+    ref = oracle.step(work, dl_tol=DL_TOL)
+    cam = work.cameras[0]
+    gv, ov = res["views"][0], ref["views"][0]
+    pre = oracle.preprocess(work.params, cam)
+    okeys, ovals, oranges = oracle.bin_sort(work.params, cam)
+    say(f"[aerial full] M={gv['M']}")
+    check_forward(gv, pre, okeys, ovals, oranges, ov["image"], ov["T_final"], ov["last"], ov["tile_processed"],
+                  tag="aerial_full")
+    check_loss_grad(gv, ov, work.w_ssim)
+    vis = pre["visible"]
+    check_grad("aerial_full grad2d", gv["grad2d"][vis], ov["g2d"][vis], ov["m2d"][vis], ov["m2d_dl"][vis])
+    check_grad("aerial_full grads", res["grads"], ref["grads"], ref["mags"], ref["mags_dl"])
+    tol_g = 1e-3 * np.abs(ref["grads"]) + 1e-4 * ref["mags"] + ref["mags_dl"]
+    check_adam(res, ref, work, p0, tol_g)
+
+
+def check_pairs_against_definition(pf, vis_idx, keys, vals, ranges, TX, tag):
+    """The sorted pair array from its definition, given the projections:
+    each visible Gaussian's rectangle tiles exactly once; ascending
+    (tile, depth bits, index); ranges delimit the tiles."""
+    rect = pf["rect"]
+    depth_bits = pf["depth"].view(np.uint32)
+    M = keys.shape[0]
+    assert M == int(pf["tiles"][vis_idx].astype(np.int64).sum()), f"{tag} M"
+    tile = (keys >> np.uint64(32)).astype(np.int64)
+    assert np.array_equal((keys & np.uint64(0xFFFFFFFF)).astype(np.uint32), depth_bits[vals]), f"{tag} depth bits"
+    tx, ty = tile % TX, tile // TX
+    r = rect[vals]
+    assert np.all((tx >= r[:, 0]) & (tx < r[:, 2]) & (ty >= r[:, 1]) & (ty < r[:, 3])), f"{tag} tile outside rect"
+    visible = np.zeros(rect.shape[0], bool)
+    visible[vis_idx] = True
+    assert visible[vals].all(), f"{tag} value not visible"
+    # strictly ascending (key, value): no pair twice; with the count above,
+    # every (Gaussian, tile of its rectangle) exactly once
+    same = keys[1:] == keys[:-1]
+    assert np.all(keys[1:] >= keys[:-1]), f"{tag} keys not sorted"
+    assert np.all(vals[1:][same] > vals[:-1][same]), f"{tag} ties not in index order"
+    T = ranges.shape[0]
+    counts = np.bincount(tile, minlength=T)
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    expect = np.stack([np.where(counts > 0, starts, 0), np.where(counts > 0, starts + counts, 0)], 1)
+    assert np.array_equal(ranges.astype(np.int64), expect), f"{tag} ranges"
+
+
+def test_capacity_full_size_pipelined_step_sampled():
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    work = synth.workload(4)
+    nv = len(work.cameras)
+    say(f"[capacity full] n={work.n} views={nv}")
+    step = gs.from_workload(work, record_tiles=True)
+    step.run_views()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    for k in (nv - 2, nv - 1):
+        cam = work.cameras[k]
+        ps, vw = step.sets[k % 2], step.views[k]
+        M = vw.num_pairs
+        V = int(step.vis_count[k].item())
+        say(f"[capacity full] view {k}: V={V} M={M}")
+        pre = oracle.preprocess(work.params, cam)
+        pf = proj_fields(ps.proj[: work.n].cpu().numpy())
+        vis_idx = step.vis_idx[k][:V].cpu().numpy()
+        vis = pre["visible"]
+        assert np.array_equal(vis_idx, np.flatnonzero(vis).astype(np.int32)), f"v{k} visible list"
+        assert np.array_equal(pf["tiles"], pre["tiles"]), f"v{k} tiles"
+        assert np.array_equal(pf["rect"][vis], pre["rect"][vis]), f"v{k} rect"
+        assert np.array_equal(pf["depth"][vis].view(np.uint32), pre["depth"][vis].view(np.uint32)), f"v{k} depth"
+        for nm in ("mean2d", "conic", "opacity", "rgb"):
+            a, b = pf[nm][vis], pre[nm][vis]
+            d = np.abs(a.astype(np.float64) - b) / np.maximum(np.abs(b.astype(np.float64)), 1e-30)
+            assert d.max() <= 1e-6, f"v{k} {nm}"
+        keys = ps.keys[:M].cpu().numpy().view(np.uint64)
+        vals = ps.vals[:M].cpu().numpy()
+        ranges = vw.ranges.cpu().numpy().view(np.uint32)
+        TX = (cam.width + 15) // 16
+        check_pairs_against_definition(pf, vis_idx, keys, vals, ranges, TX, f"v{k}")
+        del keys
+        # sampled pixels: random ones and every pixel of the longest tile
+        heavy = int(np.argmax(ranges[:, 1].astype(np.int64) - ranges[:, 0]))
+        hy, hx = np.mgrid[0:16, 0:16]
+        px = np.concatenate([rng.integers(0, cam.width, 4096), (heavy % TX) * 16 + hx.ravel()]).astype(np.int32)
+        py = np.concatenate([rng.integers(0, cam.height, 4096), (heavy // TX) * 16 + hy.ravel()]).astype(np.int32)
+        keep = (px < cam.width) & (py < cam.height)
+        px, py = px[keep], py[keep]
+        rgb, Tf, last = oracle.composite_pixels(work.params, cam, vals, ranges, px, py)
+        img = vw.image.cpu().numpy()
+        assert np.array_equal(img[:, py, px].T, rgb), f"v{k} sampled image"
+        assert np.array_equal(vw.T_final.cpu().numpy()[py, px], Tf), f"v{k} sampled T_final"
+        assert np.array_equal(vw.last.cpu().numpy().view(np.uint32)[py, px], last), f"v{k} sampled last"
+        say(f"  v{k}: {px.size} sampled pixels bit-identical (heaviest tile {heavy}, "
+            f"{int(ranges[heavy, 1] - ranges[heavy, 0])} entries)")
+    # Adam at t = 1 on sampled rows, from the step's own gradients
+    rows = np.sort(rng.choice(work.n, 20000, replace=False))
+    rows_t = torch.as_tensor(rows, device=step.device)
+    g = step.grads[:, rows_t].cpu().numpy().astype(np.float64)
+    p = step.params[:, rows_t].cpu().numpy().astype(np.float64)
+    assert np.isfinite(g).all()
+    step.adam()
+    torch.cuda.synchronize()
+    U = int(step.union_count.item())
+    union = np.unique(np.concatenate([step.vis_idx[k][: int(step.vis_count[k].item())].cpu().numpy()
+                                      for k in range(nv)]))
+    assert np.array_equal(step.union_idx[:U].cpu().numpy(), union), "union list"
+    listed = np.isin(rows, union)
+    b1, b2 = work.beta1, work.beta2
+    m_ref = (1 - b1) * g
+    v_ref = (1 - b2) * g * g
+    p_ref = p - work.lr * (m_ref / (1 - b1)) / (np.sqrt(v_ref / (1 - b2)) + work.eps)
+    p_ref[:, ~listed] = p[:, ~listed]
+    pg = step.params[:, rows_t].cpu().numpy().astype(np.float64)
+    mg = step.m[:, rows_t].cpu().numpy().astype(np.float64)
+    vg = step.v[:, rows_t].cpu().numpy().astype(np.float64)
+    # fp32 evaluation of the update: a few roundings of p and of lr * ratio
+    tol_p = 4 * np.spacing(np.abs(p).astype(np.float32)).astype(np.float64) + 1e-5 * work.lr
+    assert np.all(np.abs(pg - p_ref) <= tol_p), "adam params"
+    assert np.all(np.abs(mg[:, listed] - m_ref[:, listed]) <= 1e-6 * np.abs(m_ref[:, listed]) + 1e-38), "adam m"
+    assert np.all(np.abs(vg[:, listed] - v_ref[:, listed]) <= 1e-5 * v_ref[:, listed] + 1e-38), "adam v"
+    assert not step.grads[:, rows_t].any().item(), "consumed gradients not zeroed"
