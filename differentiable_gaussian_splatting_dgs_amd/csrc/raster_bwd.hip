@@ -98,6 +98,15 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
   const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
   float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
+  // lanes 0, 16, 32, 48 (row r = lane / 16) issue the atomics: row r of the
+  // folded sums q0 / q1 carries component (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
+  // (q2, lane 0: component 8); per-lane factors that turn the folded sums
+  // into gradients
+  const int row = lane >> 4;
+  const int comp0 = ((row & 1) << 1) | (row >> 1);
+  const bool row0 = row == 0, row2 = row == 2, even = (row & 1) == 0;
+  const float k_odd = row == 1 ? -0.5f : -1.0f;   // conic A and B: -sxx / 2, -sxy
+  const float k_q1 = row0 ? -0.5f : 1.0f;          // conic C: -syy / 2
   uint32_t lmax = wave_max_u32(lastp);     // entries a pixel of the quarter composited
   if (lmax > end - start) lmax = end - start;
   if (lmax == 0) return;
@@ -158,19 +167,16 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       // row for the mean gradient (A sx + B sy, B sx + C sy)
       const auto sw = __builtin_amdgcn_permlane32_swap(u_of(q0s), u_of(q0s), false, false);
       const float q0o = f_of(lane < 32 ? sw[1] : sw[0]);
+      // u: A sx + B sy (row 0), v: C sy + B sx (row 2), conic A / B (rows 1, 3)
+      const float A = -2.0f * a.z, B = -a.w, C = -2.0f * c.x;
+      const float m1 = row0 ? A : (row2 ? C : k_odd);
+      const float m2 = even ? B : 0.0f;
+      const float g0 = fmaf(m1, q0s, m2 * q0o);
+      const float g1 = k_q1 * q1s;
       if ((lane & 15) == 0) {
-        // row r of q0 / q1 carries component (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
-        const int row = lane >> 4;
-        const int c0 = ((row & 1) << 1) | (row >> 1);
-        const float A = -2.0f * a.z, B = -a.w, C = -2.0f * c.x;
-        const float g0 = row == 0   ? fmaf(A, q0s, B * q0o)
-                         : row == 2 ? fmaf(B, q0o, C * q0s)
-                         : row == 1 ? -0.5f * q0s
-                                    : -q0s;
-        const float g1 = row == 0 ? -0.5f * q1s : q1s;
-        float* dst = grad2d + size_t(s_g[k]) * kG2;
-        if (g0 != 0.0f) unsafeAtomicAdd(dst + c0, g0);
-        if (g1 != 0.0f) unsafeAtomicAdd(dst + 4 + c0, g1);
+        float* dst = grad2d + size_t(__builtin_amdgcn_readfirstlane(s_g[k])) * kG2;
+        if (g0 != 0.0f) unsafeAtomicAdd(dst + comp0, g0);
+        if (g1 != 0.0f) unsafeAtomicAdd(dst + 4 + comp0, g1);
         if (lane == 0 && q2s != 0.0f) unsafeAtomicAdd(dst + 8, q2s);
       }
     }
