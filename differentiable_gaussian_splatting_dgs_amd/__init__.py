@@ -403,7 +403,8 @@ class TrainStep:
                 done = torch.cuda.Event()
                 done.record(self.gstream)
             proj_done[k % 2] = done
-            self._free[k % 2] = done                       # set k % 2: last reader enqueued
+            self._free[k % 2] = raster_done                # set k % 2: its last reader (the projection
+                                                           # backward reads params, not the set)
             if k + 1 < nv:
                 with torch.cuda.stream(self.side):
                     prev = self._free[(k + 1) % 2]         # (from an earlier step when k = 0)
