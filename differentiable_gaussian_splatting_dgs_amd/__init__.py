@@ -28,7 +28,8 @@ GS_GRAD2D_WORDS = 12
 TILE = 16
 
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
-           "gs_bin_sort", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd", "gs_sparse_adam"]
+           "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
+           "gs_sparse_adam"]
 
 
 class gs_camera(C.Structure):
@@ -61,6 +62,7 @@ def lib():
     L.gs_workspace_size.argtypes = [C.c_int, _i64, _i32, _i32, _i64, C.POINTER(_sz)]
     L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _sz, _P]
     L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
+    L.gs_bin_sort_async.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
     L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
     L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
     L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
@@ -156,6 +158,16 @@ def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_cap
     return m.value
 
 
+def gs_bin_sort_async(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_capacity, num_pairs_dev,
+                      tile_ranges, workspace, tile_order=None, stream=None):
+    """As gs_bin_sort without blocking: M lands in num_pairs_dev (a device
+    int64); M > pair_capacity leaves empty ranges (checked by the caller)."""
+    _check(lib().gs_bin_sort_async(_ptr(proj), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys),
+                                   _ptr(vals), pair_capacity, _ptr(num_pairs_dev), _ptr(tile_ranges),
+                                   _ptr(tile_order), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "gs_bin_sort_async")
+
+
 def gs_render_fwd(proj, n, vals, tile_ranges, num_pairs, width, height, image, T_final, last,
                   tile_processed=None, tile_order=None, stream=None):
     _check(lib().gs_render_fwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), _ptr(tile_order), num_pairs, width,
@@ -222,8 +234,8 @@ class View:
 
 class _PairSet:
     """Buffers one view's binning and rasterisation read: projected records,
-    sorted pairs and the binning workspace.  A step alternates between two
-    sets so that the next view's preprocess and binning can run while the
+    sorted pairs and the binning workspace.  A step cycles through several
+    sets so that later views' preprocess and binning can run while the
     current view renders and back-propagates."""
 
     def __init__(self, n, cap, device):
@@ -243,7 +255,8 @@ class TrainStep:
     """Owns parameters, Adam state and scratch; ``step()`` runs one training
     step (all views of the batch, then sparse Adam).
 
-    Views alternate between two buffer sets and two screen-gradient buffers.
+    Views cycle through three buffer sets (two for a batch of two) and
+    alternate between two screen-gradient buffers.
     In ``step()`` view k + 1's preprocess and binning are issued on a second
     stream while view k renders, takes its loss and runs the raster backward
     on the caller's stream, and view k's projection backward runs on a third
@@ -277,12 +290,16 @@ class TrainStep:
         self.union_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
         self.union_count = torch.zeros(1, dtype=torch.int64, device=self.device)
         if pair_capacity is None:
-            pair_capacity = max(1 << 20, 48 * n)
+            pair_capacity = max(1 << 20, 24 * n)       # grown on demand
         self.pair_capacity = int(min(pair_capacity, (1 << 31) - 1))
         self.views = [View(c, tg, n, self.pair_capacity, self.device) for c, tg in zip(cameras, targets)]
-        self.sets = [_PairSet(n, self.pair_capacity, self.device) for _ in range(2)]
+        self.nsets = min(3, max(2, len(self.views)))
+        self.sets = [_PairSet(n, self.pair_capacity, self.device) for _ in range(self.nsets)]
         self._cur = 0                       # set of the view last prepared
-        self._free = [None, None]           # per set: event after its last reader
+        self._free = [None] * self.nsets    # per set: event after its last reader
+        self.M_dev = torch.zeros(len(self.views), dtype=torch.int64, device=self.device)
+        self.M_host = torch.zeros(len(self.views), dtype=torch.int64, pin_memory=True)
+        self._set_cap = [0] * len(self.views)       # capacity of the set each view was binned into
         self.side = torch.cuda.Stream(device=self.device)      # preprocess + binning of the next view
         self.gstream = torch.cuda.Stream(device=self.device)   # projection backward
         self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
@@ -322,24 +339,44 @@ class TrainStep:
         self.timer.setdefault(name, []).append((a, b))
 
     # -- one view ---------------------------------------------------------
-    def prepare_view(self, k):
-        """Preprocess and bin/sort view k into buffer set k % 2 (blocks the
-        host once, for the pair count)."""
+    def prepare_view(self, k, sync=True):
+        """Preprocess and bin/sort view k into buffer set k % nsets.  With
+        sync, the pair count is read (blocking) and the set grown if it
+        overflowed; without, it stays on the device in M_dev[k]."""
         vw = self.views[k]
-        ps = self.sets[k % 2]
-        self._cur = k % 2
+        ps = self.sets[k % self.nsets]
+        self._cur = k % self.nsets
         with self._stage("preprocess"):
             gs_preprocess(self.params, self.n, self.ld, vw.cam, ps.proj, self.vis_idx[k], self.vis_count[k:k + 1],
                           self.union_flags, self.ws_pre)
         with self._stage("bin_sort"):
             self._bin_sort(k, ps)
+        if sync:
+            M = int(self.M_dev[k].item())
+            if M > ps.capacity:
+                # grow (once per new high-water mark) and redo the sort
+                ps.alloc(int(min(M * 5 // 4 + 1024, (1 << 31) - 1)))
+                self.pair_capacity = max(self.pair_capacity, ps.capacity)
+                self._bin_sort(k, ps)
+            vw.num_pairs = M
+
+    def _bin_sort(self, k, ps):
+        vw = self.views[k]
+        vw.num_pairs = None
+        self._set_cap[k] = ps.capacity
+        gs_bin_sort_async(ps.proj, self.n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
+                          ps.capacity, self.M_dev[k:k + 1], vw.ranges, ps.ws_sort, vw.order)
+
+    def _pair_bound(self, k):
+        vw = self.views[k]
+        return vw.num_pairs if vw.num_pairs is not None else self.sets[k % self.nsets].capacity
 
     def render_view(self, k):
         """Forward raster and loss of a prepared view."""
         vw = self.views[k]
-        ps = self.sets[k % 2]
+        ps = self.sets[k % self.nsets]
         with self._stage("render_fwd"):
-            gs_render_fwd(ps.proj, self.n, ps.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.image, vw.T_final,
+            gs_render_fwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.image, vw.T_final,
                           vw.last, vw.tile_processed if self.record_tiles else None, vw.order)
         with self._stage("loss"):
             gs_loss(vw.image, vw.target, vw.W, vw.H, self.w_l1, self.w_ssim, vw.loss, vw.dL, self.ws_loss)
@@ -348,29 +385,13 @@ class TrainStep:
         self.prepare_view(k)
         self.render_view(k)
 
-    def _bin_sort(self, k, ps):
-        vw = self.views[k]
-        n = self.n
-        try:
-            M = gs_bin_sort(ps.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
-                            ps.capacity, vw.ranges, ps.ws_sort, vw.order)
-        except GSError as e:
-            if e.status != GS_ERR_CAPACITY:
-                raise
-            # grow (once per new high-water mark) and redo the sort
-            ps.alloc(int(min(e.num_pairs * 5 // 4 + 1024, (1 << 31) - 1)))
-            self.pair_capacity = max(self.pair_capacity, ps.capacity)
-            M = gs_bin_sort(ps.proj, n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
-                            ps.capacity, vw.ranges, ps.ws_sort, vw.order)
-        vw.num_pairs = M
-
     def backward_view(self, k, keep_grad2d=False):
         """Raster backward, then (unless keep_grad2d) projection backward."""
         vw = self.views[k]
-        ps = self.sets[k % 2]
+        ps = self.sets[k % self.nsets]
         self._gcur = k % 2
         with self._stage("render_bwd"):
-            gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, vw.num_pairs, vw.W, vw.H, vw.T_final, vw.last,
+            gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
                           vw.dL, self.g2d[k % 2], vw.order)
         if not keep_grad2d:
             self.project_view(k)
@@ -385,11 +406,34 @@ class TrainStep:
         """Every view of the batch, gradients accumulated: view k + 1 is
         prepared on the side stream and view k's projection backward runs on
         the gradient stream while the current stream renders and
-        back-propagates through the rasteriser."""
+        back-propagates through the rasteriser.  Nothing blocks until every
+        view is issued; then the pair counts are read, and a view that
+        overflowed its buffer set makes the whole batch run again with the
+        set grown."""
+        while True:
+            self._issue_views()
+            self._counts_read.synchronize()
+            M = self.M_host.tolist()
+            over = [k for k in range(len(self.views)) if M[k] > self._set_cap[k]]
+            for k, vw in enumerate(self.views):
+                vw.num_pairs = M[k]
+            if not over:
+                return
+            for k in over:
+                ps = self.sets[k % self.nsets]
+                if M[k] > ps.capacity:
+                    ps.alloc(int(min(M[k] * 5 // 4 + 1024, (1 << 31) - 1)))
+                    self.pair_capacity = max(self.pair_capacity, ps.capacity)
+            torch.cuda.current_stream(self.device).synchronize()
+            self.grads.zero_()
+
+    def _issue_views(self):
         main = torch.cuda.current_stream(self.device)
         nv = len(self.views)
         proj_done = [None, None]
-        self.prepare_view(0)
+        self.prepare_view(0, sync=False)
+        first_done = torch.cuda.Event()
+        first_done.record(main)
         for k in range(nv):
             self.render_view(k)
             if proj_done[k % 2] is not None:
@@ -403,17 +447,25 @@ class TrainStep:
                 done = torch.cuda.Event()
                 done.record(self.gstream)
             proj_done[k % 2] = done
-            self._free[k % 2] = raster_done                # set k % 2: its last reader (the projection
+            self._free[k % self.nsets] = raster_done       # the set's last reader (the projection
                                                            # backward reads params, not the set)
             if k + 1 < nv:
                 with torch.cuda.stream(self.side):
-                    prev = self._free[(k + 1) % 2]         # (from an earlier step when k = 0)
+                    if k == 0:
+                        self.side.wait_event(first_done)       # the first view's binning goes first
+                    prev = self._free[(k + 1) % self.nsets]    # (possibly from an earlier step)
                     if prev is not None:
                         self.side.wait_event(prev)
-                    self.prepare_view(k + 1)
+                    self.prepare_view(k + 1, sync=False)
                     ready = torch.cuda.Event()
                     ready.record(self.side)
                 main.wait_event(ready)
+        # pair counts to the host, after the last binning
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(first_done)
+            self.M_host.copy_(self.M_dev, non_blocking=True)
+            self._counts_read = torch.cuda.Event()
+            self._counts_read.record(self.side)
         main.wait_event(proj_done[(nv - 1) % 2])
 
     def adam(self):

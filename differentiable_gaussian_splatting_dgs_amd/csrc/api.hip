@@ -179,8 +179,30 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   if (M > pair_capacity)
     return fail(GS_ERR_CAPACITY, "%lld pairs > capacity %lld", (long long)M, (long long)pair_capacity);
   e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, M, TX, TY, keys, vals, tile_ranges, tile_order,
-                                workspace, pair_capacity, st);
+                                nullptr, workspace, pair_capacity, st);
   return hip_status(e, "gs_bin_sort");
+}
+
+gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                            int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
+                            int64_t* num_pairs_dev, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  CHECK(check_size(width, height));
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(pair_capacity >= 0 && pair_capacity < (int64_t(1) << 31), "pair_capacity out of range");
+  REQUIRE(vis_count != nullptr && num_pairs_dev != nullptr && tile_ranges != nullptr, "NULL argument");
+  REQUIRE(aligned(num_pairs_dev, 8), "misaligned num_pairs_dev");
+  if (n > 0) REQUIRE(proj && vis_idx && aligned(proj, 16), "NULL or misaligned proj / vis_idx");
+  if (pair_capacity > 0) REQUIRE(keys && vals && aligned(keys, 8), "NULL or misaligned keys / vals");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::binsort_ws_bytes(n, pair_capacity), "workspace too small");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
+  hipError_t e = gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, TX, TY, workspace, pair_capacity, st);
+  if (e != hipSuccess) return hip_status(e, "gs_bin_sort_async (depth sort)");
+  e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, -1, TX, TY, keys, vals, tile_ranges, tile_order,
+                                num_pairs_dev, workspace, pair_capacity, st);
+  return hip_status(e, "gs_bin_sort_async");
 }
 
 gs_status gs_render_fwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,

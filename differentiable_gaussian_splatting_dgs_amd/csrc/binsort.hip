@@ -217,8 +217,8 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
 // row.  Each run of one tile in the block's sorted items also extends the
 // tile's range ([min start, max end) by atomics on a range array holding
 // (UINT_MAX, 0) beforehand).
-__global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict__ pin, int64_t count,
-                                                     const uint32_t* __restrict__ H,
+__global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict__ pin, const int64_t* count_dev,
+                                                     int64_t count_host, const uint32_t* __restrict__ H,
                                                      const uint32_t* __restrict__ rowtot, int nb,
                                                      const uint32_t* __restrict__ col_tot, int32_t tiles_x,
                                                      uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
@@ -227,6 +227,7 @@ __global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict_
   __shared__ uint32_t s_col[256];
   __shared__ uint64_t s_p[kRB];
   __shared__ uint8_t s_c[kRB];
+  const int64_t count = count_of(count_dev, count_host);
   const int64_t bbase = int64_t(blockIdx.x) * kRB;
   if (bbase >= count) return;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
@@ -372,13 +373,15 @@ __global__ __launch_bounds__(1024) void k_scan_sums(int64_t* __restrict__ sums, 
 __global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
                                                    const int64_t* __restrict__ vis_count,
                                                    const int64_t* __restrict__ block_offsets, int32_t tiles_x,
-                                                   uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+                                                   const int64_t* __restrict__ m_eff, uint64_t* __restrict__ keys,
+                                                   uint32_t* __restrict__ vals) {
   __shared__ int64_t sh[kDT / 64];
   __shared__ uint32_t s_off[kDB];        // exclusive pair offset within the block
   __shared__ uint32_t s_rx[kDB];         // x0 | width << 16
   __shared__ uint32_t s_y0[kDB];
   __shared__ uint32_t s_dep[kDB];
   __shared__ uint32_t s_g[kDB];
+  if (m_eff != nullptr && *m_eff == 0) return;        // no pairs, or more than the buffers hold
   const int64_t V = *vis_count;
   const int64_t r0 = int64_t(blockIdx.x) * kDB;
   const int t = threadIdx.x;
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(kDT) void k_dup_col(const float4* __restrict__ proj
                                                  const int64_t* __restrict__ vis_count,
                                                  const uint32_t* __restrict__ colcnt,
                                                  const uint32_t* __restrict__ coltot, int nbv, int tiles_x,
-                                                 uint64_t* __restrict__ out) {
+                                                 const int64_t* __restrict__ m_eff, uint64_t* __restrict__ out) {
   __shared__ int64_t sh[kDT / 64];
   __shared__ uint32_t s_off[kDB];        // exclusive pair offset within the block
   __shared__ uint32_t s_rx[kDB];         // x0 | width << 16
@@ -499,6 +502,7 @@ __global__ __launch_bounds__(kDT) void k_dup_col(const float4* __restrict__ proj
   __shared__ RankSmem sm;
   __shared__ uint64_t s_p[kDT * kPI];
   __shared__ uint8_t s_d[kDT * kPI];
+  if (m_eff != nullptr && *m_eff == 0) return;        // no pairs, or more than the buffers hold
   const int64_t V = *vis_count;
   const int64_t r0 = int64_t(blockIdx.x) * kDB;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
@@ -576,13 +580,26 @@ __global__ __launch_bounds__(kDT) void k_dup_col(const float4* __restrict__ proj
   }
 }
 
+// The pair count the second half of the binning works with: M, or 0 when
+// M exceeds the capacity (nothing is then written but empty ranges).
+// Also copies M to the caller's device slot m_out (if any).
+__global__ __launch_bounds__(64) void k_eff_count(const int64_t* __restrict__ m_dev, int64_t cap,
+                                                  int64_t* __restrict__ m_eff, int64_t* __restrict__ m_out) {
+  if (threadIdx.x == 0) {
+    const int64_t M = *m_dev;
+    *m_eff = M <= cap ? M : 0;
+    if (m_out != nullptr) *m_out = M;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) p[i] = v;
 }
 
-__global__ __launch_bounds__(256) void k_ranges(const uint64_t* __restrict__ keys, int64_t M,
-                                                uint32_t* __restrict__ ranges) {
+__global__ __launch_bounds__(256) void k_ranges(const uint64_t* __restrict__ keys, const int64_t* count_dev,
+                                                int64_t count_host, uint32_t* __restrict__ ranges) {
+  const int64_t M = count_of(count_dev, count_host);
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= M) return;
   const uint32_t t = uint32_t(keys[i] >> 32);
@@ -658,6 +675,7 @@ struct Ws {
   uint32_t* coltot;                  // [256], pairs per tile column
   int64_t* bsums;                    // per-block tile sums [nbv + 1]
   int64_t* m_dev;                    // pair count
+  int64_t* m_eff;                    // pair count if within capacity, else 0
   uint32_t* colcnt;                  // [kMaxT][nbv + 1], pairs per (column, block), then scanned
   uint64_t* pk;                      // pair keys scratch [cap]
   uint32_t* pv;                      // pair values scratch [cap]
@@ -683,6 +701,7 @@ Ws carve(void* ws, int64_t n, int64_t cap, size_t* bytes = nullptr) {
   w.coltot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
   w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t(nbv + 1)));
   w.m_dev = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
+  w.m_eff = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.colcnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kMaxT * size_t(nbv + 1)));
   w.pk = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * size_t(cap)));
   w.pv = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(cap)));
@@ -745,26 +764,39 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
   return hipGetLastError();
 }
 
+// Second half.  M_host >= 0: the pair count read by the caller (<= the
+// capacity).  M_host < 0: the count stays on the device (nothing blocks);
+// grids are sized for the capacity and every kernel reads the effective
+// count (0 when M exceeds the capacity: then only empty ranges are written).
 hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx,
-                                 const int64_t* vis_count, int64_t M, int32_t tiles_x, int32_t tiles_y,
+                                 const int64_t* vis_count, int64_t M_host, int32_t tiles_x, int32_t tiles_y,
                                  uint64_t* keys, int32_t* vals, uint32_t* ranges, uint32_t* tile_order,
-                                 void* ws, int64_t pair_capacity, hipStream_t st) {
+                                 int64_t* num_pairs_dev, void* ws, int64_t pair_capacity, hipStream_t st) {
   (void)vis_idx;
   Ws w = carve(ws, n, pair_capacity);
   const float4* P = reinterpret_cast<const float4*>(proj);
   const int64_t T = int64_t(tiles_x) * tiles_y;
   uint32_t* uvals = reinterpret_cast<uint32_t*>(vals);
   const int nbv = int(dup_blocks(n));
-  if (M == 0) {
+  const bool on_device = M_host < 0;
+  const int64_t* m_dev = nullptr;
+  int64_t bound = M_host;                       // upper bound of the count, for grid sizes
+  if (on_device) {
+    k_eff_count<<<1, 64, 0, st>>>(w.m_dev, pair_capacity, w.m_eff, num_pairs_dev);
+    m_dev = w.m_eff;
+    bound = pair_capacity;
+  }
+  if (!on_device && M_host == 0) {
     k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
   } else if (exact_path(n, tiles_x, tiles_y)) {
     // pairs straight into tile-column order, then a stable pass on the row
-    const int nb = int(std::max<int64_t>(1, nblocks(M)));
-    k_dup_col<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.colcnt, w.coltot, nbv, tiles_x, w.pk);
-    k_upsweep<uint64_t><<<nb, kRT, 0, st>>>(w.pk, nullptr, M, 56, w.H, nb);
+    const int nb = int(std::max<int64_t>(1, nblocks(bound)));
+    if (nbv > 0) k_dup_col<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.colcnt, w.coltot, nbv, tiles_x, m_dev, w.pk);
+    k_upsweep<uint64_t><<<nb, kRT, 0, st>>>(w.pk, m_dev, M_host, 56, w.H, nb);
     k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
     k_init_ranges<<<unsigned((T + 255) / 256), 256, 0, st>>>(ranges, int(T));
-    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, M, w.H, w.rowtot, nb, w.coltot, tiles_x, keys, uvals, ranges);
+    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, m_dev, M_host, w.H, w.rowtot, nb, w.coltot, tiles_x, keys, uvals,
+                                      ranges);
     k_fix_ranges<<<unsigned((T + 255) / 256), 256, 0, st>>>(ranges, int(T));
   } else {
     // number of 8-bit passes over the tile bits
@@ -775,14 +807,15 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     uint64_t* bufk[2] = {keys, w.pk};
     uint32_t* bufv[2] = {uvals, w.pv};
     int cur = (passes & 1) ? 1 : 0;
-    k_duplicate<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, bufk[cur], bufv[cur]);
+    if (nbv > 0)
+      k_duplicate<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, m_dev, bufk[cur], bufv[cur]);
     for (int pass = 0; pass < passes; ++pass) {
-      radix_pass<uint64_t>(bufk[cur], bufv[cur], bufk[cur ^ 1], bufv[cur ^ 1], nullptr, M, M, 32 + 8 * pass, w,
-                           st);
+      radix_pass<uint64_t>(bufk[cur], bufv[cur], bufk[cur ^ 1], bufv[cur ^ 1], m_dev, M_host, bound,
+                           32 + 8 * pass, w, st);
       cur ^= 1;
     }
     k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
-    k_ranges<<<unsigned((M + 255) / 256), 256, 0, st>>>(keys, M, ranges);
+    k_ranges<<<unsigned((std::max<int64_t>(bound, 1) + 255) / 256), 256, 0, st>>>(keys, m_dev, M_host, ranges);
   }
   if (tile_order != nullptr) k_tile_order<<<1, 1024, 0, st>>>(ranges, int(T), tile_order);
   return hipGetLastError();

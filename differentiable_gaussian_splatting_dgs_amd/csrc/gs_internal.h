@@ -46,10 +46,10 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
 int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity);
 // Stage 2 (after M is known on the host): duplication, tile radix sort,
 // tile ranges.
-hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx,
-                                 const int64_t* vis_count, int64_t M, int32_t tiles_x, int32_t tiles_y,
-                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, uint32_t* tile_order,
-                                 void* ws, int64_t pair_capacity, hipStream_t st);
+hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                                 int64_t M_host, int32_t tiles_x, int32_t tiles_y, uint64_t* keys, int32_t* vals,
+                                 uint32_t* ranges, uint32_t* tile_order, int64_t* num_pairs_dev, void* ws,
+                                 int64_t pair_capacity, hipStream_t st);
 
 // --- rasteriser (raster_fwd.hip / raster_bwd.hip) ---------------------------
 hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint32_t* ranges,

@@ -152,6 +152,19 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
                       int64_t* num_pairs, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* gs_bin_sort without the blocking read: the same outputs, with M written to
+ * the device (same passages).
+ *   num_pairs_dev  device out, 8-byte aligned: M, valid in stream order
+ * Nothing blocks.  If M > pair_capacity: *num_pairs_dev = M, keys and vals
+ * are not written, every tile range is [0, 0) (and tile_order a valid order
+ * of those empty tiles); the caller detects this by comparing
+ * *num_pairs_dev with pair_capacity once the stream has reached it.  The
+ * rasterisers take pair_capacity as their num_pairs bound then. */
+gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                            int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
+                            int64_t* num_pairs_dev, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Front-to-back alpha compositing per 16x16 tile (Grendel-GS notes,
  * training pipeline: "alpha compositing").  Per pixel, over its tile's
  * pairs in order: power as in GS_PROJ_WORDS; skip if power > 0;

@@ -81,6 +81,13 @@ def test_invalid_arguments_rejected_on_host():
                            None, P(256), 1 << 30, None) == 1
     assert lib.gs_bin_sort(P(16), -1, P(16), P(16), 8, 8, P(16), P(16), 10, C.byref(m), P(16), None, P(256),
                            1 << 30, None) == 1
+    # asynchronous bin sort: NULL or misaligned device count, negative n
+    assert lib.gs_bin_sort_async(P(16), 1, P(16), P(16), 8, 8, P(16), P(16), 10, None, P(16), None, P(256),
+                                 1 << 30, None) == 1
+    assert lib.gs_bin_sort_async(P(16), 1, P(16), P(16), 8, 8, P(16), P(16), 10, P(12), P(16), None, P(256),
+                                 1 << 30, None) == 1
+    assert lib.gs_bin_sort_async(P(16), -1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None, P(256),
+                                 1 << 30, None) == 1
     # adam: zero bias correction
     assert lib.gs_sparse_adam(P(16), P(16), P(16), P(16), 4, 4, P(16), P(16), P(16), C.c_float(1e-3),
                               C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.0), C.c_float(0.1),

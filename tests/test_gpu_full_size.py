@@ -5,7 +5,7 @@
   cases in test_gpu_parity (every key, value, range, pixel and gradient).
 * capacity (12,000,000 Gaussians, 16 views of 1920x1080 per step), run as
   bench.py runs a step (views overlapped on three streams): for the last two
-  views, which the step leaves in its two buffer sets, the projection and
+  views, which the step leaves in its last buffer sets, the projection and
   visible list against the oracle's preprocess, the sorted pair array
   checked against its definition from those projections (every visible
   Gaussian's rectangle tiles exactly once, ordered by tile, depth bits,
@@ -94,7 +94,7 @@ def test_capacity_full_size_pipelined_step_sampled():
     rng = np.random.default_rng(4)
     for k in (nv - 2, nv - 1):
         cam = work.cameras[k]
-        ps, vw = step.sets[k % 2], step.views[k]
+        ps, vw = step.sets[k % step.nsets], step.views[k]
         M = vw.num_pairs
         V = int(step.vis_count[k].item())
         say(f"[capacity full] view {k}: V={V} M={M}")
