@@ -29,7 +29,7 @@ TILE = 16
 
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
            "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
-           "gs_sparse_adam"]
+           "gs_sparse_adam", "gs_project_bwd_adam"]
 
 
 class gs_camera(C.Structure):
@@ -69,6 +69,8 @@ def lib():
     L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
+    L.gs_project_bwd_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _f32,
+                                      _f32, _f32, _f32, _f32, _f32, _P, _sz, _P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = C.c_int
     _handle = L
@@ -202,6 +204,15 @@ def gs_sparse_adam(params, grads, m, v, n, ld, union_flags, union_idx, union_cou
                                _ptr(union_idx), _ptr(union_count), float(lr), float(beta1), float(beta2),
                                float(eps), float(bias_c1), float(bias_c2), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "gs_sparse_adam")
+
+
+def gs_project_bwd_adam(params, grads, m, v, n, ld, cam, proj, grad2d, union_flags, union_idx, union_count, lr,
+                        beta1, beta2, eps, bias_c1, bias_c2, workspace, stream=None):
+    _check(lib().gs_project_bwd_adam(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, C.byref(cam), _ptr(proj),
+                                     _ptr(grad2d), _ptr(union_flags), _ptr(union_idx), _ptr(union_count), lr, beta1,
+                                     beta2, eps, bias_c1, bias_c2, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gs_project_bwd_adam")
 
 
 # ---------------------------------------------------------------------------
@@ -402,16 +413,17 @@ class TrainStep:
             gs_project_bwd(self.params, self.n, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1],
                            self.g2d[k % 2], self.grads)
 
-    def run_views(self):
+    def run_views(self, defer_last_projection=False):
         """Every view of the batch, gradients accumulated: view k + 1 is
         prepared on the side stream and view k's projection backward runs on
         the gradient stream while the current stream renders and
         back-propagates through the rasteriser.  Nothing blocks until every
         view is issued; then the pair counts are read, and a view that
         overflowed its buffer set makes the whole batch run again with the
-        set grown."""
+        set grown.  With defer_last_projection the last view's screen-space
+        gradients are left for adam(fused=True)."""
         while True:
-            self._issue_views()
+            self._issue_views(defer_last_projection)
             self._counts_read.synchronize()
             M = self.M_host.tolist()
             over = [k for k in range(len(self.views)) if M[k] > self._set_cap[k]]
@@ -426,8 +438,10 @@ class TrainStep:
                     self.pair_capacity = max(self.pair_capacity, ps.capacity)
             torch.cuda.current_stream(self.device).synchronize()
             self.grads.zero_()
+            for g2 in self.g2d:
+                g2.zero_()
 
-    def _issue_views(self):
+    def _issue_views(self, defer_last):
         main = torch.cuda.current_stream(self.device)
         nv = len(self.views)
         proj_done = [None, None]
@@ -441,12 +455,13 @@ class TrainStep:
             self.backward_view(k, keep_grad2d=True)
             raster_done = torch.cuda.Event()
             raster_done.record(main)
-            with torch.cuda.stream(self.gstream):
-                self.gstream.wait_event(raster_done)
-                self.project_view(k)
-                done = torch.cuda.Event()
-                done.record(self.gstream)
-            proj_done[k % 2] = done
+            if not (defer_last and k == nv - 1):
+                with torch.cuda.stream(self.gstream):
+                    self.gstream.wait_event(raster_done)
+                    self.project_view(k)
+                    done = torch.cuda.Event()
+                    done.record(self.gstream)
+                proj_done[k % 2] = done
             self._free[k % self.nsets] = raster_done       # the set's last reader (the projection
                                                            # backward reads params, not the set)
             if k + 1 < nv:
@@ -466,22 +481,36 @@ class TrainStep:
             self.M_host.copy_(self.M_dev, non_blocking=True)
             self._counts_read = torch.cuda.Event()
             self._counts_read.record(self.side)
-        main.wait_event(proj_done[(nv - 1) % 2])
+        # every projection backward issued is done before the optimiser
+        for ev in proj_done:
+            if ev is not None:
+                main.wait_event(ev)
 
-    def adam(self):
+    def adam(self, fused=False):
+        """Sparse Adam over the union; with fused, the last view's
+        projection backward (left by run_views(defer_last_projection=True))
+        runs in the same pass."""
         self.t += 1
         bc1 = 1.0 - self.beta1 ** self.t
         bc2 = 1.0 - self.beta2 ** self.t
         with self._stage("sparse_adam"):
-            gs_sparse_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.union_flags,
-                           self.union_idx, self.union_count, self.lr, self.beta1, self.beta2, self.eps, bc1,
-                           bc2, self.ws_adam)
+            if fused:
+                k = len(self.views) - 1
+                gs_project_bwd_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.views[k].cam,
+                                    self.sets[k % self.nsets].proj, self.g2d[k % 2], self.union_flags,
+                                    self.union_idx, self.union_count, self.lr, self.beta1, self.beta2, self.eps,
+                                    bc1, bc2, self.ws_adam)
+            else:
+                gs_sparse_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.union_flags,
+                               self.union_idx, self.union_count, self.lr, self.beta1, self.beta2, self.eps, bc1,
+                               bc2, self.ws_adam)
 
     def step(self):
         """One training step: for each view preprocess, bin/sort, render,
-        loss, backward (gradients accumulate); then sparse Adam."""
-        self.run_views()
-        self.adam()
+        loss, backward (gradients accumulate); then sparse Adam, fused with
+        the last view's projection backward."""
+        self.run_views(defer_last_projection=True)
+        self.adam(fused=True)
 
 
 def from_workload(work, device="cuda", **kw) -> TrainStep:

@@ -287,4 +287,30 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
   return hip_status(e, "gs_sparse_adam");
 }
 
+gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
+                             const gs_camera* cam, const float* proj, float* grad2d, uint8_t* union_flags,
+                             int32_t* union_idx, int64_t* union_count, float lr, float beta1, float beta2, float eps,
+                             float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream) {
+  gs::CamArgs c;
+  CHECK(check_camera(cam, c));
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(ld >= n, "ld < n");
+  REQUIRE(union_count != nullptr, "union_count is NULL");
+  if (n > 0) {
+    REQUIRE(params && grads && m && v && proj && grad2d && union_flags && union_idx, "NULL array");
+    REQUIRE(aligned(union_flags, 16) && aligned(proj, 16) && aligned(grad2d, 16),
+            "union_flags / proj / grad2d not 16-byte aligned");
+  }
+  REQUIRE(std::isfinite(lr) && std::isfinite(beta1) && std::isfinite(beta2) && std::isfinite(eps), "non-finite scalar");
+  REQUIRE(bias_c1 > 0.0f && bias_c2 > 0.0f, "bias corrections must be > 0");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= adam_ws_bytes(n), "workspace too small");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = gs::launch_compact(union_flags, n, union_idx, union_count, true, workspace, st);
+  if (e == hipSuccess)
+    e = gs::launch_project_adam(params, grads, m, v, n, ld, c, proj, grad2d, union_idx, union_count, lr, beta1, beta2,
+                                eps, bias_c1, bias_c2, st);
+  return hip_status(e, "gs_project_bwd_adam");
+}
+
 }  // extern "C"

@@ -252,6 +252,22 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
                          float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* gs_project_bwd of the batch's last view followed by gs_sparse_adam, in one
+ * pass over the union rows (same passages as the two): the last view's
+ * parameter gradients are added to the accumulated ones in registers and
+ * consumed by the update at once, so the gradient planes are not written and
+ * read back in between.  Results equal the two calls in sequence.
+ *   cam, proj, grad2d   the last view's camera, its gs_preprocess records (a
+ *                       row with a non-zero tile count is one it saw) and
+ *                       its gs_render_bwd screen-space gradients (consumed
+ *                       rows re-zeroed)
+ *   the other arguments as gs_sparse_adam (grads: the earlier views'
+ *   accumulated gradients; zeroed for the listed rows). */
+gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
+                              const gs_camera* cam, const float* proj, float* grad2d, uint8_t* union_flags,
+                              int32_t* union_idx, int64_t* union_count, float lr, float beta1, float beta2, float eps,
+                              float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,6 +162,28 @@ def test_pipelined_step_matches_oracle(case):
         assert torch.equal(a.ranges, b.ranges), f"{case}/v{k} second-step ranges"
 
 
+@pytest.mark.parametrize("case", ["mid_cut", "small_cut"])
+def test_fused_step_matches_oracle(case):
+    """TrainStep.step() as bench.py runs it: the last view's projection
+    backward fused into the Adam pass.  The update against the oracle's
+    gradients (as check_adam), screen-space buffers left zero."""
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    work = workload_case(case)
+    p0 = work.params.copy()
+    ref = oracle.step(work, dl_tol=DL_TOL)
+    step = gs.from_workload(work, record_tiles=True)
+    step.step()
+    torch.cuda.synchronize()
+    U = int(step.union_count.item())
+    res = dict(params=step.params.cpu().numpy(), m=step.m.cpu().numpy(), v=step.v.cpu().numpy(),
+               union=step.union_idx[:U].cpu().numpy().copy(), grads_after=step.grads.cpu().numpy(),
+               union_flags=step.union_flags[: step.n].cpu().numpy().copy())
+    tol_g = 1e-3 * np.abs(ref["grads"]) + 1e-4 * ref["mags"] + ref["mags_dl"]
+    check_adam(res, ref, work, p0, tol_g)
+    for g2 in step.g2d:
+        assert not g2.any().item(), "screen-space gradients not re-zeroed"
+
+
 def test_pipelined_step_grows_an_overflowing_pair_buffer():
     """A pair capacity far below M: the non-blocking binning leaves empty
     ranges, the step sees the counts before Adam, grows the buffers and runs
