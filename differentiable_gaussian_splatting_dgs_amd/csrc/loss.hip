@@ -3,8 +3,11 @@
 // SSIM per channel with an 11x11 Gaussian window (sigma 1.5, zero-padded
 // "same" correlation), C1 = 0.01^2, C2 = 0.03^2, and dL/dI.
 //
-// The window is separable, so both kernels stage a 32x8 output tile plus a
-// 5-pixel halo in LDS and run a horizontal then a vertical 11-tap pass.
+// The window is separable.  Both SSIM kernels work on one channel of a
+// 32x16 output tile per block (a 5-pixel halo staged in LDS) and run a
+// horizontal then a vertical 11-tap pass, each thread computing a short run
+// of neighbouring outputs (four across, two down) from a sliding window
+// held in registers.
 //   k_ssim_fwd: five local moments (mu_x, mu_y, E[x^2], E[y^2], E[xy]) ->
 //     per-pixel SSIM and its partials wrt (mu_x, E[x^2], E[xy]); per-block
 //     sums of SSIM and |x - y|.
@@ -19,8 +22,12 @@
 namespace gs {
 namespace {
 
-constexpr int kLX = 32, kLY = 8, kHalo = 5;
-constexpr int kSX = kLX + 2 * kHalo, kSY = kLY + 2 * kHalo;   // 42 x 18 staged
+constexpr int kLX = 32, kLY = 16, kHalo = 5;
+constexpr int kSX = kLX + 2 * kHalo, kSY = kLY + 2 * kHalo;   // 42 x 26 staged
+constexpr int kSXP = kSX + 2;                                    // row stride: 16-byte rows
+constexpr int kHP = kLX + 1;                                     // horizontal-pass row stride (banks)
+constexpr int kRun = 4;                                          // horizontal outputs per thread
+constexpr int kRunV = 2;                                         // vertical outputs per thread
 constexpr float kC1 = 0.0001f, kC2 = 0.0009f;
 
 __device__ __forceinline__ float block_sum(float v, float* sh) {
@@ -34,55 +41,101 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
   return s;
 }
 
+// 11-tap window of a run of R outputs: out[o] = sum_j g[j] in[o + j].
+template <int R>
+__device__ __forceinline__ void taps(const SsimWindow& win, const float (&in)[R + 10], float (&out)[R]) {
+#pragma unroll
+  for (int o = 0; o < R; ++o) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 11; ++j) a = fmaf(win.g[j], in[o + j], a);
+    out[o] = a;
+  }
+}
+
+// The kRun + 10 inputs of a horizontal run, as 16-byte LDS reads (the
+// run's start is 16-byte aligned; neighbouring threads' runs are 16 bytes
+// apart, so the reads are conflict-free).
+__device__ __forceinline__ void load_run(const float* src, float (&in)[kRun + 10]) {
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+  for (int k = 0; k < (kRun + 10 + 3) / 4; ++k) {
+    const float4 q = s4[k];
+    const float e[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (4 * k + c < kRun + 10) in[4 * k + c] = e[c];
+  }
+}
+
+// grid (tiles x, tiles y, channel)
 __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img, const float* __restrict__ tgt, int W,
                                                   int H, SsimWindow win, float* __restrict__ maps,
                                                   float* __restrict__ partial) {
-  __shared__ float sx[kSY][kSX], sy[kSY][kSX];
-  __shared__ float h[5][kSY][kLX];
+  __shared__ __align__(16) float sx[kSY][kSXP];
+  __shared__ __align__(16) float sy[kSY][kSXP];
+  __shared__ float h[5][kSY][kHP];
   __shared__ float sh[4];
-  const int t = threadIdx.x, lx = t & 31, ly = t >> 5;
-  const int ox = blockIdx.x * kLX, oy = blockIdx.y * kLY;
-  const int x = ox + lx, y = oy + ly;
-  const bool inside = x < W && y < H;
+  const int t = threadIdx.x;
+  const int ox = blockIdx.x * kLX, oy = blockIdx.y * kLY, ch = blockIdx.z;
   const size_t P = size_t(W) * H;
+  const float* I = img + ch * P;
+  const float* J = tgt + ch * P;
+  for (int k = t; k < kSX * kSY; k += 256) {
+    const int r = k / kSX, q = k % kSX;
+    const int gx = ox + q - kHalo, gy = oy + r - kHalo;
+    const bool in = gx >= 0 && gx < W && gy >= 0 && gy < H;
+    sx[r][q] = in ? I[size_t(gy) * W + gx] : 0.0f;
+    sy[r][q] = in ? J[size_t(gy) * W + gx] : 0.0f;
+  }
+  __syncthreads();
+  // horizontal: row r, columns c0 .. c0 + 3 of the five moment maps
+  for (int task = t; task < kSY * (kLX / kRun); task += 256) {
+    const int r = task / (kLX / kRun), c0 = (task % (kLX / kRun)) * kRun;
+    float u[kRun + 10], v[kRun + 10], p[kRun + 10], o[kRun];
+    load_run(&sx[r][c0], u);
+    load_run(&sy[r][c0], v);
+    taps<kRun>(win, u, o);
+#pragma unroll
+    for (int q = 0; q < kRun; ++q) h[0][r][c0 + q] = o[q];
+    taps<kRun>(win, v, o);
+#pragma unroll
+    for (int q = 0; q < kRun; ++q) h[1][r][c0 + q] = o[q];
+#pragma unroll
+    for (int i = 0; i < kRun + 10; ++i) p[i] = u[i] * u[i];
+    taps<kRun>(win, p, o);
+#pragma unroll
+    for (int q = 0; q < kRun; ++q) h[2][r][c0 + q] = o[q];
+#pragma unroll
+    for (int i = 0; i < kRun + 10; ++i) p[i] = v[i] * v[i];
+    taps<kRun>(win, p, o);
+#pragma unroll
+    for (int q = 0; q < kRun; ++q) h[3][r][c0 + q] = o[q];
+#pragma unroll
+    for (int i = 0; i < kRun + 10; ++i) p[i] = u[i] * v[i];
+    taps<kRun>(win, p, o);
+#pragma unroll
+    for (int q = 0; q < kRun; ++q) h[4][r][c0 + q] = o[q];
+  }
+  __syncthreads();
+  // vertical: column x, rows r0 .. r0 + 3
   float ssum = 0.0f, lsum = 0.0f;
-  for (int ch = 0; ch < 3; ++ch) {
-    const float* I = img + ch * P;
-    const float* J = tgt + ch * P;
-    for (int k = t; k < kSX * kSY; k += 256) {
-      const int r = k / kSX, q = k % kSX;
-      const int gx = ox + q - kHalo, gy = oy + r - kHalo;
-      const bool in = gx >= 0 && gx < W && gy >= 0 && gy < H;
-      sx[r][q] = in ? I[size_t(gy) * W + gx] : 0.0f;
-      sy[r][q] = in ? J[size_t(gy) * W + gx] : 0.0f;
-    }
-    __syncthreads();
-    for (int k = t; k < kSY * kLX; k += 256) {
-      const int r = k / kLX, q = k % kLX;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
+  {
+    const int lx = t % kLX, r0 = (t / kLX) * kRunV;
+    float m[5][kRunV];
 #pragma unroll
-      for (int j = 0; j < 11; ++j) {
-        const float u = sx[r][q + j], v = sy[r][q + j], gj = win.g[j];
-        a0 = fmaf(gj, u, a0);
-        a1 = fmaf(gj, v, a1);
-        a2 = fmaf(gj, u * u, a2);
-        a3 = fmaf(gj, v * v, a3);
-        a4 = fmaf(gj, u * v, a4);
-      }
-      h[0][r][q] = a0; h[1][r][q] = a1; h[2][r][q] = a2; h[3][r][q] = a3; h[4][r][q] = a4;
-    }
-    __syncthreads();
-    float mx = 0.f, my = 0.f, exx = 0.f, eyy = 0.f, exy = 0.f;
+    for (int k = 0; k < 5; ++k) {
+      float col[kRunV + 10];
 #pragma unroll
-    for (int i = 0; i < 11; ++i) {
-      const float gi = win.g[i];
-      mx = fmaf(gi, h[0][ly + i][lx], mx);
-      my = fmaf(gi, h[1][ly + i][lx], my);
-      exx = fmaf(gi, h[2][ly + i][lx], exx);
-      eyy = fmaf(gi, h[3][ly + i][lx], eyy);
-      exy = fmaf(gi, h[4][ly + i][lx], exy);
+      for (int i = 0; i < kRunV + 10; ++i) col[i] = h[k][r0 + i][lx];
+      taps<kRunV>(win, col, m[k]);
     }
-    if (inside) {
+    const int x = ox + lx;
+#pragma unroll
+    for (int q = 0; q < kRunV; ++q) {
+      const int y = oy + r0 + q;
+      if (x >= W || y >= H) continue;
+      const float mx = m[0][q], my = m[1][q], exx = m[2][q], eyy = m[3][q], exy = m[4][q];
       const float vx = exx - mx * mx, vy = eyy - my * my, cxy = exy - mx * my;
       const float A1 = 2.0f * mx * my + kC1, A2 = 2.0f * cxy + kC2;
       const float B1 = mx * mx + my * my + kC1, B2 = vx + vy + kC2;
@@ -93,69 +146,68 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
       maps[(3 * ch + 1) * P + pix] = -S / B2;
       maps[(3 * ch + 2) * P + pix] = 2.0f * A1 * iD;
       ssum += S;
-      lsum += fabsf(sx[ly + kHalo][lx + kHalo] - sy[ly + kHalo][lx + kHalo]);
+      lsum += fabsf(sx[r0 + q + kHalo][lx + kHalo] - sy[r0 + q + kHalo][lx + kHalo]);
     }
-    __syncthreads();
   }
   const float s = block_sum(ssum, sh);
   const float l = block_sum(lsum, sh);
   if (t == 0) {
-    const size_t b = size_t(blockIdx.y) * gridDim.x + blockIdx.x;
+    const size_t b = (size_t(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
     partial[2 * b] = l;
     partial[2 * b + 1] = s;
   }
 }
 
+// grid (tiles x, tiles y, channel)
 __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img, const float* __restrict__ tgt, int W,
                                                   int H, SsimWindow win, const float* __restrict__ maps, float w_l1,
                                                   float w_ssim, float* __restrict__ dL) {
-  __shared__ float sm[3][kSY][kSX];
-  __shared__ float h[3][kSY][kLX];
-  const int t = threadIdx.x, lx = t & 31, ly = t >> 5;
-  const int ox = blockIdx.x * kLX, oy = blockIdx.y * kLY;
-  const int x = ox + lx, y = oy + ly;
-  const bool inside = x < W && y < H;
+  __shared__ __align__(16) float sm[3][kSY][kSXP];
+  __shared__ float h[3][kSY][kHP];
+  const int t = threadIdx.x;
+  const int ox = blockIdx.x * kLX, oy = blockIdx.y * kLY, ch = blockIdx.z;
   const size_t P = size_t(W) * H;
   const float inv = 1.0f / (3.0f * float(P));
-  for (int ch = 0; ch < 3; ++ch) {
-    for (int k = t; k < kSX * kSY; k += 256) {
-      const int r = k / kSX, q = k % kSX;
-      const int gx = ox + q - kHalo, gy = oy + r - kHalo;
-      const bool in = gx >= 0 && gx < W && gy >= 0 && gy < H;
-      const size_t pix = size_t(gy) * W + gx;
+  for (int k = t; k < kSX * kSY; k += 256) {
+    const int r = k / kSX, q = k % kSX;
+    const int gx = ox + q - kHalo, gy = oy + r - kHalo;
+    const bool in = gx >= 0 && gx < W && gy >= 0 && gy < H;
+    const size_t pix = size_t(gy) * W + gx;
 #pragma unroll
-      for (int m = 0; m < 3; ++m) sm[m][r][q] = in ? maps[(3 * ch + m) * P + pix] : 0.0f;
-    }
-    __syncthreads();
-    for (int k = t; k < kSY * kLX; k += 256) {
-      const int r = k / kLX, q = k % kLX;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+    for (int m = 0; m < 3; ++m) sm[m][r][q] = in ? maps[(3 * ch + m) * P + pix] : 0.0f;
+  }
+  __syncthreads();
+  for (int task = t; task < kSY * (kLX / kRun); task += 256) {
+    const int r = task / (kLX / kRun), c0 = (task % (kLX / kRun)) * kRun;
 #pragma unroll
-      for (int j = 0; j < 11; ++j) {
-        const float gj = win.g[j];
-        a0 = fmaf(gj, sm[0][r][q + j], a0);
-        a1 = fmaf(gj, sm[1][r][q + j], a1);
-        a2 = fmaf(gj, sm[2][r][q + j], a2);
-      }
-      h[0][r][q] = a0; h[1][r][q] = a1; h[2][r][q] = a2;
-    }
-    __syncthreads();
-    if (inside) {
-      float b0 = 0.f, b1 = 0.f, b2 = 0.f;
+    for (int m = 0; m < 3; ++m) {
+      float in[kRun + 10], o[kRun];
+      load_run(&sm[m][r][c0], in);
+      taps<kRun>(win, in, o);
 #pragma unroll
-      for (int i = 0; i < 11; ++i) {
-        const float gi = win.g[i];
-        b0 = fmaf(gi, h[0][ly + i][lx], b0);
-        b1 = fmaf(gi, h[1][ly + i][lx], b1);
-        b2 = fmaf(gi, h[2][ly + i][lx], b2);
-      }
-      const size_t pix = size_t(y) * W + x;
-      const float xv = img[ch * P + pix], yv = tgt[ch * P + pix];
-      const float d = xv - yv;
-      const float sg = d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f);
-      dL[ch * P + pix] = w_l1 * inv * sg - w_ssim * inv * (b0 + 2.0f * xv * b1 + yv * b2);
+      for (int q = 0; q < kRun; ++q) h[m][r][c0 + q] = o[q];
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  const int lx = t % kLX, r0 = (t / kLX) * kRunV;
+  float b[3][kRunV];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    float col[kRunV + 10];
+#pragma unroll
+    for (int i = 0; i < kRunV + 10; ++i) col[i] = h[m][r0 + i][lx];
+    taps<kRunV>(win, col, b[m]);
+  }
+  const int x = ox + lx;
+#pragma unroll
+  for (int q = 0; q < kRunV; ++q) {
+    const int y = oy + r0 + q;
+    if (x >= W || y >= H) continue;
+    const size_t pix = size_t(y) * W + x;
+    const float xv = img[ch * P + pix], yv = tgt[ch * P + pix];
+    const float d = xv - yv;
+    const float sg = d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f);
+    dL[ch * P + pix] = w_l1 * inv * sg - w_ssim * inv * (b[0][q] + 2.0f * xv * b[1][q] + yv * b[2][q]);
   }
 }
 
@@ -206,7 +258,7 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
 }
 
 inline int64_t ssim_blocks(int32_t W, int32_t H) {
-  return int64_t((W + kLX - 1) / kLX) * ((H + kLY - 1) / kLY);
+  return 3 * int64_t((W + kLX - 1) / kLX) * ((H + kLY - 1) / kLY);
 }
 
 }  // namespace
@@ -225,7 +277,7 @@ hipError_t launch_loss(const float* image, const float* target, int32_t width, i
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(sizeof(float) * 9 * size_t(P), 256));
   const float inv3p = float(1.0 / (3.0 * double(P)));
   if (w_ssim != 0.0f) {
-    const dim3 grid(unsigned((width + kLX - 1) / kLX), unsigned((height + kLY - 1) / kLY));
+    const dim3 grid(unsigned((width + kLX - 1) / kLX), unsigned((height + kLY - 1) / kLY), 3u);
     k_ssim_fwd<<<grid, 256, 0, st>>>(image, target, width, height, win, maps, partial);
     k_ssim_bwd<<<grid, 256, 0, st>>>(image, target, width, height, win, maps, w_l1, w_ssim, dL_dimage);
     k_finish<<<1, 256, 0, st>>>(partial, int(ssim_blocks(width, height)), inv3p, w_l1, w_ssim, 1, loss);
