@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   const int lane = threadIdx.x;
   const int tx = tile % TX, ty = tile / TX;
   const int x0 = tx * kTile, y0 = ty * kTile;
-  const float bx0 = float(x0) + 0.5f, by0 = float(y0) + 0.5f;
+  const float qx = float(x0 + (q0 & 1) * 8) + 0.5f, qy = float(y0 + (q0 >> 1) * 8) + 0.5f;
   uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
   if (end > uint64_t(num_pairs)) end = uint32_t(num_pairs);
   if (start > end) start = end;
@@ -123,9 +123,9 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
     const EntryRec nxt = load_entry(proj, gnext);
     gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= int64_t(start));
     const uint32_t pos = uint32_t(cs) + ul - start;
-    const uint32_t mq = stage_entry(cur, bx0, by0, s_a, s_c, s_b, s_g, lane);
+    const bool hit = stage_entry(cur, qx, qy, s_a, s_c, s_b, s_g, lane);
     cur = nxt;
-    uint64_t active = uint64_t(__ballot(((mq >> q0) & 1u) && pos < lmax));
+    uint64_t active = uint64_t(__ballot(hit && pos < lmax));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

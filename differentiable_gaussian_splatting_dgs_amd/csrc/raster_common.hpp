@@ -4,9 +4,9 @@
 // tile's 8x8 quarter q (x + 8 (q & 1), y + 8 (q >> 1)); lane l owns the
 // pixel at offset (l & 7, l >> 3) of it.  The tile's depth-sorted list is
 // consumed in chunks of 64 entries: lane l stages entry l's record in LDS
-// and tests the Gaussian's alpha >= 1/255 footprint box against the
-// quarters; one ballot gives the 64-bit set of chunk entries that can
-// reach the wave's quarter.  The loop then visits only set bits (scalar
+// and tests the Gaussian's alpha >= 1/255 footprint against the wave's
+// quarter; one ballot gives the 64-bit set of chunk entries that can
+// reach it.  The loop then visits only set bits (scalar
 // bit scans), so Gaussians that cannot reach a quarter cost it no vector
 // work.
 #pragma once
@@ -93,27 +93,51 @@ __device__ __forceinline__ EntryRec load_entry(const float4* __restrict__ proj, 
 // is staged, so the two dependent HBM round trips (index, then record) of
 // a chunk overlap the compositing of the one before it.
 //
-// Stage a loaded entry (if any) into LDS slot `lane` and return its 4-bit
-// quarter-overlap mask: the Gaussian's alpha >= 1/255 box
-// [u - ex, u + ex] x [v - ey, v + ey] against the quarters' pixel-centre
-// ranges [b0 + 8k, b0 + 8k + 7].  bx0/by0: pixel-centre coordinate of the
-// tile's first pixel.
-__device__ __forceinline__ uint32_t stage_entry(const EntryRec& r, float bx0, float by0, float4* s_a, float4* s_c,
-                                                float* s_b, int32_t* s_g, int lane) {
-  uint32_t m = 0;
+// True when the Gaussian's alpha is provably below 1/255 at every point of
+// the rectangle [x0, x1] x [y0, y1] of pixel centres, so no pixel there can
+// composite it.  alpha = opacity * exp(-Q / 2) with Q(d) = d^T [A B; B C] d
+// (d: pixel centre minus mean) falls below 1/255 exactly where
+// Q > 2 ln(255 opacity).  Q is convex, so its minimum over the rectangle is
+// 0 when the mean lies inside and otherwise lies on an edge, where the 1-D
+// minimiser is the unconstrained one clamped to the edge.  The margin
+// covers the rounding of this evaluation and of the rasteriser's own
+// evaluation of Q at any pixel of the rectangle (both a few fp32 ulps of
+// the term magnitudes, bounded by S below), and the hardware log2.
+__device__ __forceinline__ bool ellipse_misses(float u, float v, float A, float B, float C, float opac, float x0,
+                                               float x1, float y0, float y1) {
+  if (!(A > 0.0f && C > 0.0f)) return false;
+  const float dx0 = x0 - u, dx1 = x1 - u, dy0 = y0 - v, dy1 = y1 - v;
+  if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) return false;
+  const float rc = __fdividef(B, C), ra = __fdividef(B, A);
+  const auto quad = [&](float dx, float dy) { return fmaf(A * dx, dx, fmaf(2.0f * B * dx, dy, C * dy * dy)); };
+  const float ey0 = fminf(fmaxf(-rc * dx0, dy0), dy1), ey1 = fminf(fmaxf(-rc * dx1, dy0), dy1);
+  const float ex0 = fminf(fmaxf(-ra * dy0, dx0), dx1), ex1 = fminf(fmaxf(-ra * dy1, dx0), dx1);
+  const float qmin = fminf(fminf(quad(dx0, ey0), quad(dx1, ey1)), fminf(quad(ex0, dy0), quad(ex1, dy1)));
+  const float X = fmaxf(fabsf(dx0), fabsf(dx1)), Y = fmaxf(fabsf(dy0), fabsf(dy1));
+  const float S = fmaf(A * X, X, fmaf(2.0f * fabsf(B) * X, Y, C * Y * Y));
+  const float tau2 = 1.38629436f * __log2f(255.0f * opac);   // 2 ln(255 opacity)
+  return qmin > tau2 + 1.0e-3f * fabsf(tau2) + 2.0e-3f + 1.0e-5f * S;
+}
+
+// Stage a loaded entry (if any) into LDS slot `lane` and return whether it
+// can reach the wave's quarter, whose pixel centres span
+// [qx, qx + 7] x [qy, qy + 7]: first the Gaussian's alpha >= 1/255 box
+// [u - ex, u + ex] x [v - ey, v + ey] against the quarter, then (for finite
+// boxes) the exact test of the footprint ellipse against it.
+__device__ __forceinline__ bool stage_entry(const EntryRec& r, float qx, float qy, float4* s_a, float4* s_c,
+                                            float* s_b, int32_t* s_g, int lane) {
+  bool hit = false;
   if (r.g >= 0) {
     s_a[lane] = make_float4(r.q0.x, r.q0.y, -0.5f * r.q0.z, -r.q0.w);
     s_c[lane] = make_float4(-0.5f * r.q1.x, r.q1.y, r.q1.z, r.q1.w);
     s_b[lane] = r.b;
     if (s_g != nullptr) s_g[lane] = r.g;
-    const float lx = r.q0.x - r.ex, hx = r.q0.x + r.ex, ly = r.q0.y - r.ey, hy = r.q0.y + r.ey;
-    const bool x0 = hx >= bx0 && lx <= bx0 + 7.0f;
-    const bool x1 = hx >= bx0 + 8.0f && lx <= bx0 + 15.0f;
-    const bool y0 = hy >= by0 && ly <= by0 + 7.0f;
-    const bool y1 = hy >= by0 + 8.0f && ly <= by0 + 15.0f;
-    m = uint32_t(x0 && y0) | (uint32_t(x1 && y0) << 1) | (uint32_t(x0 && y1) << 2) | (uint32_t(x1 && y1) << 3);
+    const float u = r.q0.x, v = r.q0.y;
+    hit = u + r.ex >= qx && u - r.ex <= qx + 7.0f && v + r.ey >= qy && v - r.ey <= qy + 7.0f;
+    if (hit && r.ex < 1.0e30f)
+      hit = !ellipse_misses(u, v, r.q0.z, r.q0.w, r.q1.x, r.q1.y, qx, qx + 7.0f, qy, qy + 7.0f);
   }
-  return m;
+  return hit;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

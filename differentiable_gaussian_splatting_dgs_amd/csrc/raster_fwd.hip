@@ -33,7 +33,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   const int lane = threadIdx.x;
   const int tx = tile % TX, ty = tile / TX;
   const int x0 = tx * kTile, y0 = ty * kTile;
-  const float bx0 = float(x0) + 0.5f, by0 = float(y0) + 0.5f;
+  const float qx = float(x0 + (q0 & 1) * 8) + 0.5f, qy = float(y0 + (q0 >> 1) * 8) + 0.5f;
   uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
   if (end > uint64_t(num_pairs)) end = uint32_t(num_pairs);
   if (start > end) start = end;
@@ -52,9 +52,9 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     const EntryRec nxt = load_entry(proj, gnext);
     const uint32_t j2 = cs + 2 * kChunk + ul;
     gnext = load_index(vals, j2, j2 < end);
-    const uint32_t mq = stage_entry(cur, bx0, by0, s_a, s_c, s_b, nullptr, lane);
+    const bool hit = stage_entry(cur, qx, qy, s_a, s_c, s_b, nullptr, lane);
     cur = nxt;
-    uint64_t active = __ballot((mq >> q0) & 1u);
+    uint64_t active = __ballot(hit);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
