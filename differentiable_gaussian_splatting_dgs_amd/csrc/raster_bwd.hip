@@ -14,8 +14,9 @@
 //    visited.  The nine partials of a Gaussian are summed over a lane's
 //    pixels in registers, then over the wave by two lane-half swaps that fold
 //    several values at once (permlane32/16 swap) and four DPP row steps, and
-//    leave as nine global float atomics per (Gaussian, wave), issued from
-//    four lanes.
+//    parked in LDS; at the end of each chunk 16-lane rows turn them into
+//    gradients and add them with nine global float atomics per (Gaussian,
+//    wave), one coalesced request per Gaussian.
 //
 //  k_project_bwd -- one thread per visible Gaussian: the chain rule of the
 //    projection from the screen-space gradients to all 59 parameters
@@ -30,6 +31,7 @@ namespace gs {
 namespace {
 
 constexpr int kG2 = 12;   // floats per Gaussian in the screen-gradient buffer
+constexpr int kAcc = 13;  // LDS stride of a chunk entry's nine sums (odd: no bank conflicts)
 
 __device__ __forceinline__ float f_of(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t u_of(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   __shared__ float4 s_c[kChunk];
   __shared__ float s_b[kChunk];
   __shared__ int32_t s_g[kChunk];
+  __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
   int q0;
   const int tile = order_tile(order, nT, q0);
   if (tile < 0) return;
@@ -99,15 +102,15 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
   const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
   float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
-  // lanes 0, 16, 32, 48 (row r = lane / 16) issue the atomics: row r of the
-  // folded sums q0 / q1 carries component (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
-  // (q2, lane 0: component 8); per-lane factors that turn the folded sums
-  // into gradients
+  // lanes 0, 16, 32, 48 (row r = lane / 16) store the sums: row r of the
+  // folded sums q0 / q1 carries sum (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
+  // (q2, lane 0: sum 8)
   const int row = lane >> 4;
   const int comp0 = ((row & 1) << 1) | (row >> 1);
-  const bool row0 = row == 0, row2 = row == 2, even = (row & 1) == 0;
-  const float k_odd = row == 1 ? -0.5f : -1.0f;   // conic A and B: -sxx / 2, -sxy
-  const float k_q1 = row0 ? -0.5f : 1.0f;          // conic C: -syy / 2
+  // flush: lane (lane & 15) = c of its row writes gradient c; fk is its
+  // factor for c >= 2 (conic A, B, C: -1/2, -1, -1/2; the rest 1)
+  const int fc = lane & 15;
+  const float fk = (fc == 2 || fc == 4) ? -0.5f : (fc == 3 ? -1.0f : 1.0f);
   uint32_t lmax = wave_max_u32(lastp);     // entries a pixel of the quarter composited
   if (lmax > end - start) lmax = end - start;
   if (lmax == 0) return;
@@ -120,6 +123,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   EntryRec cur = load_entry(proj, load_index(vals, uint32_t(top) + ul, uint32_t(top) + ul - start < lmax));
   int32_t gnext = load_index(vals, uint32_t(top - kChunk) + ul, top - kChunk >= int64_t(start));
   for (int64_t cs = top; cs >= int64_t(start); cs -= kChunk) {
+    uint64_t written = 0;   // chunk entries with sums in s_acc
     const EntryRec nxt = load_entry(proj, gnext);
     gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= int64_t(start));
     const uint32_t pos = uint32_t(cs) + ul - start;
@@ -164,21 +168,38 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       const float v9[9] = {sx, sy, sx * dx, sx * dy, sy * dy, dl * e, wgt * G0, wgt * G1, wgt * G2};
       float q0s, q1s, q2s;
       wave_sum9(v9, q0s, q1s, q2s);
-      // q0 rows hold (sx, sxx, sy, sxy): lanes 0 and 32 need each other's
-      // row for the mean gradient (A sx + B sy, B sx + C sy)
-      const auto sw = __builtin_amdgcn_permlane32_swap(u_of(q0s), u_of(q0s), false, false);
-      const float q0o = f_of(lane < 32 ? sw[1] : sw[0]);
-      // u: A sx + B sy (row 0), v: C sy + B sx (row 2), conic A / B (rows 1, 3)
-      const float A = -2.0f * a.z, B = -a.w, C = -2.0f * c.x;
-      const float m1 = row0 ? A : (row2 ? C : k_odd);
-      const float m2 = even ? B : 0.0f;
-      const float g0 = fmaf(m1, q0s, m2 * q0o);
-      const float g1 = k_q1 * q1s;
       if ((lane & 15) == 0) {
-        float* dst = grad2d + size_t(__builtin_amdgcn_readfirstlane(s_g[k])) * kG2;
-        if (g0 != 0.0f) unsafeAtomicAdd(dst + comp0, g0);
-        if (g1 != 0.0f) unsafeAtomicAdd(dst + 4 + comp0, g1);
-        if (lane == 0 && q2s != 0.0f) unsafeAtomicAdd(dst + 8, q2s);
+        float* acc = s_acc + k * kAcc;
+        acc[comp0] = q0s;
+        acc[4 + comp0] = q1s;
+        if (lane == 0) acc[8] = q2s;
+      }
+      written |= 1ull << k;
+    }
+    // the chunk's entries leave four at a time, one 16-lane row each (lane
+    // c < 9 of the row: gradient c), so a Gaussian's nine atomics go out as
+    // one request: u = A sx + B sy, v = C sy + B sx, conic -sxx / 2, -sxy,
+    // -syy / 2; opacity and colour as summed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    while (written != 0) {
+      int ks[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ks[r] = written != 0 ? __builtin_ctzll(written) : -1;
+        written &= written - 1;
+      }
+      const int kk = row == 0 ? ks[0] : (row == 1 ? ks[1] : (row == 2 ? ks[2] : ks[3]));
+      if (kk >= 0 && fc < 9) {
+        const float* acc = s_acc + kk * kAcc;
+        const float x = acc[fc];
+        const float4 a = s_a[kk];
+        const float cx = s_c[kk].x;
+        const float m1 = fc == 0 ? -2.0f * a.z : (fc == 1 ? -2.0f * cx : fk);
+        // the mean gradients also take the other mean sum (lanes 0 and 1)
+        const float gval = fc < 2 ? fmaf(m1, x, -a.w * acc[fc ^ 1]) : m1 * x;
+        if (gval != 0.0f) unsafeAtomicAdd(grad2d + size_t(s_g[kk]) * kG2 + fc, gval);
       }
     }
     __builtin_amdgcn_wave_barrier();

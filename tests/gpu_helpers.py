@@ -86,8 +86,9 @@ def check_grad(name, gpu, ref, mag, extra=0.0, rel=1e-3, mtol=1e-4):
     err = np.abs(gpu - ref)
     tol = rel * np.abs(ref) + mtol * mag + extra + 1e-30
     ratio = err / tol
-    worst = float(ratio.max()) if ratio.size else 0.0
-    nbad = int((ratio > 1).sum())
+    ratio[~np.isfinite(gpu) & np.isfinite(ref)] = np.inf   # a NaN or inf is outside every tolerance
+    worst = float(np.nanmax(ratio)) if ratio.size else 0.0
+    nbad = int((~(ratio <= 1)).sum())
     say(f"  {name}: max|err|={err.max() if err.size else 0:.3g} worst err/tol={worst:.3g} bad={nbad}/{err.size}")
     if nbad:
         for idx in np.argsort(ratio, axis=None)[::-1][:8]:
