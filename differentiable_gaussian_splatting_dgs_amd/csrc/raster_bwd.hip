@@ -13,8 +13,8 @@
 //    fp32 arithmetic as the forward, so exactly the composited set is
 //    visited.  The nine partials of a Gaussian are summed over a lane's
 //    pixels in registers, then over the wave by two lane-half swaps that fold
-//    several values at once (permlane32/16 swap) and four DPP row steps, and
-//    parked in LDS; at the end of each chunk 16-lane rows turn them into
+//    several values at once (permlane32/16 swap) and three DPP row steps
+//    (to half-row totals), and parked in LDS; at the end of each chunk 16-lane rows turn them into
 //    gradients and add them with nine global float atomics per (Gaussian,
 //    wave), one coalesced request per Gaussian.
 //
@@ -31,7 +31,7 @@ namespace gs {
 namespace {
 
 constexpr int kG2 = 12;   // floats per Gaussian in the screen-gradient buffer
-constexpr int kAcc = 13;  // LDS stride of a chunk entry's nine sums (odd: no bank conflicts)
+constexpr int kAcc = 19;  // LDS stride of a chunk entry's 2 x 9 half sums (odd: no bank conflicts)
 
 __device__ __forceinline__ float f_of(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t u_of(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -49,24 +49,25 @@ __device__ __forceinline__ float fold16(float x, float y) {
   return f_of(s[0]) + f_of(s[1]);
 }
 
-// Sum over the 16 lanes of each row; every lane ends with its row's total.
-__device__ __forceinline__ float row_sum(float v) {
+// Sum over each 8-lane half of a row; every lane ends with its half's
+// total (the two halves are added when the sums leave LDS).
+__device__ __forceinline__ float half_row_sum(float v) {
   v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
   v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x140, 0xF, 0xF, false));  // row_mirror
   return v;
 }
 
 // Sums of nine per-lane values over the wave, folded so each fold serves
-// several values: q0 rows 0..3 end with the totals of v0, v2, v1, v3; q1
-// rows with v4, v6, v5, v7; q2 row 0 with v8.
+// several values: the two 8-lane halves of q0 rows 0..3 end with the half
+// totals of v0, v2, v1, v3; of q1 rows with v4, v6, v5, v7; of q2 row 0
+// with v8.
 __device__ __forceinline__ void wave_sum9(const float v[9], float& q0, float& q1, float& q2) {
   const float r0 = fold32(v[0], v[1]), r1 = fold32(v[2], v[3]), r2 = fold32(v[4], v[5]);
   const float r3 = fold32(v[6], v[7]), r4 = fold32(v[8], 0.0f);
-  q0 = row_sum(fold16(r0, r1));
-  q1 = row_sum(fold16(r2, r3));
-  q2 = row_sum(fold16(r4, 0.0f));
+  q0 = half_row_sum(fold16(r0, r1));
+  q1 = half_row_sum(fold16(r2, r3));
+  q2 = half_row_sum(fold16(r4, 0.0f));
 }
 
 __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
@@ -102,11 +103,13 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
   const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
   float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
-  // lanes 0, 16, 32, 48 (row r = lane / 16) store the sums: row r of the
-  // folded sums q0 / q1 carries sum (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]
-  // (q2, lane 0: sum 8)
+  // lanes 0, 8, 16, ..., 56 (row r = lane / 16, half h = lane / 8 % 2)
+  // store the half sums: row r of the folded sums q0 / q1 carries sum
+  // (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r] (q2, row 0: sum 8); half sum h of
+  // sum j sits at 2 j + h of the entry's slot
   const int row = lane >> 4;
   const int comp0 = ((row & 1) << 1) | (row >> 1);
+  const int half = (lane >> 3) & 1;
   // flush: lane (lane & 15) = c of its row writes gradient c; fk is its
   // factor for c >= 2 (conic A, B, C: -1/2, -1, -1/2; the rest 1)
   const int fc = lane & 15;
@@ -168,11 +171,14 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       const float v9[9] = {sx, sy, sx * dx, sx * dy, sy * dy, dl * e, wgt * G0, wgt * G1, wgt * G2};
       float q0s, q1s, q2s;
       wave_sum9(v9, q0s, q1s, q2s);
-      if ((lane & 15) == 0) {
-        float* acc = s_acc + k * kAcc;
-        acc[comp0] = q0s;
-        acc[4 + comp0] = q1s;
-        if (lane == 0) acc[8] = q2s;
+      // keeps the last DPP step's adds out of the store branch below, where
+      // they could not fuse with their DPP moves
+      asm volatile("" : "+v"(q0s), "+v"(q1s), "+v"(q2s));
+      if ((lane & 7) == 0) {
+        float* acc = s_acc + k * kAcc + half;
+        acc[2 * comp0] = q0s;
+        acc[8 + 2 * comp0] = q1s;
+        if (lane < 16) acc[16] = q2s;
       }
       written |= 1ull << k;
     }
@@ -193,12 +199,12 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       const int kk = row == 0 ? ks[0] : (row == 1 ? ks[1] : (row == 2 ? ks[2] : ks[3]));
       if (kk >= 0 && fc < 9) {
         const float* acc = s_acc + kk * kAcc;
-        const float x = acc[fc];
+        const float x = acc[2 * fc] + acc[2 * fc + 1];
         const float4 a = s_a[kk];
         const float cx = s_c[kk].x;
         const float m1 = fc == 0 ? -2.0f * a.z : (fc == 1 ? -2.0f * cx : fk);
         // the mean gradients also take the other mean sum (lanes 0 and 1)
-        const float gval = fc < 2 ? fmaf(m1, x, -a.w * acc[fc ^ 1]) : m1 * x;
+        const float gval = fc < 2 ? fmaf(m1, x, -a.w * (acc[2 * (fc ^ 1)] + acc[2 * (fc ^ 1) + 1])) : m1 * x;
         if (gval != 0.0f) unsafeAtomicAdd(grad2d + size_t(s_g[kk]) * kG2 + fc, gval);
       }
     }
