@@ -25,6 +25,7 @@ GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
 GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM = 0, 1, 2, 3
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
+GS_MAX_FUSED_VIEWS = 8
 TILE = 16
 
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
@@ -69,8 +70,9 @@ def lib():
     L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
-    L.gs_project_bwd_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _f32,
-                                      _f32, _f32, _f32, _f32, _f32, _P, _sz, _P]
+    L.gs_project_bwd_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, C.POINTER(gs_camera), _i32,
+                                      C.POINTER(C.c_void_p), _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32, _P,
+                                      _sz, _P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = C.c_int
     _handle = L
@@ -206,12 +208,18 @@ def gs_sparse_adam(params, grads, m, v, n, ld, union_flags, union_idx, union_cou
                                workspace.numel() * workspace.element_size(), _stream(stream)), "gs_sparse_adam")
 
 
-def gs_project_bwd_adam(params, grads, m, v, n, ld, cam, proj, grad2d, union_flags, union_idx, union_count, lr,
+def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, union_idx, union_count, lr,
                         beta1, beta2, eps, bias_c1, bias_c2, workspace, stream=None):
-    _check(lib().gs_project_bwd_adam(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, C.byref(cam), _ptr(proj),
-                                     _ptr(grad2d), _ptr(union_flags), _ptr(union_idx), _ptr(union_count), lr, beta1,
-                                     beta2, eps, bias_c1, bias_c2, _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+    """``cams`` / ``grad2d``: one camera and one screen-gradient buffer per
+    fused view; ``grads`` None when no other view contributed."""
+    nv = len(cams)
+    assert len(grad2d) == nv
+    carr = (gs_camera * max(nv, 1))(*[c if isinstance(c, gs_camera) else make_camera(c) for c in cams])
+    parr = (C.c_void_p * max(nv, 1))(*[g.data_ptr() for g in grad2d])
+    _check(lib().gs_project_bwd_adam(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, carr, nv, parr,
+                                     _ptr(union_flags), _ptr(union_idx), _ptr(union_count), lr, beta1, beta2, eps,
+                                     bias_c1, bias_c2, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)),
            "gs_project_bwd_adam")
 
 
@@ -266,14 +274,16 @@ class TrainStep:
     """Owns parameters, Adam state and scratch; ``step()`` runs one training
     step (all views of the batch, then sparse Adam).
 
-    Views cycle through three buffer sets (two for a batch of two) and
-    alternate between two screen-gradient buffers.
+    Views cycle through three buffer sets (two for a batch of two).  The
+    last ndefer = min(views, 8) views own a screen-gradient buffer each; the
+    earlier ones alternate between two more.
     In ``step()`` view k + 1's preprocess and binning are issued on a second
     stream while view k renders, takes its loss and runs the raster backward
-    on the caller's stream, and view k's projection backward runs on a third
-    stream; events order every reuse of a set or buffer and every hand-over.
-    ``forward_view`` / ``backward_view`` run one view's stages in order on
-    the current stream."""
+    on the caller's stream; the projection backward of an early view runs on
+    a third stream, that of the last ndefer views in the Adam pass (one read
+    of the parameters for all of them); events order every reuse of a set or
+    buffer and every hand-over.  ``forward_view`` / ``backward_view`` run
+    one view's stages in order on the current stream."""
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
                  pair_capacity=None, record_tiles=False):
@@ -292,8 +302,14 @@ class TrainStep:
         self.record_tiles = record_tiles
         self.timer = None        # optional: name -> list of (start, end) torch.cuda.Event pairs
         rows = max(n, 1)
+        # screen-gradient buffers: one per view whose projection backward
+        # step() fuses into Adam (the last ndefer views), two alternating
+        # for the earlier views
+        nv = len(cameras)
+        self.ndefer = min(nv, GS_MAX_FUSED_VIEWS)
+        self.nfirst = nv - self.ndefer
         self.g2d = [torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
-                    for _ in range(2)]
+                    for _ in range(self.ndefer + (2 if self.nfirst > 0 else 0))]
         self._gcur = 0
         self.vis_idx = [torch.empty(rows, dtype=torch.int32, device=self.device) for _ in cameras]
         self.vis_count = torch.zeros(len(cameras), dtype=torch.int64, device=self.device)
@@ -334,6 +350,10 @@ class TrainStep:
     @property
     def grad2d(self):
         return self.g2d[self._gcur]
+
+    def _gbuf(self, k):
+        """Index of view k's screen-gradient buffer."""
+        return k - self.nfirst if k >= self.nfirst else self.ndefer + k % 2
 
     @contextlib.contextmanager
     def _stage(self, name):
@@ -400,10 +420,10 @@ class TrainStep:
         """Raster backward, then (unless keep_grad2d) projection backward."""
         vw = self.views[k]
         ps = self.sets[k % self.nsets]
-        self._gcur = k % 2
+        self._gcur = self._gbuf(k)
         with self._stage("render_bwd"):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
-                          vw.dL, self.g2d[k % 2], vw.order)
+                          vw.dL, self.g2d[self._gcur], vw.order)
         if not keep_grad2d:
             self.project_view(k)
 
@@ -411,19 +431,19 @@ class TrainStep:
         vw = self.views[k]
         with self._stage("project_bwd"):
             gs_project_bwd(self.params, self.n, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1],
-                           self.g2d[k % 2], self.grads)
+                           self.g2d[self._gbuf(k)], self.grads)
 
-    def run_views(self, defer_last_projection=False):
+    def run_views(self, defer_projection=False):
         """Every view of the batch, gradients accumulated: view k + 1 is
         prepared on the side stream and view k's projection backward runs on
         the gradient stream while the current stream renders and
         back-propagates through the rasteriser.  Nothing blocks until every
         view is issued; then the pair counts are read, and a view that
         overflowed its buffer set makes the whole batch run again with the
-        set grown.  With defer_last_projection the last view's screen-space
-        gradients are left for adam(fused=True)."""
+        set grown.  With defer_projection the screen-space gradients of the
+        last ndefer views are left for adam(fused=True)."""
         while True:
-            self._issue_views(defer_last_projection)
+            self._issue_views(defer_projection)
             self._counts_read.synchronize()
             M = self.M_host.tolist()
             over = [k for k in range(len(self.views)) if M[k] > self._set_cap[k]]
@@ -441,7 +461,7 @@ class TrainStep:
             for g2 in self.g2d:
                 g2.zero_()
 
-    def _issue_views(self, defer_last):
+    def _issue_views(self, defer):
         main = torch.cuda.current_stream(self.device)
         nv = len(self.views)
         proj_done = [None, None]
@@ -450,12 +470,12 @@ class TrainStep:
         first_done.record(main)
         for k in range(nv):
             self.render_view(k)
-            if proj_done[k % 2] is not None:
-                main.wait_event(proj_done[k % 2])          # buffer k % 2 re-zeroed by view k - 2
+            if k < self.nfirst and proj_done[k % 2] is not None:
+                main.wait_event(proj_done[k % 2])          # buffer re-zeroed by view k - 2's projection
             self.backward_view(k, keep_grad2d=True)
             raster_done = torch.cuda.Event()
             raster_done.record(main)
-            if not (defer_last and k == nv - 1):
+            if not (defer and k >= self.nfirst):
                 with torch.cuda.stream(self.gstream):
                     self.gstream.wait_event(raster_done)
                     self.project_view(k)
@@ -487,19 +507,19 @@ class TrainStep:
                 main.wait_event(ev)
 
     def adam(self, fused=False):
-        """Sparse Adam over the union; with fused, the last view's
-        projection backward (left by run_views(defer_last_projection=True))
+        """Sparse Adam over the union; with fused, the projection backward
+        of the last ndefer views (left by run_views(defer_projection=True))
         runs in the same pass."""
         self.t += 1
         bc1 = 1.0 - self.beta1 ** self.t
         bc2 = 1.0 - self.beta2 ** self.t
         with self._stage("sparse_adam"):
             if fused:
-                k = len(self.views) - 1
-                gs_project_bwd_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.views[k].cam,
-                                    self.sets[k % self.nsets].proj, self.g2d[k % 2], self.union_flags,
-                                    self.union_idx, self.union_count, self.lr, self.beta1, self.beta2, self.eps,
-                                    bc1, bc2, self.ws_adam)
+                ks = range(self.nfirst, len(self.views))
+                gs_project_bwd_adam(self.params, self.grads if self.nfirst > 0 else None, self.m, self.v, self.n,
+                                    self.ld, [self.views[k].cam for k in ks], [self.g2d[self._gbuf(k)] for k in ks],
+                                    self.union_flags, self.union_idx, self.union_count, self.lr, self.beta1,
+                                    self.beta2, self.eps, bc1, bc2, self.ws_adam)
             else:
                 gs_sparse_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.union_flags,
                                self.union_idx, self.union_count, self.lr, self.beta1, self.beta2, self.eps, bc1,
@@ -508,8 +528,8 @@ class TrainStep:
     def step(self):
         """One training step: for each view preprocess, bin/sort, render,
         loss, backward (gradients accumulate); then sparse Adam, fused with
-        the last view's projection backward."""
-        self.run_views(defer_last_projection=True)
+        the projection backward of the last ndefer views."""
+        self.run_views(defer_projection=True)
         self.adam(fused=True)
 
 

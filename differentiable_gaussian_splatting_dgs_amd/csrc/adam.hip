@@ -35,16 +35,43 @@ __global__ __launch_bounds__(256) void k_adam(float* __restrict__ params, float*
   }
 }
 
-// The batch's last view's projection backward fused with the Adam step,
-// one thread per listed row: a row the last view saw (its projected record
-// has tiles) adds that view's parameter gradients, chained from its
-// screen-space gradients (which it re-zeroes), to the accumulated ones;
-// then Adam as k_adam.  The same arithmetic as the two steps one after
-// the other, without writing and re-reading the gradient planes.
-__global__ __launch_bounds__(256) void k_project_adam(float* __restrict__ params, float* __restrict__ grads,
-                                                      float* __restrict__ m, float* __restrict__ v, int64_t ld,
-                                                      CamArgs cam, const float4* __restrict__ proj,
-                                                      float4* __restrict__ grad2d, const int32_t* __restrict__ rows,
+using ArgCam = const __attribute__((address_space(4))) CamArgs;
+
+// A camera read field by field from the kernel-argument segment (scalar
+// loads: every lane reads the same words).
+__device__ __forceinline__ CamArgs arg_camera(ArgCam* c) {
+  CamArgs r;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) r.R[j] = c->R[j];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    r.t[j] = c->t[j];
+    r.campos[j] = c->campos[j];
+  }
+  r.fx = c->fx;
+  r.fy = c->fy;
+  r.cx = c->cx;
+  r.cy = c->cy;
+  r.near_z = c->near_z;
+  r.width = c->width;
+  r.height = c->height;
+  r.tiles_x = c->tiles_x;
+  r.tiles_y = c->tiles_y;
+  return r;
+}
+
+// The projection backward of the batch's last views fused with the Adam
+// step, one thread per listed row: for each fused view whose screen-space
+// row is non-zero (a row the view's raster backward reached; a zero row
+// chains to a zero gradient), that view's parameter gradients, chained
+// from the row (then re-zeroed), are added in view order to the gradients
+// accumulated so far (the gradient planes, or zero without them); then
+// Adam as k_adam.  The same arithmetic as the projection backward of each
+// view followed by k_adam, without writing and re-reading the gradient
+// planes; the parameters are read once for all the views.
+__global__ __launch_bounds__(256) void k_project_adam(FusedViews views, float* __restrict__ params,
+                                                      float* __restrict__ grads, float* __restrict__ m,
+                                                      float* __restrict__ v, int64_t ld, const int32_t* __restrict__ rows,
                                                       const int64_t* __restrict__ row_count, float lr, float b1,
                                                       float b2, float eps, float bc1, float bc2) {
   const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -53,23 +80,36 @@ __global__ __launch_bounds__(256) void k_project_adam(float* __restrict__ params
   float p[59], g[59];
 #pragma unroll
   for (int k = 0; k < 59; ++k) p[k] = params[int64_t(k) * ld + i];
-  if (__builtin_bit_cast(uint32_t, proj[4 * i + 3].w) != 0u) {
-    const float4 ga4 = grad2d[3 * i], gb4 = grad2d[3 * i + 1], gc4 = grad2d[3 * i + 2];
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    grad2d[3 * i] = z4;
-    grad2d[3 * i + 1] = z4;
-    grad2d[3 * i + 2] = z4;
-    const float grgb[3] = {gb4.z, gb4.w, gc4.x};
-    project_grads(p, cam, ga4.x, ga4.y, ga4.z, ga4.w, gb4.x, gb4.y, grgb, g);
 #pragma unroll
-    for (int k = 0; k < 59; ++k) g[k] += grads[int64_t(k) * ld + i];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 59; ++k) g[k] = grads[int64_t(k) * ld + i];
+  for (int k = 0; k < 59; ++k) g[k] = grads != nullptr ? grads[int64_t(k) * ld + i] : 0.0f;
+  // the views are read in place from the argument segment (the first
+  // argument sits at its start), so a view's camera is a few scalar loads
+  (void)views;
+  using ArgViews = const __attribute__((address_space(4))) FusedViews;
+  ArgViews* fv = (ArgViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int nv = fv->count;
+  for (int w = 0; w < nv; ++w) {
+    float4* g2 = reinterpret_cast<float4*>(fv->grad2d[w]) + 3 * i;
+    const float4 ga4 = g2[0], gb4 = g2[1], gc4 = g2[2];
+    const bool nz = ga4.x != 0.f || ga4.y != 0.f || ga4.z != 0.f || ga4.w != 0.f || gb4.x != 0.f ||
+                    gb4.y != 0.f || gb4.z != 0.f || gb4.w != 0.f || gc4.x != 0.f || gc4.y != 0.f ||
+                    gc4.z != 0.f || gc4.w != 0.f;
+    if (nz) {
+      const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      g2[0] = z4;
+      g2[1] = z4;
+      g2[2] = z4;
+      const float grgb[3] = {gb4.z, gb4.w, gc4.x};
+      const CamArgs cam = arg_camera(&fv->cam[w]);
+      project_grads<true>(p, cam, ga4.x, ga4.y, ga4.z, ga4.w, gb4.x, gb4.y, grgb, g);
+    }
   }
   const float ob1 = 1.0f - b1, ob2 = 1.0f - b2;
   const float ibc1 = 1.0f / bc1, ibc2 = 1.0f / bc2;
-#pragma unroll 4
+  // fully unrolled (p and g stay in registers: constant indices), in
+  // groups of eight planes the scheduler may not merge, so the Adam state
+  // of only one group is in flight at a time
+#pragma unroll
   for (int k = 0; k < 59; ++k) {
     const int64_t q = int64_t(k) * ld + i;
     const float mn = fmaf(b1, m[q], ob1 * g[k]);
@@ -77,20 +117,18 @@ __global__ __launch_bounds__(256) void k_project_adam(float* __restrict__ params
     m[q] = mn;
     v[q] = vn;
     params[q] = p[k] - lr * (mn * ibc1) / (sqrtf(vn * ibc2) + eps);
-    grads[q] = 0.0f;
+    if (grads != nullptr) grads[q] = 0.0f;
+    if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 }  // namespace
 
 hipError_t launch_project_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
-                               const CamArgs& cam, const float* proj, float* grad2d, const int32_t* rows,
-                               const int64_t* row_count, float lr, float beta1, float beta2, float eps, float bc1,
-                               float bc2, hipStream_t st) {
+                               const FusedViews& views, const int32_t* rows, const int64_t* row_count, float lr,
+                               float beta1, float beta2, float eps, float bc1, float bc2, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  k_project_adam<<<unsigned((n + 255) / 256), 256, 0, st>>>(params, grads, m, v, ld, cam,
-                                                            reinterpret_cast<const float4*>(proj),
-                                                            reinterpret_cast<float4*>(grad2d), rows, row_count, lr,
+  k_project_adam<<<unsigned((n + 255) / 256), 256, 0, st>>>(views, params, grads, m, v, ld, rows, row_count, lr,
                                                             beta1, beta2, eps, bc1, bc2);
   return hipGetLastError();
 }

@@ -11,6 +11,8 @@
 #include "../../include/gs.h"
 #include "gs_internal.h"
 
+static_assert(GS_MAX_FUSED_VIEWS == gs::kMaxFusedViews, "fused view limit");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -288,18 +290,27 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
 }
 
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
-                             const gs_camera* cam, const float* proj, float* grad2d, uint8_t* union_flags,
-                             int32_t* union_idx, int64_t* union_count, float lr, float beta1, float beta2, float eps,
-                             float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream) {
-  gs::CamArgs c;
-  CHECK(check_camera(cam, c));
+                              const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
+                              int32_t* union_idx, int64_t* union_count, float lr, float beta1, float beta2, float eps,
+                              float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(num_views >= 0 && num_views <= GS_MAX_FUSED_VIEWS, "num_views = %d outside [0, %d]", int(num_views),
+          GS_MAX_FUSED_VIEWS);
+  REQUIRE(num_views == 0 || (cams != nullptr && grad2d != nullptr), "cams / grad2d NULL");
+  gs::FusedViews fv{};
+  fv.count = num_views;
+  for (int32_t w = 0; w < num_views; ++w) {
+    CHECK(check_camera(cams + w, fv.cam[w]));
+    fv.grad2d[w] = grad2d[w];
+  }
   REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
   REQUIRE(ld >= n, "ld < n");
   REQUIRE(union_count != nullptr, "union_count is NULL");
   if (n > 0) {
-    REQUIRE(params && grads && m && v && proj && grad2d && union_flags && union_idx, "NULL array");
-    REQUIRE(aligned(union_flags, 16) && aligned(proj, 16) && aligned(grad2d, 16),
-            "union_flags / proj / grad2d not 16-byte aligned");
+    REQUIRE(params && m && v && union_flags && union_idx, "NULL array");
+    REQUIRE(aligned(union_flags, 16), "union_flags not 16-byte aligned");
+    for (int32_t w = 0; w < num_views; ++w)
+      REQUIRE(fv.grad2d[w] != nullptr && aligned(fv.grad2d[w], 16), "grad2d[%d] NULL or not 16-byte aligned",
+              int(w));
   }
   REQUIRE(std::isfinite(lr) && std::isfinite(beta1) && std::isfinite(beta2) && std::isfinite(eps), "non-finite scalar");
   REQUIRE(bias_c1 > 0.0f && bias_c2 > 0.0f, "bias corrections must be > 0");
@@ -308,8 +319,8 @@ gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, i
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = gs::launch_compact(union_flags, n, union_idx, union_count, true, workspace, st);
   if (e == hipSuccess)
-    e = gs::launch_project_adam(params, grads, m, v, n, ld, c, proj, grad2d, union_idx, union_count, lr, beta1, beta2,
-                                eps, bias_c1, bias_c2, st);
+    e = gs::launch_project_adam(params, grads, m, v, n, ld, fv, union_idx, union_count, lr, beta1, beta2, eps,
+                                bias_c1, bias_c2, st);
   return hip_status(e, "gs_project_bwd_adam");
 }
 

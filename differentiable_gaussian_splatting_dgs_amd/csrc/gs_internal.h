@@ -70,10 +70,16 @@ hipError_t launch_loss(const float* image, const float* target, int32_t width, i
                        void* ws, hipStream_t st);
 
 // --- sparse Adam (adam.hip) ---------------------------------------------------
+// Views whose projection backward is fused into the Adam pass.
+constexpr int kMaxFusedViews = 8;
+struct FusedViews {
+  CamArgs cam[kMaxFusedViews];
+  float* grad2d[kMaxFusedViews];
+  int32_t count;
+};
 hipError_t launch_project_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
-                               const CamArgs& cam, const float* proj, float* grad2d, const int32_t* rows,
-                               const int64_t* row_count, float lr, float beta1, float beta2, float eps, float bc1,
-                               float bc2, hipStream_t st);
+                               const FusedViews& views, const int32_t* rows, const int64_t* row_count, float lr,
+                               float beta1, float beta2, float eps, float bc1, float bc2, hipStream_t st);
 hipError_t launch_sparse_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
                               const int32_t* rows, const int64_t* row_count, float lr, float beta1,
                               float beta2, float eps, float bc1, float bc2, hipStream_t st);

@@ -27,15 +27,26 @@ __device__ __forceinline__ void sh_dir_grad(float x, float y, float z, const flo
        10.0f * GS_SH_C3C * x * z * gY[13] + GS_SH_C3E * (xx - yy) * gY[14];
 }
 
+// Writes a parameter gradient (kAdd: adds it to what g holds).
+template <bool kAdd>
+__device__ __forceinline__ void put_grad(float& d, float v) {
+  if constexpr (kAdd)
+    d += v;
+  else
+    d = v;
+}
+
 // p: the Gaussian's 59 parameters; (gu, gv, gA, gB, gC, go, gr, gg, gb): the
-// screen-space gradients (record order); g: the 59 parameter gradients.
+// screen-space gradients (record order); g: the 59 parameter gradients
+// (kAdd: added to g, as g + this view's gradient).
+template <bool kAdd = false>
 __device__ __forceinline__ void project_grads(const float (&p)[59], const CamArgs& cam, float gu, float gv,
                                               float gA, float gB, float gC, float go, const float (&grgb)[3],
                                               float (&g)[59]) {
   Fwd f;
   project(p, cam, f);
   // opacity logit
-  g[10] = go * (f.opac * (1.0f - f.opac));
+  put_grad<kAdd>(g[10], go * (f.opac * (1.0f - f.opac)));
   // colour: SH coefficients and view direction
   float Y[16];
   sh_eval(f.dir[0], f.dir[1], f.dir[2], Y);
@@ -45,9 +56,9 @@ __device__ __forceinline__ void project_grads(const float (&p)[59], const CamArg
   float gY[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    g[11 + 3 * k] = gr[0] * Y[k];
-    g[12 + 3 * k] = gr[1] * Y[k];
-    g[13 + 3 * k] = gr[2] * Y[k];
+    put_grad<kAdd>(g[11 + 3 * k], gr[0] * Y[k]);
+    put_grad<kAdd>(g[12 + 3 * k], gr[1] * Y[k]);
+    put_grad<kAdd>(g[13 + 3 * k], gr[2] * Y[k]);
     gY[k] = gr[0] * p[11 + 3 * k] + gr[1] * p[12 + 3 * k] + gr[2] * p[13 + 3 * k];
   }
   float gdx, gdy, gdz;
@@ -104,9 +115,9 @@ __device__ __forceinline__ void project_grads(const float (&p)[59], const CamArg
   gx += cam.R[0] * gtx + cam.R[3] * gty + cam.R[6] * gtz;
   gy += cam.R[1] * gtx + cam.R[4] * gty + cam.R[7] * gtz;
   gz += cam.R[2] * gtx + cam.R[5] * gty + cam.R[8] * gtz;
-  g[0] = gx;
-  g[1] = gy;
-  g[2] = gz;
+  put_grad<kAdd>(g[0], gx);
+  put_grad<kAdd>(g[1], gy);
+  put_grad<kAdd>(g[2], gz);
   // Sigma = M M^T, M = Rq diag(s):  G_M = 2 G_Sigma M
   const float* Rq = f.r;
   float GR[3][3];
@@ -120,7 +131,7 @@ __device__ __forceinline__ void project_grads(const float (&p)[59], const CamArg
       gs += gm * Rq[3 * ii + jj];
       GR[ii][jj] = gm * f.s[jj];
     }
-    g[3 + jj] = gs * f.s[jj];
+    put_grad<kAdd>(g[3 + jj], gs * f.s[jj]);
   }
   // rotation of the unit quaternion (w, x, y, z)
   const float w = f.w, x = f.x, y = f.y, z = f.z;
@@ -133,10 +144,10 @@ __device__ __forceinline__ void project_grads(const float (&p)[59], const CamArg
                             y * GR[1][2] + x * GR[2][0] + y * GR[2][1]);
   const float qdot = gw * w + gqx * x + gqy * y + gqz * z;
   const float iq = 1.0f / sqrtf(f.qn);
-  g[6] = (gw - qdot * w) * iq;
-  g[7] = (gqx - qdot * x) * iq;
-  g[8] = (gqy - qdot * y) * iq;
-  g[9] = (gqz - qdot * z) * iq;
+  put_grad<kAdd>(g[6], (gw - qdot * w) * iq);
+  put_grad<kAdd>(g[7], (gqx - qdot * x) * iq);
+  put_grad<kAdd>(g[8], (gqy - qdot * y) * iq);
+  put_grad<kAdd>(g[9], (gqz - qdot * z) * iq);
 }
 
 }  // namespace gs

@@ -82,6 +82,8 @@ typedef struct gs_camera {
 /* floats per Gaussian in the screen-space gradient buffer of gs_render_bwd:
  * dL/d(u, v, A, B, C, opacity, r, g, b) then 3 unused */
 #define GS_GRAD2D_WORDS 12
+/* most views whose projection backward gs_project_bwd_adam fuses */
+#define GS_MAX_FUSED_VIEWS 8
 
 typedef enum gs_op {
   GS_OP_PREPROCESS = 0,
@@ -252,19 +254,29 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
                          float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* gs_project_bwd of the batch's last view followed by gs_sparse_adam, in one
- * pass over the union rows (same passages as the two): the last view's
- * parameter gradients are added to the accumulated ones in registers and
- * consumed by the update at once, so the gradient planes are not written and
- * read back in between.  Results equal the two calls in sequence.
- *   cam, proj, grad2d   the last view's camera, its gs_preprocess records (a
- *                       row with a non-zero tile count is one it saw) and
- *                       its gs_render_bwd screen-space gradients (consumed
- *                       rows re-zeroed)
- *   the other arguments as gs_sparse_adam (grads: the earlier views'
- *   accumulated gradients; zeroed for the listed rows). */
+/* gs_project_bwd of the batch's last views followed by gs_sparse_adam, in
+ * one pass over the union rows (same passages as the two): each listed
+ * row's parameters are read once, every fused view's parameter gradients are
+ * added in view order to the accumulated ones in registers, and the update
+ * consumes them at once, so the gradient planes are neither written nor read
+ * back in between.  Results equal gs_project_bwd of each view (in order)
+ * followed by gs_sparse_adam, up to the sign of zero gradients.
+ *   cams, grad2d   host arrays of num_views (0..GS_MAX_FUSED_VIEWS) entries:
+ *                  the views' cameras and the device pointers of their
+ *                  gs_render_bwd screen-space gradients ([n][12], 16-byte
+ *                  aligned, one buffer per view).  A row of a view is chained
+ *                  when any of its 12 words is non-zero (rows outside the
+ *                  view's visible set are zero: gs_render_bwd writes only
+ *                  visible Gaussians, and a zero row chains to zero); chained
+ *                  rows are re-zeroed.
+ *   grads          the gradients of the batch's other views ([59][ld]),
+ *                  zeroed for the listed rows; or NULL: none (taken as zero,
+ *                  nothing written)
+ *   the other arguments as gs_sparse_adam.
+ * Errors: GS_ERR_INVALID_ARG for num_views outside the range, a NULL or
+ * misaligned buffer, an invalid camera, or as gs_sparse_adam. */
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
-                              const gs_camera* cam, const float* proj, float* grad2d, uint8_t* union_flags,
+                              const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
                               int32_t* union_idx, int64_t* union_count, float lr, float beta1, float beta2, float eps,
                               float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream);
 

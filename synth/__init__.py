@@ -243,10 +243,12 @@ def mid(seed=2) -> Workload:
                        [2 * math.pi * k / 4 for k in range(4)], seed, name="mid")
 
 
-def capacity(seed=4, n=12_000_000) -> Workload:
+def capacity(seed=4, n=12_000_000, width=1920, height=1080, views=16) -> Workload:
+    """The capacity batch: 16 ring views out of 64 positions; ``views``
+    keeps the first few, ``width`` / ``height`` shrink them (parity sizes)."""
     rng = np.random.default_rng(seed + 1000)
-    js = np.sort(rng.choice(64, 16, replace=False))
-    return plane_scene(4, n, 1920, 1080,
+    js = np.sort(rng.choice(64, 16, replace=False))[:views]
+    return plane_scene(4, n, width, height,
                        [2 * math.pi * int(j) / 64 for j in js], seed, name="capacity")
 
 

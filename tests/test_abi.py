@@ -20,7 +20,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
-              "gs_sparse_adam",
+              "gs_sparse_adam", "gs_bin_sort_async", "gs_project_bwd_adam",
               "gs_workspace_size", "gs_status_string", "gs_last_error", "gs_version"]:
         assert n in names
 
@@ -92,6 +92,20 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.gs_sparse_adam(P(16), P(16), P(16), P(16), 4, 4, P(16), P(16), P(16), C.c_float(1e-3),
                               C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.0), C.c_float(0.1),
                               P(256), 1 << 20, None) == 1
+    # fused projection backward + adam: too many views, a misaligned
+    # screen-gradient buffer, a NULL buffer list
+    cam.width = 64
+    cams = (gs.gs_camera * 9)(*([cam] * 9))
+    bufs = (C.c_void_p * 9)(*([16] * 9))
+    args = (P(16), P(16), P(16), P(16), 4, 4)
+    tail = (P(16), P(16), P(16), C.c_float(1e-3), C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15),
+            C.c_float(0.1), C.c_float(0.1), P(256), 1 << 20, None)
+    assert lib.gs_project_bwd_adam(*args, cams, gs.GS_MAX_FUSED_VIEWS + 1, bufs, *tail) == 1
+    assert b"num_views" in lib.gs_last_error()
+    bufs[1] = 20
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, *tail) == 1
+    assert b"grad2d[1]" in lib.gs_last_error()
+    assert lib.gs_project_bwd_adam(*args, cams, 2, None, *tail) == 1
 
 
 def test_workspace_sizes():

@@ -41,6 +41,8 @@ def workload_case(name):
         return synth.cut_down(synth.aerial(n=200_000), 480, 272, n=40000)
     if name == "small_full":     # the whole small workload, 1297x840
         return synth.workload(1)
+    if name == "capacity_cut":   # 10 of the capacity batch's ring views: more than the step fuses
+        return synth.capacity(n=20000, width=200, height=120, views=10)
     raise KeyError(name)
 
 
@@ -162,16 +164,19 @@ def test_pipelined_step_matches_oracle(case):
         assert torch.equal(a.ranges, b.ranges), f"{case}/v{k} second-step ranges"
 
 
-@pytest.mark.parametrize("case", ["mid_cut", "small_cut"])
+@pytest.mark.parametrize("case", ["mid_cut", "small_cut", "capacity_cut"])
 def test_fused_step_matches_oracle(case):
-    """TrainStep.step() as bench.py runs it: the last view's projection
-    backward fused into the Adam pass.  The update against the oracle's
-    gradients (as check_adam), screen-space buffers left zero."""
+    """TrainStep.step() as bench.py runs it: the projection backward of the
+    last (up to eight) views fused into the Adam pass, that of any earlier
+    view (capacity_cut: two of ten) accumulated into the gradient planes
+    first.  The update against the oracle's gradients (as check_adam),
+    screen-space buffers left zero."""
     import differentiable_gaussian_splatting_dgs_amd as gs
     work = workload_case(case)
     p0 = work.params.copy()
     ref = oracle.step(work, dl_tol=DL_TOL)
     step = gs.from_workload(work, record_tiles=True)
+    assert step.nfirst == max(0, len(work.cameras) - gs.GS_MAX_FUSED_VIEWS)
     step.step()
     torch.cuda.synchronize()
     U = int(step.union_count.item())
