@@ -77,11 +77,17 @@ __global__ __launch_bounds__(256) void k_project_adam(FusedViews views, float* _
   const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (s >= *row_count) return;
   const int64_t i = rows[s];
+  // the 48 SH coefficient gradients accumulate in LDS (plane j + 11 of
+  // this thread at s_sh[j][tid]), the other 11 in registers
+  __shared__ float s_sh[48 * 256];
+  float* sh = s_sh + threadIdx.x;
   float p[59], g[59];
 #pragma unroll
   for (int k = 0; k < 59; ++k) p[k] = params[int64_t(k) * ld + i];
 #pragma unroll
-  for (int k = 0; k < 59; ++k) g[k] = grads != nullptr ? grads[int64_t(k) * ld + i] : 0.0f;
+  for (int k = 0; k < 11; ++k) g[k] = grads != nullptr ? grads[int64_t(k) * ld + i] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < 48; ++j) sh[j * 256] = grads != nullptr ? grads[int64_t(11 + j) * ld + i] : 0.0f;
   // the views are read in place from the argument segment (the first
   // argument sits at its start), so a view's camera is a few scalar loads
   (void)views;
@@ -101,19 +107,25 @@ __global__ __launch_bounds__(256) void k_project_adam(FusedViews views, float* _
       g2[2] = z4;
       const float grgb[3] = {gb4.z, gb4.w, gc4.x};
       const CamArgs cam = arg_camera(&fv->cam[w]);
-      project_grads<true>(p, cam, ga4.x, ga4.y, ga4.z, ga4.w, gb4.x, gb4.y, grgb, g);
+      project_grads<true, 256>(p, cam, ga4.x, ga4.y, ga4.z, ga4.w, gb4.x, gb4.y, grgb, g, sh);
     }
   }
   const float ob1 = 1.0f - b1, ob2 = 1.0f - b2;
   const float ibc1 = 1.0f / bc1, ibc2 = 1.0f / bc2;
+  // the row index passed through an empty asm: the plane addresses below
+  // are recomputed rather than kept alive (two registers each) from the
+  // loads at the top across the whole projection
+  int64_t ia = i;
+  asm volatile("" : "+v"(ia));
   // fully unrolled (p and g stay in registers: constant indices), in
   // groups of eight planes the scheduler may not merge, so the Adam state
   // of only one group is in flight at a time
 #pragma unroll
   for (int k = 0; k < 59; ++k) {
-    const int64_t q = int64_t(k) * ld + i;
-    const float mn = fmaf(b1, m[q], ob1 * g[k]);
-    const float vn = fmaf(b2, v[q], ob2 * g[k] * g[k]);
+    const int64_t q = int64_t(k) * ld + ia;
+    const float gk = k < 11 ? g[k] : sh[(k - 11) * 256];
+    const float mn = fmaf(b1, m[q], ob1 * gk);
+    const float vn = fmaf(b2, v[q], ob2 * gk * gk);
     m[q] = mn;
     v[q] = vn;
     params[q] = p[k] - lr * (mn * ibc1) / (sqrtf(vn * ibc2) + eps);

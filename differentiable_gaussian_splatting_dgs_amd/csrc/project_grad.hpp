@@ -38,11 +38,13 @@ __device__ __forceinline__ void put_grad(float& d, float v) {
 
 // p: the Gaussian's 59 parameters; (gu, gv, gA, gB, gC, go, gr, gg, gb): the
 // screen-space gradients (record order); g: the 59 parameter gradients
-// (kAdd: added to g, as g + this view's gradient).
-template <bool kAdd = false>
+// (kAdd: added to g, as g + this view's gradient).  With kShStride > 0 the
+// 48 SH coefficient gradients (planes 11..58) are added to sh[j kShStride],
+// j = plane - 11, instead of g (a caller that keeps them out of registers).
+template <bool kAdd = false, int kShStride = 0>
 __device__ __forceinline__ void project_grads(const float (&p)[59], const CamArgs& cam, float gu, float gv,
                                               float gA, float gB, float gC, float go, const float (&grgb)[3],
-                                              float (&g)[59]) {
+                                              float (&g)[59], float* sh = nullptr) {
   Fwd f;
   project(p, cam, f);
   // opacity logit
@@ -56,9 +58,15 @@ __device__ __forceinline__ void project_grads(const float (&p)[59], const CamArg
   float gY[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    put_grad<kAdd>(g[11 + 3 * k], gr[0] * Y[k]);
-    put_grad<kAdd>(g[12 + 3 * k], gr[1] * Y[k]);
-    put_grad<kAdd>(g[13 + 3 * k], gr[2] * Y[k]);
+    if constexpr (kShStride > 0) {
+      sh[(3 * k) * kShStride] += gr[0] * Y[k];
+      sh[(3 * k + 1) * kShStride] += gr[1] * Y[k];
+      sh[(3 * k + 2) * kShStride] += gr[2] * Y[k];
+    } else {
+      put_grad<kAdd>(g[11 + 3 * k], gr[0] * Y[k]);
+      put_grad<kAdd>(g[12 + 3 * k], gr[1] * Y[k]);
+      put_grad<kAdd>(g[13 + 3 * k], gr[2] * Y[k]);
+    }
     gY[k] = gr[0] * p[11 + 3 * k] + gr[1] * p[12 + 3 * k] + gr[2] * p[13 + 3 * k];
   }
   float gdx, gdy, gdz;
