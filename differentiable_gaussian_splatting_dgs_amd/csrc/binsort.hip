@@ -9,17 +9,15 @@
 // all pairs:
 //   1. the visible list (ascending indices) is radix-sorted stably by the
 //      32 depth bits -- V elements, not M;
-//   2. per block of depth ranks, its pairs in each tile column come from
-//      the Gaussians' tile rectangles (a difference array over columns);
-//   3. pairs are generated in depth order and written straight to their
-//      place in tile-column order (column start + earlier blocks + stable
-//      rank in the block), packed as row << 56 | index << 32 | depth bits;
-//   4. a stable pass on the row writes the final (key, value), the column
-//      coming from the pair's position (the column groups of step 3).
-//   Column then row is tile-id order, and every placement keeps the depth
-//   order (and the index order of equal depths) inside each tile.  Images
-//   over 256 tiles wide or tall, or 2^24 or more Gaussians, use plain
-//   stable LSD passes on 8-bit digits of the 64-bit keys instead.
+//   2. each Gaussian becomes one entry per super-tile (block of 8 x 8 or
+//      16 x 16 tiles) its tile rectangle meets, placed stably by super-tile,
+//      so every super-tile holds its entries in depth order;
+//   3. per chunk of a super-tile's list, each entry's covered tiles as a
+//      64-bit mask, transposed across a wave into per-tile bit columns: the
+//      pairs of a tile leave in depth order at exact slots (tile starts
+//      from per-chunk tile counts scanned in tile-id order).
+//   Images over 256 tiles wide or tall use plain stable LSD passes on 8-bit
+//   digits of the 64-bit keys instead.
 // Radix passes are reduce-then-scan: per-block digit histograms, a scan of
 // each digit row, then a scatter whose in-block rank comes from wave64
 // ballot matching (8 ballots per digit) and per-wave running counts in LDS.
@@ -211,93 +209,6 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
   }
 }
 
-// Row pass: row << 56 | index << 32 | depth bits, grouped by column (group
-// c starts at the exclusive scan of the column pass's digit totals
-// col_tot), -> final (tile << 32 | depth bits, Gaussian index) ordered by
-// row.  Each run of one tile in the block's sorted items also extends the
-// tile's range ([min start, max end) by atomics on a range array holding
-// (UINT_MAX, 0) beforehand).
-__global__ __launch_bounds__(kRT) void k_scatter_row(const uint64_t* __restrict__ pin, const int64_t* count_dev,
-                                                     int64_t count_host, const uint32_t* __restrict__ H,
-                                                     const uint32_t* __restrict__ rowtot, int nb,
-                                                     const uint32_t* __restrict__ col_tot, int32_t tiles_x,
-                                                     uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
-                                                     uint32_t* __restrict__ ranges) {
-  __shared__ RankSmem sm;
-  __shared__ uint32_t s_col[256];
-  __shared__ uint64_t s_p[kRB];
-  __shared__ uint8_t s_c[kRB];
-  const int64_t count = count_of(count_dev, count_host);
-  const int64_t bbase = int64_t(blockIdx.x) * kRB;
-  if (bbase >= count) return;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  {
-    uint32_t tot;
-    s_col[t] = block_exclusive_scan<kRT, uint32_t>(t < tiles_x ? col_tot[t] : 0u, sm.sc, tot);
-  }
-  __syncthreads();
-  uint64_t p[kRI];
-  uint32_t d[kRI], pos[kRI], cc[kRI];
-  const int64_t base = bbase + int64_t(w) * kWaveItems;
-#pragma unroll
-  for (int it = 0; it < kRI; ++it) {
-    const int64_t idx = base + it * 64 + lane;
-    p[it] = idx < count ? pin[idx] : 0ull;
-    d[it] = uint32_t(p[it] >> 56);
-  }
-  // column group of each item: the last c with s_col[c] <= idx (empty
-  // groups share their start with the next one, so the last such c is
-  // non-empty).  A thread's indices increase with `it`: one search for the
-  // first, a forward walk for the rest.
-  {
-    int c = 0;
-#pragma unroll
-    for (int step = 128; step >= 1; step >>= 1) c = int64_t(s_col[c + step]) <= base + lane ? c + step : c;
-#pragma unroll
-    for (int it = 0; it < kRI; ++it) {
-      const int64_t idx = base + it * 64 + lane;
-      while (c < 255 && int64_t(s_col[c + 1]) <= idx) ++c;
-      cc[it] = uint32_t(c);
-    }
-  }
-  rank_block(d, base, count, H, rowtot, nb, sm, pos);
-#pragma unroll
-  for (int it = 0; it < kRI; ++it) {
-    if (base + it * 64 + lane < count) {
-      s_p[pos[it]] = p[it];
-      s_c[pos[it]] = uint8_t(cc[it]);
-    }
-  }
-  __syncthreads();
-  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
-  auto tile_at = [&](int j) { return uint32_t(s_p[j] >> 56) * uint32_t(tiles_x) + s_c[j]; };
-  for (int j = t; j < nvalid; j += kRT) {
-    const uint64_t pj = s_p[j];
-    const uint32_t row = uint32_t(pj >> 56);
-    const uint32_t g = sm.gbase[row] + (uint32_t(j) - sm.dstart[row]);
-    const uint32_t tile = row * uint32_t(tiles_x) + s_c[j];
-    keys[g] = (uint64_t(tile) << 32) | (pj & 0xFFFFFFFFull);
-    vals[g] = uint32_t(pj >> 32) & 0xFFFFFFu;
-    if (j == 0 || tile_at(j - 1) != tile) atomicMin(ranges + 2 * size_t(tile), g);
-    if (j == nvalid - 1 || tile_at(j + 1) != tile) atomicMax(ranges + 2 * size_t(tile) + 1, g + 1);
-  }
-}
-
-// Range array before the row pass: (UINT_MAX, 0) per tile.
-__global__ __launch_bounds__(256) void k_init_ranges(uint32_t* __restrict__ ranges, int T) {
-  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
-  if (i < T) {
-    ranges[2 * i] = 0xFFFFFFFFu;
-    ranges[2 * i + 1] = 0u;
-  }
-}
-
-// After it: tiles no pair reached get [0, 0).
-__global__ __launch_bounds__(256) void k_fix_ranges(uint32_t* __restrict__ ranges, int T) {
-  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
-  if (i < T && ranges[2 * i] == 0xFFFFFFFFu) ranges[2 * i] = 0u;
-}
-
 // ---------------------------------------------------------------------------
 // pipeline kernels
 // ---------------------------------------------------------------------------
@@ -433,25 +344,47 @@ __global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ pr
 }
 
 // ---------------------------------------------------------------------------
-// exact placement of the pairs (images up to 256 x 256 tiles, < 2^24
-// Gaussians): tile-column then tile-row order without histogram passes
+// exact placement through super-tiles (images up to 256 x 256 tiles)
 // ---------------------------------------------------------------------------
+// A super-tile is an S x S block of tiles (S = 8, or 16 where an 8 grid
+// would exceed 256 blocks); the image holds SX x SY <= 256 of them.
+//   a. per block of kDB Gaussians in depth order: its entries in each
+//      super-tile (one entry per super-tile a tile rectangle meets; a
+//      difference array over the super-tile grid), and its pair total;
+//   b. entries generated in depth order and placed stably by super-tile
+//      (wave-ballot ranking on the 8-bit super-tile id), so each
+//      super-tile's list is in depth order; an entry holds the Gaussian,
+//      its depth bits and its rectangle clipped to the super-tile;
+//   c. each list is cut in chunks of kQ entries; per chunk its pairs in
+//      each of the S x S tiles (difference array), scanned over the
+//      super-tile's chunks, then over all tiles in tile-id order: every
+//      tile's range and each chunk's first slot in each tile;
+//   d. per chunk, thread (part p, tile t) walks part p of the chunk's
+//      entries in order and writes the pair of each entry that covers t at
+//      t's next slot.
+// Every step keeps the depth order inside a tile, and equal depths stay in
+// index order (the depth sort is stable over the ascending visible list).
 constexpr int kMaxT = 256;               // tile columns / rows this path handles
-constexpr int kPI = 4;                   // pairs per thread per chunk of the column placement
+constexpr int kQ = 512;                  // entries per chunk
+constexpr int kEI = 4;                   // entries per thread per round of step b
+constexpr int kMaxSide = 33;             // super-tile grid side + 1, at most
 
-// Per block of kDB Gaussians in depth order: its pair total (block_sums)
-// and its pairs in each tile column (colcnt[c][b], from a difference array
-// over columns: a rectangle adds its row count on [x0, x1)); block 0 also
-// clears the total slot colcnt[c][nbv].
-__global__ __launch_bounds__(kDT) void k_count_pairs(const float4* __restrict__ proj,
-                                                     const uint32_t* __restrict__ order,
-                                                     const int64_t* __restrict__ vis_count, int nbv, int tiles_x,
-                                                     int64_t* __restrict__ block_sums, uint32_t* __restrict__ colcnt) {
+struct StGrid {
+  int shift;     // S = 1 << shift tiles per super-tile side
+  int sx, sy;    // super-tiles across, down
+  int tx, ty;    // tiles across, down
+};
+
+// Step a.  block_sums[b]: pairs of block b; stcnt[s][b]: its entries in
+// super-tile s (block 0 also clears the total slot stcnt[s][nbv]).
+__global__ __launch_bounds__(kDT) void k_count_st(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+                                                  const int64_t* __restrict__ vis_count, int nbv, StGrid sg,
+                                                  int64_t* __restrict__ block_sums, uint32_t* __restrict__ stcnt) {
   __shared__ int64_t sh[kDT / 64];
-  __shared__ uint32_t s_sc[kDT / 64];
-  __shared__ int32_t s_cd[kMaxT + 1];
+  __shared__ int32_t s_cd[kMaxSide * kMaxSide];
   const int t = threadIdx.x;
-  for (int i = t; i <= kMaxT; i += kDT) s_cd[i] = 0;
+  const int W = sg.sx + 1;
+  for (int i = t; i < kMaxSide * kMaxSide; i += kDT) s_cd[i] = 0;
   __syncthreads();
   const int64_t V = *vis_count;
   const int64_t r0 = int64_t(blockIdx.x) * kDB;
@@ -461,51 +394,86 @@ __global__ __launch_bounds__(kDT) void k_count_pairs(const float4* __restrict__ 
     const int64_t r = r0 + t * kDI + k;
     if (r < V) {
       const float4 q3 = proj[4 * int64_t(order[r]) + 3];
-      const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
-      const int x0 = int(rx & 0xFFFFu), x1 = int(rx >> 16), y0 = int(ry & 0xFFFFu), y1 = int(ry >> 16);
-      s += __builtin_bit_cast(uint32_t, q3.w);
-      const int h = y1 - y0;
-      atomicAdd(&s_cd[x0], h);
-      atomicAdd(&s_cd[x1], -h);
+      const uint32_t tiles = __builtin_bit_cast(uint32_t, q3.w);
+      s += tiles;
+      if (tiles != 0) {
+        const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
+        const int a0 = int(rx & 0xFFFFu) >> sg.shift, a1 = (int((rx >> 16) - 1u) >> sg.shift) + 1;
+        const int b0 = int(ry & 0xFFFFu) >> sg.shift, b1 = (int((ry >> 16) - 1u) >> sg.shift) + 1;
+        atomicAdd(&s_cd[b0 * W + a0], 1);
+        atomicAdd(&s_cd[b0 * W + a1], -1);
+        atomicAdd(&s_cd[b1 * W + a0], -1);
+        atomicAdd(&s_cd[b1 * W + a1], 1);
+      }
     }
   }
   int64_t tot;
   block_exclusive_scan<kDT, int64_t>(s, sh, tot);
   if (t == 0) block_sums[blockIdx.x] = tot;
-  // column counts: inclusive prefix of the column differences (mod 2^32)
-  const uint32_t v = uint32_t(s_cd[t]);
-  uint32_t vt;
-  const uint32_t incl = block_exclusive_scan<kDT, uint32_t>(v, s_sc, vt) + v;
-  if (t < tiles_x) {
-    colcnt[size_t(t) * (nbv + 1) + blockIdx.x] = incl;
-    if (blockIdx.x == 0) colcnt[size_t(t) * (nbv + 1) + nbv] = 0u;
+  // 2-D inclusive prefix of the differences: rows, then columns
+  if (t < sg.sy) {
+    int acc = 0;
+    for (int x = 0; x < sg.sx; ++x) s_cd[t * W + x] = acc += s_cd[t * W + x];
+  }
+  __syncthreads();
+  if (t < sg.sx) {
+    int acc = 0;
+    for (int y = 0; y < sg.sy; ++y) s_cd[y * W + t] = acc += s_cd[y * W + t];
+  }
+  __syncthreads();
+  if (t < sg.sx * sg.sy) {
+    stcnt[size_t(t) * (nbv + 1) + blockIdx.x] = uint32_t(s_cd[(t / sg.sx) * W + t % sg.sx]);
+    if (blockIdx.x == 0) stcnt[size_t(t) * (nbv + 1) + nbv] = 0u;
   }
 }
 
-// Pairs of a block of kDB Gaussians (depth order) straight into tile-column
-// order: generated in order (depth rank, rectangle row-major) in chunks of
-// kDT * kPI, ranked stably by column, and written at col_start[c] +
-// colcnt[c][b] (pairs of c in earlier blocks) + pairs of c in earlier
-// chunks + rank, each as row << 56 | Gaussian index << 32 | depth bits.
-__global__ __launch_bounds__(kDT) void k_dup_col(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
-                                                 const int64_t* __restrict__ vis_count,
-                                                 const uint32_t* __restrict__ colcnt,
-                                                 const uint32_t* __restrict__ coltot, int nbv, int tiles_x,
-                                                 const int64_t* __restrict__ m_eff, uint64_t* __restrict__ out) {
+// Super-tile list starts and chunk numbering: st_start[s] (exclusive scan
+// of the entry totals sttot), chunk_base[s] (exclusive scan of
+// ceil(sttot / kQ)), chunk_base[ns] = number of chunks.
+__global__ __launch_bounds__(256) void k_st_bases(const uint32_t* __restrict__ sttot, int ns,
+                                                  uint32_t* __restrict__ st_start, uint32_t* __restrict__ chunk_base) {
+  __shared__ uint32_t sh[4];
+  const int t = threadIdx.x;
+  const uint32_t c = t < ns ? sttot[t] : 0u;
+  uint32_t tot, ctot;
+  const uint32_t ex = block_exclusive_scan<256, uint32_t>(c, sh, tot);
+  const uint32_t cex = block_exclusive_scan<256, uint32_t>((c + kQ - 1) / kQ, sh, ctot);
+  if (t < ns) {
+    st_start[t] = ex;
+    chunk_base[t] = cex;
+  }
+  if (t == 0) chunk_base[ns] = ctot;
+}
+
+// Step b.  Entries of a block of kDB Gaussians (depth order) in order
+// (depth rank, super-tiles of the rectangle row-major), in chunks of
+// kDT * kEI, ranked stably by super-tile and written at st_start[s] +
+// stcnt[s][b] (entries of s in earlier blocks) + entries of s in earlier
+// chunks + rank.  Entry: Gaussian index, depth bits, clipped rectangle
+// x0 | (w - 1) << 4 | y0 << 8 | (h - 1) << 12 in tiles of the super-tile.
+__global__ __launch_bounds__(kDT) void k_dup_st(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+                                                const uint32_t* __restrict__ depth,
+                                                const int64_t* __restrict__ vis_count,
+                                                const uint32_t* __restrict__ stcnt,
+                                                const uint32_t* __restrict__ st_start, int nbv, StGrid sg,
+                                                const int64_t* __restrict__ m_eff, uint32_t* __restrict__ e_g,
+                                                uint32_t* __restrict__ e_d, uint32_t* __restrict__ e_r) {
   __shared__ int64_t sh[kDT / 64];
-  __shared__ uint32_t s_off[kDB];        // exclusive pair offset within the block
-  __shared__ uint32_t s_rx[kDB];         // x0 | width << 16
-  __shared__ uint32_t s_y0[kDB];
+  __shared__ uint32_t s_off[kDB];        // exclusive entry offset within the block
+  __shared__ uint32_t s_rx[kDB];         // x0 | x1 << 16 (tiles)
+  __shared__ uint32_t s_ry[kDB];         // y0 | y1 << 16
   __shared__ uint32_t s_g[kDB];
   __shared__ uint32_t s_dep[kDB];
-  __shared__ uint32_t s_cb[kMaxT];       // running destination of each column
+  __shared__ uint32_t s_cb[256];         // running destination of each super-tile
   __shared__ RankSmem sm;
-  __shared__ uint64_t s_p[kDT * kPI];
-  __shared__ uint8_t s_d[kDT * kPI];
-  if (m_eff != nullptr && *m_eff == 0) return;        // no pairs, or more than the buffers hold
+  __shared__ uint16_t s_pl[kDT * kEI];   // staged entries in super-tile order: Gaussian slot,
+  __shared__ uint16_t s_pr[kDT * kEI];   // clipped rectangle,
+  __shared__ uint8_t s_ps[kDT * kEI];    // super-tile
+  if (*m_eff == 0) return;               // no pairs, or more than the buffers hold
   const int64_t V = *vis_count;
   const int64_t r0 = int64_t(blockIdx.x) * kDB;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int S = 1 << sg.shift;
   uint32_t cnt[kDI];
   uint32_t s = 0;
 #pragma unroll
@@ -516,11 +484,14 @@ __global__ __launch_bounds__(kDT) void k_dup_col(const float4* __restrict__ proj
       const uint32_t g = order[r];
       const float4 q3 = proj[4 * int64_t(g) + 3];
       const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
-      const uint32_t x0 = rx & 0xFFFFu, x1 = rx >> 16;
-      cnt[k] = __builtin_bit_cast(uint32_t, q3.w);
-      s_rx[t * kDI + k] = x0 | ((x1 - x0) << 16);
-      s_y0[t * kDI + k] = ry & 0xFFFFu;
-      s_dep[t * kDI + k] = __builtin_bit_cast(uint32_t, q3.x);
+      if (__builtin_bit_cast(uint32_t, q3.w) != 0u) {
+        const uint32_t a0 = (rx & 0xFFFFu) >> sg.shift, a1 = (((rx >> 16) - 1u) >> sg.shift) + 1u;
+        const uint32_t b0 = (ry & 0xFFFFu) >> sg.shift, b1 = (((ry >> 16) - 1u) >> sg.shift) + 1u;
+        cnt[k] = (a1 - a0) * (b1 - b0);
+      }
+      s_rx[t * kDI + k] = rx;
+      s_ry[t * kDI + k] = ry;
+      s_dep[t * kDI + k] = depth[r];
       s_g[t * kDI + k] = g;
     }
     s += cnt[k];
@@ -529,53 +500,286 @@ __global__ __launch_bounds__(kDT) void k_dup_col(const float4* __restrict__ proj
   uint32_t off = uint32_t(block_exclusive_scan<kDT, int64_t>(int64_t(s), sh, tot));
 #pragma unroll
   for (int k = 0; k < kDI; ++k) {
-    // absent entries (past the visible count) get an offset no pair reaches
+    // absent entries (past the visible count) get an offset no entry reaches
     s_off[t * kDI + k] = r0 + t * kDI + k < V ? off : 0xFFFFFFFFu;
     off += cnt[k];
   }
-  {
-    uint32_t ct;
-    const uint32_t cstart = block_exclusive_scan<kDT, uint32_t>(t < tiles_x ? coltot[t] : 0u, sm.sc, ct);
-    s_cb[t] = t < tiles_x ? cstart + colcnt[size_t(t) * (nbv + 1) + blockIdx.x] : 0u;
-  }
+  const int ns = sg.sx * sg.sy;
+  s_cb[t] = t < ns ? st_start[t] + stcnt[size_t(t) * (nbv + 1) + blockIdx.x] : 0u;
   __syncthreads();
   const uint32_t total = uint32_t(tot);
-  for (uint32_t c0 = 0; c0 < total; c0 += kDT * kPI) {
-    uint32_t d[kPI], pos[kPI];
-    bool valid[kPI];
-    uint64_t pk[kPI];
+  for (uint32_t c0 = 0; c0 < total; c0 += kDT * kEI) {
+    uint32_t d[kEI], pos[kEI], rect[kEI], slot[kEI];
+    bool valid[kEI];
 #pragma unroll
-    for (int it = 0; it < kPI; ++it) {
-      const uint32_t o = c0 + uint32_t(w * kPI * 64 + it * 64 + lane);
+    for (int it = 0; it < kEI; ++it) {
+      const uint32_t o = c0 + uint32_t(w * kEI * 64 + it * 64 + lane);
       valid[it] = o < total;
       d[it] = 0;
-      pk[it] = 0;
+      rect[it] = 0;
+      slot[it] = 0;
       if (valid[it]) {
         const int lo = last_at_or_below(s_off, o);
         const uint32_t local = o - s_off[lo];
-        const uint32_t rx = s_rx[lo];
-        const uint32_t wd = rx >> 16;
-        const uint32_t ty = s_y0[lo] + local / wd, tx = (rx & 0xFFFFu) + local % wd;
-        d[it] = tx;
-        pk[it] = (uint64_t(ty) << 56) | (uint64_t(s_g[lo]) << 32) | s_dep[lo];
+        const uint32_t rx = s_rx[lo], ry = s_ry[lo];
+        const uint32_t x0 = rx & 0xFFFFu, x1 = rx >> 16, y0 = ry & 0xFFFFu, y1 = ry >> 16;
+        const uint32_t a0 = x0 >> sg.shift, na = (((x1 - 1u) >> sg.shift) + 1u) - a0;
+        const uint32_t ea = a0 + local % na, eb = (y0 >> sg.shift) + local / na;
+        const uint32_t bx = ea << sg.shift, by = eb << sg.shift;
+        const uint32_t lx0 = (x0 > bx ? x0 : bx) - bx, lx1 = (x1 < bx + S ? x1 : bx + S) - bx;
+        const uint32_t ly0 = (y0 > by ? y0 : by) - by, ly1 = (y1 < by + S ? y1 : by + S) - by;
+        d[it] = eb * uint32_t(sg.sx) + ea;
+        rect[it] = lx0 | ((lx1 - lx0 - 1u) << 4) | (ly0 << 8) | ((ly1 - ly0 - 1u) << 12);
+        slot[it] = uint32_t(lo);
       }
     }
-    rank_chunk<kPI>(d, valid, sm, pos);
+    rank_chunk<kEI>(d, valid, sm, pos);
 #pragma unroll
-    for (int it = 0; it < kPI; ++it) {
+    for (int it = 0; it < kEI; ++it) {
       if (valid[it]) {
-        s_p[pos[it]] = pk[it];
-        s_d[pos[it]] = uint8_t(d[it]);
+        s_pl[pos[it]] = uint16_t(slot[it]);
+        s_pr[pos[it]] = uint16_t(rect[it]);
+        s_ps[pos[it]] = uint8_t(d[it]);
       }
     }
     __syncthreads();
-    const int nvalid = int(total - c0 < uint32_t(kDT * kPI) ? total - c0 : uint32_t(kDT * kPI));
+    const int nvalid = int(total - c0 < uint32_t(kDT * kEI) ? total - c0 : uint32_t(kDT * kEI));
     for (int j = t; j < nvalid; j += kDT) {
-      const uint32_t dd = s_d[j];
-      out[s_cb[dd] + (uint32_t(j) - sm.dstart[dd])] = s_p[j];
+      const uint32_t st = s_ps[j];
+      const uint32_t dst = s_cb[st] + (uint32_t(j) - sm.dstart[st]);
+      const uint32_t lo = s_pl[j];
+      e_g[dst] = s_g[lo];
+      e_d[dst] = s_dep[lo];
+      e_r[dst] = s_pr[j];
     }
     __syncthreads();
     s_cb[t] += sm.dcnt[t];
+    __syncthreads();
+  }
+}
+
+// Super-tile s of chunk c and its entry span [e0, e1).
+__device__ __forceinline__ void chunk_span(const uint32_t* __restrict__ chunk_base,
+                                           const uint32_t* __restrict__ st_start,
+                                           const uint32_t* __restrict__ sttot, int ns, uint32_t c, int& s,
+                                           uint32_t& e0, uint32_t& e1) {
+  // the last s with chunk_base[s] <= c (super-tiles without chunks share
+  // the next one's base, so the last such s has chunks)
+  int lo = 0;
+#pragma unroll
+  for (int step = 128; step >= 1; step >>= 1) lo = (lo + step < ns && chunk_base[lo + step] <= c) ? lo + step : lo;
+  s = lo;
+  e0 = st_start[lo] + (c - chunk_base[lo]) * uint32_t(kQ);
+  const uint32_t end = st_start[lo] + sttot[lo];
+  e1 = e0 + uint32_t(kQ) < end ? e0 + uint32_t(kQ) : end;
+}
+
+// Step c, first half: pairs of chunk c in local tile t (ly * S + lx) to
+// cc[c][t] (a difference array over the S x S tiles).
+__global__ __launch_bounds__(256) void k_count_chunk(const uint32_t* __restrict__ chunk_base,
+                                                     const uint32_t* __restrict__ st_start,
+                                                     const uint32_t* __restrict__ sttot, int ns,
+                                                     const uint32_t* __restrict__ e_r, StGrid sg,
+                                                     const int64_t* __restrict__ m_eff, uint32_t* __restrict__ cc) {
+  __shared__ int32_t s_cd[17 * 17];
+  if (*m_eff == 0) return;
+  const int t = threadIdx.x;
+  const int S = 1 << sg.shift, W = S + 1;
+  const uint32_t C = chunk_base[ns];
+  for (uint32_t c = blockIdx.x; c < C; c += gridDim.x) {
+    for (int i = t; i < W * W; i += 256) s_cd[i] = 0;
+    __syncthreads();
+    int s;
+    uint32_t e0, e1;
+    chunk_span(chunk_base, st_start, sttot, ns, c, s, e0, e1);
+    for (uint32_t e = e0 + uint32_t(t); e < e1; e += 256) {
+      const uint32_t r = e_r[e];
+      const int x0 = int(r & 15u), x1 = x0 + int((r >> 4) & 15u) + 1;
+      const int y0 = int((r >> 8) & 15u), y1 = y0 + int(r >> 12) + 1;
+      atomicAdd(&s_cd[y0 * W + x0], 1);
+      atomicAdd(&s_cd[y0 * W + x1], -1);
+      atomicAdd(&s_cd[y1 * W + x0], -1);
+      atomicAdd(&s_cd[y1 * W + x1], 1);
+    }
+    __syncthreads();
+    if (t < S) {
+      int acc = 0;
+      for (int x = 0; x < S; ++x) s_cd[t * W + x] = acc += s_cd[t * W + x];
+    }
+    __syncthreads();
+    if (t < S) {
+      int acc = 0;
+      for (int y = 0; y < S; ++y) s_cd[y * W + t] = acc += s_cd[y * W + t];
+    }
+    __syncthreads();
+    if (t < S * S) cc[size_t(c) * 256 + t] = uint32_t(s_cd[(t >> sg.shift) * W + (t & (S - 1))]);
+    __syncthreads();
+  }
+}
+
+// Step c, second half: per super-tile (one block each), cc scanned over its
+// chunks for each local tile (exclusive, in place); each tile's pair count
+// to ranges[2 tile] (k_tile_ranges turns the counts into ranges).
+__global__ __launch_bounds__(256) void k_scan_chunks(const uint32_t* __restrict__ chunk_base, StGrid sg,
+                                                     const int64_t* __restrict__ m_eff, uint32_t* __restrict__ cc,
+                                                     uint32_t* __restrict__ ranges) {
+  const int s = blockIdx.x, t = threadIdx.x;
+  const int S = 1 << sg.shift;
+  if (t >= S * S) return;
+  const int tx = (s % sg.sx) * S + (t & (S - 1)), ty = (s / sg.sx) * S + (t >> sg.shift);
+  uint32_t run = 0;
+  if (*m_eff != 0) {
+    // sixteen chunks' counts loaded together, then scanned
+    const uint32_t c0 = chunk_base[s], c1 = chunk_base[s + 1];
+    for (uint32_t cb = c0; cb < c1; cb += 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = cb + uint32_t(k) < c1 ? cc[size_t(cb + uint32_t(k)) * 256 + t] : 0u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (cb + uint32_t(k) < c1) cc[size_t(cb + uint32_t(k)) * 256 + t] = run;
+        run += v[k];
+      }
+    }
+  }
+  if (tx < sg.tx && ty < sg.ty) ranges[2 * size_t(ty * sg.tx + tx)] = run;
+}
+
+// Tile counts (ranges[2 tile]) -> ranges [start, end) in tile-id order;
+// empty tiles [0, 0).  One workgroup.
+__global__ __launch_bounds__(1024) void k_tile_ranges(int nT, uint32_t* __restrict__ ranges) {
+  __shared__ uint32_t sh[16];
+  __shared__ uint32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < nT; base += 1024) {
+    const int i = base + int(threadIdx.x);
+    const uint32_t v = i < nT ? ranges[2 * i] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<1024, uint32_t>(v, sh, tot);
+    if (i < nT) {
+      const uint32_t start = carry + ex;
+      ranges[2 * i] = v != 0 ? start : 0u;
+      ranges[2 * i + 1] = v != 0 ? start + v : 0u;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+}
+
+// 64 x 64 bit transpose across a wave: lane r holds row r (bit c = element
+// (r, c)); on return lane c holds column c (bit r = element (r, c)).  Six
+// stages, each exchanging the off-diagonal j x j blocks of every 2j x 2j
+// block with the partner lane r ^ j.
+__device__ __forceinline__ uint64_t wave_transpose64(uint64_t x, uint32_t lane) {
+  constexpr uint64_t kHi[6] = {0xFFFFFFFF00000000ull, 0xFFFF0000FFFF0000ull, 0xFF00FF00FF00FF00ull,
+                               0xF0F0F0F0F0F0F0F0ull, 0xCCCCCCCCCCCCCCCCull, 0xAAAAAAAAAAAAAAAAull};
+#pragma unroll
+  for (int st = 0; st < 6; ++st) {
+    const int j = 32 >> st;
+    const uint32_t lo = uint32_t(x), hi = uint32_t(x >> 32);
+    const uint64_t y = uint64_t(uint32_t(__shfl_xor(int(lo), j, 64))) |
+                       (uint64_t(uint32_t(__shfl_xor(int(hi), j, 64))) << 32);
+    x = (lane & uint32_t(j)) == 0 ? (x & ~kHi[st]) | ((y & ~kHi[st]) << j) : (x & kHi[st]) | ((y & kHi[st]) >> j);
+  }
+  return x;
+}
+
+// Step d, one block per (chunk, panel of 64 tiles of its super-tile: all
+// 8 x 8 tiles, or 4 rows of a 16 x 16 super-tile).  Entry i of the chunk
+// covers a set of the panel's tiles (a 64-bit mask from its clipped
+// rectangle); for each batch k of 64 entries the masks are transposed, so
+// column word cw[k][t] has bit b set when entry 64 k + b covers tile t.
+// Tile t's pairs from batch k then go to its start + the chunk's slot
+// cc[c][t] + the pairs of t in batches before k + the rank of b among the
+// set bits of cw[k][t]: one round per (k, t), whose active lanes write
+// consecutive slots.
+__global__ __launch_bounds__(256) void k_expand(const uint32_t* __restrict__ chunk_base,
+                                                const uint32_t* __restrict__ st_start,
+                                                const uint32_t* __restrict__ sttot, int ns,
+                                                const uint32_t* __restrict__ e_g, const uint32_t* __restrict__ e_d,
+                                                const uint32_t* __restrict__ e_r, const uint32_t* __restrict__ cc,
+                                                const uint32_t* __restrict__ ranges, StGrid sg,
+                                                const int64_t* __restrict__ m_eff, uint64_t* __restrict__ keys,
+                                                uint32_t* __restrict__ vals) {
+  constexpr int kK = kQ / 64;                                   // batches of 64 entries per chunk
+  __shared__ uint64_t s_cw[kK][64];
+  __shared__ uint32_t s_pre[kK][64];
+  __shared__ uint32_t s_base[64];
+  __shared__ uint32_t s_tile[64];
+  __shared__ uint32_t s_eg[kQ];
+  __shared__ uint32_t s_ed[kQ];
+  if (*m_eff == 0) return;
+  const uint32_t t = threadIdx.x, lane = t & 63u, w = t >> 6;
+  const uint32_t S = 1u << sg.shift;
+  const uint32_t qshift = 2u * uint32_t(sg.shift) - 6u;        // panels per super-tile: 1 or 4
+  const uint32_t rows = 64u >> sg.shift;                        // tile rows per panel: 8 or 4
+  const uint64_t rep = sg.shift == 3 ? 0x0101010101010101ull : 0x0001000100010001ull;
+  const uint32_t tasks = chunk_base[ns] << qshift;
+  for (uint32_t task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const uint32_t c = task >> qshift, q = task & ((1u << qshift) - 1u);
+    int s;
+    uint32_t e0, e1;
+    chunk_span(chunk_base, st_start, sttot, ns, c, s, e0, e1);
+    const uint32_t n = e1 - e0, r0 = q * rows;
+    // entries -> panel masks, transposed per batch of 64 (wave w: batches w, w + 4)
+#pragma unroll
+    for (int h = 0; h < kK / 4; ++h) {
+      const uint32_t k = w + 4u * uint32_t(h), i = 64u * k + lane;
+      uint64_t m = 0;
+      if (i < n) {
+        const uint32_t r = e_r[e0 + i];
+        s_eg[i] = e_g[e0 + i];
+        s_ed[i] = e_d[e0 + i];
+        const uint32_t x0 = r & 15u, wd = ((r >> 4) & 15u) + 1u, y0 = (r >> 8) & 15u, y1 = y0 + (r >> 12) + 1u;
+        const uint32_t ya = y0 > r0 ? y0 : r0, yb = y1 < r0 + rows ? y1 : r0 + rows;
+        if (ya < yb) {
+          const uint64_t cm = ((1ull << wd) - 1ull) << x0;
+          const uint64_t rm = (~0ull >> (64u - S * (yb - ya))) << (S * (ya - r0));
+          m = (cm * rep) & rm;
+        }
+      }
+      const uint64_t cw = wave_transpose64(m, lane);
+      s_cw[k][lane] = cw;
+      s_pre[k][lane] = uint32_t(__popcll(cw));
+    }
+    if (t < 64) {
+      const uint32_t ly = r0 + (lane >> sg.shift), lx = lane & (S - 1u);
+      const uint32_t tx = uint32_t(s % sg.sx) * S + lx, ty = uint32_t(s / sg.sx) * S + ly;
+      const bool inside = tx < uint32_t(sg.tx) && ty < uint32_t(sg.ty);
+      const uint32_t tile = inside ? ty * uint32_t(sg.tx) + tx : 0u;
+      s_tile[lane] = tile;
+      s_base[lane] = inside ? ranges[2 * size_t(tile)] + cc[size_t(c) * 256 + (ly << sg.shift) + lx] : 0u;
+    }
+    __syncthreads();
+    if (t < 64) {
+      uint32_t run = s_base[lane];
+#pragma unroll
+      for (int k = 0; k < kK; ++k) {
+        const uint32_t v = s_pre[k][lane];
+        s_pre[k][lane] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    // rounds (k, tile): lane b writes entry 64 k + b's pair when it covers the tile
+#pragma unroll
+    for (int h = 0; h < kK / 4; ++h) {
+      const uint32_t k = w + 4u * uint32_t(h);
+      if (64u * k >= n) break;
+      const uint32_t i = 64u * k + lane;
+      const uint32_t g = i < n ? s_eg[i] : 0u, d = i < n ? s_ed[i] : 0u;
+      for (uint32_t tt = 0; tt < 64; ++tt) {
+        const uint64_t cw = s_cw[k][tt];
+        if (cw == 0) continue;
+        if ((cw >> lane) & 1ull) {
+          const uint32_t pos = s_pre[k][tt] + uint32_t(count_below(cw));
+          keys[pos] = (uint64_t(s_tile[tt]) << 32) | d;
+          vals[pos] = g;
+        }
+      }
+    }
     __syncthreads();
   }
 }
@@ -672,14 +876,21 @@ struct Ws {
   uint32_t *dkA, *dvA, *dkB, *dvB;   // depth sort ping-pong [n]
   uint32_t* H;                       // radix histograms [256][nb]
   uint32_t* rowtot;                  // [256]
-  uint32_t* coltot;                  // [256], pairs per tile column
+  uint32_t* sttot;                   // [256], entries per super-tile
+  uint32_t* st_start;                // [256], super-tile list starts
+  uint32_t* chunk_base;              // [257], first chunk of each super-tile; number of chunks
   int64_t* bsums;                    // per-block tile sums [nbv + 1]
   int64_t* m_dev;                    // pair count
   int64_t* m_eff;                    // pair count if within capacity, else 0
-  uint32_t* colcnt;                  // [kMaxT][nbv + 1], pairs per (column, block), then scanned
-  uint64_t* pk;                      // pair keys scratch [cap]
-  uint32_t* pv;                      // pair values scratch [cap]
+  uint32_t* stcnt;                   // [256][nbv + 1], entries per (super-tile, block), then scanned
+  uint32_t* cc;                      // [max_chunks(cap)][256], pairs per (chunk, local tile), then scanned
+  uint64_t* pk;                      // pair keys scratch [cap]; super-tile entries (index, depth)
+  uint32_t* pv;                      // pair values scratch [cap]; super-tile entry rectangles
 };
+
+// Chunks of the super-tile lists: at most one partial chunk per super-tile
+// beyond the entries / kQ full ones (entries <= pairs <= capacity).
+inline int64_t max_chunks(int64_t cap) { return cap / kQ + 257; }
 
 inline int64_t nblocks(int64_t count) { return (count + kRB - 1) / kRB; }
 inline int64_t dup_blocks(int64_t n) { return (n + kDB - 1) / kDB; }
@@ -698,11 +909,14 @@ Ws carve(void* ws, int64_t n, int64_t cap, size_t* bytes = nullptr) {
   w.dvB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.H = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(nbh)));
   w.rowtot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
-  w.coltot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
+  w.sttot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
+  w.st_start = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
+  w.chunk_base = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 257));
   w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t(nbv + 1)));
   w.m_dev = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.m_eff = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
-  w.colcnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kMaxT * size_t(nbv + 1)));
+  w.stcnt = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(nbv + 1)));
+  w.cc = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(max_chunks(cap))));
   w.pk = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * size_t(cap)));
   w.pv = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(cap)));
   if (bytes != nullptr) *bytes = at;
@@ -715,9 +929,26 @@ size_t carve_bytes(int64_t n, int64_t cap) {
   return b;
 }
 
-// The exact-placement path: column and row fit a byte, Gaussian indices 24 bits.
-inline bool exact_path(int64_t n, int32_t tiles_x, int32_t tiles_y) {
-  return tiles_x <= kMaxT && tiles_y <= kMaxT && n < (int64_t(1) << 24);
+// The super-tile path: images up to 256 x 256 tiles (at most 16 x 16
+// super-tiles of 16 x 16 tiles).
+inline bool exact_path(int32_t tiles_x, int32_t tiles_y) { return tiles_x <= kMaxT && tiles_y <= kMaxT; }
+
+// Super-tiles of 8 x 8 tiles where at most 256 of them cover the image,
+// else 16 x 16.
+inline StGrid st_grid(int32_t tiles_x, int32_t tiles_y) {
+  StGrid g;
+  g.tx = tiles_x;
+  g.ty = tiles_y;
+  for (g.shift = 3; g.shift < 4; ++g.shift) {
+    const int S = 1 << g.shift;
+    if (((tiles_x + S - 1) / S) * ((tiles_y + S - 1) / S) <= 256 && (tiles_x + S - 1) / S < kMaxSide &&
+        (tiles_y + S - 1) / S < kMaxSide)
+      break;
+  }
+  const int S = 1 << g.shift;
+  g.sx = (tiles_x + S - 1) / S;
+  g.sy = (tiles_y + S - 1) / S;
+  return g;
 }
 
 template <class K>
@@ -753,10 +984,13 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
     }
   }
   const int nbv = int(dup_blocks(n));
-  if (nbv > 0 && exact_path(n, tiles_x, tiles_y)) {
-    // pair totals and per-(column, block) counts
-    k_count_pairs<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, nbv, tiles_x, w.bsums, w.colcnt);
-    k_rowscan<<<unsigned(tiles_x), kRT, 0, st>>>(w.colcnt, nbv + 1, w.coltot);
+  if (nbv > 0 && exact_path(tiles_x, tiles_y)) {
+    // pair totals, entries per (super-tile, block), list starts and chunks
+    const StGrid sg = st_grid(tiles_x, tiles_y);
+    const int ns = sg.sx * sg.sy;
+    k_count_st<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, nbv, sg, w.bsums, w.stcnt);
+    k_rowscan<<<unsigned(ns), kRT, 0, st>>>(w.stcnt, nbv + 1, w.sttot);
+    k_st_bases<<<1, 256, 0, st>>>(w.sttot, ns, w.st_start, w.chunk_base);
   } else if (nbv > 0) {
     k_tilesum<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
   }
@@ -786,18 +1020,25 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     m_dev = w.m_eff;
     bound = pair_capacity;
   }
-  if (!on_device && M_host == 0) {
+  if (exact_path(tiles_x, tiles_y) && nbv > 0) {
+    // super-tile entries, per-chunk tile counts, ranges, then the pairs;
+    // every kernel reads the effective count (0: no pairs or overflow)
+    if (!on_device) k_eff_count<<<1, 64, 0, st>>>(w.m_dev, pair_capacity, w.m_eff, nullptr);
+    const StGrid sg = st_grid(tiles_x, tiles_y);
+    const int ns = sg.sx * sg.sy;
+    const unsigned grid = unsigned(std::min<int64_t>(max_chunks(pair_capacity), 2048));
+    const unsigned egrid = unsigned(std::min<int64_t>(max_chunks(pair_capacity) * 4, 4096));
+    uint32_t* e_g = reinterpret_cast<uint32_t*>(w.pk);
+    uint32_t* e_d = e_g + pair_capacity;
+    uint32_t* e_r = w.pv;
+    k_dup_st<<<nbv, kDT, 0, st>>>(P, w.dvA, w.dkA, vis_count, w.stcnt, w.st_start, nbv, sg, w.m_eff, e_g, e_d, e_r);
+    k_count_chunk<<<grid, 256, 0, st>>>(w.chunk_base, w.st_start, w.sttot, ns, e_r, sg, w.m_eff, w.cc);
+    k_scan_chunks<<<unsigned(ns), 256, 0, st>>>(w.chunk_base, sg, w.m_eff, w.cc, ranges);
+    k_tile_ranges<<<1, 1024, 0, st>>>(int(T), ranges);
+    k_expand<<<egrid, 256, 0, st>>>(w.chunk_base, w.st_start, w.sttot, ns, e_g, e_d, e_r, w.cc, ranges, sg, w.m_eff,
+                                   keys, uvals);
+  } else if (!on_device && M_host == 0) {
     k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
-  } else if (exact_path(n, tiles_x, tiles_y)) {
-    // pairs straight into tile-column order, then a stable pass on the row
-    const int nb = int(std::max<int64_t>(1, nblocks(bound)));
-    if (nbv > 0) k_dup_col<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.colcnt, w.coltot, nbv, tiles_x, m_dev, w.pk);
-    k_upsweep<uint64_t><<<nb, kRT, 0, st>>>(w.pk, m_dev, M_host, 56, w.H, nb);
-    k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
-    k_init_ranges<<<unsigned((T + 255) / 256), 256, 0, st>>>(ranges, int(T));
-    k_scatter_row<<<nb, kRT, 0, st>>>(w.pk, m_dev, M_host, w.H, w.rowtot, nb, w.coltot, tiles_x, keys, uvals,
-                                      ranges);
-    k_fix_ranges<<<unsigned((T + 255) / 256), 256, 0, st>>>(ranges, int(T));
   } else {
     // number of 8-bit passes over the tile bits
     int tbits = 0;
