@@ -170,7 +170,8 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   REQUIRE(workspace_bytes >= gs::binsort_ws_bytes(n, pair_capacity), "workspace too small");
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
-  hipError_t e = gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, TX, TY, workspace, pair_capacity, st);
+  hipError_t e =
+      gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, TX, TY, nullptr, workspace, pair_capacity, st);
   if (e != hipSuccess) return hip_status(e, "gs_bin_sort (depth sort)");
   int64_t M = 0;
   e = hipMemcpyAsync(&M, gs::binsort_count_ptr(workspace, n, pair_capacity), sizeof(int64_t), hipMemcpyDeviceToHost,
@@ -181,7 +182,7 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   if (M > pair_capacity)
     return fail(GS_ERR_CAPACITY, "%lld pairs > capacity %lld", (long long)M, (long long)pair_capacity);
   e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, M, TX, TY, keys, vals, tile_ranges, tile_order,
-                                nullptr, workspace, pair_capacity, st);
+                                workspace, pair_capacity, st);
   return hip_status(e, "gs_bin_sort");
 }
 
@@ -200,10 +201,11 @@ gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx
   REQUIRE(workspace_bytes >= gs::binsort_ws_bytes(n, pair_capacity), "workspace too small");
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
-  hipError_t e = gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, TX, TY, workspace, pair_capacity, st);
+  hipError_t e =
+      gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, TX, TY, num_pairs_dev, workspace, pair_capacity, st);
   if (e != hipSuccess) return hip_status(e, "gs_bin_sort_async (depth sort)");
   e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, -1, TX, TY, keys, vals, tile_ranges, tile_order,
-                                num_pairs_dev, workspace, pair_capacity, st);
+                                workspace, pair_capacity, st);
   return hip_status(e, "gs_bin_sort_async");
 }
 

@@ -258,23 +258,6 @@ __global__ __launch_bounds__(kDT) void k_tilesum(const float4* __restrict__ proj
   if (threadIdx.x == 0) block_sums[blockIdx.x] = tot;
 }
 
-__global__ __launch_bounds__(1024) void k_scan_sums(int64_t* __restrict__ sums, int nb, int64_t* __restrict__ total) {
-  __shared__ int64_t sh[16];
-  __shared__ int64_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < nb; base += 1024) {
-    const int i = base + int(threadIdx.x);
-    const int64_t v = i < nb ? sums[i] : 0;
-    int64_t tot;
-    const int64_t ex = block_exclusive_scan<1024, int64_t>(v, sh, tot);
-    if (i < nb) sums[i] = carry + ex;
-    __syncthreads();
-    if (threadIdx.x == 0) carry += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *total = carry;
-}
 
 // Pairs in depth order: for each visible Gaussian (depth rank r), one pair
 // per tile of its rectangle, row-major.  Load-balanced: the block's
@@ -427,22 +410,50 @@ __global__ __launch_bounds__(kDT) void k_count_st(const float4* __restrict__ pro
   }
 }
 
-// Super-tile list starts and chunk numbering: st_start[s] (exclusive scan
-// of the entry totals sttot), chunk_base[s] (exclusive scan of
+// End of stage 1, one workgroup: the per-block pair sums scanned in place
+// (exclusive), the pair count M to m_dev (and m_out if given), the
+// effective count m_eff = M, or 0 when M exceeds the capacity; with sttot,
+// the super-tile list starts st_start[s] (exclusive scan of the entry
+// totals) and chunk numbering chunk_base[s] (exclusive scan of
 // ceil(sttot / kQ)), chunk_base[ns] = number of chunks.
-__global__ __launch_bounds__(256) void k_st_bases(const uint32_t* __restrict__ sttot, int ns,
-                                                  uint32_t* __restrict__ st_start, uint32_t* __restrict__ chunk_base) {
-  __shared__ uint32_t sh[4];
+__global__ __launch_bounds__(1024) void k_stage1_tail(int64_t* __restrict__ sums, int nb, int64_t cap,
+                                                      int64_t* __restrict__ m_dev, int64_t* __restrict__ m_eff,
+                                                      int64_t* __restrict__ m_out, const uint32_t* __restrict__ sttot,
+                                                      int ns, uint32_t* __restrict__ st_start,
+                                                      uint32_t* __restrict__ chunk_base) {
+  __shared__ int64_t sh[16];
+  __shared__ uint32_t sh32[16];
+  __shared__ int64_t carry;
   const int t = threadIdx.x;
-  const uint32_t c = t < ns ? sttot[t] : 0u;
-  uint32_t tot, ctot;
-  const uint32_t ex = block_exclusive_scan<256, uint32_t>(c, sh, tot);
-  const uint32_t cex = block_exclusive_scan<256, uint32_t>((c + kQ - 1) / kQ, sh, ctot);
-  if (t < ns) {
-    st_start[t] = ex;
-    chunk_base[t] = cex;
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < nb; base += 1024) {
+    const int i = base + t;
+    const int64_t v = i < nb ? sums[i] : 0;
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan<1024, int64_t>(v, sh, tot);
+    if (i < nb) sums[i] = carry + ex;
+    __syncthreads();
+    if (t == 0) carry += tot;
+    __syncthreads();
   }
-  if (t == 0) chunk_base[ns] = ctot;
+  if (t == 0) {
+    const int64_t M = carry;
+    *m_dev = M;
+    *m_eff = M <= cap ? M : 0;
+    if (m_out != nullptr) *m_out = M;
+  }
+  if (sttot != nullptr) {
+    const uint32_t c = t < ns ? sttot[t] : 0u;
+    uint32_t tot, ctot;
+    const uint32_t ex = block_exclusive_scan<1024, uint32_t>(c, sh32, tot);
+    const uint32_t cex = block_exclusive_scan<1024, uint32_t>((c + kQ - 1) / kQ, sh32, ctot);
+    if (t < ns) {
+      st_start[t] = ex;
+      chunk_base[t] = cex;
+    }
+    if (t == 0) chunk_base[ns] = ctot;
+  }
 }
 
 // Step b.  Entries of a block of kDB Gaussians (depth order) in order
@@ -619,35 +630,55 @@ __global__ __launch_bounds__(256) void k_count_chunk(const uint32_t* __restrict_
 
 // Step c, second half: per super-tile (one block each), cc scanned over its
 // chunks for each local tile (exclusive, in place); each tile's pair count
-// to ranges[2 tile] (k_tile_ranges turns the counts into ranges).
+// to ranges[2 tile] (k_tile_ranges_order turns the counts into ranges).
+// 256 / (S x S) threads per tile, each scanning a contiguous run of the
+// chunks from the sum of the runs before it.
 __global__ __launch_bounds__(256) void k_scan_chunks(const uint32_t* __restrict__ chunk_base, StGrid sg,
                                                      const int64_t* __restrict__ m_eff, uint32_t* __restrict__ cc,
                                                      uint32_t* __restrict__ ranges) {
+  __shared__ uint32_t s_sum[256];
   const int s = blockIdx.x, t = threadIdx.x;
-  const int S = 1 << sg.shift;
-  if (t >= S * S) return;
-  const int tx = (s % sg.sx) * S + (t & (S - 1)), ty = (s / sg.sx) * S + (t >> sg.shift);
-  uint32_t run = 0;
-  if (*m_eff != 0) {
-    // sixteen chunks' counts loaded together, then scanned
-    const uint32_t c0 = chunk_base[s], c1 = chunk_base[s + 1];
-    for (uint32_t cb = c0; cb < c1; cb += 16) {
-      uint32_t v[16];
+  const int S = 1 << sg.shift, L = S * S, np = 256 / L;
+  const int lt = t & (L - 1), part = t / L;
+  const bool live = *m_eff != 0;
+  const uint32_t c0 = live ? chunk_base[s] : 0u, c1 = live ? chunk_base[s + 1] : 0u;
+  const uint32_t len = (c1 - c0 + uint32_t(np) - 1u) / uint32_t(np);
+  const uint32_t a = c0 + uint32_t(part) * len < c1 ? c0 + uint32_t(part) * len : c1;
+  const uint32_t b = a + len < c1 ? a + len : c1;
+  // sixteen chunks' counts loaded together
+  uint32_t sum = 0;
+  for (uint32_t cb = a; cb < b; cb += 16) {
+    uint32_t v[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = cb + uint32_t(k) < c1 ? cc[size_t(cb + uint32_t(k)) * 256 + t] : 0u;
+    for (int k = 0; k < 16; ++k) v[k] = cb + uint32_t(k) < b ? cc[size_t(cb + uint32_t(k)) * 256 + lt] : 0u;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (cb + uint32_t(k) < c1) cc[size_t(cb + uint32_t(k)) * 256 + t] = run;
-        run += v[k];
-      }
+    for (int k = 0; k < 16; ++k) sum += v[k];
+  }
+  s_sum[t] = sum;
+  __syncthreads();
+  uint32_t run = 0, total = 0;
+  for (int p = 0; p < np; ++p) {
+    const uint32_t v = s_sum[p * L + lt];
+    run += p < part ? v : 0u;
+    total += v;
+  }
+  for (uint32_t cb = a; cb < b; cb += 16) {
+    uint32_t v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = cb + uint32_t(k) < b ? cc[size_t(cb + uint32_t(k)) * 256 + lt] : 0u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (cb + uint32_t(k) < b) cc[size_t(cb + uint32_t(k)) * 256 + lt] = run;
+      run += v[k];
     }
   }
-  if (tx < sg.tx && ty < sg.ty) ranges[2 * size_t(ty * sg.tx + tx)] = run;
+  const int tx = (s % sg.sx) * S + (lt & (S - 1)), ty = (s / sg.sx) * S + (lt >> sg.shift);
+  if (part == 0 && tx < sg.tx && ty < sg.ty) ranges[2 * size_t(ty * sg.tx + tx)] = total;
 }
 
 // Tile counts (ranges[2 tile]) -> ranges [start, end) in tile-id order;
-// empty tiles [0, 0).  One workgroup.
-__global__ __launch_bounds__(1024) void k_tile_ranges(int nT, uint32_t* __restrict__ ranges) {
+// empty tiles [0, 0).  One workgroup (1024 threads).
+__device__ __forceinline__ void tile_ranges_block(int nT, uint32_t* __restrict__ ranges) {
   __shared__ uint32_t sh[16];
   __shared__ uint32_t carry;
   if (threadIdx.x == 0) carry = 0;
@@ -784,17 +815,6 @@ __global__ __launch_bounds__(256) void k_expand(const uint32_t* __restrict__ chu
   }
 }
 
-// The pair count the second half of the binning works with: M, or 0 when
-// M exceeds the capacity (nothing is then written but empty ranges).
-// Also copies M to the caller's device slot m_out (if any).
-__global__ __launch_bounds__(64) void k_eff_count(const int64_t* __restrict__ m_dev, int64_t cap,
-                                                  int64_t* __restrict__ m_eff, int64_t* __restrict__ m_out) {
-  if (threadIdx.x == 0) {
-    const int64_t M = *m_dev;
-    *m_eff = M <= cap ? M : 0;
-    if (m_out != nullptr) *m_out = M;
-  }
-}
 
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -816,8 +836,8 @@ __global__ __launch_bounds__(256) void k_ranges(const uint64_t* __restrict__ key
 // of the count), so the longest lists start first and short ones fill the
 // gaps.  One workgroup; deterministic (wave ballot ranking, no atomics
 // whose order matters).
-__global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ ranges, int nT,
-                                                     uint32_t* __restrict__ order) {
+__device__ __forceinline__ void tile_order_block(const uint32_t* __restrict__ ranges, int nT,
+                                                 uint32_t* __restrict__ order) {
   constexpr int kB = 33;                     // buckets: bit length 0..32
   __shared__ uint32_t s_cnt[kB];
   __shared__ uint32_t s_base[kB];
@@ -849,6 +869,91 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
     const uint32_t b = valid ? bucket_of(tile) : 0u;
     const uint64_t act = ballot(valid);
     const uint64_t peers = match_bits<6>(b, act);
+    const uint32_t below = uint32_t(count_below(peers));
+    if (t < 16 * kB) (&s_w[0][0])[t] = 0;
+    __syncthreads();
+    if (valid && below == 0) s_w[w][b] = uint32_t(__popcll(peers));
+    __syncthreads();
+    if (valid) {
+      uint32_t off = s_base[b] + below;
+      for (int k = 0; k < w; ++k) off += s_w[k][b];
+      order[off] = uint32_t(tile);
+    }
+    __syncthreads();
+    if (t < kB) {
+      uint32_t add = 0;
+      for (int k = 0; k < 16; ++k) add += s_w[k][t];
+      s_base[t] += add;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ ranges, int nT,
+                                                     uint32_t* __restrict__ order) {
+  tile_order_block(ranges, nT, order);
+}
+
+// The exact path's last step, one workgroup: tile counts to ranges, then
+// (with `order`) the tiles' launch order from them.  Up to 8192 tiles the
+// counts stay in registers between the two (tile r * 1024 + t in thread t);
+// larger images take the two steps one after the other through memory.
+__global__ __launch_bounds__(1024) void k_tile_ranges_order(int nT, uint32_t* __restrict__ ranges,
+                                                            uint32_t* __restrict__ order) {
+  constexpr int kR = 8;
+  if (nT > kR * 1024) {
+    tile_ranges_block(nT, ranges);
+    __threadfence();        // the ranges just written, read back below by other waves
+    __syncthreads();
+    if (order != nullptr) tile_order_block(ranges, nT, order);
+    return;
+  }
+  constexpr int kB = 33;                     // order buckets: bit length 0..32
+  __shared__ uint32_t sh[16];
+  __shared__ uint32_t s_cnt[kB];
+  __shared__ uint32_t s_base[kB];
+  __shared__ uint32_t s_w[16][kB];
+  const int t = threadIdx.x, w = t >> 6;
+  uint32_t v[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) v[r] = r * 1024 + t < nT ? ranges[2 * (r * 1024 + t)] : 0u;
+  if (t < kB) s_cnt[t] = 0;
+  uint32_t carry = 0;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int i = r * 1024 + t;
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<1024, uint32_t>(v[r], sh, tot);
+    if (i < nT) {
+      const uint32_t start = carry + ex;
+      ranges[2 * i] = v[r] != 0 ? start : 0u;
+      ranges[2 * i + 1] = v[r] != 0 ? start + v[r] : 0u;
+    }
+    carry += tot;
+  }
+  if (order == nullptr) return;
+  // stable counting sort by descending bucket (bucket 0 = longest lists)
+  uint32_t bk[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    bk[r] = 32u - (v[r] != 0 ? 32u - uint32_t(__builtin_clz(v[r])) : 0u);
+    if (r * 1024 + t < nT) atomicAdd(&s_cnt[bk[r]], 1u);
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint32_t run = 0;
+    for (int b = 0; b < kB; ++b) {
+      s_base[b] = run;
+      run += s_cnt[b];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int tile = r * 1024 + t;
+    const bool valid = tile < nT;
+    const uint32_t b = bk[r];
+    const uint64_t peers = match_bits<6>(b, ballot(valid));
     const uint32_t below = uint32_t(count_below(peers));
     if (t < 16 * kB) (&s_w[0][0])[t] = 0;
     __syncthreads();
@@ -969,10 +1074,9 @@ int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity) {
 }
 
 hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx,
-                                 const int64_t* vis_count, int32_t tiles_x, int32_t tiles_y, void* ws,
-                                 int64_t pair_capacity, hipStream_t st) {
+                                 const int64_t* vis_count, int32_t tiles_x, int32_t tiles_y, int64_t* num_pairs_dev,
+                                 void* ws, int64_t pair_capacity, hipStream_t st) {
   Ws w = carve(ws, n, pair_capacity);
-  int64_t* m_dev = w.m_dev;
   const float4* P = reinterpret_cast<const float4*>(proj);
   if (n > 0) {
     k_depth_gather<<<unsigned((n + 255) / 256), 256, 0, st>>>(P, vis_idx, vis_count, w.dkA, w.dvA);
@@ -984,17 +1088,19 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
     }
   }
   const int nbv = int(dup_blocks(n));
+  int ns = 0;
   if (nbv > 0 && exact_path(tiles_x, tiles_y)) {
-    // pair totals, entries per (super-tile, block), list starts and chunks
+    // pair totals, entries per (super-tile, block)
     const StGrid sg = st_grid(tiles_x, tiles_y);
-    const int ns = sg.sx * sg.sy;
+    ns = sg.sx * sg.sy;
     k_count_st<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, nbv, sg, w.bsums, w.stcnt);
     k_rowscan<<<unsigned(ns), kRT, 0, st>>>(w.stcnt, nbv + 1, w.sttot);
-    k_st_bases<<<1, 256, 0, st>>>(w.sttot, ns, w.st_start, w.chunk_base);
   } else if (nbv > 0) {
     k_tilesum<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
   }
-  k_scan_sums<<<1, 1024, 0, st>>>(w.bsums, nbv, m_dev);
+  // block offsets, M, the effective count; super-tile list starts and chunks
+  k_stage1_tail<<<1, 1024, 0, st>>>(w.bsums, nbv, pair_capacity, w.m_dev, w.m_eff, num_pairs_dev,
+                                    ns > 0 ? w.sttot : nullptr, ns, w.st_start, w.chunk_base);
   return hipGetLastError();
 }
 
@@ -1004,8 +1110,8 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
 // count (0 when M exceeds the capacity: then only empty ranges are written).
 hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx,
                                  const int64_t* vis_count, int64_t M_host, int32_t tiles_x, int32_t tiles_y,
-                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, uint32_t* tile_order,
-                                 int64_t* num_pairs_dev, void* ws, int64_t pair_capacity, hipStream_t st) {
+                                 uint64_t* keys, int32_t* vals, uint32_t* ranges, uint32_t* tile_order, void* ws,
+                                 int64_t pair_capacity, hipStream_t st) {
   (void)vis_idx;
   Ws w = carve(ws, n, pair_capacity);
   const float4* P = reinterpret_cast<const float4*>(proj);
@@ -1016,14 +1122,12 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
   const int64_t* m_dev = nullptr;
   int64_t bound = M_host;                       // upper bound of the count, for grid sizes
   if (on_device) {
-    k_eff_count<<<1, 64, 0, st>>>(w.m_dev, pair_capacity, w.m_eff, num_pairs_dev);
-    m_dev = w.m_eff;
+    m_dev = w.m_eff;                            // from stage 1
     bound = pair_capacity;
   }
   if (exact_path(tiles_x, tiles_y) && nbv > 0) {
     // super-tile entries, per-chunk tile counts, ranges, then the pairs;
     // every kernel reads the effective count (0: no pairs or overflow)
-    if (!on_device) k_eff_count<<<1, 64, 0, st>>>(w.m_dev, pair_capacity, w.m_eff, nullptr);
     const StGrid sg = st_grid(tiles_x, tiles_y);
     const int ns = sg.sx * sg.sy;
     const unsigned grid = unsigned(std::min<int64_t>(max_chunks(pair_capacity), 2048));
@@ -1034,9 +1138,10 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     k_dup_st<<<nbv, kDT, 0, st>>>(P, w.dvA, w.dkA, vis_count, w.stcnt, w.st_start, nbv, sg, w.m_eff, e_g, e_d, e_r);
     k_count_chunk<<<grid, 256, 0, st>>>(w.chunk_base, w.st_start, w.sttot, ns, e_r, sg, w.m_eff, w.cc);
     k_scan_chunks<<<unsigned(ns), 256, 0, st>>>(w.chunk_base, sg, w.m_eff, w.cc, ranges);
-    k_tile_ranges<<<1, 1024, 0, st>>>(int(T), ranges);
+    k_tile_ranges_order<<<1, 1024, 0, st>>>(int(T), ranges, tile_order);
     k_expand<<<egrid, 256, 0, st>>>(w.chunk_base, w.st_start, w.sttot, ns, e_g, e_d, e_r, w.cc, ranges, sg, w.m_eff,
                                    keys, uvals);
+    return hipGetLastError();
   } else if (!on_device && M_host == 0) {
     k_fill_u32<<<unsigned((2 * T + 255) / 256), 256, 0, st>>>(ranges, 2 * T, 0u);
   } else {

@@ -40,16 +40,19 @@ hipError_t launch_compact(uint8_t* flags, int64_t n, int32_t* idx, int64_t* coun
 // --- bin sort (binsort.hip) ------------------------------------------------
 size_t binsort_ws_bytes(int64_t n, int64_t pair_capacity);
 // Stage 1 (asynchronous): depth sort of the visible list and the pair
-// count M, left in device memory at binsort_count_ptr(ws, ...).
+// count M, left in device memory at binsort_count_ptr(ws, ...) (and at
+// num_pairs_dev if given).
 hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
-                                 int32_t tiles_x, int32_t tiles_y, void* ws, int64_t pair_capacity, hipStream_t st);
+                                 int32_t tiles_x, int32_t tiles_y, int64_t* num_pairs_dev, void* ws,
+                                 int64_t pair_capacity, hipStream_t st);
 int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity);
-// Stage 2 (after M is known on the host): duplication, tile radix sort,
-// tile ranges.
+// Stage 2: the pairs in key order and the tile ranges.  M_host >= 0: the
+// count read by the caller (<= the capacity); M_host < 0: the count stays
+// on the device (an overflow leaves empty ranges and untouched pairs).
 hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
                                  int64_t M_host, int32_t tiles_x, int32_t tiles_y, uint64_t* keys, int32_t* vals,
-                                 uint32_t* ranges, uint32_t* tile_order, int64_t* num_pairs_dev, void* ws,
-                                 int64_t pair_capacity, hipStream_t st);
+                                 uint32_t* ranges, uint32_t* tile_order, void* ws, int64_t pair_capacity,
+                                 hipStream_t st);
 
 // --- rasteriser (raster_fwd.hip / raster_bwd.hip) ---------------------------
 hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
