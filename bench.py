@@ -56,9 +56,11 @@ def algorithmic_bytes(N, views, U):
                   + 4 * M + 8 * T         # tile ranges
                   + 40 * Mp + 20 * P      # raster forward
                   + 36 * P                # loss
-                  + 40 * Mp + 20 * P + 72 * V   # raster backward
-                  + 744 * V)              # projection backward
-    return total + 1892 * U               # sparse Adam
+                  + 40 * Mp + 20 * P + 48 * V   # raster backward (screen-space gradients out)
+                  + 96 * V)               # projection backward: screen-space gradients in, re-zeroed
+    # projection backward of every view fused with sparse Adam: per updated
+    # row 236 B parameters and 472 B moments in, 708 B parameters and moments out
+    return total + 1416 * U
 
 
 def recorded_traffic(kernel, workload):
