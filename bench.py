@@ -14,6 +14,7 @@ the oracle timed on the host's cores over one step of the same workload
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -152,6 +153,13 @@ def main():
         step.step()
     torch.cuda.synchronize()
 
+    # The objects alive after set-up (torch's, numpy's, the workload's) are
+    # moved out of the garbage collector's generations: a full collection
+    # over them takes tens of milliseconds on this interpreter and, landing
+    # inside the timed loop, stalls the host between two kernel launches
+    # while the GPU drains its queue.  Host-side only; every GPU stage runs.
+    gc.collect()
+    gc.freeze()
     log(f"[bench] timing {args.steps} steps")
     step.timer = {}
     torch.cuda.synchronize()

@@ -22,10 +22,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
-GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM = 0, 1, 2, 3
+GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM, GS_OP_RASTER = 0, 1, 2, 3, 4
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
 GS_MAX_FUSED_VIEWS = 8
+SEGMENT_LEN = 512    # list entries per segment of the split raster backward
 TILE = 16
 
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
@@ -64,9 +65,9 @@ def lib():
     L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _sz, _P]
     L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
     L.gs_bin_sort_async.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
-    L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
+    L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
     L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
-    L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P]
+    L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
     L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
@@ -95,6 +96,10 @@ def _ptr(t):
     if t is None:
         return None
     return C.c_void_p(t.data_ptr())
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream=None):
@@ -173,10 +178,10 @@ def gs_bin_sort_async(proj, n, vis_idx, vis_count, width, height, keys, vals, pa
 
 
 def gs_render_fwd(proj, n, vals, tile_ranges, num_pairs, width, height, image, T_final, last,
-                  tile_processed=None, tile_order=None, stream=None):
+                  tile_processed=None, tile_order=None, split_ws=None, segment_len=SEGMENT_LEN, stream=None):
     _check(lib().gs_render_fwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), _ptr(tile_order), num_pairs, width,
-                               height,
-                              _ptr(image), _ptr(T_final), _ptr(last), _ptr(tile_processed), _stream(stream)),
+                               height, _ptr(image), _ptr(T_final), _ptr(last), _ptr(tile_processed),
+                               _ptr(split_ws), _nbytes(split_ws), segment_len, _stream(stream)),
            "gs_render_fwd")
 
 
@@ -187,10 +192,10 @@ def gs_loss(image, target, width, height, w_l1, w_ssim, loss, dL_dimage, workspa
 
 
 def gs_render_bwd(proj, n, vals, tile_ranges, num_pairs, width, height, T_final, last, dL_dimage, grad2d,
-                  tile_order=None, stream=None):
+                  tile_order=None, split_ws=None, segment_len=SEGMENT_LEN, stream=None):
     _check(lib().gs_render_bwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), _ptr(tile_order), num_pairs, width,
-                               height,
-                              _ptr(T_final), _ptr(last), _ptr(dL_dimage), _ptr(grad2d), _stream(stream)),
+                               height, _ptr(T_final), _ptr(last), _ptr(dL_dimage), _ptr(grad2d),
+                               _ptr(split_ws), _nbytes(split_ws), segment_len, _stream(stream)),
            "gs_render_bwd")
 
 
@@ -286,7 +291,7 @@ class TrainStep:
     one view's stages in order on the current stream."""
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
-                 pair_capacity=None, record_tiles=False):
+                 pair_capacity=None, record_tiles=False, segment_len=SEGMENT_LEN):
         p = torch.as_tensor(params, dtype=torch.float32)
         assert p.ndim == 2 and p.shape[0] == 59
         self.device = torch.device(device)
@@ -332,6 +337,12 @@ class TrainStep:
         self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
         self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
         self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
+        # the forward's checkpoints and segment list, read by the split raster
+        # backward of the same view (both on the current stream, the view's
+        # backward before the next view's forward); segment_len None: unsplit
+        self.segment_len = segment_len or 0
+        self.split_ws = (_bytes(max(gs_workspace_size(GS_OP_RASTER, 0, v.W, v.H) for v in self.views), self.device)
+                         if segment_len else None)
 
     # the buffer set of the view last prepared (what tests read back)
     @property
@@ -408,7 +419,8 @@ class TrainStep:
         ps = self.sets[k % self.nsets]
         with self._stage("render_fwd"):
             gs_render_fwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.image, vw.T_final,
-                          vw.last, vw.tile_processed if self.record_tiles else None, vw.order)
+                          vw.last, vw.tile_processed if self.record_tiles else None, vw.order, self.split_ws,
+                          self.segment_len)
         with self._stage("loss"):
             gs_loss(vw.image, vw.target, vw.W, vw.H, self.w_l1, self.w_ssim, vw.loss, vw.dL, self.ws_loss)
 
@@ -423,7 +435,7 @@ class TrainStep:
         self._gcur = self._gbuf(k)
         with self._stage("render_bwd"):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
-                          vw.dL, self.g2d[self._gcur], vw.order)
+                          vw.dL, self.g2d[self._gcur], vw.order, self.split_ws, self.segment_len)
         if not keep_grad2d:
             self.project_view(k)
 

@@ -69,6 +69,22 @@ gs_status check_size(int32_t width, int32_t height) {
   return GS_OK;
 }
 
+// The split backward's workspace (its size for the image) and segment
+// length (a power of two, 64 ... 65536); both ignored without a workspace.
+gs_status check_split(const void* ws, size_t ws_bytes, int32_t width, int32_t height, int32_t segment_len,
+                      int& seg_shift) {
+  seg_shift = 6;
+  if (ws == nullptr) return GS_OK;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(GS_ERR_INVALID_ARG, "split_ws not 256-byte aligned");
+  const size_t need = gs::raster_split_bytes(width, height);
+  if (ws_bytes < need)
+    return fail(GS_ERR_INVALID_ARG, "split_ws_bytes = %zu < %zu needed for %dx%d", ws_bytes, need, width, height);
+  if (segment_len < 64 || segment_len > 65536 || (segment_len & (segment_len - 1)) != 0)
+    return fail(GS_ERR_INVALID_ARG, "segment_len = %d: not a power of two in [64, 65536]", int(segment_len));
+  seg_shift = __builtin_ctz(uint32_t(segment_len));
+  return GS_OK;
+}
+
 #define REQUIRE(cond, ...)                                   \
   do {                                                       \
     if (!(cond)) return fail(GS_ERR_INVALID_ARG, __VA_ARGS__); \
@@ -131,6 +147,10 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
     case GS_OP_SPARSE_ADAM:
       REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
       *bytes = adam_ws_bytes(n);
+      return ok();
+    case GS_OP_RASTER:
+      CHECK(check_size(width, height));
+      *bytes = gs::raster_split_bytes(width, height);
       return ok();
   }
   return fail(GS_ERR_INVALID_ARG, "unknown op %d", int(op));
@@ -211,13 +231,17 @@ gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx
 
 gs_status gs_render_fwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height, float* image,
-                        float* T_final, uint32_t* last, uint32_t* tile_processed, void* stream) {
+                        float* T_final, uint32_t* last, uint32_t* tile_processed, void* split_ws,
+                        size_t split_ws_bytes, int32_t segment_len, void* stream) {
   CHECK(check_size(width, height));
   REQUIRE(n >= 0 && num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "n / num_pairs out of range");
   REQUIRE(tile_ranges && image && T_final && last, "NULL output or tile_ranges");
   if (num_pairs > 0) REQUIRE(proj && vals && aligned(proj, 16), "NULL or misaligned proj / vals");
+  int seg_shift = 0;
+  CHECK(check_split(split_ws, split_ws_bytes, width, height, segment_len, seg_shift));
   return hip_status(gs::launch_render_fwd(proj, vals, tile_ranges, tile_order, num_pairs, width, height, image,
-                                          T_final, last, tile_processed, static_cast<hipStream_t>(stream)),
+                                          T_final, last, tile_processed, split_ws, seg_shift,
+                                          static_cast<hipStream_t>(stream)),
                     "gs_render_fwd");
 }
 
@@ -238,7 +262,7 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
 gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                         const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                        void* stream) {
+                        const void* split_ws, size_t split_ws_bytes, int32_t segment_len, void* stream) {
   CHECK(check_size(width, height));
   REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
   REQUIRE(num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "num_pairs out of range");
@@ -247,8 +271,11 @@ gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const
     REQUIRE(proj && vals && grad2d, "NULL array");
     REQUIRE(aligned(proj, 16) && aligned(grad2d, 16), "proj / grad2d not 16-byte aligned");
   }
+  int seg_shift = 0;
+  CHECK(check_split(split_ws, split_ws_bytes, width, height, segment_len, seg_shift));
   return hip_status(gs::launch_render_bwd(proj, vals, tile_ranges, tile_order, num_pairs, width, height, T_final,
-                                          last, dL_dimage, grad2d, static_cast<hipStream_t>(stream)),
+                                          last, dL_dimage, grad2d, split_ws, seg_shift,
+                                          static_cast<hipStream_t>(stream)),
                     "gs_render_bwd");
 }
 

@@ -55,13 +55,21 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
                                  hipStream_t st);
 
 // --- rasteriser (raster_fwd.hip / raster_bwd.hip) ---------------------------
+// The split backward's state (checkpoints and work lists, see
+// raster_common.hpp), sized for the image; images of 2^25 tiles or more
+// run unsplit.
+size_t raster_split_bytes(int32_t width, int32_t height);
+bool raster_split_fits(int32_t width, int32_t height);
+// split: NULL or raster_split_bytes(width, height) of device memory; segments of
+// 2^seg_shift list entries (seg_shift >= 6), the same for both passes.
 hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
-                             float* image, float* T_final, uint32_t* last, uint32_t* tile_processed, hipStream_t st);
+                             float* image, float* T_final, uint32_t* last, uint32_t* tile_processed, void* split,
+                             int seg_shift, hipStream_t st);
 hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                              const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                             hipStream_t st);
+                             const void* split, int seg_shift, hipStream_t st);
 hipError_t launch_project_bwd(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
                               const int32_t* vis_idx, const int64_t* vis_count, float* grad2d, float* grads,
                               hipStream_t st);

@@ -70,39 +70,14 @@ __device__ __forceinline__ void wave_sum9(const float v[9], float& q0, float& q1
   q2 = half_row_sum(fold16(r4, 0.0f));
 }
 
-__global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
-                                                   const uint32_t* __restrict__ ranges,
-                                                   const uint32_t* __restrict__ order, int64_t num_pairs, int W,
-                                                   int H, int TX, int nT, const float* __restrict__ T_final,
-                                                   const uint32_t* __restrict__ last,
-                                                   const float* __restrict__ dL_dimage, float* __restrict__ grad2d) {
-  __shared__ float4 s_a[kChunk];
-  __shared__ float4 s_c[kChunk];
-  __shared__ float s_b[kChunk];
-  __shared__ int32_t s_g[kChunk];
-  __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
-  int q0;
-  const int tile = order_tile(order, nT, q0);
-  if (tile < 0) return;
+// One pass of a quarter's list positions [lo, hi), back to front, from the
+// per-pixel state (T, S) at position hi.
+__device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
+                                          uint32_t start, uint32_t lo, uint32_t hi, float qx, float qy, float pxc,
+                                          float pyc, uint32_t lastp, float T, float S0, float S1, float S2,
+                                          float G0, float G1, float G2, float* __restrict__ grad2d, float4* s_a,
+                                          float4* s_c, float* s_b, int32_t* s_g, float* s_acc) {
   const int lane = threadIdx.x;
-  const int tx = tile % TX, ty = tile / TX;
-  const int x0 = tx * kTile, y0 = ty * kTile;
-  const float qx = float(x0 + (q0 & 1) * 8) + 0.5f, qy = float(y0 + (q0 >> 1) * 8) + 0.5f;
-  uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
-  if (end > uint64_t(num_pairs)) end = uint32_t(num_pairs);
-  if (start > end) start = end;
-
-  const size_t P = size_t(W) * H;
-  const int px = x0 + (q0 & 1) * 8 + (lane & 7), py = y0 + (q0 >> 1) * 8 + (lane >> 3);
-  const float pxc = float(px) + 0.5f, pyc = float(py) + 0.5f;
-  const bool inside = px < W && py < H;
-  const size_t pix = size_t(py) * W + px;
-  float T = inside ? T_final[pix] : 1.0f;
-  const uint32_t lastp = inside ? last[pix] : 0u;
-  const float G0 = inside ? dL_dimage[pix] : 0.0f;
-  const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
-  const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
-  float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
   // lanes 0, 8, 16, ..., 56 (row r = lane / 16, half h = lane / 8 % 2)
   // store the half sums: row r of the folded sums q0 / q1 carries sum
   // (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r] (q2, row 0: sum 8); half sum h of
@@ -114,25 +89,23 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   // factor for c >= 2 (conic A, B, C: -1/2, -1, -1/2; the rest 1)
   const int fc = lane & 15;
   const float fk = (fc == 2 || fc == 4) ? -0.5f : (fc == 3 ? -1.0f : 1.0f);
-  uint32_t lmax = wave_max_u32(lastp);     // entries a pixel of the quarter composited
-  if (lmax > end - start) lmax = end - start;
-  if (lmax == 0) return;
+  const int64_t base = int64_t(start) + lo;    // first position of the range
 
-  // chunks from the last composited entry down to the first
-  // (every chunk below the first one processed lies wholly inside the
-  // composited prefix; entries are loaded one chunk ahead, indices two)
+  // chunks from the range's last entry down to its first (every chunk
+  // below the first one processed lies wholly inside the composited
+  // prefix; entries are loaded one chunk ahead, indices two)
   const uint32_t ul = uint32_t(lane);
-  const int64_t top = int64_t(start) + int64_t((lmax - 1) / kChunk) * kChunk;
-  EntryRec cur = load_entry(proj, load_index(vals, uint32_t(top) + ul, uint32_t(top) + ul - start < lmax));
-  int32_t gnext = load_index(vals, uint32_t(top - kChunk) + ul, top - kChunk >= int64_t(start));
-  for (int64_t cs = top; cs >= int64_t(start); cs -= kChunk) {
+  const int64_t top = int64_t(start) + int64_t((hi - 1) / kChunk) * kChunk;
+  EntryRec cur = load_entry(proj, load_index(vals, uint32_t(top) + ul, uint32_t(top) + ul - start < hi));
+  int32_t gnext = load_index(vals, uint32_t(top - kChunk) + ul, top - kChunk >= base);
+  for (int64_t cs = top; cs >= base; cs -= kChunk) {
     uint64_t written = 0;   // chunk entries with sums in s_acc
     const EntryRec nxt = load_entry(proj, gnext);
-    gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= int64_t(start));
+    gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= base);
     const uint32_t pos = uint32_t(cs) + ul - start;
     const bool hit = stage_entry(cur, qx, qy, s_a, s_c, s_b, s_g, lane);
     cur = nxt;
-    uint64_t active = uint64_t(__ballot(hit && pos < lmax));
+    uint64_t active = uint64_t(__ballot(hit && pos < hi));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -212,6 +185,91 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   }
 }
 
+// Workgroups [0, nhelp) are helpers: helper h takes the forward's listed
+// segments h / kPools, h / kPools + nhelp / kPools, ... of pool h % kPools
+// (nhelp = kPools x pool size: one each), each from its recorded state; the
+// rest own one quarter each (in `order`) and run its list from the last
+// composited entry down to the first position no helper covers.
+__global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
+                                                   const uint32_t* __restrict__ ranges,
+                                                   const uint32_t* __restrict__ order, int64_t num_pairs, int W,
+                                                   int H, int TX, int nT, const float* __restrict__ T_final,
+                                                   const uint32_t* __restrict__ last,
+                                                   const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
+                                                   const void* split, int seg_shift, int nhelp) {
+  __shared__ float4 s_a[kChunk];
+  __shared__ float4 s_c[kChunk];
+  __shared__ float s_b[kChunk];
+  __shared__ int32_t s_g[kChunk];
+  __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
+  const SplitLayout sl = split_layout(W, H);
+  const SplitState sp = split_state(const_cast<void*>(split), sl);
+  const int lane = threadIdx.x;
+  const size_t P = size_t(W) * H;
+  const bool helper = int(blockIdx.x) < nhelp;
+  const uint32_t pool = blockIdx.x % kPools;
+  uint32_t nitems = 0;
+  if (helper) {
+    nitems = sp.counters[32 * pool + 1];
+    if (nitems > uint32_t(sl.pool_slots)) nitems = uint32_t(sl.pool_slots);
+  }
+  for (uint32_t item = blockIdx.x / kPools;; item += uint32_t(nhelp / kPools)) {
+    int tile, q0;
+    uint32_t lo, seg_hi = 0, slot = 0;
+    if (helper) {
+      if (item >= nitems) return;
+      slot = sp.items[pool * uint32_t(sl.pool_slots) + item];
+      if (slot >= uint32_t(kPools * sl.pool_slots)) return;
+      const uint32_t own = sp.owner[slot];
+      tile = int(own >> 7);
+      q0 = int(own >> 5) & 3;
+      lo = (own & 31u) << seg_shift;
+      seg_hi = lo + (1u << seg_shift);
+    } else {
+      int rank;
+      quarter_of(int(blockIdx.x) - nhelp, rank, q0);   // nhelp: a multiple of kXcds
+      if (rank >= nT) return;
+      tile = order != nullptr ? int(order[rank]) : rank;
+      lo = split != nullptr ? sp.qsegs[tile * kWPT + q0] << seg_shift : 0u;
+    }
+    if (tile >= nT) return;
+    const int tx = tile % TX, ty = tile / TX;
+    const int x0 = tx * kTile, y0 = ty * kTile;
+    const float qx = float(x0 + (q0 & 1) * 8) + 0.5f, qy = float(y0 + (q0 >> 1) * 8) + 0.5f;
+    uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+    if (end > uint64_t(num_pairs)) end = uint32_t(num_pairs);
+    if (start > end) start = end;
+    const int px = x0 + (q0 & 1) * 8 + (lane & 7), py = y0 + (q0 >> 1) * 8 + (lane >> 3);
+    const bool inside = px < W && py < H;
+    const size_t pix = size_t(py) * W + px;
+    const uint32_t lastp = inside ? last[pix] : 0u;
+    uint32_t lmax = wave_max_u32(lastp);     // entries a pixel of the quarter composited
+    if (lmax > end - start) lmax = end - start;
+    // a helper's segment ends where the next one's recorded state starts;
+    // the quarter's own pass starts from T_final and black behind
+    const uint32_t hi = helper ? (seg_hi < lmax ? seg_hi : lmax) : lmax;
+    if (lo < hi) {
+      float T, S0, S1, S2;
+      if (helper) {
+        const float4 v = sp.ck[size_t(slot) * 64 + lane];
+        T = v.x;
+        S0 = v.y;
+        S1 = v.z;
+        S2 = v.w;
+      } else {
+        T = inside ? T_final[pix] : 1.0f;
+        S0 = S1 = S2 = 0.0f;
+      }
+      const float G0 = inside ? dL_dimage[pix] : 0.0f;
+      const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
+      const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
+      bwd_range(proj, vals, start, lo, hi, qx, qy, float(px) + 0.5f, float(py) + 0.5f, lastp, T, S0, S1, S2, G0, G1,
+                G2, grad2d, s_a, s_c, s_b, s_g, s_acc);
+    }
+    if (!helper) return;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_project_bwd(const float* __restrict__ params, int64_t n, int64_t ld,
                                                      CamArgs cam, const int32_t* __restrict__ vis,
                                                      const int64_t* __restrict__ vis_count,
@@ -239,11 +297,15 @@ __global__ __launch_bounds__(256) void k_project_bwd(const float* __restrict__ p
 hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                              const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                             hipStream_t st) {
+                             const void* split, int seg_shift, hipStream_t st) {
   const int TX = (width + kTile - 1) / kTile, TY = (height + kTile - 1) / kTile;
   const int nT = TX * TY;
-  k_render_bwd<<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
-                                              num_pairs, width, height, TX, nT, T_final, last, dL_dimage, grad2d);
+  if (split != nullptr && !raster_split_fits(width, height)) split = nullptr;
+  // one helper per recorded state the pools can hold
+  const int nhelp = split != nullptr ? kPools * split_layout(width, height).pool_slots : 0;
+  k_render_bwd<<<unsigned(nhelp) + raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges,
+                                                          tile_order, num_pairs, width, height, TX, nT, T_final,
+                                                          last, dL_dimage, grad2d, split, seg_shift, nhelp);
   return hipGetLastError();
 }
 

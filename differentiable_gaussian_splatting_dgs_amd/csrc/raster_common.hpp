@@ -20,17 +20,90 @@ constexpr int kChunk = 64;
 // Waves (one per quarter) per tile.
 constexpr int kWPT = 4;
 
-// Workgroup -> (tile, quarter).  Tiles are taken in `order` (longest
-// lists first) when given, so the heavy ones start early and light ones
-// fill the gaps.  Returns -1 for workgroups past the end.
+// Split backward of long lists.  While compositing, a quarter's forward
+// records its per-pixel state at each list position that is a multiple of
+// the segment length (up to kCkSeg of them, in slots taken from a counter):
+// T before that entry and the colour the segment ending there added.  At
+// its end it turns those into the colour behind each recorded position (the
+// sum of the later segments over T: positive terms, no cancellation) and
+// lists every whole segment below its last composited entry as a work
+// item.  The backward's helper waves run those segments from the recorded
+// state while one wave per quarter runs the rest of its list, so a long
+// list is walked by several waves at once instead of by one wave long after
+// the rest of the grid has finished.
+constexpr int kCkSeg = 31;               // recorded positions per quarter (5 bits)
+// Recorded states come from kPools pools of equal size; a quarter takes
+// them from pool (workgroup index mod kPools), so each slot counter is
+// contended by few waves at a time.  A quarter whose pool is exhausted
+// stops recording (the rest of its list stays one piece).  Pools hold half
+// a state per quarter of the image (at least 64 each): lists of 1080p
+// views split at 512 entries use about a third of that.
+constexpr int kPools = 64;
+constexpr int kCounterWords = kPools * 32;   // two counters per pool, 128 bytes apart
+
+// Sizes of the split state of one image.
+struct SplitLayout {
+  int64_t quarters;   // kWPT per tile
+  int pool_slots;     // states per pool
+  size_t bytes;       // the whole workspace
+};
+
+__host__ __device__ inline SplitLayout split_layout(int32_t width, int32_t height) {
+  SplitLayout l;
+  l.quarters = int64_t((width + kTile - 1) / kTile) * ((height + kTile - 1) / kTile) * kWPT;
+  const int64_t per_pool = (l.quarters / 2 + kPools - 1) / kPools;
+  l.pool_slots = int(per_pool < 64 ? 64 : per_pool);
+  const size_t slots = size_t(kPools) * l.pool_slots;
+  l.bytes = slots * 64 * 16 + 2 * slots * 4 + size_t(l.quarters) * 4 + kCounterWords * 4;
+  return l;
+}
+
+// The workspace: states, their owners, the pools' work lists, per-quarter
+// segment counts, and per pool the counters (slots taken, items listed).
+struct SplitState {
+  float4* ck;          // [slots][64]: (T, colour) per pixel
+  uint32_t* owner;     // [slots]: quarter << 5 | position index
+  uint32_t* items;     // [kPools][pool_slots]: slots whose segment the helpers run
+  uint32_t* qsegs;     // [quarters]: segments of the quarter run by helpers
+  uint32_t* counters;  // [kPools][32]
+};
+
+__host__ __device__ inline SplitState split_state(void* base, const SplitLayout& l) {
+  const uintptr_t p = reinterpret_cast<uintptr_t>(base);   // base may be NULL (no split)
+  const size_t slots = size_t(kPools) * l.pool_slots;
+  SplitState s;
+  s.ck = reinterpret_cast<float4*>(p);
+  s.owner = reinterpret_cast<uint32_t*>(p + slots * 64 * 16);
+  s.items = reinterpret_cast<uint32_t*>(p + slots * 64 * 16 + 4 * slots);
+  s.qsegs = reinterpret_cast<uint32_t*>(p + slots * 64 * 16 + 8 * slots);
+  s.counters = reinterpret_cast<uint32_t*>(p + slots * 64 * 16 + 8 * slots + 4 * size_t(l.quarters));
+  return s;
+}
+
+// Workgroup -> (tile rank, quarter).  Workgroups go to the 8 XCDs round
+// robin (workgroup b on XCD b mod 8), each XCD with its own L2; the four
+// quarters of a rank are workgroups 32 g + x + 8 q (q = 0..3) of group g,
+// all on XCD x, so one L2 serves the tile's list and records to its four
+// waves, which start within a few workgroups of each other.
+constexpr int kXcds = 8;
+__host__ __device__ inline void quarter_of(int b, int& rank, int& q0) {
+  const int g = b / (kWPT * kXcds), r = b % (kWPT * kXcds);
+  rank = g * kXcds + r % kXcds;
+  q0 = r / kXcds;
+}
+
+// Tiles are taken in `order` (longest lists first) when given, so the
+// heavy ones start early and light ones fill the gaps.  Returns -1 for
+// workgroups past the end.
 __device__ __forceinline__ int order_tile(const uint32_t* __restrict__ order, int nT, int& q0) {
-  const int rank = int(blockIdx.x) / kWPT;
-  q0 = int(blockIdx.x) % kWPT;
+  int rank;
+  quarter_of(int(blockIdx.x), rank, q0);
   if (rank >= nT) return -1;
   return order != nullptr ? int(order[rank]) : rank;
 }
 
-inline unsigned raster_grid(int nT) { return unsigned(nT * kWPT); }
+// Workgroups for nT tiles: whole groups of kXcds tiles.
+inline unsigned raster_grid(int nT) { return unsigned((nT + kXcds - 1) / kXcds * kXcds * kWPT); }
 
 // e^x for x in [-5.6, 0]: the written exponential without its range
 // checks (which never trigger there), so the same bits as pexp.

@@ -8,14 +8,18 @@
 // branches (selects), so the image and every decision are bit-identical to
 // the checker's.  A wave ends at the first chunk boundary after all 64 of
 // its pixels have stopped.
+#include <algorithm>
+
 #include "raster_common.hpp"
 
 namespace gs {
 namespace {
 
-__global__ __launch_bounds__(64) void k_fill(uint32_t* __restrict__ p, int n, uint32_t v) {
-  const int i = int(blockIdx.x) * 64 + int(threadIdx.x);
-  if (i < n) p[i] = v;
+// Zeroes the per-tile maxima and the split state's counters.
+__global__ __launch_bounds__(256) void k_clear(uint32_t* __restrict__ p, int n, uint32_t* __restrict__ counters) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (p != nullptr && i < n) p[i] = 0u;
+  if (counters != nullptr && i < kCounterWords) counters[i] = 0u;
 }
 
 __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
@@ -23,7 +27,8 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
                                                    const uint32_t* __restrict__ order, int64_t num_pairs, int W,
                                                    int H, int TX, int nT, float* __restrict__ image,
                                                    float* __restrict__ T_final, uint32_t* __restrict__ last,
-                                                   uint32_t* __restrict__ tile_processed) {
+                                                   uint32_t* __restrict__ tile_processed, void* split,
+                                                   int seg_shift) {
   __shared__ float4 s_a[kChunk];
   __shared__ float4 s_c[kChunk];
   __shared__ float s_b[kChunk];
@@ -45,10 +50,41 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   uint32_t lastp = 0, read = end - start;
   bool live = inside;       // still compositing
 
+  // split backward: lists longer than a segment record their state at the
+  // segment boundaries they reach; lane k keeps the slot of record k
+  const SplitLayout sl = split_layout(W, H);
+  const SplitState sp = split_state(split, sl);
+  const uint32_t seg_mask = (1u << seg_shift) - 1u;
+  const bool rec = split != nullptr && end - start > seg_mask + 1u;
+  const uint32_t qid = uint32_t(tile) * kWPT + uint32_t(q0);
+  const uint32_t pool = blockIdx.x % kPools;
+  uint32_t* const pool_count = sp.counters + 32 * pool;   // slots taken, items listed
+  int nck = 0;
+  bool ck_open = rec;
+  uint32_t slotv = 0;
+  float U0 = 0.0f, U1 = 0.0f, U2 = 0.0f;   // colour composited in the current segment
+
   const uint32_t ul = uint32_t(lane);
   EntryRec cur = load_entry(proj, load_index(vals, start + ul, start + ul < end));
   int32_t gnext = load_index(vals, start + kChunk + ul, start + kChunk + ul < end);
   for (uint32_t cs = start; cs < end && __any(live); cs += kChunk) {
+    if (ck_open && cs != start && ((cs - start) & seg_mask) == 0) {
+      uint32_t slot = 0;
+      if (lane == 0) slot = atomicAdd(pool_count, 1u);
+      slot = __builtin_amdgcn_readfirstlane(slot);
+      if (slot < uint32_t(sl.pool_slots)) {
+        slot += pool * uint32_t(sl.pool_slots);
+        // T before entry cs - start, and the colour the segment now ending added
+        sp.ck[size_t(slot) * 64 + lane] = make_float4(T, U0, U1, U2);
+        if (lane == 0) sp.owner[slot] = (qid << 5) | uint32_t(nck);
+        slotv = lane == nck ? slot : slotv;
+        U0 = U1 = U2 = 0.0f;
+        ++nck;
+        ck_open = nck < kCkSeg;
+      } else {
+        ck_open = false;   // pool exhausted: the segments from here on stay one
+      }
+    }
     const EntryRec nxt = load_entry(proj, gnext);
     const uint32_t j2 = cs + 2 * kChunk + ul;
     gnext = load_index(vals, j2, j2 < end);
@@ -82,6 +118,11 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
       C0 = fmaf(c.z, wgt, C0);
       C1 = fmaf(c.w, wgt, C1);
       C2 = fmaf(cb, wgt, C2);
+      if (rec) {
+        U0 = fmaf(c.z, wgt, U0);
+        U1 = fmaf(c.w, wgt, U1);
+        U2 = fmaf(cb, wgt, U2);
+      }
       T = comp ? nt : T;
       lastp = comp ? pos1 : lastp;
       read = stop ? pos1 : read;
@@ -103,19 +144,68 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     const uint32_t rmax = wave_max_u32(inside ? read : 0u);
     if (lane == 0 && rmax != 0) atomicMax(tile_processed + tile, rmax);
   }
+  if (split != nullptr) {
+    // recorded segment colours -> the colour behind each boundary b: the
+    // sum of the segments after it (positive terms, no cancellation) / T_b
+    // (T_b >= 1e-4: a pixel stops before its transmittance drops below)
+    // (loads issued four at a time, so the heaviest quarters, which record
+    // the most, do not wait for one round trip per record at their end)
+    for (int k0 = nck - 1; k0 >= 0; k0 -= 4) {
+      float4 v[4];
+      float4* p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = k0 - j >= 0 ? k0 - j : 0;
+        p[j] = sp.ck + size_t(__builtin_amdgcn_readlane(slotv, k)) * 64 + lane;
+        v[j] = *p[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (k0 - j >= 0) {
+          *p[j] = make_float4(v[j].x, U0 / v[j].x, U1 / v[j].x, U2 / v[j].x);
+          U0 += v[j].y;
+          U1 += v[j].z;
+          U2 += v[j].w;
+        }
+      }
+    }
+    // the whole segments below the last entry any pixel composited go to
+    // the helpers; the quarter's own wave keeps the rest
+    const uint32_t lmax = wave_max_u32(lastp);
+    uint32_t nseg = lmax == 0 ? 0u : (lmax - 1) >> seg_shift;
+    if (nseg > uint32_t(nck)) nseg = uint32_t(nck);
+    if (lane == 0) sp.qsegs[qid] = nseg;
+    if (nseg != 0) {
+      uint32_t b = 0;
+      if (lane == 0) b = atomicAdd(pool_count + 1, nseg);
+      b = __builtin_amdgcn_readfirstlane(b);
+      if (ul < nseg) sp.items[pool * uint32_t(sl.pool_slots) + b + ul] = slotv;
+    }
+  }
 }
 
 }  // namespace
 
+size_t raster_split_bytes(int32_t width, int32_t height) { return split_layout(width, height).bytes; }
+
+bool raster_split_fits(int32_t width, int32_t height) {
+  return split_layout(width, height).quarters < (int64_t(1) << 27);   // quarter << 5 in 32 bits
+}
+
 hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
-                             float* image, float* T_final, uint32_t* last, uint32_t* tile_processed, hipStream_t st) {
+                             float* image, float* T_final, uint32_t* last, uint32_t* tile_processed, void* split,
+                             int seg_shift, hipStream_t st) {
   const int TX = (width + kTile - 1) / kTile, TY = (height + kTile - 1) / kTile;
   const int nT = TX * TY;
-  if (tile_processed != nullptr) k_fill<<<unsigned((nT + 63) / 64), 64, 0, st>>>(tile_processed, nT, 0u);
+  if (split != nullptr && !raster_split_fits(width, height)) split = nullptr;
+  uint32_t* const counters = split != nullptr ? split_state(split, split_layout(width, height)).counters : nullptr;
+  if (tile_processed != nullptr || counters != nullptr)
+    k_clear<<<unsigned(std::max(tile_processed != nullptr ? (nT + 255) / 256 : 0, kCounterWords / 256)), 256, 0, st>>>(
+        tile_processed, nT, counters);
   k_render_fwd<<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
                                               num_pairs, width, height, TX, nT, image, T_final, last,
-                                              tile_processed);
+                                              tile_processed, split, seg_shift);
   return hipGetLastError();
 }
 

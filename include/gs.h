@@ -89,7 +89,8 @@ typedef enum gs_op {
   GS_OP_PREPROCESS = 0,
   GS_OP_BIN_SORT = 1,
   GS_OP_LOSS = 2,
-  GS_OP_SPARSE_ADAM = 3
+  GS_OP_SPARSE_ADAM = 3,
+  GS_OP_RASTER = 4
 } gs_op;
 
 /* Static description of a status code (never NULL). */
@@ -104,6 +105,7 @@ int gs_version(void);
  *   GS_OP_BIN_SORT    n, pair_capacity
  *   GS_OP_LOSS        width, height
  *   GS_OP_SPARSE_ADAM n
+ *   GS_OP_RASTER      width, height: split_ws of gs_render_fwd / gs_render_bwd
  * Unused arguments are ignored.  The workspace is caller-owned device
  * memory, 256-byte aligned; its contents need no initialisation and are
  * scratch between calls. */
@@ -181,10 +183,24 @@ gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx
  *                tile's range) of the last composited Gaussian, 0 if none
  *   tile_processed  device out or NULL, [TX*TY] uint32: per tile, the
  *                largest number of list entries any of its pixels read
- *                (up to and including the stopping one) */
+ *                (up to and including the stopping one)
+ *   split_ws, split_ws_bytes  device workspace or NULL: at least
+ *                gs_workspace_size(GS_OP_RASTER, 0, width, height) bytes,
+ *                256-byte aligned.  The forward records, for every
+ *                quarter-tile whose list reaches past segment_len entries,
+ *                the per-pixel state (transmittance, colour behind) at each
+ *                multiple of segment_len it reaches (at most 31 per quarter;
+ *                room for half a state per quarter of the image, beyond
+ *                which lists stay whole) and lists the segments
+ *                gs_render_bwd can run in parallel; ignored for images of
+ *                2^25 tiles or more.  Pass it unchanged, with the same
+ *                segment_len, to the gs_render_bwd of this view.
+ *   segment_len  list entries per segment: a power of two in [64, 65536]
+ *                (ignored when split_ws is NULL) */
 gs_status gs_render_fwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height, float* image,
-                        float* T_final, uint32_t* last, uint32_t* tile_processed, void* stream);
+                        float* T_final, uint32_t* last, uint32_t* tile_processed, void* split_ws,
+                        size_t split_ws_bytes, int32_t segment_len, void* stream);
 
 /* Loss of a rendered image against a target (Grendel-GS notes, training
  * pipeline: "L1 + SSIM loss"):
@@ -213,12 +229,17 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
  *                be zero on entry (allocate zeroed; gs_project_bwd re-zeroes
  *                the rows it consumes, so the buffer stays zero between
  *                views).
+ *   split_ws, split_ws_bytes, segment_len  NULL, or what the gs_render_fwd of this view
+ *                was given (its contents as it left them): the listed
+ *                segments of long lists are then walked by separate waves
+ *                from the recorded states, the rest of each list from its
+ *                end (the same sums up to fp32 rounding order)
  * The discrete decisions (skip, stop, 0.99 clamp) are held at the
  * forward's; the 2D mean gradient is in pixels; depth gets none. */
 gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                         const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                        void* stream);
+                        const void* split_ws, size_t split_ws_bytes, int32_t segment_len, void* stream);
 
 /* Projection backward of one view: the chain rule from the screen-space
  * gradients to all 59 parameters (SH coefficients and view direction, EWA

@@ -13,7 +13,8 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:0", dL_override=None):
+def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:0", dL_override=None,
+                 segment_len=None):
     """One training step of the HIP path; per-view snapshots.  With
     ``dL_override`` (one [3][H][W] array per view) the backward is fed that
     image gradient instead of the library's loss output (to test the
@@ -22,7 +23,8 @@ def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:
 
     import differentiable_gaussian_splatting_dgs_amd as gs
 
-    step = gs.from_workload(work, device=device, record_tiles=record_tiles, pair_capacity=pair_capacity)
+    kw = {} if segment_len is None else {"segment_len": segment_len}
+    step = gs.from_workload(work, device=device, record_tiles=record_tiles, pair_capacity=pair_capacity, **kw)
     views = []
     for k, vw in enumerate(step.views):
         step.forward_view(k)

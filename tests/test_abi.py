@@ -106,6 +106,21 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, *tail) == 1
     assert b"grad2d[1]" in lib.gs_last_error()
     assert lib.gs_project_bwd_adam(*args, cams, 2, None, *tail) == 1
+    # rasterisers: segment length not a power of two in [64, 65536],
+    # misaligned split workspace (checked before anything is launched)
+    fwd = (P(16), 4, P(16), P(16), None, 8, 64, 64, P(16), P(16), P(16), None)
+    bwd = (P(16), 4, P(16), P(16), None, 8, 64, 64, P(16), P(16), P(16), P(16))
+    need = gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 64, 64)
+    for seg in (0, 32, 100, 1 << 17):
+        assert lib.gs_render_fwd(*fwd, P(256), need, seg, None) == 1
+        assert b"segment_len" in lib.gs_last_error()
+        assert lib.gs_render_bwd(*bwd, P(256), need, seg, None) == 1
+    assert lib.gs_render_fwd(*fwd, P(272), need, 1024, None) == 1
+    assert b"split_ws" in lib.gs_last_error()
+    assert lib.gs_render_bwd(*bwd, P(272), need, 1024, None) == 1
+    assert lib.gs_render_fwd(*fwd, P(256), need - 1, 1024, None) == 1
+    assert b"split_ws_bytes" in lib.gs_last_error()
+    assert lib.gs_render_bwd(*bwd, P(256), need - 1, 1024, None) == 1
 
 
 def test_workspace_sizes():
@@ -115,5 +130,11 @@ def test_workspace_sizes():
     assert b > a > 12 * 10000
     assert gs.gs_workspace_size(gs.GS_OP_LOSS, 0, 64, 48) >= 9 * 4 * 64 * 48
     assert gs.gs_workspace_size(gs.GS_OP_PREPROCESS, 0) > 0
+    # raster split state: at least 64 recorded states (64 pixels x 16 bytes)
+    # in each of 64 pools; half a state per quarter-tile (1080p: 32640)
+    assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 64, 64) > 64 * 64 * 64 * 16
+    assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 1920, 1080) >= 16320 * 64 * 16
+    with pytest.raises(gs.GSError):
+        gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 0, 64)
     with pytest.raises(gs.GSError):
         gs.gs_workspace_size(gs.GS_OP_LOSS, 0, 0, 48)

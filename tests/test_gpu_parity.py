@@ -248,6 +248,51 @@ def test_backward_stages_in_isolation(case):
     check_grad(f"{case} grads (isolated)", res["grads"], ref["grads"], ref["mags"])
 
 
+def split_pool_counts(step, vw):
+    """Per pool of the split workspace: states requested by the last view's
+    forward (the counter runs on past the pool size) and the pool size.
+    The layout: states [slots][64] float4, owners and items [slots] u32,
+    segment counts [quarters] u32, then 64 pools x 32 counter words."""
+    import torch
+
+    quarters = ((vw.W + 15) // 16) * ((vw.H + 15) // 16) * 4
+    pool_slots = max(64, (quarters // 2 + 63) // 64)
+    slots = 64 * pool_slots
+    off = slots * 64 * 16 + 8 * slots + 4 * quarters
+    c = step.split_ws[off:off + 64 * 32 * 4].view(torch.int32).view(64, 32).cpu().numpy()
+    return c[:, 0].astype(np.int64), pool_slots
+
+
+@pytest.mark.parametrize("case,seg", [("small_cut", 64), ("mid_cut", 64), ("mid_cut", 256), ("small_full", 64)])
+def test_split_backward_matches_whole_list_backward(case, seg):
+    """The raster backward with long lists walked in segments (helper waves
+    starting from the forward's recorded states) against the oracle and
+    against the one-wave-per-quarter backward, on the oracle's image
+    gradient; short segments so that many quarters of these workloads are
+    split several times, and on the whole small workload so many that some
+    pools run out of states (those quarters keep the rest of their list
+    whole)."""
+    work = workload_case(case)
+    ref = oracle.step(work)
+    dl = [vw["dL_dimage"] for vw in ref["views"]]
+    split, step = run_gpu_step(work, dL_override=dl, segment_len=seg)
+    requested, pool_slots = split_pool_counts(step, step.views[-1])
+    whole, _ = run_gpu_step(work, dL_override=dl, segment_len=0)
+    longest = 0
+    for k, (cam, gs_, gw, ov) in enumerate(zip(work.cameras, split["views"], whole["views"], ref["views"])):
+        vis = oracle.preprocess(work.params, cam)["visible"]
+        check_grad(f"{case}/v{k} grad2d (split {seg})", gs_["grad2d"][vis], ov["g2d"][vis], ov["m2d"][vis])
+        check_grad(f"{case}/v{k} split vs whole", gs_["grad2d"][vis], gw["grad2d"][vis].astype(np.float64),
+                   ov["m2d"][vis], rel=1e-4, mtol=2e-5)
+        assert np.array_equal(gs_["last"], gw["last"]) and np.array_equal(gs_["image"], gw["image"])
+        longest = max(longest, int(gs_["last"].max()))
+    say(f"  {case}: longest composited prefix {longest} (segments of {seg}); states requested per pool "
+        f"max {requested.max()} of {pool_slots}, total {requested.sum()}")
+    assert longest > 3 * seg, "no quarter spans several segments"
+    if case == "small_full":
+        assert requested.max() > pool_slots, "no pool ran out of states"
+
+
 def test_determinism_of_integer_outputs():
     work = workload_case("small_cut")
     a, _ = run_gpu_step(work)
