@@ -262,15 +262,17 @@ class _PairSet:
     sets so that later views' preprocess and binning can run while the
     current view renders and back-propagates."""
 
-    def __init__(self, n, cap, device):
+    def __init__(self, n, cap, device, with_keys):
         rows = max(n, 1)
-        self.n, self.device = n, device
+        self.n, self.device, self.with_keys = n, device, with_keys
         self.proj = torch.empty((rows, GS_PROJ_WORDS), dtype=torch.float32, device=device)
         self.alloc(cap)
 
     def alloc(self, cap):
         self.capacity = cap
-        self.keys = torch.empty(max(cap, 1), dtype=torch.int64, device=self.device)
+        # the 64-bit sort keys are an output the rasterisers never read; the
+        # binning needs them only for images over 256 tiles on a side
+        self.keys = torch.empty(max(cap, 1), dtype=torch.int64, device=self.device) if self.with_keys else None
         self.vals = torch.empty(max(cap, 1), dtype=torch.int32, device=self.device)
         self.ws_sort = _bytes(gs_workspace_size(GS_OP_BIN_SORT, self.n, 0, 0, cap), self.device)
 
@@ -326,7 +328,8 @@ class TrainStep:
         self.pair_capacity = int(min(pair_capacity, (1 << 31) - 1))
         self.views = [View(c, tg, n, self.pair_capacity, self.device) for c, tg in zip(cameras, targets)]
         self.nsets = min(3, max(2, len(self.views)))
-        self.sets = [_PairSet(n, self.pair_capacity, self.device) for _ in range(self.nsets)]
+        with_keys = any(v.W > 4096 or v.H > 4096 for v in self.views)
+        self.sets = [_PairSet(n, self.pair_capacity, self.device, with_keys) for _ in range(self.nsets)]
         self._cur = 0                       # set of the view last prepared
         self._free = [None] * self.nsets    # per set: event after its last reader
         self.M_dev = torch.zeros(len(self.views), dtype=torch.int64, device=self.device)
@@ -351,6 +354,8 @@ class TrainStep:
 
     @property
     def keys(self):
+        """The sorted keys of the view last prepared, or None when the
+        binning left them unwritten (images of at most 256 x 256 tiles)."""
         return self.sets[self._cur].keys
 
     @property

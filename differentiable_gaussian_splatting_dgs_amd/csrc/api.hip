@@ -185,7 +185,9 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   REQUIRE(pair_capacity >= 0 && pair_capacity < (int64_t(1) << 31), "pair_capacity out of range");
   REQUIRE(vis_count != nullptr && num_pairs != nullptr && tile_ranges != nullptr, "NULL argument");
   if (n > 0) REQUIRE(proj && vis_idx && aligned(proj, 16), "NULL or misaligned proj / vis_idx");
-  if (pair_capacity > 0) REQUIRE(keys && vals && aligned(keys, 8), "NULL or misaligned keys / vals");
+  if (pair_capacity > 0)
+    REQUIRE(vals && (keys ? aligned(keys, 8) : gs::binsort_keys_optional((width + 15) / 16, (height + 15) / 16)),
+            "NULL or misaligned keys / vals (keys may be NULL only up to 256 x 256 tiles)");
   REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
   REQUIRE(workspace_bytes >= gs::binsort_ws_bytes(n, pair_capacity), "workspace too small");
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -216,7 +218,9 @@ gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx
   REQUIRE(vis_count != nullptr && num_pairs_dev != nullptr && tile_ranges != nullptr, "NULL argument");
   REQUIRE(aligned(num_pairs_dev, 8), "misaligned num_pairs_dev");
   if (n > 0) REQUIRE(proj && vis_idx && aligned(proj, 16), "NULL or misaligned proj / vis_idx");
-  if (pair_capacity > 0) REQUIRE(keys && vals && aligned(keys, 8), "NULL or misaligned keys / vals");
+  if (pair_capacity > 0)
+    REQUIRE(vals && (keys ? aligned(keys, 8) : gs::binsort_keys_optional((width + 15) / 16, (height + 15) / 16)),
+            "NULL or misaligned keys / vals (keys may be NULL only up to 256 x 256 tiles)");
   REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
   REQUIRE(workspace_bytes >= gs::binsort_ws_bytes(n, pair_capacity), "workspace too small");
   const hipStream_t st = static_cast<hipStream_t>(stream);

@@ -806,7 +806,7 @@ __global__ __launch_bounds__(256) void k_expand(const uint32_t* __restrict__ chu
         if (cw == 0) continue;
         if ((cw >> lane) & 1ull) {
           const uint32_t pos = s_pre[k][tt] + uint32_t(count_below(cw));
-          keys[pos] = (uint64_t(s_tile[tt]) << 32) | d;
+          if (keys != nullptr) keys[pos] = (uint64_t(s_tile[tt]) << 32) | d;
           vals[pos] = g;
         }
       }
@@ -1068,6 +1068,8 @@ void radix_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, cons
 }  // namespace
 
 size_t binsort_ws_bytes(int64_t n, int64_t pair_capacity) { return carve_bytes(n, pair_capacity); }
+
+bool binsort_keys_optional(int32_t tiles_x, int32_t tiles_y) { return exact_path(tiles_x, tiles_y); }
 
 int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity) {
   return carve(ws, n, pair_capacity).m_dev;

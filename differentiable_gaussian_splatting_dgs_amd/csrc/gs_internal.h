@@ -39,6 +39,9 @@ hipError_t launch_compact(uint8_t* flags, int64_t n, int32_t* idx, int64_t* coun
 
 // --- bin sort (binsort.hip) ------------------------------------------------
 size_t binsort_ws_bytes(int64_t n, int64_t pair_capacity);
+// True when the sort runs on the super-tile path, where the 64-bit keys are
+// an output only (may be NULL); the plain LSD path sorts them in place.
+bool binsort_keys_optional(int32_t tiles_x, int32_t tiles_y);
 // Stage 1 (asynchronous): depth sort of the visible list and the pair
 // count M, left in device memory at binsort_count_ptr(ws, ...) (and at
 // num_pairs_dev if given).

@@ -138,7 +138,10 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
  *   proj, vis_idx, vis_count   device, from gs_preprocess (same n, view)
  *   keys         device out, [pair_capacity] uint64: (tile << 32) | bit
  *                pattern of the fp32 depth, ascending; equal keys in
- *                ascending Gaussian index
+ *                ascending Gaussian index.  May be NULL when the image is
+ *                at most 256 tiles wide and tall (4096 pixels): the keys
+ *                then go unwritten (vals and tile_ranges determine them:
+ *                the tile from the range, the depth from the record)
  *   vals         device out, [pair_capacity] int32 Gaussian index per pair
  *   num_pairs    host out: M, the number of pairs
  *   tile_ranges  device out, [TX*TY][2] uint32: [start, end) of each tile's

@@ -35,7 +35,7 @@ def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:
             proj=step.proj[: step.n].cpu().numpy().copy(),
             vis=step.vis_idx[k][:V].cpu().numpy().copy(),
             M=M,
-            keys=step.keys[:M].cpu().numpy().view(np.uint64).copy(),
+            keys=step_keys(step, vw, M),
             vals=step.vals[:M].cpu().numpy().copy(),
             ranges=vw.ranges.cpu().numpy().view(np.uint32).copy(),
             order=vw.order.cpu().numpy().view(np.uint32).copy(),
@@ -65,6 +65,32 @@ def run_gpu_step(work, t=1, record_tiles=True, pair_capacity=None, device="cuda:
                union_flags=step.union_flags[: step.n].cpu().numpy().copy(),
                grads_after=step.grads.cpu().numpy())
     return res, step
+
+
+def keys_from_pairs(vals, ranges, proj):
+    """The 64-bit sort keys (tile << 32 | depth bits) of a pair array, from
+    its values, the tile ranges and the projected records: every position
+    inside tile t's range gets tile t; a position no range covers keeps an
+    all-ones tile, so gaps or ranges past the end never pass as a match."""
+    M = vals.shape[0]
+    r = ranges.astype(np.int64).reshape(-1, 2)
+    tiles = np.full(M, 0xFFFFFFFF, np.uint64)
+    nz = np.flatnonzero(r[:, 1] > r[:, 0])
+    lens = r[nz, 1] - r[nz, 0]
+    pos = np.arange(int(lens.sum()), dtype=np.int64) - np.repeat(np.cumsum(lens) - lens, lens) + np.repeat(r[nz, 0], lens)
+    assert pos.size == 0 or (pos.min() >= 0 and pos.max() < M), "tile range outside the pair array"
+    tiles[pos] = np.repeat(nz.astype(np.uint64), lens)
+    depth = np.ascontiguousarray(proj[:, 12]).view(np.uint32).astype(np.uint64)
+    return (tiles << np.uint64(32)) | depth[vals]
+
+
+def step_keys(step, vw, M):
+    """The keys of the view last prepared: as written by the binning when the
+    step keeps them, else rebuilt from its values, ranges and records."""
+    if step.keys is not None:
+        return step.keys[:M].cpu().numpy().view(np.uint64).copy()
+    return keys_from_pairs(step.vals[:M].cpu().numpy(), vw.ranges.cpu().numpy().view(np.uint32),
+                           step.proj[: step.n].cpu().numpy())
 
 
 def proj_fields(proj):

@@ -88,6 +88,12 @@ def test_invalid_arguments_rejected_on_host():
                                  1 << 30, None) == 1
     assert lib.gs_bin_sort_async(P(16), -1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None, P(256),
                                  1 << 30, None) == 1
+    # bin sort without keys: only up to 256 x 256 tiles (4128 px = 258 tiles)
+    assert lib.gs_bin_sort_async(P(16), 1, P(16), P(16), 4128, 64, None, P(16), 10, P(16), P(16), None, P(256),
+                                 1 << 30, None) == 1
+    assert b"keys may be NULL" in lib.gs_last_error()
+    assert lib.gs_bin_sort(P(16), 1, P(16), P(16), 64, 4128, None, P(16), 10, C.byref(m), P(16), None, P(256),
+                           1 << 30, None) == 1
     # adam: zero bias correction
     assert lib.gs_sparse_adam(P(16), P(16), P(16), P(16), 4, 4, P(16), P(16), P(16), C.c_float(1e-3),
                               C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.0), C.c_float(0.1),

@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import check_grad, proj_fields, run_gpu_step, say
+from gpu_helpers import check_grad, keys_from_pairs, proj_fields, run_gpu_step, say
 
 pytestmark = pytest.mark.gpu
 
@@ -110,9 +110,12 @@ def test_capacity_full_size_pipelined_step_sampled():
             a, b = pf[nm][vis], pre[nm][vis]
             d = np.abs(a.astype(np.float64) - b) / np.maximum(np.abs(b.astype(np.float64)), 1e-30)
             assert d.max() <= 1e-6, f"v{k} {nm}"
-        keys = ps.keys[:M].cpu().numpy().view(np.uint64)
         vals = ps.vals[:M].cpu().numpy()
         ranges = vw.ranges.cpu().numpy().view(np.uint32)
+        # the step leaves the keys unwritten: rebuilt from values, ranges and
+        # records, then held to their definition
+        assert ps.keys is None
+        keys = keys_from_pairs(vals, ranges, ps.proj[: work.n].cpu().numpy())
         TX = (cam.width + 15) // 16
         check_pairs_against_definition(pf, vis_idx, keys, vals, ranges, TX, f"v{k}")
         del keys

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import check_forward, check_grad, proj_fields, run_gpu_step, say
+from gpu_helpers import check_forward, check_grad, proj_fields, run_gpu_step, say, step_keys
 
 pytestmark = pytest.mark.gpu
 
@@ -231,8 +231,15 @@ def test_async_bin_sort_overflow_leaves_empty_ranges():
                          m_dev, ranges, ws)
     torch.cuda.synchronize()
     assert int(m_dev.item()) == M
-    assert torch.equal(keys, step.keys[:M]) and torch.equal(vals, step.vals[:M])
-    assert torch.equal(ranges, vw.ranges)
+    assert np.array_equal(keys.cpu().numpy().view(np.uint64), step_keys(step, vw, M))
+    assert torch.equal(vals, step.vals[:M]) and torch.equal(ranges, vw.ranges)
+    # without keys (what the training step passes): the same values and ranges
+    vals2 = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    ranges2 = torch.full((vw.T, 2), 7, dtype=torch.int32, device="cuda")
+    gs.gs_bin_sort_async(step.proj, step.n, step.vis_idx[0], step.vis_count[0:1], vw.W, vw.H, None, vals2, M,
+                         m_dev, ranges2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(vals2, vals) and torch.equal(ranges2, ranges)
 
 
 @pytest.mark.parametrize("case", ["small_cut", "mid_cut"])
@@ -313,7 +320,7 @@ def forward_only_parity(one, tag):
     vw = step.views[0]
     M = vw.num_pairs
     gv = dict(proj=step.proj.cpu().numpy(), vis=step.vis_idx[0][: int(step.vis_count[0].item())].cpu().numpy(),
-              M=M, keys=step.keys[:M].cpu().numpy().view(np.uint64), vals=step.vals[:M].cpu().numpy(),
+              M=M, keys=step_keys(step, vw, M), vals=step.vals[:M].cpu().numpy(),
               ranges=vw.ranges.cpu().numpy().view(np.uint32), image=vw.image.cpu().numpy(),
               T_final=vw.T_final.cpu().numpy(), last=vw.last.cpu().numpy().view(np.uint32),
               tile_processed=vw.tile_processed.cpu().numpy().view(np.uint32))
