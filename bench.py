@@ -5,11 +5,13 @@ seeded synthetic Gaussians, four 1920x1080 ring views per step.
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
 
 Prints ONE JSON line.  `value` = steps/s with every input resident in HBM
-when the timed region starts.  Per-stage times come from HIP events on the
-stream the library launches on; the dominant raster kernel's roofline uses
-them (each raster entry point is a single kernel launch).  `cpu_baseline` is
-the oracle timed on the host's cores over one step of the same workload
-(bounded: see cpu_baseline).
+when the timed region starts.  Inside the timed region HIP events on the
+stream the library launches on bracket the two raster entry points
+(render_bwd: the k_render_bwd launch; render_fwd: a counter fill and the
+k_render_fwd launch); the dominant one's roofline uses them.  The other
+stages' times come from a shorter pass after it with every stage bracketed.
+`cpu_baseline` is the oracle timed on the host's cores over one step of the
+same workload (bounded: see cpu_baseline).
 """
 from __future__ import annotations
 
@@ -161,18 +163,29 @@ def main():
     gc.collect()
     gc.freeze()
     log(f"[bench] timing {args.steps} steps")
+    # HIP events around the two raster kernels only: an event pair between
+    # two launches leaves the stream idle for several microseconds, and
+    # around every stage (six per view) they cost about 3 % of the step
     step.timer = {}
+    step.timer_stages = {"render_fwd", "render_bwd"}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timer, step.timer = step.timer, None
-    stages = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in timer.items()}
-    launches = {k: len(v) for k, v in timer.items()}
+    timer = step.timer
     ms_per_step = 1e3 * wall / args.steps
     steps_per_s = args.steps / wall
+    # the full per-stage breakdown from a shorter pass with every stage timed
+    step.timer, step.timer_stages = {}, None
+    for _ in range(min(args.steps, 10)):
+        step.step()
+    torch.cuda.synchronize()
+    all_stages, step.timer = step.timer, None
+    stages = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in all_stages.items()}
+    raster = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in timer.items()}
+    launches = {k: len(v) for k, v in timer.items()}
 
     # sizes of the last step (scene drifts slowly under Adam; sizes are re-read)
     views = []
@@ -184,17 +197,17 @@ def main():
     B = algorithmic_bytes(N, views, U)
 
     # roofline of the dominant raster kernel (one launch per view)
-    dom = max(("render_fwd", "render_bwd"), key=lambda k: stages.get(k, 0.0))
+    dom = max(("render_fwd", "render_bwd"), key=lambda k: raster.get(k, 0.0))
     evals = float(np.mean([TILE * TILE * v["M_proc"] for v in views]))
     flops = evals * FLOPS_PER_EVAL[dom]
-    achieved = flops / (stages[dom] * 1e-3)
+    achieved = flops / (raster[dom] * 1e-3)
     kname = "k_render_bwd" if dom == "render_bwd" else "k_render_fwd"
     wl = {2: "mid_1080p"}.get(args.config)
     roofline = {"kernel": kname, "bound": "alu",
                 "achieved": achieved / 1e12, "peak": FP32_VECTOR_PEAK / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / FP32_VECTOR_PEAK,
                 "traffic": recorded_traffic(kname, wl) if wl else None,
-                "avg_launch_ms": stages[dom], "flops_per_launch": flops,
+                "avg_launch_ms": raster[dom], "launches": launches[dom], "flops_per_launch": flops,
                 "evals_per_launch": evals, "flops_per_eval": FLOPS_PER_EVAL[dom]}
 
     out = {
@@ -217,8 +230,8 @@ def main():
         "images_per_s": steps_per_s * len(work.cameras),
         "hbm": {"alg_bytes_per_step": B, "alg_GBps": B / (ms_per_step * 1e-3) / 1e9,
                 "frac_of_peak": B / (ms_per_step * 1e-3) / HBM_PEAK},
+        "raster_ms_per_launch": raster,
         "stages_ms_per_launch": stages,
-        "launches": launches,
         "sizes": {"V": [v["V"] for v in views], "M": [v["M"] for v in views],
                   "M_proc": [v["M_proc"] for v in views], "U": U},
         "roofline": roofline,

@@ -308,6 +308,7 @@ class TrainStep:
         self.t = 0
         self.record_tiles = record_tiles
         self.timer = None        # optional: name -> list of (start, end) torch.cuda.Event pairs
+        self.timer_stages = None  # optional: the stage names to time (None: all)
         rows = max(n, 1)
         # screen-gradient buffers: one per view whose projection backward
         # step() fuses into Adam (the last ndefer views), two alternating
@@ -375,7 +376,7 @@ class TrainStep:
     def _stage(self, name):
         """Bracket the enclosed launches with events on the current stream
         (the stream the library launches on) when timing is enabled."""
-        if self.timer is None:
+        if self.timer is None or (self.timer_stages is not None and name not in self.timer_stages):
             yield
             return
         a = torch.cuda.Event(enable_timing=True)
