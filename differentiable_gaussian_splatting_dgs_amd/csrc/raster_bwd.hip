@@ -75,8 +75,8 @@ __device__ __forceinline__ void wave_sum9(const float v[9], float& q0, float& q1
 __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                           uint32_t start, uint32_t lo, uint32_t hi, float qx, float qy, float pxc,
                                           float pyc, uint32_t lastp, float T, float S0, float S1, float S2,
-                                          float G0, float G1, float G2, float* __restrict__ grad2d, float4* s_a,
-                                          float4* s_c, float* s_b, int32_t* s_g, float* s_acc) {
+                                          float G0, float G1, float G2, float* __restrict__ grad2d, LdsRecs& s_rec,
+                                          float* s_acc) {
   const int lane = threadIdx.x;
   // lanes 0, 8, 16, ..., 56 (row r = lane / 16, half h = lane / 8 % 2)
   // store the half sums: row r of the folded sums q0 / q1 carries sum
@@ -103,7 +103,7 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
     const EntryRec nxt = load_entry(proj, gnext);
     gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= base);
     const uint32_t pos = uint32_t(cs) + ul - start;
-    const bool hit = stage_entry(cur, qx, qy, s_a, s_c, s_b, s_g, lane);
+    const bool hit = stage_entry(cur, qx, qy, s_rec, lane);
     cur = nxt;
     uint64_t active = uint64_t(__ballot(hit && pos < hi));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -113,26 +113,26 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
     while (active != 0) {
       const int k = 63 - __builtin_clzll(active);      // back to front
       active &= ~(1ull << k);
-      const float4 a = s_a[k];
-      const float4 c = s_c[k];
+      const float4 a = s_rec.ac[2 * k];
+      const float hc = s_rec.d[k].x;
       const uint32_t kpos = pos0 + uint32_t(k);
       const float dx = pxc - a.x, dy = pyc - a.y;
-      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
+      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
       bool ok = kpos < lastp && !(power > 0.0f) && !(power < -5.6f);
-      if (!__any(ok)) continue;
-      const float cb = s_b[k];
+      if (!wave_any(ok)) continue;
+      const float4 c = s_rec.ac[2 * k + 1];   // opacity, r, g, b
       const float e = pexp_core(power);
-      const float araw = c.y * e;
+      const float araw = c.x * e;
       const float alpha = fminf(0.99f, araw);
       ok = ok && !(alpha < 1.0f / 255.0f);
       // same decisions as the forward: `ok` = this pixel composited it
       const float om = 1.0f - alpha;
       const float Ti = T * __builtin_amdgcn_rcpf(om);
       const float wgt = ok ? alpha * Ti : 0.0f;
-      const float dal = Ti * fmaf(cb - S2, G2, fmaf(c.w - S1, G1, (c.z - S0) * G0));
-      S0 = ok ? fmaf(alpha, c.z, om * S0) : S0;
-      S1 = ok ? fmaf(alpha, c.w, om * S1) : S1;
-      S2 = ok ? fmaf(alpha, cb, om * S2) : S2;
+      const float dal = Ti * fmaf(c.w - S2, G2, fmaf(c.z - S1, G1, (c.y - S0) * G0));
+      S0 = ok ? fmaf(alpha, c.y, om * S0) : S0;
+      S1 = ok ? fmaf(alpha, c.z, om * S1) : S1;
+      S2 = ok ? fmaf(alpha, c.w, om * S2) : S2;
       T = ok ? Ti : T;
       // the 0.99 clamp passes no gradient
       const float dl = (ok && !(araw > 0.99f)) ? dal : 0.0f;
@@ -173,12 +173,13 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       if (kk >= 0 && fc < 9) {
         const float* acc = s_acc + kk * kAcc;
         const float x = acc[2 * fc] + acc[2 * fc + 1];
-        const float4 a = s_a[kk];
-        const float cx = s_c[kk].x;
-        const float m1 = fc == 0 ? -2.0f * a.z : (fc == 1 ? -2.0f * cx : fk);
+        const float4 a = s_rec.ac[2 * kk];
+        const float2 d = s_rec.d[kk];   // -C/2, index bits
+        const float m1 = fc == 0 ? -2.0f * a.z : (fc == 1 ? -2.0f * d.x : fk);
         // the mean gradients also take the other mean sum (lanes 0 and 1)
         const float gval = fc < 2 ? fmaf(m1, x, -a.w * (acc[2 * (fc ^ 1)] + acc[2 * (fc ^ 1) + 1])) : m1 * x;
-        if (gval != 0.0f) unsafeAtomicAdd(grad2d + size_t(s_g[kk]) * kG2 + fc, gval);
+        const int32_t gi = __builtin_bit_cast(int32_t, d.y);
+        if (gval != 0.0f) unsafeAtomicAdd(grad2d + size_t(gi) * kG2 + fc, gval);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -197,10 +198,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
                                                    const uint32_t* __restrict__ last,
                                                    const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
                                                    const void* split, int seg_shift, int nhelp) {
-  __shared__ float4 s_a[kChunk];
-  __shared__ float4 s_c[kChunk];
-  __shared__ float s_b[kChunk];
-  __shared__ int32_t s_g[kChunk];
+  __shared__ LdsRecs s_rec;
   __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
   const SplitLayout sl = split_layout(W, H);
   const SplitState sp = split_state(const_cast<void*>(split), sl);
@@ -264,7 +262,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
       const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
       bwd_range(proj, vals, start, lo, hi, qx, qy, float(px) + 0.5f, float(py) + 0.5f, lastp, T, S0, S1, S2, G0, G1,
-                G2, grad2d, s_a, s_c, s_b, s_g, s_acc);
+                G2, grad2d, s_rec, s_acc);
     }
     if (!helper) return;
   }

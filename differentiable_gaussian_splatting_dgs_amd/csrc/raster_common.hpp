@@ -122,13 +122,19 @@ __device__ __forceinline__ float pexp_core(float x) {
   return ldexpf(p, static_cast<int>(kf));
 }
 
-// A Gaussian as the rasterisers read it from LDS: (u, v, -A/2, -B),
-// (-C/2, opacity, r, g), b.
-struct RasterRec {
-  float4 a;
-  float4 c;
-  float b;
+// A chunk's Gaussians as the rasterisers read them from LDS, 40 bytes per
+// entry: ac[2 k] = (u, v, -A/2, -B) and ac[2 k + 1] = (opacity, r, g, b)
+// from one address, d[k] = (-C/2, Gaussian index bits).  A visit reads
+// ac[2 k] and d[k].x for the exponent, then ac[2 k + 1] (uniform LDS
+// broadcasts).
+struct LdsRecs {
+  float4 ac[2 * kChunk];
+  float2 d[kChunk];
 };
+
+// Any lane of the wave true (the predicate's ballot, tested in scalar
+// registers).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // One list entry's record as loaded from HBM: the first 11 words of the
 // projected record (u, v, A, B | C, opacity, r, g | b, cull extent x, y)
@@ -181,7 +187,9 @@ __device__ __forceinline__ bool ellipse_misses(float u, float v, float A, float 
   if (!(A > 0.0f && C > 0.0f)) return false;
   const float dx0 = x0 - u, dx1 = x1 - u, dy0 = y0 - v, dy1 = y1 - v;
   if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) return false;
-  const float rc = __fdividef(B, C), ra = __fdividef(B, A);
+  // (hardware reciprocals: a perturbed minimiser is still a point of the
+  // edge, and Q grows only quadratically away from the true one)
+  const float rc = B * __builtin_amdgcn_rcpf(C), ra = B * __builtin_amdgcn_rcpf(A);
   const auto quad = [&](float dx, float dy) { return fmaf(A * dx, dx, fmaf(2.0f * B * dx, dy, C * dy * dy)); };
   const float ey0 = fminf(fmaxf(-rc * dx0, dy0), dy1), ey1 = fminf(fmaxf(-rc * dx1, dy0), dy1);
   const float ex0 = fminf(fmaxf(-ra * dy0, dx0), dx1), ex1 = fminf(fmaxf(-ra * dy1, dx0), dx1);
@@ -192,19 +200,17 @@ __device__ __forceinline__ bool ellipse_misses(float u, float v, float A, float 
   return qmin > tau2 + 1.0e-3f * fabsf(tau2) + 2.0e-3f + 1.0e-5f * S;
 }
 
-// Stage a loaded entry (if any) into LDS slot `lane` and return whether it
-// can reach the wave's quarter, whose pixel centres span
+// Stage a loaded entry (if any) into LDS record `lane` and return whether
+// it can reach the wave's quarter, whose pixel centres span
 // [qx, qx + 7] x [qy, qy + 7]: first the Gaussian's alpha >= 1/255 box
 // [u - ex, u + ex] x [v - ey, v + ey] against the quarter, then (for finite
 // boxes) the exact test of the footprint ellipse against it.
-__device__ __forceinline__ bool stage_entry(const EntryRec& r, float qx, float qy, float4* s_a, float4* s_c,
-                                            float* s_b, int32_t* s_g, int lane) {
+__device__ __forceinline__ bool stage_entry(const EntryRec& r, float qx, float qy, LdsRecs& s_rec, int lane) {
   bool hit = false;
   if (r.g >= 0) {
-    s_a[lane] = make_float4(r.q0.x, r.q0.y, -0.5f * r.q0.z, -r.q0.w);
-    s_c[lane] = make_float4(-0.5f * r.q1.x, r.q1.y, r.q1.z, r.q1.w);
-    s_b[lane] = r.b;
-    if (s_g != nullptr) s_g[lane] = r.g;
+    s_rec.ac[2 * lane] = make_float4(r.q0.x, r.q0.y, -0.5f * r.q0.z, -r.q0.w);
+    s_rec.ac[2 * lane + 1] = make_float4(r.q1.y, r.q1.z, r.q1.w, r.b);
+    s_rec.d[lane] = make_float2(-0.5f * r.q1.x, __builtin_bit_cast(float, r.g));
     const float u = r.q0.x, v = r.q0.y;
     hit = u + r.ex >= qx && u - r.ex <= qx + 7.0f && v + r.ey >= qy && v - r.ey <= qy + 7.0f;
     if (hit && r.ex < 1.0e30f)

@@ -29,9 +29,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
                                                    float* __restrict__ T_final, uint32_t* __restrict__ last,
                                                    uint32_t* __restrict__ tile_processed, void* split,
                                                    int seg_shift) {
-  __shared__ float4 s_a[kChunk];
-  __shared__ float4 s_c[kChunk];
-  __shared__ float s_b[kChunk];
+  __shared__ LdsRecs s_rec;
   int q0;
   const int tile = order_tile(order, nT, q0);
   if (tile < 0) return;
@@ -67,7 +65,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   const uint32_t ul = uint32_t(lane);
   EntryRec cur = load_entry(proj, load_index(vals, start + ul, start + ul < end));
   int32_t gnext = load_index(vals, start + kChunk + ul, start + kChunk + ul < end);
-  for (uint32_t cs = start; cs < end && __any(live); cs += kChunk) {
+  for (uint32_t cs = start; cs < end && wave_any(live); cs += kChunk) {
     if (ck_open && cs != start && ((cs - start) & seg_mask) == 0) {
       uint32_t slot = 0;
       if (lane == 0) slot = atomicAdd(pool_count, 1u);
@@ -88,7 +86,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     const EntryRec nxt = load_entry(proj, gnext);
     const uint32_t j2 = cs + 2 * kChunk + ul;
     gnext = load_index(vals, j2, j2 < end);
-    const bool hit = stage_entry(cur, qx, qy, s_a, s_c, s_b, nullptr, lane);
+    const bool hit = stage_entry(cur, qx, qy, s_rec, lane);
     cur = nxt;
     uint64_t active = __ballot(hit);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -98,15 +96,15 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     while (active != 0) {
       const int k = __builtin_ctzll(active);
       active &= active - 1;
-      const float4 a = s_a[k];
-      const float4 c = s_c[k];
+      const float4 a = s_rec.ac[2 * k];
+      const float hc = s_rec.d[k].x;
       const float dx = pxc - a.x, dy = pyc - a.y;
-      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (c.x * dy) * dy);
+      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
       // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1
       bool ok = live && !(power > 0.0f) && !(power < -5.6f);
-      if (!__any(ok)) continue;
-      const float cb = s_b[k];
-      const float alpha = fminf(0.99f, c.y * pexp_core(power));
+      if (!wave_any(ok)) continue;
+      const float4 c = s_rec.ac[2 * k + 1];   // opacity, r, g, b
+      const float alpha = fminf(0.99f, c.x * pexp_core(power));
       ok = ok && !(alpha < 1.0f / 255.0f);
       const float nt = T * (1.0f - alpha);
       const bool stop = ok && nt < 0.0001f;
@@ -115,14 +113,14 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
       // a zero weight leaves the colour sums exactly as they are
       // (non-negative colours, sums from +0)
       const float wgt = comp ? alpha * T : 0.0f;
-      C0 = fmaf(c.z, wgt, C0);
-      C1 = fmaf(c.w, wgt, C1);
-      C2 = fmaf(cb, wgt, C2);
-      if (rec) {
-        U0 = fmaf(c.z, wgt, U0);
-        U1 = fmaf(c.w, wgt, U1);
-        U2 = fmaf(cb, wgt, U2);
-      }
+      C0 = fmaf(c.y, wgt, C0);
+      C1 = fmaf(c.z, wgt, C1);
+      C2 = fmaf(c.w, wgt, C2);
+      // (kept for every list: cheaper than selecting on `rec`, and unused
+      // when nothing is recorded)
+      U0 = fmaf(c.y, wgt, U0);
+      U1 = fmaf(c.z, wgt, U1);
+      U2 = fmaf(c.w, wgt, U2);
       T = comp ? nt : T;
       lastp = comp ? pos1 : lastp;
       read = stop ? pos1 : read;
