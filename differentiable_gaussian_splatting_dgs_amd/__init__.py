@@ -31,7 +31,7 @@ TILE = 16
 
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
            "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
-           "gs_sparse_adam", "gs_project_bwd_adam"]
+           "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list"]
 
 
 class gs_camera(C.Structure):
@@ -72,8 +72,9 @@ def lib():
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
     L.gs_project_bwd_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, C.POINTER(gs_camera), _i32,
-                                      C.POINTER(C.c_void_p), _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32, _P,
-                                      _sz, _P]
+                                      C.POINTER(C.c_void_p), _P, _P, _P, C.POINTER(gs_camera), _P, _P, _f32, _f32,
+                                      _f32, _f32, _f32, _f32, _P, _sz, _P]
+    L.gs_visible_list.argtypes = [_P, _i64, _P, _P, _P, _sz, _P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = C.c_int
     _handle = L
@@ -214,18 +215,28 @@ def gs_sparse_adam(params, grads, m, v, n, ld, union_flags, union_idx, union_cou
 
 
 def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, union_idx, union_count, lr,
-                        beta1, beta2, eps, bias_c1, bias_c2, workspace, stream=None):
+                        beta1, beta2, eps, bias_c1, bias_c2, workspace, next_cam=None, next_proj=None,
+                        next_flags=None, stream=None):
     """``cams`` / ``grad2d``: one camera and one screen-gradient buffer per
-    fused view; ``grads`` None when no other view contributed."""
+    fused view; ``grads`` None when no other view contributed; ``next_*``:
+    the preprocess of the view rendered next, on the updated rows."""
     nv = len(cams)
     assert len(grad2d) == nv
     carr = (gs_camera * max(nv, 1))(*[c if isinstance(c, gs_camera) else make_camera(c) for c in cams])
     parr = (C.c_void_p * max(nv, 1))(*[g.data_ptr() for g in grad2d])
+    nc = None
+    if next_cam is not None:
+        nc = C.byref(next_cam if isinstance(next_cam, gs_camera) else make_camera(next_cam))
     _check(lib().gs_project_bwd_adam(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, carr, nv, parr,
-                                     _ptr(union_flags), _ptr(union_idx), _ptr(union_count), lr, beta1, beta2, eps,
-                                     bias_c1, bias_c2, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _stream(stream)),
+                                     _ptr(union_flags), _ptr(union_idx), _ptr(union_count), nc, _ptr(next_proj),
+                                     _ptr(next_flags), lr, beta1, beta2, eps, bias_c1, bias_c2, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "gs_project_bwd_adam")
+
+
+def gs_visible_list(flags, n, vis_idx, vis_count, workspace, stream=None):
+    _check(lib().gs_visible_list(_ptr(flags), n, _ptr(vis_idx), _ptr(vis_count), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)), "gs_visible_list")
 
 
 # ---------------------------------------------------------------------------
@@ -293,7 +304,7 @@ class TrainStep:
     one view's stages in order on the current stream."""
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
-                 pair_capacity=None, record_tiles=False, segment_len=SEGMENT_LEN):
+                 pair_capacity=None, record_tiles=False, segment_len=SEGMENT_LEN, fuse_next_preprocess=True):
         p = torch.as_tensor(params, dtype=torch.float32)
         assert p.ndim == 2 and p.shape[0] == 59
         self.device = torch.device(device)
@@ -341,6 +352,13 @@ class TrainStep:
         self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
         self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
         self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
+        # step()'s Adam pass also runs the next step's first preprocess on the
+        # rows it updates (the views are the same every step, so a row
+        # outside the union was invisible in view 0 and keeps its record);
+        # its visibility bytes wait here, zero between uses
+        self.fuse_next_preprocess = fuse_next_preprocess
+        self.next_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
+        self._pre0 = False       # view 0's records and flags come from the last Adam pass
         # the forward's checkpoints and segment list, read by the split raster
         # backward of the same view (both on the current stream, the view's
         # backward before the next view's forward); segment_len None: unsplit
@@ -395,8 +413,17 @@ class TrainStep:
         ps = self.sets[k % self.nsets]
         self._cur = k % self.nsets
         with self._stage("preprocess"):
-            gs_preprocess(self.params, self.n, self.ld, vw.cam, ps.proj, self.vis_idx[k], self.vis_count[k:k + 1],
-                          self.union_flags, self.ws_pre)
+            if k == 0 and self._pre0:
+                # records and flags from the last Adam pass
+                gs_visible_list(self.next_flags, self.n, self.vis_idx[0], self.vis_count[0:1], self.ws_pre)
+                self._pre0 = False
+            else:
+                if self._pre0 and k % self.nsets == 0:
+                    # another view takes view 0's set: drop what the Adam pass left
+                    self.next_flags.zero_()
+                    self._pre0 = False
+                gs_preprocess(self.params, self.n, self.ld, vw.cam, ps.proj, self.vis_idx[k],
+                              self.vis_count[k:k + 1], self.union_flags, self.ws_pre)
         with self._stage("bin_sort"):
             self._bin_sort(k, ps)
         if sync:
@@ -534,10 +561,18 @@ class TrainStep:
         with self._stage("sparse_adam"):
             if fused:
                 ks = range(self.nfirst, len(self.views))
+                nxt = {}
+                if self.fuse_next_preprocess:
+                    # (set 0 holds a preprocess of this batch's parameters:
+                    # rows outside the union are invisible there, tiles 0)
+                    if self._pre0:
+                        self.next_flags.zero_()
+                    nxt = dict(next_cam=self.views[0].cam, next_proj=self.sets[0].proj, next_flags=self.next_flags)
                 gs_project_bwd_adam(self.params, self.grads if self.nfirst > 0 else None, self.m, self.v, self.n,
                                     self.ld, [self.views[k].cam for k in ks], [self.g2d[self._gbuf(k)] for k in ks],
                                     self.union_flags, self.union_idx, self.union_count, self.lr, self.beta1,
-                                    self.beta2, self.eps, bc1, bc2, self.ws_adam)
+                                    self.beta2, self.eps, bc1, bc2, self.ws_adam, **nxt)
+                self._pre0 = bool(nxt)
             else:
                 gs_sparse_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.union_flags,
                                self.union_idx, self.union_count, self.lr, self.beta1, self.beta2, self.eps, bc1,

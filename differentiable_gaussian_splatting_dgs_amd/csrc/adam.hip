@@ -9,6 +9,7 @@
 // consumed gradient is zeroed for the next step.  Rows not in the list are
 // never touched.
 #include "project_grad.hpp"
+#include "project_record.hpp"
 
 namespace gs {
 namespace {
@@ -128,9 +129,25 @@ __global__ __launch_bounds__(256) void k_project_adam(FusedViews views, float* _
     const float vn = fmaf(b2, v[q], ob2 * gk * gk);
     m[q] = mn;
     v[q] = vn;
-    params[q] = p[k] - lr * (mn * ibc1) / (sqrtf(vn * ibc2) + eps);
+    p[k] = p[k] - lr * (mn * ibc1) / (sqrtf(vn * ibc2) + eps);
+    params[q] = p[k];
     if (grads != nullptr) grads[q] = 0.0f;
     if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+  // the next view's record of the updated row (as the preprocess computes it)
+  if (fv->next_proj != nullptr) {
+    const CamArgs nc = arg_camera(&fv->next);
+    float4 rec[4];
+    const bool visible = project_record(p, nc, rec);
+    float4* r = reinterpret_cast<float4*>(fv->next_proj) + 4 * ia;
+    r[0] = rec[0];
+    r[1] = rec[1];
+    r[2] = rec[2];
+    r[3] = rec[3];
+    if (visible) {
+      fv->next_flags[ia] = 1;
+      fv->union_flags[ia] = 1;
+    }
   }
 }
 

@@ -324,7 +324,8 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
 
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
                               const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
-                              int32_t* union_idx, int64_t* union_count, float lr, float beta1, float beta2, float eps,
+                              int32_t* union_idx, int64_t* union_count, const gs_camera* next_cam,
+                              float* next_proj, uint8_t* next_flags, float lr, float beta1, float beta2, float eps,
                               float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream) {
   REQUIRE(num_views >= 0 && num_views <= GS_MAX_FUSED_VIEWS, "num_views = %d outside [0, %d]", int(num_views),
           GS_MAX_FUSED_VIEWS);
@@ -349,12 +350,33 @@ gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, i
   REQUIRE(bias_c1 > 0.0f && bias_c2 > 0.0f, "bias corrections must be > 0");
   REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
   REQUIRE(workspace_bytes >= adam_ws_bytes(n), "workspace too small");
+  REQUIRE((next_cam == nullptr) == (next_proj == nullptr) && (next_cam == nullptr) == (next_flags == nullptr),
+          "next_cam, next_proj and next_flags: all NULL or none");
+  if (next_cam != nullptr) {
+    CHECK(check_camera(next_cam, fv.next));
+    REQUIRE(aligned(next_proj, 16), "next_proj not 16-byte aligned");
+    fv.next_proj = next_proj;
+    fv.next_flags = next_flags;
+    fv.union_flags = union_flags;
+  }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = gs::launch_compact(union_flags, n, union_idx, union_count, true, workspace, st);
   if (e == hipSuccess)
     e = gs::launch_project_adam(params, grads, m, v, n, ld, fv, union_idx, union_count, lr, beta1, beta2, eps,
                                 bias_c1, bias_c2, st);
   return hip_status(e, "gs_project_bwd_adam");
+}
+
+gs_status gs_visible_list(uint8_t* flags, int64_t n, int32_t* vis_idx, int64_t* vis_count, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(vis_count != nullptr, "vis_count is NULL");
+  if (n > 0) REQUIRE(flags && vis_idx && aligned(flags, 16), "NULL or misaligned flags / vis_idx");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::compact_ws_bytes(n), "workspace too small");
+  return hip_status(gs::launch_compact(flags, n, vis_idx, vis_count, true, workspace,
+                                       static_cast<hipStream_t>(stream)),
+                    "gs_visible_list");
 }
 
 }  // extern "C"

@@ -30,7 +30,7 @@ namespace gs {
 namespace {
 
 constexpr int kRT = 256;                 // radix threads per block
-constexpr int kRI = 16;                  // items per thread
+constexpr int kRI = 8;                   // items per thread
 constexpr int kRB = kRT * kRI;           // items per block
 constexpr int kWaves = kRT / 64;
 constexpr int kWaveItems = kRI * 64;

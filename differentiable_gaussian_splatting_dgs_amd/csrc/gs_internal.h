@@ -90,6 +90,13 @@ struct FusedViews {
   CamArgs cam[kMaxFusedViews];
   float* grad2d[kMaxFusedViews];
   int32_t count;
+  // Optional (next_proj != NULL): each updated row is then projected with
+  // `next` into next_proj, next_flags[row] = 1 and union_flags[row] = 1 if
+  // it is visible there (the preprocess of the view rendered next).
+  CamArgs next;
+  float* next_proj;
+  uint8_t* next_flags;
+  uint8_t* union_flags;
 };
 hipError_t launch_project_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
                                const FusedViews& views, const int32_t* rows, const int64_t* row_count, float lr,

@@ -296,13 +296,38 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
  *   grads          the gradients of the batch's other views ([59][ld]),
  *                  zeroed for the listed rows; or NULL: none (taken as zero,
  *                  nothing written)
+ *   next_cam, next_proj, next_flags   NULL, or the preprocess of the view
+ *                rendered next, done on each listed row right after its
+ *                update (Grendel-GS notes, training pipeline: the Gaussian
+ *                transform): the row's projected record with next_cam goes
+ *                to next_proj ([n][GS_PROJ_WORDS], 16-byte aligned) as
+ *                gs_preprocess writes it, and when the row is visible
+ *                next_flags[row] (device, [n] uint8) and union_flags[row]
+ *                are set to 1.  Unlisted rows are not touched: a caller
+ *                whose next view was one of this batch's (unlisted rows
+ *                were invisible in it and keep their parameters) keeps
+ *                their records and flags from that view's gs_preprocess
+ *                and zero flags.  gs_visible_list turns next_flags into
+ *                the view's visible list.
  *   the other arguments as gs_sparse_adam.
  * Errors: GS_ERR_INVALID_ARG for num_views outside the range, a NULL or
  * misaligned buffer, an invalid camera, or as gs_sparse_adam. */
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
                               const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
-                              int32_t* union_idx, int64_t* union_count, float lr, float beta1, float beta2, float eps,
+                              int32_t* union_idx, int64_t* union_count, const gs_camera* next_cam,
+                              float* next_proj, uint8_t* next_flags, float lr, float beta1, float beta2, float eps,
                               float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The ascending visible list of a view from per-Gaussian visibility bytes
+ * (the compaction gs_preprocess ends with; Odin summary page, "Background
+ * and motivation": the sparse, view-dependent set of primitives a view
+ * touches).
+ *   flags        device in/out, [n] uint8, 16-byte aligned: non-zero =
+ *                visible; cleared to 0 on return
+ *   vis_idx, vis_count   device out, as gs_preprocess
+ *   workspace    device, >= gs_workspace_size(GS_OP_PREPROCESS, n) bytes */
+gs_status gs_visible_list(uint8_t* flags, int64_t n, int32_t* vis_idx, int64_t* vis_count, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -154,6 +154,8 @@ def check_forward(gv, ov_pre, okeys, ovals, oranges, oimg, oT, olast, oproc, tag
         bits = np.where(n_pairs > 0, np.floor(np.log2(np.maximum(n_pairs, 1))).astype(np.int64) + 1, 0)
         expect = np.argsort(-bits, kind="stable").astype(np.uint32)
         assert np.array_equal(gv["order"], expect), f"{tag} tile order"
+    if oimg is None:       # preprocess and binning only
+        return
     d_img = float(np.max(np.abs(gv["image"] - oimg))) if oimg.size else 0.0
     n_img = int((gv["image"].view(np.uint32) != oimg.view(np.uint32)).sum())
     say(f"  {tag} image max|diff|={d_img:.3g} not bit-identical {n_img}/{oimg.size}")

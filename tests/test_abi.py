@@ -104,14 +104,26 @@ def test_invalid_arguments_rejected_on_host():
     cams = (gs.gs_camera * 9)(*([cam] * 9))
     bufs = (C.c_void_p * 9)(*([16] * 9))
     args = (P(16), P(16), P(16), P(16), 4, 4)
-    tail = (P(16), P(16), P(16), C.c_float(1e-3), C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15),
-            C.c_float(0.1), C.c_float(0.1), P(256), 1 << 20, None)
+    scal = (C.c_float(1e-3), C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.1), C.c_float(0.1),
+            P(256), 1 << 20, None)
+    tail = (P(16), P(16), P(16), None, None, None) + scal
     assert lib.gs_project_bwd_adam(*args, cams, gs.GS_MAX_FUSED_VIEWS + 1, bufs, *tail) == 1
     assert b"num_views" in lib.gs_last_error()
     bufs[1] = 20
     assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, *tail) == 1
     assert b"grad2d[1]" in lib.gs_last_error()
     assert lib.gs_project_bwd_adam(*args, cams, 2, None, *tail) == 1
+    # the next view's preprocess: camera, records and flags together, records aligned
+    bufs[1] = 16
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), None, P(16), *scal) == 1
+    assert b"next_cam" in lib.gs_last_error()
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), P(20), P(16),
+                                   *scal) == 1
+    assert b"next_proj" in lib.gs_last_error()
+    # visible list: misaligned flags, small workspace
+    assert lib.gs_visible_list(P(17), 10, P(16), P(16), P(256), 1 << 20, None) == 1
+    assert lib.gs_visible_list(P(16), 1 << 20, P(16), P(16), P(256), 16, None) == 1
+    assert b"workspace" in lib.gs_last_error()
     # rasterisers: segment length not a power of two in [64, 65536],
     # misaligned split workspace (checked before anything is launched)
     fwd = (P(16), 4, P(16), P(16), None, 8, 64, 64, P(16), P(16), P(16), None)

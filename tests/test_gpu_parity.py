@@ -170,7 +170,9 @@ def test_fused_step_matches_oracle(case):
     last (up to eight) views fused into the Adam pass, that of any earlier
     view (capacity_cut: two of ten) accumulated into the gradient planes
     first.  The update against the oracle's gradients (as check_adam),
-    screen-space buffers left zero."""
+    screen-space buffers left zero; the union flags the pass leaves are the
+    next step's first view's visibility (its preprocess of the updated
+    rows)."""
     import differentiable_gaussian_splatting_dgs_amd as gs
     work = workload_case(case)
     p0 = work.params.copy()
@@ -183,6 +185,9 @@ def test_fused_step_matches_oracle(case):
     res = dict(params=step.params.cpu().numpy(), m=step.m.cpu().numpy(), v=step.v.cpu().numpy(),
                union=step.union_idx[:U].cpu().numpy().copy(), grads_after=step.grads.cpu().numpy(),
                union_flags=step.union_flags[: step.n].cpu().numpy().copy())
+    nxt = oracle.preprocess(res["params"], work.cameras[0])["visible"]
+    assert np.array_equal(res["union_flags"], nxt.astype(np.uint8)), "union flags of the next step's view 0"
+    res["union_flags"] = np.zeros_like(res["union_flags"])
     tol_g = 1e-3 * np.abs(ref["grads"]) + 1e-4 * ref["mags"] + ref["mags_dl"]
     check_adam(res, ref, work, p0, tol_g)
     for g2 in step.g2d:
@@ -298,6 +303,38 @@ def test_split_backward_matches_whole_list_backward(case, seg):
     assert longest > 3 * seg, "no quarter spans several segments"
     if case == "small_full":
         assert requested.max() > pool_slots, "no pool ran out of states"
+
+
+@pytest.mark.parametrize("case", ["small_cut", "mid_cut"])
+def test_next_step_preprocess_in_the_optimiser_pass(case):
+    """step() projects the updated rows for the next step's first view inside
+    the Adam pass.  After one step: view 0's records (visible rows, every
+    row's tile count), its visible list and the union flags, against the
+    oracle's preprocess of the parameters the step produced; then the next
+    step's first binning from them against the oracle's."""
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    work = workload_case(case)
+    step = gs.from_workload(work, record_tiles=True)
+    step.step()
+    torch.cuda.synchronize()
+    assert step._pre0
+    p1 = step.params.cpu().numpy()
+    cam = work.cameras[0]
+    pre = oracle.preprocess(p1, cam)
+    vis = pre["visible"]
+    assert np.array_equal(step.union_flags[: step.n].cpu().numpy(), vis.astype(np.uint8)), "union flags"
+    step.prepare_view(0)                       # visible list from the pass's flags, then binning
+    torch.cuda.synchronize()
+    assert not step._pre0 and not step.next_flags.any().item(), "flags not consumed"
+    vw = step.views[0]
+    M = vw.num_pairs
+    V = int(step.vis_count[0].item())
+    gv = dict(proj=step.sets[0].proj[: step.n].cpu().numpy(), vis=step.vis_idx[0][:V].cpu().numpy(), M=M,
+              keys=step_keys(step, vw, M), vals=step.vals[:M].cpu().numpy(),
+              ranges=vw.ranges.cpu().numpy().view(np.uint32))
+    okeys, ovals, oranges = oracle.bin_sort(p1, cam)
+    check_forward(gv, pre, okeys, ovals, oranges, None, None, None, None, tag=f"{case} next v0")
+    say(f"  {case}: view 0 after one step: {V} visible, {M} pairs")
 
 
 def test_determinism_of_integer_outputs():
