@@ -125,15 +125,20 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       const float araw = c.x * e;
       const float alpha = fminf(0.99f, araw);
       ok = ok && !(alpha < 1.0f / 255.0f);
-      // same decisions as the forward: `ok` = this pixel composited it
-      const float om = 1.0f - alpha;
+      // same decisions as the forward: `ok` = this pixel composited it.  A
+      // lane that did not takes alpha 0: 1 - 0 = 1 has an exact hardware
+      // reciprocal, T * 1 = T and fma(0, c, 1 * S) = S (colours and S are
+      // finite and >= 0), so its T and S pass through bit for bit, as a
+      // select would keep them, and its weight is 0
+      const float a_ok = ok ? alpha : 0.0f;
+      const float om = 1.0f - a_ok;
       const float Ti = T * __builtin_amdgcn_rcpf(om);
-      const float wgt = ok ? alpha * Ti : 0.0f;
+      const float wgt = a_ok * Ti;
       const float dal = Ti * fmaf(c.w - S2, G2, fmaf(c.z - S1, G1, (c.y - S0) * G0));
-      S0 = ok ? fmaf(alpha, c.y, om * S0) : S0;
-      S1 = ok ? fmaf(alpha, c.z, om * S1) : S1;
-      S2 = ok ? fmaf(alpha, c.w, om * S2) : S2;
-      T = ok ? Ti : T;
+      S0 = fmaf(a_ok, c.y, om * S0);
+      S1 = fmaf(a_ok, c.z, om * S1);
+      S2 = fmaf(a_ok, c.w, om * S2);
+      T = Ti;
       // the 0.99 clamp passes no gradient
       const float dl = (ok && !(araw > 0.99f)) ? dal : 0.0f;
       const float dp = dl * alpha;
