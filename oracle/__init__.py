@@ -330,6 +330,47 @@ def union_list(visible_lists):
 
 
 # ---------------------------------------------------------------------------
+# view coupling (Odin summary page, "Relative locality graph" and the
+# importance-based edge weight / scheduling priority formulas), over the
+# views' visible-index lists as the views' point sets
+# ---------------------------------------------------------------------------
+
+def view_overlap(visible_lists):
+    """[B][B] int64 matrix of |V_i n V_j| (the diagonal: |V_i|) for B
+    ascending visible-index lists, one np.intersect1d per pair."""
+    B = len(visible_lists)
+    inter = np.zeros((B, B), np.int64)
+    for i in range(B):
+        for j in range(i, B):
+            c = np.intersect1d(visible_lists[i], visible_lists[j], assume_unique=True).size
+            inter[i, j] = inter[j, i] = c
+    return inter
+
+
+def view_coupling(inter):
+    """Jaccard edge weights w_ij = |V_i n V_j| / |V_i u V_j| in fp64, with
+    |V_i u V_j| = |V_i| + |V_j| - |V_i n V_j|; w_ij = 0 when the union is
+    empty."""
+    inter = np.asarray(inter, np.int64)
+    d = np.diag(inter)
+    union = d[:, None] + d[None, :] - inter
+    w = np.zeros(inter.shape, np.float64)
+    nz = union > 0
+    w[nz] = inter[nz].astype(np.float64) / union[nz].astype(np.float64)
+    return w
+
+
+def view_priority(w, prev):
+    """s(v | U_prev) = sum over u in U_prev of w_uv, for every view v, the
+    terms added in the order of ``prev`` (fp64)."""
+    w = np.asarray(w, np.float64)
+    s = np.zeros(w.shape[0], np.float64)
+    for u in prev:
+        s = s + w[u]
+    return s
+
+
+# ---------------------------------------------------------------------------
 # one whole training step, stage by stage
 # ---------------------------------------------------------------------------
 

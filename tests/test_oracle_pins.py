@@ -485,3 +485,50 @@ def test_adam_matches_torch_on_gathered_rows():
         opt.step()
         P, M, V = oracle.adam(P, g, M, V, rows, lr, b1, b2, eps, step=t)
     assert np.allclose(P[:, rows], tp.detach().numpy(), rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# view coupling (Odin summary page: Jaccard edge weight, priority score)
+# ---------------------------------------------------------------------------
+
+def test_view_coupling_closed_forms():
+    """Identical sets weigh 1, disjoint 0, an empty union 0 (the page's
+    rule); a hand-worked example: {1,2,3,4} and {3,4,5} share 2 of 5."""
+    a = np.array([1, 2, 3, 4], np.int32)
+    b = np.array([3, 4, 5], np.int32)
+    c = np.array([7, 9], np.int32)
+    e = np.zeros(0, np.int32)
+    inter = oracle.view_overlap([a, b, a, c, e])
+    assert inter.tolist() == [[4, 2, 4, 0, 0], [2, 3, 2, 0, 0], [4, 2, 4, 0, 0], [0, 0, 0, 2, 0],
+                              [0, 0, 0, 0, 0]]
+    w = oracle.view_coupling(inter)
+    assert w[0, 1] == 2 / 5 and w[1, 0] == 2 / 5
+    assert w[0, 2] == 1.0 and w[0, 3] == 0.0 and w[4, 4] == 0.0 and w[4, 0] == 0.0
+    assert w[3, 3] == 1.0
+    # s(v | {0, 3}) = w_0v + w_3v
+    s = oracle.view_priority(w, [0, 3])
+    assert s.tolist() == [1.0, 2 / 5, 1.0, 1.0, 0.0]
+
+
+def test_view_coupling_against_python_sets():
+    """Random subsets of 0..999: intersections and Jaccard weights against
+    Python set arithmetic (a different route to the same definition);
+    the matrix is symmetric with the set sizes on its diagonal."""
+    rng = np.random.default_rng(11)
+    lists = []
+    for k in range(7):
+        p = rng.uniform(0.05, 0.9)
+        lists.append(np.flatnonzero(rng.uniform(size=1000) < p).astype(np.int32))
+    lists.append(np.zeros(0, np.int32))
+    inter = oracle.view_overlap(lists)
+    w = oracle.view_coupling(inter)
+    sets = [set(x.tolist()) for x in lists]
+    for i in range(len(sets)):
+        for j in range(len(sets)):
+            assert inter[i, j] == len(sets[i] & sets[j])
+            u = len(sets[i] | sets[j])
+            assert w[i, j] == (len(sets[i] & sets[j]) / u if u else 0.0)
+    prev = [2, 5, 0]
+    s = oracle.view_priority(w, prev)
+    for v in range(len(sets)):
+        assert s[v] == (w[2, v] + w[5, v]) + w[0, v]
