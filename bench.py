@@ -11,7 +11,9 @@ stream the library launches on bracket the two raster entry points
 k_render_fwd launch); the dominant one's roofline uses them.  The other
 stages' times come from a shorter pass after it with every stage bracketed.
 `cpu_baseline` is the oracle timed on the host's cores over one step of the
-same workload (bounded: see cpu_baseline).
+same workload (bounded: see cpu_baseline).  `view_coupling` times the
+coupling graph of 1,024 flight views over the aerial scene (see
+view_coupling_bench).
 """
 from __future__ import annotations
 
@@ -125,6 +127,64 @@ def cpu_baseline(work, budget_s=30.0):
                       f", Adam over {rows.shape[0]:,} rows in {t_adam:.1f} s"}
 
 
+VALU_INT_PEAK = 256 * 64 * 2.4e9   # 32-bit VALU ops/s: 256 CUs x 64 lanes/clock x 2.4 GHz
+
+
+def view_coupling_bench(calls=20, views=1024, width=1920, height=1080):
+    """gs_view_overlap (counts + Jaccard weights) over the visible lists of
+    ``views`` flight views of the aerial scene (3,000,000 Gaussians), timed
+    per call with HIP events on the stream it launches on; its oracle timed
+    on three of the lists."""
+    import numpy as np
+    import torch
+
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    import oracle
+    import synth
+
+    log(f"[bench] view coupling: aerial scene, {views} flight views")
+    work = synth.workload(3)
+    cams = synth.flight_cameras(width, height, views)
+    vc = gs.ViewCoupling(work.n, views, "cuda:0")
+    dp = torch.from_numpy(work.params).cuda()
+    vc.visible_lists(dp, work.n, cams)
+    vc.overlap()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        a.record(st)
+        vc.overlap()
+        b.record(st)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    words = (work.n + 31) // 32
+    pairs = views * (views + 1) // 2
+    ops = 2.0 * pairs * words          # one AND and one popcount-accumulate per word of a pair
+    counts = vc.counts.cpu().numpy()
+    del vc, dp
+    torch.cuda.empty_cache()
+    # the oracle on three of the lists (their own visible lists, untimed)
+    sample = [0, 417, 1023]
+    olists = [oracle.visible_list(work.params, cams[v]) for v in sample]
+    t0 = time.perf_counter()
+    oracle.view_overlap(olists)
+    t_or = time.perf_counter() - t0
+    return {
+        "workload": f"aerial scene: {work.n:,} Gaussians, {views} flight views of {width}x{height}, "
+                    "visible lists from the preprocess",
+        "views": views, "n": work.n, "pairs": pairs, "mean_list_len": float(counts.mean()),
+        "ms_per_call": ms, "pairs_per_s": pairs / (ms * 1e-3), "calls": calls,
+        "roofline": {"kernel": "k_overlap", "bound": "alu", "achieved": ops / (ms * 1e-3) / 1e12,
+                     "peak": VALU_INT_PEAK / 1e12, "unit": "Tops/s (32-bit VALU)",
+                     "frac": ops / (ms * 1e-3) / VALU_INT_PEAK, "traffic": None,
+                     "ops_per_call": ops, "timed": "whole gs_view_overlap call (zero fill, bitmaps, "
+                                                   "pair tiles, weights)"},
+        "cpu_oracle": {"value": 6 / t_or, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+                       "sample": "np.intersect1d over the 6 pairs (with the diagonal) of 3 of the lists"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +192,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-coupling", action="store_true", help="skip the view-coupling measurement")
+    ap.add_argument("--coupling-only", action="store_true",
+                    help="print only the view-coupling measurement (for profiling it alone)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -145,6 +208,9 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.coupling_only:
+        print(json.dumps({"view_coupling": view_coupling_bench()}), flush=True)
+        return
     log(f"[bench] generating workload {args.config}")
     work = synth.workload(args.config)
     N = work.n
@@ -239,6 +305,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] oracle cpu baseline")
         out["cpu_baseline"] = cpu_baseline(work)
+    if not args.no_coupling:
+        del step
+        torch.cuda.empty_cache()
+        out["view_coupling"] = view_coupling_bench()
     print(json.dumps(out), flush=True)
 
 

@@ -23,15 +23,17 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
 GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM, GS_OP_RASTER = 0, 1, 2, 3, 4
+GS_OP_VIEW_OVERLAP = 5
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
 GS_MAX_FUSED_VIEWS = 8
+GS_MAX_COUPLED_VIEWS = 65536
 SEGMENT_LEN = 512    # list entries per segment of the split raster backward
 TILE = 16
 
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
            "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
-           "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list"]
+           "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list", "gs_view_overlap", "gs_view_priority"]
 
 
 class gs_camera(C.Structure):
@@ -75,6 +77,8 @@ def lib():
                                       C.POINTER(C.c_void_p), _P, _P, _P, C.POINTER(gs_camera), _P, _P, _f32, _f32,
                                       _f32, _f32, _f32, _f32, _P, _sz, _P]
     L.gs_visible_list.argtypes = [_P, _i64, _P, _P, _P, _sz, _P]
+    L.gs_view_overlap.argtypes = [_P, _i64, _P, _i32, _i64, _P, _P, _P, _sz, _P]
+    L.gs_view_priority.argtypes = [_P, _i32, _P, _i32, _P, _P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = C.c_int
     _handle = L
@@ -237,6 +241,52 @@ def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, u
 def gs_visible_list(flags, n, vis_idx, vis_count, workspace, stream=None):
     _check(lib().gs_visible_list(_ptr(flags), n, _ptr(vis_idx), _ptr(vis_count), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)), "gs_visible_list")
+
+
+def gs_view_overlap(lists, ld, counts, num_views, n, inter, weights, workspace, stream=None):
+    _check(lib().gs_view_overlap(_ptr(lists), ld, _ptr(counts), num_views, n, _ptr(inter), _ptr(weights),
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_view_overlap")
+
+
+def gs_view_priority(weights, num_views, prev, num_prev, score, stream=None):
+    _check(lib().gs_view_priority(_ptr(weights), num_views, _ptr(prev), num_prev, _ptr(score), _stream(stream)),
+           "gs_view_priority")
+
+
+class ViewCoupling:
+    """Visible lists of a set of views over one scene and their coupling
+    graph (gs_preprocess per view into row v of ``lists``, then
+    gs_view_overlap).  Buffers are allocated once for ``num_views`` views
+    of ``n`` Gaussians."""
+
+    def __init__(self, n: int, num_views: int, device="cuda"):
+        self.n, self.B, self.device = int(n), int(num_views), torch.device(device)
+        self.ld = max(self.n, 1)
+        self.lists = torch.empty((self.B, self.ld), dtype=torch.int32, device=self.device)
+        self.counts = torch.zeros(self.B, dtype=torch.int64, device=self.device)
+        self.inter = torch.empty((self.B, self.B), dtype=torch.int64, device=self.device)
+        self.weights = torch.empty((self.B, self.B), dtype=torch.float64, device=self.device)
+        self.ws = _bytes(gs_workspace_size(GS_OP_VIEW_OVERLAP, self.n, self.B), self.device)
+        self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, self.n), self.device)
+        self.proj = torch.empty((max(self.n, 1), GS_PROJ_WORDS), dtype=torch.float32, device=self.device)
+
+    def visible_lists(self, params, ld, cams, stream=None):
+        """Row v of ``lists`` and counts[v] = the visible list of cams[v]."""
+        assert len(cams) == self.B
+        for v, cam in enumerate(cams):
+            gs_preprocess(params, self.n, ld, cam, self.proj, self.lists[v], self.counts[v:v + 1], None,
+                          self.ws_pre, stream)
+
+    def overlap(self, weights=True, stream=None):
+        gs_view_overlap(self.lists, self.ld, self.counts, self.B, self.n, self.inter,
+                        self.weights if weights else None, self.ws, stream)
+        return self.inter, (self.weights if weights else None)
+
+    def priority(self, prev, stream=None):
+        """s(v | prev) for every view, prev an int32 device tensor."""
+        score = torch.empty(self.B, dtype=torch.float64, device=self.device)
+        gs_view_priority(self.weights, self.B, prev, int(prev.numel()), score, stream)
+        return score
 
 
 # ---------------------------------------------------------------------------

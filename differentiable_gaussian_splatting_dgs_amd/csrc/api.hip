@@ -12,6 +12,7 @@
 #include "gs_internal.h"
 
 static_assert(GS_MAX_FUSED_VIEWS == gs::kMaxFusedViews, "fused view limit");
+static_assert(GS_MAX_COUPLED_VIEWS == gs::kMaxCoupledViews, "coupled view limit");
 
 namespace {
 
@@ -151,6 +152,11 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
     case GS_OP_RASTER:
       CHECK(check_size(width, height));
       *bytes = gs::raster_split_bytes(width, height);
+      return ok();
+    case GS_OP_VIEW_OVERLAP:
+      REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+      REQUIRE(width >= 0 && width <= GS_MAX_COUPLED_VIEWS, "num_views = %d out of range", width);
+      *bytes = gs::coupling_ws_bytes(n, width);
       return ok();
   }
   return fail(GS_ERR_INVALID_ARG, "unknown op %d", int(op));
@@ -377,6 +383,40 @@ gs_status gs_visible_list(uint8_t* flags, int64_t n, int32_t* vis_idx, int64_t* 
   return hip_status(gs::launch_compact(flags, n, vis_idx, vis_count, true, workspace,
                                        static_cast<hipStream_t>(stream)),
                     "gs_visible_list");
+}
+
+gs_status gs_view_overlap(const int32_t* lists, int64_t ld, const int64_t* counts, int32_t num_views, int64_t n,
+                          int64_t* inter, double* weights, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(num_views >= 0 && num_views <= GS_MAX_COUPLED_VIEWS, "num_views = %d out of range", num_views);
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(ld >= 1, "ld = %lld < 1", (long long)ld);
+  if (num_views == 0) return ok();
+  REQUIRE(lists != nullptr && counts != nullptr, "lists or counts is NULL");
+  REQUIRE(aligned(counts, 8), "counts not 8-byte aligned");
+  REQUIRE(inter != nullptr && aligned(inter, 8), "inter NULL or not 8-byte aligned");
+  REQUIRE(weights == nullptr || aligned(weights, 8), "weights not 8-byte aligned");
+  REQUIRE(aligned(lists, 4), "lists not 4-byte aligned");
+  const size_t need = gs::coupling_ws_bytes(n, num_views);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+    REQUIRE(workspace_bytes >= need, "workspace too small (%zu < %zu)", workspace_bytes, need);
+  }
+  return hip_status(gs::launch_view_overlap(lists, ld, counts, num_views, n, inter, weights, workspace,
+                                            static_cast<hipStream_t>(stream)),
+                    "gs_view_overlap");
+}
+
+gs_status gs_view_priority(const double* weights, int32_t num_views, const int32_t* prev, int32_t num_prev,
+                           double* score, void* stream) {
+  REQUIRE(num_views >= 0 && num_views <= GS_MAX_COUPLED_VIEWS, "num_views = %d out of range", num_views);
+  REQUIRE(num_prev >= 0, "num_prev = %d < 0", num_prev);
+  if (num_views == 0) return ok();
+  REQUIRE(weights != nullptr && aligned(weights, 8), "weights NULL or not 8-byte aligned");
+  REQUIRE(score != nullptr && aligned(score, 8), "score NULL or not 8-byte aligned");
+  REQUIRE(num_prev == 0 || prev != nullptr, "prev is NULL");
+  return hip_status(gs::launch_view_priority(weights, num_views, prev, num_prev, score,
+                                             static_cast<hipStream_t>(stream)),
+                    "gs_view_priority");
 }
 
 }  // extern "C"

@@ -105,4 +105,15 @@ hipError_t launch_sparse_adam(float* params, float* grads, float* m, float* v, i
                               const int32_t* rows, const int64_t* row_count, float lr, float beta1,
                               float beta2, float eps, float bc1, float bc2, hipStream_t st);
 
+// --- view coupling (coupling.hip) ---------------------------------------------
+constexpr int kMaxCoupledViews = 65536;
+// bitmap workspace of the overlap pass
+size_t coupling_ws_bytes(int64_t n, int32_t num_views);
+// lists: [B][ld] int32, view v ascending in its first counts[v] entries;
+// inter: [B][B] int64 intersection counts; weights: NULL or [B][B] fp64 Jaccard.
+hipError_t launch_view_overlap(const int32_t* lists, int64_t ld, const int64_t* counts, int B, int64_t n,
+                               int64_t* inter, double* weights, void* ws, hipStream_t st);
+hipError_t launch_view_priority(const double* weights, int B, const int32_t* prev, int nprev, double* score,
+                                hipStream_t st);
+
 }  // namespace gs

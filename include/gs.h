@@ -84,13 +84,16 @@ typedef struct gs_camera {
 #define GS_GRAD2D_WORDS 12
 /* most views whose projection backward gs_project_bwd_adam fuses */
 #define GS_MAX_FUSED_VIEWS 8
+/* most views gs_view_overlap couples in one call */
+#define GS_MAX_COUPLED_VIEWS 65536
 
 typedef enum gs_op {
   GS_OP_PREPROCESS = 0,
   GS_OP_BIN_SORT = 1,
   GS_OP_LOSS = 2,
   GS_OP_SPARSE_ADAM = 3,
-  GS_OP_RASTER = 4
+  GS_OP_RASTER = 4,
+  GS_OP_VIEW_OVERLAP = 5
 } gs_op;
 
 /* Static description of a status code (never NULL). */
@@ -106,6 +109,7 @@ int gs_version(void);
  *   GS_OP_LOSS        width, height
  *   GS_OP_SPARSE_ADAM n
  *   GS_OP_RASTER      width, height: split_ws of gs_render_fwd / gs_render_bwd
+ *   GS_OP_VIEW_OVERLAP n, width = num_views
  * Unused arguments are ignored.  The workspace is caller-owned device
  * memory, 256-byte aligned; its contents need no initialisation and are
  * scratch between calls. */
@@ -328,6 +332,51 @@ gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, i
  *   workspace    device, >= gs_workspace_size(GS_OP_PREPROCESS, n) bytes */
 gs_status gs_visible_list(uint8_t* flags, int64_t n, int32_t* vis_idx, int64_t* vis_count, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Pairwise overlap of views' visible sets and their coupling weights
+ * (Odin summary page, "Relative locality graph": the edge weight of two
+ * data items is the Jaccard similarity of their point sets, |P_i n P_j| /
+ * |P_i u P_j|, and 0 when the union is empty).  The point set of a view is
+ * its visible list as gs_preprocess writes it (the page builds its graph
+ * from SfM tracks ahead of time and notes a computation-based variant; the
+ * visible lists are that variant's sets).
+ *   lists        device, [num_views][ld] int32: view v's set in the first
+ *                counts[v] entries of row v, strictly ascending, each in
+ *                [0, n) (what gs_preprocess writes to vis_idx)
+ *   ld           row stride of lists in entries, >= 1
+ *   counts       device, [num_views] int64 (gs_preprocess's vis_count);
+ *                read as min(max(counts[v], 0), ld)
+ *   num_views    0 .. GS_MAX_COUPLED_VIEWS
+ *   n            number of Gaussians (the universe of the sets), 0 .. 2^31-1
+ *   inter        device out, [num_views][num_views] int64, 8-byte aligned:
+ *                |P_i n P_j|; the diagonal holds |P_i|
+ *   weights      device out, [num_views][num_views] fp64, 8-byte aligned,
+ *                or NULL: w_ij, computed in fp64 as inter_ij /
+ *                (inter_ii + inter_jj - inter_ij), and 0 where that union
+ *                is 0 (so w_ii = 1 for a non-empty set)
+ *   workspace    device, >= gs_workspace_size(GS_OP_VIEW_OVERLAP, n,
+ *                num_views) bytes, 256-byte aligned
+ * Entries outside [0, n) are skipped.  Lists that are not strictly
+ * ascending give unspecified counts (every access stays inside the
+ * buffers).  Counts are exact integers; the result does not depend on the
+ * launch schedule.
+ * Errors: GS_ERR_INVALID_ARG for sizes out of range or a NULL or
+ * misaligned buffer. */
+gs_status gs_view_overlap(const int32_t* lists, int64_t ld, const int64_t* counts, int32_t num_views, int64_t n,
+                          int64_t* inter, double* weights, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scheduling priority of every view given the previously scheduled set
+ * (Odin summary page, "Relative locality graph": s(v | U_prev) is the sum
+ * of w_uv over u in U_prev).
+ *   weights      device, [num_views][num_views] fp64 (gs_view_overlap)
+ *   prev         device, [num_prev] int32 view indices (U_prev; a repeated
+ *                index is added again, one outside [0, num_views) is
+ *                skipped); may be NULL when num_prev is 0
+ *   score        device out, [num_views] fp64: s(v | U_prev), the terms
+ *                added in fp64 in the order of prev, from 0
+ * Errors: GS_ERR_INVALID_ARG for sizes out of range or a NULL buffer. */
+gs_status gs_view_priority(const double* weights, int32_t num_views, const int32_t* prev, int32_t num_prev,
+                           double* score, void* stream);
 
 #ifdef __cplusplus
 }

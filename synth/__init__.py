@@ -123,6 +123,41 @@ def ring_camera(width, height, theta, radius=4.0) -> Camera:
     return look_camera(width, height, eye, -eye, (0.0, 1.0, 0.0))
 
 
+def orbit_cameras(width, height, count, radius=4.0, max_elev_deg=35.0):
+    """``count`` cameras on a band of the sphere of ``radius`` around the
+    origin, all looking at the origin: azimuths step by the golden angle,
+    elevations spread evenly in sine up to +-``max_elev_deg`` (a spiral
+    that covers the band without repeats, like a capture orbit)."""
+    golden = math.pi * (3.0 - math.sqrt(5.0))
+    smax = math.sin(math.radians(max_elev_deg))
+    cams = []
+    for k in range(count):
+        th = k * golden
+        el = math.asin(smax * (2.0 * (k + 0.5) / count - 1.0)) if count > 1 else 0.0
+        eye = np.array([radius * math.cos(el) * math.sin(th), -radius * math.sin(el),
+                        -radius * math.cos(el) * math.cos(th)])
+        cams.append(look_camera(width, height, eye, -eye, (0.0, 1.0, 0.0)))
+    return cams
+
+
+def random_visible_lists(rng, n, count):
+    """``count`` ascending int32 index lists over [0, n) with the shapes
+    visible sets take: an empty one, a full one, a single index, then
+    random mixes of contiguous runs (a region in view: whole 32-index words
+    set) and scattered indices (small, distant Gaussians), at densities
+    from 0.1% to 90%."""
+    out = [np.zeros(0, np.int32), np.arange(n, dtype=np.int32),
+           np.array([n - 1] if n > 0 else [], np.int32)]
+    while len(out) < count:
+        dens = float(rng.choice([0.001, 0.01, 0.1, 0.3, 0.6, 0.9]))
+        mask = rng.random(n) < dens * 0.5
+        for _ in range(int(rng.integers(0, 6))):
+            a = int(rng.integers(0, max(n, 1)))
+            mask[a:a + int(rng.integers(1, max(2, int(dens * n))))] = True
+        out.append(np.flatnonzero(mask).astype(np.int32))
+    return out[:count]
+
+
 # --------------------------------------------------------------------------
 # targets
 # --------------------------------------------------------------------------
@@ -260,6 +295,28 @@ def aerial_camera(width=3840, height=2160, height_above=4.0, tilt_deg=30.0) -> C
     fwd = (0.0, math.cos(t), math.sin(t))
     down = (0.0, math.sin(t), -math.cos(t))
     return look_camera(width, height, (0.0, -height_above, 0.0), fwd, down)
+
+
+def flight_cameras(width, height, count, seed=7, height_above=4.0, tilt_deg=30.0,
+                   x_range=(-3.0, 3.0), z_range=(-2.5, 0.5), max_yaw_deg=25.0):
+    """``count`` aerial cameras over the ground plane of the aerial scene,
+    as a survey flight takes them: eyes ``height_above`` the plane at
+    uniform random (x, z) in the ranges, each tilted ``tilt_deg`` from nadir
+    and turned by a uniform random yaw of up to +-``max_yaw_deg`` from +z.
+    Views near one another see overlapping parts of the ground; distant ones
+    see disjoint parts."""
+    rng = np.random.default_rng(seed)
+    xs = rng.uniform(*x_range, count)
+    zs = rng.uniform(*z_range, count)
+    yaws = np.radians(rng.uniform(-max_yaw_deg, max_yaw_deg, count))
+    t = math.radians(tilt_deg)
+    cams = []
+    for x, z, a in zip(xs, zs, yaws):
+        h = (math.sin(a), 0.0, math.cos(a))          # heading on the ground
+        fwd = (math.sin(t) * h[0], math.cos(t), math.sin(t) * h[2])
+        down = (-math.cos(t) * h[0], math.sin(t), -math.cos(t) * h[2])
+        cams.append(look_camera(width, height, (float(x), -height_above, float(z)), fwd, down))
+    return cams
 
 
 def _pixel_rays(cam: Camera, u, v):

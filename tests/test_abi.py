@@ -20,7 +20,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
-              "gs_sparse_adam", "gs_bin_sort_async", "gs_project_bwd_adam",
+              "gs_sparse_adam", "gs_bin_sort_async", "gs_project_bwd_adam", "gs_visible_list",
+              "gs_view_overlap", "gs_view_priority",
               "gs_workspace_size", "gs_status_string", "gs_last_error", "gs_version"]:
         assert n in names
 
@@ -139,6 +140,31 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.gs_render_fwd(*fwd, P(256), need - 1, 1024, None) == 1
     assert b"split_ws_bytes" in lib.gs_last_error()
     assert lib.gs_render_bwd(*bwd, P(256), need - 1, 1024, None) == 1
+    # view coupling: view count and n out of range, NULL / misaligned
+    # buffers, small workspace; zero views is a no-op
+    ws = gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1000, 3)
+    ov = lambda lists=P(16), ld=1000, counts=P(16), B=3, n=1000, inter=P(16), w=P(16), wsp=P(256), wsb=ws: \
+        lib.gs_view_overlap(lists, ld, counts, B, n, inter, w, wsp, wsb, None)
+    assert ov(B=0, lists=None, counts=None, inter=None, w=None, wsp=None, wsb=0) == 0
+    assert ov(B=-1) == 1 and ov(B=gs.GS_MAX_COUPLED_VIEWS + 1) == 1
+    assert b"num_views" in lib.gs_last_error()
+    assert ov(n=-1) == 1 and ov(n=1 << 31) == 1
+    assert ov(ld=0) == 1
+    assert ov(lists=None) == 1 and ov(counts=None) == 1
+    assert ov(counts=P(20)) == 1 and ov(lists=P(18)) == 1
+    assert ov(inter=None) == 1 and ov(inter=P(20)) == 1
+    assert b"inter" in lib.gs_last_error()
+    assert ov(w=P(20)) == 1
+    assert b"weights" in lib.gs_last_error()
+    assert ov(wsp=P(272)) == 1 and ov(wsp=None) == 1
+    assert ov(wsb=ws - 1) == 1
+    assert b"workspace" in lib.gs_last_error()
+    pr = lambda w=P(16), B=3, prev=P(16), k=2, s=P(16): lib.gs_view_priority(w, B, prev, k, s, None)
+    assert pr(B=0, w=None, prev=None, s=None) == 0
+    assert pr(B=-1) == 1 and pr(k=-1) == 1
+    assert pr(w=None) == 1 and pr(w=P(20)) == 1 and pr(s=None) == 1 and pr(s=P(12)) == 1
+    assert pr(prev=None) == 1
+    assert b"prev" in lib.gs_last_error()
 
 
 def test_workspace_sizes():
@@ -152,6 +178,12 @@ def test_workspace_sizes():
     # in each of 64 pools; half a state per quarter-tile (1080p: 32640)
     assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 64, 64) > 64 * 64 * 64 * 16
     assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 1920, 1080) >= 16320 * 64 * 16
+    # view overlap: one bitmap row per view, n bits padded to 64 words
+    assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1000, 3) == 3 * 64 * 4
+    assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1_000_000, 1024) == 1024 * 31296 * 4
+    assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 0, 5) == 0
+    with pytest.raises(gs.GSError):
+        gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 10, gs.GS_MAX_COUPLED_VIEWS + 1)
     with pytest.raises(gs.GSError):
         gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 0, 64)
     with pytest.raises(gs.GSError):

@@ -160,3 +160,47 @@ def test_capacity_full_size_pipelined_step_sampled():
     assert np.all(np.abs(mg[:, listed] - m_ref[:, listed]) <= 1e-6 * np.abs(m_ref[:, listed]) + 1e-38), "adam m"
     assert np.all(np.abs(vg[:, listed] - v_ref[:, listed]) <= 1e-5 * v_ref[:, listed] + 1e-38), "adam v"
     assert not step.grads[:, rows_t].any().item(), "consumed gradients not zeroed"
+
+
+def test_view_coupling_full_size_sampled():
+    """The coupling graph of 1,024 flight views (1920x1080) over the aerial
+    scene's 3,000,000 Gaussians, as bench.py times it: for 5 sampled views
+    the visible lists against the oracle's, their 5 x 5 block of counts
+    exactly and of weights and priorities bit for bit against the oracle
+    on the oracle's lists; over the whole matrix the properties any
+    intersection matrix has (symmetric, diagonal = list lengths, entries
+    within [0, min of the two lengths], weights in [0, 1])."""
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    work = synth.workload(3)
+    cams = synth.flight_cameras(1920, 1080, 1024)
+    say(f"[coupling full] n={work.n} views={len(cams)}")
+    vc = gs.ViewCoupling(work.n, len(cams), "cuda")
+    dp = torch.from_numpy(work.params).cuda()
+    vc.visible_lists(dp, work.n, cams)
+    inter, w = vc.overlap()
+    sample = [0, 1, 417, 800, 1023]
+    prev = torch.tensor(sample[:3], dtype=torch.int32, device="cuda")
+    s = vc.priority(prev)
+    torch.cuda.synchronize()
+    inter, w, s = inter.cpu().numpy(), w.cpu().numpy(), s.cpu().numpy()
+    counts = vc.counts.cpu().numpy()
+    olists = []
+    for v in sample:
+        ol = oracle.visible_list(work.params, cams[v])
+        row = vc.lists[v, :ol.size].cpu().numpy()
+        assert counts[v] == ol.size and np.array_equal(row, ol), f"view {v} visible list"
+        olists.append(ol)
+    oi = oracle.view_overlap(olists)
+    ow = oracle.view_coupling(oi)
+    sub = np.ix_(sample, sample)
+    assert np.array_equal(inter[sub], oi)
+    assert np.array_equal(w[sub].view(np.uint64), ow.view(np.uint64))
+    os_ = oracle.view_priority(ow, [0, 1, 2])
+    assert np.array_equal(s[sample].view(np.uint64), os_.view(np.uint64))
+    assert np.array_equal(inter, inter.T)
+    assert np.array_equal(np.diag(inter), counts)
+    lo = np.minimum(counts[:, None], counts[None, :])
+    assert (inter >= 0).all() and (inter <= lo).all()
+    assert (w >= 0).all() and (w <= 1).all()
+    say(f"[coupling full] sampled block exact; mean off-diagonal weight "
+        f"{(w.sum() - np.trace(w)) / (len(cams) * (len(cams) - 1)):.3f}")
