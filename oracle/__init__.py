@@ -370,6 +370,70 @@ def view_priority(w, prev):
     return s
 
 
+def tile_partition(cost, num_blocks):
+    """Bounds of ``num_blocks`` contiguous runs of tile ids of about equal
+    total cost (Grendel-GS notes, "dynamic load balancing", pixel-wise
+    balancing: cumulative sum of the per-tile cost, then a sorted search
+    for the multiples of total / K).  P is the exclusive prefix sum of
+    ``cost`` (P[0] = 0, P[T] = total); bounds[0] = 0, bounds[K] = T, and
+    bounds[d] for 0 < d < K is the first t with P[t] >= d * total / K,
+    compared exactly as K * P[t] >= d * total in integers."""
+    cost = np.asarray(cost, np.uint64)
+    T, K = cost.size, int(num_blocks)
+    P = np.zeros(T + 1, dtype=object)
+    P[1:] = np.cumsum(cost.astype(object))
+    total = P[T]
+    bounds = np.zeros(K + 1, np.int64)
+    bounds[K] = T
+    for d in range(1, K):
+        # searchsorted on the exact rational targets d * total / K
+        t = 0
+        while t < T and K * P[t] < d * total:
+            t += 1
+        bounds[d] = t
+    return bounds
+
+
+def tile_blocks_of_rect(rect, bounds, TX):
+    """Ascending block ids whose tile-id range holds a tile of the half-open
+    rectangle rect = (x0, y0, x1, y1): the tiles are enumerated one by one
+    and each is looked up in the bounds."""
+    x0, y0, x1, y1 = (int(r) for r in rect)
+    ids = np.array([ty * TX + tx for ty in range(y0, y1) for tx in range(x0, x1)], np.int64)
+    if ids.size == 0:
+        return np.zeros(0, np.int64)
+    return np.unique(np.searchsorted(np.asarray(bounds, np.int64), ids, side="right") - 1)
+
+
+def pack_records(rects, visible, bounds, TX):
+    """The sending side of the sparse all-to-all from the Gaussian-wise to
+    the pixel-wise split (Grendel-GS notes, "hybrid parallel strategy" and
+    "sparse all-to-all communication"): for each tile block d, in order,
+    the ascending indices of the visible Gaussians whose rectangle holds a
+    tile of block d.  Returns (offsets [K + 1] int64, indices int32)."""
+    K = len(bounds) - 1
+    per = [[] for _ in range(K)]
+    for i in np.flatnonzero(np.asarray(visible)):
+        for d in tile_blocks_of_rect(rects[i], bounds, TX):
+            per[d].append(int(i))
+    offsets = np.zeros(K + 1, np.int64)
+    offsets[1:] = np.cumsum([len(x) for x in per])
+    idx = np.array([i for x in per for i in x], np.int32)
+    return offsets, idx
+
+
+def unpack_grads(grad2d, recv, offsets, idx):
+    """The receiving end of the reverse all-to-all: each block's gradient
+    rows (``recv`` in the packed order) added into the Gaussians' rows,
+    block by block in ascending order, in fp32 (each Gaussian appears at
+    most once per block)."""
+    g = np.array(grad2d, np.float32, copy=True)
+    for d in range(len(offsets) - 1):
+        a, b = int(offsets[d]), int(offsets[d + 1])
+        g[idx[a:b]] = g[idx[a:b]] + np.asarray(recv[a:b], np.float32)
+    return g
+
+
 # ---------------------------------------------------------------------------
 # one whole training step, stage by stage
 # ---------------------------------------------------------------------------

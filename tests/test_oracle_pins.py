@@ -532,3 +532,74 @@ def test_view_coupling_against_python_sets():
     s = oracle.view_priority(w, prev)
     for v in range(len(sets)):
         assert s[v] == (w[2, v] + w[5, v]) + w[0, v]
+
+
+# --- tile partition and the sparse all-to-all's two ends ---------------------
+
+def test_tile_partition_closed_forms():
+    # equal costs split into equal runs; a single costly tile closes the
+    # block whose share it completes; no cost at all puts every tile in the
+    # last block
+    assert list(oracle.tile_partition([1] * 12, 4)) == [0, 3, 6, 9, 12]
+    assert list(oracle.tile_partition([5] * 10, 5)) == [0, 2, 4, 6, 8, 10]
+    assert list(oracle.tile_partition([0, 0, 100, 0], 3)) == [0, 3, 3, 4]
+    assert list(oracle.tile_partition([0] * 5, 3)) == [0, 0, 0, 5]
+    assert list(oracle.tile_partition([7, 1, 1, 1], 1)) == [0, 4]
+
+
+def test_tile_partition_is_numpy_searchsorted():
+    """bounds[d] = 1 + searchsorted(inclusive cumsum, d * total / K, 'left')
+    (the exact rational targets are representable here: totals < 2^40 and
+    K a power of two), and each block's cost stays within total / K plus
+    one tile of the target."""
+    rng = np.random.default_rng(11)
+    for T, K in ((1, 1), (50, 4), (333, 8), (8160, 64), (977, 16)):
+        cost = rng.integers(0, 5000, T) * (rng.random(T) < 0.7)
+        b = oracle.tile_partition(cost, K)
+        C = np.cumsum(cost.astype(np.int64))
+        total = int(C[-1])
+        ref = [0] + [1 + int(np.searchsorted(C, d * total / K, side="left")) if total > 0 else 0
+                     for d in range(1, K)] + [T]
+        assert list(b) == ref, (T, K)
+        assert all(b[d] <= b[d + 1] for d in range(K))
+        for d in range(K):
+            blk = int(cost[b[d]:b[d + 1]].sum())
+            assert blk <= total / K + cost.max() + 1e-9
+
+
+def test_pack_records_against_the_sort_pairs():
+    """With one block per tile the packed lists are the tile lists of the
+    binning (the same pairs, ascending index instead of depth order); with
+    one block every visible Gaussian is listed once, in order; unpacking
+    rows of ones counts each Gaussian's blocks."""
+    w = synth.cut_down(synth.workload(1), 160, 96, n=3000)
+    cam = w.cameras[0]
+    pre = oracle.preprocess(w.params, cam)
+    TX, TY = oracle.tiles_of(cam)
+    T = TX * TY
+    _, vals, ranges = oracle.bin_sort(w.params, cam)
+    off, idx = oracle.pack_records(pre["rect"], pre["visible"], np.arange(T + 1), TX)
+    for t in range(T):
+        a, b = ranges[t]
+        assert np.array_equal(idx[off[t]:off[t + 1]], np.sort(vals[a:b])), t
+    off1, idx1 = oracle.pack_records(pre["rect"], pre["visible"], [0, T], TX)
+    assert list(off1) == [0, int(pre["visible"].sum())]
+    assert np.array_equal(idx1, np.flatnonzero(pre["visible"]))
+    # rows of ones: each Gaussian's row gains its number of blocks
+    g = oracle.unpack_grads(np.zeros((w.n, 12), np.float32), np.ones((idx.size, 12), np.float32), off, idx)
+    assert np.array_equal(g[:, 0], pre["tiles"].astype(np.float32))
+    # one block: the rows land on their Gaussians unchanged
+    rows = np.random.default_rng(3).standard_normal((idx1.size, 12)).astype(np.float32)
+    g1 = oracle.unpack_grads(np.zeros((w.n, 12), np.float32), rows, off1, idx1)
+    assert np.array_equal(g1[idx1], rows)
+
+
+def test_tile_blocks_of_rect_by_hand():
+    # 4 tiles per row; blocks [0,2) [2,5) [5,8) [8,12)
+    b = [0, 2, 5, 8, 12]
+    assert list(oracle.tile_blocks_of_rect((1, 0, 3, 2), b, 4)) == [0, 1, 2]
+    assert list(oracle.tile_blocks_of_rect((0, 2, 1, 3), b, 4)) == [3]
+    assert list(oracle.tile_blocks_of_rect((3, 1, 4, 2), b, 4)) == [2]
+    # a block lying in the gap between two rows of a rectangle is skipped
+    b2 = [0, 3, 5, 12]          # block 1 = tiles 3, 4: (3, 0) and (0, 1)
+    assert list(oracle.tile_blocks_of_rect((1, 0, 3, 3), b2, 4)) == [0, 2]
