@@ -185,6 +185,68 @@ def view_coupling_bench(calls=20, views=1024, width=1920, height=1080):
     }
 
 
+def shard_bench(step, work, K=8, calls=20):
+    """gs_tile_partition, gs_pack_records and gs_unpack_grads on view 0 of
+    the step's workload, cut into K tile blocks by the rasteriser's
+    per-tile counts of the last step; each call timed with HIP events."""
+    import numpy as np
+    import torch
+
+    import differentiable_gaussian_splatting_dgs_amd as gs
+
+    log(f"[bench] tile blocks and the all-to-all's two ends, K={K}")
+    vw = step.views[0]
+    n = step.n
+    proj = torch.empty((n, gs.GS_PROJ_WORDS), dtype=torch.float32, device=step.device)
+    vis = torch.empty(n, dtype=torch.int32, device=step.device)
+    cnt = torch.zeros(1, dtype=torch.int64, device=step.device)
+    ws_pre = torch.empty(gs.gs_workspace_size(gs.GS_OP_PREPROCESS, n), dtype=torch.uint8, device=step.device)
+    gs.gs_preprocess(step.params, n, step.ld, vw.cam, proj, vis, cnt, None, ws_pre)
+    cost = vw.tile_processed
+    bounds = torch.empty(K + 1, dtype=torch.int32, device=step.device)
+    offs = torch.empty(K + 1, dtype=torch.int64, device=step.device)
+    ws = torch.empty(gs.gs_workspace_size(gs.GS_OP_PACK, n, K), dtype=torch.uint8, device=step.device)
+    gs.gs_tile_partition(cost, vw.T, K, bounds)
+    gs.gs_pack_records(proj, n, vis, cnt, vw.W, vw.H, bounds, K, 0, offs, None, None, ws)
+    total = int(offs[K].item())
+    idx = torch.empty(total, dtype=torch.int32, device=step.device)
+    rec = torch.empty((total, gs.GS_PROJ_WORDS), dtype=torch.float32, device=step.device)
+    recv = torch.randn((total, gs.GS_GRAD2D_WORDS), dtype=torch.float32, device=step.device)
+    grad = torch.zeros((n, gs.GS_GRAD2D_WORDS), dtype=torch.float32, device=step.device)
+    st = torch.cuda.current_stream()
+    calls_by = {
+        "partition": lambda: gs.gs_tile_partition(cost, vw.T, K, bounds),
+        "pack": lambda: gs.gs_pack_records(proj, n, vis, cnt, vw.W, vw.H, bounds, K, total, offs, idx, rec, ws),
+        "unpack": lambda: gs.gs_unpack_grads(recv, offs, idx, K, total, grad, n),
+    }
+    ms = {}
+    for name, fn in calls_by.items():
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for a, b in ev:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        ms[name] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    V = int(cnt.item())
+    pack_bytes = 68.0 * V + 68.0 * total          # index + record in, per visible; index + record out, per entry
+    unpack_bytes = 148.0 * total                   # row + index in, Gaussian row read and written, per entry
+    return {
+        "workload": f"{work.name} view 0: {n:,} Gaussians, {vw.W}x{vw.H}, {K} tile blocks by the last "
+                    "step's per-tile processed counts",
+        "blocks": K, "visible": V, "packed": total, "bounds": bounds.cpu().tolist(),
+        "ms_per_call": ms,
+        "pack_roofline": {"bound": "hbm", "achieved": pack_bytes / (ms["pack"] * 1e-3) / 1e9,
+                          "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                          "frac": pack_bytes / (ms["pack"] * 1e-3) / HBM_PEAK, "bytes_per_call": pack_bytes},
+        "unpack_roofline": {"bound": "hbm", "achieved": unpack_bytes / (ms["unpack"] * 1e-3) / 1e9,
+                            "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": unpack_bytes / (ms["unpack"] * 1e-3) / HBM_PEAK,
+                            "bytes_per_call": unpack_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +257,8 @@ def main():
     ap.add_argument("--no-coupling", action="store_true", help="skip the view-coupling measurement")
     ap.add_argument("--coupling-only", action="store_true",
                     help="print only the view-coupling measurement (for profiling it alone)")
+    ap.add_argument("--shard-only", action="store_true",
+                    help="one step, then print only the tile-block / all-to-all measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -216,6 +280,11 @@ def main():
     N = work.n
     step = gs.from_workload(work, device="cuda:0", record_tiles=True)
     torch.cuda.synchronize()
+    if args.shard_only:
+        step.step()
+        torch.cuda.synchronize()
+        print(json.dumps({"shard": shard_bench(step, work)}), flush=True)
+        return
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step.step()
@@ -305,6 +374,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] oracle cpu baseline")
         out["cpu_baseline"] = cpu_baseline(work)
+    out["shard"] = shard_bench(step, work)
     if not args.no_coupling:
         del step
         torch.cuda.empty_cache()

@@ -23,17 +23,20 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
 GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM, GS_OP_RASTER = 0, 1, 2, 3, 4
-GS_OP_VIEW_OVERLAP = 5
+GS_OP_VIEW_OVERLAP, GS_OP_PACK = 5, 6
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
 GS_MAX_FUSED_VIEWS = 8
 GS_MAX_COUPLED_VIEWS = 65536
+GS_MAX_TILE_BLOCKS = 64
+GS_MAX_PARTITION_TILES = 1 << 21
 SEGMENT_LEN = 512    # list entries per segment of the split raster backward
 TILE = 16
 
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
            "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
-           "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list", "gs_view_overlap", "gs_view_priority"]
+           "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list", "gs_view_overlap", "gs_view_priority",
+           "gs_tile_partition", "gs_pack_records", "gs_unpack_grads"]
 
 
 class gs_camera(C.Structure):
@@ -79,6 +82,9 @@ def lib():
     L.gs_visible_list.argtypes = [_P, _i64, _P, _P, _P, _sz, _P]
     L.gs_view_overlap.argtypes = [_P, _i64, _P, _i32, _i64, _P, _P, _P, _sz, _P]
     L.gs_view_priority.argtypes = [_P, _i32, _P, _i32, _P, _P]
+    L.gs_tile_partition.argtypes = [_P, _i32, _i32, _P, _P]
+    L.gs_pack_records.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _i32, _i64, _P, _P, _P, _P, _sz, _P]
+    L.gs_unpack_grads.argtypes = [_P, _P, _P, _i32, _i64, _P, _i64, _P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = C.c_int
     _handle = L
@@ -251,6 +257,23 @@ def gs_view_overlap(lists, ld, counts, num_views, n, inter, weights, workspace, 
 def gs_view_priority(weights, num_views, prev, num_prev, score, stream=None):
     _check(lib().gs_view_priority(_ptr(weights), num_views, _ptr(prev), num_prev, _ptr(score), _stream(stream)),
            "gs_view_priority")
+
+
+def gs_tile_partition(cost, num_tiles, num_blocks, bounds, stream=None):
+    _check(lib().gs_tile_partition(_ptr(cost), num_tiles, num_blocks, _ptr(bounds), _stream(stream)),
+           "gs_tile_partition")
+
+
+def gs_pack_records(proj, n, vis_idx, vis_count, width, height, bounds, num_blocks, capacity, send_offsets,
+                    send_idx, send_rec, workspace, stream=None):
+    _check(lib().gs_pack_records(_ptr(proj), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(bounds),
+                                 num_blocks, capacity, _ptr(send_offsets), _ptr(send_idx), _ptr(send_rec),
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_pack_records")
+
+
+def gs_unpack_grads(recv_grad, send_offsets, send_idx, num_blocks, capacity, grad2d, n, stream=None):
+    _check(lib().gs_unpack_grads(_ptr(recv_grad), _ptr(send_offsets), _ptr(send_idx), num_blocks, capacity,
+                                 _ptr(grad2d), n, _stream(stream)), "gs_unpack_grads")
 
 
 class ViewCoupling:

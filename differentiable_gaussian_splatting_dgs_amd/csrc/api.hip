@@ -13,6 +13,8 @@
 
 static_assert(GS_MAX_FUSED_VIEWS == gs::kMaxFusedViews, "fused view limit");
 static_assert(GS_MAX_COUPLED_VIEWS == gs::kMaxCoupledViews, "coupled view limit");
+static_assert(GS_MAX_TILE_BLOCKS == gs::kMaxTileBlocks, "tile block limit");
+static_assert(GS_MAX_PARTITION_TILES == gs::kMaxPartitionTiles, "partition tile limit");
 
 namespace {
 
@@ -152,6 +154,11 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
     case GS_OP_RASTER:
       CHECK(check_size(width, height));
       *bytes = gs::raster_split_bytes(width, height);
+      return ok();
+    case GS_OP_PACK:
+      REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+      REQUIRE(width >= 1 && width <= GS_MAX_TILE_BLOCKS, "num_blocks = %d out of range", width);
+      *bytes = gs::pack_ws_bytes(n, width);
       return ok();
     case GS_OP_VIEW_OVERLAP:
       REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
@@ -417,6 +424,56 @@ gs_status gs_view_priority(const double* weights, int32_t num_views, const int32
   return hip_status(gs::launch_view_priority(weights, num_views, prev, num_prev, score,
                                              static_cast<hipStream_t>(stream)),
                     "gs_view_priority");
+}
+
+gs_status gs_tile_partition(const uint32_t* cost, int32_t num_tiles, int32_t num_blocks, int32_t* bounds,
+                            void* stream) {
+  REQUIRE(num_tiles >= 1 && num_tiles <= GS_MAX_PARTITION_TILES, "num_tiles = %d out of range", num_tiles);
+  REQUIRE(num_blocks >= 1 && num_blocks <= GS_MAX_TILE_BLOCKS, "num_blocks = %d out of range", num_blocks);
+  REQUIRE(cost != nullptr && aligned(cost, 4), "cost NULL or misaligned");
+  REQUIRE(bounds != nullptr && aligned(bounds, 4), "bounds NULL or misaligned");
+  return hip_status(gs::launch_tile_partition(cost, num_tiles, num_blocks, bounds, static_cast<hipStream_t>(stream)),
+                    "gs_tile_partition");
+}
+
+gs_status gs_pack_records(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                          int32_t width, int32_t height, const int32_t* bounds, int32_t num_blocks,
+                          int64_t capacity, int64_t* send_offsets, int32_t* send_idx, float* send_rec,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(check_size(width, height));
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(num_blocks >= 1 && num_blocks <= GS_MAX_TILE_BLOCKS, "num_blocks = %d out of range", num_blocks);
+  REQUIRE(capacity >= 0 && capacity < (int64_t(1) << 40), "capacity out of range");
+  REQUIRE(vis_count != nullptr && aligned(vis_count, 8), "vis_count NULL or misaligned");
+  REQUIRE(bounds != nullptr && aligned(bounds, 4), "bounds NULL or misaligned");
+  REQUIRE(send_offsets != nullptr && aligned(send_offsets, 8), "send_offsets NULL or misaligned");
+  if (n > 0) REQUIRE(proj != nullptr && aligned(proj, 16) && vis_idx != nullptr, "NULL or misaligned proj / vis_idx");
+  if (capacity > 0) {
+    REQUIRE(send_idx != nullptr, "send_idx is NULL");
+    REQUIRE(send_rec == nullptr || aligned(send_rec, 16), "send_rec not 16-byte aligned");
+  }
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::pack_ws_bytes(n, num_blocks), "workspace too small");
+  return hip_status(gs::launch_pack_records(proj, n, vis_idx, vis_count, (width + 15) / 16, bounds, num_blocks,
+                                            capacity, send_offsets, send_idx, send_rec, workspace,
+                                            static_cast<hipStream_t>(stream)),
+                    "gs_pack_records");
+}
+
+gs_status gs_unpack_grads(const float* recv_grad, const int64_t* send_offsets, const int32_t* send_idx,
+                          int32_t num_blocks, int64_t capacity, float* grad2d, int64_t n, void* stream) {
+  REQUIRE(num_blocks >= 1 && num_blocks <= GS_MAX_TILE_BLOCKS, "num_blocks = %d out of range", num_blocks);
+  REQUIRE(capacity >= 0 && capacity < (int64_t(1) << 40), "capacity out of range");
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(send_offsets != nullptr && aligned(send_offsets, 8), "send_offsets NULL or misaligned");
+  if (capacity > 0)
+    REQUIRE(recv_grad != nullptr && aligned(recv_grad, 16) && send_idx != nullptr,
+            "NULL or misaligned recv_grad / send_idx");
+  if (n > 0) REQUIRE(grad2d != nullptr && aligned(grad2d, 16), "grad2d NULL or not 16-byte aligned");
+  if (capacity == 0 || n == 0) return ok();
+  return hip_status(gs::launch_unpack_grads(recv_grad, send_offsets, send_idx, num_blocks, capacity, grad2d, n,
+                                            static_cast<hipStream_t>(stream)),
+                    "gs_unpack_grads");
 }
 
 }  // extern "C"

@@ -116,4 +116,16 @@ hipError_t launch_view_overlap(const int32_t* lists, int64_t ld, const int64_t* 
 hipError_t launch_view_priority(const double* weights, int B, const int32_t* prev, int nprev, double* score,
                                 hipStream_t st);
 
+// --- tile blocks and the sparse all-to-all's two ends (shard.hip) -----------
+constexpr int kMaxTileBlocks = 64;
+constexpr int32_t kMaxPartitionTiles = 1 << 21;
+size_t pack_ws_bytes(int64_t n, int32_t num_blocks);
+hipError_t launch_tile_partition(const uint32_t* cost, int32_t T, int32_t K, int32_t* bounds, hipStream_t st);
+hipError_t launch_pack_records(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                               int32_t tiles_x, const int32_t* bounds, int32_t K, int64_t capacity,
+                               int64_t* send_offsets, int32_t* send_idx, float* send_rec, void* ws,
+                               hipStream_t st);
+hipError_t launch_unpack_grads(const float* recv, const int64_t* send_offsets, const int32_t* send_idx, int32_t K,
+                               int64_t capacity, float* grad2d, int64_t n, hipStream_t st);
+
 }  // namespace gs

@@ -86,6 +86,10 @@ typedef struct gs_camera {
 #define GS_MAX_FUSED_VIEWS 8
 /* most views gs_view_overlap couples in one call */
 #define GS_MAX_COUPLED_VIEWS 65536
+/* most tile blocks of gs_tile_partition / gs_pack_records, and most tiles
+ * gs_tile_partition splits */
+#define GS_MAX_TILE_BLOCKS 64
+#define GS_MAX_PARTITION_TILES (1 << 21)
 
 typedef enum gs_op {
   GS_OP_PREPROCESS = 0,
@@ -93,7 +97,8 @@ typedef enum gs_op {
   GS_OP_LOSS = 2,
   GS_OP_SPARSE_ADAM = 3,
   GS_OP_RASTER = 4,
-  GS_OP_VIEW_OVERLAP = 5
+  GS_OP_VIEW_OVERLAP = 5,
+  GS_OP_PACK = 6
 } gs_op;
 
 /* Static description of a status code (never NULL). */
@@ -110,6 +115,7 @@ int gs_version(void);
  *   GS_OP_SPARSE_ADAM n
  *   GS_OP_RASTER      width, height: split_ws of gs_render_fwd / gs_render_bwd
  *   GS_OP_VIEW_OVERLAP n, width = num_views
+ *   GS_OP_PACK        n, width = num_blocks
  * Unused arguments are ignored.  The workspace is caller-owned device
  * memory, 256-byte aligned; its contents need no initialisation and are
  * scratch between calls. */
@@ -377,6 +383,70 @@ gs_status gs_view_overlap(const int32_t* lists, int64_t ld, const int64_t* count
  * Errors: GS_ERR_INVALID_ARG for sizes out of range or a NULL buffer. */
 gs_status gs_view_priority(const double* weights, int32_t num_views, const int32_t* prev, int32_t num_prev,
                            double* score, void* stream);
+
+/* Contiguous runs of tile ids with about equal total cost (Grendel-GS
+ * notes, "dynamic load balancing", pixel-wise balancing: the cumulative sum
+ * of the per-block cost is searched at the multiples of total / K).
+ *   cost         device, [num_tiles] uint32 cost per 16x16 tile in
+ *                row-major tile order (the rasteriser's tile_processed
+ *                counts are one such cost)
+ *   num_tiles    1 .. GS_MAX_PARTITION_TILES
+ *   num_blocks   K, 1 .. GS_MAX_TILE_BLOCKS
+ *   bounds       device out, [K + 1] int32: block d is tiles
+ *                [bounds[d], bounds[d + 1]); bounds[0] = 0, bounds[K] =
+ *                num_tiles, and for 0 < d < K bounds[d] is the first t with
+ *                K * P(t) >= d * total, P(t) the cost of tiles [0, t), in
+ *                exact integer arithmetic (a block ends with the tile at
+ *                which its share is reached; with no cost at all every tile
+ *                is in the last block)
+ * Errors: GS_ERR_INVALID_ARG for sizes out of range or a NULL buffer. */
+gs_status gs_tile_partition(const uint32_t* cost, int32_t num_tiles, int32_t num_blocks, int32_t* bounds,
+                            void* stream);
+
+/* The sending end of the sparse all-to-all from the Gaussian-wise to the
+ * pixel-wise split, for one view (Grendel-GS notes, "hybrid parallel
+ * strategy" and "sparse all-to-all communication": each Gaussian goes only
+ * to the pixel blocks its screen footprint reaches).  Block d receives the
+ * visible Gaussians whose tile rectangle holds a tile of [bounds[d],
+ * bounds[d + 1]), in ascending index order, each with its record.
+ *   proj, vis_idx, vis_count   device, the view's gs_preprocess outputs
+ *   n            number of Gaussians, 0 .. 2^31-1
+ *   width, height  the view's image size (the tile grid of the rectangles)
+ *   bounds       device, [num_blocks + 1] int32 (gs_tile_partition's form;
+ *                other contents give other lists but no access out of
+ *                bounds)
+ *   num_blocks   1 .. GS_MAX_TILE_BLOCKS
+ *   capacity     entries send_idx / send_rec hold
+ *   send_offsets device out, [num_blocks + 1] int64, 8-byte aligned: block
+ *                d's entries are [send_offsets[d], send_offsets[d + 1]);
+ *                send_offsets[num_blocks] is the total.  When the total
+ *                exceeds capacity no entry at or past capacity is written:
+ *                call again with capacity >= the total.
+ *   send_idx     device out, [capacity] int32 Gaussian indices
+ *   send_rec     device out, [capacity][GS_PROJ_WORDS] records, 16-byte
+ *                aligned, or NULL for indices only
+ *   workspace    device, >= gs_workspace_size(GS_OP_PACK, n, num_blocks)
+ *                bytes, 256-byte aligned
+ * Errors: GS_ERR_INVALID_ARG for sizes out of range or a NULL or
+ * misaligned buffer. */
+gs_status gs_pack_records(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+                          int32_t width, int32_t height, const int32_t* bounds, int32_t num_blocks,
+                          int64_t capacity, int64_t* send_offsets, int32_t* send_idx, float* send_rec,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* The receiving end of the reverse all-to-all: the screen-space gradient
+ * rows the tile blocks computed for their packed Gaussians, added into the
+ * Gaussians' rows block by block in ascending block order (fp32; a
+ * Gaussian appears at most once per block, so the sums are deterministic).
+ *   recv_grad    device, [capacity][GS_GRAD2D_WORDS] fp32, 16-byte aligned,
+ *                row j for packed entry j
+ *   send_offsets, send_idx   as gs_pack_records wrote them; entries at or
+ *                past capacity and indices outside [0, n) are skipped
+ *   grad2d       device in/out, [n][GS_GRAD2D_WORDS] fp32, 16-byte aligned
+ * Errors: GS_ERR_INVALID_ARG for sizes out of range or a NULL or
+ * misaligned buffer. */
+gs_status gs_unpack_grads(const float* recv_grad, const int64_t* send_offsets, const int32_t* send_idx,
+                          int32_t num_blocks, int64_t capacity, float* grad2d, int64_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
               "gs_sparse_adam", "gs_bin_sort_async", "gs_project_bwd_adam", "gs_visible_list",
-              "gs_view_overlap", "gs_view_priority",
+              "gs_view_overlap", "gs_view_priority", "gs_tile_partition", "gs_pack_records", "gs_unpack_grads",
               "gs_workspace_size", "gs_status_string", "gs_last_error", "gs_version"]:
         assert n in names
 
@@ -159,6 +159,27 @@ def test_invalid_arguments_rejected_on_host():
     assert ov(wsp=P(272)) == 1 and ov(wsp=None) == 1
     assert ov(wsb=ws - 1) == 1
     assert b"workspace" in lib.gs_last_error()
+    # tile partition / pack / unpack: sizes out of range, NULL or
+    # misaligned buffers, small workspace
+    tp = lambda cost=P(16), T=100, K=4, b=P(16): lib.gs_tile_partition(cost, T, K, b, None)
+    assert tp(T=0) == 1 and tp(T=gs.GS_MAX_PARTITION_TILES + 1) == 1
+    assert tp(K=0) == 1 and tp(K=gs.GS_MAX_TILE_BLOCKS + 1) == 1
+    assert b"num_blocks" in lib.gs_last_error()
+    assert tp(cost=None) == 1 and tp(cost=P(18)) == 1 and tp(b=None) == 1
+    pws = gs.gs_workspace_size(gs.GS_OP_PACK, 1000, 4)
+    pk = lambda proj=P(16), n=1000, W=64, H=64, b=P(16), K=4, cap=10, offs=P(16), idx=P(16), rec=P(16), \
+        wsp=P(256), wsb=pws: lib.gs_pack_records(proj, n, P(16), P(16), W, H, b, K, cap, offs, idx, rec, wsp, wsb,
+                                                 None)
+    assert pk(K=0) == 1 and pk(K=65) == 1 and pk(W=0) == 1 and pk(n=-1) == 1 and pk(cap=-1) == 1
+    assert pk(proj=P(20)) == 1 and pk(rec=P(20)) == 1 and pk(offs=P(20)) == 1 and pk(b=None) == 1
+    assert pk(idx=None) == 1
+    assert pk(wsb=pws - 1) == 1
+    assert b"workspace" in lib.gs_last_error()
+    up = lambda recv=P(16), offs=P(16), idx=P(16), K=4, cap=10, g=P(16), n=100: \
+        lib.gs_unpack_grads(recv, offs, idx, K, cap, g, n, None)
+    assert up(K=0) == 1 and up(cap=-1) == 1 and up(n=-1) == 1
+    assert up(recv=P(20)) == 1 and up(g=P(20)) == 1 and up(offs=None) == 1 and up(idx=None) == 1
+    assert up(cap=0, recv=None, idx=None) == 0      # nothing to add: no launch
     pr = lambda w=P(16), B=3, prev=P(16), k=2, s=P(16): lib.gs_view_priority(w, B, prev, k, s, None)
     assert pr(B=0, w=None, prev=None, s=None) == 0
     assert pr(B=-1) == 1 and pr(k=-1) == 1
@@ -182,6 +203,10 @@ def test_workspace_sizes():
     assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1000, 3) == 3 * 64 * 4
     assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1_000_000, 1024) == 1024 * 31296 * 4
     assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 0, 5) == 0
+    # pack: a count and a 64-bit offset per (block, 512-entry segment)
+    assert gs.gs_workspace_size(gs.GS_OP_PACK, 1_000_000, 8) >= 1954 * 8 * 12
+    with pytest.raises(gs.GSError):
+        gs.gs_workspace_size(gs.GS_OP_PACK, 10, 0)
     with pytest.raises(gs.GSError):
         gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 10, gs.GS_MAX_COUPLED_VIEWS + 1)
     with pytest.raises(gs.GSError):
