@@ -434,6 +434,82 @@ def unpack_grads(grad2d, recv, offsets, idx):
     return g
 
 
+def densify_stats(grad2d, rows, accum, denom):
+    """One view's contribution to the densification statistic (Grendel-GS
+    notes, "training pipeline": densification clones or splits Gaussians
+    whose screen position keeps being pulled, prunes transparent ones): for
+    every listed (visible) row, accum += |dL/d(u, v)| in pixel units and
+    denom += 1.  fp32, one rounding per operation (u*u, v*v, their sum, the
+    square root, the accumulation), since the statistic decides."""
+    g = np.asarray(grad2d, np.float32)
+    r = np.asarray(rows, np.int64)
+    a = np.array(accum, np.float32, copy=True)
+    d = np.array(denom, np.int32, copy=True)
+    gu, gv = g[r, 0], g[r, 1]
+    a[r] = a[r] + np.sqrt(gu * gu + gv * gv)
+    d[r] = d[r] + 1
+    return a, d
+
+
+def _rot(q):
+    """Rotation matrices [n][3][3] of quaternions (w, x, y, z) [4][n], fp64."""
+    q = np.asarray(q, np.float64)
+    q = q / np.linalg.norm(q, axis=0)
+    w, x, y, z = q
+    return np.stack([
+        np.stack([1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y)], -1),
+        np.stack([2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x)], -1),
+        np.stack([2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)], -1)], -2)
+
+
+def densify(params, m, v, accum, denom, grad_threshold, log_scale_threshold, logit_threshold, normals,
+            log_shrink):
+    """Clone / split / prune (Grendel-GS notes, "training pipeline",
+    densification), on the [59][n] parameter planes:
+
+    * g = accum / denom (fp32; 0 where denom = 0); a Gaussian densifies
+      when g >= grad_threshold;
+    * a densifying Gaussian whose largest log-scale is <= log_scale_threshold
+      is cloned (kept, plus an identical copy); a larger one is split: it is
+      replaced by two children at mean + R(q) (exp(log-scale) * z_c) for the
+      caller's standard normals z_c = normals[c, :, i], with log-scales
+      lowered by log_shrink (fp32) and every other parameter copied;
+    * a Gaussian whose opacity logit is not >= logit_threshold is pruned
+      with all its copies.
+
+    Output columns: the kept originals in index order, then the clones, then
+    every split parent's first child, then every second child.  New
+    Gaussians start with zero Adam moments; kept ones keep theirs.  Returns
+    (params, m, v) with the children's means in fp64, the rest copied."""
+    p = np.asarray(params, np.float32)
+    a = np.asarray(accum, np.float32)
+    d = np.asarray(denom, np.int32)
+    g = np.zeros_like(a)
+    nz = d > 0
+    g[nz] = a[nz] / d[nz].astype(np.float32)
+    dense = g >= np.float32(grad_threshold)
+    maxls = p[3:6].max(axis=0)
+    small = maxls <= np.float32(log_scale_threshold)
+    big = maxls > np.float32(log_scale_threshold)
+    low = ~(p[10] >= np.float32(logit_threshold))
+    clone = dense & small & ~low
+    split = dense & big & ~low
+    keep = ~(dense & big) & ~low
+    kids = []
+    for c in range(2):
+        ch = p[:, split].astype(np.float64)
+        s = np.exp(p[3:6, split].astype(np.float64))
+        off = np.einsum("nij,nj->ni", _rot(p[6:10, split]), (s * np.asarray(normals, np.float64)[c][:, split]).T)
+        ch[0:3] = p[0:3, split].astype(np.float64) + off.T
+        ch[3:6] = (p[3:6, split] - np.float32(log_shrink)).astype(np.float64)
+        kids.append(ch)
+    out = np.concatenate([p[:, keep].astype(np.float64), p[:, clone].astype(np.float64)] + kids, axis=1)
+    zeros = np.zeros((p.shape[0], int(clone.sum()) + 2 * int(split.sum())), np.float32)
+    om = np.concatenate([np.asarray(m, np.float32)[:, keep], zeros], axis=1)
+    ov = np.concatenate([np.asarray(v, np.float32)[:, keep], zeros], axis=1)
+    return out, om, ov
+
+
 # ---------------------------------------------------------------------------
 # one whole training step, stage by stage
 # ---------------------------------------------------------------------------

@@ -603,3 +603,74 @@ def test_tile_blocks_of_rect_by_hand():
     # a block lying in the gap between two rows of a rectangle is skipped
     b2 = [0, 3, 5, 12]          # block 1 = tiles 3, 4: (3, 0) and (0, 1)
     assert list(oracle.tile_blocks_of_rect((1, 0, 3, 3), b2, 4)) == [0, 2]
+
+
+# --- densification -----------------------------------------------------------
+
+def test_densify_stats_closed_form():
+    g = np.zeros((4, 12), np.float32)
+    g[1, :2] = (3.0, 4.0)
+    g[2, :2] = (-5.0, 12.0)
+    g[3, :2] = (1e-30, 0.0)       # u*u = 1e-60 underflows to 0 in fp32 (below the denormals)
+    a, d = oracle.densify_stats(g, [1, 2, 3], np.zeros(4, np.float32), np.zeros(4, np.int32))
+    assert list(a) == [0.0, 5.0, 13.0, 0.0] and list(d) == [0, 1, 1, 1]
+    a, d = oracle.densify_stats(g, [1], a, d)
+    assert a[1] == 10.0 and d[1] == 2
+
+
+def _dens_params(n=6):
+    p = np.zeros((59, n), np.float32)
+    p[0] = np.arange(n)                     # means along x
+    p[6] = 1.0                              # identity rotations
+    p[10] = 2.0                             # opaque
+    p[11:] = np.arange(48)[:, None] * 0.01 + np.arange(n)[None, :]
+    return p
+
+
+def test_densify_by_hand():
+    """Six Gaussians: 0 kept (small gradient), 1 cloned (small), 2 split
+    (large), 3 pruned (transparent), 4 never seen (denom 0), 5 split but
+    transparent (pruned with its children)."""
+    p = _dens_params()
+    p[3:6, 1] = -5.0
+    p[3:6, 2] = (0.0, -1.0, -2.0)           # largest log-scale 0 -> scale 1
+    p[3:6, 5] = (0.5, 0.0, 0.0)
+    p[10, 3] = -6.0
+    p[10, 5] = -7.0
+    accum = np.array([0.1, 5.0, 6.0, 9.0, 0.0, 9.0], np.float32)
+    denom = np.array([1, 2, 2, 1, 0, 1], np.int32)
+    m = np.arange(59 * 6, dtype=np.float32).reshape(59, 6)
+    v = m + 1000
+    z = np.zeros((2, 3, 6), np.float32)
+    z[0, :, 2] = (1.0, 0.0, 0.0)
+    z[1, :, 2] = (0.0, 0.0, -2.0)
+    out, om, ov = oracle.densify(p, m, v, accum, denom, 1.0, -3.0, -4.0, z, np.log(1.6))
+    # columns: kept 0, 1, 4; clone of 1; child 0 of 2; child 1 of 2
+    assert out.shape == (59, 6)
+    assert np.array_equal(out[:, 0:3], p[:, [0, 1, 4]])
+    assert np.array_equal(out[:, 3], p[:, 1])
+    c0, c1 = out[:, 4], out[:, 5]
+    assert np.allclose(c0[0:3], (2.0 + 1.0, 0.0, 0.0)) and np.allclose(c1[0:3], (2.0, 0.0, -2.0 * np.exp(-2.0)))
+    assert np.array_equal(c0[3:6].astype(np.float32), p[3:6, 2] - np.float32(np.log(1.6)))
+    assert np.array_equal(c0[6:], p[6:, 2]) and np.array_equal(c1[6:], p[6:, 2])
+    assert np.array_equal(om[:, 0:3], m[:, [0, 1, 4]]) and (om[:, 3:] == 0).all()
+    assert np.array_equal(ov[:, 0:3], v[:, [0, 1, 4]]) and (ov[:, 3:] == 0).all()
+
+
+def test_densify_split_rotates_the_offset():
+    """A quarter turn about z maps the child's x offset onto y; the offset
+    scales with exp(log-scale) per axis before the rotation."""
+    p = _dens_params(1)
+    p[3:6, 0] = (np.log(2.0), np.log(3.0), 0.0)
+    p[6:10, 0] = (np.cos(np.pi / 4), 0.0, 0.0, np.sin(np.pi / 4))
+    z = np.zeros((2, 3, 1), np.float32)
+    z[0, 0, 0] = 1.0
+    z[1, 1, 0] = 1.0
+    out, _, _ = oracle.densify(p, p, p, np.array([1.0], np.float32), np.array([1], np.int32), 0.5, 0.0, -4.0, z,
+                               np.log(1.6))
+    assert np.allclose(out[0:3, 0], (0.0, 2.0, 0.0), atol=1e-6)     # x offset 2 -> +y
+    assert np.allclose(out[0:3, 1], (-3.0, 0.0, 0.0), atol=1e-6)    # y offset 3 -> -x
+    # nothing densifies below the threshold, nothing is pruned above it
+    out, _, _ = oracle.densify(p, p, p, np.array([0.4], np.float32), np.array([1], np.int32), 0.5, 0.0, -4.0, z,
+                               np.log(1.6))
+    assert np.array_equal(out, p.astype(np.float64))
