@@ -247,6 +247,60 @@ def shard_bench(step, work, K=8, calls=20):
     }
 
 
+def densify_bench(step, calls=20):
+    """gs_densify_stats (one view's visible rows) and gs_densify over the
+    step's parameters and Adam state, with seeded statistics whose
+    thresholds clone or split about a fifth of the Gaussians; each call
+    timed with HIP events."""
+    import numpy as np
+    import torch
+
+    import differentiable_gaussian_splatting_dgs_amd as gs
+
+    log("[bench] densification")
+    n, dev = step.n, step.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    grad2d = torch.randn((n, gs.GS_GRAD2D_WORDS), generator=gen, device=dev)
+    accum = torch.zeros(n, dtype=torch.float32, device=dev)
+    denom = torch.zeros(n, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for a, b in ev:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_stats = timed(lambda: gs.gs_densify_stats(grad2d, step.vis_idx[0], step.vis_count[0:1], n, accum, denom))
+    p = step.params[:, :n]
+    g = accum / denom.clamp(min=1).float()
+    thr = float(torch.quantile(g[:1 << 20], 0.8).item())
+    lst = float(torch.quantile(p[3:6, :1 << 20].max(0).values, 0.5).item())
+    lgt = float(torch.quantile(p[10, :1 << 20], 0.05).item())
+    normals = torch.randn((2, 3, n), generator=gen, device=dev)
+    ld_out = 2 * n
+    out = [torch.empty((59, ld_out), dtype=torch.float32, device=dev) for _ in range(3)]
+    out_n = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(gs.gs_workspace_size(gs.GS_OP_DENSIFY, n), dtype=torch.uint8, device=dev)
+    ms_dens = timed(lambda: gs.gs_densify(step.params, step.m, step.v, n, step.ld, accum, denom, normals, thr, lst,
+                                          lgt, float(np.log(1.6)), out[0], out[1], out[2], ld_out, out_n, ws))
+    N = int(out_n.item())
+    dens_bytes = 3 * 236.0 * n + 3 * 236.0 * N + n * 13.0   # planes in and out, statistics and normals of a row
+    return {
+        "workload": f"step parameters and Adam state, {n:,} Gaussians; seeded statistics with thresholds at their "
+                    "80th percentile (gradient), median (largest log-scale) and 5th percentile (opacity logit)",
+        "n_out": N, "ms_per_call": {"stats_one_view": ms_stats, "densify": ms_dens},
+        "densify_roofline": {"bound": "hbm", "achieved": dens_bytes / (ms_dens * 1e-3) / 1e9,
+                             "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                             "frac": dens_bytes / (ms_dens * 1e-3) / HBM_PEAK, "bytes_per_call": dens_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,7 +337,7 @@ def main():
     if args.shard_only:
         step.step()
         torch.cuda.synchronize()
-        print(json.dumps({"shard": shard_bench(step, work)}), flush=True)
+        print(json.dumps({"shard": shard_bench(step, work), "densify": densify_bench(step)}), flush=True)
         return
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -375,6 +429,7 @@ def main():
         log("[bench] oracle cpu baseline")
         out["cpu_baseline"] = cpu_baseline(work)
     out["shard"] = shard_bench(step, work)
+    out["densify"] = densify_bench(step)
     if not args.no_coupling:
         del step
         torch.cuda.empty_cache()

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
 GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM, GS_OP_RASTER = 0, 1, 2, 3, 4
-GS_OP_VIEW_OVERLAP, GS_OP_PACK = 5, 6
+GS_OP_VIEW_OVERLAP, GS_OP_PACK, GS_OP_DENSIFY = 5, 6, 7
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
 GS_MAX_FUSED_VIEWS = 8
@@ -36,7 +36,7 @@ TILE = 16
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
            "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
            "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list", "gs_view_overlap", "gs_view_priority",
-           "gs_tile_partition", "gs_pack_records", "gs_unpack_grads"]
+           "gs_tile_partition", "gs_pack_records", "gs_unpack_grads", "gs_densify_stats", "gs_densify"]
 
 
 class gs_camera(C.Structure):
@@ -85,6 +85,9 @@ def lib():
     L.gs_tile_partition.argtypes = [_P, _i32, _i32, _P, _P]
     L.gs_pack_records.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _i32, _i64, _P, _P, _P, _P, _sz, _P]
     L.gs_unpack_grads.argtypes = [_P, _P, _P, _i32, _i64, _P, _i64, _P]
+    L.gs_densify_stats.argtypes = [_P, _P, _P, _i64, _P, _P, _P]
+    L.gs_densify.argtypes = [_P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _P, _P, _P, _i64, _P, _P,
+                             _sz, _P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = C.c_int
     _handle = L
@@ -274,6 +277,19 @@ def gs_pack_records(proj, n, vis_idx, vis_count, width, height, bounds, num_bloc
 def gs_unpack_grads(recv_grad, send_offsets, send_idx, num_blocks, capacity, grad2d, n, stream=None):
     _check(lib().gs_unpack_grads(_ptr(recv_grad), _ptr(send_offsets), _ptr(send_idx), num_blocks, capacity,
                                  _ptr(grad2d), n, _stream(stream)), "gs_unpack_grads")
+
+
+def gs_densify_stats(grad2d, vis_idx, vis_count, n, accum, denom, stream=None):
+    _check(lib().gs_densify_stats(_ptr(grad2d), _ptr(vis_idx), _ptr(vis_count), n, _ptr(accum), _ptr(denom),
+                                  _stream(stream)), "gs_densify_stats")
+
+
+def gs_densify(params, m, v, n, ld, accum, denom, normals, grad_threshold, log_scale_threshold, logit_threshold,
+               log_shrink, out_params, out_m, out_v, ld_out, out_n, workspace, stream=None):
+    _check(lib().gs_densify(_ptr(params), _ptr(m), _ptr(v), n, ld, _ptr(accum), _ptr(denom), _ptr(normals),
+                            grad_threshold, log_scale_threshold, logit_threshold, log_shrink, _ptr(out_params),
+                            _ptr(out_m), _ptr(out_v), ld_out, _ptr(out_n), _ptr(workspace), _nbytes(workspace),
+                            _stream(stream)), "gs_densify")
 
 
 class ViewCoupling:

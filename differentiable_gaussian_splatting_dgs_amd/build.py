@@ -24,7 +24,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "compact.hip", "preprocess.hip", "binsort.hip", "raster_fwd.hip", "raster_bwd.hip",
-           "loss.hip", "adam.hip", "coupling.hip", "shard.hip"]
+           "loss.hip", "adam.hip", "coupling.hip", "shard.hip", "densify.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

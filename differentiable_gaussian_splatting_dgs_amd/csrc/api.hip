@@ -155,6 +155,10 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
       CHECK(check_size(width, height));
       *bytes = gs::raster_split_bytes(width, height);
       return ok();
+    case GS_OP_DENSIFY:
+      REQUIRE(n >= 0 && n < (int64_t(1) << 30), "n = %lld out of range", (long long)n);
+      *bytes = gs::densify_ws_bytes(n);
+      return ok();
     case GS_OP_PACK:
       REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
       REQUIRE(width >= 1 && width <= GS_MAX_TILE_BLOCKS, "num_blocks = %d out of range", width);
@@ -474,6 +478,38 @@ gs_status gs_unpack_grads(const float* recv_grad, const int64_t* send_offsets, c
   return hip_status(gs::launch_unpack_grads(recv_grad, send_offsets, send_idx, num_blocks, capacity, grad2d, n,
                                             static_cast<hipStream_t>(stream)),
                     "gs_unpack_grads");
+}
+
+gs_status gs_densify_stats(const float* grad2d, const int32_t* vis_idx, const int64_t* vis_count, int64_t n,
+                           float* accum, int32_t* denom, void* stream) {
+  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(vis_count != nullptr && aligned(vis_count, 8), "vis_count NULL or misaligned");
+  if (n == 0) return ok();
+  REQUIRE(grad2d != nullptr && vis_idx != nullptr && accum != nullptr && denom != nullptr, "NULL argument");
+  REQUIRE(aligned(grad2d, 4) && aligned(vis_idx, 4) && aligned(accum, 4) && aligned(denom, 4), "misaligned array");
+  return hip_status(gs::launch_densify_stats(grad2d, vis_idx, vis_count, n, accum, denom,
+                                             static_cast<hipStream_t>(stream)),
+                    "gs_densify_stats");
+}
+
+gs_status gs_densify(const float* params, const float* m, const float* v, int64_t n, int64_t ld,
+                     const float* accum, const int32_t* denom, const float* normals, float grad_threshold,
+                     float log_scale_threshold, float logit_threshold, float log_shrink, float* out_params,
+                     float* out_m, float* out_v, int64_t ld_out, int64_t* out_n, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  REQUIRE(n >= 0 && n < (int64_t(1) << 30), "n = %lld out of range", (long long)n);
+  REQUIRE(ld >= n && ld >= 1, "ld < n");
+  REQUIRE(ld_out >= 0 && ld_out < (int64_t(1) << 31), "ld_out out of range");
+  REQUIRE(out_n != nullptr && aligned(out_n, 8), "out_n NULL or misaligned");
+  if (n > 0)
+    REQUIRE(params && m && v && accum && denom && normals, "NULL params / m / v / accum / denom / normals");
+  if (ld_out > 0) REQUIRE(out_params && out_m && out_v, "NULL out_params / out_m / out_v");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::densify_ws_bytes(n), "workspace too small");
+  return hip_status(gs::launch_densify(params, m, v, n, ld, accum, denom, normals, grad_threshold,
+                                       log_scale_threshold, logit_threshold, log_shrink, out_params, out_m, out_v,
+                                       ld_out, out_n, workspace, static_cast<hipStream_t>(stream)),
+                    "gs_densify");
 }
 
 }  // extern "C"

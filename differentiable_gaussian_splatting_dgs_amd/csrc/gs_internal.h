@@ -128,4 +128,13 @@ hipError_t launch_pack_records(const float* proj, int64_t n, const int32_t* vis_
 hipError_t launch_unpack_grads(const float* recv, const int64_t* send_offsets, const int32_t* send_idx, int32_t K,
                                int64_t capacity, float* grad2d, int64_t n, hipStream_t st);
 
+// --- densification (densify.hip) ----------------------------------------------
+size_t densify_ws_bytes(int64_t n);
+hipError_t launch_densify_stats(const float* grad2d, const int32_t* vis_idx, const int64_t* vis_count, int64_t n,
+                                float* accum, int32_t* denom, hipStream_t st);
+hipError_t launch_densify(const float* params, const float* m, const float* v, int64_t n, int64_t ld,
+                          const float* accum, const int32_t* denom, const float* normals, float grad_threshold,
+                          float log_scale_threshold, float logit_threshold, float log_shrink, float* out_params,
+                          float* out_m, float* out_v, int64_t ld_out, int64_t* out_n, void* ws, hipStream_t st);
+
 }  // namespace gs

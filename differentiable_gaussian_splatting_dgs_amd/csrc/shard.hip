@@ -266,7 +266,8 @@ int64_t segments_of(int64_t n) { return (n + kSegE - 1) / kSegE; }
 }  // namespace
 
 size_t pack_ws_bytes(int64_t n, int32_t num_blocks) {
-  const size_t E = size_t(segments_of(n)) * size_t(std::max(num_blocks, 0));
+  // the launch runs at least one segment
+  const size_t E = size_t(std::max<int64_t>(1, segments_of(n))) * size_t(std::max(num_blocks, 0));
   return align_up(sizeof(uint32_t) * E, 256) + align_up(sizeof(int64_t) * E, 256);
 }
 

@@ -98,7 +98,8 @@ typedef enum gs_op {
   GS_OP_SPARSE_ADAM = 3,
   GS_OP_RASTER = 4,
   GS_OP_VIEW_OVERLAP = 5,
-  GS_OP_PACK = 6
+  GS_OP_PACK = 6,
+  GS_OP_DENSIFY = 7
 } gs_op;
 
 /* Static description of a status code (never NULL). */
@@ -116,6 +117,7 @@ int gs_version(void);
  *   GS_OP_RASTER      width, height: split_ws of gs_render_fwd / gs_render_bwd
  *   GS_OP_VIEW_OVERLAP n, width = num_views
  *   GS_OP_PACK        n, width = num_blocks
+ *   GS_OP_DENSIFY     n
  * Unused arguments are ignored.  The workspace is caller-owned device
  * memory, 256-byte aligned; its contents need no initialisation and are
  * scratch between calls. */
@@ -447,6 +449,57 @@ gs_status gs_pack_records(const float* proj, int64_t n, const int32_t* vis_idx, 
  * misaligned buffer. */
 gs_status gs_unpack_grads(const float* recv_grad, const int64_t* send_offsets, const int32_t* send_idx,
                           int32_t num_blocks, int64_t capacity, float* grad2d, int64_t n, void* stream);
+
+/* One view's contribution to the densification statistic (Grendel-GS
+ * notes, "training pipeline": densification clones or splits the Gaussians
+ * whose screen position keeps being pulled and prunes transparent ones).
+ * For every visible row i: accum[i] += |dL/d(u, v)| (pixel units, from
+ * grad2d words 0 and 1; fp32 with one rounding per operation: u*u, v*v,
+ * their sum, the square root, the accumulation) and denom[i] += 1.  Call
+ * it after gs_render_bwd for each view whose gradients are still in grad2d.
+ *   grad2d       device, [n][GS_GRAD2D_WORDS] fp32
+ *   vis_idx, vis_count  device, the view's visible list (gs_preprocess)
+ *   accum, denom device in/out, [n] fp32 / int32; the caller zeroes them
+ *                when a densification interval starts
+ * Errors: GS_ERR_INVALID_ARG for n out of range or a NULL buffer. */
+gs_status gs_densify_stats(const float* grad2d, const int32_t* vis_idx, const int64_t* vis_count, int64_t n,
+                           float* accum, int32_t* denom, void* stream);
+
+/* Clone / split / prune (the same page and line), into new parameter and
+ * Adam buffers:
+ *   g = accum / denom (fp32; 0 where denom is 0).  A Gaussian with
+ *   g >= grad_threshold densifies: if its largest log-scale is
+ *   <= log_scale_threshold it is kept and cloned (an identical copy), else
+ *   it is replaced by two children at mean + R(q) (exp(log-scale) * z_c),
+ *   z_c = (normals[c][0][i], normals[c][1][i], normals[c][2][i]), with
+ *   log-scales lowered by log_shrink and every other parameter copied.  A
+ *   Gaussian whose opacity logit is not >= logit_threshold is dropped with
+ *   all its copies.
+ *   Output columns: the kept originals in index order, then the clones,
+ *   then every split Gaussian's first child, then every second child (each
+ *   group in index order).  Kept columns keep their Adam moments, new ones
+ *   start from 0.
+ *   params, m, v   device, [59][ld] fp32 (ld >= n)
+ *   accum, denom   device, [n] (gs_densify_stats)
+ *   normals        device, [2][3][n] fp32 standard normals (the caller's
+ *                  random draws; read only for split Gaussians)
+ *   thresholds     grad_threshold (pixel units, as accum),
+ *                  log_scale_threshold = log(percent_dense * extent),
+ *                  logit_threshold = logit(min_opacity),
+ *                  log_shrink = log(0.8 * 2)
+ *   out_params, out_m, out_v  device out, [59][ld_out] fp32; columns at or
+ *                  past ld_out are not written
+ *   out_n          device out, int64: the new count (may exceed ld_out:
+ *                  call again with ld_out >= it; at most 2n)
+ *   workspace      device, >= gs_workspace_size(GS_OP_DENSIFY, n) bytes,
+ *                  256-byte aligned
+ * Errors: GS_ERR_INVALID_ARG for sizes out of range, ld < n, or a NULL
+ * buffer. */
+gs_status gs_densify(const float* params, const float* m, const float* v, int64_t n, int64_t ld,
+                     const float* accum, const int32_t* denom, const float* normals, float grad_threshold,
+                     float log_scale_threshold, float logit_threshold, float log_shrink, float* out_params,
+                     float* out_m, float* out_v, int64_t ld_out, int64_t* out_n, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

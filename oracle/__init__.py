@@ -446,7 +446,8 @@ def densify_stats(grad2d, rows, accum, denom):
     a = np.array(accum, np.float32, copy=True)
     d = np.array(denom, np.int32, copy=True)
     gu, gv = g[r, 0], g[r, 1]
-    a[r] = a[r] + np.sqrt(gu * gu + gv * gv)
+    with np.errstate(over="ignore"):      # a huge gradient overflows to +inf, as in fp32 anywhere
+        a[r] = a[r] + np.sqrt(gu * gu + gv * gv)
     d[r] = d[r] + 1
     return a, d
 

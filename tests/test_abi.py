@@ -22,6 +22,7 @@ def test_header_declares_the_entry_points():
     for n in ["gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
               "gs_sparse_adam", "gs_bin_sort_async", "gs_project_bwd_adam", "gs_visible_list",
               "gs_view_overlap", "gs_view_priority", "gs_tile_partition", "gs_pack_records", "gs_unpack_grads",
+              "gs_densify_stats", "gs_densify",
               "gs_workspace_size", "gs_status_string", "gs_last_error", "gs_version"]:
         assert n in names
 
@@ -180,6 +181,17 @@ def test_invalid_arguments_rejected_on_host():
     assert up(K=0) == 1 and up(cap=-1) == 1 and up(n=-1) == 1
     assert up(recv=P(20)) == 1 and up(g=P(20)) == 1 and up(offs=None) == 1 and up(idx=None) == 1
     assert up(cap=0, recv=None, idx=None) == 0      # nothing to add: no launch
+    # densification: sizes, ld, NULL buffers, small workspace
+    ds = lambda g=P(16), vi=P(16), vc=P(16), n=100, a=P(16), d=P(16): lib.gs_densify_stats(g, vi, vc, n, a, d, None)
+    assert ds(n=-1) == 1 and ds(vc=None) == 1 and ds(vc=P(20)) == 1 and ds(a=None) == 1 and ds(g=P(18)) == 1
+    assert ds(n=0, g=None, vi=None, a=None, d=None) == 0
+    dws = gs.gs_workspace_size(gs.GS_OP_DENSIFY, 100)
+    dn = lambda n=100, ld=100, z=P(16), ldo=200, on=P(16), o=P(16), wsp=P(256), wsb=dws: lib.gs_densify(
+        P(16), P(16), P(16), n, ld, P(16), P(16), z, 1.0, 0.0, -4.0, 0.47, o, o, o, ldo, on, wsp, wsb, None)
+    assert dn(n=-1) == 1 and dn(ld=99) == 1 and dn(ldo=-1) == 1 and dn(on=None) == 1 and dn(on=P(20)) == 1
+    assert dn(z=None) == 1 and dn(o=None) == 1
+    assert dn(wsb=dws - 1) == 1
+    assert b"workspace" in lib.gs_last_error()
     pr = lambda w=P(16), B=3, prev=P(16), k=2, s=P(16): lib.gs_view_priority(w, B, prev, k, s, None)
     assert pr(B=0, w=None, prev=None, s=None) == 0
     assert pr(B=-1) == 1 and pr(k=-1) == 1
