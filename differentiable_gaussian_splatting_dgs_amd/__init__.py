@@ -292,6 +292,18 @@ def gs_densify(params, m, v, n, ld, accum, denom, normals, grad_threshold, log_s
                             _stream(stream)), "gs_densify")
 
 
+def auto_segment_len(width: int, height: int) -> int:
+    """Segment length of the split raster backward for a width x height
+    view, from its count of 8x8 quarter-tiles (one wave each): splitting
+    pays while the few longest lists set the raster time and the rest of
+    the chip has run dry; measured on MI355X, 256 is best near 17k
+    quarters (1297x840), 512 near 33k (1920x1080), and with 130k (3840x2160)
+    the chip stays full to the end and the split only adds the records'
+    traffic (0: unsplit)."""
+    q = ((width + TILE - 1) // TILE) * ((height + TILE - 1) // TILE) * 4
+    return 256 if q < 24_000 else (512 if q < 64_000 else 0)
+
+
 class ViewCoupling:
     """Visible lists of a set of views over one scene and their coupling
     graph (gs_preprocess per view into row v of ``lists``, then
@@ -393,7 +405,7 @@ class TrainStep:
     one view's stages in order on the current stream."""
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
-                 pair_capacity=None, record_tiles=False, segment_len=SEGMENT_LEN, fuse_next_preprocess=True):
+                 pair_capacity=None, record_tiles=False, segment_len="auto", fuse_next_preprocess=True):
         p = torch.as_tensor(params, dtype=torch.float32)
         assert p.ndim == 2 and p.shape[0] == 59
         self.device = torch.device(device)
@@ -451,9 +463,13 @@ class TrainStep:
         # the forward's checkpoints and segment list, read by the split raster
         # backward of the same view (both on the current stream, the view's
         # backward before the next view's forward); segment_len None: unsplit
-        self.segment_len = segment_len or 0
-        self.split_ws = (_bytes(max(gs_workspace_size(GS_OP_RASTER, 0, v.W, v.H) for v in self.views), self.device)
-                         if segment_len else None)
+        if segment_len == "auto":
+            self.seg = [auto_segment_len(v.W, v.H) for v in self.views]
+        else:
+            self.seg = [int(segment_len or 0)] * len(self.views)
+        split_views = [v for v, sg in zip(self.views, self.seg) if sg]
+        self.split_ws = (_bytes(max(gs_workspace_size(GS_OP_RASTER, 0, v.W, v.H) for v in split_views), self.device)
+                         if split_views else None)
 
     # the buffer set of the view last prepared (what tests read back)
     @property
@@ -541,8 +557,8 @@ class TrainStep:
         ps = self.sets[k % self.nsets]
         with self._stage("render_fwd"):
             gs_render_fwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.image, vw.T_final,
-                          vw.last, vw.tile_processed if self.record_tiles else None, vw.order, self.split_ws,
-                          self.segment_len)
+                          vw.last, vw.tile_processed if self.record_tiles else None, vw.order,
+                          self.split_ws if self.seg[k] else None, self.seg[k])
         with self._stage("loss"):
             gs_loss(vw.image, vw.target, vw.W, vw.H, self.w_l1, self.w_ssim, vw.loss, vw.dL, self.ws_loss)
 
@@ -557,7 +573,8 @@ class TrainStep:
         self._gcur = self._gbuf(k)
         with self._stage("render_bwd"):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
-                          vw.dL, self.g2d[self._gcur], vw.order, self.split_ws, self.segment_len)
+                          vw.dL, self.g2d[self._gcur], vw.order, self.split_ws if self.seg[k] else None,
+                          self.seg[k])
         if not keep_grad2d:
             self.project_view(k)
 

@@ -200,6 +200,14 @@ def test_invalid_arguments_rejected_on_host():
     assert b"prev" in lib.gs_last_error()
 
 
+def test_auto_segment_length():
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    assert gs.auto_segment_len(128, 128) == 256          # 256 quarters
+    assert gs.auto_segment_len(1297, 840) == 256         # 17,384
+    assert gs.auto_segment_len(1920, 1080) == 512        # 32,640
+    assert gs.auto_segment_len(3840, 2160) == 0          # 129,600: unsplit
+
+
 def test_workspace_sizes():
     import differentiable_gaussian_splatting_dgs_amd as gs
     a = gs.gs_workspace_size(gs.GS_OP_BIN_SORT, 1000, 0, 0, 10000)
