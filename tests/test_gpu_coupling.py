@@ -143,3 +143,22 @@ def test_priority_matches_oracle():
     s = gpu_priority(ow, [-1, 2, B, 7])
     assert np.array_equal(s, oracle.view_priority(ow, [2, 7]))
     say("[coupling priority] bit-exact")
+
+
+def test_overlap_many_views_sampled():
+    """4,096 views (64 tiles of 64 views a side, 2,080 tiles on or above the
+    diagonal): 3,000 sampled pairs against the oracle on just those two
+    lists, the diagonal against the list lengths, symmetry."""
+    rng = np.random.default_rng(4096)
+    n, B = 3001, 4096
+    lists = synth.random_visible_lists(rng, n, B)
+    inter, w = gpu_overlap(lists, n)
+    assert np.array_equal(inter, inter.T)
+    assert np.array_equal(np.diag(inter), [l.size for l in lists])
+    pairs = rng.integers(0, B, (3000, 2))
+    for i, j in pairs:
+        oi = oracle.view_overlap([lists[i], lists[j]])
+        ow = oracle.view_coupling(oi)
+        assert inter[i, j] == oi[0, 1], (i, j)
+        assert w[i, j].view(np.uint64) == ow[0, 1].view(np.uint64), (i, j)
+    say(f"[coupling B={B}] 3000 sampled pairs exact")

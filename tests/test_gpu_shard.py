@@ -33,7 +33,7 @@ def gpu_partition(cost, K):
 
 
 @pytest.mark.parametrize("T,K", [(1, 1), (117, 1), (117, 3), (117, 8), (117, 64), (8160, 8), (32400, 64),
-                                 (50, 64)])
+                                 (50, 64), (100_003, 64)])
 def test_partition_matches_oracle(T, K):
     rng = np.random.default_rng(T * 100 + K)
     for kind in ("random", "sky", "zero", "one"):
@@ -48,7 +48,7 @@ def test_partition_matches_oracle(T, K):
             cost[T // 2] = 12345
         b = gpu_partition(cost, K)
         assert np.array_equal(b, oracle.tile_partition(cost, K)), (kind, T, K)
-    # the largest costs: 2^21 tiles of 2^32 - 1 each
+    # the largest costs: tiles of 2^32 - 1 each
     if T == 32400:
         cost = np.full(T, 0xFFFFFFFF, np.uint64)
         cost[:100] = 0
@@ -177,23 +177,23 @@ def test_pack_full_size_mid_view():
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     ws = torch.empty(gs.gs_workspace_size(gs.GS_OP_PREPROCESS, w.n), dtype=torch.uint8, device="cuda")
     gs.gs_preprocess(dp, w.n, w.n, cam, proj, vis, cnt, None, ws)
-    K = 8
     cost = (ranges[:, 1] - ranges[:, 0]).astype(np.int64)
-    ob = oracle.tile_partition(cost, K)
-    assert np.array_equal(gpu_partition(cost, K), ob)
-    # the pairs are grouped by tile in tile order (an empty tile's range is
-    # [0, 0)): block d's pairs are those of tiles [ob[d], ob[d + 1])
     pair_tile = np.repeat(np.arange(TX * TY), cost)
-    cut = np.searchsorted(pair_tile, ob)
-    expect = [np.unique(vals[cut[d]:cut[d + 1]]) for d in range(K)]
-    total = sum(e.size for e in expect)
-    offs, idx, rec = gpu_pack(w, cam, proj, vis, cnt, ob, K, total)
-    go, gi = offs.cpu().numpy(), idx.cpu().numpy()
-    assert go[-1] == total
-    for d in range(K):
-        assert np.array_equal(gi[go[d]:go[d + 1]], expect[d]), d
-    pf = proj_fields(rec.cpu().numpy())
-    assert np.array_equal(pf["rect"], pre["rect"][gi])
+    for K in (64, 8):
+        ob = oracle.tile_partition(cost, K)
+        assert np.array_equal(gpu_partition(cost, K), ob)
+        # the pairs are grouped by tile in tile order (an empty tile's range
+        # is [0, 0)): block d's pairs are those of tiles [ob[d], ob[d + 1])
+        cut = np.searchsorted(pair_tile, ob)
+        expect = [np.unique(vals[cut[d]:cut[d + 1]]) for d in range(K)]
+        total = sum(e.size for e in expect)
+        offs, idx, rec = gpu_pack(w, cam, proj, vis, cnt, ob, K, total)
+        go, gi = offs.cpu().numpy(), idx.cpu().numpy()
+        assert go[-1] == total
+        for d in range(K):
+            assert np.array_equal(gi[go[d]:go[d + 1]], expect[d]), (K, d)
+        pf = proj_fields(rec.cpu().numpy())
+        assert np.array_equal(pf["rect"], pre["rect"][gi])
     rng = np.random.default_rng(2)
     recv = rng.standard_normal((total, 12)).astype(np.float32)
     g0 = np.zeros((w.n, 12), np.float32)
