@@ -102,8 +102,10 @@ __global__ __launch_bounds__(256) void k_bitmap(const int32_t* __restrict__ list
     // staged position of entry r0 - 1 + k is 33 lane + k + (k >> 5) for k < 64
     const int32_t* const mine = buf + 33 * lane;
     const int jend = int(std::max<int64_t>(0, std::min<int64_t>(2 * kSlice, count - r0)));
+    // 0 <= g < n as one unsigned compare (n < 2^31)
+    const uint32_t un = uint32_t(n);
     const int32_t gp = mine[0];
-    const int32_t wprev = gp >= 0 && int64_t(gp) < n ? gp >> 5 : -1;
+    const int32_t wprev = uint32_t(gp) < un ? gp >> 5 : -1;
     int32_t wcur = -1;
     uint32_t bits = 0;
     bool cont = true;   // the open word may go on past the entries read so far
@@ -118,11 +120,13 @@ __global__ __launch_bounds__(256) void k_bitmap(const int32_t* __restrict__ list
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int j = j0 + q;
-        const bool valid = j < jend && g[q] >= 0 && int64_t(g[q]) < n;
+        // (bitwise &: every operand is already computed, a branch per
+        // condition would cost more than the operation)
+        const bool valid = (j < jend) & (uint32_t(g[q]) < un);
         const int32_t w = valid ? g[q] >> 5 : -2;
         // past the slice only the open word's entries count
-        const bool take = valid && w != wprev && (j < kSlice || w == wcur);
-        const bool fresh = take && w != wcur;
+        const bool take = valid & (w != wprev) & ((j < kSlice) | (w == wcur));
+        const bool fresh = take & (w != wcur);
         if (fresh && wcur >= 0) row[wcur] = bits;
         bits = fresh ? 0u : bits;
         wcur = fresh ? w : wcur;
