@@ -64,6 +64,7 @@ def lib():
         L.or_sh_basis_f32.argtypes = [P, i64, P]
         L.or_preprocess.argtypes = [P, i64, i64, P] + [P] * 11
         L.or_preprocess_f64.argtypes = [P, i64, i64, P] + [P] * 6
+        L.or_projection_internals_f64.argtypes = [P, i64, i64, P, P, P, P]
         L.or_bin.restype = i64
         L.or_bin.argtypes = [P, i64, i64, P, P, P, i64, P]
         L.or_render.argtypes = [P, i64, i64, P, P, P, P, P]
@@ -160,6 +161,20 @@ def preprocess_f64(params64, cam):
     lib().or_preprocess_f64(_p(p), n, n, C.byref(c), *[_p(out[k]) for k in (
         "mean2d", "depth", "cov2d", "conic", "opacity", "rgb")])
     return out
+
+
+def projection_internals_f64(params64, cam):
+    """fp64 intermediates of the projection: the normalised quaternion's
+    rotation R_q [n][3][3], the world covariance Sigma [n][3][3] and the
+    screen covariance before the 0.3 dilation [n][3] (a, b, c)."""
+    p = np.ascontiguousarray(params64, np.float64)
+    n = p.shape[1]
+    Rq = np.empty((n, 3, 3))
+    Sig = np.empty((n, 3, 3))
+    cov = np.empty((n, 3))
+    c = cam_struct(cam)
+    lib().or_projection_internals_f64(_p(p), n, n, C.byref(c), _p(Rq), _p(Sig), _p(cov))
+    return Rq, Sig, cov
 
 
 def visible_list(params, cam):

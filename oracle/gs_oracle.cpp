@@ -746,6 +746,27 @@ void or_preprocess_f64(const double* params, int64_t n, int64_t ld, const or_cam
   }
 }
 
+// The projection's intermediates in fp64 for the covariance pins: the
+// rotation of the normalised quaternion R_q [n][9] (row-major), the world
+// covariance Sigma = R_q S^2 R_q^T [n][9] (full, row-major) and the screen
+// covariance before the 0.3 dilation [n][3] (a, b, c).
+void or_projection_internals_f64(const double* params, int64_t n, int64_t ld, const or_camera* cam, double* Rq,
+                                 double* Sigma, double* cov2d_raw) {
+  for (int64_t i = 0; i < n; ++i) {
+    double p[59];
+    for (int k = 0; k < 59; ++k) p[k] = params[k * ld + i];
+    Proj<double> o;
+    project_one<double>(p, *cam, o);
+    for (int k = 0; k < 9; ++k) Rq[9 * i + k] = o.R[k];
+    const double* S = o.S;   // 00 01 02 11 12 22
+    const double full[9] = {S[0], S[1], S[2], S[1], S[3], S[4], S[2], S[4], S[5]};
+    for (int k = 0; k < 9; ++k) Sigma[9 * i + k] = full[k];
+    cov2d_raw[3 * i] = o.a - 0.3;
+    cov2d_raw[3 * i + 1] = o.b;
+    cov2d_raw[3 * i + 2] = o.c - 0.3;
+  }
+}
+
 // Gaussian-tile pairs sorted by (tile, depth bits, index): keys
 // (tile << 32 | depth bits), values = Gaussian index, ranges [T][2].
 // Returns M; writes at most `cap` pairs (pass cap = 0 to count only).
@@ -1080,81 +1101,90 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
   tile_lists(g, TX, TY, lists);
   const size_t P = size_t(W) * H;
   const int64_t T = int64_t(TX) * TY;
-  // per tile: partial sums per list position (value 9 + magnitude 9)
-  std::vector<std::vector<double>> part(T);
-#pragma omp parallel for schedule(dynamic, 4)
-  for (int64_t t = 0; t < T; ++t) {
-    const int tx = int(t % TX), ty = int(t / TX);
-    const std::vector<int32_t>& L = lists[t];
-    std::vector<double>& acc = part[t];
-    acc.assign(L.size() * 18, 0.0);
-    PixelTrace tr;
-    std::vector<double> al, Ti;
-    for (int py = ty * kTile; py < std::min(H, (ty + 1) * kTile); ++py)
-      for (int px = tx * kTile; px < std::min(W, (tx + 1) * kTile); ++px) {
-        trace_pixel(g, L.data(), int64_t(L.size()), px, py, tr);
-        const size_t pix = size_t(py) * W + px;
-        const double G[3] = {dL_dimage[pix], dL_dimage[P + pix], dL_dimage[2 * P + pix]};
-        // magnitude of the image gradient used by the bound: |G|, or the
-        // caller's map (e.g. a tolerance on G, to propagate it)
-        const double Gm[3] = {gmag ? gmag[pix] : std::fabs(G[0]), gmag ? gmag[P + pix] : std::fabs(G[1]),
-                              gmag ? gmag[2 * P + pix] : std::fabs(G[2])};
-        const double pxc = px + 0.5, pyc = py + 0.5;
-        const size_t K = tr.pos.size();
-        al.assign(K, 0.0);
-        Ti.assign(K, 0.0);
-        double Tc = 1.0;
-        for (size_t k = 0; k < K; ++k) {
-          const Proj<double>& q = h[L[tr.pos[k]]];
-          const double dx = pxc - q.u, dy = pyc - q.v;
-          const double power = -0.5 * (q.A * dx * dx + q.C * dy * dy) - q.B * dx * dy;
-          al[k] = tr.clamped[k] ? 0.99 : q.opacity * std::exp(power);
-          Ti[k] = Tc;
-          Tc *= (1.0 - al[k]);
-        }
-        double S[3] = {0, 0, 0};
-        for (size_t kk = K; kk-- > 0;) {
-          const int32_t pos = tr.pos[kk];
-          const Proj<double>& q = h[L[pos]];
-          const double a = al[kk], Tk = Ti[kk];
-          double* o = &acc[size_t(pos) * 18];
-          double dalpha = 0.0, malpha = 0.0;
-          for (int c = 0; c < 3; ++c) {
-            o[6 + c] += a * Tk * G[c];
-            o[9 + 6 + c] += a * Tk * Gm[c];
-            dalpha += Tk * (q.rgb[c] - S[c]) * G[c];
-            malpha += Tk * (std::fabs(q.rgb[c]) + std::fabs(S[c])) * Gm[c];
-          }
-          for (int c = 0; c < 3; ++c) S[c] = a * q.rgb[c] + (1.0 - a) * S[c];
-          if (tr.clamped[kk]) continue;
-          const double dx = pxc - q.u, dy = pyc - q.v;
-          const double e = a / q.opacity;  // exp(power)
-          const double dpow = dalpha * a, mpow = malpha * a;
-          o[5] += dalpha * e;
-          o[9 + 5] += malpha * e;
-          o[2] += dpow * (-0.5 * dx * dx);
-          o[9 + 2] += mpow * (0.5 * dx * dx);
-          o[3] += dpow * (-dx * dy);
-          o[9 + 3] += mpow * std::fabs(dx * dy);
-          o[4] += dpow * (-0.5 * dy * dy);
-          o[9 + 4] += mpow * (0.5 * dy * dy);
-          o[0] += dpow * (q.A * dx + q.B * dy);
-          o[9 + 0] += mpow * (std::fabs(q.A * dx) + std::fabs(q.B * dy));
-          o[1] += dpow * (q.B * dx + q.C * dy);
-          o[9 + 1] += mpow * (std::fabs(q.B * dx) + std::fabs(q.C * dy));
-        }
-      }
-  }
+  // per tile: partial sums per list position (value 9 + magnitude 9),
+  // formed for a band of tile rows at a time (in parallel over its tiles)
+  // and merged into the per-Gaussian sums in ascending tile order, so the
+  // result is that of one pass over all tiles in tile order, for any band
+  // height and thread count, with the partials of one band held at a time
   std::memset(g2d, 0, sizeof(double) * 9 * size_t(n));
   std::memset(m2d, 0, sizeof(double) * 9 * size_t(n));
-  for (int64_t t = 0; t < T; ++t) {
-    const std::vector<int32_t>& L = lists[t];
-    for (size_t j = 0; j < L.size(); ++j) {
-      const double* o = &part[t][j * 18];
-      for (int c = 0; c < 9; ++c) {
-        g2d[size_t(L[j]) * 9 + c] += o[c];
-        m2d[size_t(L[j]) * 9 + c] += o[9 + c];
+  const int band = std::max(1, (1024 + TX - 1) / TX);
+  std::vector<std::vector<double>> part(size_t(band) * TX);
+  for (int ty0 = 0; ty0 < TY; ty0 += band) {
+    const int64_t t_lo = int64_t(ty0) * TX, t_hi = std::min<int64_t>(T, int64_t(ty0 + band) * TX);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = t_lo; t < t_hi; ++t) {
+      const int tx = int(t % TX), ty = int(t / TX);
+      const std::vector<int32_t>& L = lists[t];
+      std::vector<double>& acc = part[t - t_lo];
+      acc.assign(L.size() * 18, 0.0);
+      PixelTrace tr;
+      std::vector<double> al, Ti;
+      for (int py = ty * kTile; py < std::min(H, (ty + 1) * kTile); ++py)
+        for (int px = tx * kTile; px < std::min(W, (tx + 1) * kTile); ++px) {
+          trace_pixel(g, L.data(), int64_t(L.size()), px, py, tr);
+          const size_t pix = size_t(py) * W + px;
+          const double G[3] = {dL_dimage[pix], dL_dimage[P + pix], dL_dimage[2 * P + pix]};
+          // magnitude of the image gradient used by the bound: |G|, or the
+          // caller's map (e.g. a tolerance on G, to propagate it)
+          const double Gm[3] = {gmag ? gmag[pix] : std::fabs(G[0]), gmag ? gmag[P + pix] : std::fabs(G[1]),
+                                gmag ? gmag[2 * P + pix] : std::fabs(G[2])};
+          const double pxc = px + 0.5, pyc = py + 0.5;
+          const size_t K = tr.pos.size();
+          al.assign(K, 0.0);
+          Ti.assign(K, 0.0);
+          double Tc = 1.0;
+          for (size_t k = 0; k < K; ++k) {
+            const Proj<double>& q = h[L[tr.pos[k]]];
+            const double dx = pxc - q.u, dy = pyc - q.v;
+            const double power = -0.5 * (q.A * dx * dx + q.C * dy * dy) - q.B * dx * dy;
+            al[k] = tr.clamped[k] ? 0.99 : q.opacity * std::exp(power);
+            Ti[k] = Tc;
+            Tc *= (1.0 - al[k]);
+          }
+          double S[3] = {0, 0, 0};
+          for (size_t kk = K; kk-- > 0;) {
+            const int32_t pos = tr.pos[kk];
+            const Proj<double>& q = h[L[pos]];
+            const double a = al[kk], Tk = Ti[kk];
+            double* o = &acc[size_t(pos) * 18];
+            double dalpha = 0.0, malpha = 0.0;
+            for (int c = 0; c < 3; ++c) {
+              o[6 + c] += a * Tk * G[c];
+              o[9 + 6 + c] += a * Tk * Gm[c];
+              dalpha += Tk * (q.rgb[c] - S[c]) * G[c];
+              malpha += Tk * (std::fabs(q.rgb[c]) + std::fabs(S[c])) * Gm[c];
+            }
+            for (int c = 0; c < 3; ++c) S[c] = a * q.rgb[c] + (1.0 - a) * S[c];
+            if (tr.clamped[kk]) continue;
+            const double dx = pxc - q.u, dy = pyc - q.v;
+            const double e = a / q.opacity;  // exp(power)
+            const double dpow = dalpha * a, mpow = malpha * a;
+            o[5] += dalpha * e;
+            o[9 + 5] += malpha * e;
+            o[2] += dpow * (-0.5 * dx * dx);
+            o[9 + 2] += mpow * (0.5 * dx * dx);
+            o[3] += dpow * (-dx * dy);
+            o[9 + 3] += mpow * std::fabs(dx * dy);
+            o[4] += dpow * (-0.5 * dy * dy);
+            o[9 + 4] += mpow * (0.5 * dy * dy);
+            o[0] += dpow * (q.A * dx + q.B * dy);
+            o[9 + 0] += mpow * (std::fabs(q.A * dx) + std::fabs(q.B * dy));
+            o[1] += dpow * (q.B * dx + q.C * dy);
+            o[9 + 1] += mpow * (std::fabs(q.B * dx) + std::fabs(q.C * dy));
+          }
+        }
+    }
+    for (int64_t t = t_lo; t < t_hi; ++t) {
+      const std::vector<int32_t>& L = lists[t];
+      for (size_t j = 0; j < L.size(); ++j) {
+        const double* o = &part[t - t_lo][j * 18];
+        for (int c = 0; c < 9; ++c) {
+          g2d[size_t(L[j]) * 9 + c] += o[c];
+          m2d[size_t(L[j]) * 9 + c] += o[9 + c];
+        }
       }
+      std::vector<double>().swap(part[t - t_lo]);
     }
   }
 #pragma omp parallel for schedule(static)
