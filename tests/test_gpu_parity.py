@@ -275,7 +275,8 @@ def split_pool_counts(step, vw):
     return c[:, 0].astype(np.int64), pool_slots
 
 
-@pytest.mark.parametrize("case,seg", [("small_cut", 64), ("mid_cut", 64), ("mid_cut", 256), ("small_full", 64)])
+@pytest.mark.parametrize("case,seg", [("small_cut", 64), ("mid_cut", 64), ("mid_cut", 256), ("small_full", 64),
+                                      ("small_full", 512)])
 def test_split_backward_matches_whole_list_backward(case, seg):
     """The raster backward with long lists walked in segments (helper waves
     starting from the forward's recorded states) against the oracle and
@@ -283,7 +284,8 @@ def test_split_backward_matches_whole_list_backward(case, seg):
     gradient; short segments so that many quarters of these workloads are
     split several times, and on the whole small workload so many that some
     pools run out of states (those quarters keep the rest of their list
-    whole)."""
+    whole); and the whole small workload at the 512-entry segments the
+    training step uses for 1080p views (its longest lists span three)."""
     work = workload_case(case)
     ref = oracle.step(work)
     dl = [vw["dL_dimage"] for vw in ref["views"]]
@@ -301,7 +303,7 @@ def test_split_backward_matches_whole_list_backward(case, seg):
     say(f"  {case}: longest composited prefix {longest} (segments of {seg}); states requested per pool "
         f"max {requested.max()} of {pool_slots}, total {requested.sum()}")
     assert longest > 3 * seg, "no quarter spans several segments"
-    if case == "small_full":
+    if case == "small_full" and seg == 64:
         assert requested.max() > pool_slots, "no pool ran out of states"
 
 
