@@ -76,6 +76,8 @@ def lib():
         L.or_loss_frozen_f64.restype = f64
         L.or_loss_frozen_f64.argtypes = [P, P, P, i32, i32, f64, f64]
         L.or_backward.argtypes = [P, i64, i64, P, P, P, P, P, P, P, i32]
+        L.or_train_view.restype = f64
+        L.or_train_view.argtypes = [P, i64, i64, P, P, f64, f64, P, P]
         L.or_project_backward.argtypes = [P, i64, i64, P, P, P]
         L.or_project_outputs_f64.argtypes = [P, P, i64, i64, P, P]
         L.or_adam.argtypes = [P, P, P, P, i64, P, i64, f64, f64, f64, f64, f64, f64]
@@ -299,6 +301,22 @@ def backward(params, cam, dL_dimage, grads=None, mags=None, at_fp32=False, gmag=
     lib().or_backward(_p(p), n, n, C.byref(c), _p(dL), None if gm is None else _p(gm), _p(g2d), _p(m2d),
                       _p(grads), _p(mags), int(at_fp32))
     return g2d, m2d, grads, mags
+
+
+def train_view(params, cam, target, w_l1, w_ssim, grads=None):
+    """One view of the step projecting once and without magnitudes (the
+    plain step the CPU baseline times): returns (loss, image [3][H][W] f32,
+    grads [59][n] f64 with this view's gradients added)."""
+    p = _params(params)
+    n = p.shape[1]
+    t = np.ascontiguousarray(target, np.float32)
+    img = np.empty((3, cam.height, cam.width), np.float32)
+    if grads is None:
+        grads = np.zeros((59, n))
+    assert grads.dtype == np.float64 and grads.flags.c_contiguous and grads.shape == (59, n)
+    c = cam_struct(cam)
+    L = lib().or_train_view(_p(p), n, n, C.byref(c), _p(t), float(w_l1), float(w_ssim), _p(img), _p(grads))
+    return L, img, grads
 
 
 def project_backward(params, cam, g2d):

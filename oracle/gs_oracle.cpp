@@ -1073,32 +1073,29 @@ double or_loss_frozen_f64(const double* image, const float* image32, const float
 // Per-tile partial sums are merged in tile order, so the result does not
 // depend on the thread count.
 // ---------------------------------------------------------------------------
-void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* cam,
-                 const double* dL_dimage, const double* gmag, double* g2d, double* m2d, double* grads,
-                 double* mags, int at_fp32) {
-  std::vector<Proj<float>> g;
-  project_all(params, n, ld, *cam, g);
+// The backward given the fp32 projections `g` and the per-tile lists; with
+// want_mags false the magnitudes (m2d, mags) are neither formed nor written.
+static void backward_impl(const float* params, int64_t n, int64_t ld, const or_camera* cam,
+                          const std::vector<Proj<float>>& g, const std::vector<std::vector<int32_t>>& lists,
+                          const double* dL_dimage, const double* gmag, double* g2d, double* m2d, double* grads,
+                          double* mags, int at_fp32, bool want_mags) {
   std::vector<Proj<double>> h(n);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
+    if (at_fp32) {
+      // evaluate the raster backward at the fp32 forward's screen-space
+      // values (what the rendered image was computed from)
+      h[i] = widen(g[i]);
+      continue;
+    }
     double p[59];
     load_params<double>(params, ld, i, p);
     project_one<double>(p, *cam, h[i]);
     // frozen colour clamp: the raw value passes where the fp32 run said > 0
     for (int c = 0; c < 3; ++c) h[i].rgb[c] = g[i].rgb_pos[c] ? h[i].rgb_raw[c] : 0.0;
-    if (at_fp32) {
-      // evaluate the raster backward at the fp32 forward's screen-space
-      // values (what the rendered image was computed from)
-      h[i].u = g[i].u; h[i].v = g[i].v;
-      h[i].A = g[i].A; h[i].B = g[i].B; h[i].C = g[i].C;
-      h[i].opacity = g[i].opacity;
-      for (int c = 0; c < 3; ++c) h[i].rgb[c] = g[i].rgb[c];
-    }
   }
   const int W = cam->width, H = cam->height;
   const int TX = (W + kTile - 1) / kTile, TY = (H + kTile - 1) / kTile;
-  std::vector<std::vector<int32_t>> lists;
-  tile_lists(g, TX, TY, lists);
   const size_t P = size_t(W) * H;
   const int64_t T = int64_t(TX) * TY;
   // per tile: partial sums per list position (value 9 + magnitude 9),
@@ -1107,7 +1104,7 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
   // result is that of one pass over all tiles in tile order, for any band
   // height and thread count, with the partials of one band held at a time
   std::memset(g2d, 0, sizeof(double) * 9 * size_t(n));
-  std::memset(m2d, 0, sizeof(double) * 9 * size_t(n));
+  if (want_mags) std::memset(m2d, 0, sizeof(double) * 9 * size_t(n));
   const int band = std::max(1, (1024 + TX - 1) / TX);
   std::vector<std::vector<double>> part(size_t(band) * TX);
   for (int ty0 = 0; ty0 < TY; ty0 += band) {
@@ -1151,9 +1148,11 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
             double dalpha = 0.0, malpha = 0.0;
             for (int c = 0; c < 3; ++c) {
               o[6 + c] += a * Tk * G[c];
-              o[9 + 6 + c] += a * Tk * Gm[c];
               dalpha += Tk * (q.rgb[c] - S[c]) * G[c];
-              malpha += Tk * (std::fabs(q.rgb[c]) + std::fabs(S[c])) * Gm[c];
+              if (want_mags) {
+                o[9 + 6 + c] += a * Tk * Gm[c];
+                malpha += Tk * (std::fabs(q.rgb[c]) + std::fabs(S[c])) * Gm[c];
+              }
             }
             for (int c = 0; c < 3; ++c) S[c] = a * q.rgb[c] + (1.0 - a) * S[c];
             if (tr.clamped[kk]) continue;
@@ -1161,17 +1160,19 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
             const double e = a / q.opacity;  // exp(power)
             const double dpow = dalpha * a, mpow = malpha * a;
             o[5] += dalpha * e;
-            o[9 + 5] += malpha * e;
             o[2] += dpow * (-0.5 * dx * dx);
-            o[9 + 2] += mpow * (0.5 * dx * dx);
             o[3] += dpow * (-dx * dy);
-            o[9 + 3] += mpow * std::fabs(dx * dy);
             o[4] += dpow * (-0.5 * dy * dy);
-            o[9 + 4] += mpow * (0.5 * dy * dy);
             o[0] += dpow * (q.A * dx + q.B * dy);
-            o[9 + 0] += mpow * (std::fabs(q.A * dx) + std::fabs(q.B * dy));
             o[1] += dpow * (q.B * dx + q.C * dy);
-            o[9 + 1] += mpow * (std::fabs(q.B * dx) + std::fabs(q.C * dy));
+            if (want_mags) {
+              o[9 + 5] += malpha * e;
+              o[9 + 2] += mpow * (0.5 * dx * dx);
+              o[9 + 3] += mpow * std::fabs(dx * dy);
+              o[9 + 4] += mpow * (0.5 * dy * dy);
+              o[9 + 0] += mpow * (std::fabs(q.A * dx) + std::fabs(q.B * dy));
+              o[9 + 1] += mpow * (std::fabs(q.B * dx) + std::fabs(q.C * dy));
+            }
           }
         }
     }
@@ -1179,10 +1180,9 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
       const std::vector<int32_t>& L = lists[t];
       for (size_t j = 0; j < L.size(); ++j) {
         const double* o = &part[t - t_lo][j * 18];
-        for (int c = 0; c < 9; ++c) {
-          g2d[size_t(L[j]) * 9 + c] += o[c];
-          m2d[size_t(L[j]) * 9 + c] += o[9 + c];
-        }
+        for (int c = 0; c < 9; ++c) g2d[size_t(L[j]) * 9 + c] += o[c];
+        if (want_mags)
+          for (int c = 0; c < 9; ++c) m2d[size_t(L[j]) * 9 + c] += o[9 + c];
       }
       std::vector<double>().swap(part[t - t_lo]);
     }
@@ -1195,14 +1195,55 @@ void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* ca
     double gp[59];
     const Proj<double> f = at_fp32 ? widen(g[i]) : h[i];
     project_backward_one<double>(f, p, *cam, g[i].rgb_pos, &g2d[size_t(i) * 9], gp);
+    for (int k = 0; k < 59; ++k) grads[k * ld + i] += gp[k];
+    if (!want_mags) continue;
     Mag mp[59], m9[9];
     for (int c = 0; c < 9; ++c) m9[c].v = m2d[size_t(i) * 9 + c];
     project_backward_one<Mag>(f, p, *cam, g[i].rgb_pos, m9, mp);
-    for (int k = 0; k < 59; ++k) {
-      grads[k * ld + i] += gp[k];
-      mags[k * ld + i] += mp[k].v;
-    }
+    for (int k = 0; k < 59; ++k) mags[k * ld + i] += mp[k].v;
   }
+}
+
+void or_backward(const float* params, int64_t n, int64_t ld, const or_camera* cam,
+                 const double* dL_dimage, const double* gmag, double* g2d, double* m2d, double* grads,
+                 double* mags, int at_fp32) {
+  std::vector<Proj<float>> g;
+  project_all(params, n, ld, *cam, g);
+  std::vector<std::vector<int32_t>> lists;
+  tile_lists(g, (cam->width + kTile - 1) / kTile, (cam->height + kTile - 1) / kTile, lists);
+  backward_impl(params, n, ld, cam, g, lists, dL_dimage, gmag, g2d, m2d, grads, mags, at_fp32, true);
+}
+
+// One view of the training step, stage by stage, projecting once: fp32
+// projection, per-tile lists in (depth bits, index) order, the render of
+// every pixel, the fp64 loss and its image gradient, and the backward at
+// the fp32 forward's values (as or_backward with at_fp32), its gradients
+// ADDED into grads [59][ld]; no magnitudes.  Writes image [3][H][W] and
+// returns the loss.  (The plain step the CPU baseline times.)
+double or_train_view(const float* params, int64_t n, int64_t ld, const or_camera* cam, const float* target,
+                     double w_l1, double w_ssim, float* image, double* grads) {
+  std::vector<Proj<float>> g;
+  project_all(params, n, ld, *cam, g);
+  const int W = cam->width, H = cam->height;
+  const int TX = (W + kTile - 1) / kTile, TY = (H + kTile - 1) / kTile;
+  std::vector<std::vector<int32_t>> lists;
+  tile_lists(g, TX, TY, lists);
+  const size_t P = size_t(W) * H;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t t = 0; t < int64_t(TX) * TY; ++t) {
+    const int tx = int(t % TX), ty = int(t / TX);
+    const std::vector<int32_t>& L = lists[t];
+    PixelTrace tr;
+    for (int py = ty * kTile; py < std::min(H, (ty + 1) * kTile); ++py)
+      for (int px = tx * kTile; px < std::min(W, (tx + 1) * kTile); ++px) {
+        trace_pixel(g, L.data(), int64_t(L.size()), px, py, tr);
+        for (int c = 0; c < 3; ++c) image[c * P + size_t(py) * W + px] = tr.rgb[c];
+      }
+  }
+  std::vector<double> dL(3 * P), g2d(9 * size_t(n));
+  const double L = or_loss(image, target, W, H, w_l1, w_ssim, dL.data(), nullptr, nullptr);
+  backward_impl(params, n, ld, cam, g, lists, dL.data(), nullptr, g2d.data(), nullptr, grads, nullptr, 1, false);
+  return L;
 }
 
 // Projection backward alone (fp64): g2d [n][9] given, adds into grads

@@ -674,3 +674,18 @@ def test_densify_split_rotates_the_offset():
     out, _, _ = oracle.densify(p, p, p, np.array([0.4], np.float32), np.array([1], np.int32), 0.5, 0.0, -4.0, z,
                                np.log(1.6))
     assert np.array_equal(out, p.astype(np.float64))
+
+
+@pytest.mark.parametrize("case", ["tiny", "small_cut"])
+def test_train_view_equals_the_stages(case):
+    """The one-view step the CPU baseline times (projection once, no
+    magnitudes) gives the render, loss and backward of the separate stages
+    bit for bit."""
+    w = synth.workload(0) if case == "tiny" else synth.cut_down(synth.workload(1), 200, 136, n=6000)
+    cam, tgt = w.cameras[0], w.targets[0]
+    L, img, grads = oracle.train_view(w.params, cam, tgt, w.w_l1, w.w_ssim)
+    img2, _, _, _ = oracle.render(w.params, cam)
+    L2, dL, _, _ = oracle.loss(img2, tgt, w.w_l1, w.w_ssim)
+    _, _, g2, _ = oracle.backward(w.params, cam, dL, at_fp32=True)
+    assert np.array_equal(img, img2) and L == L2
+    assert np.array_equal(grads, g2)
