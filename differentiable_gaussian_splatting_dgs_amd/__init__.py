@@ -36,7 +36,10 @@ TILE = 16
 EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size", "gs_preprocess",
            "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
            "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list", "gs_view_overlap", "gs_view_priority",
-           "gs_tile_partition", "gs_pack_records", "gs_unpack_grads", "gs_densify_stats", "gs_densify"]
+           "gs_tile_partition", "gs_pack_records", "gs_unpack_grads", "gs_densify_stats", "gs_densify",
+           "gs_sparse_adam_noalloc"]
+GS_NOALLOC_SCRATCH_BYTES = 256 * 1024
+GS_NOALLOC_MAX_N = (GS_NOALLOC_SCRATCH_BYTES // 4 - 1) * 4096
 
 
 class gs_camera(C.Structure):
@@ -76,6 +79,8 @@ def lib():
     L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
+    L.gs_sparse_adam_noalloc.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32,
+                                         _f32, _P]
     L.gs_project_bwd_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, C.POINTER(gs_camera), _i32,
                                       C.POINTER(C.c_void_p), _P, _P, _P, C.POINTER(gs_camera), _P, _P, _f32, _f32,
                                       _f32, _f32, _f32, _f32, _P, _sz, _P]
@@ -225,6 +230,14 @@ def gs_sparse_adam(params, grads, m, v, n, ld, union_flags, union_idx, union_cou
                                _ptr(union_idx), _ptr(union_count), float(lr), float(beta1), float(beta2),
                                float(eps), float(bias_c1), float(bias_c2), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "gs_sparse_adam")
+
+
+def gs_sparse_adam_noalloc(params, grads, m, v, n, ld, union_flags, union_idx, union_count, lr, beta1, beta2,
+                           eps, bias_c1, bias_c2, stream=None):
+    _check(lib().gs_sparse_adam_noalloc(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, _ptr(union_flags),
+                                        _ptr(union_idx), _ptr(union_count), float(lr), float(beta1), float(beta2),
+                                        float(eps), float(bias_c1), float(bias_c2), _stream(stream)),
+           "gs_sparse_adam_noalloc")
 
 
 def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, union_idx, union_count, lr,

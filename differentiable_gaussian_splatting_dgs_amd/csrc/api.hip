@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gs.h"
 #include "gs_internal.h"
@@ -111,6 +112,41 @@ gs::SsimWindow make_window() {
 }
 
 size_t adam_ws_bytes(int64_t n) { return gs::compact_ws_bytes(n); }
+
+}  // namespace
+
+// The scratch of gs_sparse_adam_noalloc.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device (each device holds its
+// own copy), taken once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[GS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device).
+gs_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "gs_sparse_adam_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(GS_ERR_HIP, "gs_sparse_adam_noalloc: device %d beyond the %d the library tracks", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "gs_sparse_adam_noalloc (hipGetSymbolAddress)");
+    if (p == nullptr) return fail(GS_ERR_HIP, "gs_sparse_adam_noalloc: NULL scratch address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GS_OK;
+}
 
 }  // namespace
 
@@ -337,6 +373,33 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
     e = gs::launch_sparse_adam(params, grads, m, v, n, ld, union_idx, union_count, lr, beta1, beta2, eps, bias_c1,
                                bias_c2, st);
   return hip_status(e, "gs_sparse_adam");
+}
+
+gs_status gs_sparse_adam_noalloc(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
+                                 uint8_t* union_flags, int32_t* union_idx, int64_t* union_count, float lr,
+                                 float beta1, float beta2, float eps, float bias_c1, float bias_c2, void* stream) {
+  REQUIRE(n >= 0 && n <= GS_NOALLOC_MAX_N, "n = %lld outside [0, %lld]: the union compaction needs %zu scratch "
+          "bytes, the allocation-free entry holds %zu", (long long)n, (long long)GS_NOALLOC_MAX_N,
+          adam_ws_bytes(n), size_t(GS_NOALLOC_SCRATCH_BYTES));
+  REQUIRE(adam_ws_bytes(n) <= size_t(GS_NOALLOC_SCRATCH_BYTES), "n = %lld: scratch too small", (long long)n);
+  REQUIRE(ld >= n, "ld < n");
+  REQUIRE(union_count != nullptr, "union_count is NULL");
+  if (n > 0) {
+    REQUIRE(params && grads && m && v && union_flags && union_idx, "NULL array");
+    REQUIRE(aligned(union_flags, 16), "union_flags not 16-byte aligned");
+  }
+  REQUIRE(std::isfinite(lr) && std::isfinite(beta1) && std::isfinite(beta2) && std::isfinite(eps), "non-finite scalar");
+  REQUIRE(bias_c1 > 0.0f && bias_c2 > 0.0f, "bias corrections must be > 0");
+  static_assert(GS_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+  void* ws = nullptr;
+  CHECK(scratch_address(&ws));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // (k_count writes every block count k_scan_counts and k_write read)
+  hipError_t e = gs::launch_compact(union_flags, n, union_idx, union_count, true, ws, st);
+  if (e == hipSuccess)
+    e = gs::launch_sparse_adam(params, grads, m, v, n, ld, union_idx, union_count, lr, beta1, beta2, eps, bias_c1,
+                               bias_c2, st);
+  return hip_status(e, "gs_sparse_adam_noalloc");
 }
 
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,

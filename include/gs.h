@@ -290,6 +290,27 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
                          float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* gs_sparse_adam without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving and
+ * training loops, harnesses that forbid hipMalloc).  Its scratch (the union
+ * compaction's per-block counts) lives in a file-scope device array of
+ * GS_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends; the call allocates nothing and frees nothing.
+ *   arguments and results as gs_sparse_adam.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from different threads) race and must be
+ * ordered by the caller.  Nothing in the array has to start at zero: each
+ * call writes every word it reads before reading it.
+ * Errors: as gs_sparse_adam; GS_ERR_INVALID_ARG also when n > GS_NOALLOC_MAX_N
+ * (the union compaction of more rows would not fit the array); GS_ERR_HIP
+ * when the array's device address cannot be obtained.  Nothing is launched
+ * on an error. */
+#define GS_NOALLOC_SCRATCH_BYTES (256 * 1024)
+#define GS_NOALLOC_MAX_N ((int64_t)(GS_NOALLOC_SCRATCH_BYTES / 4 - 1) * 4096)
+gs_status gs_sparse_adam_noalloc(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
+                                 uint8_t* union_flags, int32_t* union_idx, int64_t* union_count, float lr,
+                                 float beta1, float beta2, float eps, float bias_c1, float bias_c2, void* stream);
+
 /* gs_project_bwd of the batch's last views followed by gs_sparse_adam, in
  * one pass over the union rows (same passages as the two): each listed
  * row's parameters are read once, every fused view's parameter gradients are
