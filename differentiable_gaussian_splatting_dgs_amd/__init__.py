@@ -49,6 +49,11 @@ class gs_camera(C.Structure):
                 ("near_z", C.c_float)]
 
 
+class gs_param_grads(C.Structure):
+    _fields_ = [("params", C.c_void_p), ("ld", C.c_int64), ("cam", C.POINTER(gs_camera)),
+                ("vis_idx", C.c_void_p), ("vis_count", C.c_void_p), ("grads", C.c_void_p)]
+
+
 _P, _i64, _i32, _f32, _sz = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_size_t
 _handle = None
 
@@ -75,7 +80,8 @@ def lib():
     L.gs_bin_sort_async.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
     L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
     L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
-    L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
+    L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32,
+                                C.POINTER(gs_param_grads), _P, _P]
     L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
@@ -211,10 +217,22 @@ def gs_loss(image, target, width, height, w_l1, w_ssim, loss, dL_dimage, workspa
 
 
 def gs_render_bwd(proj, n, vals, tile_ranges, num_pairs, width, height, T_final, last, dL_dimage, grad2d,
-                  tile_order=None, split_ws=None, segment_len=SEGMENT_LEN, stream=None):
+                  tile_order=None, split_ws=None, segment_len=SEGMENT_LEN, param_grads=None, visits=None,
+                  stream=None):
+    """``param_grads``: None, or (params, ld, cam, vis_idx, vis_count,
+    grads) to chain the view's projection backward into the [59][ld]
+    gradient planes in the same call; ``visits``: None or a device int64
+    scalar the number of back-propagated (pixel, entry) pairs is added to."""
+    pg = None
+    if param_grads is not None:
+        params, ld, cam, vis_idx, vis_count, grads = param_grads
+        c = cam if isinstance(cam, gs_camera) else make_camera(cam)
+        pg = gs_param_grads(params.data_ptr(), int(ld), C.pointer(c), vis_idx.data_ptr(), vis_count.data_ptr(),
+                            grads.data_ptr())
     _check(lib().gs_render_bwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), _ptr(tile_order), num_pairs, width,
                                height, _ptr(T_final), _ptr(last), _ptr(dL_dimage), _ptr(grad2d),
-                               _ptr(split_ws), _nbytes(split_ws), segment_len, _stream(stream)),
+                               _ptr(split_ws), _nbytes(split_ws), segment_len,
+                               None if pg is None else C.byref(pg), _ptr(visits), _stream(stream)),
            "gs_render_bwd")
 
 
@@ -434,6 +452,8 @@ class TrainStep:
         self.record_tiles = record_tiles
         self.timer = None        # optional: name -> list of (start, end) torch.cuda.Event pairs
         self.timer_stages = None  # optional: the stage names to time (None: all)
+        self.visits = None       # optional: device int64 scalar the raster backward adds its
+                                 # back-propagated (pixel, entry) count to
         rows = max(n, 1)
         # screen-gradient buffers: one per view whose projection backward
         # step() fuses into Adam (the last ndefer views), two alternating
@@ -580,16 +600,18 @@ class TrainStep:
         self.render_view(k)
 
     def backward_view(self, k, keep_grad2d=False):
-        """Raster backward, then (unless keep_grad2d) projection backward."""
+        """Raster backward; unless keep_grad2d, the projection backward is
+        chained on in the same call (the view's parameter gradients added
+        to the gradient planes, the screen-space buffer left zero)."""
         vw = self.views[k]
         ps = self.sets[k % self.nsets]
         self._gcur = self._gbuf(k)
-        with self._stage("render_bwd"):
+        pg = None if keep_grad2d else (self.params, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1],
+                                       self.grads)
+        with self._stage("render_bwd" if keep_grad2d else "render_bwd+project_bwd"):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
                           vw.dL, self.g2d[self._gcur], vw.order, self.split_ws if self.seg[k] else None,
-                          self.seg[k])
-        if not keep_grad2d:
-            self.project_view(k)
+                          self.seg[k], param_grads=pg, visits=self.visits)
 
     def project_view(self, k):
         vw = self.views[k]
@@ -703,6 +725,29 @@ class TrainStep:
         the projection backward of the last ndefer views."""
         self.run_views(defer_projection=True)
         self.adam(fused=True)
+
+    # -- training state ------------------------------------------------------
+    def state(self):
+        """Device copies of the training state: parameters, both Adam
+        moments and the step count (what a checkpoint holds)."""
+        return dict(params=self.params.clone(), m=self.m.clone(), v=self.v.clone(), t=self.t)
+
+    def load_state(self, st):
+        """Continue from a state(): parameters and moments copied in, the
+        step count restored; what the last Adam pass left for the next
+        step's first view (records, visibility bytes, union flags) is
+        dropped, so that view is projected afresh."""
+        torch.cuda.current_stream(self.device).synchronize()
+        self.params.copy_(st["params"])
+        self.m.copy_(st["m"])
+        self.v.copy_(st["v"])
+        self.t = int(st["t"])
+        self.grads.zero_()
+        for g2 in self.g2d:
+            g2.zero_()
+        self.union_flags.zero_()
+        self.next_flags.zero_()
+        self._pre0 = False
 
 
 def from_workload(work, device="cuda", **kw) -> TrainStep:

@@ -319,21 +319,36 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
 gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                         const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                        const void* split_ws, size_t split_ws_bytes, int32_t segment_len, void* stream) {
+                        const void* split_ws, size_t split_ws_bytes, int32_t segment_len,
+                        const gs_param_grads* param_grads, uint64_t* visits, void* stream) {
   CHECK(check_size(width, height));
   REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
   REQUIRE(num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "num_pairs out of range");
   REQUIRE(tile_ranges && T_final && last && dL_dimage, "NULL argument");
-  if (num_pairs > 0) {
-    REQUIRE(proj && vals && grad2d, "NULL array");
-    REQUIRE(aligned(proj, 16) && aligned(grad2d, 16), "proj / grad2d not 16-byte aligned");
+  if (num_pairs > 0 || (param_grads != nullptr && n > 0)) {
+    REQUIRE(grad2d != nullptr && aligned(grad2d, 16), "grad2d NULL or not 16-byte aligned");
   }
+  if (num_pairs > 0) REQUIRE(proj && vals && aligned(proj, 16), "NULL or misaligned proj / vals");
+  REQUIRE(visits == nullptr || aligned(visits, 8), "visits not 8-byte aligned");
   int seg_shift = 0;
   CHECK(check_split(split_ws, split_ws_bytes, width, height, segment_len, seg_shift));
-  return hip_status(gs::launch_render_bwd(proj, vals, tile_ranges, tile_order, num_pairs, width, height, T_final,
-                                          last, dL_dimage, grad2d, split_ws, seg_shift,
-                                          static_cast<hipStream_t>(stream)),
-                    "gs_render_bwd");
+  gs::CamArgs c{};
+  if (param_grads != nullptr) {
+    CHECK(check_camera(param_grads->cam, c));
+    REQUIRE(c.width == width && c.height == height, "param_grads->cam is %dx%d, the image %dx%d", c.width, c.height,
+            width, height);
+    REQUIRE(param_grads->ld >= n, "param_grads->ld < n");
+    REQUIRE(param_grads->vis_count != nullptr, "param_grads->vis_count is NULL");
+    if (n > 0)
+      REQUIRE(param_grads->params && param_grads->vis_idx && param_grads->grads, "NULL array in param_grads");
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = gs::launch_render_bwd(proj, vals, tile_ranges, tile_order, num_pairs, width, height, T_final, last,
+                                       dL_dimage, grad2d, split_ws, seg_shift, visits, st);
+  if (e == hipSuccess && param_grads != nullptr)
+    e = gs::launch_project_bwd(param_grads->params, n, param_grads->ld, c, param_grads->vis_idx,
+                               param_grads->vis_count, grad2d, param_grads->grads, st);
+  return hip_status(e, "gs_render_bwd");
 }
 
 gs_status gs_project_bwd(const float* params, int64_t n, int64_t ld, const gs_camera* cam, const int32_t* vis_idx,

@@ -72,7 +72,7 @@ hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint3
 hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                              const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                             const void* split, int seg_shift, hipStream_t st);
+                             const void* split, int seg_shift, uint64_t* visits, hipStream_t st);
 hipError_t launch_project_bwd(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
                               const int32_t* vis_idx, const int64_t* vis_count, float* grad2d, float* grads,
                               hipStream_t st);

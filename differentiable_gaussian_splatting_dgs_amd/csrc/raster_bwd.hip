@@ -71,12 +71,14 @@ __device__ __forceinline__ void wave_sum9(const float v[9], float& q0, float& q1
 }
 
 // One pass of a quarter's list positions [lo, hi), back to front, from the
-// per-pixel state (T, S) at position hi.
+// per-pixel state (T, S) at position hi.  With kCount, nvis counts the
+// lane's pixel-entry pairs that composited (the steps back-propagated).
+template <bool kCount>
 __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                           uint32_t start, uint32_t lo, uint32_t hi, float qx, float qy, float pxc,
                                           float pyc, uint32_t lastp, float T, float S0, float S1, float S2,
                                           float G0, float G1, float G2, float* __restrict__ grad2d, LdsRecs& s_rec,
-                                          float* s_acc) {
+                                          float* s_acc, uint32_t& nvis) {
   const int lane = threadIdx.x;
   // lanes 0, 8, 16, ..., 56 (row r = lane / 16, half h = lane / 8 % 2)
   // store the half sums: row r of the folded sums q0 / q1 carries sum
@@ -125,6 +127,7 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       const float araw = c.x * e;
       const float alpha = fminf(0.99f, araw);
       ok = ok && !(alpha < 1.0f / 255.0f);
+      if constexpr (kCount) nvis += ok ? 1u : 0u;
       // same decisions as the forward: `ok` = this pixel composited it.  A
       // lane that did not takes alpha 0: 1 - 0 = 1 has an exact hardware
       // reciprocal, T * 1 = T and fma(0, c, 1 * S) = S (colours and S are
@@ -196,13 +199,15 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
 // (nhelp = kPools x pool size: one each), each from its recorded state; the
 // rest own one quarter each (in `order`) and run its list from the last
 // composited entry down to the first position no helper covers.
+template <bool kCount>
 __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                                    const uint32_t* __restrict__ ranges,
                                                    const uint32_t* __restrict__ order, int64_t num_pairs, int W,
                                                    int H, int TX, int nT, const float* __restrict__ T_final,
                                                    const uint32_t* __restrict__ last,
                                                    const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
-                                                   const void* split, int seg_shift, int nhelp) {
+                                                   const void* split, int seg_shift, int nhelp,
+                                                   unsigned long long* __restrict__ visits) {
   __shared__ LdsRecs s_rec;
   __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
   const SplitLayout sl = split_layout(W, H);
@@ -216,13 +221,14 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
     nitems = sp.counters[32 * pool + 1];
     if (nitems > uint32_t(sl.pool_slots)) nitems = uint32_t(sl.pool_slots);
   }
+  uint32_t nvis = 0;
   for (uint32_t item = blockIdx.x / kPools;; item += uint32_t(nhelp / kPools)) {
     int tile, q0;
     uint32_t lo, seg_hi = 0, slot = 0;
     if (helper) {
-      if (item >= nitems) return;
+      if (item >= nitems) break;
       slot = sp.items[pool * uint32_t(sl.pool_slots) + item];
-      if (slot >= uint32_t(kPools * sl.pool_slots)) return;
+      if (slot >= uint32_t(kPools * sl.pool_slots)) break;
       const uint32_t own = sp.owner[slot];
       tile = int(own >> 7);
       q0 = int(own >> 5) & 3;
@@ -231,11 +237,11 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
     } else {
       int rank;
       quarter_of(int(blockIdx.x) - nhelp, rank, q0);   // nhelp: a multiple of kXcds
-      if (rank >= nT) return;
+      if (rank >= nT) break;
       tile = order != nullptr ? int(order[rank]) : rank;
       lo = split != nullptr ? sp.qsegs[tile * kWPT + q0] << seg_shift : 0u;
     }
-    if (tile >= nT) return;
+    if (tile >= nT) break;
     const int tx = tile % TX, ty = tile / TX;
     const int x0 = tx * kTile, y0 = ty * kTile;
     const float qx = float(x0 + (q0 & 1) * 8) + 0.5f, qy = float(y0 + (q0 >> 1) * 8) + 0.5f;
@@ -266,10 +272,17 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       const float G0 = inside ? dL_dimage[pix] : 0.0f;
       const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
       const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
-      bwd_range(proj, vals, start, lo, hi, qx, qy, float(px) + 0.5f, float(py) + 0.5f, lastp, T, S0, S1, S2, G0, G1,
-                G2, grad2d, s_rec, s_acc);
+      bwd_range<kCount>(proj, vals, start, lo, hi, qx, qy, float(px) + 0.5f, float(py) + 0.5f, lastp, T, S0, S1, S2,
+                        G0, G1, G2, grad2d, s_rec, s_acc, nvis);
     }
-    if (!helper) return;
+    if (!helper) break;
+  }
+  if constexpr (kCount) {
+    // (every exit above is taken by the whole wave)
+    uint32_t c = nvis;
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) c += uint32_t(__shfl_xor(int(c), d, 64));
+    if (lane == 0 && c != 0) atomicAdd(visits, static_cast<unsigned long long>(c));
   }
 }
 
@@ -300,15 +313,22 @@ __global__ __launch_bounds__(256) void k_project_bwd(const float* __restrict__ p
 hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                              const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                             const void* split, int seg_shift, hipStream_t st) {
+                             const void* split, int seg_shift, uint64_t* visits, hipStream_t st) {
   const int TX = (width + kTile - 1) / kTile, TY = (height + kTile - 1) / kTile;
   const int nT = TX * TY;
   if (split != nullptr && !raster_split_fits(width, height)) split = nullptr;
   // one helper per recorded state the pools can hold
   const int nhelp = split != nullptr ? kPools * split_layout(width, height).pool_slots : 0;
-  k_render_bwd<<<unsigned(nhelp) + raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges,
-                                                          tile_order, num_pairs, width, height, TX, nT, T_final,
-                                                          last, dL_dimage, grad2d, split, seg_shift, nhelp);
+  const unsigned grid = unsigned(nhelp) + raster_grid(nT);
+  unsigned long long* const vc = reinterpret_cast<unsigned long long*>(visits);
+  if (visits != nullptr)
+    k_render_bwd<true><<<grid, 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order, num_pairs,
+                                            width, height, TX, nT, T_final, last, dL_dimage, grad2d, split, seg_shift,
+                                            nhelp, vc);
+  else
+    k_render_bwd<false><<<grid, 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
+                                             num_pairs, width, height, TX, nT, T_final, last, dL_dimage, grad2d, split,
+                                             seg_shift, nhelp, nullptr);
   return hipGetLastError();
 }
 

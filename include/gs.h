@@ -249,12 +249,39 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
  *                segments of long lists are then walked by separate waves
  *                from the recorded states, the rest of each list from its
  *                end (the same sums up to fp32 rounding order)
+ *   param_grads  NULL (screen-space gradients only, left in grad2d for a
+ *                later gs_project_bwd or gs_project_bwd_adam), or the
+ *                projection backward of the view chained on in the same
+ *                call (Odin summary page: a view's backward writes the
+ *                gradients of its primitive set only): the view's
+ *                parameter gradients dL/dparams are ADDED (+=) to
+ *                param_grads->grads ([59][ld]) for the rows of its visible
+ *                list, exactly as gs_project_bwd computes them, and those
+ *                grad2d rows are re-zeroed (grad2d is then scratch: zero on
+ *                entry and on return)
+ *   visits       device, uint64 scalar, or NULL: the number of (pixel,
+ *                list entry) pairs whose compositing step was
+ *                back-propagated (the pixels that composited the entry)
+ *                is ADDED to *visits -- the backward's unit of work (the
+ *                counting costs an atomic add per wave)
  * The discrete decisions (skip, stop, 0.99 clamp) are held at the
- * forward's; the 2D mean gradient is in pixels; depth gets none. */
+ * forward's; the 2D mean gradient is in pixels; depth gets none.
+ * Errors: GS_ERR_INVALID_ARG for sizes out of range, NULL or misaligned
+ * buffers, a split workspace of the wrong size or segment length, an
+ * invalid camera or ld < n in param_grads. */
+typedef struct {
+  const float* params;      /* device, [59][ld] fp32: the view's parameters */
+  int64_t ld;               /* plane stride, >= n */
+  const gs_camera* cam;     /* host: the view's camera */
+  const int32_t* vis_idx;   /* device: the view's visible list (gs_preprocess) */
+  const int64_t* vis_count; /* device: its length */
+  float* grads;             /* device in/out, [59][ld] fp32: += dL/dparams */
+} gs_param_grads;
 gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const uint32_t* tile_ranges,
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                         const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                        const void* split_ws, size_t split_ws_bytes, int32_t segment_len, void* stream);
+                        const void* split_ws, size_t split_ws_bytes, int32_t segment_len,
+                        const gs_param_grads* param_grads, uint64_t* visits, void* stream);
 
 /* Projection backward of one view: the chain rule from the screen-space
  * gradients to all 59 parameters (SH coefficients and view direction, EWA

@@ -69,6 +69,7 @@ def lib():
         L.or_bin.argtypes = [P, i64, i64, P, P, P, i64, P]
         L.or_render.argtypes = [P, i64, i64, P, P, P, P, P]
         L.or_render_brute.argtypes = [P, i64, i64, P, P, P, P]
+        L.or_composited_counts.argtypes = [P, i64, i64, P, P]
         L.or_composite_pixels.argtypes = [P, i64, i64, P, P, P, P, P, i64, P, P, P]
         L.or_loss.restype = f64
         L.or_loss.argtypes = [P, P, i32, i32, f64, f64, P, P, P]
@@ -213,6 +214,16 @@ def render(params, cam):
     c = cam_struct(cam)
     lib().or_render(_p(p), n, n, C.byref(c), _p(img), _p(Tf), _p(last), _p(proc))
     return img, Tf, last, proc
+
+
+def composited_counts(params, cam):
+    """Per pixel the number of Gaussians composited, [H][W] uint32."""
+    p = _params(params)
+    n = p.shape[1]
+    out = np.empty((cam.height, cam.width), np.uint32)
+    c = cam_struct(cam)
+    lib().or_composited_counts(_p(p), n, n, C.byref(c), _p(out))
+    return out
 
 
 def render_brute(params, cam):

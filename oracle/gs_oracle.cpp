@@ -830,6 +830,29 @@ void or_render(const float* params, int64_t n, int64_t ld, const or_camera* cam,
   }
 }
 
+// Per pixel, the number of Gaussians it composited (fp32 rule of or_render):
+// counts [H][W].  Their sum is the number of (pixel, list entry) steps a
+// backward pass back-propagates.
+void or_composited_counts(const float* params, int64_t n, int64_t ld, const or_camera* cam, uint32_t* counts) {
+  std::vector<Proj<float>> g;
+  project_all(params, n, ld, *cam, g);
+  const int W = cam->width, H = cam->height;
+  const int TX = (W + kTile - 1) / kTile, TY = (H + kTile - 1) / kTile;
+  std::vector<std::vector<int32_t>> lists;
+  tile_lists(g, TX, TY, lists);
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t t = 0; t < int64_t(TX) * TY; ++t) {
+    const int tx = int(t % TX), ty = int(t / TX);
+    const std::vector<int32_t>& L = lists[t];
+    PixelTrace tr;
+    for (int py = ty * kTile; py < std::min(H, (ty + 1) * kTile); ++py)
+      for (int px = tx * kTile; px < std::min(W, (tx + 1) * kTile); ++px) {
+        trace_pixel(g, L.data(), int64_t(L.size()), px, py, tr);
+        counts[size_t(py) * W + px] = uint32_t(tr.pos.size());
+      }
+  }
+}
+
 // Brute-force render: every pixel scans ALL n Gaussians, keeps the visible
 // ones whose tile rectangle holds the pixel's tile, sorts them by (depth
 // bits, index) and composites.  Must equal or_render bit for bit.

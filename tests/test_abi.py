@@ -134,13 +134,28 @@ def test_invalid_arguments_rejected_on_host():
     for seg in (0, 32, 100, 1 << 17):
         assert lib.gs_render_fwd(*fwd, P(256), need, seg, None) == 1
         assert b"segment_len" in lib.gs_last_error()
-        assert lib.gs_render_bwd(*bwd, P(256), need, seg, None) == 1
+        assert lib.gs_render_bwd(*bwd, P(256), need, seg, None, None, None) == 1
     assert lib.gs_render_fwd(*fwd, P(272), need, 1024, None) == 1
     assert b"split_ws" in lib.gs_last_error()
-    assert lib.gs_render_bwd(*bwd, P(272), need, 1024, None) == 1
+    assert lib.gs_render_bwd(*bwd, P(272), need, 1024, None, None, None) == 1
     assert lib.gs_render_fwd(*fwd, P(256), need - 1, 1024, None) == 1
     assert b"split_ws_bytes" in lib.gs_last_error()
-    assert lib.gs_render_bwd(*bwd, P(256), need - 1, 1024, None) == 1
+    assert lib.gs_render_bwd(*bwd, P(256), need - 1, 1024, None, None, None) == 1
+    # raster backward with the projection backward chained: camera of
+    # another size, ld < n, NULL gradient planes; misaligned visit counter
+    pg = gs.gs_param_grads(16, 4, C.pointer(cam), 16, 16, 16)
+    cam.width = 32
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None) == 1
+    assert b"param_grads->cam" in lib.gs_last_error()
+    cam.width = 64
+    pg.ld = 3
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None) == 1
+    assert b"ld" in lib.gs_last_error()
+    pg.ld, pg.grads = 4, None
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None) == 1
+    assert b"param_grads" in lib.gs_last_error()
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, None, P(20), None) == 1
+    assert b"visits" in lib.gs_last_error()
     # view coupling: view count and n out of range, NULL / misaligned
     # buffers, small workspace; zero views is a no-op
     ws = gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1000, 3)

@@ -260,6 +260,34 @@ def test_backward_stages_in_isolation(case):
     check_grad(f"{case} grads (isolated)", res["grads"], ref["grads"], ref["mags"])
 
 
+@pytest.mark.parametrize("case", ["small_cut", "mid_cut"])
+def test_render_bwd_parameter_mode_and_visit_count(case):
+    """gs_render_bwd with the view's projection backward chained on in the
+    same call (parameters, camera and visible list given, dL/dparams added
+    to the [59][n] planes): the batch's accumulated gradients against the
+    oracle on the oracle's image gradient, the screen-space buffers left
+    zero; and the backward's count of back-propagated (pixel, entry) pairs
+    equal to the oracle's count of composited ones, exactly."""
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    work = workload_case(case)
+    ref = oracle.step(work)
+    step = gs.from_workload(work, record_tiles=True)
+    step.visits = torch.zeros(1, dtype=torch.int64, device="cuda")
+    total = 0
+    for k, cam in enumerate(work.cameras):
+        step.forward_view(k)
+        step.views[k].dL.copy_(torch.as_tensor(np.asarray(ref["views"][k]["dL_dimage"], np.float32)))
+        step.backward_view(k)
+        torch.cuda.synchronize()
+        cnt = oracle.composited_counts(work.params, cam).astype(np.int64)
+        total += int(cnt.sum())
+        say(f"  {case}/v{k}: composited (pixel, entry) pairs {int(cnt.sum())}, GPU total {int(step.visits.item())}")
+        assert int(step.visits.item()) == total, f"{case}/v{k} visits"
+    check_grad(f"{case} grads (render_bwd parameter mode)", step.grads.cpu().numpy(), ref["grads"], ref["mags"])
+    for g2 in step.g2d:
+        assert not g2.any().item(), "screen-space gradients not re-zeroed"
+
+
 def split_pool_counts(step, vw):
     """Per pool of the split workspace: states requested by the last view's
     forward (the counter runs on past the pool size) and the pool size.

@@ -230,6 +230,26 @@ def test_stacked_gaussians_front_to_back():
 # invariants and brute force on the seeded scenes
 # ---------------------------------------------------------------------------
 
+def test_composited_counts_against_the_weights():
+    """A pixel's composited count is the number of non-zero compositing
+    weights (alpha T >= 1/255 * 1e-4 > 0): with one colour c for every
+    Gaussian, C / c = sum of weights, and each composited Gaussian adds at
+    least 1/255 of T >= 1e-4; the count never exceeds `last`."""
+    w = synth.workload(0)
+    cam = w.cameras[0]
+    cnt = oracle.composited_counts(w.params, cam)
+    _, _, last, _ = oracle.render(w.params, cam)
+    assert np.all(cnt <= last) and np.array_equal(cnt > 0, last > 0)
+    p = w.params.copy()
+    p[11:59] = 0.0
+    p[11:14] = 0.7
+    img, Tf, _, _ = oracle.render(p, cam)
+    rgb = oracle.preprocess(p, cam)["rgb"][0]
+    wsum = img[0] / rgb[0]
+    assert np.all(wsum >= cnt * (1e-4 / 255) * (1 - 1e-5))
+    assert cnt.sum() > 5 * cnt.size
+
+
 def test_weights_plus_transmittance_is_one():
     w = synth.workload(0)
     p = w.params.copy()

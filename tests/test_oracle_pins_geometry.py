@@ -198,6 +198,7 @@ def test_stop_rule_closed_form():
         T *= 1 - alpha[k]
     assert T * (1 - alpha[3]) < 1e-4 < T          # far from the threshold either way
     assert int(last[0, 0]) == 3 and int(proc[0]) == 4
+    assert int(oracle.composited_counts(p, cam)[0, 0]) == 3
     assert Tf[0, 0] == pytest.approx(T, rel=1e-5)
     assert np.allclose(img[:, 0, 0], C, rtol=1e-6, atol=1e-7)
 
@@ -214,6 +215,7 @@ def test_stop_rule_with_clamp_and_skip():
     assert alpha[0] == 0.99 and alpha[1] < 1 / 255
     img, Tf, last, proc = oracle.render(p, cam)
     assert int(last[0, 0]) == 3 and int(proc[0]) == 4
+    assert int(oracle.composited_counts(p, cam)[0, 0]) == 2      # the skipped one is not counted
     assert Tf[0, 0] == pytest.approx(0.01 * 0.5, rel=1e-5)
     assert np.allclose(img[:, 0, 0], 0.99 * col[0] + 0.5 * 0.01 * col[2], rtol=1e-6)
 
