@@ -6,10 +6,10 @@ seeded synthetic Gaussians, four 1920x1080 ring views per step.
 
 Prints ONE JSON line.  `value` = steps/s with every input resident in HBM
 when the timed region starts.  Protocol: W warm-up steps from the seeded
-parameters, then the state (parameters, Adam moments, step count) is
-restored from a device copy before every block of RESTORE_EVERY steps,
-outside the timed region, so every block trains the same ten steps from the
-same scene instead of a drifting one.  Each block is bracketed by device
+parameters; the state they leave (parameters, Adam moments, step count) is
+kept as a device copy and restored before every block of RESTORE_EVERY
+steps, outside the timed region, so every block trains the same ten steps
+from the same scene instead of a drifting one.  Each block is bracketed by device
 synchronisations; `value` = K / (sum of the blocks' wall times); every step
 is also bracketed by HIP events on the caller's stream (median reported).
 Inside the timed blocks HIP events on the stream the library launches on
@@ -443,11 +443,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"shard": shard_bench(step, work), "densify": densify_bench(step)}), flush=True)
         return
-    init = step.state()
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step.step()
     torch.cuda.synchronize()
+    # the state every timed block starts from: after the warm-up steps
+    init = step.state()
 
     # The objects alive after set-up (torch's, numpy's, the workload's) are
     # moved out of the garbage collector's generations: a full collection
@@ -526,6 +527,7 @@ def main():
         return o / (ms * 1e-3) / VALU_PEAK
 
     per_view = {k: v / nv for k, v in B_stage.items()}
+    fused_bytes = float(np.mean([1416 * U + 96 * sum(v["V"] for v in vs) + 64 * U for vs, U in sizes]))
     stage_bound = {
         "preprocess": {"bound": "hbm", "frac": hbm_frac(per_view["preprocess"], float(np.mean(pre_rest)))
                        if pre_rest else None, "note": "views 1..3 (view 0 is projected in the Adam pass)"},
@@ -537,9 +539,12 @@ def main():
         "render_bwd": {"bound": "alu", "frac": alu_frac(visits_per_launch * OPS_PER_VISIT["render_bwd"],
                                                         stages["render_bwd"]),
                        "hbm_frac": hbm_frac(per_view["render_bwd"], stages["render_bwd"])},
-        "sparse_adam": {"bound": "hbm", "frac": hbm_frac(B_stage["project_bwd"] + B_stage["sparse_adam"],
-                                                         stages["sparse_adam"]),
-                        "note": "every view's projection backward fused into the Adam pass"},
+        "sparse_adam": {"bound": "hbm", "frac": hbm_frac(fused_bytes, stages["sparse_adam"]),
+                        "alg_bytes": fused_bytes,
+                        "note": "every view's projection backward and the next step's first projection fused "
+                                "into the Adam pass: 1416 B per union row (parameters and moments in and out) "
+                                "+ 96 B per (view, visible row) (screen gradients read and re-zeroed) + 64 B "
+                                "per row (the next record)"},
     }
 
     last_views, U = sizes[-1]

@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import contextlib
 import ctypes as C
+import math
 import os
 
 import torch
@@ -440,12 +441,7 @@ class TrainStep:
         p = torch.as_tensor(params, dtype=torch.float32)
         assert p.ndim == 2 and p.shape[0] == 59
         self.device = torch.device(device)
-        self.n = n = int(p.shape[1])
-        self.ld = n
-        self.params = p.to(self.device).contiguous()
-        self.grads = torch.zeros_like(self.params)
-        self.m = torch.zeros_like(self.params)
-        self.v = torch.zeros_like(self.params)
+        n = int(p.shape[1])
         self.w_l1, self.w_ssim = float(w_l1), float(w_ssim)
         self.lr, self.beta1, self.beta2, self.eps = float(lr), float(beta1), float(beta2), float(eps)
         self.t = 0
@@ -454,44 +450,39 @@ class TrainStep:
         self.timer_stages = None  # optional: the stage names to time (None: all)
         self.visits = None       # optional: device int64 scalar the raster backward adds its
                                  # back-propagated (pixel, entry) count to
-        rows = max(n, 1)
+        # densification statistic (track_densify): per Gaussian the summed
+        # |dL/d(u, v)| and the number of views it was visible in
+        self.dens_accum = None
+        self.dens_denom = None
         # screen-gradient buffers: one per view whose projection backward
         # step() fuses into Adam (the last ndefer views), two alternating
         # for the earlier views
         nv = len(cameras)
         self.ndefer = min(nv, GS_MAX_FUSED_VIEWS)
         self.nfirst = nv - self.ndefer
-        self.g2d = [torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
-                    for _ in range(self.ndefer + (2 if self.nfirst > 0 else 0))]
-        self._gcur = 0
-        self.vis_idx = [torch.empty(rows, dtype=torch.int32, device=self.device) for _ in cameras]
         self.vis_count = torch.zeros(len(cameras), dtype=torch.int64, device=self.device)
-        self.union_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
-        self.union_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
         self.union_count = torch.zeros(1, dtype=torch.int64, device=self.device)
         if pair_capacity is None:
             pair_capacity = max(1 << 20, 24 * n)       # grown on demand
         self.pair_capacity = int(min(pair_capacity, (1 << 31) - 1))
         self.views = [View(c, tg, n, self.pair_capacity, self.device) for c, tg in zip(cameras, targets)]
         self.nsets = min(3, max(2, len(self.views)))
-        with_keys = any(v.W > 4096 or v.H > 4096 for v in self.views)
-        self.sets = [_PairSet(n, self.pair_capacity, self.device, with_keys) for _ in range(self.nsets)]
+        self._with_keys = any(v.W > 4096 or v.H > 4096 for v in self.views)
         self._cur = 0                       # set of the view last prepared
         self._free = [None] * self.nsets    # per set: event after its last reader
+        self._gcur = 0
+        self._alloc_rows(p.to(self.device).contiguous(), None, None)
         self.M_dev = torch.zeros(len(self.views), dtype=torch.int64, device=self.device)
         self.M_host = torch.zeros(len(self.views), dtype=torch.int64, pin_memory=True)
         self._set_cap = [0] * len(self.views)       # capacity of the set each view was binned into
         self.side = torch.cuda.Stream(device=self.device)      # preprocess + binning of the next view
         self.gstream = torch.cuda.Stream(device=self.device)   # projection backward
-        self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
         self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
-        self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
         # step()'s Adam pass also runs the next step's first preprocess on the
         # rows it updates (the views are the same every step, so a row
         # outside the union was invisible in view 0 and keeps its record);
-        # its visibility bytes wait here, zero between uses
+        # its visibility bytes wait in next_flags, zero between uses
         self.fuse_next_preprocess = fuse_next_preprocess
-        self.next_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
         self._pre0 = False       # view 0's records and flags come from the last Adam pass
         # the forward's checkpoints and segment list, read by the split raster
         # backward of the same view (both on the current stream, the view's
@@ -503,6 +494,30 @@ class TrainStep:
         split_views = [v for v, sg in zip(self.views, self.seg) if sg]
         self.split_ws = (_bytes(max(gs_workspace_size(GS_OP_RASTER, 0, v.W, v.H) for v in split_views), self.device)
                          if split_views else None)
+
+    def _alloc_rows(self, params, m, v):
+        """Every buffer with a row per Gaussian, for the n = params.shape[1]
+        Gaussians of `params` (device, [59][n], kept); Adam moments from m, v
+        or zero; gradients, screen-space gradients and flags zero."""
+        self.n = n = int(params.shape[1])
+        self.ld = n
+        rows = max(n, 1)
+        self.params = params
+        self.grads = torch.zeros_like(params)
+        self.m = m if m is not None else torch.zeros_like(params)
+        self.v = v if v is not None else torch.zeros_like(params)
+        self.g2d = [torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
+                    for _ in range(self.ndefer + (2 if self.nfirst > 0 else 0))]
+        self.vis_idx = [torch.empty(rows, dtype=torch.int32, device=self.device) for _ in self.views]
+        self.union_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
+        self.union_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
+        self.next_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
+        self.sets = [_PairSet(n, self.pair_capacity, self.device, self._with_keys) for _ in range(self.nsets)]
+        self._free = [None] * self.nsets
+        self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
+        self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
+        if self.dens_accum is not None:
+            self.track_densify()
 
     # the buffer set of the view last prepared (what tests read back)
     @property
@@ -606,12 +621,19 @@ class TrainStep:
         vw = self.views[k]
         ps = self.sets[k % self.nsets]
         self._gcur = self._gbuf(k)
-        pg = None if keep_grad2d else (self.params, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1],
-                                       self.grads)
-        with self._stage("render_bwd" if keep_grad2d else "render_bwd+project_bwd"):
+        # (the densification statistic reads the screen-space gradients
+        # before the projection backward re-zeroes them)
+        chain = not keep_grad2d and self.dens_accum is None
+        pg = (self.params, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1], self.grads) if chain else None
+        with self._stage("render_bwd+project_bwd" if chain else "render_bwd"):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
                           vw.dL, self.g2d[self._gcur], vw.order, self.split_ws if self.seg[k] else None,
                           self.seg[k], param_grads=pg, visits=self.visits)
+        if self.dens_accum is not None:
+            gs_densify_stats(self.g2d[self._gcur], self.vis_idx[k], self.vis_count[k:k + 1], self.n,
+                             self.dens_accum, self.dens_denom)
+            if not keep_grad2d:
+                self.project_view(k)
 
     def project_view(self, k):
         vw = self.views[k]
@@ -628,6 +650,9 @@ class TrainStep:
         overflowed its buffer set makes the whole batch run again with the
         set grown.  With defer_projection the screen-space gradients of the
         last ndefer views are left for adam(fused=True)."""
+        stat0 = None
+        if self.dens_accum is not None:
+            stat0 = (self.dens_accum.clone(), self.dens_denom.clone())
         while True:
             self._issue_views(defer_projection)
             self._counts_read.synchronize()
@@ -646,6 +671,9 @@ class TrainStep:
             self.grads.zero_()
             for g2 in self.g2d:
                 g2.zero_()
+            if stat0 is not None:
+                self.dens_accum.copy_(stat0[0])
+                self.dens_denom.copy_(stat0[1])
 
     def _issue_views(self, defer):
         main = torch.cuda.current_stream(self.device)
@@ -731,6 +759,60 @@ class TrainStep:
         """Device copies of the training state: parameters, both Adam
         moments and the step count (what a checkpoint holds)."""
         return dict(params=self.params.clone(), m=self.m.clone(), v=self.v.clone(), t=self.t)
+
+    def save_checkpoint(self, path):
+        """Write the training state (parameters, Adam moments, step count)
+        to `path` (tensors only, loadable without unpickling code)."""
+        torch.cuda.current_stream(self.device).synchronize()
+        torch.save({"params": self.params.cpu(), "m": self.m.cpu(), "v": self.v.cpu(),
+                    "t": torch.tensor(self.t, dtype=torch.int64)}, path)
+
+    def load_checkpoint(self, path):
+        """Continue from save_checkpoint's file (the same Gaussian count)."""
+        ck = torch.load(path, map_location="cpu", weights_only=True)
+        assert ck["params"].shape == self.params.shape, "checkpoint of another Gaussian count"
+        self.load_state({"params": ck["params"].to(self.device), "m": ck["m"].to(self.device),
+                         "v": ck["v"].to(self.device), "t": int(ck["t"])})
+
+    # -- densification ------------------------------------------------------
+    def track_densify(self):
+        """Start (or restart from zero) the densification statistic: every
+        raster backward from now on adds its visible rows' |dL/d(u, v)| and a
+        count (gs_densify_stats), before the projection backward consumes
+        the screen-space gradients."""
+        rows = max(self.n, 1)
+        self.dens_accum = torch.zeros(rows, dtype=torch.float32, device=self.device)
+        self.dens_denom = torch.zeros(rows, dtype=torch.int32, device=self.device)
+
+    def densify(self, grad_threshold, log_scale_threshold, logit_threshold, normals=None, seed=0,
+                log_shrink=math.log(1.6)):
+        """Clone / split / prune from the statistic gathered since
+        track_densify (gs_densify), then continue with the new Gaussians:
+        every per-Gaussian buffer is rebuilt for the new count, kept
+        Gaussians keep their Adam moments, new ones start from zero, the
+        statistic restarts from zero and the step count carries on.
+        `normals` ([2][3][n] device fp32 standard normals) are the split
+        children's random offsets; drawn from `seed` when not given.
+        Returns the new Gaussian count."""
+        assert self.dens_accum is not None, "track_densify() first"
+        n = self.n
+        if normals is None:
+            gen = torch.Generator(device=self.device)
+            gen.manual_seed(int(seed))
+            normals = torch.randn((2, 3, max(n, 1)), generator=gen, device=self.device, dtype=torch.float32)
+        ld_out = max(2 * n, 1)
+        out = [torch.empty((59, ld_out), dtype=torch.float32, device=self.device) for _ in range(3)]
+        out_n = torch.zeros(1, dtype=torch.int64, device=self.device)
+        ws = _bytes(gs_workspace_size(GS_OP_DENSIFY, n), self.device)
+        gs_densify(self.params, self.m, self.v, n, self.ld, self.dens_accum, self.dens_denom, normals,
+                   float(grad_threshold), float(log_scale_threshold), float(logit_threshold), float(log_shrink),
+                   out[0], out[1], out[2], ld_out, out_n, ws)
+        n_new = int(out_n.item())
+        p, m, v = (o[:, :n_new].contiguous() for o in out)
+        del out
+        self._alloc_rows(p, m, v)
+        self._pre0 = False
+        return n_new
 
     def load_state(self, st):
         """Continue from a state(): parameters and moments copied in, the
