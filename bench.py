@@ -13,7 +13,10 @@ from the same scene instead of a drifting one.  Each block is bracketed by devic
 synchronisations; `value` = K / (sum of the blocks' wall times); every step
 is also bracketed by HIP events on the caller's stream (median reported).
 Inside the timed blocks HIP events on the stream the library launches on
-bracket the two raster entry points; the dominant one's roofline uses them.
+bracket the raster backward, the dominant kernel, whose roofline uses
+them (an event pair between two launches idles the stream for several
+microseconds, so nothing else is bracketed there); the step runs as a
+training loop runs it, without the per-tile processed counts.
 A counting pass (one block with the raster backward's visit counter on,
 outside the timed region) gives the back-propagated (pixel, entry) pairs of
 the timed launches, the roofline's unit.  The other stages' times come from
@@ -436,7 +439,7 @@ def main():
     work = synth.workload(args.config)
     N = work.n
     nv = len(work.cameras)
-    step = gs.from_workload(work, device="cuda:0", record_tiles=True)
+    step = gs.from_workload(work, device="cuda:0", record_tiles=args.shard_only)
     torch.cuda.synchronize()
     if args.shard_only:
         step.step()
@@ -463,6 +466,7 @@ def main():
     log(f"[bench] counting block of {RESTORE_EVERY} steps")
     step.load_state(init)
     step.visits = torch.zeros(1, dtype=torch.int64, device=step.device)
+    step.record_tiles = True          # per-tile processed counts: M_proc
     sizes = []
     for _ in range(RESTORE_EVERY):
         step.step()
@@ -473,6 +477,7 @@ def main():
         sizes.append((views, int(step.union_count.item())))
     visits = int(step.visits.item())
     step.visits = None
+    step.record_tiles = False
     visits_per_launch = visits / (RESTORE_EVERY * nv)
     B_steps = [algorithmic_bytes(N, v, U) for v, U in sizes]
     B = float(np.mean([b[0] for b in B_steps]))
@@ -484,7 +489,7 @@ def main():
     left = args.steps
     while left > 0:
         k = min(RESTORE_EVERY, left)
-        w, ms, ev = run_block(step, init, k, timed_stages={"render_fwd", "render_bwd"})
+        w, ms, ev = run_block(step, init, k, timed_stages={"render_bwd"})
         wall += w
         step_ms += ms
         for name, pairs in ev.items():
@@ -507,6 +512,8 @@ def main():
     # roofline of the dominant raster kernel (one launch per view): the
     # back-propagated (pixel, entry) pairs the counting block measured,
     # times the canonical rule's operations per pair, over the launch time
+    raster.setdefault("render_fwd", stages["render_fwd"])    # (from the breakdown block)
+    launches.setdefault("render_fwd", len(stage_t["render_fwd"]))
     dom = max(("render_fwd", "render_bwd"), key=lambda k: raster.get(k, 0.0))
     kname = "k_render_bwd" if dom == "render_bwd" else "k_render_fwd"
     ops = visits_per_launch * OPS_PER_VISIT[dom]

@@ -495,6 +495,10 @@ class TrainStep:
         self.split_ws = (_bytes(max(gs_workspace_size(GS_OP_RASTER, 0, v.W, v.H) for v in split_views), self.device)
                          if split_views else None)
 
+    def _split(self, k):
+        """View k's split workspace (None when its backward runs unsplit)."""
+        return self.split_ws if self.seg[k] else None
+
     def _alloc_rows(self, params, m, v):
         """Every buffer with a row per Gaussian, for the n = params.shape[1]
         Gaussians of `params` (device, [59][n], kept); Adam moments from m, v
@@ -601,12 +605,19 @@ class TrainStep:
 
     def render_view(self, k):
         """Forward raster and loss of a prepared view."""
+        self.render_fwd_view(k)
+        self.loss_view(k)
+
+    def render_fwd_view(self, k):
         vw = self.views[k]
         ps = self.sets[k % self.nsets]
         with self._stage("render_fwd"):
             gs_render_fwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.image, vw.T_final,
-                          vw.last, vw.tile_processed if self.record_tiles else None, vw.order,
-                          self.split_ws if self.seg[k] else None, self.seg[k])
+                          vw.last, vw.tile_processed if self.record_tiles else None, vw.order, self._split(k),
+                          self.seg[k])
+
+    def loss_view(self, k):
+        vw = self.views[k]
         with self._stage("loss"):
             gs_loss(vw.image, vw.target, vw.W, vw.H, self.w_l1, self.w_ssim, vw.loss, vw.dL, self.ws_loss)
 
@@ -627,8 +638,8 @@ class TrainStep:
         pg = (self.params, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1], self.grads) if chain else None
         with self._stage("render_bwd+project_bwd" if chain else "render_bwd"):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
-                          vw.dL, self.g2d[self._gcur], vw.order, self.split_ws if self.seg[k] else None,
-                          self.seg[k], param_grads=pg, visits=self.visits)
+                          vw.dL, self.g2d[self._gcur], vw.order, self._split(k), self.seg[k], param_grads=pg,
+                          visits=self.visits)
         if self.dens_accum is not None:
             gs_densify_stats(self.g2d[self._gcur], self.vis_idx[k], self.vis_count[k:k + 1], self.n,
                              self.dens_accum, self.dens_denom)

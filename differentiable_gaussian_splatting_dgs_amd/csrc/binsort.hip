@@ -908,69 +908,84 @@ __global__ __launch_bounds__(1024) void k_tile_ranges_order(int nT, uint32_t* __
     if (order != nullptr) tile_order_block(ranges, nT, order);
     return;
   }
+  // Tile t = r * 1024 + threadIdx.x for r = 0..7.  Ranges: a wave-level
+  // exclusive scan per r, then one exchange of the 8 x 16 wave totals, so
+  // the whole scan waits at two barriers.  Order: a stable counting sort
+  // of the tiles by descending bit length of their pair counts (bucket
+  // 32 - bit length), ranked with wave ballots: per (r, wave, bucket) the
+  // count of matching lanes, scanned in (bucket, r, wave) order.
   constexpr int kB = 33;                     // order buckets: bit length 0..32
-  __shared__ uint32_t sh[16];
-  __shared__ uint32_t s_cnt[kB];
-  __shared__ uint32_t s_base[kB];
-  __shared__ uint32_t s_w[16][kB];
-  const int t = threadIdx.x, w = t >> 6;
-  uint32_t v[kR];
+  constexpr int kW = 16;                     // waves
+  __shared__ uint32_t s_wt[kR][kW];          // wave totals of the counts, then their exclusive scan
+  __shared__ uint32_t s_w[kB][kR][kW];       // lanes per (bucket, r, wave), then their exclusive scan
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  uint32_t v[kR], ex[kR];
 #pragma unroll
   for (int r = 0; r < kR; ++r) v[r] = r * 1024 + t < nT ? ranges[2 * (r * 1024 + t)] : 0u;
-  if (t < kB) s_cnt[t] = 0;
-  uint32_t carry = 0;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const uint32_t inc = wave_inclusive_scan(v[r]);
+    ex[r] = inc - v[r];
+    if (lane == 63) s_wt[r][w] = inc;
+  }
+  if (order != nullptr)
+    for (int k = t; k < kB * kR * kW; k += 1024) (&s_w[0][0][0])[k] = 0u;
+  __syncthreads();
+  if (t < 64) {
+    // exclusive scan of the 128 wave totals in (r, w) order: two per lane
+    const uint32_t a0 = (&s_wt[0][0])[2 * t], a1 = (&s_wt[0][0])[2 * t + 1];
+    const uint32_t inc = wave_inclusive_scan(a0 + a1);
+    (&s_wt[0][0])[2 * t] = inc - a0 - a1;
+    (&s_wt[0][0])[2 * t + 1] = inc - a1;
+  }
+  // bucket of each tile and its rank among the wave's lanes of that bucket
+  uint32_t bk[kR], below[kR];
+  if (order != nullptr) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const bool valid = r * 1024 + t < nT;
+      bk[r] = 32u - (v[r] != 0 ? 32u - uint32_t(__builtin_clz(v[r])) : 0u);
+      const uint64_t peers = match_bits<6>(bk[r], ballot(valid));
+      below[r] = uint32_t(count_below(peers));
+      if (valid && below[r] == 0) s_w[bk[r]][r][w] = uint32_t(__popcll(peers));
+    }
+  }
+  __syncthreads();
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
     const int i = r * 1024 + t;
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<1024, uint32_t>(v[r], sh, tot);
     if (i < nT) {
-      const uint32_t start = carry + ex;
+      const uint32_t start = s_wt[r][w] + ex[r];
       ranges[2 * i] = v[r] != 0 ? start : 0u;
       ranges[2 * i + 1] = v[r] != 0 ? start + v[r] : 0u;
     }
-    carry += tot;
   }
   if (order == nullptr) return;
-  // stable counting sort by descending bucket (bucket 0 = longest lists)
-  uint32_t bk[kR];
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    bk[r] = 32u - (v[r] != 0 ? 32u - uint32_t(__builtin_clz(v[r])) : 0u);
-    if (r * 1024 + t < nT) atomicAdd(&s_cnt[bk[r]], 1u);
-  }
-  __syncthreads();
-  if (t == 0) {
-    uint32_t run = 0;
-    for (int b = 0; b < kB; ++b) {
-      s_base[b] = run;
-      run += s_cnt[b];
+  // exclusive scan of the (bucket, r, wave) counts in that order: wave 0
+  // runs it, each lane over a contiguous run of the 33 x 128 entries
+  if (t < 64) {
+    constexpr int kN = kB * kR * kW, kPer = (kN + 63) / 64;
+    uint32_t* e = &s_w[0][0][0];
+    uint32_t sum = 0;
+    for (int k = 0; k < kPer; ++k) {
+      const int j = t * kPer + k;
+      sum += j < kN ? e[j] : 0u;
+    }
+    uint32_t run = wave_inclusive_scan(sum) - sum;
+    for (int k = 0; k < kPer; ++k) {
+      const int j = t * kPer + k;
+      if (j < kN) {
+        const uint32_t c = e[j];
+        e[j] = run;
+        run += c;
+      }
     }
   }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
     const int tile = r * 1024 + t;
-    const bool valid = tile < nT;
-    const uint32_t b = bk[r];
-    const uint64_t peers = match_bits<6>(b, ballot(valid));
-    const uint32_t below = uint32_t(count_below(peers));
-    if (t < 16 * kB) (&s_w[0][0])[t] = 0;
-    __syncthreads();
-    if (valid && below == 0) s_w[w][b] = uint32_t(__popcll(peers));
-    __syncthreads();
-    if (valid) {
-      uint32_t off = s_base[b] + below;
-      for (int k = 0; k < w; ++k) off += s_w[k][b];
-      order[off] = uint32_t(tile);
-    }
-    __syncthreads();
-    if (t < kB) {
-      uint32_t add = 0;
-      for (int k = 0; k < 16; ++k) add += s_w[k][t];
-      s_base[t] += add;
-    }
-    __syncthreads();
+    if (tile < nT) order[s_w[bk[r]][r][w] + below[r]] = uint32_t(tile);
   }
 }
 
