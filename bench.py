@@ -13,10 +13,11 @@ from the same scene instead of a drifting one.  Each block is bracketed by devic
 synchronisations; `value` = K / (sum of the blocks' wall times); every step
 is also bracketed by HIP events on the caller's stream (median reported).
 Inside the timed blocks HIP events on the stream the library launches on
-bracket the raster backward, the dominant kernel, whose roofline uses
-them (an event pair between two launches idles the stream for several
-microseconds, so nothing else is bracketed there); the step runs as a
-training loop runs it, without the per-tile processed counts.
+bracket one raster backward per step (the dominant kernel; the view
+rotates with the step and the block), whose roofline uses them: an event
+pair between two launches idles the stream for several microseconds, so
+nothing else is bracketed there.  The steps run as a training loop runs
+them, without the per-tile processed counts.
 A counting pass (one block with the raster backward's visit counter on,
 outside the timed region) gives the back-propagated (pixel, entry) pairs of
 the timed launches, the roofline's unit.  The other stages' times come from
@@ -381,12 +382,14 @@ def device_copy_GBps(nbytes=1 << 30, reps=10):
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
-def run_block(step, init, nsteps, timed_stages=None):
+def run_block(step, init, nsteps, timed_stages=None, timed_view=None):
     """`nsteps` training steps from the restored state `init` (restored
     before the clock starts), bracketed by device synchronisations; every
-    step bracketed by HIP events on the caller's stream.  Returns the
-    block's wall time (s), per-step event times (ms) and, with
-    timed_stages, the stage events."""
+    step bracketed by HIP events on the caller's stream.  With
+    timed_stages, those stages' launches are bracketed too (with
+    timed_view(i), only view timed_view(i)'s launch in step i).  Returns
+    the block's wall time (s), per-step event times (ms) and the stage
+    events."""
     import torch
     step.load_state(init)
     step.timer = {} if timed_stages is not None else None
@@ -395,13 +398,14 @@ def run_block(step, init, nsteps, timed_stages=None):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
+        step.timer_views = None if timed_view is None else {timed_view(i)}
         a.record(st)
         step.step()
         b.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timer, step.timer, step.timer_stages = step.timer, None, None
+    timer, step.timer, step.timer_stages, step.timer_views = step.timer, None, None, None
     return wall, [a.elapsed_time(b) for a, b in evs], timer
 
 
@@ -465,36 +469,44 @@ def main():
     # runs, with the raster backward's visit counter on; sizes per step
     log(f"[bench] counting block of {RESTORE_EVERY} steps")
     step.load_state(init)
-    step.visits = torch.zeros(1, dtype=torch.int64, device=step.device)
+    step.visits = torch.zeros(nv, dtype=torch.int64, device=step.device)
     step.record_tiles = True          # per-tile processed counts: M_proc
     sizes = []
+    visits_by = []                    # [cycle step][view]: back-propagated pairs of that launch
     for _ in range(RESTORE_EVERY):
         step.step()
         torch.cuda.synchronize()
+        visits_by.append([int(x) for x in step.visits.tolist()])
+        step.visits.zero_()
         views = [dict(V=int(step.vis_count[k].item()), M=vw.num_pairs,
                       M_proc=int(vw.tile_processed.to(torch.int64).sum().item()), P=vw.W * vw.H, T=vw.T)
                  for k, vw in enumerate(step.views)]
         sizes.append((views, int(step.union_count.item())))
-    visits = int(step.visits.item())
     step.visits = None
     step.record_tiles = False
-    visits_per_launch = visits / (RESTORE_EVERY * nv)
+    visits_per_launch = sum(map(sum, visits_by)) / (RESTORE_EVERY * nv)
     B_steps = [algorithmic_bytes(N, v, U) for v, U in sizes]
     B = float(np.mean([b[0] for b in B_steps]))
     B_stage = {k: float(np.mean([b[1][k] for b in B_steps])) for k in B_steps[0][1]}
 
     # timed blocks, restored before each
     log(f"[bench] timing {args.steps} steps in blocks of {RESTORE_EVERY}")
-    wall, step_ms, raster_ev = 0.0, [], {}
-    left = args.steps
+    # (one raster backward per step is bracketed, the view rotating with the
+    # step and the block, so the sampled launches cover every (step, view)
+    # of the cycle; their visits come from the counting block)
+    wall, step_ms, raster_ev, sampled_visits = 0.0, [], {}, []
+    left, blk = args.steps, 0
     while left > 0:
         k = min(RESTORE_EVERY, left)
-        w, ms, ev = run_block(step, init, k, timed_stages={"render_bwd"})
+        view_of = (lambda i, b=blk: (i + b) % nv)
+        w, ms, ev = run_block(step, init, k, timed_stages={"render_bwd"}, timed_view=view_of)
         wall += w
         step_ms += ms
         for name, pairs in ev.items():
             raster_ev.setdefault(name, []).extend(pairs)
+        sampled_visits += [visits_by[i][view_of(i)] for i in range(k)]
         left -= k
+        blk += 1
     ms_per_step = 1e3 * wall / args.steps
     steps_per_s = args.steps / wall
     raster = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in raster_ev.items()}
@@ -516,7 +528,9 @@ def main():
     launches.setdefault("render_fwd", len(stage_t["render_fwd"]))
     dom = max(("render_fwd", "render_bwd"), key=lambda k: raster.get(k, 0.0))
     kname = "k_render_bwd" if dom == "render_bwd" else "k_render_fwd"
-    ops = visits_per_launch * OPS_PER_VISIT[dom]
+    # the sampled backward launches' own pairs (the forward: the average)
+    vpl = float(np.mean(sampled_visits)) if dom == "render_bwd" else visits_per_launch
+    ops = vpl * OPS_PER_VISIT[dom]
     achieved = ops / (raster[dom] * 1e-3)
     wl = {2: "mid_1080p"}.get(args.config)
     valu = recorded_valu_issue(kname, wl) if wl else None
@@ -524,7 +538,7 @@ def main():
                 "unit": "Tops/s (32-bit VALU)", "frac": achieved / VALU_PEAK,
                 "traffic": recorded_traffic(kname, wl) if wl else None,
                 "avg_launch_ms": raster[dom], "launches": launches[dom], "ops_per_launch": ops,
-                "visits_per_launch": visits_per_launch, "ops_per_visit": OPS_PER_VISIT[dom],
+                "visits_per_launch": vpl, "ops_per_visit": OPS_PER_VISIT[dom],
                 "valu_issue_frac": (valu / (CUS * CLOCK * raster[dom] * 1e-3)) if valu else None}
 
     def hbm_frac(b, ms):

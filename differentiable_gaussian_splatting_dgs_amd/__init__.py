@@ -27,7 +27,7 @@ GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM, GS_OP_RASTER = 
 GS_OP_VIEW_OVERLAP, GS_OP_PACK, GS_OP_DENSIFY = 5, 6, 7
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
-GS_MAX_FUSED_VIEWS = 8
+GS_MAX_FUSED_VIEWS = 16
 GS_MAX_COUPLED_VIEWS = 65536
 GS_MAX_TILE_BLOCKS = 64
 GS_MAX_PARTITION_TILES = 1 << 21
@@ -426,8 +426,9 @@ class TrainStep:
     step (all views of the batch, then sparse Adam).
 
     Views cycle through three buffer sets (two for a batch of two).  The
-    last ndefer = min(views, 8) views own a screen-gradient buffer each; the
-    earlier ones alternate between two more.
+    last ndefer = min(views, max_fused_views) views (at most
+    GS_MAX_FUSED_VIEWS) own a screen-gradient buffer each; the earlier ones
+    alternate between two more.
     In ``step()`` view k + 1's preprocess and binning are issued on a second
     stream while view k renders, takes its loss and runs the raster backward
     on the caller's stream; the projection backward of an early view runs on
@@ -437,7 +438,8 @@ class TrainStep:
     one view's stages in order on the current stream."""
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
-                 pair_capacity=None, record_tiles=False, segment_len="auto", fuse_next_preprocess=True):
+                 pair_capacity=None, record_tiles=False, segment_len="auto", fuse_next_preprocess=True,
+                 max_fused_views=GS_MAX_FUSED_VIEWS):
         p = torch.as_tensor(params, dtype=torch.float32)
         assert p.ndim == 2 and p.shape[0] == 59
         self.device = torch.device(device)
@@ -448,8 +450,9 @@ class TrainStep:
         self.record_tiles = record_tiles
         self.timer = None        # optional: name -> list of (start, end) torch.cuda.Event pairs
         self.timer_stages = None  # optional: the stage names to time (None: all)
-        self.visits = None       # optional: device int64 scalar the raster backward adds its
-                                 # back-propagated (pixel, entry) count to
+        self.timer_views = None   # optional: the views whose raster backward is timed (None: all)
+        self.visits = None       # optional: device int64 [views]: view k's raster backward adds its
+                                 # back-propagated (pixel, entry) count to visits[k]
         # densification statistic (track_densify): per Gaussian the summed
         # |dL/d(u, v)| and the number of views it was visible in
         self.dens_accum = None
@@ -458,7 +461,8 @@ class TrainStep:
         # step() fuses into Adam (the last ndefer views), two alternating
         # for the earlier views
         nv = len(cameras)
-        self.ndefer = min(nv, GS_MAX_FUSED_VIEWS)
+        assert 1 <= max_fused_views <= GS_MAX_FUSED_VIEWS
+        self.ndefer = min(nv, int(max_fused_views))
         self.nfirst = nv - self.ndefer
         self.vis_count = torch.zeros(len(cameras), dtype=torch.int64, device=self.device)
         self.union_count = torch.zeros(1, dtype=torch.int64, device=self.device)
@@ -548,10 +552,11 @@ class TrainStep:
         return k - self.nfirst if k >= self.nfirst else self.ndefer + k % 2
 
     @contextlib.contextmanager
-    def _stage(self, name):
+    def _stage(self, name, view=None):
         """Bracket the enclosed launches with events on the current stream
         (the stream the library launches on) when timing is enabled."""
-        if self.timer is None or (self.timer_stages is not None and name not in self.timer_stages):
+        if self.timer is None or (self.timer_stages is not None and name not in self.timer_stages) or \
+                (view is not None and self.timer_views is not None and view not in self.timer_views):
             yield
             return
         a = torch.cuda.Event(enable_timing=True)
@@ -636,10 +641,10 @@ class TrainStep:
         # before the projection backward re-zeroes them)
         chain = not keep_grad2d and self.dens_accum is None
         pg = (self.params, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1], self.grads) if chain else None
-        with self._stage("render_bwd+project_bwd" if chain else "render_bwd"):
+        with self._stage("render_bwd+project_bwd" if chain else "render_bwd", k):
             gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
                           vw.dL, self.g2d[self._gcur], vw.order, self._split(k), self.seg[k], param_grads=pg,
-                          visits=self.visits)
+                          visits=None if self.visits is None else self.visits[k:k + 1])
         if self.dens_accum is not None:
             gs_densify_stats(self.g2d[self._gcur], self.vis_idx[k], self.vis_count[k:k + 1], self.n,
                              self.dens_accum, self.dens_denom)

@@ -8,7 +8,12 @@
 // exactly that order with far less traffic than a 45-bit radix sort of
 // all pairs:
 //   1. the visible list (ascending indices) is radix-sorted stably by the
-//      32 depth bits -- V elements, not M;
+//      32 depth bits -- V elements, not M.  Each visible Gaussian's compact
+//      record (index, tile rectangle, depth: 16 bytes) is gathered once, in
+//      ascending index order, and the sort carries its rank in that list;
+//      the last pass writes the records themselves in depth order, so the
+//      steps below read them contiguously instead of gathering 64-byte
+//      projection records at random twice;
 //   2. each Gaussian becomes one entry per super-tile (block of 8 x 8 or
 //      16 x 16 tiles) its tile rectangle meets, placed stably by super-tile,
 //      so every super-tile holds its entries in depth order;
@@ -209,20 +214,71 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
   }
 }
 
+// The depth sort's last pass: as k_scatter, but each item's compact record
+// crec[value] (gathered as the block loads its items, so the random reads
+// overlap the ranking) is written at its sorted place instead of the key
+// and value.
+__global__ __launch_bounds__(kRT) void k_scatter_rec(const uint32_t* __restrict__ kin,
+                                                     const uint32_t* __restrict__ vin,
+                                                     const uint4* __restrict__ crec, uint4* __restrict__ rout,
+                                                     const int64_t* count_dev, int shift,
+                                                     const uint32_t* __restrict__ H,
+                                                     const uint32_t* __restrict__ rowtot, int nb) {
+  __shared__ RankSmem sm;
+  __shared__ uint4 s_rec[kRB];
+  const int64_t count = *count_dev;
+  const int64_t bbase = int64_t(blockIdx.x) * kRB;
+  if (bbase >= count) return;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  uint32_t d[kRI], pos[kRI];
+  uint4 rec[kRI];
+  const int64_t base = bbase + int64_t(w) * kWaveItems;
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    const int64_t idx = base + it * 64 + lane;
+    const bool valid = idx < count;
+    d[it] = valid ? digit_of(kin[idx], shift) : 0u;
+    rec[it] = valid ? crec[vin[idx]] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  rank_block(d, base, count, H, rowtot, nb, sm, pos);
+#pragma unroll
+  for (int it = 0; it < kRI; ++it) {
+    if (base + it * 64 + lane < count) s_rec[pos[it]] = rec[it];
+  }
+  __syncthreads();
+  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
+  for (int j = t; j < nvalid; j += kRT) {
+    const uint4 e = s_rec[j];
+    const uint32_t dg = digit_of(e.w, shift);
+    rout[sm.gbase[dg] + (uint32_t(j) - sm.dstart[dg])] = e;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // pipeline kernels
 // ---------------------------------------------------------------------------
 
-// depth keys of the visible list (in ascending index order)
+// Visible rank r (ascending index order): depth key, the rank itself as
+// the sort's value, and the compact record (index, x0 | x1 << 16,
+// y0 | y1 << 16, depth bits) from the projection record's last word.
 __global__ __launch_bounds__(256) void k_depth_gather(const float4* __restrict__ proj,
                                                       const int32_t* __restrict__ vis,
                                                       const int64_t* __restrict__ vis_count,
-                                                      uint32_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+                                                      uint32_t* __restrict__ keys, uint32_t* __restrict__ vals,
+                                                      uint4* __restrict__ crec) {
   const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (r >= *vis_count) return;
   const int32_t g = vis[r];
-  keys[r] = __builtin_bit_cast(uint32_t, proj[4 * int64_t(g) + 3].x);
-  vals[r] = uint32_t(g);
+  const float4 q3 = proj[4 * int64_t(g) + 3];
+  const uint32_t d = __builtin_bit_cast(uint32_t, q3.x);
+  keys[r] = d;
+  vals[r] = uint32_t(r);
+  crec[r] = make_uint4(uint32_t(g), __builtin_bit_cast(uint32_t, q3.y), __builtin_bit_cast(uint32_t, q3.z), d);
+}
+
+// Tiles of a compact record's rectangle (0 for an empty one).
+__device__ __forceinline__ uint32_t rec_tiles(const uint4& e) {
+  return ((e.y >> 16) - (e.y & 0xFFFFu)) * ((e.z >> 16) - (e.z & 0xFFFFu));
 }
 
 // Duplication works on blocks of kDB consecutive depth ranks.
@@ -241,7 +297,7 @@ __device__ __forceinline__ int last_at_or_below(const uint32_t* off, uint32_t o)
 }
 
 // per-block sums of tiles_touched in depth order
-__global__ __launch_bounds__(kDT) void k_tilesum(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+__global__ __launch_bounds__(kDT) void k_tilesum(const uint4* __restrict__ srec,
                                                  const int64_t* __restrict__ vis_count,
                                                  int64_t* __restrict__ block_sums) {
   __shared__ int64_t sh[kDT / 64];
@@ -251,7 +307,7 @@ __global__ __launch_bounds__(kDT) void k_tilesum(const float4* __restrict__ proj
 #pragma unroll
   for (int k = 0; k < kDI; ++k) {
     const int64_t r = start + k;
-    if (r < V) s += __builtin_bit_cast(uint32_t, proj[4 * int64_t(order[r]) + 3].w);
+    if (r < V) s += rec_tiles(srec[r]);
   }
   int64_t tot;
   block_exclusive_scan<kDT, int64_t>(s, sh, tot);
@@ -264,7 +320,7 @@ __global__ __launch_bounds__(kDT) void k_tilesum(const float4* __restrict__ proj
 // Gaussians and their exclusive pair offsets go to LDS, then the block's
 // threads write its output range round-robin (coalesced), each locating
 // its Gaussian by binary search over the offsets.
-__global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+__global__ __launch_bounds__(kDT) void k_duplicate(const uint4* __restrict__ srec,
                                                    const int64_t* __restrict__ vis_count,
                                                    const int64_t* __restrict__ block_offsets, int32_t tiles_x,
                                                    const int64_t* __restrict__ m_eff, uint64_t* __restrict__ keys,
@@ -286,15 +342,14 @@ __global__ __launch_bounds__(kDT) void k_duplicate(const float4* __restrict__ pr
     const int64_t r = r0 + t * kDI + k;
     cnt[k] = 0;
     if (r < V) {
-      const uint32_t g = order[r];
-      const float4 q3 = proj[4 * int64_t(g) + 3];
-      const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
+      const uint4 e = srec[r];
+      const uint32_t rx = e.y, ry = e.z;
       const uint32_t x0 = rx & 0xFFFFu, x1 = rx >> 16;
-      cnt[k] = __builtin_bit_cast(uint32_t, q3.w);
+      cnt[k] = rec_tiles(e);
       s_rx[t * kDI + k] = x0 | ((x1 - x0) << 16);
       s_y0[t * kDI + k] = ry & 0xFFFFu;
-      s_dep[t * kDI + k] = __builtin_bit_cast(uint32_t, q3.x);
-      s_g[t * kDI + k] = g;
+      s_dep[t * kDI + k] = e.w;
+      s_g[t * kDI + k] = e.x;
     }
     s += cnt[k];
   }
@@ -360,7 +415,7 @@ struct StGrid {
 
 // Step a.  block_sums[b]: pairs of block b; stcnt[s][b]: its entries in
 // super-tile s (block 0 also clears the total slot stcnt[s][nbv]).
-__global__ __launch_bounds__(kDT) void k_count_st(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
+__global__ __launch_bounds__(kDT) void k_count_st(const uint4* __restrict__ srec,
                                                   const int64_t* __restrict__ vis_count, int nbv, StGrid sg,
                                                   int64_t* __restrict__ block_sums, uint32_t* __restrict__ stcnt) {
   __shared__ int64_t sh[kDT / 64];
@@ -376,11 +431,11 @@ __global__ __launch_bounds__(kDT) void k_count_st(const float4* __restrict__ pro
   for (int k = 0; k < kDI; ++k) {
     const int64_t r = r0 + t * kDI + k;
     if (r < V) {
-      const float4 q3 = proj[4 * int64_t(order[r]) + 3];
-      const uint32_t tiles = __builtin_bit_cast(uint32_t, q3.w);
+      const uint4 e = srec[r];
+      const uint32_t tiles = rec_tiles(e);
       s += tiles;
       if (tiles != 0) {
-        const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
+        const uint32_t rx = e.y, ry = e.z;
         const int a0 = int(rx & 0xFFFFu) >> sg.shift, a1 = (int((rx >> 16) - 1u) >> sg.shift) + 1;
         const int b0 = int(ry & 0xFFFFu) >> sg.shift, b1 = (int((ry >> 16) - 1u) >> sg.shift) + 1;
         atomicAdd(&s_cd[b0 * W + a0], 1);
@@ -462,8 +517,7 @@ __global__ __launch_bounds__(1024) void k_stage1_tail(int64_t* __restrict__ sums
 // stcnt[s][b] (entries of s in earlier blocks) + entries of s in earlier
 // chunks + rank.  Entry: Gaussian index, depth bits, clipped rectangle
 // x0 | (w - 1) << 4 | y0 << 8 | (h - 1) << 12 in tiles of the super-tile.
-__global__ __launch_bounds__(kDT) void k_dup_st(const float4* __restrict__ proj, const uint32_t* __restrict__ order,
-                                                const uint32_t* __restrict__ depth,
+__global__ __launch_bounds__(kDT) void k_dup_st(const uint4* __restrict__ srec,
                                                 const int64_t* __restrict__ vis_count,
                                                 const uint32_t* __restrict__ stcnt,
                                                 const uint32_t* __restrict__ st_start, int nbv, StGrid sg,
@@ -492,18 +546,17 @@ __global__ __launch_bounds__(kDT) void k_dup_st(const float4* __restrict__ proj,
     const int64_t r = r0 + t * kDI + k;
     cnt[k] = 0;
     if (r < V) {
-      const uint32_t g = order[r];
-      const float4 q3 = proj[4 * int64_t(g) + 3];
-      const uint32_t rx = __builtin_bit_cast(uint32_t, q3.y), ry = __builtin_bit_cast(uint32_t, q3.z);
-      if (__builtin_bit_cast(uint32_t, q3.w) != 0u) {
+      const uint4 e = srec[r];
+      const uint32_t rx = e.y, ry = e.z;
+      if (rec_tiles(e) != 0u) {
         const uint32_t a0 = (rx & 0xFFFFu) >> sg.shift, a1 = (((rx >> 16) - 1u) >> sg.shift) + 1u;
         const uint32_t b0 = (ry & 0xFFFFu) >> sg.shift, b1 = (((ry >> 16) - 1u) >> sg.shift) + 1u;
         cnt[k] = (a1 - a0) * (b1 - b0);
       }
       s_rx[t * kDI + k] = rx;
       s_ry[t * kDI + k] = ry;
-      s_dep[t * kDI + k] = depth[r];
-      s_g[t * kDI + k] = g;
+      s_dep[t * kDI + k] = e.w;
+      s_g[t * kDI + k] = e.x;
     }
     s += cnt[k];
   }
@@ -630,12 +683,12 @@ __global__ __launch_bounds__(256) void k_count_chunk(const uint32_t* __restrict_
 
 // Step c, second half: per super-tile (one block each), cc scanned over its
 // chunks for each local tile (exclusive, in place); each tile's pair count
-// to ranges[2 tile] (k_tile_ranges_order turns the counts into ranges).
+// to tcount[tile] (k_tile_ranges_order turns the counts into ranges).
 // 256 / (S x S) threads per tile, each scanning a contiguous run of the
 // chunks from the sum of the runs before it.
 __global__ __launch_bounds__(256) void k_scan_chunks(const uint32_t* __restrict__ chunk_base, StGrid sg,
                                                      const int64_t* __restrict__ m_eff, uint32_t* __restrict__ cc,
-                                                     uint32_t* __restrict__ ranges) {
+                                                     uint32_t* __restrict__ tcount) {
   __shared__ uint32_t s_sum[256];
   const int s = blockIdx.x, t = threadIdx.x;
   const int S = 1 << sg.shift, L = S * S, np = 256 / L;
@@ -673,30 +726,7 @@ __global__ __launch_bounds__(256) void k_scan_chunks(const uint32_t* __restrict_
     }
   }
   const int tx = (s % sg.sx) * S + (lt & (S - 1)), ty = (s / sg.sx) * S + (lt >> sg.shift);
-  if (part == 0 && tx < sg.tx && ty < sg.ty) ranges[2 * size_t(ty * sg.tx + tx)] = total;
-}
-
-// Tile counts (ranges[2 tile]) -> ranges [start, end) in tile-id order;
-// empty tiles [0, 0).  One workgroup (1024 threads).
-__device__ __forceinline__ void tile_ranges_block(int nT, uint32_t* __restrict__ ranges) {
-  __shared__ uint32_t sh[16];
-  __shared__ uint32_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < nT; base += 1024) {
-    const int i = base + int(threadIdx.x);
-    const uint32_t v = i < nT ? ranges[2 * i] : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<1024, uint32_t>(v, sh, tot);
-    if (i < nT) {
-      const uint32_t start = carry + ex;
-      ranges[2 * i] = v != 0 ? start : 0u;
-      ranges[2 * i + 1] = v != 0 ? start + v : 0u;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) carry += tot;
-    __syncthreads();
-  }
+  if (part == 0 && tx < sg.tx && ty < sg.ty) tcount[ty * sg.tx + tx] = total;
 }
 
 // 64 x 64 bit transpose across a wave: lane r holds row r (bit c = element
@@ -894,98 +924,99 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
   tile_order_block(ranges, nT, order);
 }
 
-// The exact path's last step, one workgroup: tile counts to ranges, then
-// (with `order`) the tiles' launch order from them.  Up to 8192 tiles the
-// counts stay in registers between the two (tile r * 1024 + t in thread t);
-// larger images take the two steps one after the other through memory.
-__global__ __launch_bounds__(1024) void k_tile_ranges_order(int nT, uint32_t* __restrict__ ranges,
-                                                            uint32_t* __restrict__ order) {
-  constexpr int kR = 8;
-  if (nT > kR * 1024) {
-    tile_ranges_block(nT, ranges);
-    __threadfence();        // the ranges just written, read back below by other waves
-    __syncthreads();
-    if (order != nullptr) tile_order_block(ranges, nT, order);
-    return;
+// The exact path's last step: tile counts to ranges [start, end) in tile-id
+// order (empty tiles [0, 0)) and, with `order`, the rasterisers' launch
+// order (as tile_order_block: a stable counting sort by descending bit
+// length of the counts).  Workgroup b takes tiles [b kSlice, (b + 1)
+// kSlice).  It first reads the counts of the tiles before its slice (their
+// pair sum: the slice's first start) and, for the order, every tile's
+// bucket (per bucket, the tiles in all and those before the slice), so no
+// workgroup waits on another; the slice is then scanned and ranked with
+// wave ballots, per (bucket, r, wave) in tile-id order.
+constexpr int kTR = 256;                     // threads
+constexpr int kTRR = 2;                      // tiles per thread
+constexpr int kSlice = kTR * kTRR;           // tiles per workgroup
+constexpr int kBk = 33;                      // order buckets: bit length 0..32
+
+__device__ __forceinline__ uint32_t order_bucket(uint32_t len) {  // 0 = longest lists
+  return 32u - (len != 0 ? 32u - uint32_t(__builtin_clz(len)) : 0u);
+}
+
+__global__ __launch_bounds__(kTR) void k_tile_ranges_order(int nT, const uint32_t* __restrict__ tcount,
+                                                           uint32_t* __restrict__ ranges,
+                                                           uint32_t* __restrict__ order) {
+  constexpr int kW = kTR / 64;
+  __shared__ uint32_t s_all[kBk], s_before[kBk];
+  __shared__ uint32_t s_cnt[kBk][kTRR][kW];  // lanes per (bucket, r, wave), then their first slots
+  __shared__ uint32_t sh[kW];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int s0 = int(blockIdx.x) * kSlice;
+  const bool want_order = order != nullptr;
+  if (t < kBk) {
+    s_all[t] = 0;
+    s_before[t] = 0;
   }
-  // Tile t = r * 1024 + threadIdx.x for r = 0..7.  Ranges: a wave-level
-  // exclusive scan per r, then one exchange of the 8 x 16 wave totals, so
-  // the whole scan waits at two barriers.  Order: a stable counting sort
-  // of the tiles by descending bit length of their pair counts (bucket
-  // 32 - bit length), ranked with wave ballots: per (r, wave, bucket) the
-  // count of matching lanes, scanned in (bucket, r, wave) order.
-  constexpr int kB = 33;                     // order buckets: bit length 0..32
-  constexpr int kW = 16;                     // waves
-  __shared__ uint32_t s_wt[kR][kW];          // wave totals of the counts, then their exclusive scan
-  __shared__ uint32_t s_w[kB][kR][kW];       // lanes per (bucket, r, wave), then their exclusive scan
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  uint32_t v[kR], ex[kR];
-#pragma unroll
-  for (int r = 0; r < kR; ++r) v[r] = r * 1024 + t < nT ? ranges[2 * (r * 1024 + t)] : 0u;
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const uint32_t inc = wave_inclusive_scan(v[r]);
-    ex[r] = inc - v[r];
-    if (lane == 63) s_wt[r][w] = inc;
-  }
-  if (order != nullptr)
-    for (int k = t; k < kB * kR * kW; k += 1024) (&s_w[0][0][0])[k] = 0u;
+  for (int k = t; k < kBk * kTRR * kW; k += kTR) (&s_cnt[0][0][0])[k] = 0;
   __syncthreads();
-  if (t < 64) {
-    // exclusive scan of the 128 wave totals in (r, w) order: two per lane
-    const uint32_t a0 = (&s_wt[0][0])[2 * t], a1 = (&s_wt[0][0])[2 * t + 1];
-    const uint32_t inc = wave_inclusive_scan(a0 + a1);
-    (&s_wt[0][0])[2 * t] = inc - a0 - a1;
-    (&s_wt[0][0])[2 * t + 1] = inc - a1;
-  }
-  // bucket of each tile and its rank among the wave's lanes of that bucket
-  uint32_t bk[kR], below[kR];
-  if (order != nullptr) {
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const bool valid = r * 1024 + t < nT;
-      bk[r] = 32u - (v[r] != 0 ? 32u - uint32_t(__builtin_clz(v[r])) : 0u);
-      const uint64_t peers = match_bits<6>(bk[r], ballot(valid));
-      below[r] = uint32_t(count_below(peers));
-      if (valid && below[r] == 0) s_w[bk[r]][r][w] = uint32_t(__popcll(peers));
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int i = r * 1024 + t;
-    if (i < nT) {
-      const uint32_t start = s_wt[r][w] + ex[r];
-      ranges[2 * i] = v[r] != 0 ? start : 0u;
-      ranges[2 * i + 1] = v[r] != 0 ? start + v[r] : 0u;
-    }
-  }
-  if (order == nullptr) return;
-  // exclusive scan of the (bucket, r, wave) counts in that order: wave 0
-  // runs it, each lane over a contiguous run of the 33 x 128 entries
-  if (t < 64) {
-    constexpr int kN = kB * kR * kW, kPer = (kN + 63) / 64;
-    uint32_t* e = &s_w[0][0][0];
-    uint32_t sum = 0;
-    for (int k = 0; k < kPer; ++k) {
-      const int j = t * kPer + k;
-      sum += j < kN ? e[j] : 0u;
-    }
-    uint32_t run = wave_inclusive_scan(sum) - sum;
-    for (int k = 0; k < kPer; ++k) {
-      const int j = t * kPer + k;
-      if (j < kN) {
-        const uint32_t c = e[j];
-        e[j] = run;
-        run += c;
+  uint32_t before = 0;
+  const int scan_end = want_order ? nT : s0;
+  for (int base = 0; base < scan_end; base += kTR) {
+    const int j = base + t;
+    const bool valid = j < nT;
+    const uint32_t c = valid ? tcount[j] : 0u;
+    const bool pre = base < s0;              // (kSlice is a multiple of kTR: chunks never straddle s0)
+    before += pre ? c : 0u;
+    if (want_order) {
+      const uint32_t b = order_bucket(c);
+      const uint64_t peers = match_bits<6>(b, ballot(valid));
+      if (valid && count_below(peers) == 0) {
+        const uint32_t k = uint32_t(__popcll(peers));
+        atomicAdd(&s_all[b], k);
+        if (pre) atomicAdd(&s_before[b], k);
       }
     }
   }
+  uint32_t carry;
+  block_exclusive_scan<kTR, uint32_t>(before, sh, carry);
+  uint32_t bk[kTRR], below[kTRR];
+#pragma unroll
+  for (int r = 0; r < kTRR; ++r) {
+    const int i = s0 + r * kTR + t;
+    const bool valid = i < nT;
+    const uint32_t v = valid ? tcount[i] : 0u;
+    uint32_t tot;
+    const uint32_t start = carry + block_exclusive_scan<kTR, uint32_t>(v, sh, tot);
+    carry += tot;
+    if (valid) {
+      ranges[2 * size_t(i)] = v != 0 ? start : 0u;
+      ranges[2 * size_t(i) + 1] = v != 0 ? start + v : 0u;
+    }
+    bk[r] = order_bucket(v);
+    below[r] = 0;
+    if (want_order) {
+      const uint64_t peers = match_bits<6>(bk[r], ballot(valid));
+      below[r] = uint32_t(count_below(peers));
+      if (valid && below[r] == 0) s_cnt[bk[r]][r][w] = uint32_t(__popcll(peers));
+    }
+  }
+  if (!want_order) return;
+  __syncthreads();
+  if (t < kBk) {
+    // tiles of longer buckets, then this bucket's tiles before the slice
+    uint32_t run = s_before[t];
+    for (int b = 0; b < t; ++b) run += s_all[b];
+    for (int r = 0; r < kTRR; ++r)
+      for (int k = 0; k < kW; ++k) {
+        const uint32_t c = s_cnt[t][r][k];
+        s_cnt[t][r][k] = run;
+        run += c;
+      }
+  }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int tile = r * 1024 + t;
-    if (tile < nT) order[s_w[bk[r]][r][w] + below[r]] = uint32_t(tile);
+  for (int r = 0; r < kTRR; ++r) {
+    const int i = s0 + r * kTR + t;
+    if (i < nT) order[s_cnt[bk[r]][r][w] + below[r]] = uint32_t(i);
   }
 }
 
@@ -994,11 +1025,14 @@ __global__ __launch_bounds__(1024) void k_tile_ranges_order(int nT, uint32_t* __
 // ---------------------------------------------------------------------------
 struct Ws {
   uint32_t *dkA, *dvA, *dkB, *dvB;   // depth sort ping-pong [n]
+  uint4* crec;                       // compact records [n], visible-rank order
+  uint4* srec;                       // the same, depth order
   uint32_t* H;                       // radix histograms [256][nb]
   uint32_t* rowtot;                  // [256]
   uint32_t* sttot;                   // [256], entries per super-tile
   uint32_t* st_start;                // [256], super-tile list starts
   uint32_t* chunk_base;              // [257], first chunk of each super-tile; number of chunks
+  uint32_t* tcount;                  // [kMaxT * kMaxT], pairs per tile
   int64_t* bsums;                    // per-block tile sums [nbv + 1]
   int64_t* m_dev;                    // pair count
   int64_t* m_eff;                    // pair count if within capacity, else 0
@@ -1027,11 +1061,14 @@ Ws carve(void* ws, int64_t n, int64_t cap, size_t* bytes = nullptr) {
   w.dvA = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.dkB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
   w.dvB = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(n)));
+  w.crec = reinterpret_cast<uint4*>(take(sizeof(uint4) * size_t(n)));
+  w.srec = reinterpret_cast<uint4*>(take(sizeof(uint4) * size_t(n)));
   w.H = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256 * size_t(nbh)));
   w.rowtot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
   w.sttot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
   w.st_start = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 256));
   w.chunk_base = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 257));
+  w.tcount = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * size_t(kMaxT) * kMaxT));
   w.bsums = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * size_t(nbv + 1)));
   w.m_dev = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
   w.m_eff = reinterpret_cast<int64_t*>(take(sizeof(int64_t)));
@@ -1096,13 +1133,18 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
   Ws w = carve(ws, n, pair_capacity);
   const float4* P = reinterpret_cast<const float4*>(proj);
   if (n > 0) {
-    k_depth_gather<<<unsigned((n + 255) / 256), 256, 0, st>>>(P, vis_idx, vis_count, w.dkA, w.dvA);
-    // stable LSD radix on the 32 depth bits: A -> B -> A -> B -> A
-    for (int pass = 0; pass < 4; ++pass) {
+    k_depth_gather<<<unsigned((n + 255) / 256), 256, 0, st>>>(P, vis_idx, vis_count, w.dkA, w.dvA, w.crec);
+    // stable LSD radix on the 32 depth bits: A -> B -> A -> B, then the
+    // records in depth order
+    for (int pass = 0; pass < 3; ++pass) {
       const bool even = (pass & 1) == 0;
       radix_pass<uint32_t>(even ? w.dkA : w.dkB, even ? w.dvA : w.dvB, even ? w.dkB : w.dkA,
                            even ? w.dvB : w.dvA, vis_count, 0, n, 8 * pass, w, st);
     }
+    const int nb = int(std::max<int64_t>(1, nblocks(n)));
+    k_upsweep<uint32_t><<<nb, kRT, 0, st>>>(w.dkB, vis_count, 0, 24, w.H, nb);
+    k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
+    k_scatter_rec<<<nb, kRT, 0, st>>>(w.dkB, w.dvB, w.crec, w.srec, vis_count, 24, w.H, w.rowtot, nb);
   }
   const int nbv = int(dup_blocks(n));
   int ns = 0;
@@ -1110,10 +1152,10 @@ hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vi
     // pair totals, entries per (super-tile, block)
     const StGrid sg = st_grid(tiles_x, tiles_y);
     ns = sg.sx * sg.sy;
-    k_count_st<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, nbv, sg, w.bsums, w.stcnt);
+    k_count_st<<<nbv, kDT, 0, st>>>(w.srec, vis_count, nbv, sg, w.bsums, w.stcnt);
     k_rowscan<<<unsigned(ns), kRT, 0, st>>>(w.stcnt, nbv + 1, w.sttot);
   } else if (nbv > 0) {
-    k_tilesum<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums);
+    k_tilesum<<<nbv, kDT, 0, st>>>(w.srec, vis_count, w.bsums);
   }
   // block offsets, M, the effective count; super-tile list starts and chunks
   k_stage1_tail<<<1, 1024, 0, st>>>(w.bsums, nbv, pair_capacity, w.m_dev, w.m_eff, num_pairs_dev,
@@ -1130,8 +1172,8 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
                                  uint64_t* keys, int32_t* vals, uint32_t* ranges, uint32_t* tile_order, void* ws,
                                  int64_t pair_capacity, hipStream_t st) {
   (void)vis_idx;
+  (void)proj;
   Ws w = carve(ws, n, pair_capacity);
-  const float4* P = reinterpret_cast<const float4*>(proj);
   const int64_t T = int64_t(tiles_x) * tiles_y;
   uint32_t* uvals = reinterpret_cast<uint32_t*>(vals);
   const int nbv = int(dup_blocks(n));
@@ -1152,10 +1194,10 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     uint32_t* e_g = reinterpret_cast<uint32_t*>(w.pk);
     uint32_t* e_d = e_g + pair_capacity;
     uint32_t* e_r = w.pv;
-    k_dup_st<<<nbv, kDT, 0, st>>>(P, w.dvA, w.dkA, vis_count, w.stcnt, w.st_start, nbv, sg, w.m_eff, e_g, e_d, e_r);
+    k_dup_st<<<nbv, kDT, 0, st>>>(w.srec, vis_count, w.stcnt, w.st_start, nbv, sg, w.m_eff, e_g, e_d, e_r);
     k_count_chunk<<<grid, 256, 0, st>>>(w.chunk_base, w.st_start, w.sttot, ns, e_r, sg, w.m_eff, w.cc);
-    k_scan_chunks<<<unsigned(ns), 256, 0, st>>>(w.chunk_base, sg, w.m_eff, w.cc, ranges);
-    k_tile_ranges_order<<<1, 1024, 0, st>>>(int(T), ranges, tile_order);
+    k_scan_chunks<<<unsigned(ns), 256, 0, st>>>(w.chunk_base, sg, w.m_eff, w.cc, w.tcount);
+    k_tile_ranges_order<<<unsigned((T + kSlice - 1) / kSlice), kTR, 0, st>>>(int(T), w.tcount, ranges, tile_order);
     k_expand<<<egrid, 256, 0, st>>>(w.chunk_base, w.st_start, w.sttot, ns, e_g, e_d, e_r, w.cc, ranges, sg, w.m_eff,
                                    keys, uvals);
     return hipGetLastError();
@@ -1171,7 +1213,7 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     uint32_t* bufv[2] = {uvals, w.pv};
     int cur = (passes & 1) ? 1 : 0;
     if (nbv > 0)
-      k_duplicate<<<nbv, kDT, 0, st>>>(P, w.dvA, vis_count, w.bsums, tiles_x, m_dev, bufk[cur], bufv[cur]);
+      k_duplicate<<<nbv, kDT, 0, st>>>(w.srec, vis_count, w.bsums, tiles_x, m_dev, bufk[cur], bufv[cur]);
     for (int pass = 0; pass < passes; ++pass) {
       radix_pass<uint64_t>(bufk[cur], bufv[cur], bufk[cur ^ 1], bufv[cur ^ 1], m_dev, M_host, bound,
                            32 + 8 * pass, w, st);

@@ -85,7 +85,7 @@ hipError_t launch_loss(const float* image, const float* target, int32_t width, i
 
 // --- sparse Adam (adam.hip) ---------------------------------------------------
 // Views whose projection backward is fused into the Adam pass.
-constexpr int kMaxFusedViews = 8;
+constexpr int kMaxFusedViews = 16;
 struct FusedViews {
   CamArgs cam[kMaxFusedViews];
   float* grad2d[kMaxFusedViews];

@@ -83,7 +83,7 @@ typedef struct gs_camera {
  * dL/d(u, v, A, B, C, opacity, r, g, b) then 3 unused */
 #define GS_GRAD2D_WORDS 12
 /* most views whose projection backward gs_project_bwd_adam fuses */
-#define GS_MAX_FUSED_VIEWS 8
+#define GS_MAX_FUSED_VIEWS 16
 /* most views gs_view_overlap couples in one call */
 #define GS_MAX_COUPLED_VIEWS 65536
 /* most tile blocks of gs_tile_partition / gs_pack_records, and most tiles

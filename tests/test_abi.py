@@ -103,8 +103,9 @@ def test_invalid_arguments_rejected_on_host():
     # fused projection backward + adam: too many views, a misaligned
     # screen-gradient buffer, a NULL buffer list
     cam.width = 64
-    cams = (gs.gs_camera * 9)(*([cam] * 9))
-    bufs = (C.c_void_p * 9)(*([16] * 9))
+    nmax = gs.GS_MAX_FUSED_VIEWS + 1
+    cams = (gs.gs_camera * nmax)(*([cam] * nmax))
+    bufs = (C.c_void_p * nmax)(*([16] * nmax))
     args = (P(16), P(16), P(16), P(16), 4, 4)
     scal = (C.c_float(1e-3), C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.1), C.c_float(0.1),
             P(256), 1 << 20, None)

@@ -164,12 +164,13 @@ def test_pipelined_step_matches_oracle(case):
         assert torch.equal(a.ranges, b.ranges), f"{case}/v{k} second-step ranges"
 
 
-@pytest.mark.parametrize("case", ["mid_cut", "small_cut", "capacity_cut"])
-def test_fused_step_matches_oracle(case):
+@pytest.mark.parametrize("case,max_fused", [("mid_cut", None), ("small_cut", None), ("capacity_cut", None),
+                                            ("capacity_cut", 8)])
+def test_fused_step_matches_oracle(case, max_fused):
     """TrainStep.step() as bench.py runs it: the projection backward of the
-    last (up to eight) views fused into the Adam pass, that of any earlier
-    view (capacity_cut: two of ten) accumulated into the gradient planes
-    first.  The update against the oracle's gradients (as check_adam),
+    last views (all of them, up to GS_MAX_FUSED_VIEWS; 8 in the last case)
+    fused into the Adam pass, that of any earlier view (capacity_cut with 8
+    fused: two of ten) accumulated into the gradient planes first.  The update against the oracle's gradients (as check_adam),
     screen-space buffers left zero; the union flags the pass leaves are the
     next step's first view's visibility (its preprocess of the updated
     rows)."""
@@ -177,8 +178,9 @@ def test_fused_step_matches_oracle(case):
     work = workload_case(case)
     p0 = work.params.copy()
     ref = oracle.step(work, dl_tol=DL_TOL)
-    step = gs.from_workload(work, record_tiles=True)
-    assert step.nfirst == max(0, len(work.cameras) - gs.GS_MAX_FUSED_VIEWS)
+    kw = {} if max_fused is None else dict(max_fused_views=max_fused)
+    step = gs.from_workload(work, record_tiles=True, **kw)
+    assert step.nfirst == max(0, len(work.cameras) - (max_fused or gs.GS_MAX_FUSED_VIEWS))
     step.step()
     torch.cuda.synchronize()
     U = int(step.union_count.item())
@@ -272,7 +274,7 @@ def test_render_bwd_parameter_mode_and_visit_count(case):
     work = workload_case(case)
     ref = oracle.step(work)
     step = gs.from_workload(work, record_tiles=True)
-    step.visits = torch.zeros(1, dtype=torch.int64, device="cuda")
+    step.visits = torch.zeros(len(work.cameras), dtype=torch.int64, device="cuda")
     total = 0
     for k, cam in enumerate(work.cameras):
         step.forward_view(k)
@@ -281,8 +283,9 @@ def test_render_bwd_parameter_mode_and_visit_count(case):
         torch.cuda.synchronize()
         cnt = oracle.composited_counts(work.params, cam).astype(np.int64)
         total += int(cnt.sum())
-        say(f"  {case}/v{k}: composited (pixel, entry) pairs {int(cnt.sum())}, GPU total {int(step.visits.item())}")
-        assert int(step.visits.item()) == total, f"{case}/v{k} visits"
+        say(f"  {case}/v{k}: composited (pixel, entry) pairs {int(cnt.sum())}, GPU {int(step.visits[k].item())}")
+        assert int(step.visits[k].item()) == int(cnt.sum()), f"{case}/v{k} visits"
+        assert int(step.visits.sum().item()) == total
     check_grad(f"{case} grads (render_bwd parameter mode)", step.grads.cpu().numpy(), ref["grads"], ref["mags"])
     for g2 in step.g2d:
         assert not g2.any().item(), "screen-space gradients not re-zeroed"
