@@ -10,9 +10,11 @@
 // current one is computed) and run a horizontal then a vertical 11-tap
 // pass over LDS: 168 horizontal runs of eight outputs (the 42 rows the
 // vertical pass needs), then one vertical run of four outputs per thread.
-//   k_ssim_fwd: five local moments (mu_x, mu_y, E[x^2], E[y^2], E[xy]) ->
-//     per-pixel SSIM and its partials wrt (mu_x, E[x^2], E[xy]); per-tile
-//     sums of SSIM and |x - y|.
+//   k_ssim_fwd: four local moments (mu_x, mu_y, E[x^2 + y^2], E[xy]: the
+//     variances enter SSIM only through sigma_x^2 + sigma_y^2, so one
+//     windowed map of x^2 + y^2 serves both) -> per-pixel SSIM and its
+//     partials wrt (mu_x, E[x^2], E[xy]); per-tile sums of SSIM and
+//     |x - y|.
 //   k_ssim_bwd: the transposed (= same, the window is symmetric) window
 //     applied to the three partial maps, combined into dL/dI with the L1
 //     subgradient (0 at 0).
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
                                                   int H, int tx, int ty, SsimWindow win, float* __restrict__ maps,
                                                   float* __restrict__ partial) {
   __shared__ __align__(16) float sxy[2][kSY][kSXP];
-  __shared__ __align__(16) float h[5][kSY][kHP];
+  __shared__ __align__(16) float h[4][kSY][kHP];
   __shared__ float sh[8];
   const int t = threadIdx.x;
   const size_t P = size_t(W) * H;
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
       const float* const src[2] = {img + nx.ch * P, tgt + nx.ch * P};
       stage_load<2>(src, W, H, nx.ox, nx.oy, st);
     }
-    // horizontal: row r, columns c0 .. c0 + 7 of the five moment maps
+    // horizontal: row r, columns c0 .. c0 + 7 of the four moment maps
     if (t < kTasksH) {
       const int r = t / (kLX / kRunH), c0 = (t % (kLX / kRunH)) * kRunH;
       float u[kRunH + 10], v[kRunH + 10], p[kRunH + 10], o[kRunH];
@@ -261,25 +263,21 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
       taps<kRunH>(win, v, o);
       store_run(&h[1][r][c0], o);
 #pragma unroll
-      for (int k = 0; k < kRunH + 10; ++k) p[k] = u[k] * u[k];
+      for (int k = 0; k < kRunH + 10; ++k) p[k] = fmaf(u[k], u[k], v[k] * v[k]);
       taps<kRunH>(win, p, o);
       store_run(&h[2][r][c0], o);
 #pragma unroll
-      for (int k = 0; k < kRunH + 10; ++k) p[k] = v[k] * v[k];
-      taps<kRunH>(win, p, o);
-      store_run(&h[3][r][c0], o);
-#pragma unroll
       for (int k = 0; k < kRunH + 10; ++k) p[k] = u[k] * v[k];
       taps<kRunH>(win, p, o);
-      store_run(&h[4][r][c0], o);
+      store_run(&h[3][r][c0], o);
     }
     __syncthreads();
     // vertical: column lx, rows r0 .. r0 + kRunV - 1
     float ssum = 0.0f, lsum = 0.0f;
     {
-      float m[5][kRunV];
+      float m[4][kRunV];
 #pragma unroll
-      for (int k = 0; k < 5; ++k) {
+      for (int k = 0; k < 4; ++k) {
         float col[kRunV + 10];
 #pragma unroll
         for (int j = 0; j < kRunV + 10; ++j) col[j] = h[k][r0 + j][lx];
@@ -290,10 +288,11 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
       for (int q = 0; q < kRunV; ++q) {
         const int y = oy + r0 + q;
         if (x >= W || y >= H) continue;
-        const float mx = m[0][q], my = m[1][q], exx = m[2][q], eyy = m[3][q], exy = m[4][q];
-        const float vx = exx - mx * mx, vy = eyy - my * my, cxy = exy - mx * my;
+        const float mx = m[0][q], my = m[1][q], ess = m[2][q], exy = m[3][q];
+        const float cxy = exy - mx * my;
         const float A1 = 2.0f * mx * my + kC1, A2 = 2.0f * cxy + kC2;
-        const float B1 = mx * mx + my * my + kC1, B2 = vx + vy + kC2;
+        const float mm = fmaf(mx, mx, my * my);
+        const float B1 = mm + kC1, B2 = (ess - mm) + kC2;
         // (hardware reciprocals: the loss feeds no discrete decision, and
         // their 1-ulp error is far inside its tolerance)
         const float iB2 = __builtin_amdgcn_rcpf(B2);
@@ -462,9 +461,9 @@ hipError_t launch_loss(const float* image, const float* target, int32_t width, i
   if (w_ssim != 0.0f) {
     const int tx = (width + kLX - 1) / kLX, ty = (height + kLY - 1) / kLY;
     const int64_t tiles = ssim_blocks(width, height);
-    // 45 KB / 40 KB of LDS per workgroup: three of each per CU
-    k_ssim_fwd<<<persistent_blocks(3, tiles), 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, partial);
-    k_ssim_bwd<<<persistent_blocks(3, tiles), 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, w_l1,
+    // 39 KB / 40 KB of LDS per workgroup: four of each per CU
+    k_ssim_fwd<<<persistent_blocks(4, tiles), 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, partial);
+    k_ssim_bwd<<<persistent_blocks(4, tiles), 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, w_l1,
                                                             w_ssim, dL_dimage, partial, loss);
   } else {
     const int64_t n3 = 3 * P;
