@@ -31,6 +31,7 @@ GS_MAX_FUSED_VIEWS = 16
 GS_MAX_COUPLED_VIEWS = 65536
 GS_MAX_TILE_BLOCKS = 64
 GS_MAX_PARTITION_TILES = 1 << 21
+GS_MAX_PLANE_ROWS = 1 << 30
 SEGMENT_LEN = 512    # list entries per segment of the split raster backward
 TILE = 16
 

@@ -214,7 +214,7 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
                         size_t workspace_bytes, void* stream) {
   gs::CamArgs c;
   CHECK(check_camera(cam, c));
-  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(n >= 0 && n < GS_MAX_PLANE_ROWS, "n = %lld out of range", (long long)n);
   REQUIRE(ld >= n, "ld < n");
   REQUIRE(vis_count != nullptr, "vis_count is NULL");
   if (n > 0) {
@@ -337,6 +337,7 @@ gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const
     CHECK(check_camera(param_grads->cam, c));
     REQUIRE(c.width == width && c.height == height, "param_grads->cam is %dx%d, the image %dx%d", c.width, c.height,
             width, height);
+    REQUIRE(n < GS_MAX_PLANE_ROWS, "n = %lld out of range with param_grads", (long long)n);
     REQUIRE(param_grads->ld >= n, "param_grads->ld < n");
     REQUIRE(param_grads->vis_count != nullptr, "param_grads->vis_count is NULL");
     if (n > 0)
@@ -355,7 +356,7 @@ gs_status gs_project_bwd(const float* params, int64_t n, int64_t ld, const gs_ca
                          const int64_t* vis_count, float* grad2d, float* grads, void* stream) {
   gs::CamArgs c;
   CHECK(check_camera(cam, c));
-  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(n >= 0 && n < GS_MAX_PLANE_ROWS, "n = %lld out of range", (long long)n);
   REQUIRE(ld >= n, "ld < n");
   REQUIRE(vis_count != nullptr, "vis_count is NULL");
   if (n > 0) {
@@ -371,7 +372,7 @@ gs_status gs_sparse_adam(float* params, float* grads, float* m, float* v, int64_
                          uint8_t* union_flags, int32_t* union_idx, int64_t* union_count, float lr, float beta1,
                          float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(n >= 0 && n < GS_MAX_PLANE_ROWS, "n = %lld out of range", (long long)n);
   REQUIRE(ld >= n, "ld < n");
   REQUIRE(union_count != nullptr, "union_count is NULL");
   if (n > 0) {
@@ -431,7 +432,7 @@ gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, i
     CHECK(check_camera(cams + w, fv.cam[w]));
     fv.grad2d[w] = grad2d[w];
   }
-  REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+  REQUIRE(n >= 0 && n < GS_MAX_PLANE_ROWS, "n = %lld out of range", (long long)n);
   REQUIRE(ld >= n, "ld < n");
   REQUIRE(union_count != nullptr, "union_count is NULL");
   if (n > 0) {

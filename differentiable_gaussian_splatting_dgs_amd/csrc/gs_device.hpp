@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gs_internal.h"
 
 namespace gs {
@@ -210,6 +212,24 @@ __device__ __forceinline__ void project(const float* __restrict__ p, const CamAr
     ok = (f.x1 - f.x0) > 0 && (f.y1 - f.y0) > 0;
   }
   f.visible = ok;
+}
+
+// Element (k, i) of a plane-major [planes][ld] fp32 array, given i as the
+// byte offset i * 4 (i < 2^30, so it fits 32 bits): the plane's start is the
+// same for every lane, so the access is one global load or store of a
+// scalar-register base plus a 32-bit lane offset, with no 64-bit address
+// arithmetic per lane.  (The base passes through an empty asm that pins it
+// to scalar registers, so the compiler cannot fold the lane offset into a
+// per-lane 64-bit address instead.)
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* plane_elem(T* base, int64_t ld, int k,
+                                                                          uint32_t off4) {
+  using G = __attribute__((address_space(1))) T;
+  using GB = typename std::conditional<std::is_const<T>::value, const __attribute__((address_space(1))) char,
+                                       __attribute__((address_space(1))) char>::type;
+  uint64_t pb = reinterpret_cast<uint64_t>(base + int64_t(k) * ld);
+  asm volatile("" : "+s"(pb));
+  return reinterpret_cast<G*>(reinterpret_cast<GB*>(pb) + off4);
 }
 
 // ---------------------------------------------------------------------------

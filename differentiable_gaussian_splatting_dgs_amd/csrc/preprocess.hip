@@ -21,9 +21,10 @@ __global__ __launch_bounds__(kPT) void k_preprocess(const float* __restrict__ pa
                                                     uint8_t* __restrict__ union_flags) {
   const int64_t i = int64_t(blockIdx.x) * kPT + threadIdx.x;
   if (i >= n) return;
+  const uint32_t off4 = uint32_t(i) << 2;
   float p[59];
 #pragma unroll
-  for (int k = 0; k < 59; ++k) p[k] = params[int64_t(k) * ld + i];
+  for (int k = 0; k < 59; ++k) p[k] = *plane_elem(params, ld, k, off4);
   float4 q[4];
   const bool visible = project_record(p, cam, q);
   float4* r = proj + 4 * i;

@@ -298,14 +298,15 @@ __global__ __launch_bounds__(256) void k_project_bwd(const float* __restrict__ p
   grad2d[3 * i] = z4;            // consumed: the buffer is zero again for the next view
   grad2d[3 * i + 1] = z4;
   grad2d[3 * i + 2] = z4;
+  const uint32_t off4 = uint32_t(i) << 2;
   float p[59];
 #pragma unroll
-  for (int k = 0; k < 59; ++k) p[k] = params[int64_t(k) * ld + i];
+  for (int k = 0; k < 59; ++k) p[k] = *plane_elem(params, ld, k, off4);
   const float grgb[3] = {gb4.z, gb4.w, gc4.x};
   float g[59];
   project_grads(p, cam, ga4.x, ga4.y, ga4.z, ga4.w, gb4.x, gb4.y, grgb, g);
 #pragma unroll
-  for (int k = 0; k < 59; ++k) grads[int64_t(k) * ld + i] += g[k];
+  for (int k = 0; k < 59; ++k) *plane_elem(grads, ld, k, off4) += g[k];
 }
 
 }  // namespace

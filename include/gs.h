@@ -90,6 +90,11 @@ typedef struct gs_camera {
  * gs_tile_partition splits */
 #define GS_MAX_TILE_BLOCKS 64
 #define GS_MAX_PARTITION_TILES (1 << 21)
+/* most Gaussians (n) of the calls that read or write the [59][ld] parameter
+ * planes (gs_preprocess, gs_project_bwd, gs_render_bwd with param_grads,
+ * gs_sparse_adam, gs_project_bwd_adam): their kernels address a row by a
+ * 32-bit byte offset; larger n is rejected with GS_ERR_INVALID_ARG */
+#define GS_MAX_PLANE_ROWS ((int64_t)1 << 30)
 
 typedef enum gs_op {
   GS_OP_PREPROCESS = 0,

@@ -96,10 +96,15 @@ def test_invalid_arguments_rejected_on_host():
     assert b"keys may be NULL" in lib.gs_last_error()
     assert lib.gs_bin_sort(P(16), 1, P(16), P(16), 64, 4128, None, P(16), 10, C.byref(m), P(16), None, P(256),
                            1 << 30, None) == 1
-    # adam: zero bias correction
+    # adam: zero bias correction; more rows than the plane offsets address
     assert lib.gs_sparse_adam(P(16), P(16), P(16), P(16), 4, 4, P(16), P(16), P(16), C.c_float(1e-3),
                               C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.0), C.c_float(0.1),
                               P(256), 1 << 20, None) == 1
+    big = gs.GS_MAX_PLANE_ROWS
+    assert lib.gs_sparse_adam(P(16), P(16), P(16), P(16), big, big, P(16), P(16), P(16), C.c_float(1e-3),
+                              C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.1), C.c_float(0.1),
+                              P(256), 1 << 40, None) == 1
+    assert b"out of range" in lib.gs_last_error()
     # fused projection backward + adam: too many views, a misaligned
     # screen-gradient buffer, a NULL buffer list
     cam.width = 64
