@@ -704,22 +704,28 @@ class TrainStep:
             if k < self.nfirst and proj_done[k % 2] is not None:
                 main.wait_event(proj_done[k % 2])          # buffer re-zeroed by view k - 2's projection
             self.backward_view(k, keep_grad2d=True)
-            raster_done = torch.cuda.Event()
-            raster_done.record(main)
-            if not (defer and k >= self.nfirst):
+            project = not (defer and k >= self.nfirst)
+            # the set's last reader is this raster backward (the projection
+            # backward reads params, not the set); an event marks it only
+            # when a later view of this batch takes the set (a later batch's
+            # side-stream work starts behind this batch's optimiser pass)
+            raster_done = None
+            if project or k + self.nsets < nv:
+                raster_done = torch.cuda.Event()
+                raster_done.record(main)
+            if project:
                 with torch.cuda.stream(self.gstream):
                     self.gstream.wait_event(raster_done)
                     self.project_view(k)
                     done = torch.cuda.Event()
                     done.record(self.gstream)
                 proj_done[k % 2] = done
-            self._free[k % self.nsets] = raster_done       # the set's last reader (the projection
-                                                           # backward reads params, not the set)
+            self._free[k % self.nsets] = raster_done if k + self.nsets < nv else None
             if k + 1 < nv:
                 with torch.cuda.stream(self.side):
                     if k == 0:
                         self.side.wait_event(first_done)       # the first view's binning goes first
-                    prev = self._free[(k + 1) % self.nsets]    # (possibly from an earlier step)
+                    prev = self._free[(k + 1) % self.nsets]
                     if prev is not None:
                         self.side.wait_event(prev)
                     self.prepare_view(k + 1, sync=False)

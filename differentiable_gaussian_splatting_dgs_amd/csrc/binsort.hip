@@ -960,19 +960,31 @@ __global__ __launch_bounds__(kTR) void k_tile_ranges_order(int nT, const uint32_
   __syncthreads();
   uint32_t before = 0;
   const int scan_end = want_order ? nT : s0;
-  for (int base = 0; base < scan_end; base += kTR) {
-    const int j = base + t;
-    const bool valid = j < nT;
-    const uint32_t c = valid ? tcount[j] : 0u;
-    const bool pre = base < s0;              // (kSlice is a multiple of kTR: chunks never straddle s0)
-    before += pre ? c : 0u;
-    if (want_order) {
-      const uint32_t b = order_bucket(c);
-      const uint64_t peers = match_bits<6>(b, ballot(valid));
-      if (valid && count_below(peers) == 0) {
-        const uint32_t k = uint32_t(__popcll(peers));
-        atomicAdd(&s_all[b], k);
-        if (pre) atomicAdd(&s_before[b], k);
+  // (eight chunks' counts loaded together, so their latencies overlap)
+  constexpr int kU = 8;
+  for (int base0 = 0; base0 < scan_end; base0 += kU * kTR) {
+    uint32_t cv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = base0 + u * kTR + t;
+      cv[u] = base0 + u * kTR < scan_end && j < nT ? tcount[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int base = base0 + u * kTR;
+      if (base >= scan_end) break;
+      const bool valid = base + t < nT;
+      const uint32_t c = cv[u];
+      const bool pre = base < s0;            // (kSlice is a multiple of kTR: chunks never straddle s0)
+      before += pre ? c : 0u;
+      if (want_order) {
+        const uint32_t b = order_bucket(c);
+        const uint64_t peers = match_bits<6>(b, ballot(valid));
+        if (valid && count_below(peers) == 0) {
+          const uint32_t k = uint32_t(__popcll(peers));
+          atomicAdd(&s_all[b], k);
+          if (pre) atomicAdd(&s_before[b], k);
+        }
       }
     }
   }

@@ -3,8 +3,10 @@
 // Odin summary page, "Background and motivation": a view reads and writes
 // only a sparse, view-dependent set of primitive indices).
 //
-// Reduce-then-scan, three launches: per-block counts, one-block scan of the
-// counts, per-block write.  No inter-workgroup waiting.
+// Reduce-then-scan in two launches: per-block counts, then a per-block
+// write whose offset is the sum of the counts before the block (each block
+// adds them itself; the last one also writes the total).  No
+// inter-workgroup waiting.
 #include "gs_scan.hpp"
 
 namespace gs {
@@ -45,36 +47,24 @@ __global__ __launch_bounds__(kCT) void k_count(const uint8_t* __restrict__ flags
   if (threadIdx.x == 0) block_counts[blockIdx.x] = total;
 }
 
-// One block of 1024 threads scans nb counts in place (exclusive) and writes
-// the total.
-__global__ __launch_bounds__(1024) void k_scan_counts(int32_t* __restrict__ counts, int nb,
-                                                       int64_t* __restrict__ total_out) {
-  __shared__ int64_t sh[16];
-  __shared__ int64_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < nb; base += 1024) {
-    const int i = base + int(threadIdx.x);
-    const int64_t v = i < nb ? counts[i] : 0;
-    int64_t tot;
-    const int64_t ex = block_exclusive_scan<1024, int64_t>(v, sh, tot);
-    if (i < nb) counts[i] = int32_t(carry + ex);
-    __syncthreads();
-    if (threadIdx.x == 0) carry += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *total_out = carry;
-}
-
+// Grid: max(1, blocks) workgroups; the last writes the total count.
 __global__ __launch_bounds__(kCT) void k_write(uint8_t* __restrict__ flags, int64_t n,
-                                               const int32_t* __restrict__ block_offsets,
-                                               int32_t* __restrict__ idx, int clear) {
+                                               const int32_t* __restrict__ block_counts,
+                                               int32_t* __restrict__ idx, int64_t* __restrict__ total_out,
+                                               int clear) {
   __shared__ int sh[kCT / 64];
+  __shared__ int64_t sh64[kCT / 64];
   const int64_t start = int64_t(blockIdx.x) * kCB + int64_t(threadIdx.x) * kCI;
+  // the counts of the blocks before this one
+  int64_t before = 0;
+  for (int j = int(threadIdx.x); j < int(blockIdx.x); j += kCT) before += block_counts[j];
   uint8_t f[kCI];
   const int c = load_flags(flags, n, start, f);
+  int64_t base;
+  block_exclusive_scan<kCT, int64_t>(before, sh64, base);
   int total;
-  int off = block_exclusive_scan<kCT>(c, sh, total) + block_offsets[blockIdx.x];
+  int off = block_exclusive_scan<kCT>(c, sh, total) + int(base);
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *total_out = base + total;
 #pragma unroll
   for (int k = 0; k < kCI; ++k)
     if (f[k]) idx[off++] = int32_t(start + k);
@@ -99,13 +89,8 @@ hipError_t launch_compact(uint8_t* flags, int64_t n, int32_t* idx, int64_t* coun
                           void* ws, hipStream_t st) {
   const int64_t nb = (n + kCB - 1) / kCB;
   int32_t* counts = static_cast<int32_t*>(ws);
-  if (nb == 0) {
-    k_scan_counts<<<1, 1024, 0, st>>>(counts, 0, count);
-    return hipGetLastError();
-  }
-  k_count<<<dim3(unsigned(nb)), kCT, 0, st>>>(flags, n, counts);
-  k_scan_counts<<<1, 1024, 0, st>>>(counts, int(nb), count);
-  k_write<<<dim3(unsigned(nb)), kCT, 0, st>>>(flags, n, counts, idx, clear_flags ? 1 : 0);
+  if (nb > 0) k_count<<<dim3(unsigned(nb)), kCT, 0, st>>>(flags, n, counts);
+  k_write<<<dim3(unsigned(nb > 0 ? nb : 1)), kCT, 0, st>>>(flags, n, counts, idx, count, clear_flags ? 1 : 0);
   return hipGetLastError();
 }
 
