@@ -22,6 +22,9 @@ __global__ __launch_bounds__(256) void k_clear(uint32_t* __restrict__ p, int n, 
   if (counters != nullptr && i < kCounterWords) counters[i] = 0u;
 }
 
+// kTiles: the per-tile count of processed list entries is recorded (it
+// needs the list position where each pixel stopped).
+template <bool kTiles>
 __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                                    const uint32_t* __restrict__ ranges,
                                                    const uint32_t* __restrict__ order, int64_t num_pairs, int W,
@@ -46,7 +49,8 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   const bool inside = px < W && py < H;
   float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
   uint32_t lastp = 0, read = end - start;
-  bool live = inside;       // still compositing
+  // lanes still compositing, as a wave mask (scalar registers)
+  uint64_t livem = __builtin_amdgcn_ballot_w64(inside);
 
   // split backward: lists longer than a segment record their state at the
   // segment boundaries they reach; lane k keeps the slot of record k
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   const uint32_t ul = uint32_t(lane);
   EntryRec cur = load_entry(proj, load_index(vals, start + ul, start + ul < end));
   int32_t gnext = load_index(vals, start + kChunk + ul, start + kChunk + ul < end);
-  for (uint32_t cs = start; cs < end && wave_any(live); cs += kChunk) {
+  for (uint32_t cs = start; cs < end && livem != 0; cs += kChunk) {
     if (ck_open && cs != start && ((cs - start) & seg_mask) == 0) {
       uint32_t slot = 0;
       if (lane == 0) slot = atomicAdd(pool_count, 1u);
@@ -100,15 +104,18 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
       const float hc = s_rec.d[k].x;
       const float dx = pxc - a.x, dy = pyc - a.y;
       const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
-      // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1
-      bool ok = live && !(power > 0.0f) && !(power < -5.6f);
-      if (!wave_any(ok)) continue;
+      // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1.
+      // (Decisions are kept as wave masks of direct comparisons, so none is
+      // turned into a per-lane value and back.)
+      const uint64_t okm = __builtin_amdgcn_ballot_w64(!(power > 0.0f)) &
+                           __builtin_amdgcn_ballot_w64(!(power < -5.6f)) & livem;
+      if (okm == 0) continue;
       const float4 c = s_rec.ac[2 * k + 1];   // opacity, r, g, b
       const float alpha = fminf(0.99f, c.x * pexp_core(power));
-      ok = ok && !(alpha < 1.0f / 255.0f);
+      const uint64_t okm2 = okm & __builtin_amdgcn_ballot_w64(!(alpha < 1.0f / 255.0f));
       const float nt = T * (1.0f - alpha);
-      const bool stop = ok && nt < 0.0001f;
-      const bool comp = ok && !stop;
+      const uint64_t stopm = okm2 & __builtin_amdgcn_ballot_w64(nt < 0.0001f);
+      const bool comp = __builtin_amdgcn_inverse_ballot_w64(okm2 & ~stopm);
       const uint32_t pos1 = pos0 + uint32_t(k);
       // a zero weight leaves the colour sums exactly as they are
       // (non-negative colours, sums from +0)
@@ -123,8 +130,8 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
       U2 = fmaf(c.w, wgt, U2);
       T = comp ? nt : T;
       lastp = comp ? pos1 : lastp;
-      read = stop ? pos1 : read;
-      live = live && !stop;
+      if constexpr (kTiles) read = __builtin_amdgcn_inverse_ballot_w64(stopm) ? pos1 : read;
+      livem &= ~stopm;
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     T_final[pix] = T;
     last[pix] = lastp;
   }
-  if (tile_processed != nullptr) {
+  if (kTiles) {
     const uint32_t rmax = wave_max_u32(inside ? read : 0u);
     if (lane == 0 && rmax != 0) atomicMax(tile_processed + tile, rmax);
   }
@@ -201,9 +208,14 @@ hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint3
   if (tile_processed != nullptr || counters != nullptr)
     k_clear<<<unsigned(std::max(tile_processed != nullptr ? (nT + 255) / 256 : 0, kCounterWords / 256)), 256, 0, st>>>(
         tile_processed, nT, counters);
-  k_render_fwd<<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
-                                              num_pairs, width, height, TX, nT, image, T_final, last,
-                                              tile_processed, split, seg_shift);
+  if (tile_processed != nullptr)
+    k_render_fwd<true><<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
+                                                      num_pairs, width, height, TX, nT, image, T_final, last,
+                                                      tile_processed, split, seg_shift);
+  else
+    k_render_fwd<false><<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges,
+                                                       tile_order, num_pairs, width, height, TX, nT, image, T_final,
+                                                       last, nullptr, split, seg_shift);
   return hipGetLastError();
 }
 
