@@ -112,17 +112,19 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint32_t pos0 = uint32_t(cs) - start;
+    // chunk entry k lies before the lane's last composited one when k < klim
+    // (list positions < 2^31)
+    const int32_t klim = int32_t(lastp) - int32_t(pos0);
     while (active != 0) {
       const int k = 63 - __builtin_clzll(active);      // back to front
       active &= ~(1ull << k);
-      const float4 a = s_rec.ac[2 * k];
-      const float hc = s_rec.d[k].x;
-      const uint32_t kpos = pos0 + uint32_t(k);
+      const float4 a = s_rec.r[k].a;
+      const float hc = s_rec.r[k].d.x;
       const float dx = pxc - a.x, dy = pyc - a.y;
       const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
-      bool ok = kpos < lastp && !(power > 0.0f) && !(power < -5.6f);
+      bool ok = k < klim && !(power > 0.0f) && !(power < -5.6f);
       if (!wave_any(ok)) continue;
-      const float4 c = s_rec.ac[2 * k + 1];   // opacity, r, g, b
+      const float4 c = s_rec.r[k].c;   // opacity, r, g, b
       const float e = pexp_core(power);
       const float araw = c.x * e;
       const float alpha = fminf(0.99f, araw);
@@ -181,8 +183,8 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       if (kk >= 0 && fc < 9) {
         const float* acc = s_acc + kk * kAcc;
         const float x = acc[2 * fc] + acc[2 * fc + 1];
-        const float4 a = s_rec.ac[2 * kk];
-        const float2 d = s_rec.d[kk];   // -C/2, index bits
+        const float4 a = s_rec.r[kk].a;
+        const float2 d = s_rec.r[kk].d;   // -C/2, index bits
         const float m1 = fc == 0 ? -2.0f * a.z : (fc == 1 ? -2.0f * d.x : fk);
         // the mean gradients also take the other mean sum (lanes 0 and 1)
         const float gval = fc < 2 ? fmaf(m1, x, -a.w * (acc[2 * (fc ^ 1)] + acc[2 * (fc ^ 1) + 1])) : m1 * x;

@@ -122,14 +122,17 @@ __device__ __forceinline__ float pexp_core(float x) {
   return ldexpf(p, static_cast<int>(kf));
 }
 
-// A chunk's Gaussians as the rasterisers read them from LDS, 40 bytes per
-// entry: ac[2 k] = (u, v, -A/2, -B) and ac[2 k + 1] = (opacity, r, g, b)
-// from one address, d[k] = (-C/2, Gaussian index bits).  A visit reads
-// ac[2 k] and d[k].x for the exponent, then ac[2 k + 1] (uniform LDS
-// broadcasts).
+// A chunk's Gaussians as the rasterisers read them from LDS, one 48-byte
+// record per entry: a = (u, v, -A/2, -B), c = (opacity, r, g, b),
+// d = (-C/2, Gaussian index bits).  A visit reads a and d.x for the
+// exponent, then c: uniform LDS broadcasts from one address register (one
+// base, immediate offsets).
+struct LdsRec {
+  float4 a, c;
+  float2 d, pad;
+};
 struct LdsRecs {
-  float4 ac[2 * kChunk];
-  float2 d[kChunk];
+  LdsRec r[kChunk];
 };
 
 // Any lane of the wave true (the predicate's ballot, tested in scalar
@@ -208,9 +211,9 @@ __device__ __forceinline__ bool ellipse_misses(float u, float v, float A, float 
 __device__ __forceinline__ bool stage_entry(const EntryRec& r, float qx, float qy, LdsRecs& s_rec, int lane) {
   bool hit = false;
   if (r.g >= 0) {
-    s_rec.ac[2 * lane] = make_float4(r.q0.x, r.q0.y, -0.5f * r.q0.z, -r.q0.w);
-    s_rec.ac[2 * lane + 1] = make_float4(r.q1.y, r.q1.z, r.q1.w, r.b);
-    s_rec.d[lane] = make_float2(-0.5f * r.q1.x, __builtin_bit_cast(float, r.g));
+    s_rec.r[lane].a = make_float4(r.q0.x, r.q0.y, -0.5f * r.q0.z, -r.q0.w);
+    s_rec.r[lane].c = make_float4(r.q1.y, r.q1.z, r.q1.w, r.b);
+    s_rec.r[lane].d = make_float2(-0.5f * r.q1.x, __builtin_bit_cast(float, r.g));
     const float u = r.q0.x, v = r.q0.y;
     hit = u + r.ex >= qx && u - r.ex <= qx + 7.0f && v + r.ey >= qy && v - r.ey <= qy + 7.0f;
     if (hit && r.ex < 1.0e30f)

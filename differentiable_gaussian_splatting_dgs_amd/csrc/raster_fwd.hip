@@ -100,8 +100,8 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     while (active != 0) {
       const int k = __builtin_ctzll(active);
       active &= active - 1;
-      const float4 a = s_rec.ac[2 * k];
-      const float hc = s_rec.d[k].x;
+      const float4 a = s_rec.r[k].a;
+      const float hc = s_rec.r[k].d.x;
       const float dx = pxc - a.x, dy = pyc - a.y;
       const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
       // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1.
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
       const uint64_t okm = __builtin_amdgcn_ballot_w64(!(power > 0.0f)) &
                            __builtin_amdgcn_ballot_w64(!(power < -5.6f)) & livem;
       if (okm == 0) continue;
-      const float4 c = s_rec.ac[2 * k + 1];   // opacity, r, g, b
+      const float4 c = s_rec.r[k].c;   // opacity, r, g, b
       const float alpha = fminf(0.99f, c.x * pexp_core(power));
       const uint64_t okm2 = okm & __builtin_amdgcn_ballot_w64(!(alpha < 1.0f / 255.0f));
       const float nt = T * (1.0f - alpha);
