@@ -229,6 +229,9 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
   __shared__ __align__(16) float sxy[2][kSY][kSXP];
   __shared__ __align__(16) float h[4][kSY][kHP];
   __shared__ float sh[8];
+  // issue priority over the next view's binning sharing the CUs (this
+  // kernel is on the step's critical path)
+  __builtin_amdgcn_s_setprio(2);
   const int t = threadIdx.x;
   const size_t P = size_t(W) * H;
   const int ntiles = 3 * tx * ty;
@@ -324,6 +327,7 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img,
                                                   const float* __restrict__ partial, float* __restrict__ loss) {
   __shared__ __align__(16) float sm[3][kSY][kSXP];
   __shared__ __align__(16) float h[3][kSY][kHP];   // (the last block reuses it for the fp64 reduction)
+  __builtin_amdgcn_s_setprio(2);   // (as the forward)
   const int t = threadIdx.x;
   const size_t P = size_t(W) * H;
   const float inv = 1.0f / (3.0f * float(P));

@@ -212,6 +212,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
                                                    unsigned long long* __restrict__ visits) {
   __shared__ LdsRecs s_rec;
   __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
+  __builtin_amdgcn_s_setprio(kRasterPrio);   // (as the forward)
   const SplitLayout sl = split_layout(W, H);
   const SplitState sp = split_state(const_cast<void*>(split), sl);
   const int lane = threadIdx.x;

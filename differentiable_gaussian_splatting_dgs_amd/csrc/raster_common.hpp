@@ -17,6 +17,10 @@ namespace gs {
 
 constexpr int kChunk = 64;
 
+// Wave issue priority of the rasterisers (s_setprio, 0..3; other kernels
+// run at 0).
+constexpr int kRasterPrio = 2;
+
 // Waves (one per quarter) per tile.
 constexpr int kWPT = 4;
 

@@ -33,6 +33,10 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
                                                    uint32_t* __restrict__ tile_processed, void* split,
                                                    int seg_shift) {
   __shared__ LdsRecs s_rec;
+  // issue priority over waves of other kernels sharing the CU (the next
+  // view's binning on the side stream): this kernel is issue-bound and on
+  // the step's critical path
+  __builtin_amdgcn_s_setprio(kRasterPrio);
   int q0;
   const int tile = order_tile(order, nT, q0);
   if (tile < 0) return;
