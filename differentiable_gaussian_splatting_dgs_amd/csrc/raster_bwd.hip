@@ -58,16 +58,31 @@ __device__ __forceinline__ float half_row_sum(float v) {
   return v;
 }
 
-// Sums of nine per-lane values over the wave, folded so each fold serves
-// several values: the two 8-lane halves of q0 rows 0..3 end with the half
-// totals of v0, v2, v1, v3; of q1 rows with v4, v6, v5, v7; of q2 row 0
-// with v8.
+// The wave's total of v in lane 63 (other lanes: partial sums): half-row
+// sums, row sums (mirror), then each row adds the last lane of the row
+// before it (row_bcast:15: row 3 holds rows 2 + 3, lane 31 rows 0 + 1),
+// and rows 2 and 3 add lane 31 (row_bcast:31).  (Every row takes part in
+// the two broadcasts, so each is one fused add; what rows 0 and 1 end with
+// is not used.)
+__device__ __forceinline__ float wave_total_lane63(float v) {
+  v = half_row_sum(v);
+  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x140, 0xF, 0xF, false));   // row_mirror
+  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x142, 0xF, 0xF, false));   // row_bcast:15
+  v += f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x143, 0xF, 0xF, false));   // row_bcast:31
+  return v;
+}
+
+// Sums of nine per-lane values over the wave.  The first eight are folded
+// so each fold serves several values: the two 8-lane halves of q0 rows
+// 0..3 end with the half totals of v0, v2, v1, v3; of q1 rows with v4, v6,
+// v5, v7.  The ninth has no partner and takes the plain DPP reduction
+// (six steps, against two folds with a zero register plus three steps).
 __device__ __forceinline__ void wave_sum9(const float v[9], float& q0, float& q1, float& q2) {
   const float r0 = fold32(v[0], v[1]), r1 = fold32(v[2], v[3]), r2 = fold32(v[4], v[5]);
-  const float r3 = fold32(v[6], v[7]), r4 = fold32(v[8], 0.0f);
+  const float r3 = fold32(v[6], v[7]);
   q0 = half_row_sum(fold16(r0, r1));
   q1 = half_row_sum(fold16(r2, r3));
-  q2 = half_row_sum(fold16(r4, 0.0f));
+  q2 = wave_total_lane63(v[8]);
 }
 
 // One pass of a quarter's list positions [lo, hi), back to front, from the
@@ -82,8 +97,8 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
   const int lane = threadIdx.x;
   // lanes 0, 8, 16, ..., 56 (row r = lane / 16, half h = lane / 8 % 2)
   // store the half sums: row r of the folded sums q0 / q1 carries sum
-  // (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r] (q2, row 0: sum 8); half sum h of
-  // sum j sits at 2 j + h of the entry's slot
+  // (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]; half sum h of sum j sits at 2 j + h
+  // of the entry's slot.  Lane 63 stores sum 8 whole at 16 (17 stays 0)
   const int row = lane >> 4;
   const int comp0 = ((row & 1) << 1) | (row >> 1);
   const int half = (lane >> 3) & 1;
@@ -161,8 +176,8 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
         float* acc = s_acc + k * kAcc + half;
         acc[2 * comp0] = q0s;
         acc[8 + 2 * comp0] = q1s;
-        if (lane < 16) acc[16] = q2s;
       }
+      if (lane == 63) s_acc[k * kAcc + 16] = q2s;
       written |= 1ull << k;
     }
     // the chunk's entries leave four at a time, one 16-lane row each (lane
@@ -213,6 +228,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   __shared__ LdsRecs s_rec;
   __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
   __builtin_amdgcn_s_setprio(kRasterPrio);   // (as the forward)
+  s_acc[threadIdx.x * kAcc + 17] = 0.0f;     // the unused half of sum 8
   const SplitLayout sl = split_layout(W, H);
   const SplitState sp = split_state(const_cast<void*>(split), sl);
   const int lane = threadIdx.x;

@@ -22,6 +22,101 @@ __global__ __launch_bounds__(256) void k_clear(uint32_t* __restrict__ p, int n, 
   if (counters != nullptr && i < kCounterWords) counters[i] = 0u;
 }
 
+// Compositing state of a quarter's 64 pixels (one per lane).
+struct FwdState {
+  float T, C0, C1, C2;
+  uint32_t lastp, read;
+  uint64_t livem;           // lanes still compositing, as a wave mask (scalar registers)
+  int nck;                  // states recorded
+  uint32_t slotv;           // lane k: the slot of record k
+  float U0, U1, U2;         // colour composited in the current segment
+};
+
+// The quarter's list [start, end) front to back until every pixel has
+// stopped.  kRec: the list is longer than a segment and records its state
+// at the segment boundaries it reaches (only then are the segment colours
+// U summed: a list that records nothing leaves them unused).  kTiles: the
+// list position where each pixel stopped is kept (per-tile processed
+// counts).
+template <bool kTiles, bool kRec>
+__device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
+                                         uint32_t start, uint32_t end, float qx, float qy, float pxc, float pyc,
+                                         const SplitLayout& sl, const SplitState& sp, uint32_t seg_mask,
+                                         uint32_t qid, uint32_t pool, LdsRecs& s_rec, FwdState& st) {
+  const int lane = threadIdx.x;
+  uint32_t* const pool_count = sp.counters + 32 * pool;   // slots taken, items listed
+  bool ck_open = kRec;
+  const uint32_t ul = uint32_t(lane);
+  EntryRec cur = load_entry(proj, load_index(vals, start + ul, start + ul < end));
+  int32_t gnext = load_index(vals, start + kChunk + ul, start + kChunk + ul < end);
+  for (uint32_t cs = start; cs < end && st.livem != 0; cs += kChunk) {
+    if (kRec && ck_open && cs != start && ((cs - start) & seg_mask) == 0) {
+      uint32_t slot = 0;
+      if (lane == 0) slot = atomicAdd(pool_count, 1u);
+      slot = __builtin_amdgcn_readfirstlane(slot);
+      if (slot < uint32_t(sl.pool_slots)) {
+        slot += pool * uint32_t(sl.pool_slots);
+        // T before entry cs - start, and the colour the segment now ending added
+        sp.ck[size_t(slot) * 64 + lane] = make_float4(st.T, st.U0, st.U1, st.U2);
+        if (lane == 0) sp.owner[slot] = (qid << 5) | uint32_t(st.nck);
+        st.slotv = lane == st.nck ? slot : st.slotv;
+        st.U0 = st.U1 = st.U2 = 0.0f;
+        ++st.nck;
+        ck_open = st.nck < kCkSeg;
+      } else {
+        ck_open = false;   // pool exhausted: the segments from here on stay one
+      }
+    }
+    const EntryRec nxt = load_entry(proj, gnext);
+    const uint32_t j2 = cs + 2 * kChunk + ul;
+    gnext = load_index(vals, j2, j2 < end);
+    const bool hit = stage_entry(cur, qx, qy, s_rec, lane);
+    cur = nxt;
+    uint64_t active = __ballot(hit);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t pos0 = cs - start + 1;   // list position + 1 of the chunk's entry 0
+    while (active != 0) {
+      const int k = __builtin_ctzll(active);
+      active &= active - 1;
+      const float4 a = s_rec.r[k].a;
+      const float hc = s_rec.r[k].d.x;
+      const float dx = pxc - a.x, dy = pyc - a.y;
+      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
+      // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1.
+      // (Decisions are kept as wave masks of direct comparisons, so none is
+      // turned into a per-lane value and back.)
+      const uint64_t okm = __builtin_amdgcn_ballot_w64(!(power > 0.0f)) &
+                           __builtin_amdgcn_ballot_w64(!(power < -5.6f)) & st.livem;
+      if (okm == 0) continue;
+      const float4 c = s_rec.r[k].c;   // opacity, r, g, b
+      const float alpha = fminf(0.99f, c.x * pexp_core(power));
+      const uint64_t okm2 = okm & __builtin_amdgcn_ballot_w64(!(alpha < 1.0f / 255.0f));
+      const float nt = st.T * (1.0f - alpha);
+      const uint64_t stopm = okm2 & __builtin_amdgcn_ballot_w64(nt < 0.0001f);
+      const bool comp = __builtin_amdgcn_inverse_ballot_w64(okm2 & ~stopm);
+      const uint32_t pos1 = pos0 + uint32_t(k);
+      // a zero weight leaves the colour sums exactly as they are
+      // (non-negative colours, sums from +0)
+      const float wgt = comp ? alpha * st.T : 0.0f;
+      st.C0 = fmaf(c.y, wgt, st.C0);
+      st.C1 = fmaf(c.z, wgt, st.C1);
+      st.C2 = fmaf(c.w, wgt, st.C2);
+      if constexpr (kRec) {
+        st.U0 = fmaf(c.y, wgt, st.U0);
+        st.U1 = fmaf(c.z, wgt, st.U1);
+        st.U2 = fmaf(c.w, wgt, st.U2);
+      }
+      st.T = comp ? nt : st.T;
+      st.lastp = comp ? pos1 : st.lastp;
+      if constexpr (kTiles) st.read = __builtin_amdgcn_inverse_ballot_w64(stopm) ? pos1 : st.read;
+      st.livem &= ~stopm;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // kTiles: the per-tile count of processed list entries is recorded (it
 // needs the list position where each pixel stopped).
 template <bool kTiles>
@@ -51,10 +146,15 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   const int px = x0 + (q0 & 1) * 8 + (lane & 7), py = y0 + (q0 >> 1) * 8 + (lane >> 3);
   const float pxc = float(px) + 0.5f, pyc = float(py) + 0.5f;
   const bool inside = px < W && py < H;
-  float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
-  uint32_t lastp = 0, read = end - start;
-  // lanes still compositing, as a wave mask (scalar registers)
-  uint64_t livem = __builtin_amdgcn_ballot_w64(inside);
+  FwdState st;
+  st.T = 1.0f;
+  st.C0 = st.C1 = st.C2 = 0.0f;
+  st.lastp = 0;
+  st.read = end - start;
+  st.livem = __builtin_amdgcn_ballot_w64(inside);
+  st.nck = 0;
+  st.slotv = 0;
+  st.U0 = st.U1 = st.U2 = 0.0f;
 
   // split backward: lists longer than a segment record their state at the
   // segment boundaries they reach; lane k keeps the slot of record k
@@ -64,96 +164,28 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   const bool rec = split != nullptr && end - start > seg_mask + 1u;
   const uint32_t qid = uint32_t(tile) * kWPT + uint32_t(q0);
   const uint32_t pool = blockIdx.x % kPools;
-  uint32_t* const pool_count = sp.counters + 32 * pool;   // slots taken, items listed
-  int nck = 0;
-  bool ck_open = rec;
-  uint32_t slotv = 0;
-  float U0 = 0.0f, U1 = 0.0f, U2 = 0.0f;   // colour composited in the current segment
-
-  const uint32_t ul = uint32_t(lane);
-  EntryRec cur = load_entry(proj, load_index(vals, start + ul, start + ul < end));
-  int32_t gnext = load_index(vals, start + kChunk + ul, start + kChunk + ul < end);
-  for (uint32_t cs = start; cs < end && livem != 0; cs += kChunk) {
-    if (ck_open && cs != start && ((cs - start) & seg_mask) == 0) {
-      uint32_t slot = 0;
-      if (lane == 0) slot = atomicAdd(pool_count, 1u);
-      slot = __builtin_amdgcn_readfirstlane(slot);
-      if (slot < uint32_t(sl.pool_slots)) {
-        slot += pool * uint32_t(sl.pool_slots);
-        // T before entry cs - start, and the colour the segment now ending added
-        sp.ck[size_t(slot) * 64 + lane] = make_float4(T, U0, U1, U2);
-        if (lane == 0) sp.owner[slot] = (qid << 5) | uint32_t(nck);
-        slotv = lane == nck ? slot : slotv;
-        U0 = U1 = U2 = 0.0f;
-        ++nck;
-        ck_open = nck < kCkSeg;
-      } else {
-        ck_open = false;   // pool exhausted: the segments from here on stay one
-      }
-    }
-    const EntryRec nxt = load_entry(proj, gnext);
-    const uint32_t j2 = cs + 2 * kChunk + ul;
-    gnext = load_index(vals, j2, j2 < end);
-    const bool hit = stage_entry(cur, qx, qy, s_rec, lane);
-    cur = nxt;
-    uint64_t active = __ballot(hit);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint32_t pos0 = cs - start + 1;   // list position + 1 of the chunk's entry 0
-    while (active != 0) {
-      const int k = __builtin_ctzll(active);
-      active &= active - 1;
-      const float4 a = s_rec.r[k].a;
-      const float hc = s_rec.r[k].d.x;
-      const float dx = pxc - a.x, dy = pyc - a.y;
-      const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
-      // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1.
-      // (Decisions are kept as wave masks of direct comparisons, so none is
-      // turned into a per-lane value and back.)
-      const uint64_t okm = __builtin_amdgcn_ballot_w64(!(power > 0.0f)) &
-                           __builtin_amdgcn_ballot_w64(!(power < -5.6f)) & livem;
-      if (okm == 0) continue;
-      const float4 c = s_rec.r[k].c;   // opacity, r, g, b
-      const float alpha = fminf(0.99f, c.x * pexp_core(power));
-      const uint64_t okm2 = okm & __builtin_amdgcn_ballot_w64(!(alpha < 1.0f / 255.0f));
-      const float nt = T * (1.0f - alpha);
-      const uint64_t stopm = okm2 & __builtin_amdgcn_ballot_w64(nt < 0.0001f);
-      const bool comp = __builtin_amdgcn_inverse_ballot_w64(okm2 & ~stopm);
-      const uint32_t pos1 = pos0 + uint32_t(k);
-      // a zero weight leaves the colour sums exactly as they are
-      // (non-negative colours, sums from +0)
-      const float wgt = comp ? alpha * T : 0.0f;
-      C0 = fmaf(c.y, wgt, C0);
-      C1 = fmaf(c.z, wgt, C1);
-      C2 = fmaf(c.w, wgt, C2);
-      // (kept for every list: cheaper than selecting on `rec`, and unused
-      // when nothing is recorded)
-      U0 = fmaf(c.y, wgt, U0);
-      U1 = fmaf(c.z, wgt, U1);
-      U2 = fmaf(c.w, wgt, U2);
-      T = comp ? nt : T;
-      lastp = comp ? pos1 : lastp;
-      if constexpr (kTiles) read = __builtin_amdgcn_inverse_ballot_w64(stopm) ? pos1 : read;
-      livem &= ~stopm;
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+  if (rec)
+    fwd_list<kTiles, true>(proj, vals, start, end, qx, qy, pxc, pyc, sl, sp, seg_mask, qid, pool, s_rec, st);
+  else
+    fwd_list<kTiles, false>(proj, vals, start, end, qx, qy, pxc, pyc, sl, sp, seg_mask, qid, pool, s_rec, st);
 
   if (inside) {
     const size_t P = size_t(W) * H;
     const size_t pix = size_t(py) * W + px;
-    image[pix] = C0;
-    image[P + pix] = C1;
-    image[2 * P + pix] = C2;
-    T_final[pix] = T;
-    last[pix] = lastp;
+    image[pix] = st.C0;
+    image[P + pix] = st.C1;
+    image[2 * P + pix] = st.C2;
+    T_final[pix] = st.T;
+    last[pix] = st.lastp;
   }
   if (kTiles) {
-    const uint32_t rmax = wave_max_u32(inside ? read : 0u);
+    const uint32_t rmax = wave_max_u32(inside ? st.read : 0u);
     if (lane == 0 && rmax != 0) atomicMax(tile_processed + tile, rmax);
   }
   if (split != nullptr) {
+    const uint32_t slotv = st.slotv;
+    const int nck = st.nck;
+    float U0 = st.U0, U1 = st.U1, U2 = st.U2;
     // recorded segment colours -> the colour behind each boundary b: the
     // sum of the segments after it (positive terms, no cancellation) / T_b
     // (T_b >= 1e-4: a pixel stops before its transmittance drops below)
@@ -180,15 +212,15 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
     }
     // the whole segments below the last entry any pixel composited go to
     // the helpers; the quarter's own wave keeps the rest
-    const uint32_t lmax = wave_max_u32(lastp);
+    const uint32_t lmax = wave_max_u32(st.lastp);
     uint32_t nseg = lmax == 0 ? 0u : (lmax - 1) >> seg_shift;
     if (nseg > uint32_t(nck)) nseg = uint32_t(nck);
     if (lane == 0) sp.qsegs[qid] = nseg;
     if (nseg != 0) {
       uint32_t b = 0;
-      if (lane == 0) b = atomicAdd(pool_count + 1, nseg);
+      if (lane == 0) b = atomicAdd(sp.counters + 32 * pool + 1, nseg);
       b = __builtin_amdgcn_readfirstlane(b);
-      if (ul < nseg) sp.items[pool * uint32_t(sl.pool_slots) + b + ul] = slotv;
+      if (uint32_t(lane) < nseg) sp.items[pool * uint32_t(sl.pool_slots) + b + uint32_t(lane)] = slotv;
     }
   }
 }
