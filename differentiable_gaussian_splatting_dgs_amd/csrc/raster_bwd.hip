@@ -213,9 +213,10 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
 
 // Workgroups [0, nhelp) are helpers: helper h takes the forward's listed
 // segments h / kPools, h / kPools + nhelp / kPools, ... of pool h % kPools
-// (nhelp = kPools x pool size: one each), each from its recorded state; the
-// rest own one quarter each (in `order`) and run its list from the last
-// composited entry down to the first position no helper covers.
+// (nhelp = kPools x half the pool size: a pool's items rarely exceed
+// that), each from its recorded state; the rest own one quarter each (in
+// `order`) and run its list from the last composited entry down to the
+// first position no helper covers.
 template <bool kCount>
 __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                                    const uint32_t* __restrict__ ranges,
@@ -337,8 +338,9 @@ hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint3
   const int TX = (width + kTile - 1) / kTile, TY = (height + kTile - 1) / kTile;
   const int nT = TX * TY;
   if (split != nullptr && !raster_split_fits(width, height)) split = nullptr;
-  // one helper per recorded state the pools can hold
-  const int nhelp = split != nullptr ? kPools * split_layout(width, height).pool_slots : 0;
+  // a helper per two recorded states the pools can hold (a multiple of
+  // kXcds, so the quarters' workgroups keep their XCD mapping)
+  const int nhelp = split != nullptr ? kPools * ((split_layout(width, height).pool_slots + 1) / 2) : 0;
   const unsigned grid = unsigned(nhelp) + raster_grid(nT);
   unsigned long long* const vc = reinterpret_cast<unsigned long long*>(visits);
   if (visits != nullptr)

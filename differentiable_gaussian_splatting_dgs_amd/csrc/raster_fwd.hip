@@ -43,7 +43,7 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
                                          uint32_t start, uint32_t end, float qx, float qy, float pxc, float pyc,
                                          const SplitLayout& sl, const SplitState& sp, uint32_t seg_mask,
                                          uint32_t qid, uint32_t pool, LdsRecs& s_rec, FwdState& st) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   uint32_t* const pool_count = sp.counters + 32 * pool;   // slots taken, items listed
   bool ck_open = kRec;
   const uint32_t ul = uint32_t(lane);
@@ -120,22 +120,24 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
 // kTiles: the per-tile count of processed list entries is recorded (it
 // needs the list position where each pixel stopped).
 template <bool kTiles>
-__global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
+__global__ __launch_bounds__(64 * kWPT) void k_render_fwd(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                                    const uint32_t* __restrict__ ranges,
                                                    const uint32_t* __restrict__ order, int64_t num_pairs, int W,
                                                    int H, int TX, int nT, float* __restrict__ image,
                                                    float* __restrict__ T_final, uint32_t* __restrict__ last,
                                                    uint32_t* __restrict__ tile_processed, void* split,
                                                    int seg_shift) {
-  __shared__ LdsRecs s_rec;
+  __shared__ LdsRecs s_recs[kWPT];
   // issue priority over waves of other kernels sharing the CU (the next
   // view's binning on the side stream): this kernel is issue-bound and on
   // the step's critical path
   __builtin_amdgcn_s_setprio(kRasterPrio);
-  int q0;
-  const int tile = order_tile(order, nT, q0);
-  if (tile < 0) return;
-  const int lane = threadIdx.x;
+  const int rank = int(blockIdx.x);
+  if (rank >= nT) return;
+  const int tile = order != nullptr ? int(order[rank]) : rank;
+  const int q0 = int(threadIdx.x) >> 6;
+  const int lane = int(threadIdx.x) & 63;
+  LdsRecs& s_rec = s_recs[q0];
   const int tx = tile % TX, ty = tile / TX;
   const int x0 = tx * kTile, y0 = ty * kTile;
   const float qx = float(x0 + (q0 & 1) * 8) + 0.5f, qy = float(y0 + (q0 >> 1) * 8) + 0.5f;
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(64) void k_render_fwd(const float4* __restrict__ pr
   const uint32_t seg_mask = (1u << seg_shift) - 1u;
   const bool rec = split != nullptr && end - start > seg_mask + 1u;
   const uint32_t qid = uint32_t(tile) * kWPT + uint32_t(q0);
-  const uint32_t pool = blockIdx.x % kPools;
+  const uint32_t pool = (blockIdx.x * kWPT + uint32_t(q0)) % kPools;
   if (rec)
     fwd_list<kTiles, true>(proj, vals, start, end, qx, qy, pxc, pyc, sl, sp, seg_mask, qid, pool, s_rec, st);
   else
@@ -245,11 +247,11 @@ hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint3
     k_clear<<<unsigned(std::max(tile_processed != nullptr ? (nT + 255) / 256 : 0, kCounterWords / 256)), 256, 0, st>>>(
         tile_processed, nT, counters);
   if (tile_processed != nullptr)
-    k_render_fwd<true><<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
+    k_render_fwd<true><<<unsigned(nT), 64 * kWPT, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
                                                       num_pairs, width, height, TX, nT, image, T_final, last,
                                                       tile_processed, split, seg_shift);
   else
-    k_render_fwd<false><<<raster_grid(nT), 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges,
+    k_render_fwd<false><<<unsigned(nT), 64 * kWPT, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges,
                                                        tile_order, num_pairs, width, height, TX, nT, image, T_final,
                                                        last, nullptr, split, seg_shift);
   return hipGetLastError();

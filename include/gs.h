@@ -210,7 +210,7 @@ gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx
  *                quarter-tile whose list reaches past segment_len entries,
  *                the per-pixel state (transmittance, colour behind) at each
  *                multiple of segment_len it reaches (at most 31 per quarter;
- *                room for half a state per quarter of the image, beyond
+ *                room for one state per quarter of the image, beyond
  *                which lists stay whole) and lists the segments
  *                gs_render_bwd can run in parallel; ignored for images of
  *                2^25 tiles or more.  Pass it unchanged, with the same

@@ -237,9 +237,9 @@ def test_workspace_sizes():
     assert gs.gs_workspace_size(gs.GS_OP_LOSS, 0, 64, 48) >= 9 * 4 * 64 * 48
     assert gs.gs_workspace_size(gs.GS_OP_PREPROCESS, 0) > 0
     # raster split state: at least 64 recorded states (64 pixels x 16 bytes)
-    # in each of 64 pools; half a state per quarter-tile (1080p: 32640)
+    # in each of 64 pools; one state per quarter-tile (1080p: 32640)
     assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 64, 64) > 64 * 64 * 64 * 16
-    assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 1920, 1080) >= 16320 * 64 * 16
+    assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 1920, 1080) >= 32640 * 64 * 16
     # view overlap: one bitmap row per view, n bits padded to 64 words
     assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1000, 3) == 3 * 64 * 4
     assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1_000_000, 1024) == 1024 * 31296 * 4

@@ -299,7 +299,7 @@ def split_pool_counts(step, vw):
     import torch
 
     quarters = ((vw.W + 15) // 16) * ((vw.H + 15) // 16) * 4
-    pool_slots = max(64, (quarters // 2 + 63) // 64)
+    pool_slots = max(64, (quarters + 63) // 64)
     slots = 64 * pool_slots
     off = slots * 64 * 16 + 8 * slots + 4 * quarters
     c = step.split_ws[off:off + 64 * 32 * 4].view(torch.int32).view(64, 32).cpu().numpy()
