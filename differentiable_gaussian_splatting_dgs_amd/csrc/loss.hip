@@ -319,8 +319,11 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
   }
 }
 
-// The same tiles and walk as k_ssim_fwd; the last workgroup also turns
-// k_ssim_fwd's per-tile sums into the loss.
+// The same tiles and walk as k_ssim_fwd; the last workgroup (which has at
+// most as many tiles as any other) first turns k_ssim_fwd's per-tile sums
+// into the loss (they are complete: k_ssim_fwd has finished), so that
+// single-workgroup reduction runs beside the other workgroups' tiles
+// rather than after them.
 __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img, const float* __restrict__ tgt, int W,
                                                   int H, int tx, int ty, SsimWindow win, const float* __restrict__ maps,
                                                   float w_l1, float w_ssim, float* __restrict__ dL,
@@ -340,6 +343,9 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img,
     const float* const src[3] = {maps + (3 * id.ch) * P, maps + (3 * id.ch + 1) * P, maps + (3 * id.ch + 2) * P};
     stage_load<3>(src, W, H, id.ox, id.oy, st);
   }
+  if (blockIdx.x == gridDim.x - 1)   // (its LDS planes are free until the first tile)
+    finish_loss(partial, ntiles, 1.0f / (3.0f * float(P)), w_l1, w_ssim, 1, loss,
+                reinterpret_cast<double(*)[256]>(&h[0][0][0]));
   const int lx = t % kLX, r0 = (t / kLX) * kRunV;
   for (; i < wk.end; i += wk.step) {
     const TileId id = tile_id(i, tx, ty);
@@ -392,13 +398,6 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img,
       const float sg = d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f);
       dL[ch * P + pix] = w_l1 * inv * sg - w_ssim * inv * (b[0][q] + 2.0f * xv[q] * b[1][q] + yv[q] * b[2][q]);
     }
-  }
-  // the last workgroup turns k_ssim_fwd's per-tile sums into the loss (they
-  // are complete: k_ssim_fwd has finished); its LDS planes are free
-  if (blockIdx.x == gridDim.x - 1) {
-    __syncthreads();
-    finish_loss(partial, ntiles, 1.0f / (3.0f * float(P)), w_l1, w_ssim, 1, loss,
-                reinterpret_cast<double(*)[256]>(&h[0][0][0]));
   }
 }
 
