@@ -517,9 +517,12 @@ def main():
     _, _, all_stages = run_block(step, init, RESTORE_EVERY, timed_stages=set())
     stage_t = {k: [a.elapsed_time(b) for a, b in v] for k, v in all_stages.items()}
     stages = {k: float(np.mean(v)) for k, v in stage_t.items()}
-    # view 0's projection runs inside the previous step's Adam pass; its
-    # preprocess stage only lists the visible rows
-    pre_rest = [t for i, t in enumerate(stage_t.get("preprocess", [])) if i % nv != 0]
+    # view 0's projection runs inside the previous step's Adam pass (its
+    # preprocess stage only lists the visible rows); views 1.. are projected
+    # in one pass over the parameters (stage preprocess_views): the
+    # parameters read once, each view's records, flags and list written
+    pv_t = stage_t.get("preprocess_views", [])
+    pv_bytes = 236.0 * N + (nv - 1) * 80.0 * N
 
     # roofline of the dominant raster kernel (one launch per view): the
     # back-propagated (pixel, entry) pairs the counting block measured,
@@ -550,8 +553,9 @@ def main():
     per_view = {k: v / nv for k, v in B_stage.items()}
     fused_bytes = float(np.mean([1416 * U + 96 * sum(v["V"] for v in vs) + 64 * U for vs, U in sizes]))
     stage_bound = {
-        "preprocess": {"bound": "hbm", "frac": hbm_frac(per_view["preprocess"], float(np.mean(pre_rest)))
-                       if pre_rest else None, "note": "views 1..3 (view 0 is projected in the Adam pass)"},
+        "preprocess": {"bound": "hbm", "frac": hbm_frac(pv_bytes, float(np.mean(pv_t))) if pv_t else None,
+                       "note": "views 1.. in one pass over the parameters (236 B in, 80 B out per Gaussian and "
+                               "view; view 0 is projected in the Adam pass)"},
         "bin_sort": {"bound": "hbm", "frac": hbm_frac(per_view["bin_sort"], stages["bin_sort"])},
         "render_fwd": {"bound": "alu", "frac": alu_frac(visits_per_launch * OPS_PER_VISIT["render_fwd"],
                                                         stages["render_fwd"]),

@@ -24,10 +24,11 @@ LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
 GS_OP_PREPROCESS, GS_OP_BIN_SORT, GS_OP_LOSS, GS_OP_SPARSE_ADAM, GS_OP_RASTER = 0, 1, 2, 3, 4
-GS_OP_VIEW_OVERLAP, GS_OP_PACK, GS_OP_DENSIFY = 5, 6, 7
+GS_OP_VIEW_OVERLAP, GS_OP_PACK, GS_OP_DENSIFY, GS_OP_PREPROCESS_VIEWS = 5, 6, 7, 8
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
 GS_MAX_FUSED_VIEWS = 16
+GS_MAX_PREPROCESS_VIEWS = 16
 GS_MAX_COUPLED_VIEWS = 65536
 GS_MAX_TILE_BLOCKS = 64
 GS_MAX_PARTITION_TILES = 1 << 21
@@ -39,7 +40,7 @@ EXPORTS = ["gs_status_string", "gs_last_error", "gs_version", "gs_workspace_size
            "gs_bin_sort", "gs_bin_sort_async", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
            "gs_sparse_adam", "gs_project_bwd_adam", "gs_visible_list", "gs_view_overlap", "gs_view_priority",
            "gs_tile_partition", "gs_pack_records", "gs_unpack_grads", "gs_densify_stats", "gs_densify",
-           "gs_sparse_adam_noalloc"]
+           "gs_sparse_adam_noalloc", "gs_preprocess_views"]
 GS_NOALLOC_SCRATCH_BYTES = 256 * 1024
 GS_NOALLOC_MAX_N = (GS_NOALLOC_SCRATCH_BYTES // 4 - 1) * 4096
 
@@ -78,6 +79,7 @@ def lib():
     L.gs_version.restype = C.c_int
     L.gs_workspace_size.argtypes = [C.c_int, _i64, _i32, _i32, _i64, C.POINTER(_sz)]
     L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _sz, _P]
+    L.gs_preprocess_views.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _i32, _P, _P, _P, _P, _P, _sz, _P]
     L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
     L.gs_bin_sort_async.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
     L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
@@ -177,6 +179,20 @@ def gs_preprocess(params, n, ld, cam, proj, vis_idx, vis_count, union_flags, wor
     _check(lib().gs_preprocess(_ptr(params), n, ld, C.byref(c), _ptr(proj), _ptr(vis_idx), _ptr(vis_count),
                               _ptr(union_flags), _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream)), "gs_preprocess")
+
+
+def gs_preprocess_views(params, n, ld, cams, proj, vis_idx, vis_count, union_flags, workspace, stream=None):
+    """gs_preprocess of several views in one pass over the parameters:
+    ``cams``, ``proj`` and ``vis_idx`` hold one entry per view,
+    ``vis_count`` is a device int64 tensor with one count per view."""
+    nv = len(cams)
+    assert len(proj) == nv and len(vis_idx) == nv
+    carr = (gs_camera * max(nv, 1))(*[c if isinstance(c, gs_camera) else make_camera(c) for c in cams])
+    parr = (C.c_void_p * max(nv, 1))(*[t.data_ptr() for t in proj])
+    varr = (C.c_void_p * max(nv, 1))(*[t.data_ptr() for t in vis_idx])
+    _check(lib().gs_preprocess_views(_ptr(params), n, ld, carr, nv, parr, varr, _ptr(vis_count), _ptr(union_flags),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)), "gs_preprocess_views")
 
 
 def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_capacity, tile_ranges, workspace,
@@ -402,15 +418,13 @@ class View:
 
 
 class _PairSet:
-    """Buffers one view's binning and rasterisation read: projected records,
-    sorted pairs and the binning workspace.  A step cycles through several
-    sets so that later views' preprocess and binning can run while the
-    current view renders and back-propagates."""
+    """Buffers of one view's binning that its rasterisation reads: sorted
+    pairs and the binning workspace.  A step cycles through several sets so
+    that later views' binning can run while the current view renders and
+    back-propagates."""
 
     def __init__(self, n, cap, device, with_keys):
-        rows = max(n, 1)
         self.n, self.device, self.with_keys = n, device, with_keys
-        self.proj = torch.empty((rows, GS_PROJ_WORDS), dtype=torch.float32, device=device)
         self.alloc(cap)
 
     def alloc(self, cap):
@@ -474,6 +488,7 @@ class TrainStep:
         self.nsets = min(3, max(2, len(self.views)))
         self._with_keys = any(v.W > 4096 or v.H > 4096 for v in self.views)
         self._cur = 0                       # set of the view last prepared
+        self._curv = 0                      # the view last prepared
         self._free = [None] * self.nsets    # per set: event after its last reader
         self._gcur = 0
         self._alloc_rows(p.to(self.device).contiguous(), None, None)
@@ -489,6 +504,7 @@ class TrainStep:
         # its visibility bytes wait in next_flags, zero between uses
         self.fuse_next_preprocess = fuse_next_preprocess
         self._pre0 = False       # view 0's records and flags come from the last Adam pass
+        self.preprocess_after_first = False   # the other views' preprocess waits for view 0's binning
         # the forward's checkpoints and segment list, read by the split raster
         # backward of the same view (both on the current stream, the view's
         # backward before the next view's forward); segment_len None: unsplit
@@ -518,20 +534,26 @@ class TrainStep:
         self.g2d = [torch.zeros((rows, GS_GRAD2D_WORDS), dtype=torch.float32, device=self.device)
                     for _ in range(self.ndefer + (2 if self.nfirst > 0 else 0))]
         self.vis_idx = [torch.empty(rows, dtype=torch.int32, device=self.device) for _ in self.views]
+        # every view's projected records (the views' preprocess runs in one
+        # pass over the parameters at the start of a step)
+        self.vproj = [torch.empty((rows, GS_PROJ_WORDS), dtype=torch.float32, device=self.device)
+                      for _ in self.views]
         self.union_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
         self.union_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
         self.next_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
         self.sets = [_PairSet(n, self.pair_capacity, self.device, self._with_keys) for _ in range(self.nsets)]
         self._free = [None] * self.nsets
         self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
+        npv = min(len(self.views), GS_MAX_PREPROCESS_VIEWS)
+        self.ws_pre_views = _bytes(gs_workspace_size(GS_OP_PREPROCESS_VIEWS, n, npv), self.device)
         self.ws_adam = _bytes(gs_workspace_size(GS_OP_SPARSE_ADAM, n), self.device)
         if self.dens_accum is not None:
             self.track_densify()
 
-    # the buffer set of the view last prepared (what tests read back)
+    # the records of the view last prepared (what tests read back)
     @property
     def proj(self):
-        return self.sets[self._cur].proj
+        return self.vproj[self._curv]
 
     @property
     def keys(self):
@@ -568,25 +590,24 @@ class TrainStep:
         self.timer.setdefault(name, []).append((a, b))
 
     # -- one view ---------------------------------------------------------
-    def prepare_view(self, k, sync=True):
-        """Preprocess and bin/sort view k into buffer set k % nsets.  With
-        sync, the pair count is read (blocking) and the set grown if it
-        overflowed; without, it stays on the device in M_dev[k]."""
+    def prepare_view(self, k, sync=True, preprocess=True):
+        """Preprocess view k (unless preprocess is False: its records and
+        visible list are there already) and bin/sort it into buffer set
+        k % nsets.  With sync, the pair count is read (blocking) and the set
+        grown if it overflowed; without, it stays on the device in M_dev[k]."""
         vw = self.views[k]
         ps = self.sets[k % self.nsets]
         self._cur = k % self.nsets
-        with self._stage("preprocess"):
-            if k == 0 and self._pre0:
-                # records and flags from the last Adam pass
-                gs_visible_list(self.next_flags, self.n, self.vis_idx[0], self.vis_count[0:1], self.ws_pre)
-                self._pre0 = False
-            else:
-                if self._pre0 and k % self.nsets == 0:
-                    # another view takes view 0's set: drop what the Adam pass left
-                    self.next_flags.zero_()
+        self._curv = k
+        if preprocess:
+            with self._stage("preprocess"):
+                if k == 0 and self._pre0:
+                    # records and flags from the last Adam pass
+                    gs_visible_list(self.next_flags, self.n, self.vis_idx[0], self.vis_count[0:1], self.ws_pre)
                     self._pre0 = False
-                gs_preprocess(self.params, self.n, self.ld, vw.cam, ps.proj, self.vis_idx[k],
-                              self.vis_count[k:k + 1], self.union_flags, self.ws_pre)
+                else:
+                    gs_preprocess(self.params, self.n, self.ld, vw.cam, self.vproj[k], self.vis_idx[k],
+                                  self.vis_count[k:k + 1], self.union_flags, self.ws_pre)
         with self._stage("bin_sort"):
             self._bin_sort(k, ps)
         if sync:
@@ -602,7 +623,7 @@ class TrainStep:
         vw = self.views[k]
         vw.num_pairs = None
         self._set_cap[k] = ps.capacity
-        gs_bin_sort_async(ps.proj, self.n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
+        gs_bin_sort_async(self.vproj[k], self.n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
                           ps.capacity, self.M_dev[k:k + 1], vw.ranges, ps.ws_sort, vw.order)
 
     def _pair_bound(self, k):
@@ -618,7 +639,7 @@ class TrainStep:
         vw = self.views[k]
         ps = self.sets[k % self.nsets]
         with self._stage("render_fwd"):
-            gs_render_fwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.image, vw.T_final,
+            gs_render_fwd(self.vproj[k], self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.image, vw.T_final,
                           vw.last, vw.tile_processed if self.record_tiles else None, vw.order, self._split(k),
                           self.seg[k])
 
@@ -643,7 +664,7 @@ class TrainStep:
         chain = not keep_grad2d and self.dens_accum is None
         pg = (self.params, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1], self.grads) if chain else None
         with self._stage("render_bwd+project_bwd" if chain else "render_bwd", k):
-            gs_render_bwd(ps.proj, self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
+            gs_render_bwd(self.vproj[k], self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
                           vw.dL, self.g2d[self._gcur], vw.order, self._split(k), self.seg[k], param_grads=pg,
                           visits=None if self.visits is None else self.visits[k:k + 1])
         if self.dens_accum is not None:
@@ -692,13 +713,35 @@ class TrainStep:
                 self.dens_accum.copy_(stat0[0])
                 self.dens_denom.copy_(stat0[1])
 
+    def preprocess_views(self, ks):
+        """The preprocess of views ``ks`` in one pass over the parameters per
+        GS_MAX_PREPROCESS_VIEWS of them (records, visible lists, counts, the
+        union flags) on the current stream."""
+        ks = list(ks)
+        with self._stage("preprocess_views"):
+            for i in range(0, len(ks), GS_MAX_PREPROCESS_VIEWS):
+                grp = ks[i:i + GS_MAX_PREPROCESS_VIEWS]
+                k0 = grp[0]
+                assert grp == list(range(k0, k0 + len(grp))), "consecutive views"
+                gs_preprocess_views(self.params, self.n, self.ld, [self.views[k].cam for k in grp],
+                                    [self.vproj[k] for k in grp], [self.vis_idx[k] for k in grp],
+                                    self.vis_count[k0:k0 + len(grp)], self.union_flags, self.ws_pre_views)
+
     def _issue_views(self, defer):
         main = torch.cuda.current_stream(self.device)
         nv = len(self.views)
         proj_done = [None, None]
+        start = torch.cuda.Event()
+        start.record(main)
         self.prepare_view(0, sync=False)
         first_done = torch.cuda.Event()
         first_done.record(main)
+        if nv > 1:
+            # the other views' preprocess, one pass over the parameters, on
+            # the side stream beside the first view's binning
+            with torch.cuda.stream(self.side):
+                self.side.wait_event(first_done if self.preprocess_after_first else start)
+                self.preprocess_views(range(1, nv))
         for k in range(nv):
             self.render_view(k)
             if k < self.nfirst and proj_done[k % 2] is not None:
@@ -728,7 +771,7 @@ class TrainStep:
                     prev = self._free[(k + 1) % self.nsets]
                     if prev is not None:
                         self.side.wait_event(prev)
-                    self.prepare_view(k + 1, sync=False)
+                    self.prepare_view(k + 1, sync=False, preprocess=False)
                     ready = torch.cuda.Event()
                     ready.record(self.side)
                 main.wait_event(ready)
@@ -755,11 +798,12 @@ class TrainStep:
                 ks = range(self.nfirst, len(self.views))
                 nxt = {}
                 if self.fuse_next_preprocess:
-                    # (set 0 holds a preprocess of this batch's parameters:
-                    # rows outside the union are invisible there, tiles 0)
+                    # (view 0's records hold a preprocess of this batch's
+                    # parameters: rows outside the union are invisible
+                    # there, tiles 0)
                     if self._pre0:
                         self.next_flags.zero_()
-                    nxt = dict(next_cam=self.views[0].cam, next_proj=self.sets[0].proj, next_flags=self.next_flags)
+                    nxt = dict(next_cam=self.views[0].cam, next_proj=self.vproj[0], next_flags=self.next_flags)
                 gs_project_bwd_adam(self.params, self.grads if self.nfirst > 0 else None, self.m, self.v, self.n,
                                     self.ld, [self.views[k].cam for k in ks], [self.g2d[self._gbuf(k)] for k in ks],
                                     self.union_flags, self.union_idx, self.union_count, self.lr, self.beta1,

@@ -13,6 +13,7 @@
 #include "gs_internal.h"
 
 static_assert(GS_MAX_FUSED_VIEWS == gs::kMaxFusedViews, "fused view limit");
+static_assert(GS_MAX_PREPROCESS_VIEWS == gs::kMaxPreprocessViews, "preprocess view limit");
 static_assert(GS_MAX_COUPLED_VIEWS == gs::kMaxCoupledViews, "coupled view limit");
 static_assert(GS_MAX_TILE_BLOCKS == gs::kMaxTileBlocks, "tile block limit");
 static_assert(GS_MAX_PARTITION_TILES == gs::kMaxPartitionTiles, "partition tile limit");
@@ -191,6 +192,11 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
       CHECK(check_size(width, height));
       *bytes = gs::raster_split_bytes(width, height);
       return ok();
+    case GS_OP_PREPROCESS_VIEWS:
+      REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
+      REQUIRE(width >= 1 && width <= GS_MAX_PREPROCESS_VIEWS, "num_views = %d out of range", width);
+      *bytes = gs::preprocess_views_ws_bytes(n, width);
+      return ok();
     case GS_OP_DENSIFY:
       REQUIRE(n >= 0 && n < (int64_t(1) << 30), "n = %lld out of range", (long long)n);
       *bytes = gs::densify_ws_bytes(n);
@@ -227,6 +233,32 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
   return hip_status(gs::launch_preprocess(params, n, ld, c, proj, vis_idx, vis_count, union_flags, workspace,
                                           static_cast<hipStream_t>(stream)),
                     "gs_preprocess");
+}
+
+gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const gs_camera* cams, int32_t num_views,
+                              float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
+                              uint8_t* union_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(num_views >= 1 && num_views <= GS_MAX_PREPROCESS_VIEWS, "num_views = %d outside [1, %d]", int(num_views),
+          GS_MAX_PREPROCESS_VIEWS);
+  REQUIRE(cams != nullptr && proj != nullptr && vis_idx != nullptr, "cams / proj / vis_idx NULL");
+  gs::CamArgs c[gs::kMaxPreprocessViews];
+  for (int32_t w = 0; w < num_views; ++w) CHECK(check_camera(cams + w, c[w]));
+  REQUIRE(n >= 0 && n < GS_MAX_PLANE_ROWS, "n = %lld out of range", (long long)n);
+  REQUIRE(ld >= n, "ld < n");
+  REQUIRE(vis_count != nullptr && aligned(vis_count, 8), "vis_count NULL or misaligned");
+  if (n > 0) {
+    REQUIRE(params != nullptr && aligned(params, 4), "params NULL or misaligned");
+    for (int32_t w = 0; w < num_views; ++w) {
+      REQUIRE(proj[w] != nullptr && aligned(proj[w], 16), "proj[%d] NULL or not 16-byte aligned", int(w));
+      REQUIRE(vis_idx[w] != nullptr && aligned(vis_idx[w], 4), "vis_idx[%d] NULL or misaligned", int(w));
+    }
+  }
+  REQUIRE(union_flags == nullptr || aligned(union_flags, 16), "union_flags not 16-byte aligned");
+  REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
+  REQUIRE(workspace_bytes >= gs::preprocess_views_ws_bytes(n, num_views), "workspace too small");
+  return hip_status(gs::launch_preprocess_views(params, n, ld, c, num_views, proj, vis_idx, vis_count, union_flags,
+                                                workspace, static_cast<hipStream_t>(stream)),
+                    "gs_preprocess_views");
 }
 
 gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,

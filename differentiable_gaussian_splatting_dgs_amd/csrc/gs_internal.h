@@ -30,6 +30,20 @@ size_t preprocess_ws_bytes(int64_t n);
 hipError_t launch_preprocess(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
                              float* proj, int32_t* vis_idx, int64_t* vis_count,
                              uint8_t* union_flags, void* ws, hipStream_t st);
+// Up to kMaxPreprocessViews views in one pass over the parameters: view w's
+// records to proj[w], its visibility bytes to the w-th n-byte slice of the
+// workspace, then its ascending list to vis_idx[w] / vis_count[w].
+constexpr int kMaxPreprocessViews = 16;
+struct PreViews {
+  CamArgs cam[kMaxPreprocessViews];
+  float4* proj[kMaxPreprocessViews];
+  uint8_t* flags[kMaxPreprocessViews];
+  int32_t count;
+};
+size_t preprocess_views_ws_bytes(int64_t n, int32_t num_views);
+hipError_t launch_preprocess_views(const float* params, int64_t n, int64_t ld, const CamArgs* cams, int32_t num_views,
+                                   float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
+                                   uint8_t* union_flags, void* ws, hipStream_t st);
 
 // --- compaction of a flag array into ascending indices (compact.hip) -----
 size_t compact_ws_bytes(int64_t n);

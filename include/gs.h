@@ -84,6 +84,8 @@ typedef struct gs_camera {
 #define GS_GRAD2D_WORDS 12
 /* most views whose projection backward gs_project_bwd_adam fuses */
 #define GS_MAX_FUSED_VIEWS 16
+/* most views gs_preprocess_views projects in one call */
+#define GS_MAX_PREPROCESS_VIEWS 16
 /* most views gs_view_overlap couples in one call */
 #define GS_MAX_COUPLED_VIEWS 65536
 /* most tile blocks of gs_tile_partition / gs_pack_records, and most tiles
@@ -91,8 +93,9 @@ typedef struct gs_camera {
 #define GS_MAX_TILE_BLOCKS 64
 #define GS_MAX_PARTITION_TILES (1 << 21)
 /* most Gaussians (n) of the calls that read or write the [59][ld] parameter
- * planes (gs_preprocess, gs_project_bwd, gs_render_bwd with param_grads,
- * gs_sparse_adam, gs_project_bwd_adam): their kernels address a row by a
+ * planes (gs_preprocess, gs_preprocess_views, gs_project_bwd, gs_render_bwd
+ * with param_grads, gs_sparse_adam, gs_project_bwd_adam): their kernels
+ * address a row by a
  * 32-bit byte offset; larger n is rejected with GS_ERR_INVALID_ARG */
 #define GS_MAX_PLANE_ROWS ((int64_t)1 << 30)
 
@@ -104,7 +107,8 @@ typedef enum gs_op {
   GS_OP_RASTER = 4,
   GS_OP_VIEW_OVERLAP = 5,
   GS_OP_PACK = 6,
-  GS_OP_DENSIFY = 7
+  GS_OP_DENSIFY = 7,
+  GS_OP_PREPROCESS_VIEWS = 8
 } gs_op;
 
 /* Static description of a status code (never NULL). */
@@ -123,6 +127,7 @@ int gs_version(void);
  *   GS_OP_VIEW_OVERLAP n, width = num_views
  *   GS_OP_PACK        n, width = num_blocks
  *   GS_OP_DENSIFY     n
+ *   GS_OP_PREPROCESS_VIEWS n, width = num_views
  * Unused arguments are ignored.  The workspace is caller-owned device
  * memory, 256-byte aligned; its contents need no initialisation and are
  * scratch between calls. */
@@ -148,6 +153,29 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
 gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_camera* cam, float* proj,
                         int32_t* vis_idx, int64_t* vis_count, uint8_t* union_flags, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* gs_preprocess of several views in one pass over the parameters (the same
+ * passages): each Gaussian's 59 parameters are read once and projected with
+ * every camera in turn, so a batch's views cost one read of the parameter
+ * planes instead of one per view.  Each view's records, visible list and
+ * count are bit for bit those of gs_preprocess with that camera.
+ *   cams         host array of num_views (1..GS_MAX_PREPROCESS_VIEWS)
+ *                cameras
+ *   proj         host array of num_views device pointers, one buffer per
+ *                view: [n][GS_PROJ_WORDS], 16-byte aligned
+ *   vis_idx      host array of num_views device pointers: [n] int32 each,
+ *                as gs_preprocess's
+ *   vis_count    device out, [num_views] int64: view w's count at w
+ *   union_flags  as gs_preprocess: set for a Gaussian visible in any of
+ *                the views
+ *   workspace    device, >= gs_workspace_size(GS_OP_PREPROCESS_VIEWS, n,
+ *                num_views) bytes (the views' visibility bytes and the
+ *                compaction's counts)
+ * Errors: GS_ERR_INVALID_ARG for num_views outside the range, an invalid
+ * camera, a NULL or misaligned buffer, or as gs_preprocess. */
+gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const gs_camera* cams, int32_t num_views,
+                              float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
+                              uint8_t* union_flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Gaussian-tile pairs sorted by depth within each tile, and the tile ranges
  * (Grendel-GS notes, training pipeline: "find the covering Gaussians, sort

@@ -22,7 +22,7 @@ def test_header_declares_the_entry_points():
     for n in ["gs_preprocess", "gs_bin_sort", "gs_render_fwd", "gs_loss", "gs_render_bwd", "gs_project_bwd",
               "gs_sparse_adam", "gs_bin_sort_async", "gs_project_bwd_adam", "gs_visible_list",
               "gs_view_overlap", "gs_view_priority", "gs_tile_partition", "gs_pack_records", "gs_unpack_grads",
-              "gs_densify_stats", "gs_densify",
+              "gs_densify_stats", "gs_densify", "gs_preprocess_views",
               "gs_workspace_size", "gs_status_string", "gs_last_error", "gs_version"]:
         assert n in names
 
@@ -128,6 +128,29 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), P(20), P(16),
                                    *scal) == 1
     assert b"next_proj" in lib.gs_last_error()
+    # several views' preprocess: no view, too many, a misaligned record
+    # buffer, a NULL list buffer, a small workspace, an invalid camera
+    nmp = gs.GS_MAX_PREPROCESS_VIEWS + 1
+    pcams = (gs.gs_camera * nmp)(*([cam] * nmp))
+    pbufs = (C.c_void_p * nmp)(*([16] * nmp))
+    vbufs = (C.c_void_p * nmp)(*([16] * nmp))
+    ws_ok = gs.gs_workspace_size(gs.GS_OP_PREPROCESS_VIEWS, 4, 2)
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 0, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, nmp, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert b"num_views" in lib.gs_last_error()
+    pbufs[1] = 20
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert b"proj[1]" in lib.gs_last_error()
+    pbufs[1] = 16
+    vbufs[0] = None
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert b"vis_idx[0]" in lib.gs_last_error()
+    vbufs[0] = 16
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), ws_ok - 1, None) == 1
+    assert b"workspace" in lib.gs_last_error()
+    pcams[1].width = 0
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert b"camera" in lib.gs_last_error()
     # visible list: misaligned flags, small workspace
     assert lib.gs_visible_list(P(17), 10, P(16), P(16), P(256), 1 << 20, None) == 1
     assert lib.gs_visible_list(P(16), 1 << 20, P(16), P(16), P(256), 16, None) == 1
@@ -240,6 +263,11 @@ def test_workspace_sizes():
     # in each of 64 pools; one state per quarter-tile (1080p: 32640)
     assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 64, 64) > 64 * 64 * 64 * 16
     assert gs.gs_workspace_size(gs.GS_OP_RASTER, 0, 1920, 1080) >= 32640 * 64 * 16
+    # several views' preprocess: a visibility byte per Gaussian and view,
+    # and the compaction's counts
+    assert gs.gs_workspace_size(gs.GS_OP_PREPROCESS_VIEWS, 1000, 3) >= 3 * 1000
+    with pytest.raises(gs.GSError):
+        gs.gs_workspace_size(gs.GS_OP_PREPROCESS_VIEWS, 1000, gs.GS_MAX_PREPROCESS_VIEWS + 1)
     # view overlap: one bitmap row per view, n bits padded to 64 words
     assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1000, 3) == 3 * 64 * 4
     assert gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1_000_000, 1024) == 1024 * 31296 * 4

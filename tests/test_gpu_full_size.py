@@ -115,7 +115,7 @@ def test_capacity_full_size_pipelined_step_sampled(capacity_work):
         V = int(step.vis_count[k].item())
         say(f"[capacity full] view {k}: V={V} M={M}")
         pre = oracle.preprocess(work.params, cam)
-        pf = proj_fields(ps.proj[: work.n].cpu().numpy())
+        pf = proj_fields(step.vproj[k][: work.n].cpu().numpy())
         vis_idx = step.vis_idx[k][:V].cpu().numpy()
         vis = pre["visible"]
         assert np.array_equal(vis_idx, np.flatnonzero(vis).astype(np.int32)), f"v{k} visible list"
@@ -131,7 +131,7 @@ def test_capacity_full_size_pipelined_step_sampled(capacity_work):
         # the step leaves the keys unwritten: rebuilt from values, ranges and
         # records, then held to their definition
         assert ps.keys is None
-        keys = keys_from_pairs(vals, ranges, ps.proj[: work.n].cpu().numpy())
+        keys = keys_from_pairs(vals, ranges, step.vproj[k][: work.n].cpu().numpy())
         TX = (cam.width + 15) // 16
         check_pairs_against_definition(pf, vis_idx, keys, vals, ranges, TX, f"v{k}")
         del keys
@@ -239,7 +239,7 @@ def test_mid_full_size_step():
     step.prepare_view(0)
     torch.cuda.synchronize()
     M0 = step.views[0].num_pairs
-    v0 = dict(vals=step.sets[0].vals[:M0].cpu().numpy(), proj=step.sets[0].proj[: work.n].cpu().numpy())
+    v0 = dict(vals=step.sets[0].vals[:M0].cpu().numpy(), proj=step.vproj[0][: work.n].cpu().numpy())
     say("[mid full] step()")
     step.step()
     torch.cuda.synchronize()
@@ -262,8 +262,8 @@ def test_mid_full_size_step():
             gv["vals"], gv["proj"] = v0["vals"], v0["proj"]
         else:
             gv["vals"] = ps.vals[:M].cpu().numpy()
-            # set 0 (view 3's) now holds the next step's view-0 records
-            gv["proj"] = ps.proj[: work.n].cpu().numpy() if k % step.nsets != 0 else None
+            # (view 0's records are now the next step's: the Adam pass wrote them)
+            gv["proj"] = step.vproj[k][: work.n].cpu().numpy()
         views.append(gv)
     say("[mid full] oracle step")
     ref = oracle.step(work, dl_tol=DL_TOL)

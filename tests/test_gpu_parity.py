@@ -362,7 +362,7 @@ def test_next_step_preprocess_in_the_optimiser_pass(case):
     vw = step.views[0]
     M = vw.num_pairs
     V = int(step.vis_count[0].item())
-    gv = dict(proj=step.sets[0].proj[: step.n].cpu().numpy(), vis=step.vis_idx[0][:V].cpu().numpy(), M=M,
+    gv = dict(proj=step.vproj[0][: step.n].cpu().numpy(), vis=step.vis_idx[0][:V].cpu().numpy(), M=M,
               keys=step_keys(step, vw, M), vals=step.vals[:M].cpu().numpy(),
               ranges=vw.ranges.cpu().numpy().view(np.uint32))
     okeys, ovals, oranges = oracle.bin_sort(p1, cam)
@@ -521,3 +521,48 @@ def test_single_gaussian_matches_closed_form_on_gpu():
         assert np.max(np.abs(img[c] - rgb[c] * np.where(mask, alpha, 0.0))) < 2e-6
     pf = proj_fields(res["views"][0]["proj"])
     assert pf["radius"][0] == r
+
+
+@pytest.mark.parametrize("case", ["mid_cut", "capacity_cut", "ring_18"])
+def test_preprocess_views_matches_per_view(case):
+    """gs_preprocess_views (the training step's preprocess of a batch's
+    views, one pass over the parameters per 16 views) against gs_preprocess
+    of each view: records, visible lists and counts bit for bit, the same
+    union flags; and each view's visible set, rectangles, tile counts and
+    depths against the oracle's preprocess.  18 ring views take two calls
+    (16 + 2)."""
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    if case == "ring_18":
+        work = synth.plane_scene(4, 8000, 160, 96, [2 * math.pi * j / 18 for j in range(18)], 4, name="ring")
+    else:
+        work = workload_case(case)
+    step = gs.from_workload(work)
+    n, nv = step.n, len(work.cameras)
+    step.union_flags.zero_()
+    step.preprocess_views(range(nv))
+    torch.cuda.synchronize()
+    multi = []
+    for k in range(nv):
+        V = int(step.vis_count[k].item())
+        multi.append((step.vproj[k][:n].cpu().numpy().copy(), step.vis_idx[k][:V].cpu().numpy().copy()))
+    uf_multi = step.union_flags[:n].cpu().numpy().copy()
+    step.union_flags.zero_()
+    proj = torch.empty_like(step.vproj[0])
+    vis = torch.empty_like(step.vis_idx[0])
+    cnt = torch.zeros(1, dtype=torch.int64, device=proj.device)
+    for k, cam in enumerate(work.cameras):
+        gs.gs_preprocess(step.params, n, step.ld, step.views[k].cam, proj, vis, cnt, step.union_flags, step.ws_pre)
+        torch.cuda.synchronize()
+        V = int(cnt.item())
+        one = proj[:n].cpu().numpy()
+        assert np.array_equal(one.view(np.uint32), multi[k][0].view(np.uint32)), f"v{k} records"
+        assert np.array_equal(vis[:V].cpu().numpy(), multi[k][1]), f"v{k} visible list"
+        pre = oracle.preprocess(work.params, cam)
+        assert np.array_equal(multi[k][1], np.flatnonzero(pre["visible"]).astype(np.int32)), f"v{k} oracle list"
+        pf = proj_fields(multi[k][0])
+        sel = pre["visible"]
+        assert np.array_equal(pf["tiles"], pre["tiles"]), f"v{k} tiles"
+        assert np.array_equal(pf["rect"][sel], pre["rect"][sel]), f"v{k} rect"
+        assert np.array_equal(pf["depth"][sel].view(np.uint32), pre["depth"][sel].view(np.uint32)), f"v{k} depth"
+    assert np.array_equal(step.union_flags[:n].cpu().numpy(), uf_multi), "union flags"
+    say(f"  {case}: {nv} views, visible {[len(m[1]) for m in multi]}")
