@@ -444,17 +444,21 @@ class TrainStep:
     last ndefer = min(views, max_fused_views) views (at most
     GS_MAX_FUSED_VIEWS) own a screen-gradient buffer each; the earlier ones
     alternate between two more.
-    In ``step()`` view k + 1's preprocess and binning are issued on a second
-    stream while view k renders, takes its loss and runs the raster backward
-    on the caller's stream; the projection backward of an early view runs on
-    a third stream, that of the last ndefer views in the Adam pass (one read
-    of the parameters for all of them); events order every reuse of a set or
-    buffer and every hand-over.  ``forward_view`` / ``backward_view`` run
+    In ``step()`` the first view is binned on the caller's stream (its
+    records come from the previous step's Adam pass) while the other views'
+    preprocess runs in one pass over the parameters on a side stream; view
+    k + 1's binning is then issued on a side stream (two alternating ones
+    for batches of more than 8 views, ``bin_streams``) while view k renders,
+    takes its loss and runs the raster backward on the caller's stream; the
+    projection backward of an early view runs on another stream, that of the
+    last ndefer views in the Adam pass (one read of the parameters for all
+    of them); events order every reuse of a set or buffer and every
+    hand-over.  ``forward_view`` / ``backward_view`` run
     one view's stages in order on the current stream."""
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
                  pair_capacity=None, record_tiles=False, segment_len="auto", fuse_next_preprocess=True,
-                 max_fused_views=GS_MAX_FUSED_VIEWS):
+                 max_fused_views=GS_MAX_FUSED_VIEWS, bin_streams="auto"):
         p = torch.as_tensor(params, dtype=torch.float32)
         assert p.ndim == 2 and p.shape[0] == 59
         self.device = torch.device(device)
@@ -495,7 +499,14 @@ class TrainStep:
         self.M_dev = torch.zeros(len(self.views), dtype=torch.int64, device=self.device)
         self.M_host = torch.zeros(len(self.views), dtype=torch.int64, pin_memory=True)
         self._set_cap = [0] * len(self.views)       # capacity of the set each view was binned into
-        self.side = torch.cuda.Stream(device=self.device)      # preprocess + binning of the next view
+        self.side = torch.cuda.Stream(device=self.device)      # preprocess + binning of the next views
+        self.side2 = torch.cuda.Stream(device=self.device)     # binning of every other view
+        # binnings in flight beside the rendered view (three sets allow two):
+        # with few views a view's render chain outlasts the next binning and a
+        # second binning beside it only slows it (4 views: 3.71 vs 3.79 ms per
+        # step); with many, the binnings bound the step (16 views: 57.2 vs
+        # 53.8 ms)
+        self.bin_streams = (2 if len(cameras) > 8 else 1) if bin_streams == "auto" else int(bin_streams)
         self.gstream = torch.cuda.Stream(device=self.device)   # projection backward
         self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
         # step()'s Adam pass also runs the next step's first preprocess on the
@@ -736,12 +747,19 @@ class TrainStep:
         self.prepare_view(0, sync=False)
         first_done = torch.cuda.Event()
         first_done.record(main)
+        pre_done = None
         if nv > 1:
             # the other views' preprocess, one pass over the parameters, on
             # the side stream beside the first view's binning
             with torch.cuda.stream(self.side):
                 self.side.wait_event(first_done if self.preprocess_after_first else start)
                 self.preprocess_views(range(1, nv))
+                pre_done = torch.cuda.Event()
+                pre_done.record(self.side)
+        # views 1, 2, 3, ... are binned on the side streams in turn, so two
+        # binnings (sets k + 1 and k + 2) can run beside view k
+        sides = [self.side, self.side2][:max(1, min(2, self.bin_streams, self.nsets - 1))]
+        bin_done = [None] * len(sides)
         for k in range(nv):
             self.render_view(k)
             if k < self.nfirst and proj_done[k % 2] is not None:
@@ -765,19 +783,26 @@ class TrainStep:
                 proj_done[k % 2] = done
             self._free[k % self.nsets] = raster_done if k + self.nsets < nv else None
             if k + 1 < nv:
-                with torch.cuda.stream(self.side):
-                    if k == 0:
-                        self.side.wait_event(first_done)       # the first view's binning goes first
+                sd = sides[k % len(sides)]
+                with torch.cuda.stream(sd):
+                    if k < len(sides):
+                        sd.wait_event(first_done)              # the first view's binning goes first
+                        if sd is not self.side:
+                            sd.wait_event(pre_done)
                     prev = self._free[(k + 1) % self.nsets]
                     if prev is not None:
-                        self.side.wait_event(prev)
+                        sd.wait_event(prev)
                     self.prepare_view(k + 1, sync=False, preprocess=False)
                     ready = torch.cuda.Event()
-                    ready.record(self.side)
+                    ready.record(sd)
+                    bin_done[k % len(sides)] = ready
                 main.wait_event(ready)
         # pair counts to the host, after the last binning
         with torch.cuda.stream(self.side):
             self.side.wait_event(first_done)
+            for ev in bin_done[1:]:
+                if ev is not None:
+                    self.side.wait_event(ev)
             self.M_host.copy_(self.M_dev, non_blocking=True)
             self._counts_read = torch.cuda.Event()
             self._counts_read.record(self.side)
