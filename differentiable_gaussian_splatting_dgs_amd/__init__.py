@@ -489,7 +489,16 @@ class TrainStep:
             pair_capacity = max(1 << 20, 24 * n)       # grown on demand
         self.pair_capacity = int(min(pair_capacity, (1 << 31) - 1))
         self.views = [View(c, tg, n, self.pair_capacity, self.device) for c, tg in zip(cameras, targets)]
-        self.nsets = min(3, max(2, len(self.views)))
+        # binnings in flight beside the rendered view: with few views a
+        # view's render chain outlasts the next binning and a second binning
+        # beside it gains nothing (4 views of 1080p: 3.680 ms per step with
+        # one, 3.689 with two); with many, the binnings bound the step (16
+        # views: 57.2 ms with one, 52.9 with two, 54.1 with three, 57.4 with
+        # four)
+        self.bin_streams = (2 if len(cameras) > 8 else 1) if bin_streams == "auto" else int(bin_streams)
+        assert 1 <= self.bin_streams <= 4
+        # a set per binning in flight, one for the rendered view and one spare
+        self.nsets = min(self.bin_streams + 2, max(2, len(self.views)))
         self._with_keys = any(v.W > 4096 or v.H > 4096 for v in self.views)
         self._cur = 0                       # set of the view last prepared
         self._curv = 0                      # the view last prepared
@@ -499,14 +508,9 @@ class TrainStep:
         self.M_dev = torch.zeros(len(self.views), dtype=torch.int64, device=self.device)
         self.M_host = torch.zeros(len(self.views), dtype=torch.int64, pin_memory=True)
         self._set_cap = [0] * len(self.views)       # capacity of the set each view was binned into
-        self.side = torch.cuda.Stream(device=self.device)      # preprocess + binning of the next views
-        self.side2 = torch.cuda.Stream(device=self.device)     # binning of every other view
-        # binnings in flight beside the rendered view (three sets allow two):
-        # with few views a view's render chain outlasts the next binning and a
-        # second binning beside it only slows it (4 views: 3.71 vs 3.79 ms per
-        # step); with many, the binnings bound the step (16 views: 57.2 vs
-        # 53.8 ms)
-        self.bin_streams = (2 if len(cameras) > 8 else 1) if bin_streams == "auto" else int(bin_streams)
+        # preprocess + binning of the next views, and further binning streams
+        self.side = torch.cuda.Stream(device=self.device)
+        self.sides = [self.side] + [torch.cuda.Stream(device=self.device) for _ in range(self.bin_streams - 1)]
         self.gstream = torch.cuda.Stream(device=self.device)   # projection backward
         self.ws_loss = _bytes(max(gs_workspace_size(GS_OP_LOSS, 0, v.W, v.H) for v in self.views), self.device)
         # step()'s Adam pass also runs the next step's first preprocess on the
@@ -758,7 +762,7 @@ class TrainStep:
                 pre_done.record(self.side)
         # views 1, 2, 3, ... are binned on the side streams in turn, so two
         # binnings (sets k + 1 and k + 2) can run beside view k
-        sides = [self.side, self.side2][:max(1, min(2, self.bin_streams, self.nsets - 1))]
+        sides = self.sides[:max(1, min(len(self.sides), self.nsets - 1))]
         bin_done = [None] * len(sides)
         for k in range(nv):
             self.render_view(k)
