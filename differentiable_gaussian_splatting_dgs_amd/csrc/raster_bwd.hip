@@ -13,10 +13,10 @@
 //    fp32 arithmetic as the forward, so exactly the composited set is
 //    visited.  The nine partials of a Gaussian are summed over a lane's
 //    pixels in registers, then over the wave by two lane-half swaps that fold
-//    several values at once (permlane32/16 swap) and three DPP row steps
-//    (to half-row totals), and parked in LDS; at the end of each chunk 16-lane rows turn them into
-//    gradients and add them with nine global float atomics per (Gaussian,
-//    wave), one coalesced request per Gaussian.
+//    several values at once (permlane32/16 swap) and four DPP row steps
+//    (to row totals), and parked in LDS; at the end of each chunk 16-lane
+//    rows turn them into gradients and add them with nine global float
+//    atomics per (Gaussian, wave), one coalesced request per Gaussian.
 //
 //  k_project_bwd -- one thread per visible Gaussian: the chain rule of the
 //    projection from the screen-space gradients to all 59 parameters
@@ -31,7 +31,7 @@ namespace gs {
 namespace {
 
 constexpr int kG2 = 12;   // floats per Gaussian in the screen-gradient buffer
-constexpr int kAcc = 19;  // LDS stride of a chunk entry's 2 x 9 half sums (odd: no bank conflicts)
+constexpr int kAcc = 9;   // LDS stride of a chunk entry's nine sums (odd: no bank conflicts)
 
 __device__ __forceinline__ float f_of(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t u_of(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -72,16 +72,22 @@ __device__ __forceinline__ float wave_total_lane63(float v) {
   return v;
 }
 
+// Sum over each 16-lane row; every lane ends with its row's total.
+__device__ __forceinline__ float row_sum(float v) {
+  v = half_row_sum(v);
+  return v + f_of(__builtin_amdgcn_update_dpp(0, u_of(v), 0x140, 0xF, 0xF, false));   // row_mirror
+}
+
 // Sums of nine per-lane values over the wave.  The first eight are folded
-// so each fold serves several values: the two 8-lane halves of q0 rows
-// 0..3 end with the half totals of v0, v2, v1, v3; of q1 rows with v4, v6,
-// v5, v7.  The ninth has no partner and takes the plain DPP reduction
-// (six steps, against two folds with a zero register plus three steps).
+// so each fold serves several values: rows 0..3 of q0 end with the totals
+// of v0, v2, v1, v3, of q1 with those of v4, v6, v5, v7.  The ninth has no
+// partner and takes the plain DPP reduction (six steps, against two folds
+// with a zero register plus four steps).
 __device__ __forceinline__ void wave_sum9(const float v[9], float& q0, float& q1, float& q2) {
   const float r0 = fold32(v[0], v[1]), r1 = fold32(v[2], v[3]), r2 = fold32(v[4], v[5]);
   const float r3 = fold32(v[6], v[7]);
-  q0 = half_row_sum(fold16(r0, r1));
-  q1 = half_row_sum(fold16(r2, r3));
+  q0 = row_sum(fold16(r0, r1));
+  q1 = row_sum(fold16(r2, r3));
   q2 = wave_total_lane63(v[8]);
 }
 
@@ -95,13 +101,13 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
                                           float G0, float G1, float G2, float* __restrict__ grad2d, LdsRecs& s_rec,
                                           float* s_acc, uint32_t& nvis) {
   const int lane = threadIdx.x;
-  // lanes 0, 8, 16, ..., 56 (row r = lane / 16, half h = lane / 8 % 2)
-  // store the half sums: row r of the folded sums q0 / q1 carries sum
-  // (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r]; half sum h of sum j sits at 2 j + h
-  // of the entry's slot.  Lane 63 stores sum 8 whole at 16 (17 stays 0)
+  // lanes 0, 16, 32, 48 (row r = lane / 16) store the row totals: row r of
+  // the folded sums q0 / q1 carries sum (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r],
+  // sum j sits at j of the entry's slot; lane 63 stores sum 8.  (Nine words
+  // per entry, not two half sums each: the smaller LDS footprint admits
+  // more waves per CU.)
   const int row = lane >> 4;
   const int comp0 = ((row & 1) << 1) | (row >> 1);
-  const int half = (lane >> 3) & 1;
   // flush: lane (lane & 15) = c of its row writes gradient c; fk is its
   // factor for c >= 2 (conic A, B, C: -1/2, -1, -1/2; the rest 1)
   const int fc = lane & 15;
@@ -172,12 +178,12 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       // keeps the last DPP step's adds out of the store branch below, where
       // they could not fuse with their DPP moves
       asm volatile("" : "+v"(q0s), "+v"(q1s), "+v"(q2s));
-      if ((lane & 7) == 0) {
-        float* acc = s_acc + k * kAcc + half;
-        acc[2 * comp0] = q0s;
-        acc[8 + 2 * comp0] = q1s;
+      if ((lane & 15) == 0) {
+        float* acc = s_acc + k * kAcc;
+        acc[comp0] = q0s;
+        acc[4 + comp0] = q1s;
       }
-      if (lane == 63) s_acc[k * kAcc + 16] = q2s;
+      if (lane == 63) s_acc[k * kAcc + 8] = q2s;
       written |= 1ull << k;
     }
     // the chunk's entries leave four at a time, one 16-lane row each (lane
@@ -197,12 +203,12 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       const int kk = row == 0 ? ks[0] : (row == 1 ? ks[1] : (row == 2 ? ks[2] : ks[3]));
       if (kk >= 0 && fc < 9) {
         const float* acc = s_acc + kk * kAcc;
-        const float x = acc[2 * fc] + acc[2 * fc + 1];
+        const float x = acc[fc];
         const float4 a = s_rec.r[kk].a;
         const float2 d = s_rec.r[kk].d;   // -C/2, index bits
         const float m1 = fc == 0 ? -2.0f * a.z : (fc == 1 ? -2.0f * d.x : fk);
         // the mean gradients also take the other mean sum (lanes 0 and 1)
-        const float gval = fc < 2 ? fmaf(m1, x, -a.w * (acc[2 * (fc ^ 1)] + acc[2 * (fc ^ 1) + 1])) : m1 * x;
+        const float gval = fc < 2 ? fmaf(m1, x, -a.w * acc[fc ^ 1]) : m1 * x;
         const int32_t gi = __builtin_bit_cast(int32_t, d.y);
         if (gval != 0.0f) unsafeAtomicAdd(grad2d + size_t(gi) * kG2 + fc, gval);
       }
@@ -229,7 +235,6 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
   __shared__ LdsRecs s_rec;
   __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
   __builtin_amdgcn_s_setprio(kRasterPrio);   // (as the forward)
-  s_acc[threadIdx.x * kAcc + 17] = 0.0f;     // the unused half of sum 8
   const SplitLayout sl = split_layout(W, H);
   const SplitState sp = split_state(const_cast<void*>(split), sl);
   const int lane = threadIdx.x;
