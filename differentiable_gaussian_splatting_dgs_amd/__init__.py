@@ -79,7 +79,8 @@ def lib():
     L.gs_version.restype = C.c_int
     L.gs_workspace_size.argtypes = [C.c_int, _i64, _i32, _i32, _i64, C.POINTER(_sz)]
     L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _sz, _P]
-    L.gs_preprocess_views.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _i32, _P, _P, _P, _P, _P, _sz, _P]
+    L.gs_preprocess_views.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _i32, _P, _P, _P, _P, _i32, _P, _sz,
+                                      _P]
     L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
     L.gs_bin_sort_async.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
     L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
@@ -181,17 +182,19 @@ def gs_preprocess(params, n, ld, cam, proj, vis_idx, vis_count, union_flags, wor
                               _stream(stream)), "gs_preprocess")
 
 
-def gs_preprocess_views(params, n, ld, cams, proj, vis_idx, vis_count, union_flags, workspace, stream=None):
+def gs_preprocess_views(params, n, ld, cams, proj, vis_idx, vis_count, union_flags, workspace, stream=None,
+                        max_workgroups=0):
     """gs_preprocess of several views in one pass over the parameters:
     ``cams``, ``proj`` and ``vis_idx`` hold one entry per view,
-    ``vis_count`` is a device int64 tensor with one count per view."""
+    ``vis_count`` is a device int64 tensor with one count per view;
+    ``max_workgroups`` > 0 caps the grid (a smaller HBM share)."""
     nv = len(cams)
     assert len(proj) == nv and len(vis_idx) == nv
     carr = (gs_camera * max(nv, 1))(*[c if isinstance(c, gs_camera) else make_camera(c) for c in cams])
     parr = (C.c_void_p * max(nv, 1))(*[t.data_ptr() for t in proj])
     varr = (C.c_void_p * max(nv, 1))(*[t.data_ptr() for t in vis_idx])
     _check(lib().gs_preprocess_views(_ptr(params), n, ld, carr, nv, parr, varr, _ptr(vis_count), _ptr(union_flags),
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     int(max_workgroups), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)), "gs_preprocess_views")
 
 
@@ -520,6 +523,7 @@ class TrainStep:
         self.fuse_next_preprocess = fuse_next_preprocess
         self._pre0 = False       # view 0's records and flags come from the last Adam pass
         self.preprocess_after_first = False   # the other views' preprocess waits for view 0's binning
+        self.preprocess_workgroups = 0        # grid cap of that preprocess (0: full)
         # the forward's checkpoints and segment list, read by the split raster
         # backward of the same view (both on the current stream, the view's
         # backward before the next view's forward); segment_len None: unsplit
@@ -740,7 +744,8 @@ class TrainStep:
                 assert grp == list(range(k0, k0 + len(grp))), "consecutive views"
                 gs_preprocess_views(self.params, self.n, self.ld, [self.views[k].cam for k in grp],
                                     [self.vproj[k] for k in grp], [self.vis_idx[k] for k in grp],
-                                    self.vis_count[k0:k0 + len(grp)], self.union_flags, self.ws_pre_views)
+                                    self.vis_count[k0:k0 + len(grp)], self.union_flags, self.ws_pre_views,
+                                    max_workgroups=self.preprocess_workgroups)
 
     def _issue_views(self, defer):
         main = torch.cuda.current_stream(self.device)

@@ -237,7 +237,8 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
 
 gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const gs_camera* cams, int32_t num_views,
                               float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                              uint8_t* union_flags, void* workspace, size_t workspace_bytes, void* stream) {
+                              uint8_t* union_flags, int32_t max_workgroups, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   REQUIRE(num_views >= 1 && num_views <= GS_MAX_PREPROCESS_VIEWS, "num_views = %d outside [1, %d]", int(num_views),
           GS_MAX_PREPROCESS_VIEWS);
   REQUIRE(cams != nullptr && proj != nullptr && vis_idx != nullptr, "cams / proj / vis_idx NULL");
@@ -254,10 +255,11 @@ gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const 
     }
   }
   REQUIRE(union_flags == nullptr || aligned(union_flags, 16), "union_flags not 16-byte aligned");
+  REQUIRE(max_workgroups >= 0, "max_workgroups = %d < 0", int(max_workgroups));
   REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
   REQUIRE(workspace_bytes >= gs::preprocess_views_ws_bytes(n, num_views), "workspace too small");
   return hip_status(gs::launch_preprocess_views(params, n, ld, c, num_views, proj, vis_idx, vis_count, union_flags,
-                                                workspace, static_cast<hipStream_t>(stream)),
+                                                max_workgroups, workspace, static_cast<hipStream_t>(stream)),
                     "gs_preprocess_views");
 }
 

@@ -43,7 +43,7 @@ struct PreViews {
 size_t preprocess_views_ws_bytes(int64_t n, int32_t num_views);
 hipError_t launch_preprocess_views(const float* params, int64_t n, int64_t ld, const CamArgs* cams, int32_t num_views,
                                    float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                                   uint8_t* union_flags, void* ws, hipStream_t st);
+                                   uint8_t* union_flags, int32_t max_workgroups, void* ws, hipStream_t st);
 
 // --- compaction of a flag array into ascending indices (compact.hip) -----
 size_t compact_ws_bytes(int64_t n);

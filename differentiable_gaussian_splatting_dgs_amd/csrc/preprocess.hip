@@ -45,12 +45,13 @@ using ArgPreViews = const __attribute__((address_space(4))) PreViews;
 // k_preprocess writes).  The cameras are read in place from the
 // kernel-argument segment (scalar loads; the struct is the kernel's only
 // argument, at the segment's start).
+// (A grid smaller than n / kPT workgroups walks the Gaussians with a
+// stride: fewer loads in flight, a smaller share of the HBM bandwidth.)
 __global__ __launch_bounds__(kPT) void k_preprocess_views(PreViews pv, const float* __restrict__ params, int64_t n,
                                                           int64_t ld, uint8_t* __restrict__ union_flags) {
-  const int64_t i = int64_t(blockIdx.x) * kPT + threadIdx.x;
-  if (i >= n) return;
   (void)pv;
   ArgPreViews* a = (ArgPreViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  for (int64_t i = int64_t(blockIdx.x) * kPT + threadIdx.x; i < n; i += int64_t(gridDim.x) * kPT) {
   const uint32_t off4 = uint32_t(i) << 2;
   float p[59];
 #pragma unroll
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(kPT) void k_preprocess_views(PreViews pv, const flo
     any = any || visible;
   }
   if (union_flags != nullptr && any) union_flags[i] = 1;
+  }
 }
 
 }  // namespace
@@ -96,7 +98,7 @@ size_t preprocess_views_ws_bytes(int64_t n, int32_t num_views) {
 
 hipError_t launch_preprocess_views(const float* params, int64_t n, int64_t ld, const CamArgs* cams, int32_t num_views,
                                    float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                                   uint8_t* union_flags, void* ws, hipStream_t st) {
+                                   uint8_t* union_flags, int32_t max_workgroups, void* ws, hipStream_t st) {
   if (num_views <= 0) return hipSuccess;
   PreViews pv{};
   pv.count = num_views;
@@ -107,8 +109,11 @@ hipError_t launch_preprocess_views(const float* params, int64_t n, int64_t ld, c
     pv.flags[w] = flags + size_t(w) * align_up(size_t(n), 256);
   }
   void* cws = static_cast<char*>(ws) + size_t(num_views) * align_up(size_t(n), 256);
-  if (n > 0)
-    k_preprocess_views<<<unsigned((n + kPT - 1) / kPT), kPT, 0, st>>>(pv, params, n, ld, union_flags);
+  if (n > 0) {
+    int64_t grid = (n + kPT - 1) / kPT;
+    if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+    k_preprocess_views<<<unsigned(grid), kPT, 0, st>>>(pv, params, n, ld, union_flags);
+  }
   hipError_t e = hipGetLastError();
   // the views' lists one after another (they share the compaction's counts)
   for (int32_t w = 0; w < num_views && e == hipSuccess; ++w)

@@ -168,14 +168,21 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
  *   vis_count    device out, [num_views] int64: view w's count at w
  *   union_flags  as gs_preprocess: set for a Gaussian visible in any of
  *                the views
+ *   max_workgroups  0: one workgroup per 256 Gaussians; else at most this
+ *                many, each walking the Gaussians with a stride (fewer
+ *                loads in flight: a caller running the call beside
+ *                latency-bound work keeps its share of the HBM bandwidth
+ *                small; the results do not depend on it)
  *   workspace    device, >= gs_workspace_size(GS_OP_PREPROCESS_VIEWS, n,
  *                num_views) bytes (the views' visibility bytes and the
  *                compaction's counts)
  * Errors: GS_ERR_INVALID_ARG for num_views outside the range, an invalid
- * camera, a NULL or misaligned buffer, or as gs_preprocess. */
+ * camera, a NULL or misaligned buffer, max_workgroups < 0, or as
+ * gs_preprocess. */
 gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const gs_camera* cams, int32_t num_views,
                               float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                              uint8_t* union_flags, void* workspace, size_t workspace_bytes, void* stream);
+                              uint8_t* union_flags, int32_t max_workgroups, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* Gaussian-tile pairs sorted by depth within each tile, and the tile ranges
  * (Grendel-GS notes, training pipeline: "find the covering Gaussians, sort

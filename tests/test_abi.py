@@ -135,21 +135,23 @@ def test_invalid_arguments_rejected_on_host():
     pbufs = (C.c_void_p * nmp)(*([16] * nmp))
     vbufs = (C.c_void_p * nmp)(*([16] * nmp))
     ws_ok = gs.gs_workspace_size(gs.GS_OP_PREPROCESS_VIEWS, 4, 2)
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 0, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, nmp, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 0, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, nmp, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
     assert b"num_views" in lib.gs_last_error()
     pbufs[1] = 20
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
     assert b"proj[1]" in lib.gs_last_error()
     pbufs[1] = 16
     vbufs[0] = None
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
     assert b"vis_idx[0]" in lib.gs_last_error()
     vbufs[0] = 16
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), ws_ok - 1, None) == 1
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), ws_ok - 1, None) == 1
     assert b"workspace" in lib.gs_last_error()
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, -1, P(256), 1 << 20, None) == 1
+    assert b"max_workgroups" in lib.gs_last_error()
     pcams[1].width = 0
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, P(256), 1 << 20, None) == 1
+    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
     assert b"camera" in lib.gs_last_error()
     # visible list: misaligned flags, small workspace
     assert lib.gs_visible_list(P(17), 10, P(16), P(16), P(256), 1 << 20, None) == 1
