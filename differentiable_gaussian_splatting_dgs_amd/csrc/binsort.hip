@@ -34,6 +34,13 @@
 namespace gs {
 namespace {
 
+// Issue priority of the binning's few-workgroup kernels (scans, the stage
+// tail, tile ranges): beside the rasterisers (priority 2) on another stream
+// their handful of waves would otherwise wait behind them, and the next
+// view's binning, which the caller's stream will wait for, stretches.  Few
+// waves: the rasterisers lose little.
+constexpr int kFewPrio = 3;
+
 constexpr int kRT = 256;                 // radix threads per block
 constexpr int kRI = 8;                   // items per thread
 constexpr int kRB = kRT * kRI;           // items per block
@@ -79,6 +86,7 @@ __global__ __launch_bounds__(kRT) void k_upsweep(const K* __restrict__ keys, con
 // grid = 256 blocks, one per digit: exclusive scan of H[d][0..nb) in place,
 // row total to rowtot[d].
 __global__ __launch_bounds__(kRT) void k_rowscan(uint32_t* __restrict__ H, int nb, uint32_t* __restrict__ rowtot) {
+  __builtin_amdgcn_s_setprio(kFewPrio);
   __shared__ uint32_t sh[kRT / 64];
   uint32_t* row = H + size_t(blockIdx.x) * nb;
   uint32_t carry = 0;
@@ -476,6 +484,7 @@ __global__ __launch_bounds__(1024) void k_stage1_tail(int64_t* __restrict__ sums
                                                       int64_t* __restrict__ m_out, const uint32_t* __restrict__ sttot,
                                                       int ns, uint32_t* __restrict__ st_start,
                                                       uint32_t* __restrict__ chunk_base) {
+  __builtin_amdgcn_s_setprio(kFewPrio);
   __shared__ int64_t sh[16];
   __shared__ uint32_t sh32[16];
   __shared__ int64_t carry;
@@ -689,6 +698,7 @@ __global__ __launch_bounds__(256) void k_count_chunk(const uint32_t* __restrict_
 __global__ __launch_bounds__(256) void k_scan_chunks(const uint32_t* __restrict__ chunk_base, StGrid sg,
                                                      const int64_t* __restrict__ m_eff, uint32_t* __restrict__ cc,
                                                      uint32_t* __restrict__ tcount) {
+  __builtin_amdgcn_s_setprio(kFewPrio);
   __shared__ uint32_t s_sum[256];
   const int s = blockIdx.x, t = threadIdx.x;
   const int S = 1 << sg.shift, L = S * S, np = 256 / L;
@@ -945,6 +955,7 @@ __device__ __forceinline__ uint32_t order_bucket(uint32_t len) {  // 0 = longest
 __global__ __launch_bounds__(kTR) void k_tile_ranges_order(int nT, const uint32_t* __restrict__ tcount,
                                                            uint32_t* __restrict__ ranges,
                                                            uint32_t* __restrict__ order) {
+  __builtin_amdgcn_s_setprio(kFewPrio);
   constexpr int kW = kTR / 64;
   __shared__ uint32_t s_all[kBk], s_before[kBk];
   __shared__ uint32_t s_cnt[kBk][kTRR][kW];  // lanes per (bucket, r, wave), then their first slots
