@@ -77,11 +77,12 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint32_t pos0 = cs - start + 1;   // list position + 1 of the chunk's entry 0
-    while (active != 0) {
-      const int k = __builtin_ctzll(active);
-      active &= active - 1;
-      const float4 a = s_rec.r[k].a;
-      const float hc = s_rec.r[k].d.x;
+    // Visits in order of the set bits.  The next visit's record is read from
+    // LDS while the current one is composited, so the read's latency is off
+    // the serial chain of the long quarters, which run with few waves
+    // beside them at the kernel's end (unrolled by two: the two records
+    // alternate between two register sets without copies).
+    const auto visit = [&](int k, const float4& a, float hc, const float4& c) {
       const float dx = pxc - a.x, dy = pyc - a.y;
       const float power = fmaf(dx, fmaf(a.z, dx, a.w * dy), (hc * dy) * dy);
       // power < -5.6 gives alpha < e^-5.6 < 1/255 for any opacity <= 1.
@@ -89,8 +90,8 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
       // turned into a per-lane value and back.)
       const uint64_t okm = __builtin_amdgcn_ballot_w64(!(power > 0.0f)) &
                            __builtin_amdgcn_ballot_w64(!(power < -5.6f)) & st.livem;
-      if (okm == 0) continue;
-      const float4 c = s_rec.r[k].c;   // opacity, r, g, b
+      if (okm == 0) return;
+      // c: opacity, r, g, b
       const float alpha = fminf(0.99f, c.x * pexp_core(power));
       const uint64_t okm2 = okm & __builtin_amdgcn_ballot_w64(!(alpha < 1.0f / 255.0f));
       const float nt = st.T * (1.0f - alpha);
@@ -112,6 +113,28 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
       st.lastp = comp ? pos1 : st.lastp;
       if constexpr (kTiles) st.read = __builtin_amdgcn_inverse_ballot_w64(stopm) ? pos1 : st.read;
       st.livem &= ~stopm;
+    };
+    if (active != 0) {
+      int k = __builtin_ctzll(active);
+      float4 aa = s_rec.r[k].a, ca = s_rec.r[k].c;
+      float ha = s_rec.r[k].d.x;
+      for (;;) {
+        active &= active - 1;
+        const int kb = active != 0 ? __builtin_ctzll(active) : k;
+        const float4 ab = s_rec.r[kb].a, cb = s_rec.r[kb].c;
+        const float hb = s_rec.r[kb].d.x;
+        visit(k, aa, ha, ca);
+        if (active == 0) break;
+        k = kb;
+        active &= active - 1;
+        const int ka = active != 0 ? __builtin_ctzll(active) : k;
+        aa = s_rec.r[ka].a;
+        ca = s_rec.r[ka].c;
+        ha = s_rec.r[ka].d.x;
+        visit(k, ab, hb, cb);
+        if (active == 0) break;
+        k = ka;
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
