@@ -78,11 +78,11 @@ def lib():
     L.gs_last_error.argtypes = []
     L.gs_version.restype = C.c_int
     L.gs_workspace_size.argtypes = [C.c_int, _i64, _i32, _i32, _i64, C.POINTER(_sz)]
-    L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _sz, _P]
-    L.gs_preprocess_views.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _i32, _P, _P, _P, _P, _i32, _P, _sz,
-                                      _P]
-    L.gs_bin_sort.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
-    L.gs_bin_sort_async.argtypes = [_P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
+    L.gs_preprocess.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P, _P, _sz, _P]
+    L.gs_preprocess_views.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _i32, _P, _P, _P, _P, _P, _i32, _P,
+                                      _sz, _P]
+    L.gs_bin_sort.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
+    L.gs_bin_sort_async.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
     L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
     L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
     L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32,
@@ -93,7 +93,7 @@ def lib():
     L.gs_sparse_adam_noalloc.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32,
                                          _f32, _P]
     L.gs_project_bwd_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, C.POINTER(gs_camera), _i32,
-                                      C.POINTER(C.c_void_p), _P, _P, _P, C.POINTER(gs_camera), _P, _P, _f32, _f32,
+                                      C.POINTER(C.c_void_p), _P, _P, _P, C.POINTER(gs_camera), _P, _P, _P, _f32, _f32,
                                       _f32, _f32, _f32, _f32, _P, _sz, _P]
     L.gs_visible_list.argtypes = [_P, _i64, _P, _P, _P, _sz, _P]
     L.gs_view_overlap.argtypes = [_P, _i64, _P, _i32, _i64, _P, _P, _P, _sz, _P]
@@ -175,17 +175,21 @@ def gs_workspace_size(op: int, n: int = 0, width: int = 0, height: int = 0, pair
     return b.value
 
 
-def gs_preprocess(params, n, ld, cam, proj, vis_idx, vis_count, union_flags, workspace, stream=None):
+def gs_preprocess(params, n, ld, cam, proj, vis_idx, vis_count, union_flags, workspace, stream=None,
+                  proj_bin=None):
+    """``proj_bin``: None, or a [n][4] float32 tensor that also receives
+    each record's last four words (what the binning reads)."""
     c = cam if isinstance(cam, gs_camera) else make_camera(cam)
-    _check(lib().gs_preprocess(_ptr(params), n, ld, C.byref(c), _ptr(proj), _ptr(vis_idx), _ptr(vis_count),
-                              _ptr(union_flags), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                              _stream(stream)), "gs_preprocess")
+    _check(lib().gs_preprocess(_ptr(params), n, ld, C.byref(c), _ptr(proj), _ptr(proj_bin), _ptr(vis_idx),
+                              _ptr(vis_count), _ptr(union_flags), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)), "gs_preprocess")
 
 
 def gs_preprocess_views(params, n, ld, cams, proj, vis_idx, vis_count, union_flags, workspace, stream=None,
-                        max_workgroups=0):
+                        max_workgroups=0, proj_bin=None):
     """gs_preprocess of several views in one pass over the parameters:
-    ``cams``, ``proj`` and ``vis_idx`` hold one entry per view,
+    ``cams``, ``proj`` and ``vis_idx`` hold one entry per view (and
+    ``proj_bin``, when given, one tensor or None per view),
     ``vis_count`` is a device int64 tensor with one count per view;
     ``max_workgroups`` > 0 caps the grid (a smaller HBM share)."""
     nv = len(cams)
@@ -193,17 +197,23 @@ def gs_preprocess_views(params, n, ld, cams, proj, vis_idx, vis_count, union_fla
     carr = (gs_camera * max(nv, 1))(*[c if isinstance(c, gs_camera) else make_camera(c) for c in cams])
     parr = (C.c_void_p * max(nv, 1))(*[t.data_ptr() for t in proj])
     varr = (C.c_void_p * max(nv, 1))(*[t.data_ptr() for t in vis_idx])
-    _check(lib().gs_preprocess_views(_ptr(params), n, ld, carr, nv, parr, varr, _ptr(vis_count), _ptr(union_flags),
-                                     int(max_workgroups), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _stream(stream)), "gs_preprocess_views")
+    barr = None
+    if proj_bin is not None:
+        assert len(proj_bin) == nv
+        barr = (C.c_void_p * max(nv, 1))(*[None if t is None else t.data_ptr() for t in proj_bin])
+    _check(lib().gs_preprocess_views(_ptr(params), n, ld, carr, nv, parr, barr, varr, _ptr(vis_count),
+                                     _ptr(union_flags), int(max_workgroups), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gs_preprocess_views")
 
 
 def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_capacity, tile_ranges, workspace,
-                tile_order=None, stream=None) -> int:
+                tile_order=None, stream=None, proj_bin=None) -> int:
     """Returns M (the pair count); raises GSError(GS_ERR_CAPACITY) with
-    ``.num_pairs`` set when M > pair_capacity."""
+    ``.num_pairs`` set when M > pair_capacity.  ``proj_bin``: None or the
+    view's dense copy from gs_preprocess."""
     m = _i64(0)
-    st = lib().gs_bin_sort(_ptr(proj), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys), _ptr(vals),
+    st = lib().gs_bin_sort(_ptr(proj), _ptr(proj_bin), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys), _ptr(vals),
                           pair_capacity, C.byref(m), _ptr(tile_ranges), _ptr(tile_order), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(stream))
     if st != GS_OK:
@@ -214,10 +224,10 @@ def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_cap
 
 
 def gs_bin_sort_async(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_capacity, num_pairs_dev,
-                      tile_ranges, workspace, tile_order=None, stream=None):
+                      tile_ranges, workspace, tile_order=None, stream=None, proj_bin=None):
     """As gs_bin_sort without blocking: M lands in num_pairs_dev (a device
     int64); M > pair_capacity leaves empty ranges (checked by the caller)."""
-    _check(lib().gs_bin_sort_async(_ptr(proj), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys),
+    _check(lib().gs_bin_sort_async(_ptr(proj), _ptr(proj_bin), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys),
                                    _ptr(vals), pair_capacity, _ptr(num_pairs_dev), _ptr(tile_ranges),
                                    _ptr(tile_order), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "gs_bin_sort_async")
@@ -281,7 +291,7 @@ def gs_sparse_adam_noalloc(params, grads, m, v, n, ld, union_flags, union_idx, u
 
 def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, union_idx, union_count, lr,
                         beta1, beta2, eps, bias_c1, bias_c2, workspace, next_cam=None, next_proj=None,
-                        next_flags=None, stream=None):
+                        next_flags=None, stream=None, next_proj_bin=None):
     """``cams`` / ``grad2d``: one camera and one screen-gradient buffer per
     fused view; ``grads`` None when no other view contributed; ``next_*``:
     the preprocess of the view rendered next, on the updated rows."""
@@ -294,7 +304,7 @@ def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, u
         nc = C.byref(next_cam if isinstance(next_cam, gs_camera) else make_camera(next_cam))
     _check(lib().gs_project_bwd_adam(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, carr, nv, parr,
                                      _ptr(union_flags), _ptr(union_idx), _ptr(union_count), nc, _ptr(next_proj),
-                                     _ptr(next_flags), lr, beta1, beta2, eps, bias_c1, bias_c2, _ptr(workspace),
+                                     _ptr(next_proj_bin), _ptr(next_flags), lr, beta1, beta2, eps, bias_c1, bias_c2, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)),
            "gs_project_bwd_adam")
 
@@ -459,6 +469,11 @@ class TrainStep:
     hand-over.  ``forward_view`` / ``backward_view`` run
     one view's stages in order on the current stream."""
 
+    # every projection also writes a dense [n][4] copy of the records' last
+    # four words per view, which the binning reads (16 bytes per Gaussian
+    # instead of a 64-byte record)
+    dense_bin = True
+
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
                  pair_capacity=None, record_tiles=False, segment_len="auto", fuse_next_preprocess=True,
                  max_fused_views=GS_MAX_FUSED_VIEWS, bin_streams="auto"):
@@ -557,6 +572,8 @@ class TrainStep:
         # pass over the parameters at the start of a step)
         self.vproj = [torch.empty((rows, GS_PROJ_WORDS), dtype=torch.float32, device=self.device)
                       for _ in self.views]
+        self.vbin = [torch.empty((rows, 4), dtype=torch.float32, device=self.device) if self.dense_bin else None
+                     for _ in self.views]
         self.union_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
         self.union_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
         self.next_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
@@ -626,7 +643,7 @@ class TrainStep:
                     self._pre0 = False
                 else:
                     gs_preprocess(self.params, self.n, self.ld, vw.cam, self.vproj[k], self.vis_idx[k],
-                                  self.vis_count[k:k + 1], self.union_flags, self.ws_pre)
+                                  self.vis_count[k:k + 1], self.union_flags, self.ws_pre, proj_bin=self.vbin[k])
         with self._stage("bin_sort"):
             self._bin_sort(k, ps)
         if sync:
@@ -643,7 +660,7 @@ class TrainStep:
         vw.num_pairs = None
         self._set_cap[k] = ps.capacity
         gs_bin_sort_async(self.vproj[k], self.n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
-                          ps.capacity, self.M_dev[k:k + 1], vw.ranges, ps.ws_sort, vw.order)
+                          ps.capacity, self.M_dev[k:k + 1], vw.ranges, ps.ws_sort, vw.order, proj_bin=self.vbin[k])
 
     def _pair_bound(self, k):
         vw = self.views[k]
@@ -745,7 +762,8 @@ class TrainStep:
                 gs_preprocess_views(self.params, self.n, self.ld, [self.views[k].cam for k in grp],
                                     [self.vproj[k] for k in grp], [self.vis_idx[k] for k in grp],
                                     self.vis_count[k0:k0 + len(grp)], self.union_flags, self.ws_pre_views,
-                                    max_workgroups=self.preprocess_workgroups)
+                                    max_workgroups=self.preprocess_workgroups,
+                                    proj_bin=[self.vbin[k] for k in grp])
 
     def _issue_views(self, defer):
         main = torch.cuda.current_stream(self.device)
@@ -837,7 +855,8 @@ class TrainStep:
                     # there, tiles 0)
                     if self._pre0:
                         self.next_flags.zero_()
-                    nxt = dict(next_cam=self.views[0].cam, next_proj=self.vproj[0], next_flags=self.next_flags)
+                    nxt = dict(next_cam=self.views[0].cam, next_proj=self.vproj[0], next_flags=self.next_flags,
+                               next_proj_bin=self.vbin[0])
                 gs_project_bwd_adam(self.params, self.grads if self.nfirst > 0 else None, self.m, self.v, self.n,
                                     self.ld, [self.views[k].cam for k in ks], [self.g2d[self._gbuf(k)] for k in ks],
                                     self.union_flags, self.union_idx, self.union_count, self.lr, self.beta1,

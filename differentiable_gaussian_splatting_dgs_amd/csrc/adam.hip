@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256) void k_project_adam(FusedViews views, float* _
     r[1] = rec[1];
     r[2] = rec[2];
     r[3] = rec[3];
+    if (fv->next_bin != nullptr) reinterpret_cast<float4*>(fv->next_bin)[i] = rec[3];
     if (visible) {
       fv->next_flags[i] = 1;
       fv->union_flags[i] = 1;

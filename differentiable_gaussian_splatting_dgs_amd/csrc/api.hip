@@ -216,7 +216,7 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
 }
 
 gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_camera* cam, float* proj,
-                        int32_t* vis_idx, int64_t* vis_count, uint8_t* union_flags, void* workspace,
+                        float* proj_bin, int32_t* vis_idx, int64_t* vis_count, uint8_t* union_flags, void* workspace,
                         size_t workspace_bytes, void* stream) {
   gs::CamArgs c;
   CHECK(check_camera(cam, c));
@@ -227,18 +227,19 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
     REQUIRE(params && proj && vis_idx, "NULL array");
     REQUIRE(aligned(proj, 16) && aligned(params, 4) && aligned(vis_idx, 4), "misaligned array");
   }
+  REQUIRE(proj_bin == nullptr || aligned(proj_bin, 16), "proj_bin not 16-byte aligned");
   REQUIRE(union_flags == nullptr || aligned(union_flags, 16), "union_flags not 16-byte aligned");
   REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
   REQUIRE(workspace_bytes >= gs::preprocess_ws_bytes(n), "workspace too small");
-  return hip_status(gs::launch_preprocess(params, n, ld, c, proj, vis_idx, vis_count, union_flags, workspace,
-                                          static_cast<hipStream_t>(stream)),
+  return hip_status(gs::launch_preprocess(params, n, ld, c, proj, proj_bin, vis_idx, vis_count, union_flags,
+                                          workspace, static_cast<hipStream_t>(stream)),
                     "gs_preprocess");
 }
 
 gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const gs_camera* cams, int32_t num_views,
-                              float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                              uint8_t* union_flags, int32_t max_workgroups, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              float* const* proj, float* const* proj_bin, int32_t* const* vis_idx,
+                              int64_t* vis_count, uint8_t* union_flags, int32_t max_workgroups, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   REQUIRE(num_views >= 1 && num_views <= GS_MAX_PREPROCESS_VIEWS, "num_views = %d outside [1, %d]", int(num_views),
           GS_MAX_PREPROCESS_VIEWS);
   REQUIRE(cams != nullptr && proj != nullptr && vis_idx != nullptr, "cams / proj / vis_idx NULL");
@@ -254,16 +255,21 @@ gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const 
       REQUIRE(vis_idx[w] != nullptr && aligned(vis_idx[w], 4), "vis_idx[%d] NULL or misaligned", int(w));
     }
   }
+  if (proj_bin != nullptr)
+    for (int32_t w = 0; w < num_views; ++w)
+      REQUIRE(proj_bin[w] == nullptr || aligned(proj_bin[w], 16), "proj_bin[%d] not 16-byte aligned", int(w));
   REQUIRE(union_flags == nullptr || aligned(union_flags, 16), "union_flags not 16-byte aligned");
   REQUIRE(max_workgroups >= 0, "max_workgroups = %d < 0", int(max_workgroups));
   REQUIRE(workspace != nullptr && aligned(workspace, 256), "workspace NULL or not 256-byte aligned");
   REQUIRE(workspace_bytes >= gs::preprocess_views_ws_bytes(n, num_views), "workspace too small");
-  return hip_status(gs::launch_preprocess_views(params, n, ld, c, num_views, proj, vis_idx, vis_count, union_flags,
-                                                max_workgroups, workspace, static_cast<hipStream_t>(stream)),
+  return hip_status(gs::launch_preprocess_views(params, n, ld, c, num_views, proj, proj_bin, vis_idx, vis_count,
+                                                union_flags, max_workgroups, workspace,
+                                                static_cast<hipStream_t>(stream)),
                     "gs_preprocess_views");
 }
 
-gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+gs_status gs_bin_sort(const float* proj, const float* proj_bin, int64_t n, const int32_t* vis_idx,
+                      const int64_t* vis_count,
                       int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
                       int64_t* num_pairs, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
                       size_t workspace_bytes, void* stream) {
@@ -272,6 +278,7 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   REQUIRE(pair_capacity >= 0 && pair_capacity < (int64_t(1) << 31), "pair_capacity out of range");
   REQUIRE(vis_count != nullptr && num_pairs != nullptr && tile_ranges != nullptr, "NULL argument");
   if (n > 0) REQUIRE(proj && vis_idx && aligned(proj, 16), "NULL or misaligned proj / vis_idx");
+  REQUIRE(proj_bin == nullptr || aligned(proj_bin, 16), "proj_bin not 16-byte aligned");
   if (pair_capacity > 0)
     REQUIRE(vals && (keys ? aligned(keys, 8) : gs::binsort_keys_optional((width + 15) / 16, (height + 15) / 16)),
             "NULL or misaligned keys / vals (keys may be NULL only up to 256 x 256 tiles)");
@@ -280,7 +287,8 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
   hipError_t e =
-      gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, TX, TY, nullptr, workspace, pair_capacity, st);
+      gs::launch_binsort_stage1(proj, proj_bin, n, vis_idx, vis_count, TX, TY, nullptr, workspace, pair_capacity,
+                                st);
   if (e != hipSuccess) return hip_status(e, "gs_bin_sort (depth sort)");
   int64_t M = 0;
   e = hipMemcpyAsync(&M, gs::binsort_count_ptr(workspace, n, pair_capacity), sizeof(int64_t), hipMemcpyDeviceToHost,
@@ -295,7 +303,8 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
   return hip_status(e, "gs_bin_sort");
 }
 
-gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+gs_status gs_bin_sort_async(const float* proj, const float* proj_bin, int64_t n, const int32_t* vis_idx,
+                            const int64_t* vis_count,
                             int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
                             int64_t* num_pairs_dev, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
                             size_t workspace_bytes, void* stream) {
@@ -305,6 +314,7 @@ gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx
   REQUIRE(vis_count != nullptr && num_pairs_dev != nullptr && tile_ranges != nullptr, "NULL argument");
   REQUIRE(aligned(num_pairs_dev, 8), "misaligned num_pairs_dev");
   if (n > 0) REQUIRE(proj && vis_idx && aligned(proj, 16), "NULL or misaligned proj / vis_idx");
+  REQUIRE(proj_bin == nullptr || aligned(proj_bin, 16), "proj_bin not 16-byte aligned");
   if (pair_capacity > 0)
     REQUIRE(vals && (keys ? aligned(keys, 8) : gs::binsort_keys_optional((width + 15) / 16, (height + 15) / 16)),
             "NULL or misaligned keys / vals (keys may be NULL only up to 256 x 256 tiles)");
@@ -313,7 +323,8 @@ gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
   hipError_t e =
-      gs::launch_binsort_stage1(proj, n, vis_idx, vis_count, TX, TY, num_pairs_dev, workspace, pair_capacity, st);
+      gs::launch_binsort_stage1(proj, proj_bin, n, vis_idx, vis_count, TX, TY, num_pairs_dev, workspace,
+                                pair_capacity, st);
   if (e != hipSuccess) return hip_status(e, "gs_bin_sort_async (depth sort)");
   e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, -1, TX, TY, keys, vals, tile_ranges, tile_order,
                                 workspace, pair_capacity, st);
@@ -455,8 +466,9 @@ gs_status gs_sparse_adam_noalloc(float* params, float* grads, float* m, float* v
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
                               const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
                               int32_t* union_idx, int64_t* union_count, const gs_camera* next_cam,
-                              float* next_proj, uint8_t* next_flags, float lr, float beta1, float beta2, float eps,
-                              float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream) {
+                              float* next_proj, float* next_proj_bin, uint8_t* next_flags, float lr, float beta1,
+                              float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   REQUIRE(num_views >= 0 && num_views <= GS_MAX_FUSED_VIEWS, "num_views = %d outside [0, %d]", int(num_views),
           GS_MAX_FUSED_VIEWS);
   REQUIRE(num_views == 0 || (cams != nullptr && grad2d != nullptr), "cams / grad2d NULL");
@@ -482,10 +494,13 @@ gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, i
   REQUIRE(workspace_bytes >= adam_ws_bytes(n), "workspace too small");
   REQUIRE((next_cam == nullptr) == (next_proj == nullptr) && (next_cam == nullptr) == (next_flags == nullptr),
           "next_cam, next_proj and next_flags: all NULL or none");
+  REQUIRE(next_cam != nullptr || next_proj_bin == nullptr, "next_proj_bin given without next_proj");
   if (next_cam != nullptr) {
     CHECK(check_camera(next_cam, fv.next));
     REQUIRE(aligned(next_proj, 16), "next_proj not 16-byte aligned");
+    REQUIRE(next_proj_bin == nullptr || aligned(next_proj_bin, 16), "next_proj_bin not 16-byte aligned");
     fv.next_proj = next_proj;
+    fv.next_bin = next_proj_bin;
     fv.next_flags = next_flags;
     fv.union_flags = union_flags;
   }

@@ -269,7 +269,10 @@ __global__ __launch_bounds__(kRT) void k_scatter_rec(const uint32_t* __restrict_
 // Visible rank r (ascending index order): depth key, the rank itself as
 // the sort's value, and the compact record (index, x0 | x1 << 16,
 // y0 | y1 << 16, depth bits) from the projection record's last word.
+// (bin: NULL, or the records' last four words again, densely [n][4]: 16
+// bytes per Gaussian fetched instead of a 64-byte record's)
 __global__ __launch_bounds__(256) void k_depth_gather(const float4* __restrict__ proj,
+                                                      const float4* __restrict__ bin,
                                                       const int32_t* __restrict__ vis,
                                                       const int64_t* __restrict__ vis_count,
                                                       uint32_t* __restrict__ keys, uint32_t* __restrict__ vals,
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(256) void k_depth_gather(const float4* __restrict__
   const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (r >= *vis_count) return;
   const int32_t g = vis[r];
-  const float4 q3 = proj[4 * int64_t(g) + 3];
+  const float4 q3 = bin != nullptr ? bin[g] : proj[4 * int64_t(g) + 3];
   const uint32_t d = __builtin_bit_cast(uint32_t, q3.x);
   keys[r] = d;
   vals[r] = uint32_t(r);
@@ -1150,13 +1153,14 @@ int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity) {
   return carve(ws, n, pair_capacity).m_dev;
 }
 
-hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx,
+hipError_t launch_binsort_stage1(const float* proj, const float* proj_bin, int64_t n, const int32_t* vis_idx,
                                  const int64_t* vis_count, int32_t tiles_x, int32_t tiles_y, int64_t* num_pairs_dev,
                                  void* ws, int64_t pair_capacity, hipStream_t st) {
   Ws w = carve(ws, n, pair_capacity);
   const float4* P = reinterpret_cast<const float4*>(proj);
   if (n > 0) {
-    k_depth_gather<<<unsigned((n + 255) / 256), 256, 0, st>>>(P, vis_idx, vis_count, w.dkA, w.dvA, w.crec);
+    k_depth_gather<<<unsigned((n + 255) / 256), 256, 0, st>>>(P, reinterpret_cast<const float4*>(proj_bin), vis_idx,
+                                                               vis_count, w.dkA, w.dvA, w.crec);
     // stable LSD radix on the 32 depth bits: A -> B -> A -> B, then the
     // records in depth order
     for (int pass = 0; pass < 3; ++pass) {

@@ -27,8 +27,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // --- preprocess (preprocess.hip) -----------------------------------------
 size_t preprocess_ws_bytes(int64_t n);
+// proj_bin: NULL, or [n][4] that also gets each record's last four words.
 hipError_t launch_preprocess(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
-                             float* proj, int32_t* vis_idx, int64_t* vis_count,
+                             float* proj, float* proj_bin, int32_t* vis_idx, int64_t* vis_count,
                              uint8_t* union_flags, void* ws, hipStream_t st);
 // Up to kMaxPreprocessViews views in one pass over the parameters: view w's
 // records to proj[w], its visibility bytes to the w-th n-byte slice of the
@@ -37,13 +38,15 @@ constexpr int kMaxPreprocessViews = 16;
 struct PreViews {
   CamArgs cam[kMaxPreprocessViews];
   float4* proj[kMaxPreprocessViews];
+  float4* bin[kMaxPreprocessViews];   // NULL, or the dense copy of the records' last four words
   uint8_t* flags[kMaxPreprocessViews];
   int32_t count;
 };
 size_t preprocess_views_ws_bytes(int64_t n, int32_t num_views);
 hipError_t launch_preprocess_views(const float* params, int64_t n, int64_t ld, const CamArgs* cams, int32_t num_views,
-                                   float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                                   uint8_t* union_flags, int32_t max_workgroups, void* ws, hipStream_t st);
+                                   float* const* proj, float* const* proj_bin, int32_t* const* vis_idx,
+                                   int64_t* vis_count, uint8_t* union_flags, int32_t max_workgroups, void* ws,
+                                   hipStream_t st);
 
 // --- compaction of a flag array into ascending indices (compact.hip) -----
 size_t compact_ws_bytes(int64_t n);
@@ -59,7 +62,10 @@ bool binsort_keys_optional(int32_t tiles_x, int32_t tiles_y);
 // Stage 1 (asynchronous): depth sort of the visible list and the pair
 // count M, left in device memory at binsort_count_ptr(ws, ...) (and at
 // num_pairs_dev if given).
-hipError_t launch_binsort_stage1(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
+// proj_bin: NULL, or the records' last four words again, densely [n][4]
+// (what the depth gather reads, 16 instead of 64 bytes per Gaussian).
+hipError_t launch_binsort_stage1(const float* proj, const float* proj_bin, int64_t n, const int32_t* vis_idx,
+                                 const int64_t* vis_count,
                                  int32_t tiles_x, int32_t tiles_y, int64_t* num_pairs_dev, void* ws,
                                  int64_t pair_capacity, hipStream_t st);
 int64_t* binsort_count_ptr(void* ws, int64_t n, int64_t pair_capacity);
@@ -109,6 +115,7 @@ struct FusedViews {
   // it is visible there (the preprocess of the view rendered next).
   CamArgs next;
   float* next_proj;
+  float* next_bin;     // NULL, or the dense copy of the next records' last four words
   uint8_t* next_flags;
   uint8_t* union_flags;
 };

@@ -18,7 +18,7 @@ constexpr int kPT = 256;
 
 __global__ __launch_bounds__(kPT) void k_preprocess(const float* __restrict__ params, int64_t n, int64_t ld,
                                                     CamArgs cam, float4* __restrict__ proj,
-                                                    uint8_t* __restrict__ vis_flags,
+                                                    float4* __restrict__ bin, uint8_t* __restrict__ vis_flags,
                                                     uint8_t* __restrict__ union_flags) {
   const int64_t i = int64_t(blockIdx.x) * kPT + threadIdx.x;
   if (i >= n) return;
@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kPT) void k_preprocess(const float* __restrict__ pa
   r[1] = q[1];
   r[2] = q[2];
   r[3] = q[3];
+  if (bin != nullptr) bin[i] = q[3];
   vis_flags[i] = visible ? 1 : 0;
   if (union_flags != nullptr && visible) union_flags[i] = 1;
 }
@@ -83,6 +84,7 @@ __global__ __launch_bounds__(kPT) void k_preprocess_views(PreViews pv, const flo
     r[1] = q[1];
     r[2] = q[2];
     r[3] = q[3];
+    if (a->bin[w] != nullptr) a->bin[w][i] = q[3];
     a->flags[w][i] = visible ? 1 : 0;
     any = any || visible;
   }
@@ -97,8 +99,9 @@ size_t preprocess_views_ws_bytes(int64_t n, int32_t num_views) {
 }
 
 hipError_t launch_preprocess_views(const float* params, int64_t n, int64_t ld, const CamArgs* cams, int32_t num_views,
-                                   float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                                   uint8_t* union_flags, int32_t max_workgroups, void* ws, hipStream_t st) {
+                                   float* const* proj, float* const* proj_bin, int32_t* const* vis_idx,
+                                   int64_t* vis_count, uint8_t* union_flags, int32_t max_workgroups, void* ws,
+                                   hipStream_t st) {
   if (num_views <= 0) return hipSuccess;
   PreViews pv{};
   pv.count = num_views;
@@ -106,6 +109,7 @@ hipError_t launch_preprocess_views(const float* params, int64_t n, int64_t ld, c
   for (int32_t w = 0; w < num_views; ++w) {
     pv.cam[w] = cams[w];
     pv.proj[w] = reinterpret_cast<float4*>(proj[w]);
+    pv.bin[w] = proj_bin != nullptr ? reinterpret_cast<float4*>(proj_bin[w]) : nullptr;
     pv.flags[w] = flags + size_t(w) * align_up(size_t(n), 256);
   }
   void* cws = static_cast<char*>(ws) + size_t(num_views) * align_up(size_t(n), 256);
@@ -126,14 +130,14 @@ size_t preprocess_ws_bytes(int64_t n) {
 }
 
 hipError_t launch_preprocess(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
-                             float* proj, int32_t* vis_idx, int64_t* vis_count,
+                             float* proj, float* proj_bin, int32_t* vis_idx, int64_t* vis_count,
                              uint8_t* union_flags, void* ws, hipStream_t st) {
   uint8_t* flags = static_cast<uint8_t*>(ws);
   void* cws = static_cast<char*>(ws) + align_up(size_t(n), 256);
   if (n > 0) {
     const unsigned grid = unsigned((n + kPT - 1) / kPT);
-    k_preprocess<<<grid, kPT, 0, st>>>(params, n, ld, cam, reinterpret_cast<float4*>(proj), flags,
-                                       union_flags);
+    k_preprocess<<<grid, kPT, 0, st>>>(params, n, ld, cam, reinterpret_cast<float4*>(proj),
+                                       reinterpret_cast<float4*>(proj_bin), flags, union_flags);
   }
   return launch_compact(flags, n, vis_idx, vis_count, false, cws, st);
 }

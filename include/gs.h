@@ -140,6 +140,10 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
  *   params       device, [59][ld] fp32, ld >= n
  *   cam          host
  *   proj         device out, [n][GS_PROJ_WORDS], 16-byte aligned
+ *   proj_bin     device out, or NULL: [n][4] fp32, 16-byte aligned, each
+ *                record's last four words again (depth, rectangle, tile
+ *                count), densely: what gs_bin_sort reads, 16 bytes per
+ *                Gaussian instead of a 64-byte record's
  *   vis_idx      device out, [n] int32: the visible indices in ascending
  *                order in the first *vis_count entries
  *   vis_count    device out, int64 scalar
@@ -151,7 +155,7 @@ gs_status gs_workspace_size(gs_op op, int64_t n, int32_t width, int32_t height, 
  * quaternion and screen covariance, finite projection, and a non-empty
  * tile rectangle. */
 gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_camera* cam, float* proj,
-                        int32_t* vis_idx, int64_t* vis_count, uint8_t* union_flags, void* workspace,
+                        float* proj_bin, int32_t* vis_idx, int64_t* vis_count, uint8_t* union_flags, void* workspace,
                         size_t workspace_bytes, void* stream);
 
 /* gs_preprocess of several views in one pass over the parameters (the same
@@ -163,6 +167,8 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
  *                cameras
  *   proj         host array of num_views device pointers, one buffer per
  *                view: [n][GS_PROJ_WORDS], 16-byte aligned
+ *   proj_bin     NULL, or a host array of num_views device pointers (each
+ *                NULL or as gs_preprocess's proj_bin)
  *   vis_idx      host array of num_views device pointers: [n] int32 each,
  *                as gs_preprocess's
  *   vis_count    device out, [num_views] int64: view w's count at w
@@ -180,14 +186,18 @@ gs_status gs_preprocess(const float* params, int64_t n, int64_t ld, const gs_cam
  * camera, a NULL or misaligned buffer, max_workgroups < 0, or as
  * gs_preprocess. */
 gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const gs_camera* cams, int32_t num_views,
-                              float* const* proj, int32_t* const* vis_idx, int64_t* vis_count,
-                              uint8_t* union_flags, int32_t max_workgroups, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              float* const* proj, float* const* proj_bin, int32_t* const* vis_idx,
+                              int64_t* vis_count, uint8_t* union_flags, int32_t max_workgroups, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Gaussian-tile pairs sorted by depth within each tile, and the tile ranges
  * (Grendel-GS notes, training pipeline: "find the covering Gaussians, sort
  * by depth"; Odin summary page, stage task graph: range extraction).
  *   proj, vis_idx, vis_count   device, from gs_preprocess (same n, view)
+ *   proj_bin     device or NULL: gs_preprocess's proj_bin of the same view;
+ *                when given, the depths, rectangles and tile counts come
+ *                from it (16 bytes per Gaussian) instead of proj's records;
+ *                results are the same either way
  *   keys         device out, [pair_capacity] uint64: (tile << 32) | bit
  *                pattern of the fp32 depth, ascending; equal keys in
  *                ascending Gaussian index.  May be NULL when the image is
@@ -206,10 +216,10 @@ gs_status gs_preprocess_views(const float* params, int64_t n, int64_t ld, const 
  * Blocks the calling thread once, to read M.  If M > pair_capacity the call
  * writes *num_pairs = M, returns GS_ERR_CAPACITY and writes neither pairs
  * nor ranges.  pair_capacity must be < 2^31. */
-gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
-                      int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
-                      int64_t* num_pairs, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
-                      size_t workspace_bytes, void* stream);
+gs_status gs_bin_sort(const float* proj, const float* proj_bin, int64_t n, const int32_t* vis_idx,
+                      const int64_t* vis_count, int32_t width, int32_t height, uint64_t* keys, int32_t* vals,
+                      int64_t pair_capacity, int64_t* num_pairs, uint32_t* tile_ranges, uint32_t* tile_order,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* gs_bin_sort without the blocking read: the same outputs, with M written to
  * the device (same passages).
@@ -219,10 +229,10 @@ gs_status gs_bin_sort(const float* proj, int64_t n, const int32_t* vis_idx, cons
  * of those empty tiles); the caller detects this by comparing
  * *num_pairs_dev with pair_capacity once the stream has reached it.  The
  * rasterisers take pair_capacity as their num_pairs bound then. */
-gs_status gs_bin_sort_async(const float* proj, int64_t n, const int32_t* vis_idx, const int64_t* vis_count,
-                            int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
-                            int64_t* num_pairs_dev, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
-                            size_t workspace_bytes, void* stream);
+gs_status gs_bin_sort_async(const float* proj, const float* proj_bin, int64_t n, const int32_t* vis_idx,
+                            const int64_t* vis_count, int32_t width, int32_t height, uint64_t* keys, int32_t* vals,
+                            int64_t pair_capacity, int64_t* num_pairs_dev, uint32_t* tile_ranges,
+                            uint32_t* tile_order, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Front-to-back alpha compositing per 16x16 tile (Grendel-GS notes,
  * training pipeline: "alpha compositing").  Per pixel, over its tile's
@@ -409,14 +419,17 @@ gs_status gs_sparse_adam_noalloc(float* params, float* grads, float* m, float* v
  *                their records and flags from that view's gs_preprocess
  *                and zero flags.  gs_visible_list turns next_flags into
  *                the view's visible list.
+ *   next_proj_bin  NULL, or with next_proj: the rows' dense copies of the
+ *                records' last four words, as gs_preprocess's proj_bin
  *   the other arguments as gs_sparse_adam.
  * Errors: GS_ERR_INVALID_ARG for num_views outside the range, a NULL or
  * misaligned buffer, an invalid camera, or as gs_sparse_adam. */
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
                               const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
                               int32_t* union_idx, int64_t* union_count, const gs_camera* next_cam,
-                              float* next_proj, uint8_t* next_flags, float lr, float beta1, float beta2, float eps,
-                              float bias_c1, float bias_c2, void* workspace, size_t workspace_bytes, void* stream);
+                              float* next_proj, float* next_proj_bin, uint8_t* next_flags, float lr, float beta1,
+                              float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* The ascending visible list of a view from per-Gaussian visibility bytes
  * (the compaction gs_preprocess ends with; Odin summary page, "Background

@@ -61,40 +61,48 @@ def test_invalid_arguments_rejected_on_host():
     cam.width, cam.height, cam.fx, cam.fy, cam.cx, cam.cy, cam.near_z = 64, 64, 50.0, 50.0, 32.0, 32.0, 0.2
     cnt = C.c_int64(0)
     P = C.c_void_p
+    def pre(params_n, ld, camp, proj, ws_bytes=1 << 20, proj_bin=None):
+        return lib.gs_preprocess(P(16), params_n, ld, camp, proj, proj_bin, P(16), C.byref(cnt), None, P(256),
+                                 ws_bytes, None)
     # NULL camera
-    assert lib.gs_preprocess(P(16), 1, 1, None, P(16), P(16), C.byref(cnt), None, P(256), 1 << 20, None) == 1
+    assert pre(1, 1, None, P(16)) == 1
     assert b"camera" in lib.gs_last_error()
     # ld < n
-    assert lib.gs_preprocess(P(16), 10, 5, C.byref(cam), P(16), P(16), C.byref(cnt), None, P(256), 1 << 20, None) == 1
-    # misaligned proj
-    assert lib.gs_preprocess(P(16), 10, 10, C.byref(cam), P(20), P(16), C.byref(cnt), None, P(256), 1 << 20, None) == 1
+    assert pre(10, 5, C.byref(cam), P(16)) == 1
+    # misaligned proj, misaligned dense copy
+    assert pre(10, 10, C.byref(cam), P(20)) == 1
+    assert pre(10, 10, C.byref(cam), P(16), proj_bin=P(24)) == 1
+    assert b"proj_bin" in lib.gs_last_error()
     # workspace too small
-    assert lib.gs_preprocess(P(16), 10, 10, C.byref(cam), P(16), P(16), C.byref(cnt), None, P(256), 8, None) == 1
+    assert pre(10, 10, C.byref(cam), P(16), ws_bytes=8) == 1
     # bad camera size
     cam.width = 0
-    assert lib.gs_preprocess(P(16), 1, 1, C.byref(cam), P(16), P(16), C.byref(cnt), None, P(256), 1 << 20, None) == 1
+    assert pre(1, 1, C.byref(cam), P(16)) == 1
     # loss: non-finite weight, NULL image
     assert lib.gs_loss(P(16), P(16), 8, 8, C.c_float(float("nan")), C.c_float(0.0), P(16), P(16), P(256),
                        1 << 20, None) == 1
     assert lib.gs_loss(None, P(16), 8, 8, C.c_float(1.0), C.c_float(0.0), P(16), P(16), P(256), 1 << 20, None) == 1
     # bin sort: capacity beyond int32 range, negative n
     m = C.c_int64(0)
-    assert lib.gs_bin_sort(P(16), 1, P(16), P(16), 8, 8, P(16), P(16), C.c_int64(1 << 31), C.byref(m), P(16),
+    assert lib.gs_bin_sort(P(16), None, 1, P(16), P(16), 8, 8, P(16), P(16), C.c_int64(1 << 31), C.byref(m), P(16),
                            None, P(256), 1 << 30, None) == 1
-    assert lib.gs_bin_sort(P(16), -1, P(16), P(16), 8, 8, P(16), P(16), 10, C.byref(m), P(16), None, P(256),
+    assert lib.gs_bin_sort(P(16), None, -1, P(16), P(16), 8, 8, P(16), P(16), 10, C.byref(m), P(16), None, P(256),
                            1 << 30, None) == 1
     # asynchronous bin sort: NULL or misaligned device count, negative n
-    assert lib.gs_bin_sort_async(P(16), 1, P(16), P(16), 8, 8, P(16), P(16), 10, None, P(16), None, P(256),
+    assert lib.gs_bin_sort_async(P(16), None, 1, P(16), P(16), 8, 8, P(16), P(16), 10, None, P(16), None, P(256),
                                  1 << 30, None) == 1
-    assert lib.gs_bin_sort_async(P(16), 1, P(16), P(16), 8, 8, P(16), P(16), 10, P(12), P(16), None, P(256),
+    assert lib.gs_bin_sort_async(P(16), None, 1, P(16), P(16), 8, 8, P(16), P(16), 10, P(12), P(16), None, P(256),
                                  1 << 30, None) == 1
-    assert lib.gs_bin_sort_async(P(16), -1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None, P(256),
+    assert lib.gs_bin_sort_async(P(16), None, -1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None, P(256),
                                  1 << 30, None) == 1
+    assert lib.gs_bin_sort_async(P(16), P(40), 1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None,
+                                 P(256), 1 << 30, None) == 1
+    assert b"proj_bin" in lib.gs_last_error()
     # bin sort without keys: only up to 256 x 256 tiles (4128 px = 258 tiles)
-    assert lib.gs_bin_sort_async(P(16), 1, P(16), P(16), 4128, 64, None, P(16), 10, P(16), P(16), None, P(256),
+    assert lib.gs_bin_sort_async(P(16), None, 1, P(16), P(16), 4128, 64, None, P(16), 10, P(16), P(16), None, P(256),
                                  1 << 30, None) == 1
     assert b"keys may be NULL" in lib.gs_last_error()
-    assert lib.gs_bin_sort(P(16), 1, P(16), P(16), 64, 4128, None, P(16), 10, C.byref(m), P(16), None, P(256),
+    assert lib.gs_bin_sort(P(16), None, 1, P(16), P(16), 64, 4128, None, P(16), 10, C.byref(m), P(16), None, P(256),
                            1 << 30, None) == 1
     # adam: zero bias correction; more rows than the plane offsets address
     assert lib.gs_sparse_adam(P(16), P(16), P(16), P(16), 4, 4, P(16), P(16), P(16), C.c_float(1e-3),
@@ -114,7 +122,7 @@ def test_invalid_arguments_rejected_on_host():
     args = (P(16), P(16), P(16), P(16), 4, 4)
     scal = (C.c_float(1e-3), C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.1), C.c_float(0.1),
             P(256), 1 << 20, None)
-    tail = (P(16), P(16), P(16), None, None, None) + scal
+    tail = (P(16), P(16), P(16), None, None, None, None) + scal
     assert lib.gs_project_bwd_adam(*args, cams, gs.GS_MAX_FUSED_VIEWS + 1, bufs, *tail) == 1
     assert b"num_views" in lib.gs_last_error()
     bufs[1] = 20
@@ -123,11 +131,17 @@ def test_invalid_arguments_rejected_on_host():
     assert lib.gs_project_bwd_adam(*args, cams, 2, None, *tail) == 1
     # the next view's preprocess: camera, records and flags together, records aligned
     bufs[1] = 16
-    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), None, P(16), *scal) == 1
-    assert b"next_cam" in lib.gs_last_error()
-    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), P(20), P(16),
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), None, None, P(16),
                                    *scal) == 1
+    assert b"next_cam" in lib.gs_last_error()
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), P(20), None,
+                                   P(16), *scal) == 1
     assert b"next_proj" in lib.gs_last_error()
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), P(16), P(24),
+                                   P(16), *scal) == 1
+    assert b"next_proj_bin" in lib.gs_last_error()
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), None, None, P(16), None, *scal) == 1
+    assert b"next_proj_bin" in lib.gs_last_error()
     # several views' preprocess: no view, too many, a misaligned record
     # buffer, a NULL list buffer, a small workspace, an invalid camera
     nmp = gs.GS_MAX_PREPROCESS_VIEWS + 1
@@ -135,23 +149,31 @@ def test_invalid_arguments_rejected_on_host():
     pbufs = (C.c_void_p * nmp)(*([16] * nmp))
     vbufs = (C.c_void_p * nmp)(*([16] * nmp))
     ws_ok = gs.gs_workspace_size(gs.GS_OP_PREPROCESS_VIEWS, 4, 2)
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 0, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, nmp, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
+
+    def pv(nv, bins=None, max_wg=0, ws_bytes=1 << 20):
+        return lib.gs_preprocess_views(P(16), 4, 4, pcams, nv, pbufs, bins, vbufs, P(16), None, max_wg, P(256),
+                                       ws_bytes, None)
+    assert pv(0) == 1
+    assert pv(nmp) == 1
     assert b"num_views" in lib.gs_last_error()
     pbufs[1] = 20
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
+    assert pv(2) == 1
     assert b"proj[1]" in lib.gs_last_error()
     pbufs[1] = 16
+    bbufs = (C.c_void_p * nmp)(*([None] * nmp))
+    bbufs[1] = 40
+    assert pv(2, bins=bbufs) == 1
+    assert b"proj_bin[1]" in lib.gs_last_error()
     vbufs[0] = None
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
+    assert pv(2) == 1
     assert b"vis_idx[0]" in lib.gs_last_error()
     vbufs[0] = 16
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), ws_ok - 1, None) == 1
+    assert pv(2, ws_bytes=ws_ok - 1) == 1
     assert b"workspace" in lib.gs_last_error()
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, -1, P(256), 1 << 20, None) == 1
+    assert pv(2, max_wg=-1) == 1
     assert b"max_workgroups" in lib.gs_last_error()
     pcams[1].width = 0
-    assert lib.gs_preprocess_views(P(16), 4, 4, pcams, 2, pbufs, vbufs, P(16), None, 0, P(256), 1 << 20, None) == 1
+    assert pv(2) == 1
     assert b"camera" in lib.gs_last_error()
     # visible list: misaligned flags, small workspace
     assert lib.gs_visible_list(P(17), 10, P(16), P(16), P(256), 1 << 20, None) == 1

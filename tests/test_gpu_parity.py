@@ -247,6 +247,21 @@ def test_async_bin_sort_overflow_leaves_empty_ranges():
                          m_dev, ranges2, ws)
     torch.cuda.synchronize()
     assert torch.equal(vals2, vals) and torch.equal(ranges2, ranges)
+    # from the dense copy of the records' last words: the same again; an
+    # overflow again leaves the ranges empty
+    assert step.vbin[0] is not None
+    keys3 = torch.full((M,), -1, dtype=torch.int64, device="cuda")
+    vals3 = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    ranges3 = torch.full((vw.T, 2), 7, dtype=torch.int32, device="cuda")
+    gs.gs_bin_sort_async(step.proj, step.n, step.vis_idx[0], step.vis_count[0:1], vw.W, vw.H, keys3, vals3, M - 1,
+                         m_dev, ranges3, ws, proj_bin=step.vbin[0])
+    torch.cuda.synchronize()
+    assert int(m_dev.item()) == M and not ranges3.any().item()
+    gs.gs_bin_sort_async(step.proj, step.n, step.vis_idx[0], step.vis_count[0:1], vw.W, vw.H, keys3, vals3, M,
+                         m_dev, ranges3, ws, proj_bin=step.vbin[0])
+    torch.cuda.synchronize()
+    assert int(m_dev.item()) == M
+    assert torch.equal(keys3, keys) and torch.equal(vals3, vals) and torch.equal(ranges3, ranges)
 
 
 @pytest.mark.parametrize("case", ["small_cut", "mid_cut"])
@@ -356,6 +371,10 @@ def test_next_step_preprocess_in_the_optimiser_pass(case):
     pre = oracle.preprocess(p1, cam)
     vis = pre["visible"]
     assert np.array_equal(step.union_flags[: step.n].cpu().numpy(), vis.astype(np.uint8)), "union flags"
+    # the dense copy the binning reads: the records' last four words, every
+    # row (updated rows from the pass, the rest from the first preprocess)
+    assert np.array_equal(step.vbin[0][: step.n].cpu().numpy().view(np.uint32),
+                          step.vproj[0][: step.n, 12:16].cpu().numpy().view(np.uint32)), "dense copy"
     step.prepare_view(0)                       # visible list from the pass's flags, then binning
     torch.cuda.synchronize()
     assert not step._pre0 and not step.next_flags.any().item(), "flags not consumed"
@@ -547,16 +566,21 @@ def test_preprocess_views_matches_per_view(case):
     for k in range(nv):
         V = int(step.vis_count[k].item())
         multi.append((step.vproj[k][:n].cpu().numpy().copy(), step.vis_idx[k][:V].cpu().numpy().copy()))
+        assert np.array_equal(step.vbin[k][:n].cpu().numpy().view(np.uint32),
+                              multi[k][0][:, 12:16].view(np.uint32)), f"v{k} dense copy"
     uf_multi = step.union_flags[:n].cpu().numpy().copy()
     step.union_flags.zero_()
     proj = torch.empty_like(step.vproj[0])
+    pbin = torch.empty_like(step.vbin[0])
     vis = torch.empty_like(step.vis_idx[0])
     cnt = torch.zeros(1, dtype=torch.int64, device=proj.device)
     for k, cam in enumerate(work.cameras):
-        gs.gs_preprocess(step.params, n, step.ld, step.views[k].cam, proj, vis, cnt, step.union_flags, step.ws_pre)
+        gs.gs_preprocess(step.params, n, step.ld, step.views[k].cam, proj, vis, cnt, step.union_flags, step.ws_pre,
+                         proj_bin=pbin)
         torch.cuda.synchronize()
         V = int(cnt.item())
         one = proj[:n].cpu().numpy()
+        assert np.array_equal(pbin[:n].cpu().numpy().view(np.uint32), one[:, 12:16].view(np.uint32))
         assert np.array_equal(one.view(np.uint32), multi[k][0].view(np.uint32)), f"v{k} records"
         assert np.array_equal(vis[:V].cpu().numpy(), multi[k][1]), f"v{k} visible list"
         pre = oracle.preprocess(work.params, cam)
