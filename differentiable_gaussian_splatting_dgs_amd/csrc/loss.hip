@@ -146,6 +146,19 @@ __device__ __forceinline__ void store_run(float* dst, const float (&o)[kRunH]) {
   for (int k = 0; k < kRunH / 4; ++k) d4[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
 }
 
+// The float `e` elements past a wave-uniform base.  With Ix = uint32_t (a
+// plane of fewer than 2^30 pixels) the byte offset is a 32-bit lane value,
+// so the access takes the scalar-base + 32-bit vector-offset form and no
+// 64-bit address arithmetic per lane.
+template <typename Ix>
+__device__ __forceinline__ const float& elem(const float* base, Ix e) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + e * Ix(4));
+}
+template <typename Ix>
+__device__ __forceinline__ float& elem(float* base, Ix e) {
+  return *reinterpret_cast<float*>(reinterpret_cast<char*>(base) + e * Ix(4));
+}
+
 // Staging of `kN` planes of a tile with its halo (42 x 42): thread t < 252
 // owns column t % 42 and rows t / 42 + 6 i (i = 0..6), so its column bound
 // is tested once per tile and its address steps by 6 rows; values outside
@@ -168,7 +181,7 @@ __device__ __forceinline__ TileId tile_id(int i, int tx, int ty) {
   return id;
 }
 
-template <int kN>
+template <typename Ix, int kN>
 __device__ __forceinline__ void stage_load(const float* const (&src)[kN], int W, int H, int ox, int oy,
                                            Staged<kN>& st) {
   const int t = threadIdx.x;
@@ -179,9 +192,9 @@ __device__ __forceinline__ void stage_load(const float* const (&src)[kN], int W,
   for (int i = 0; i < kStage; ++i) {
     const int gy = oy + r0 + kStageRows * i - kHalo;
     const bool in = colok && gy >= 0 && gy < H;
-    const size_t g = in ? size_t(gy) * W + gx : 0;
+    const Ix g = in ? Ix(gy) * Ix(W) + Ix(gx) : Ix(0);
 #pragma unroll
-    for (int m = 0; m < kN; ++m) st.v[m][i] = in ? src[m][g] : 0.0f;
+    for (int m = 0; m < kN; ++m) st.v[m][i] = in ? elem<Ix>(src[m], g) : 0.0f;
   }
 }
 
@@ -222,7 +235,9 @@ __device__ __forceinline__ TileWalk tile_walk(int ntiles) {
   return w;
 }
 
-// Per tile the per-block sums go to partial[2 i].
+// Per tile the per-block sums go to partial[2 i].  Ix: the type of a
+// pixel offset within a plane (uint32_t below 2^30 pixels, else uint64_t).
+template <typename Ix>
 __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img, const float* __restrict__ tgt, int W,
                                                   int H, int tx, int ty, SsimWindow win, float* __restrict__ maps,
                                                   float* __restrict__ partial) {
@@ -242,7 +257,7 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
   {
     const TileId id = tile_id(i, tx, ty);
     const float* const src[2] = {img + id.ch * P, tgt + id.ch * P};
-    stage_load<2>(src, W, H, id.ox, id.oy, st);
+    stage_load<Ix, 2>(src, W, H, id.ox, id.oy, st);
   }
   const int lx = t % kLX, r0 = (t / kLX) * kRunV;
   for (; i < wk.end; i += wk.step) {
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
     if (i + wk.step < wk.end) {
       const TileId nx = tile_id(i + wk.step, tx, ty);
       const float* const src[2] = {img + nx.ch * P, tgt + nx.ch * P};
-      stage_load<2>(src, W, H, nx.ox, nx.oy, st);
+      stage_load<Ix, 2>(src, W, H, nx.ox, nx.oy, st);
     }
     // horizontal: row r, columns c0 .. c0 + 7 of the four moment maps
     if (t < kTasksH) {
@@ -287,6 +302,9 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
         taps<kRunV>(win, col, m[k]);
       }
       const int x = ox + lx;
+      float* const map0 = maps + size_t(3 * ch) * P;
+      float* const map1 = map0 + P;
+      float* const map2 = map1 + P;
 #pragma unroll
       for (int q = 0; q < kRunV; ++q) {
         const int y = oy + r0 + q;
@@ -301,10 +319,10 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
         const float iB2 = __builtin_amdgcn_rcpf(B2);
         const float iD = __builtin_amdgcn_rcpf(B1) * iB2;
         const float S = A1 * A2 * iD;
-        const size_t pix = size_t(y) * W + x;
-        maps[(3 * ch + 0) * P + pix] = (2.0f * my * (A2 - A1) - 2.0f * S * mx * (B2 - B1)) * iD;
-        maps[(3 * ch + 1) * P + pix] = -S * iB2;
-        maps[(3 * ch + 2) * P + pix] = 2.0f * A1 * iD;
+        const Ix pix = Ix(y) * Ix(W) + Ix(x);
+        elem<Ix>(map0, pix) = (2.0f * my * (A2 - A1) - 2.0f * S * mx * (B2 - B1)) * iD;
+        elem<Ix>(map1, pix) = -S * iB2;
+        elem<Ix>(map2, pix) = 2.0f * A1 * iD;
         ssum += S;
         lsum += fabsf(sxy[0][r0 + q + kHalo][lx + kHalo] - sxy[1][r0 + q + kHalo][lx + kHalo]);
       }
@@ -319,11 +337,12 @@ __global__ __launch_bounds__(256) void k_ssim_fwd(const float* __restrict__ img,
   }
 }
 
-// The same tiles and walk as k_ssim_fwd; the last workgroup (which has at
+// The same tiles, walk and offset type as k_ssim_fwd; the last workgroup (which has at
 // most as many tiles as any other) first turns k_ssim_fwd's per-tile sums
 // into the loss (they are complete: k_ssim_fwd has finished), so that
 // single-workgroup reduction runs beside the other workgroups' tiles
 // rather than after them.
+template <typename Ix>
 __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img, const float* __restrict__ tgt, int W,
                                                   int H, int tx, int ty, SsimWindow win, const float* __restrict__ maps,
                                                   float w_l1, float w_ssim, float* __restrict__ dL,
@@ -341,7 +360,7 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img,
   if (i < wk.end) {
     const TileId id = tile_id(i, tx, ty);
     const float* const src[3] = {maps + (3 * id.ch) * P, maps + (3 * id.ch + 1) * P, maps + (3 * id.ch + 2) * P};
-    stage_load<3>(src, W, H, id.ox, id.oy, st);
+    stage_load<Ix, 3>(src, W, H, id.ox, id.oy, st);
   }
   if (blockIdx.x == gridDim.x - 1)   // (its LDS planes are free until the first tile)
     finish_loss(partial, ntiles, 1.0f / (3.0f * float(P)), w_l1, w_ssim, 1, loss,
@@ -357,7 +376,7 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img,
     if (i + wk.step < wk.end) {
       const TileId nx = tile_id(i + wk.step, tx, ty);
       const float* const src[3] = {maps + (3 * nx.ch) * P, maps + (3 * nx.ch + 1) * P, maps + (3 * nx.ch + 2) * P};
-      stage_load<3>(src, W, H, nx.ox, nx.oy, st);
+      stage_load<Ix, 3>(src, W, H, nx.ox, nx.oy, st);
     }
     if (t < kTasksH) {
       const int r = t / (kLX / kRunH), c0 = (t % (kLX / kRunH)) * kRunH;
@@ -371,15 +390,18 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img,
     }
     __syncthreads();
     const int x = ox + lx;
+    const float* const imc = img + ch * P;
+    const float* const tgc = tgt + ch * P;
+    float* const dlc = dL + ch * P;
     // the output pixels' image and target values, loaded before the taps
     float xv[kRunV], yv[kRunV];
 #pragma unroll
     for (int q = 0; q < kRunV; ++q) {
       const int y = oy + r0 + q;
       const bool in = x < W && y < H;
-      const size_t pix = in ? size_t(y) * W + x : 0;
-      xv[q] = in ? img[ch * P + pix] : 0.0f;
-      yv[q] = in ? tgt[ch * P + pix] : 0.0f;
+      const Ix pix = in ? Ix(y) * Ix(W) + Ix(x) : Ix(0);
+      xv[q] = in ? elem<Ix>(imc, pix) : 0.0f;
+      yv[q] = in ? elem<Ix>(tgc, pix) : 0.0f;
     }
     float b[3][kRunV];
 #pragma unroll
@@ -393,10 +415,10 @@ __global__ __launch_bounds__(256) void k_ssim_bwd(const float* __restrict__ img,
     for (int q = 0; q < kRunV; ++q) {
       const int y = oy + r0 + q;
       if (x >= W || y >= H) continue;
-      const size_t pix = size_t(y) * W + x;
+      const Ix pix = Ix(y) * Ix(W) + Ix(x);
       const float d = xv[q] - yv[q];
       const float sg = d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f);
-      dL[ch * P + pix] = w_l1 * inv * sg - w_ssim * inv * (b[0][q] + 2.0f * xv[q] * b[1][q] + yv[q] * b[2][q]);
+      elem<Ix>(dlc, pix) = w_l1 * inv * sg - w_ssim * inv * (b[0][q] + 2.0f * xv[q] * b[1][q] + yv[q] * b[2][q]);
     }
   }
 }
@@ -465,9 +487,16 @@ hipError_t launch_loss(const float* image, const float* target, int32_t width, i
     const int tx = (width + kLX - 1) / kLX, ty = (height + kLY - 1) / kLY;
     const int64_t tiles = ssim_blocks(width, height);
     // 39 KB / 40 KB of LDS per workgroup: four of each per CU
-    k_ssim_fwd<<<persistent_blocks(4, tiles), 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, partial);
-    k_ssim_bwd<<<persistent_blocks(4, tiles), 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, w_l1,
-                                                            w_ssim, dL_dimage, partial, loss);
+    const int nb = persistent_blocks(4, tiles);
+    if (P < (int64_t(1) << 30)) {
+      k_ssim_fwd<uint32_t><<<nb, 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, partial);
+      k_ssim_bwd<uint32_t><<<nb, 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, w_l1, w_ssim,
+                                               dL_dimage, partial, loss);
+    } else {
+      k_ssim_fwd<uint64_t><<<nb, 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, partial);
+      k_ssim_bwd<uint64_t><<<nb, 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, w_l1, w_ssim,
+                                               dL_dimage, partial, loss);
+    }
   } else {
     const int64_t n3 = 3 * P;
     const int nb = int((n3 + 4095) / 4096);
