@@ -108,6 +108,7 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
   // more waves per CU.)
   const int row = lane >> 4;
   const int comp0 = ((row & 1) << 1) | (row >> 1);
+  const uint32_t acc_lane = lds_addr(s_acc) + 4u * uint32_t(comp0);   // word comp0 of entry 0
   // flush: lane (lane & 15) = c of its row writes gradient c; fk is its
   // factor for c >= 2 (conic A, B, C: -1/2, -1, -1/2; the rest 1)
   const int fc = lane & 15;
@@ -179,9 +180,9 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       // they could not fuse with their DPP moves
       asm volatile("" : "+v"(q0s), "+v"(q1s), "+v"(q2s));
       if ((lane & 15) == 0) {
-        float* acc = s_acc + k * kAcc;
-        acc[comp0] = q0s;
-        acc[4 + comp0] = q1s;
+        const uint32_t acc = lds_add_uniform(acc_lane, uint32_t(k) * uint32_t(kAcc * 4));
+        lds_store1(acc, q0s);
+        lds_store1(acc + 16, q1s);
       }
       if (lane == 63) s_acc[k * kAcc + 8] = q2s;
       written |= 1ull << k;
@@ -202,13 +203,15 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       }
       const int kk = row == 0 ? ks[0] : (row == 1 ? ks[1] : (row == 2 ? ks[2] : ks[3]));
       if (kk >= 0 && fc < 9) {
-        const float* acc = s_acc + kk * kAcc;
-        const float x = acc[fc];
-        const float4 a = s_rec.r[kk].a;
-        const float2 d = s_rec.r[kk].d;   // -C/2, index bits
+        // (24-bit multiplies for the offsets: full rate)
+        const uint32_t acc = lds_addr(s_acc) + __umul24(uint32_t(kk), uint32_t(kAcc * 4));
+        const uint32_t rk = lds_addr(s_rec.r) + __umul24(uint32_t(kk), uint32_t(sizeof(LdsRec)));
+        const float x = lds_load1(acc + 4 * fc);
+        const float4 a = lds_load4(rk);
+        const float2 d = lds_load2(rk + 32);   // -C/2, index bits
         const float m1 = fc == 0 ? -2.0f * a.z : (fc == 1 ? -2.0f * d.x : fk);
         // the mean gradients also take the other mean sum (lanes 0 and 1)
-        const float gval = fc < 2 ? fmaf(m1, x, -a.w * acc[fc ^ 1]) : m1 * x;
+        const float gval = fc < 2 ? fmaf(m1, x, -a.w * lds_load1(acc + 4 * (fc ^ 1))) : m1 * x;
         const int32_t gi = __builtin_bit_cast(int32_t, d.y);
         if (gval != 0.0f) unsafeAtomicAdd(grad2d + size_t(gi) * kG2 + fc, gval);
       }

@@ -141,6 +141,36 @@ struct LdsRecs {
   LdsRec r[kChunk];
 };
 
+// LDS addresses as 32-bit byte offsets.  Record reads and sum stores go
+// through them so that an entry's address is one 32-bit add: through a
+// generic pointer the compiler forms it with a 64-bit multiply-add, a
+// quarter-rate instruction, on every visit.
+using LdsFloatL = __attribute__((address_space(3))) float;
+typedef float F4v __attribute__((ext_vector_type(4)));
+typedef float F2v __attribute__((ext_vector_type(2)));
+using LdsF4L = __attribute__((address_space(3))) F4v;
+using LdsF2L = __attribute__((address_space(3))) F2v;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((__attribute__((address_space(3))) const char*)p));
+}
+// base + off for a wave-uniform offset: the offset is kept in a scalar
+// register, opaque to the compiler (which would otherwise fold a multiply
+// into the add as that 64-bit multiply-add), so the sum is one vector add.
+__device__ __forceinline__ uint32_t lds_add_uniform(uint32_t base, uint32_t off) {
+  asm("" : "+s"(off));
+  return base + off;
+}
+__device__ __forceinline__ float4 lds_load4(uint32_t a) {
+  const auto v = *(LdsF4L*)uintptr_t(a);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float2 lds_load2(uint32_t a) {
+  const auto v = *(LdsF2L*)uintptr_t(a);
+  return make_float2(v.x, v.y);
+}
+__device__ __forceinline__ float lds_load1(uint32_t a) { return *(LdsFloatL*)uintptr_t(a); }
+__device__ __forceinline__ void lds_store1(uint32_t a, float x) { *(LdsFloatL*)uintptr_t(a) = x; }
+
 // Any lane of the wave true (the predicate's ballot, tested in scalar
 // registers).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }

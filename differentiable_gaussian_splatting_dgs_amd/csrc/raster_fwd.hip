@@ -115,22 +115,27 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
       st.livem &= ~stopm;
     };
     if (active != 0) {
+      // record k at rb + 48 k: a (u, v, -A/2, -B) at +0, c at +16, -C/2 at +32
+      const uint32_t rb = lds_addr(s_rec.r);
       int k = __builtin_ctzll(active);
-      float4 aa = s_rec.r[k].a, ca = s_rec.r[k].c;
-      float ha = s_rec.r[k].d.x;
+      uint32_t ra = lds_add_uniform(rb, uint32_t(k) * uint32_t(sizeof(LdsRec)));
+      float4 aa = lds_load4(ra), ca = lds_load4(ra + 16);
+      float ha = lds_load1(ra + 32);
       for (;;) {
         active &= active - 1;
         const int kb = active != 0 ? __builtin_ctzll(active) : k;
-        const float4 ab = s_rec.r[kb].a, cb = s_rec.r[kb].c;
-        const float hb = s_rec.r[kb].d.x;
+        const uint32_t rbb = lds_add_uniform(rb, uint32_t(kb) * uint32_t(sizeof(LdsRec)));
+        const float4 ab = lds_load4(rbb), cb = lds_load4(rbb + 16);
+        const float hb = lds_load1(rbb + 32);
         visit(k, aa, ha, ca);
         if (active == 0) break;
         k = kb;
         active &= active - 1;
         const int ka = active != 0 ? __builtin_ctzll(active) : k;
-        aa = s_rec.r[ka].a;
-        ca = s_rec.r[ka].c;
-        ha = s_rec.r[ka].d.x;
+        ra = lds_add_uniform(rb, uint32_t(ka) * uint32_t(sizeof(LdsRec)));
+        aa = lds_load4(ra);
+        ca = lds_load4(ra + 16);
+        ha = lds_load1(ra + 32);
         visit(k, ab, hb, cb);
         if (active == 0) break;
         k = ka;
