@@ -147,7 +147,7 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       bool ok = k < klim && !(power > 0.0f) && !(power < -5.6f);
       if (!wave_any(ok)) continue;
       const float4 c = s_rec.r[k].c;   // opacity, r, g, b
-      const float e = pexp_core(power);
+      const float e = aexp(power);
       const float araw = c.x * e;
       const float alpha = fminf(0.99f, araw);
       ok = ok && !(alpha < 1.0f / 255.0f);

@@ -111,20 +111,20 @@ __device__ __forceinline__ int order_tile(const uint32_t* __restrict__ order, in
 // Workgroups for nT tiles: whole groups of kXcds tiles.
 inline unsigned raster_grid(int nT) { return unsigned((nT + kXcds - 1) / kXcds * kXcds * kWPT); }
 
-// e^x for x in [-5.6, 0]: the written exponential without its range
-// checks (which never trigger there), so the same bits as pexp.
-__device__ __forceinline__ float pexp_core(float x) {
-  const float kf = rintf(x * 1.44269504088896341f);
-  float r = fmaf(-kf, 0.693145751953125f, x);
-  r = fmaf(-kf, 1.428606820309417232e-6f, r);
-  float p = 1.0f / 5040.0f;
-  p = fmaf(p, r, 1.0f / 720.0f);
-  p = fmaf(p, r, 1.0f / 120.0f);
-  p = fmaf(p, r, 1.0f / 24.0f);
-  p = fmaf(p, r, 1.0f / 6.0f);
-  p = fmaf(p, r, 0.5f);
-  p = fmaf(p, r, 1.0f);
-  p = fmaf(p, r, 1.0f);
+// e^x for x in [-5.6, 0], the compositing weight's exponential: 2^t with
+// t = x log2 e, t = k + f (k = rint(t), f = t - k exact), 2^f by a degree-5
+// polynomial (near-minimax on [-1/2, 1/2] in relative error) with fmaf,
+// then 2^k; within 6e-7 relative of e^x.  Ten instructions.
+__device__ __forceinline__ float aexp(float x) {
+  const float t = x * 1.44269504088896341f;
+  const float kf = rintf(t);
+  const float f = t - kf;
+  float p = 0x1.5bb9e4p-10f;
+  p = fmaf(p, f, 0x1.3cea7ap-7f);
+  p = fmaf(p, f, 0x1.c6b752p-5f);
+  p = fmaf(p, f, 0x1.ebf9bcp-3f);
+  p = fmaf(p, f, 0x1.62e42ap-1f);
+  p = fmaf(p, f, 1.0f);
   return ldexpf(p, static_cast<int>(kf));
 }
 

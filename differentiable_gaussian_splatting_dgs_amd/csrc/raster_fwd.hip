@@ -92,7 +92,7 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
                            __builtin_amdgcn_ballot_w64(!(power < -5.6f)) & st.livem;
       if (okm == 0) return;
       // c: opacity, r, g, b
-      const float alpha = fminf(0.99f, c.x * pexp_core(power));
+      const float alpha = fminf(0.99f, c.x * aexp(power));
       const uint64_t okm2 = okm & __builtin_amdgcn_ballot_w64(!(alpha < 1.0f / 255.0f));
       const float nt = st.T * (1.0f - alpha);
       const uint64_t stopm = okm2 & __builtin_amdgcn_ballot_w64(nt < 0.0001f);

@@ -58,6 +58,8 @@ def lib():
         i64, i32, f64 = C.c_int64, C.c_int, C.c_double
         L.or_pexp.restype = C.c_float
         L.or_pexp.argtypes = [C.c_float]
+        L.or_aexp.restype = C.c_float
+        L.or_aexp.argtypes = [C.c_float]
         L.or_num_threads.restype = C.c_int
         L.or_set_threads.argtypes = [C.c_int]
         L.or_sh_basis_f64.argtypes = [P, i64, P]
@@ -125,6 +127,12 @@ def num_threads() -> int:
 
 def pexp(x):
     f = lib().or_pexp
+    return np.array([f(float(v)) for v in np.asarray(x, np.float32).ravel()], np.float32)
+
+
+def aexp(x):
+    """The compositing weight's exponential (x in [-5.6, 0])."""
+    f = lib().or_aexp
     return np.array([f(float(v)) for v in np.asarray(x, np.float32).ravel()], np.float32)
 
 

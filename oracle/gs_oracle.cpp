@@ -25,8 +25,9 @@
 //  * fp32 "canonical" -- the forward quantities that feed a discrete decision
 //    (culling, radius, tile rectangle, alpha skip, transmittance stop, colour
 //    clamp) are evaluated in fp32 with a fixed operation order, explicit
-//    fmaf, IEEE division and square root, and the written exponential
-//    `pexp` below.  The GPU library obeys the same contract, so these
+//    fmaf, IEEE division and square root, and the written exponentials
+//    `pexp` and (compositing weight) `aexp` below.  The GPU library obeys
+//    the same contract, so these
 //    decisions, the sort keys and the image agree bit for bit.
 //  * fp64 -- the smooth function with every discrete decision frozen at the
 //    fp32 run's outcome.  Its gradient is the exact derivative the backward
@@ -91,6 +92,31 @@ float pexp(float x) {
 
 inline float xexp(float x) { return pexp(x); }
 inline double xexp(double x) { return std::exp(x); }
+
+// ---------------------------------------------------------------------------
+// The compositing weight's exponential (fp32), for x in [-5.6, 0] only: the
+// compositing rule never asks for it elsewhere (power > 0 and power < -5.6
+// are skipped first).  2^t with t = x log2 e rounded once: t = k + f with
+// k = rint(t) and f = t - k (exact, |f| <= 1/2), then 2^f by a degree-5
+// polynomial 1 + f (c1 + f (c2 + f (c3 + f (c4 + f c5)))) by Horner with
+// fmaf, then scaling by 2^k.  The coefficients are a near-minimax fit of
+// 2^f on [-1/2, 1/2] in relative error (least squares reweighted by
+// Lawson's iteration), 9.2e-8 there; with the rounding of t (at most
+// 2^-21 for |t| < 8.1, a relative 3.3e-7 in 2^t) and of the evaluation the
+// result is within 6e-7 relative of e^x.  Never subnormal: e^-5.6 > 2^-9.
+// ---------------------------------------------------------------------------
+float aexp(float x) {
+  const float t = x * 1.44269504088896341f;
+  const float kf = std::rint(t);
+  const float f = t - kf;
+  float p = 0x1.5bb9e4p-10f;
+  p = std::fma(p, f, 0x1.3cea7ap-7f);
+  p = std::fma(p, f, 0x1.c6b752p-5f);
+  p = std::fma(p, f, 0x1.ebf9bcp-3f);
+  p = std::fma(p, f, 0x1.62e42ap-1f);
+  p = std::fma(p, f, 1.0f);
+  return std::ldexp(p, static_cast<int>(kf));
+}
 
 // Real spherical harmonics of degree <= 3 (no Condon-Shortley phase), the
 // view-dependent colour of the 48 SH coefficients in the Grendel-GS
@@ -383,8 +409,9 @@ inline Step32 composite_step(float u, float v, float A, float B, float C, float 
   const float dx = pxc - u, dy = pyc - v;
   const float hA = -0.5f * A, hC = -0.5f * C, nB = -B;
   const float power = std::fma(dx, std::fma(hA, dx, nB * dy), (hC * dy) * dy);
-  if (power > 0.0f) return s;
-  const float araw = o * pexp(power);
+  // power < -5.6: o e^power < e^-5.6 < 1/255 (o <= 1), the skip below
+  if (power > 0.0f || power < -5.6f) return s;
+  const float araw = o * aexp(power);
   const float alpha = std::min(0.99f, araw);
   if (alpha < 1.0f / 255.0f) return s;
   const float nt = T * (1.0f - alpha);
@@ -692,6 +719,7 @@ void or_set_threads(int n) {
 }
 
 float or_pexp(float x) { return pexp(x); }
+float or_aexp(float x) { return aexp(x); }
 
 void or_sh_basis_f64(const double* dirs, int64_t n, double* Y) {
   for (int64_t i = 0; i < n; ++i) sh_basis<double>(dirs[3 * i], dirs[3 * i + 1], dirs[3 * i + 2], Y + 16 * i);

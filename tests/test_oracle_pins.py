@@ -43,6 +43,26 @@ def test_pexp_accuracy_and_specials():
     assert np.all(got[:-7] >= np.finfo(np.float32).tiny)  # never subnormal
 
 
+def test_aexp_accuracy_and_range():
+    """The compositing weight's exponential on [-5.6, 0]: within 6e-7
+    relative of e^x (the polynomial's 9.2e-8 on [-1/2, 1/2], the rounding
+    of x log2 e -- at most 2^-21, a relative 3.3e-7 of 2^t -- and the fp32
+    evaluation), exactly 1 at 0, nondecreasing, and below 1/255 at -5.6, so
+    skipping power < -5.6 drops no entry the rule would composite (o <= 1).
+    A wrong coefficient, sign or scaling breaks the bound."""
+    xs = np.linspace(-5.6, 0.0, 200001, dtype=np.float32)
+    got = oracle.aexp(xs).astype(np.float64)
+    ref = np.exp(xs.astype(np.float64))
+    assert np.max(np.abs(got - ref) / ref) <= 6e-7
+    assert np.all(np.diff(got) >= 0.0)
+    assert oracle.aexp([0.0])[0] == 1.0 and oracle.aexp([-0.0])[0] == 1.0
+    assert oracle.aexp([-5.6])[0] < 1.0 / 255.0
+    # integer powers of e^(ln 2) land on powers of two up to the fit's error
+    for k in range(0, 9):
+        x = np.float32(-k * math.log(2.0))
+        assert abs(float(oracle.aexp([x])[0]) - math.exp(float(x))) <= 6e-7 * math.exp(float(x))
+
+
 # ---------------------------------------------------------------------------
 # spherical harmonics (view-dependent colour of the 48 coefficients)
 # ---------------------------------------------------------------------------
