@@ -28,6 +28,7 @@ GS_OP_VIEW_OVERLAP, GS_OP_PACK, GS_OP_DENSIFY, GS_OP_PREPROCESS_VIEWS = 5, 6, 7,
 GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
 GS_MAX_FUSED_VIEWS = 16
+GS_TOUCHED_SLOTS = 16
 GS_MAX_PREPROCESS_VIEWS = 16
 GS_MAX_COUPLED_VIEWS = 65536
 GS_MAX_TILE_BLOCKS = 64
@@ -86,14 +87,14 @@ def lib():
     L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
     L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
     L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32,
-                                C.POINTER(gs_param_grads), _P, _P]
+                                C.POINTER(gs_param_grads), _P, _P, _i32, _P]
     L.gs_project_bwd.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _P, _P, _P, _P, _P]
     L.gs_sparse_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32, _f32,
                                  _P, _sz, _P]
     L.gs_sparse_adam_noalloc.argtypes = [_P, _P, _P, _P, _i64, _i64, _P, _P, _P, _f32, _f32, _f32, _f32, _f32,
                                          _f32, _P]
     L.gs_project_bwd_adam.argtypes = [_P, _P, _P, _P, _i64, _i64, C.POINTER(gs_camera), _i32,
-                                      C.POINTER(C.c_void_p), _P, _P, _P, C.POINTER(gs_camera), _P, _P, _P, _f32, _f32,
+                                      C.POINTER(C.c_void_p), _P, _P, _P, _P, C.POINTER(gs_camera), _P, _P, _P, _f32, _f32,
                                       _f32, _f32, _f32, _f32, _P, _sz, _P]
     L.gs_visible_list.argtypes = [_P, _i64, _P, _P, _P, _sz, _P]
     L.gs_view_overlap.argtypes = [_P, _i64, _P, _i32, _i64, _P, _P, _P, _sz, _P]
@@ -249,7 +250,7 @@ def gs_loss(image, target, width, height, w_l1, w_ssim, loss, dL_dimage, workspa
 
 def gs_render_bwd(proj, n, vals, tile_ranges, num_pairs, width, height, T_final, last, dL_dimage, grad2d,
                   tile_order=None, split_ws=None, segment_len=SEGMENT_LEN, param_grads=None, visits=None,
-                  stream=None):
+                  stream=None, touched=None, touched_slot=0):
     """``param_grads``: None, or (params, ld, cam, vis_idx, vis_count,
     grads) to chain the view's projection backward into the [59][ld]
     gradient planes in the same call; ``visits``: None or a device int64
@@ -263,7 +264,8 @@ def gs_render_bwd(proj, n, vals, tile_ranges, num_pairs, width, height, T_final,
     _check(lib().gs_render_bwd(_ptr(proj), n, _ptr(vals), _ptr(tile_ranges), _ptr(tile_order), num_pairs, width,
                                height, _ptr(T_final), _ptr(last), _ptr(dL_dimage), _ptr(grad2d),
                                _ptr(split_ws), _nbytes(split_ws), segment_len,
-                               None if pg is None else C.byref(pg), _ptr(visits), _stream(stream)),
+                               None if pg is None else C.byref(pg), _ptr(visits), _ptr(touched),
+                               int(touched_slot), _stream(stream)),
            "gs_render_bwd")
 
 
@@ -291,7 +293,7 @@ def gs_sparse_adam_noalloc(params, grads, m, v, n, ld, union_flags, union_idx, u
 
 def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, union_idx, union_count, lr,
                         beta1, beta2, eps, bias_c1, bias_c2, workspace, next_cam=None, next_proj=None,
-                        next_flags=None, stream=None, next_proj_bin=None):
+                        next_flags=None, stream=None, next_proj_bin=None, touched=None):
     """``cams`` / ``grad2d``: one camera and one screen-gradient buffer per
     fused view; ``grads`` None when no other view contributed; ``next_*``:
     the preprocess of the view rendered next, on the updated rows."""
@@ -303,7 +305,7 @@ def gs_project_bwd_adam(params, grads, m, v, n, ld, cams, grad2d, union_flags, u
     if next_cam is not None:
         nc = C.byref(next_cam if isinstance(next_cam, gs_camera) else make_camera(next_cam))
     _check(lib().gs_project_bwd_adam(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), n, ld, carr, nv, parr,
-                                     _ptr(union_flags), _ptr(union_idx), _ptr(union_count), nc, _ptr(next_proj),
+                                     _ptr(touched), _ptr(union_flags), _ptr(union_idx), _ptr(union_count), nc, _ptr(next_proj),
                                      _ptr(next_proj_bin), _ptr(next_flags), lr, beta1, beta2, eps, bias_c1, bias_c2, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)),
            "gs_project_bwd_adam")
@@ -473,6 +475,13 @@ class TrainStep:
     # four words per view, which the binning reads (16 bytes per Gaussian
     # instead of a 64-byte record)
     dense_bin = True
+    # the fused views' raster backward marks the rows it reaches, and the
+    # Adam pass reads only those rows' screen-space gradients: "auto" turns
+    # it on for more than 8 fused views, where those buffers outgrow the
+    # caches (at 16 views of 12 M Gaussians: the pass 8.9 -> 8.2 ms, the
+    # marking +45 us per raster backward; at 4 views of 1 M the pass gains
+    # nothing and the marking costs ~10 us per view)
+    use_touched = "auto"
 
     def __init__(self, params, cameras, targets, w_l1, w_ssim, lr, beta1, beta2, eps, device="cuda",
                  pair_capacity=None, record_tiles=False, segment_len="auto", fuse_next_preprocess=True,
@@ -550,6 +559,11 @@ class TrainStep:
         self.split_ws = (_bytes(max(gs_workspace_size(GS_OP_RASTER, 0, v.W, v.H) for v in split_views), self.device)
                          if split_views else None)
 
+    def _touched_on(self):
+        if self.use_touched == "auto":
+            return self.ndefer > 8
+        return bool(self.use_touched)
+
     def _split(self, k):
         """View k's split workspace (None when its backward runs unsplit)."""
         return self.split_ws if self.seg[k] else None
@@ -577,6 +591,10 @@ class TrainStep:
         self.union_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
         self.union_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
         self.next_flags = torch.zeros(((rows + 15) // 16) * 16, dtype=torch.uint8, device=self.device)
+        # which fused view's raster backward reached each row (byte w: fused
+        # view w), so the Adam pass reads only those screen-space rows; zero
+        # between steps (the pass clears what it reads)
+        self.touched = torch.zeros((rows, GS_TOUCHED_SLOTS), dtype=torch.uint8, device=self.device)
         self.sets = [_PairSet(n, self.pair_capacity, self.device, self._with_keys) for _ in range(self.nsets)]
         self._free = [None] * self.nsets
         self.ws_pre = _bytes(gs_workspace_size(GS_OP_PREPROCESS, n), self.device)
@@ -699,10 +717,14 @@ class TrainStep:
         # before the projection backward re-zeroes them)
         chain = not keep_grad2d and self.dens_accum is None
         pg = (self.params, self.ld, vw.cam, self.vis_idx[k], self.vis_count[k:k + 1], self.grads) if chain else None
+        # a view whose screen-space rows go to the fused Adam pass marks
+        # the rows it reaches in its slot of the touched map
+        fused = keep_grad2d and k >= self.nfirst and self._touched_on()
         with self._stage("render_bwd+project_bwd" if chain else "render_bwd", k):
             gs_render_bwd(self.vproj[k], self.n, ps.vals, vw.ranges, self._pair_bound(k), vw.W, vw.H, vw.T_final, vw.last,
                           vw.dL, self.g2d[self._gcur], vw.order, self._split(k), self.seg[k], param_grads=pg,
-                          visits=None if self.visits is None else self.visits[k:k + 1])
+                          visits=None if self.visits is None else self.visits[k:k + 1],
+                          touched=self.touched if fused else None, touched_slot=k - self.nfirst if fused else 0)
         if self.dens_accum is not None:
             gs_densify_stats(self.g2d[self._gcur], self.vis_idx[k], self.vis_count[k:k + 1], self.n,
                              self.dens_accum, self.dens_denom)
@@ -745,6 +767,7 @@ class TrainStep:
             self.grads.zero_()
             for g2 in self.g2d:
                 g2.zero_()
+            self.touched.zero_()
             if stat0 is not None:
                 self.dens_accum.copy_(stat0[0])
                 self.dens_denom.copy_(stat0[1])
@@ -860,7 +883,8 @@ class TrainStep:
                 gs_project_bwd_adam(self.params, self.grads if self.nfirst > 0 else None, self.m, self.v, self.n,
                                     self.ld, [self.views[k].cam for k in ks], [self.g2d[self._gbuf(k)] for k in ks],
                                     self.union_flags, self.union_idx, self.union_count, self.lr, self.beta1,
-                                    self.beta2, self.eps, bc1, bc2, self.ws_adam, **nxt)
+                                    self.beta2, self.eps, bc1, bc2, self.ws_adam,
+                                    touched=self.touched if self._touched_on() else None, **nxt)
                 self._pre0 = bool(nxt)
             else:
                 gs_sparse_adam(self.params, self.grads, self.m, self.v, self.n, self.ld, self.union_flags,
@@ -947,6 +971,7 @@ class TrainStep:
         self.grads.zero_()
         for g2 in self.g2d:
             g2.zero_()
+        self.touched.zero_()
         self.union_flags.zero_()
         self.next_flags.zero_()
         self._pre0 = False

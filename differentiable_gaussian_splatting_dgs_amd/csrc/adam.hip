@@ -101,7 +101,19 @@ __global__ __launch_bounds__(256) void k_project_adam(FusedViews views, float* _
   using ArgViews = const __attribute__((address_space(4))) FusedViews;
   ArgViews* fv = (ArgViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int nv = fv->count;
+  // the views that may have touched the row (all without a touched map)
+  uint32_t tbits = 0xFFFFu;
+  uint8_t* const tmap = fv->touched;
+  if (tmap != nullptr) {
+    const uint4 tb = reinterpret_cast<const uint4*>(tmap)[i];
+    const uint32_t tw[4] = {tb.x, tb.y, tb.z, tb.w};
+    tbits = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) tbits |= ((tw[b >> 2] >> (8 * (b & 3))) & 0xFFu) != 0u ? (1u << b) : 0u;
+    if (tbits != 0) reinterpret_cast<uint4*>(tmap)[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   for (int w = 0; w < nv; ++w) {
+    if (((tbits >> w) & 1u) == 0) continue;   // (a row the view's backward never reached is zero)
     float4* g2 = reinterpret_cast<float4*>(fv->grad2d[w]) + 3 * i;
     const float4 ga4 = g2[0], gb4 = g2[1], gc4 = g2[2];
     const bool nz = ga4.x != 0.f || ga4.y != 0.f || ga4.z != 0.f || ga4.w != 0.f || gb4.x != 0.f ||

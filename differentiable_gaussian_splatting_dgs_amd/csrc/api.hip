@@ -365,7 +365,8 @@ gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                         const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
                         const void* split_ws, size_t split_ws_bytes, int32_t segment_len,
-                        const gs_param_grads* param_grads, uint64_t* visits, void* stream) {
+                        const gs_param_grads* param_grads, uint64_t* visits, uint8_t* touched,
+                        int32_t touched_slot, void* stream) {
   CHECK(check_size(width, height));
   REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
   REQUIRE(num_pairs >= 0 && num_pairs < (int64_t(1) << 31), "num_pairs out of range");
@@ -375,6 +376,11 @@ gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const
   }
   if (num_pairs > 0) REQUIRE(proj && vals && aligned(proj, 16), "NULL or misaligned proj / vals");
   REQUIRE(visits == nullptr || aligned(visits, 8), "visits not 8-byte aligned");
+  if (touched != nullptr) {
+    REQUIRE(aligned(touched, 16), "touched not 16-byte aligned");
+    REQUIRE(touched_slot >= 0 && touched_slot < GS_TOUCHED_SLOTS, "touched_slot = %d out of range", touched_slot);
+    REQUIRE(param_grads == nullptr, "touched with param_grads (the screen-space rows are consumed in the call)");
+  }
   int seg_shift = 0;
   CHECK(check_split(split_ws, split_ws_bytes, width, height, segment_len, seg_shift));
   gs::CamArgs c{};
@@ -390,7 +396,8 @@ gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = gs::launch_render_bwd(proj, vals, tile_ranges, tile_order, num_pairs, width, height, T_final, last,
-                                       dL_dimage, grad2d, split_ws, seg_shift, visits, st);
+                                       dL_dimage, grad2d, touched != nullptr ? touched + touched_slot : nullptr,
+                                       split_ws, seg_shift, visits, st);
   if (e == hipSuccess && param_grads != nullptr)
     e = gs::launch_project_bwd(param_grads->params, n, param_grads->ld, c, param_grads->vis_idx,
                                param_grads->vis_count, grad2d, param_grads->grads, st);
@@ -464,16 +471,19 @@ gs_status gs_sparse_adam_noalloc(float* params, float* grads, float* m, float* v
 }
 
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
-                              const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
-                              int32_t* union_idx, int64_t* union_count, const gs_camera* next_cam,
+                              const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* touched,
+                              uint8_t* union_flags, int32_t* union_idx, int64_t* union_count,
+                              const gs_camera* next_cam,
                               float* next_proj, float* next_proj_bin, uint8_t* next_flags, float lr, float beta1,
                               float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
                               size_t workspace_bytes, void* stream) {
   REQUIRE(num_views >= 0 && num_views <= GS_MAX_FUSED_VIEWS, "num_views = %d outside [0, %d]", int(num_views),
           GS_MAX_FUSED_VIEWS);
   REQUIRE(num_views == 0 || (cams != nullptr && grad2d != nullptr), "cams / grad2d NULL");
+  REQUIRE(touched == nullptr || aligned(touched, 16), "touched not 16-byte aligned");
   gs::FusedViews fv{};
   fv.count = num_views;
+  fv.touched = touched;
   for (int32_t w = 0; w < num_views; ++w) {
     CHECK(check_camera(cams + w, fv.cam[w]));
     fv.grad2d[w] = grad2d[w];

@@ -92,7 +92,7 @@ hipError_t launch_render_fwd(const float* proj, const int32_t* vals, const uint3
 hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                              const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                             const void* split, int seg_shift, uint64_t* visits, hipStream_t st);
+                             uint8_t* touched, const void* split, int seg_shift, uint64_t* visits, hipStream_t st);
 hipError_t launch_project_bwd(const float* params, int64_t n, int64_t ld, const CamArgs& cam,
                               const int32_t* vis_idx, const int64_t* vis_count, float* grad2d, float* grads,
                               hipStream_t st);
@@ -106,10 +106,17 @@ hipError_t launch_loss(const float* image, const float* target, int32_t width, i
 // --- sparse Adam (adam.hip) ---------------------------------------------------
 // Views whose projection backward is fused into the Adam pass.
 constexpr int kMaxFusedViews = 16;
+// The touched map: a row of 16 bytes per Gaussian, byte w set by the raster
+// backward of fused view w when it flushes gradient into the row.
+constexpr int kTouchedStride = 16;
 struct FusedViews {
   CamArgs cam[kMaxFusedViews];
   float* grad2d[kMaxFusedViews];
   int32_t count;
+  // Optional: the touched map ([n][16] bytes; byte w of a row non-zero when
+  // view w may have a non-zero screen-space row there).  Rows whose byte is
+  // zero are not read; the pass clears the bytes of the rows it updates.
+  uint8_t* touched;
   // Optional (next_proj != NULL): each updated row is then projected with
   // `next` into next_proj, next_flags[row] = 1 and union_flags[row] = 1 if
   // it is visible there (the preprocess of the view rendered next).

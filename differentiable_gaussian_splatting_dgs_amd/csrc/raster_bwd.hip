@@ -98,8 +98,9 @@ template <bool kCount>
 __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const int32_t* __restrict__ vals,
                                           uint32_t start, uint32_t lo, uint32_t hi, float qx, float qy, float pxc,
                                           float pyc, uint32_t lastp, float T, float S0, float S1, float S2,
-                                          float G0, float G1, float G2, float* __restrict__ grad2d, LdsRecs& s_rec,
-                                          float* s_acc, uint32_t& nvis) {
+                                          float G0, float G1, float G2, float* __restrict__ grad2d,
+                                          uint8_t* __restrict__ touched, LdsRecs& s_rec, float* s_acc,
+                                          uint32_t& nvis) {
   const int lane = threadIdx.x;
   // lanes 0, 16, 32, 48 (row r = lane / 16) store the row totals: row r of
   // the folded sums q0 / q1 carries sum (0, 2, 1, 3)[r] / (4, 6, 5, 7)[r],
@@ -214,6 +215,9 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
         const float gval = fc < 2 ? fmaf(m1, x, -a.w * lds_load1(acc + 4 * (fc ^ 1))) : m1 * x;
         const int32_t gi = __builtin_bit_cast(int32_t, d.y);
         if (gval != 0.0f) unsafeAtomicAdd(grad2d + size_t(gi) * kG2 + fc, gval);
+        // the row's byte in the touched map: every row with a non-zero word
+        // has it set (any flushed entry marks its row)
+        if (touched != nullptr && fc == 0) touched[size_t(gi) * kTouchedStride] = 1;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -233,8 +237,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
                                                    int H, int TX, int nT, const float* __restrict__ T_final,
                                                    const uint32_t* __restrict__ last,
                                                    const float* __restrict__ dL_dimage, float* __restrict__ grad2d,
-                                                   const void* split, int seg_shift, int nhelp,
-                                                   unsigned long long* __restrict__ visits) {
+                                                   uint8_t* __restrict__ touched, const void* split, int seg_shift,
+                                                   int nhelp, unsigned long long* __restrict__ visits) {
   __shared__ LdsRecs s_rec;
   __shared__ float s_acc[kChunk * kAcc];   // a chunk's nine wave sums per entry
   __builtin_amdgcn_s_setprio(kRasterPrio);   // (as the forward)
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(const float4* __restrict__ pr
       const float G1 = inside ? dL_dimage[P + pix] : 0.0f;
       const float G2 = inside ? dL_dimage[2 * P + pix] : 0.0f;
       bwd_range<kCount>(proj, vals, start, lo, hi, qx, qy, float(px) + 0.5f, float(py) + 0.5f, lastp, T, S0, S1, S2,
-                        G0, G1, G2, grad2d, s_rec, s_acc, nvis);
+                        G0, G1, G2, grad2d, touched, s_rec, s_acc, nvis);
     }
     if (!helper) break;
   }
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256) void k_project_bwd(const float* __restrict__ p
 hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint32_t* ranges,
                              const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                              const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
-                             const void* split, int seg_shift, uint64_t* visits, hipStream_t st) {
+                             uint8_t* touched, const void* split, int seg_shift, uint64_t* visits, hipStream_t st) {
   const int TX = (width + kTile - 1) / kTile, TY = (height + kTile - 1) / kTile;
   const int nT = TX * TY;
   if (split != nullptr && !raster_split_fits(width, height)) split = nullptr;
@@ -353,12 +357,12 @@ hipError_t launch_render_bwd(const float* proj, const int32_t* vals, const uint3
   unsigned long long* const vc = reinterpret_cast<unsigned long long*>(visits);
   if (visits != nullptr)
     k_render_bwd<true><<<grid, 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order, num_pairs,
-                                            width, height, TX, nT, T_final, last, dL_dimage, grad2d, split, seg_shift,
-                                            nhelp, vc);
+                                            width, height, TX, nT, T_final, last, dL_dimage, grad2d, touched, split,
+                                            seg_shift, nhelp, vc);
   else
     k_render_bwd<false><<<grid, 64, 0, st>>>(reinterpret_cast<const float4*>(proj), vals, ranges, tile_order,
-                                             num_pairs, width, height, TX, nT, T_final, last, dL_dimage, grad2d, split,
-                                             seg_shift, nhelp, nullptr);
+                                             num_pairs, width, height, TX, nT, T_final, last, dL_dimage, grad2d,
+                                             touched, split, seg_shift, nhelp, nullptr);
   return hipGetLastError();
 }
 

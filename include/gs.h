@@ -84,6 +84,9 @@ typedef struct gs_camera {
 #define GS_GRAD2D_WORDS 12
 /* most views whose projection backward gs_project_bwd_adam fuses */
 #define GS_MAX_FUSED_VIEWS 16
+/* bytes per Gaussian in the touched map of gs_render_bwd and
+ * gs_project_bwd_adam (one slot per fused view) */
+#define GS_TOUCHED_SLOTS 16
 /* most views gs_preprocess_views projects in one call */
 #define GS_MAX_PREPROCESS_VIEWS 16
 /* most views gs_view_overlap couples in one call */
@@ -314,11 +317,19 @@ gs_status gs_loss(const float* image, const float* target, int32_t width, int32_
  *                back-propagated (the pixels that composited the entry)
  *                is ADDED to *visits -- the backward's unit of work (the
  *                counting costs an atomic add per wave)
+ *   touched, touched_slot   NULL, or the touched map: device,
+ *                [n][GS_TOUCHED_SLOTS] uint8, 16-byte aligned, and this
+ *                view's slot (0 .. GS_TOUCHED_SLOTS - 1): byte
+ *                touched_slot of every row the call adds gradient into is
+ *                set to 1 (every row with a non-zero grad2d word is marked;
+ *                a marked row may still be all zero).  Only without
+ *                param_grads.  gs_project_bwd_adam reads and clears it.
  * The discrete decisions (skip, stop, 0.99 clamp) are held at the
  * forward's; the 2D mean gradient is in pixels; depth gets none.
  * Errors: GS_ERR_INVALID_ARG for sizes out of range, NULL or misaligned
  * buffers, a split workspace of the wrong size or segment length, an
- * invalid camera or ld < n in param_grads. */
+ * invalid camera or ld < n in param_grads, a touched slot out of range or
+ * touched with param_grads. */
 typedef struct {
   const float* params;      /* device, [59][ld] fp32: the view's parameters */
   int64_t ld;               /* plane stride, >= n */
@@ -331,7 +342,8 @@ gs_status gs_render_bwd(const float* proj, int64_t n, const int32_t* vals, const
                         const uint32_t* tile_order, int64_t num_pairs, int32_t width, int32_t height,
                         const float* T_final, const uint32_t* last, const float* dL_dimage, float* grad2d,
                         const void* split_ws, size_t split_ws_bytes, int32_t segment_len,
-                        const gs_param_grads* param_grads, uint64_t* visits, void* stream);
+                        const gs_param_grads* param_grads, uint64_t* visits, uint8_t* touched,
+                        int32_t touched_slot, void* stream);
 
 /* Projection backward of one view: the chain rule from the screen-space
  * gradients to all 59 parameters (SH coefficients and view direction, EWA
@@ -403,6 +415,13 @@ gs_status gs_sparse_adam_noalloc(float* params, float* grads, float* m, float* v
  *                  view's visible set are zero: gs_render_bwd writes only
  *                  visible Gaussians, and a zero row chains to zero); chained
  *                  rows are re-zeroed.
+ *   touched        NULL, or the touched map the views' gs_render_bwd calls
+ *                  marked (fused view w in slot w; [n][GS_TOUCHED_SLOTS]
+ *                  uint8, 16-byte aligned): a listed row's grad2d row of
+ *                  view w is read only when its byte w is set, and the
+ *                  listed rows' bytes are cleared (so the map is zero again
+ *                  once every marked row was listed).  Same results as
+ *                  without it, fewer bytes read.
  *   grads          the gradients of the batch's other views ([59][ld]),
  *                  zeroed for the listed rows; or NULL: none (taken as zero,
  *                  nothing written)
@@ -425,8 +444,9 @@ gs_status gs_sparse_adam_noalloc(float* params, float* grads, float* m, float* v
  * Errors: GS_ERR_INVALID_ARG for num_views outside the range, a NULL or
  * misaligned buffer, an invalid camera, or as gs_sparse_adam. */
 gs_status gs_project_bwd_adam(float* params, float* grads, float* m, float* v, int64_t n, int64_t ld,
-                              const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* union_flags,
-                              int32_t* union_idx, int64_t* union_count, const gs_camera* next_cam,
+                              const gs_camera* cams, int32_t num_views, float* const* grad2d, uint8_t* touched,
+                              uint8_t* union_flags, int32_t* union_idx, int64_t* union_count,
+                              const gs_camera* next_cam,
                               float* next_proj, float* next_proj_bin, uint8_t* next_flags, float lr, float beta1,
                               float beta2, float eps, float bias_c1, float bias_c2, void* workspace,
                               size_t workspace_bytes, void* stream);

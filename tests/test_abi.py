@@ -123,25 +123,28 @@ def test_invalid_arguments_rejected_on_host():
     scal = (C.c_float(1e-3), C.c_float(0.9), C.c_float(0.999), C.c_float(1e-15), C.c_float(0.1), C.c_float(0.1),
             P(256), 1 << 20, None)
     tail = (P(16), P(16), P(16), None, None, None, None) + scal
-    assert lib.gs_project_bwd_adam(*args, cams, gs.GS_MAX_FUSED_VIEWS + 1, bufs, *tail) == 1
+    assert lib.gs_project_bwd_adam(*args, cams, gs.GS_MAX_FUSED_VIEWS + 1, bufs, None, *tail) == 1
     assert b"num_views" in lib.gs_last_error()
     bufs[1] = 20
-    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, *tail) == 1
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, None, *tail) == 1
     assert b"grad2d[1]" in lib.gs_last_error()
-    assert lib.gs_project_bwd_adam(*args, cams, 2, None, *tail) == 1
+    assert lib.gs_project_bwd_adam(*args, cams, 2, None, None, *tail) == 1
     # the next view's preprocess: camera, records and flags together, records aligned
     bufs[1] = 16
-    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), None, None, P(16),
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, None, P(16), P(16), P(16), C.byref(cam), None, None, P(16),
                                    *scal) == 1
     assert b"next_cam" in lib.gs_last_error()
-    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), P(20), None,
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, None, P(16), P(16), P(16), C.byref(cam), P(20), None,
                                    P(16), *scal) == 1
     assert b"next_proj" in lib.gs_last_error()
-    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), C.byref(cam), P(16), P(24),
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, None, P(16), P(16), P(16), C.byref(cam), P(16), P(24),
                                    P(16), *scal) == 1
     assert b"next_proj_bin" in lib.gs_last_error()
-    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(16), P(16), P(16), None, None, P(16), None, *scal) == 1
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, None, P(16), P(16), P(16), None, None, P(16), None, *scal) == 1
     assert b"next_proj_bin" in lib.gs_last_error()
+    # a misaligned touched map
+    assert lib.gs_project_bwd_adam(*args, cams, 2, bufs, P(24), *tail) == 1
+    assert b"touched" in lib.gs_last_error()
     # several views' preprocess: no view, too many, a misaligned record
     # buffer, a NULL list buffer, a small workspace, an invalid camera
     nmp = gs.GS_MAX_PREPROCESS_VIEWS + 1
@@ -187,28 +190,36 @@ def test_invalid_arguments_rejected_on_host():
     for seg in (0, 32, 100, 1 << 17):
         assert lib.gs_render_fwd(*fwd, P(256), need, seg, None) == 1
         assert b"segment_len" in lib.gs_last_error()
-        assert lib.gs_render_bwd(*bwd, P(256), need, seg, None, None, None) == 1
+        assert lib.gs_render_bwd(*bwd, P(256), need, seg, None, None, None, 0, None) == 1
     assert lib.gs_render_fwd(*fwd, P(272), need, 1024, None) == 1
     assert b"split_ws" in lib.gs_last_error()
-    assert lib.gs_render_bwd(*bwd, P(272), need, 1024, None, None, None) == 1
+    assert lib.gs_render_bwd(*bwd, P(272), need, 1024, None, None, None, 0, None) == 1
     assert lib.gs_render_fwd(*fwd, P(256), need - 1, 1024, None) == 1
     assert b"split_ws_bytes" in lib.gs_last_error()
-    assert lib.gs_render_bwd(*bwd, P(256), need - 1, 1024, None, None, None) == 1
+    assert lib.gs_render_bwd(*bwd, P(256), need - 1, 1024, None, None, None, 0, None) == 1
     # raster backward with the projection backward chained: camera of
     # another size, ld < n, NULL gradient planes; misaligned visit counter
     pg = gs.gs_param_grads(16, 4, C.pointer(cam), 16, 16, 16)
     cam.width = 32
-    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None) == 1
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None, 0, None) == 1
     assert b"param_grads->cam" in lib.gs_last_error()
     cam.width = 64
     pg.ld = 3
-    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None) == 1
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None, 0, None) == 1
     assert b"ld" in lib.gs_last_error()
     pg.ld, pg.grads = 4, None
-    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None) == 1
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, None, 0, None) == 1
     assert b"param_grads" in lib.gs_last_error()
-    assert lib.gs_render_bwd(*bwd, None, 0, 1024, None, P(20), None) == 1
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, None, P(20), None, 0, None) == 1
     assert b"visits" in lib.gs_last_error()
+    # touched map: misaligned, slot out of range, with param_grads
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, None, None, P(24), 0, None) == 1
+    assert b"touched" in lib.gs_last_error()
+    for slot in (-1, gs.GS_TOUCHED_SLOTS):
+        assert lib.gs_render_bwd(*bwd, None, 0, 1024, None, None, P(16), slot, None) == 1
+        assert b"touched_slot" in lib.gs_last_error()
+    assert lib.gs_render_bwd(*bwd, None, 0, 1024, C.byref(pg), None, P(16), 0, None) == 1
+    assert b"touched" in lib.gs_last_error()
     # view coupling: view count and n out of range, NULL / misaligned
     # buffers, small workspace; zero views is a no-op
     ws = gs.gs_workspace_size(gs.GS_OP_VIEW_OVERLAP, 1000, 3)

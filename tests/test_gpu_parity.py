@@ -353,6 +353,59 @@ def test_split_backward_matches_whole_list_backward(case, seg):
         assert requested.max() > pool_slots, "no pool ran out of states"
 
 
+@pytest.mark.parametrize("case", ["small_cut", "mid_cut", "ring_18"])
+def test_touched_map_reads_only_marked_rows(case):
+    """The fused views' raster backward marks the rows it reaches in the
+    touched map; the fused Adam pass with the map reads only those rows'
+    screen-space gradients.  Every row with a non-zero screen-space word has
+    its view's byte set; parameters, moments, the next view's records and
+    flags after the pass are bit for bit those of the pass without the map;
+    the map is zero afterwards.  18 ring views: 16 fused (slots 0-15), the
+    first two projected separately (they mark nothing)."""
+    import differentiable_gaussian_splatting_dgs_amd as gs
+    if case == "ring_18":
+        work = synth.plane_scene(4, 8000, 160, 96, [2 * math.pi * j / 18 for j in range(18)], 4, name="ring")
+    else:
+        work = workload_case(case)
+    step = gs.from_workload(work)
+    step.use_touched = True
+    step.step()                                    # a step with the map
+    step.run_views(defer_projection=True)
+    torch.cuda.synchronize()
+    ks = list(range(step.nfirst, len(step.views)))
+    g2 = [step.g2d[step._gbuf(k)] for k in ks]
+    tm = step.touched[: step.n].cpu().numpy()
+    assert not tm[:, len(ks):].any(), "bytes beyond the fused views"
+    marked = 0
+    for w, g in enumerate(g2):
+        nz = (g[: step.n] != 0).any(dim=1).cpu().numpy()
+        assert np.all(tm[nz, w] != 0), f"fused view {w}: a non-zero row unmarked"
+        marked += int((tm[:, w] != 0).sum())
+    save = dict(params=step.params.clone(), m=step.m.clone(), v=step.v.clone(), grads=step.grads.clone(),
+                uf=step.union_flags.clone(), nf=step.next_flags.clone(), tm=step.touched.clone(),
+                g2=[g.clone() for g in g2])
+    outs = []
+    for use in (True, False):
+        step.params.copy_(save["params"]); step.m.copy_(save["m"]); step.v.copy_(save["v"])
+        step.grads.copy_(save["grads"]); step.union_flags.copy_(save["uf"]); step.next_flags.copy_(save["nf"])
+        step.touched.copy_(save["tm"])
+        for g, s0 in zip(g2, save["g2"]):
+            g.copy_(s0)
+        step.use_touched = use
+        step.adam(fused=True)
+        step.t -= 1                                # (the same bias corrections both times)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy().copy() for t in (step.params, step.m, step.v, step.vproj[0], step.vbin[0],
+                                                      step.next_flags, step.union_flags)])
+        if use:
+            assert not step.touched.any().item(), "map not cleared"
+            assert all(not g.any().item() for g in g2), "screen-space rows left"
+    for name, a, b in zip(("params", "m", "v", "next records", "next dense copy", "next flags", "union flags"),
+                          outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), name
+    say(f"  {case}: {len(ks)} fused views, {marked} marked (row, view) of {step.n * len(ks)}")
+
+
 @pytest.mark.parametrize("case", ["small_cut", "mid_cut"])
 def test_next_step_preprocess_in_the_optimiser_pass(case):
     """step() projects the updated rows for the next step's first view inside
