@@ -75,11 +75,13 @@ __device__ __forceinline__ CamArgs arg_camera(ArgCam* c) {
 // Adam as k_adam.  The same arithmetic as the projection backward of each
 // view followed by k_adam, without writing and re-reading the gradient
 // planes; the parameters are read once for all the views.
-__global__ __launch_bounds__(256) void k_project_adam(FusedViews views, float* __restrict__ params,
-                                                      float* __restrict__ grads, float* __restrict__ m,
-                                                      float* __restrict__ v, int64_t ld, const int32_t* __restrict__ rows,
-                                                      const int64_t* __restrict__ row_count, float lr, float b1,
-                                                      float b2, float eps, float bc1, float bc2) {
+// (Three waves per SIMD, what its 48 KB of LDS per workgroup allows: the
+// register allocation is held to that, 168 VGPRs; one more register would
+// drop it to two waves.)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_project_adam(
+    FusedViews views, float* __restrict__ params, float* __restrict__ grads, float* __restrict__ m,
+    float* __restrict__ v, int64_t ld, const int32_t* __restrict__ rows, const int64_t* __restrict__ row_count,
+    float lr, float b1, float b2, float eps, float bc1, float bc2) {
   const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (s >= *row_count) return;
   const int64_t i = rows[s];
