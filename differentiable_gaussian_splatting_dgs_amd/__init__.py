@@ -29,6 +29,7 @@ GS_PROJ_WORDS = 16
 GS_GRAD2D_WORDS = 12
 GS_MAX_FUSED_VIEWS = 16
 GS_TOUCHED_SLOTS = 16
+GS_BIN_ALL, GS_BIN_DEPTH, GS_BIN_PAIRS = 0, 1, 2
 GS_MAX_PREPROCESS_VIEWS = 16
 GS_MAX_COUPLED_VIEWS = 65536
 GS_MAX_TILE_BLOCKS = 64
@@ -83,7 +84,7 @@ def lib():
     L.gs_preprocess_views.argtypes = [_P, _i64, _i64, C.POINTER(gs_camera), _i32, _P, _P, _P, _P, _P, _i32, _P,
                                       _sz, _P]
     L.gs_bin_sort.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, C.POINTER(_i64), _P, _P, _P, _sz, _P]
-    L.gs_bin_sort_async.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _P]
+    L.gs_bin_sort_async.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _P, _P, _i64, _P, _P, _P, _P, _sz, _i32, _P]
     L.gs_render_fwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32, _P]
     L.gs_loss.argtypes = [_P, _P, _i32, _i32, _f32, _f32, _P, _P, _P, _sz, _P]
     L.gs_render_bwd.argtypes = [_P, _i64, _P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _P, _sz, _i32,
@@ -225,13 +226,13 @@ def gs_bin_sort(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_cap
 
 
 def gs_bin_sort_async(proj, n, vis_idx, vis_count, width, height, keys, vals, pair_capacity, num_pairs_dev,
-                      tile_ranges, workspace, tile_order=None, stream=None, proj_bin=None):
+                      tile_ranges, workspace, tile_order=None, stream=None, proj_bin=None, part=0):
     """As gs_bin_sort without blocking: M lands in num_pairs_dev (a device
     int64); M > pair_capacity leaves empty ranges (checked by the caller)."""
-    _check(lib().gs_bin_sort_async(_ptr(proj), _ptr(proj_bin), n, _ptr(vis_idx), _ptr(vis_count), width, height, _ptr(keys),
-                                   _ptr(vals), pair_capacity, _ptr(num_pairs_dev), _ptr(tile_ranges),
+    _check(lib().gs_bin_sort_async(_ptr(proj), _ptr(proj_bin), n, _ptr(vis_idx), _ptr(vis_count), width, height,
+                                   _ptr(keys), _ptr(vals), pair_capacity, _ptr(num_pairs_dev), _ptr(tile_ranges),
                                    _ptr(tile_order), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _stream(stream)), "gs_bin_sort_async")
+                                   int(part), _stream(stream)), "gs_bin_sort_async")
 
 
 def gs_render_fwd(proj, n, vals, tile_ranges, num_pairs, width, height, image, T_final, last,
@@ -547,6 +548,10 @@ class TrainStep:
         self.fuse_next_preprocess = fuse_next_preprocess
         self._pre0 = False       # view 0's records and flags come from the last Adam pass
         self.preprocess_after_first = False   # the other views' preprocess waits for view 0's binning
+        # ... for view 0's depth sort (batches of up to 8 views: at 4 views
+        # 3.597 -> 3.588 ms per step; at 16 the long preprocess then delays
+        # view 1's binning, 51.76 -> 52.37 ms)
+        self.preprocess_after_depth = len(self.views) <= 8
         self.preprocess_workgroups = 0        # grid cap of that preprocess (0: full)
         # the forward's checkpoints and segment list, read by the split raster
         # backward of the same view (both on the current stream, the view's
@@ -644,11 +649,13 @@ class TrainStep:
         self.timer.setdefault(name, []).append((a, b))
 
     # -- one view ---------------------------------------------------------
-    def prepare_view(self, k, sync=True, preprocess=True):
+    def prepare_view(self, k, sync=True, preprocess=True, between=None):
         """Preprocess view k (unless preprocess is False: its records and
         visible list are there already) and bin/sort it into buffer set
         k % nsets.  With sync, the pair count is read (blocking) and the set
-        grown if it overflowed; without, it stays on the device in M_dev[k]."""
+        grown if it overflowed; without, it stays on the device in M_dev[k].
+        ``between``: None, or a function called (to issue work on the
+        stream) between the binning's depth sort and its pairs."""
         vw = self.views[k]
         ps = self.sets[k % self.nsets]
         self._cur = k % self.nsets
@@ -663,7 +670,7 @@ class TrainStep:
                     gs_preprocess(self.params, self.n, self.ld, vw.cam, self.vproj[k], self.vis_idx[k],
                                   self.vis_count[k:k + 1], self.union_flags, self.ws_pre, proj_bin=self.vbin[k])
         with self._stage("bin_sort"):
-            self._bin_sort(k, ps)
+            self._bin_sort(k, ps, between)
         if sync:
             M = int(self.M_dev[k].item())
             if M > ps.capacity:
@@ -673,12 +680,18 @@ class TrainStep:
                 self._bin_sort(k, ps)
             vw.num_pairs = M
 
-    def _bin_sort(self, k, ps):
+    def _bin_sort(self, k, ps, between=None):
         vw = self.views[k]
         vw.num_pairs = None
         self._set_cap[k] = ps.capacity
-        gs_bin_sort_async(self.vproj[k], self.n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
-                          ps.capacity, self.M_dev[k:k + 1], vw.ranges, ps.ws_sort, vw.order, proj_bin=self.vbin[k])
+        args = (self.vproj[k], self.n, self.vis_idx[k], self.vis_count[k:k + 1], vw.W, vw.H, ps.keys, ps.vals,
+                ps.capacity, self.M_dev[k:k + 1], vw.ranges, ps.ws_sort, vw.order)
+        if between is None:
+            gs_bin_sort_async(*args, proj_bin=self.vbin[k])
+        else:
+            gs_bin_sort_async(*args, proj_bin=self.vbin[k], part=GS_BIN_DEPTH)
+            between()
+            gs_bin_sort_async(*args, proj_bin=self.vbin[k], part=GS_BIN_PAIRS)
 
     def _pair_bound(self, k):
         vw = self.views[k]
@@ -794,7 +807,12 @@ class TrainStep:
         proj_done = [None, None]
         start = torch.cuda.Event()
         start.record(main)
-        self.prepare_view(0, sync=False)
+        # (the batch preprocess waits for the first view's depth sort: the
+        # sort's latency-bound kernels run at full speed first, and the
+        # preprocess then streams beside the pairs' generation)
+        depth_done = torch.cuda.Event()
+        after_depth = self.preprocess_after_depth and nv > 1 and not self.preprocess_after_first
+        self.prepare_view(0, sync=False, between=(lambda: depth_done.record(main)) if after_depth else None)
         first_done = torch.cuda.Event()
         first_done.record(main)
         pre_done = None
@@ -802,7 +820,8 @@ class TrainStep:
             # the other views' preprocess, one pass over the parameters, on
             # the side stream beside the first view's binning
             with torch.cuda.stream(self.side):
-                self.side.wait_event(first_done if self.preprocess_after_first else start)
+                self.side.wait_event(first_done if self.preprocess_after_first else
+                                     (depth_done if after_depth else start))
                 self.preprocess_views(range(1, nv))
                 pre_done = torch.cuda.Event()
                 pre_done.record(self.side)

@@ -307,8 +307,10 @@ gs_status gs_bin_sort_async(const float* proj, const float* proj_bin, int64_t n,
                             const int64_t* vis_count,
                             int32_t width, int32_t height, uint64_t* keys, int32_t* vals, int64_t pair_capacity,
                             int64_t* num_pairs_dev, uint32_t* tile_ranges, uint32_t* tile_order, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, int32_t part, void* stream) {
   CHECK(check_size(width, height));
+  REQUIRE(part == GS_BIN_ALL || part == GS_BIN_DEPTH || part == GS_BIN_PAIRS, "part = %d is not a binning part",
+          int(part));
   REQUIRE(n >= 0 && n < (int64_t(1) << 31), "n = %lld out of range", (long long)n);
   REQUIRE(pair_capacity >= 0 && pair_capacity < (int64_t(1) << 31), "pair_capacity out of range");
   REQUIRE(vis_count != nullptr && num_pairs_dev != nullptr && tile_ranges != nullptr, "NULL argument");
@@ -322,12 +324,15 @@ gs_status gs_bin_sort_async(const float* proj, const float* proj_bin, int64_t n,
   REQUIRE(workspace_bytes >= gs::binsort_ws_bytes(n, pair_capacity), "workspace too small");
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t TX = (width + 15) / 16, TY = (height + 15) / 16;
-  hipError_t e =
-      gs::launch_binsort_stage1(proj, proj_bin, n, vis_idx, vis_count, TX, TY, num_pairs_dev, workspace,
-                                pair_capacity, st);
-  if (e != hipSuccess) return hip_status(e, "gs_bin_sort_async (depth sort)");
-  e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, -1, TX, TY, keys, vals, tile_ranges, tile_order,
-                                workspace, pair_capacity, st);
+  hipError_t e = hipSuccess;
+  if (part != GS_BIN_PAIRS) {
+    e = gs::launch_binsort_stage1(proj, proj_bin, n, vis_idx, vis_count, TX, TY, num_pairs_dev, workspace,
+                                  pair_capacity, st);
+    if (e != hipSuccess) return hip_status(e, "gs_bin_sort_async (depth sort)");
+  }
+  if (part != GS_BIN_DEPTH)
+    e = gs::launch_binsort_stage2(proj, n, vis_idx, vis_count, -1, TX, TY, keys, vals, tile_ranges, tile_order,
+                                  workspace, pair_capacity, st);
   return hip_status(e, "gs_bin_sort_async");
 }
 

@@ -231,11 +231,24 @@ gs_status gs_bin_sort(const float* proj, const float* proj_bin, int64_t n, const
  * are not written, every tile range is [0, 0) (and tile_order a valid order
  * of those empty tiles); the caller detects this by comparing
  * *num_pairs_dev with pair_capacity once the stream has reached it.  The
- * rasterisers take pair_capacity as their num_pairs bound then. */
+ * rasterisers take pair_capacity as their num_pairs bound then.
+ *   part           GS_BIN_ALL; or the two halves as two calls with the same
+ *                  arguments, in stream order: GS_BIN_DEPTH (the visible
+ *                  Gaussians in depth order and the pair count M, kept in
+ *                  the workspace; num_pairs_dev written) then GS_BIN_PAIRS
+ *                  (the pairs, ranges and order from them) -- so that other
+ *                  work can be ordered between the depth sort and the pairs
+ *                  (Grendel-GS notes, training pipeline: the covering
+ *                  Gaussians found and sorted by depth per tile).
+ * GS_ERR_INVALID_ARG also for another part value. */
+#define GS_BIN_ALL 0
+#define GS_BIN_DEPTH 1
+#define GS_BIN_PAIRS 2
 gs_status gs_bin_sort_async(const float* proj, const float* proj_bin, int64_t n, const int32_t* vis_idx,
                             const int64_t* vis_count, int32_t width, int32_t height, uint64_t* keys, int32_t* vals,
                             int64_t pair_capacity, int64_t* num_pairs_dev, uint32_t* tile_ranges,
-                            uint32_t* tile_order, void* workspace, size_t workspace_bytes, void* stream);
+                            uint32_t* tile_order, void* workspace, size_t workspace_bytes, int32_t part,
+                            void* stream);
 
 /* Front-to-back alpha compositing per 16x16 tile (Grendel-GS notes,
  * training pipeline: "alpha compositing").  Per pixel, over its tile's

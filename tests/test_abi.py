@@ -90,17 +90,21 @@ def test_invalid_arguments_rejected_on_host():
                            1 << 30, None) == 1
     # asynchronous bin sort: NULL or misaligned device count, negative n
     assert lib.gs_bin_sort_async(P(16), None, 1, P(16), P(16), 8, 8, P(16), P(16), 10, None, P(16), None, P(256),
-                                 1 << 30, None) == 1
+                                 1 << 30, 0, None) == 1
     assert lib.gs_bin_sort_async(P(16), None, 1, P(16), P(16), 8, 8, P(16), P(16), 10, P(12), P(16), None, P(256),
-                                 1 << 30, None) == 1
+                                 1 << 30, 0, None) == 1
     assert lib.gs_bin_sort_async(P(16), None, -1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None, P(256),
-                                 1 << 30, None) == 1
+                                 1 << 30, 0, None) == 1
     assert lib.gs_bin_sort_async(P(16), P(40), 1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None,
-                                 P(256), 1 << 30, None) == 1
+                                 P(256), 1 << 30, 0, None) == 1
     assert b"proj_bin" in lib.gs_last_error()
+    for part in (-1, 3):
+        assert lib.gs_bin_sort_async(P(16), None, 1, P(16), P(16), 8, 8, P(16), P(16), 10, P(16), P(16), None,
+                                     P(256), 1 << 30, part, None) == 1
+        assert b"part" in lib.gs_last_error()
     # bin sort without keys: only up to 256 x 256 tiles (4128 px = 258 tiles)
     assert lib.gs_bin_sort_async(P(16), None, 1, P(16), P(16), 4128, 64, None, P(16), 10, P(16), P(16), None, P(256),
-                                 1 << 30, None) == 1
+                                 1 << 30, 0, None) == 1
     assert b"keys may be NULL" in lib.gs_last_error()
     assert lib.gs_bin_sort(P(16), None, 1, P(16), P(16), 64, 4128, None, P(16), 10, C.byref(m), P(16), None, P(256),
                            1 << 30, None) == 1

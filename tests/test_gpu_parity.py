@@ -262,6 +262,20 @@ def test_async_bin_sort_overflow_leaves_empty_ranges():
     torch.cuda.synchronize()
     assert int(m_dev.item()) == M
     assert torch.equal(keys3, keys) and torch.equal(vals3, vals) and torch.equal(ranges3, ranges)
+    # in two calls (depth sort, then pairs), other work between them: the same
+    keys4 = torch.full((M,), -1, dtype=torch.int64, device="cuda")
+    vals4 = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    ranges4 = torch.full((vw.T, 2), 7, dtype=torch.int32, device="cuda")
+    m_dev.zero_()
+    args = (step.proj, step.n, step.vis_idx[0], step.vis_count[0:1], vw.W, vw.H, keys4, vals4, M, m_dev, ranges4, ws)
+    gs.gs_bin_sort_async(*args, proj_bin=step.vbin[0], part=gs.GS_BIN_DEPTH)
+    torch.cuda.synchronize()
+    assert int(m_dev.item()) == M, "the depth part writes the pair count"
+    scratch = torch.ones(1 << 20, device="cuda") * 2.0          # unrelated work in between
+    gs.gs_bin_sort_async(*args, proj_bin=step.vbin[0], part=gs.GS_BIN_PAIRS)
+    torch.cuda.synchronize()
+    assert float(scratch.sum().item()) == 2.0 * (1 << 20)
+    assert torch.equal(keys4, keys) and torch.equal(vals4, vals) and torch.equal(ranges4, ranges)
 
 
 @pytest.mark.parametrize("case", ["small_cut", "mid_cut"])
