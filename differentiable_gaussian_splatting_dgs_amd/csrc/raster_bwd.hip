@@ -128,16 +128,18 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
     const EntryRec nxt = load_entry(proj, gnext);
     gnext = load_index(vals, uint32_t(cs - 2 * kChunk) + ul, cs - 2 * kChunk >= base);
     const uint32_t pos = uint32_t(cs) + ul - start;
-    const bool hit = stage_entry(cur, qx, qy, s_rec, lane);
+    const uint32_t pos0 = uint32_t(cs) - start;
+    // chunk entry k lies before the lane's last composited one when k < klim
+    // (list positions < 2^31); entries are staged against the box of the
+    // pixels with klim > 0, the only ones that take any entry of the chunk
+    const int32_t klim = int32_t(lastp) - int32_t(pos0);
+    const uint64_t live = __builtin_amdgcn_ballot_w64(klim > 0);
+    const bool hit = stage_entry(cur, live != 0 ? live_box(live, qx, qy) : quarter_box(qx, qy), s_rec, lane);
     cur = nxt;
     uint64_t active = uint64_t(__ballot(hit && pos < hi));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint32_t pos0 = uint32_t(cs) - start;
-    // chunk entry k lies before the lane's last composited one when k < klim
-    // (list positions < 2^31)
-    const int32_t klim = int32_t(lastp) - int32_t(pos0);
     while (active != 0) {
       const int k = 63 - __builtin_clzll(active);      // back to front
       active &= ~(1ull << k);

@@ -239,21 +239,43 @@ __device__ __forceinline__ bool ellipse_misses(float u, float v, float A, float 
   return qmin > tau2 + 1.0e-3f * fabsf(tau2) + 2.0e-3f + 1.0e-5f * S;
 }
 
+// A box of pixel centres [x0, x1] x [y0, y1].
+struct PixBox {
+  float x0, x1, y0, y1;
+};
+__device__ __forceinline__ PixBox quarter_box(float qx, float qy) { return {qx, qx + 7.0f, qy, qy + 7.0f}; }
+
+// The box spanned by the rows and columns of a quarter's lanes in `live`
+// (lane = 8 row + column; non-zero): an entry whose footprint misses it
+// reaches none of those pixels.  `live` is wave-uniform, so the masks are
+// scalar work.
+__device__ __forceinline__ PixBox live_box(uint64_t live, float qx, float qy) {
+  uint64_t c = live | (live >> 32);
+  c |= c >> 16;
+  c |= c >> 8;
+  const uint32_t cols = uint32_t(c) & 0xFFu;
+  uint32_t rows = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) rows |= ((live >> (8 * r)) & 0xFFu) != 0 ? (1u << r) : 0u;
+  return {qx + float(__builtin_ctz(cols)), qx + float(31 - __builtin_clz(cols)), qy + float(__builtin_ctz(rows)),
+          qy + float(31 - __builtin_clz(rows))};
+}
+
 // Stage a loaded entry (if any) into LDS record `lane` and return whether
-// it can reach the wave's quarter, whose pixel centres span
-// [qx, qx + 7] x [qy, qy + 7]: first the Gaussian's alpha >= 1/255 box
-// [u - ex, u + ex] x [v - ey, v + ey] against the quarter, then (for finite
+// it can reach a pixel centre of the box (the wave's quarter, or the part
+// of it whose pixels still composite): first the Gaussian's alpha >= 1/255
+// box [u - ex, u + ex] x [v - ey, v + ey] against it, then (for finite
 // boxes) the exact test of the footprint ellipse against it.
-__device__ __forceinline__ bool stage_entry(const EntryRec& r, float qx, float qy, LdsRecs& s_rec, int lane) {
+__device__ __forceinline__ bool stage_entry(const EntryRec& r, const PixBox& bx, LdsRecs& s_rec, int lane) {
   bool hit = false;
   if (r.g >= 0) {
     s_rec.r[lane].a = make_float4(r.q0.x, r.q0.y, -0.5f * r.q0.z, -r.q0.w);
     s_rec.r[lane].c = make_float4(r.q1.y, r.q1.z, r.q1.w, r.b);
     s_rec.r[lane].d = make_float2(-0.5f * r.q1.x, __builtin_bit_cast(float, r.g));
     const float u = r.q0.x, v = r.q0.y;
-    hit = u + r.ex >= qx && u - r.ex <= qx + 7.0f && v + r.ey >= qy && v - r.ey <= qy + 7.0f;
+    hit = u + r.ex >= bx.x0 && u - r.ex <= bx.x1 && v + r.ey >= bx.y0 && v - r.ey <= bx.y1;
     if (hit && r.ex < 1.0e30f)
-      hit = !ellipse_misses(u, v, r.q0.z, r.q0.w, r.q1.x, r.q1.y, qx, qx + 7.0f, qy, qy + 7.0f);
+      hit = !ellipse_misses(u, v, r.q0.z, r.q0.w, r.q1.x, r.q1.y, bx.x0, bx.x1, bx.y0, bx.y1);
   }
   return hit;
 }

@@ -70,7 +70,9 @@ __device__ __forceinline__ void fwd_list(const float4* __restrict__ proj, const 
     const EntryRec nxt = load_entry(proj, gnext);
     const uint32_t j2 = cs + 2 * kChunk + ul;
     gnext = load_index(vals, j2, j2 < end);
-    const bool hit = stage_entry(cur, qx, qy, s_rec, lane);
+    // (against the box of the pixels still compositing: an entry outside
+    // it would be skipped by every one of them)
+    const bool hit = stage_entry(cur, live_box(st.livem, qx, qy), s_rec, lane);
     cur = nxt;
     uint64_t active = __ballot(hit);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
