@@ -425,8 +425,8 @@ def main():
                     help="one step, then print only the tile-block / all-to-all measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the multi-GPU sharding is a design in DESIGN.md, not code)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the step's sharding over "
+              "several GPUs is described in the design notes, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
