@@ -206,7 +206,7 @@ __device__ __forceinline__ void bwd_range(const float4* __restrict__ proj, const
       }
       const int kk = row == 0 ? ks[0] : (row == 1 ? ks[1] : (row == 2 ? ks[2] : ks[3]));
       if (kk >= 0 && fc < 9) {
-        // (24-bit multiplies for the offsets: full rate)
+        // (the offsets as 24-bit multiplies: kk < 64)
         const uint32_t acc = lds_addr(s_acc) + __umul24(uint32_t(kk), uint32_t(kAcc * 4));
         const uint32_t rk = lds_addr(s_rec.r) + __umul24(uint32_t(kk), uint32_t(sizeof(LdsRec)));
         const float x = lds_load1(acc + 4 * fc);

@@ -142,9 +142,9 @@ struct LdsRecs {
 };
 
 // LDS addresses as 32-bit byte offsets.  Record reads and sum stores go
-// through them so that an entry's address is one 32-bit add: through a
-// generic pointer the compiler forms it with a 64-bit multiply-add, a
-// quarter-rate instruction, on every visit.
+// through them so that an entry's address is one 32-bit add of a scalar
+// offset (through a generic pointer the compiler formed it with a 64-bit
+// multiply-add on every visit).
 using LdsFloatL = __attribute__((address_space(3))) float;
 typedef float F4v __attribute__((ext_vector_type(4)));
 typedef float F2v __attribute__((ext_vector_type(2)));
