@@ -450,8 +450,8 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
   finish_loss(partial, nb, inv3p, w_l1, w_ssim, with_ssim, loss, sh);
 }
 
-// Workgroups of a persistent SSIM kernel: as many as fit on the device at
-// once (LDS-limited), at most one per tile.
+// Workgroups of a persistent SSIM kernel: per_cu per compute unit, at most
+// one per tile.
 int persistent_blocks(int per_cu, int64_t tiles) {
   static int cus[64] = {0};
   int dev = 0;
@@ -486,8 +486,11 @@ hipError_t launch_loss(const float* image, const float* target, int32_t width, i
   if (w_ssim != 0.0f) {
     const int tx = (width + kLX - 1) / kLX, ty = (height + kLY - 1) / kLY;
     const int64_t tiles = ssim_blocks(width, height);
-    // 39 KB / 40 KB of LDS per workgroup: four of each per CU
-    const int nb = persistent_blocks(4, tiles);
+    // 39 KB / 40 KB of LDS per workgroup: four of each fit on a CU.  Twice
+    // that many workgroups, each with half the tiles: where other kernels
+    // still hold part of the CUs, the second half starts wherever slots free
+    // up, so fewer tiles wait behind a late-starting workgroup
+    const int nb = persistent_blocks(8, tiles);
     if (P < (int64_t(1) << 30)) {
       k_ssim_fwd<uint32_t><<<nb, 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, partial);
       k_ssim_bwd<uint32_t><<<nb, 256, 0, st>>>(image, target, width, height, tx, ty, win, maps, w_l1, w_ssim,
