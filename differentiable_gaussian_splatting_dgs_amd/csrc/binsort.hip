@@ -42,10 +42,15 @@ namespace {
 constexpr int kFewPrio = 3;
 
 constexpr int kRT = 256;                 // radix threads per block
-constexpr int kRI = 8;                   // items per thread
-constexpr int kRB = kRT * kRI;           // items per block
+constexpr int kRI = 8;                   // items per thread (blocks of 2048 items)
+constexpr int kRIBig = 16;               // items per thread of a large sort
+constexpr int kRB = kRT * kRI;           // items per block: the most blocks a sort uses
 constexpr int kWaves = kRT / 64;
-constexpr int kWaveItems = kRI * 64;
+// Sorts of at least this many items (an upper bound known on the host) take
+// kRIBig items per thread: half the blocks, so half the digit histograms to
+// write, scan and read back, and still >= 1024 blocks for 256 CUs.  Below it
+// the smaller blocks keep the device full (a 1M-item sort is 489 blocks).
+constexpr int64_t kBigSort = int64_t(1) << 22;
 
 __device__ __forceinline__ uint32_t digit_of(uint16_t k, int shift) { return (uint32_t(k) >> shift) & 0xFFu; }
 __device__ __forceinline__ uint32_t digit_of(uint32_t k, int shift) { return (k >> shift) & 0xFFu; }
@@ -58,7 +63,7 @@ __device__ __forceinline__ int64_t count_of(const int64_t* dev, int64_t host) {
 // ---------------------------------------------------------------------------
 // radix pass pieces
 // ---------------------------------------------------------------------------
-template <class K>
+template <class K, int NI>
 __global__ __launch_bounds__(kRT) void k_upsweep(const K* __restrict__ keys, const int64_t* count_dev,
                                                  int64_t count_host, int shift, uint32_t* __restrict__ H,
                                                  int nb) {
@@ -67,16 +72,16 @@ __global__ __launch_bounds__(kRT) void k_upsweep(const K* __restrict__ keys, con
   hist[t] = 0;
   __syncthreads();
   const int64_t count = count_of(count_dev, count_host);
-  const int64_t base = int64_t(blockIdx.x) * kRB + int64_t(w) * kWaveItems;
+  const int64_t base = int64_t(blockIdx.x) * (kRT * NI) + int64_t(w) * (NI * 64);
   // all loads first, so they are in flight together
-  uint32_t dg[kRI];
+  uint32_t dg[NI];
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
+  for (int it = 0; it < NI; ++it) {
     const int64_t idx = base + it * 64 + lane;
     dg[it] = idx < count ? digit_of(keys[idx], shift) : 0u;
   }
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
+  for (int it = 0; it < NI; ++it) {
     if (base + it * 64 + lane < count) atomicAdd(&hist[dg[it]], 1u);
   }
   __syncthreads();
@@ -158,17 +163,18 @@ __device__ __forceinline__ void rank_chunk(const uint32_t (&d)[NI], const bool (
   __syncthreads();
 }
 
-// One radix block (kRI items per thread, input index base + it * 64 + lane
+// One radix block (NI items per thread, input index base + it * 64 + lane
 // for this thread, absent past `count`): rank_chunk plus each digit's
 // global destination from the scanned histograms H / rowtot.
-__device__ __forceinline__ void rank_block(const uint32_t (&d)[kRI], int64_t base, int64_t count,
+template <int NI>
+__device__ __forceinline__ void rank_block(const uint32_t (&d)[NI], int64_t base, int64_t count,
                                            const uint32_t* __restrict__ H, const uint32_t* __restrict__ rowtot,
-                                           int nb, RankSmem& sm, uint32_t (&pos)[kRI]) {
+                                           int nb, RankSmem& sm, uint32_t (&pos)[NI]) {
   const int t = threadIdx.x, lane = t & 63;
-  bool valid[kRI];
+  bool valid[NI];
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) valid[it] = base + it * 64 + lane < count;
-  rank_chunk<kRI>(d, valid, sm, pos);
+  for (int it = 0; it < NI; ++it) valid[it] = base + it * 64 + lane < count;
+  rank_chunk<NI>(d, valid, sm, pos);
   uint32_t rtot;
   const uint32_t rex = block_exclusive_scan<kRT, uint32_t>(rowtot[t], sm.sc, rtot);
   sm.gbase[t] = rex + H[size_t(t) * nb + blockIdx.x];
@@ -177,42 +183,42 @@ __device__ __forceinline__ void rank_block(const uint32_t (&d)[kRI], int64_t bas
 
 // Plain stable pass: (key, value) -> (key, value) ordered by the digit at
 // `shift`.
-template <class K>
+template <class K, int NI>
 __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, const uint32_t* __restrict__ vin,
                                                  K* __restrict__ kout, uint32_t* __restrict__ vout,
                                                  const int64_t* count_dev, int64_t count_host, int shift,
                                                  const uint32_t* __restrict__ H,
                                                  const uint32_t* __restrict__ rowtot, int nb) {
   __shared__ RankSmem sm;
-  __shared__ K s_key[kRB];
-  __shared__ uint32_t s_val[kRB];
+  __shared__ K s_key[(kRT * NI)];
+  __shared__ uint32_t s_val[(kRT * NI)];
   const int64_t count = count_of(count_dev, count_host);
-  const int64_t bbase = int64_t(blockIdx.x) * kRB;
+  const int64_t bbase = int64_t(blockIdx.x) * (kRT * NI);
   if (bbase >= count) return;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  K key[kRI];
-  uint32_t val[kRI], d[kRI], pos[kRI];
-  const int64_t base = bbase + int64_t(w) * kWaveItems;
+  K key[NI];
+  uint32_t val[NI], d[NI], pos[NI];
+  const int64_t base = bbase + int64_t(w) * (NI * 64);
   // all loads first, so they are in flight together
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
+  for (int it = 0; it < NI; ++it) {
     const int64_t idx = base + it * 64 + lane;
     const bool valid = idx < count;
     key[it] = valid ? kin[idx] : K(0);
     val[it] = valid ? vin[idx] : 0u;
   }
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) d[it] = digit_of(key[it], shift);
+  for (int it = 0; it < NI; ++it) d[it] = digit_of(key[it], shift);
   rank_block(d, base, count, H, rowtot, nb, sm, pos);
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
+  for (int it = 0; it < NI; ++it) {
     if (base + it * 64 + lane < count) {
       s_key[pos[it]] = key[it];
       s_val[pos[it]] = val[it];
     }
   }
   __syncthreads();
-  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
+  const int nvalid = int(count - bbase < (kRT * NI) ? count - bbase : (kRT * NI));
   for (int j = t; j < nvalid; j += kRT) {
     const K k = s_key[j];
     const uint32_t dg = digit_of(k, shift);
@@ -226,6 +232,7 @@ __global__ __launch_bounds__(kRT) void k_scatter(const K* __restrict__ kin, cons
 // crec[value] (gathered as the block loads its items, so the random reads
 // overlap the ranking) is written at its sorted place instead of the key
 // and value.
+template <int NI>
 __global__ __launch_bounds__(kRT) void k_scatter_rec(const uint32_t* __restrict__ kin,
                                                      const uint32_t* __restrict__ vin,
                                                      const uint4* __restrict__ crec, uint4* __restrict__ rout,
@@ -233,16 +240,16 @@ __global__ __launch_bounds__(kRT) void k_scatter_rec(const uint32_t* __restrict_
                                                      const uint32_t* __restrict__ H,
                                                      const uint32_t* __restrict__ rowtot, int nb) {
   __shared__ RankSmem sm;
-  __shared__ uint4 s_rec[kRB];
+  __shared__ uint4 s_rec[(kRT * NI)];
   const int64_t count = *count_dev;
-  const int64_t bbase = int64_t(blockIdx.x) * kRB;
+  const int64_t bbase = int64_t(blockIdx.x) * (kRT * NI);
   if (bbase >= count) return;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-  uint32_t d[kRI], pos[kRI];
-  uint4 rec[kRI];
-  const int64_t base = bbase + int64_t(w) * kWaveItems;
+  uint32_t d[NI], pos[NI];
+  uint4 rec[NI];
+  const int64_t base = bbase + int64_t(w) * (NI * 64);
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
+  for (int it = 0; it < NI; ++it) {
     const int64_t idx = base + it * 64 + lane;
     const bool valid = idx < count;
     d[it] = valid ? digit_of(kin[idx], shift) : 0u;
@@ -250,11 +257,11 @@ __global__ __launch_bounds__(kRT) void k_scatter_rec(const uint32_t* __restrict_
   }
   rank_block(d, base, count, H, rowtot, nb, sm, pos);
 #pragma unroll
-  for (int it = 0; it < kRI; ++it) {
+  for (int it = 0; it < NI; ++it) {
     if (base + it * 64 + lane < count) s_rec[pos[it]] = rec[it];
   }
   __syncthreads();
-  const int nvalid = int(count - bbase < kRB ? count - bbase : kRB);
+  const int nvalid = int(count - bbase < (kRT * NI) ? count - bbase : (kRT * NI));
   for (int j = t; j < nvalid; j += kRT) {
     const uint4 e = s_rec[j];
     const uint32_t dg = digit_of(e.w, shift);
@@ -1134,13 +1141,37 @@ inline StGrid st_grid(int32_t tiles_x, int32_t tiles_y) {
   return g;
 }
 
+// Blocks of a sort of at most count_bound items at NI items per thread.
+template <int NI>
+int radix_blocks(int64_t count_bound) {
+  return int(std::max<int64_t>(1, (count_bound + kRT * NI - 1) / (kRT * NI)));
+}
+
+template <class K, int NI>
+void radix_pass_ni(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, const int64_t* count_dev,
+                   int64_t count_host, int64_t count_bound, int shift, const Ws& w, hipStream_t st) {
+  const int nb = radix_blocks<NI>(count_bound);
+  k_upsweep<K, NI><<<nb, kRT, 0, st>>>(kin, count_dev, count_host, shift, w.H, nb);
+  k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
+  k_scatter<K, NI><<<nb, kRT, 0, st>>>(kin, vin, kout, vout, count_dev, count_host, shift, w.H, w.rowtot, nb);
+}
+
 template <class K>
 void radix_pass(const K* kin, const uint32_t* vin, K* kout, uint32_t* vout, const int64_t* count_dev,
                 int64_t count_host, int64_t count_bound, int shift, const Ws& w, hipStream_t st) {
-  const int nb = int(std::max<int64_t>(1, nblocks(count_bound)));
-  k_upsweep<K><<<nb, kRT, 0, st>>>(kin, count_dev, count_host, shift, w.H, nb);
+  if (count_bound >= kBigSort)
+    radix_pass_ni<K, kRIBig>(kin, vin, kout, vout, count_dev, count_host, count_bound, shift, w, st);
+  else
+    radix_pass_ni<K, kRI>(kin, vin, kout, vout, count_dev, count_host, count_bound, shift, w, st);
+}
+
+// The depth sort's last pass (digit 24..31), records out.
+template <int NI>
+void rec_pass(const Ws& w, const int64_t* vis_count, int64_t n, hipStream_t st) {
+  const int nb = radix_blocks<NI>(n);
+  k_upsweep<uint32_t, NI><<<nb, kRT, 0, st>>>(w.dkB, vis_count, 0, 24, w.H, nb);
   k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
-  k_scatter<K><<<nb, kRT, 0, st>>>(kin, vin, kout, vout, count_dev, count_host, shift, w.H, w.rowtot, nb);
+  k_scatter_rec<NI><<<nb, kRT, 0, st>>>(w.dkB, w.dvB, w.crec, w.srec, vis_count, 24, w.H, w.rowtot, nb);
 }
 
 }  // namespace
@@ -1168,10 +1199,10 @@ hipError_t launch_binsort_stage1(const float* proj, const float* proj_bin, int64
       radix_pass<uint32_t>(even ? w.dkA : w.dkB, even ? w.dvA : w.dvB, even ? w.dkB : w.dkA,
                            even ? w.dvB : w.dvA, vis_count, 0, n, 8 * pass, w, st);
     }
-    const int nb = int(std::max<int64_t>(1, nblocks(n)));
-    k_upsweep<uint32_t><<<nb, kRT, 0, st>>>(w.dkB, vis_count, 0, 24, w.H, nb);
-    k_rowscan<<<256, kRT, 0, st>>>(w.H, nb, w.rowtot);
-    k_scatter_rec<<<nb, kRT, 0, st>>>(w.dkB, w.dvB, w.crec, w.srec, vis_count, 24, w.H, w.rowtot, nb);
+    if (n >= kBigSort)
+      rec_pass<kRIBig>(w, vis_count, n, st);
+    else
+      rec_pass<kRI>(w, vis_count, n, st);
   }
   const int nbv = int(dup_blocks(n));
   int ns = 0;
