@@ -1248,7 +1248,10 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     const StGrid sg = st_grid(tiles_x, tiles_y);
     const int ns = sg.sx * sg.sy;
     const unsigned grid = unsigned(std::min<int64_t>(max_chunks(pair_capacity), 2048));
-    const unsigned egrid = unsigned(std::min<int64_t>(max_chunks(pair_capacity) * 4, 4096));
+    // the pair expansion's (chunk, panel) tasks: up to 64 workgroups per CU,
+    // most of them queued, so the CUs that the rasterisers on the other
+    // stream free first take more of the tasks
+    const unsigned egrid = unsigned(std::min<int64_t>(max_chunks(pair_capacity) * 4, 16384));
     uint32_t* e_g = reinterpret_cast<uint32_t*>(w.pk);
     uint32_t* e_d = e_g + pair_capacity;
     uint32_t* e_r = w.pv;
