@@ -1247,7 +1247,9 @@ hipError_t launch_binsort_stage2(const float* proj, int64_t n, const int32_t* vi
     // every kernel reads the effective count (0: no pairs or overflow)
     const StGrid sg = st_grid(tiles_x, tiles_y);
     const int ns = sg.sx * sg.sy;
-    const unsigned grid = unsigned(std::min<int64_t>(max_chunks(pair_capacity), 2048));
+    // the chunk counts' grid: up to 32 workgroups per CU, as the expansion's
+    // below (a large capped grid lets the CUs freed first take more chunks)
+    const unsigned grid = unsigned(std::min<int64_t>(max_chunks(pair_capacity), 8192));
     // the pair expansion's (chunk, panel) tasks: up to 64 workgroups per CU,
     // most of them queued, so the CUs that the rasterisers on the other
     // stream free first take more of the tasks
